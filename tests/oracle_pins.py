@@ -1,0 +1,309 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each check takes a bound oracle (``oracle.Bound``) so the same battery can be
+run against the real oracle and against builds with a planted mistake. A
+check raises AssertionError when the oracle disagrees with the fact it pins.
+
+The facts (neighborhood attention as described in NATTEN issue #161, "Backward
+pass is very slow towards much tokens and large kernels": scores over a window,
+softmax over the window, weighted sum of values; backward = the gradients of
+that composition):
+  * window shape: along each axis exactly k in-bounds keys of the query's own
+    residue class, containing the query, centered when that fits and otherwise
+    the nearest such run (ties go to the lower start) -- brute force;
+  * kernel = whole grid: NA is plain softmax attention, so torch's
+    scaled_dot_product_attention (float64, CPU) and its autograd fix out,
+    logsumexp and all three gradients;
+  * the window weights of every query sum to one and lse lies in
+    [max score, max score + ln K];
+  * central finite differences of the oracle's own forward fix dq, dk, dv;
+  * k = 1: out = v, lse = scale <q, k>, dq = dk = 0, dv = dout;
+  * 3D with k_t = 1 is 2D NA applied to every frame;
+  * with dilation d, each residue class is an undilated NA on its sub-grid;
+  * heads and batch elements are independent (permutation equivariance);
+  * sum_y dv_y = sum_x dout_x and sum_y dk_y = 0 per (b, head, channel);
+  * mirroring an axis (odd k, d = 1) mirrors every output;
+  * the score scale is linear: NA(c q; scale=1) = NA(q; scale=c).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import torch
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _inputs(shape, seed, dout_ones=False):
+    r = _rng(seed)
+    q, k, v = (r.standard_normal(shape) for _ in range(3))
+    dout = np.ones(shape) if dout_ones else r.standard_normal(shape)
+    return q, k, v, dout
+
+
+# --------------------------------------------------------------------------- windows
+
+def check_windows(orc, max_len=18, max_d=3):
+    """Brute-force window properties on every small axis."""
+    for L in range(1, max_len + 1):
+        for d in range(1, max_d + 1):
+            n_min = min((L - r + d - 1) // d for r in range(min(d, L)))
+            for k in range(1, n_min + 1):
+                for x in range(L):
+                    s = orc.window_start(L, k, d, x)
+                    keys = [s + d * t for t in range(k)]
+                    assert all(0 <= y < L for y in keys), (L, k, d, x, keys)
+                    assert all(y % d == x % d for y in keys), (L, k, d, x, keys)
+                    assert x in keys, (L, k, d, x, keys)
+                    # all runs of k consecutive class members that contain x
+                    r = x % d
+                    n = (L - r + d - 1) // d
+                    i = x // d
+                    runs = [a for a in range(0, n - k + 1) if a <= i < a + k]
+                    # nearest run center to the query; ties go to the lower start
+                    best = min(runs, key=lambda a: (abs((a + (k - 1) / 2) - i), a))
+                    assert s == r + d * best, (L, k, d, x, s, r + d * best)
+
+
+# --------------------------------------------------------------------------- dense
+
+def _flat(a, ndim):
+    """[B, (T,) H, W, h, D] -> [B, h, N, D]."""
+    B, h, D = a.shape[0], a.shape[-2], a.shape[-1]
+    return a.reshape(B, -1, h, D).transpose(0, 2, 1, 3)
+
+
+def check_dense(orc, grid=(4, 5), heads=2, D=3, seed=0, tol=1e-11):
+    """kernel = whole grid: compare with torch's dense attention and autograd."""
+    shape = (2,) + tuple(grid) + (heads, D)
+    q, k, v, dout = _inputs(shape, seed)
+    scale = 0.7
+    out, lse = orc.na_fwd(q, k, v, grid, 1, scale)
+    dq, dk, dv = orc.na_bwd(q, k, v, dout, grid, 1, scale)
+
+    nd = len(grid)
+    tq, tk, tv = (torch.tensor(_flat(a, nd), requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    tlse = torch.logsumexp(scale * (tq @ tk.transpose(-1, -2)), dim=-1)
+    to.backward(torch.tensor(_flat(dout, nd)))
+
+    ref = {
+        "out": to.detach().numpy(), "lse": tlse.detach().numpy(),
+        "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy(),
+    }
+    got = {"out": _flat(out, nd), "lse": lse.reshape(2, -1, heads).transpose(0, 2, 1),
+           "dq": _flat(dq, nd), "dk": _flat(dk, nd), "dv": _flat(dv, nd)}
+    for name in ref:
+        err = np.max(np.abs(got[name] - ref[name])) / max(1.0, np.max(np.abs(ref[name])))
+        assert err < tol, (name, err)
+
+
+# --------------------------------------------------------------------------- weights
+
+def check_weights(orc, seed=1):
+    for shape, kernel, dil in [((1, 7, 6, 2, 4), (3, 5), 1), ((1, 9, 8, 1, 3), (3, 3), 2),
+                               ((1, 4, 6, 6, 2, 3), (3, 3, 5), (1, 2, 1))]:
+        q, k, v, _ = _inputs(shape, seed)
+        scale = 0.9
+        w, keys = orc.na_weights(q, k, kernel, dil, scale)
+        assert np.max(np.abs(w.sum(1) - 1.0)) < 1e-12
+        assert np.all(w >= 0)
+        # every key of a window is distinct
+        assert all(len(set(r)) == r.size for r in keys)
+        _, lse = orc.na_fwd(q, k, v, kernel, dil, scale)
+        # scores reconstructed from the weights: s = lse + log w; max s <= lse <= max s + ln K
+        lse = lse.reshape(-1)
+        smax = lse + np.log(w.max(1))
+        K = w.shape[1]
+        assert np.all(lse >= smax - 1e-12) and np.all(lse <= smax + np.log(K) + 1e-12)
+        # the weights are the softmax of scale * <q, k_y> over the listed keys
+        h = shape[-2]
+        qf = q.reshape(-1, shape[-1])
+        kf = k.reshape(shape[0], -1, h, shape[-1])
+        n_tok = kf.shape[1]
+        for u in range(0, qf.shape[0], max(1, qf.shape[0] // 23)):
+            b, tok, hh = u // (h * n_tok), (u // h) % n_tok, u % h
+            s = scale * kf[b, keys[u], hh] @ qf[u]
+            e = np.exp(s - s.max())
+            assert np.max(np.abs(e / e.sum() - w[u])) < 1e-12
+
+
+# --------------------------------------------------------------------------- finite differences
+
+FD_CASES = [
+    ((1, 5, 6, 2, 3), (3, 3), 1),
+    ((1, 7, 7, 1, 2), (3, 3), 2),
+    ((1, 3, 4, 5, 1, 2), (3, 3, 3), 1),
+    ((1, 6, 5, 1, 2), (4, 2), 1),
+    ((2, 5, 4, 1, 2), (2, 3), (2, 1)),
+]
+
+
+def check_fd(orc, case, seed=2, h=1e-6, tol=2e-7):
+    shape, kernel, dil = case
+    q, k, v, dout = _inputs(shape, seed)
+    scale = 0.8
+    dq, dk, dv = orc.na_bwd(q, k, v, dout, kernel, dil, scale)
+
+    def loss(qq, kk, vv):
+        out, _ = orc.na_fwd(qq, kk, vv, kernel, dil, scale)
+        return float(np.sum(out * dout))
+
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        num = np.empty_like(g)
+        for idx in np.ndindex(g.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            t = {"dq": 0, "dk": 1, "dv": 2}[name]
+            args[t][idx] += h
+            lp = loss(*args)
+            args[t][idx] -= 2 * h
+            lm = loss(*args)
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(num - g)) / max(1.0, np.max(np.abs(g)))
+        assert err < tol, (name, case, err)
+
+
+# --------------------------------------------------------------------------- special cases
+
+def check_k1(orc, seed=3):
+    for shape, kernel in [((2, 4, 5, 3, 4), (1, 1)), ((1, 2, 3, 4, 2, 3), (1, 1, 1))]:
+        q, k, v, dout = _inputs(shape, seed)
+        scale = 1.3
+        out, lse = orc.na_fwd(q, k, v, kernel, 1, scale)
+        assert np.max(np.abs(out - v)) < 1e-13
+        assert np.max(np.abs(lse - scale * np.sum(q * k, -1))) < 1e-12
+        dq, dk, dv = orc.na_bwd(q, k, v, dout, kernel, 1, scale)
+        assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+        assert np.max(np.abs(dv - dout)) < 1e-13
+
+
+def check_kt1(orc, seed=4):
+    shape = (1, 3, 6, 6, 2, 3)
+    q, k, v, dout = _inputs(shape, seed)
+    out3, lse3 = orc.na_fwd(q, k, v, (1, 3, 3), (1, 1, 2))
+    g3 = orc.na_bwd(q, k, v, dout, (1, 3, 3), (1, 1, 2))
+    for t in range(shape[1]):
+        sl = (slice(None), t)
+        out2, lse2 = orc.na_fwd(q[sl], k[sl], v[sl], (3, 3), (1, 2))
+        g2 = orc.na_bwd(q[sl], k[sl], v[sl], dout[sl], (3, 3), (1, 2))
+        assert np.max(np.abs(out3[sl] - out2)) < 1e-13
+        assert np.max(np.abs(lse3[sl] - lse2)) < 1e-13
+        for a, b in zip(g3, g2):
+            assert np.max(np.abs(a[sl] - b)) < 1e-12
+
+
+def check_dilation(orc, seed=5):
+    for shape, kernel, dil in [((1, 9, 9, 2, 3), (3, 3), (2, 3)),
+                               ((1, 5, 7, 6, 1, 2), (2, 3, 2), (2, 2, 3))]:
+        q, k, v, dout = _inputs(shape, seed)
+        out, lse = orc.na_fwd(q, k, v, kernel, dil)
+        g = orc.na_bwd(q, k, v, dout, kernel, dil)
+        nd = len(kernel)
+        for res in itertools.product(*(range(d) for d in dil)):
+            sl = (slice(None),) + tuple(slice(r, None, d) for r, d in zip(res, dil))
+            o2, l2 = orc.na_fwd(q[sl], k[sl], v[sl], kernel, 1)
+            g2 = orc.na_bwd(q[sl], k[sl], v[sl], dout[sl], kernel, 1)
+            assert np.max(np.abs(out[sl] - o2)) < 1e-13, (res, nd)
+            assert np.max(np.abs(lse[sl] - l2)) < 1e-13
+            for a, b in zip(g, g2):
+                assert np.max(np.abs(a[sl] - b)) < 1e-12
+
+
+def check_heads(orc, seed=6):
+    shape = (3, 5, 6, 4, 3)
+    q, k, v, dout = _inputs(shape, seed)
+    perm_h = np.array([2, 0, 3, 1])
+    perm_b = np.array([1, 2, 0])
+    out, lse = orc.na_fwd(q, k, v, (3, 5))
+    g = orc.na_bwd(q, k, v, dout, (3, 5))
+    P = lambda a: a[perm_b][..., perm_h, :]  # noqa: E731
+    o2, l2 = orc.na_fwd(P(q), P(k), P(v), (3, 5))
+    g2 = orc.na_bwd(P(q), P(k), P(v), P(dout), (3, 5))
+    assert np.max(np.abs(P(out) - o2)) < 1e-14
+    assert np.max(np.abs(lse[perm_b][..., perm_h] - l2)) < 1e-14
+    for a, b in zip(g, g2):
+        assert np.max(np.abs(P(a) - b)) < 1e-13
+
+
+def check_sums(orc, seed=7):
+    for shape, kernel, dil in [((2, 6, 7, 2, 3), (3, 5), 1), ((1, 3, 5, 6, 2, 2), (3, 3, 3), (1, 1, 2))]:
+        q, k, v, dout = _inputs(shape, seed)
+        dq, dk, dv = orc.na_bwd(q, k, v, dout, kernel, dil)
+        axes = tuple(range(1, len(shape) - 2))  # spatial axes
+        assert np.max(np.abs(dv.sum(axes) - dout.sum(axes))) < 1e-11
+        assert np.max(np.abs(dk.sum(axes))) < 1e-11
+
+
+def check_reflection(orc, seed=8):
+    shape = (1, 4, 7, 6, 2, 3)
+    kernel = (3, 5, 3)
+    q, k, v, dout = _inputs(shape, seed)
+    out, lse = orc.na_fwd(q, k, v, kernel)
+    g = orc.na_bwd(q, k, v, dout, kernel)
+    for ax in (1, 2, 3):
+        F = lambda a: np.flip(a, ax)  # noqa: E731
+        o2, l2 = orc.na_fwd(F(q), F(k), F(v), kernel)
+        g2 = orc.na_bwd(F(q), F(k), F(v), F(dout), kernel)
+        assert np.max(np.abs(F(out) - o2)) < 1e-13, ax
+        assert np.max(np.abs(F(lse) - l2)) < 1e-13, ax
+        for a, b in zip(g, g2):
+            assert np.max(np.abs(F(a) - b)) < 1e-12, ax
+
+
+def check_scale(orc, seed=9):
+    shape = (1, 6, 5, 2, 3)
+    q, k, v, dout = _inputs(shape, seed)
+    c = 0.37
+    o1, l1 = orc.na_fwd(q, k, v, (3, 3), 1, c)
+    o2, l2 = orc.na_fwd(c * q, k, v, (3, 3), 1, 1.0)
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.max(np.abs(l1 - l2)) < 1e-13
+    dq1, dk1, dv1 = orc.na_bwd(q, k, v, dout, (3, 3), 1, c)
+    dq2, dk2, dv2 = orc.na_bwd(c * q, k, v, dout, (3, 3), 1, 1.0)
+    assert np.max(np.abs(dq1 - c * dq2)) < 1e-12
+    assert np.max(np.abs(dk1 - dk2)) < 1e-12 and np.max(np.abs(dv1 - dv2)) < 1e-12
+
+
+def check_selection(orc, seed=10):
+    """Sampled evaluation returns exactly the full evaluation's entries."""
+    shape = (2, 5, 6, 3, 4)
+    q, k, v, dout = _inputs(shape, seed)
+    out, lse = orc.na_fwd(q, k, v, (3, 3), 1)
+    dq, dk, dv = orc.na_bwd(q, k, v, dout, (3, 3), 1)
+    sel = np.array([0, 7, 31, 59, 100, 179])
+    o2, l2 = orc.na_fwd(q, k, v, (3, 3), 1, sel=sel)
+    g2 = orc.na_bwd(q, k, v, dout, (3, 3), 1, sel=sel)
+    D = shape[-1]
+    assert np.array_equal(out.reshape(-1, D)[sel], o2)
+    assert np.array_equal(lse.reshape(-1)[sel], l2)
+    for a, b in zip((dq, dk, dv), g2):
+        assert np.array_equal(a.reshape(-1, D)[sel], b)
+
+
+ALL_CHECKS = [
+    ("windows", lambda o: check_windows(o)),
+    ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
+    ("dense3d", lambda o: check_dense(o, grid=(2, 3, 4))),
+    ("weights", check_weights),
+    ("k1", check_k1),
+    ("kt1", check_kt1),
+    ("dilation", check_dilation),
+    ("heads", check_heads),
+    ("sums", check_sums),
+    ("reflection", check_reflection),
+    ("scale", check_scale),
+    ("selection", check_selection),
+] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
+
+
+def failing_checks(orc):
+    """Names of the checks the given oracle build fails."""
+    bad = []
+    for name, fn in ALL_CHECKS:
+        try:
+            fn(orc)
+        except (AssertionError, IndexError, ValueError, FloatingPointError):
+            bad.append(name)
+    return bad
