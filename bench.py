@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of fused neighborhood attention forward + backward on one MI355X.
+
+One step is the whole hot path on one batch of synthetic input: na_fwd, then
+the gather backward (na_bwd_dq, na_bwd_dkdv -- together exactly na_bwd with
+NA_BWD_GATHER), inputs resident in HBM. W untimed warm-up steps, then K timed
+steps between two device synchronizations; per-kernel durations come from HIP
+events recorded on the stream the kernels are launched on.
+
+Workloads (from NATTEN issue #161's benchmark script: 8 heads of dimension 32,
+fp32, q/k/v standard normal, loss = out.sum() so dout = ones): the headline is
+the 2D 1024x1024 grid with a 9x9 window; the 3D 16x256x256 grid with a 3x5x5
+window is measured in the same run and reported beside it.
+
+Effective FLOPs (the metric's convention): forward 4*N*heads*K*D, backward
+2.5x that, with N tokens and K = prod(kernel). Prints one JSON line on stdout;
+progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fwd_bwd_amd import na  # noqa: E402
+from fwd_bwd_amd.inputs import HEADLINE, HEADLINE_3D, WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "NA fwd+bwd ms & TFLOP/s (% roofline): 2D 1024² k9×9, 3D 16×256² k3×5×5"
+PEAK_TFLOPS = {"fp32_mfma": 157.3, "bf16_mfma": 2516.6}
+PEAK_HBM_GBS = 8000.0
+
+# contraction FLOPs each kernel performs per (query or key) x window entry x channel,
+# without tile waste: fwd = QK^T + PV; dq = QK^T + dO V^T + dS K;
+# dk/dv = QK^T + dO V^T + P^T dO + dS^T Q
+KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops(w):
+    base = w.tokens * w.heads * w.window * w.head_dim
+    return 4.0 * base, 10.0 * base
+
+
+def algorithmic_bytes(w):
+    e = torch.tensor([], dtype=w.dtype).element_size()
+    t = w.tokens * w.heads * w.head_dim * e
+    rows = w.tokens * w.heads * 4
+    fwd = 4 * t + rows                  # q, k, v read; out written; lse written
+    bwd = 8 * t + rows + 2 * rows       # q, k, v, out, dout read; dq, dk, dv written; lse; delta w+r
+    return fwd, bwd, {"fwd": 4 * t + rows, "bwd_dq": 5 * t + 2 * rows,
+                      "bwd_dkdv": 6 * t + 2 * rows}
+
+
+class Runner:
+    def __init__(self, w, variant, seed=0):
+        self.w = w
+        self.variant = variant
+        dev = torch.device("cuda:0")
+        log(f"[bench] generating inputs for {w.name}")
+        q, k, v, dout = make_inputs(w, seed)
+        self.host = (q, k, v, dout)
+        self.q, self.k, self.v, self.dout = (t.to(dev) for t in (q, k, v, dout))
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.delta = torch.empty_like(self.lse)
+        p = na.make_problem(w.shape, w.dtype, w.kernel, w.dilation, w.the_scale)
+        ws = na.bwd_workspace_bytes(p, na.VARIANTS[variant])
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.args = (w.kernel, w.dilation, w.the_scale)
+
+    def fwd(self):
+        na.na_fwd(self.q, self.k, self.v, *self.args, out=self.out, lse=self.lse)
+
+    def bwd_dq(self):
+        na.na_bwd_dq(self.q, self.k, self.v, self.out, self.dout, self.lse, *self.args,
+                     dq=self.dq, delta=self.delta)
+
+    def bwd_dkdv(self):
+        na.na_bwd_dkdv(self.q, self.k, self.v, self.dout, self.lse, self.delta, *self.args,
+                       dk=self.dk, dv=self.dv)
+
+    def bwd_kvpar(self):
+        na.na_bwd(self.q, self.k, self.v, self.out, self.dout, self.lse, *self.args,
+                  variant="kvparallel", workspace=self.ws, grads=(self.dq, self.dk, self.dv))
+
+    def phases(self):
+        if self.variant == "gather":
+            return [("fwd", self.fwd), ("bwd_dq", self.bwd_dq), ("bwd_dkdv", self.bwd_dkdv)]
+        return [("fwd", self.fwd), ("bwd_kvparallel", self.bwd_kvpar)]
+
+    def time(self, steps, warmup):
+        ph = self.phases()
+        for _ in range(warmup):
+            for _, f in ph:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ph) + 1)]
+              for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for s in range(steps):
+            ev[s][0].record()
+            for i, (_, f) in enumerate(ph):
+                f()
+                ev[s][i + 1].record()
+        end.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        per = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+               for i, (name, _) in enumerate(ph)}
+        return start.elapsed_time(end) / steps, wall, per
+
+
+def summarize(w, ms_step, per):
+    f_fwd, f_bwd = flops(w)
+    b_fwd, b_bwd, b_kern = algorithmic_bytes(w)
+    fwd_ms = per["fwd"]
+    bwd_ms = sum(v for k, v in per.items() if k != "fwd")
+    peak = PEAK_TFLOPS["fp32_mfma"]   # every contraction runs on fp32 MFMA
+    return {
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(ms_step, 4),
+        "tflops_fwd": round(f_fwd / fwd_ms / 1e9, 3), "tflops_bwd": round(f_bwd / bwd_ms / 1e9, 3),
+        "tflops_total": round((f_fwd + f_bwd) / ms_step / 1e9, 3),
+        "mfma_frac_fwd": round(f_fwd / fwd_ms / 1e9 / peak, 4),
+        "mfma_frac_bwd": round(f_bwd / bwd_ms / 1e9 / peak, 4),
+        "mfma_frac_total": round((f_fwd + f_bwd) / ms_step / 1e9 / peak, 4),
+        "hbm_frac_fwd": round(b_fwd / fwd_ms / 1e6 / PEAK_HBM_GBS, 4),
+        "hbm_frac_bwd": round(b_bwd / bwd_ms / 1e6 / PEAK_HBM_GBS, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+    }
+
+
+def roofline(w, per):
+    name = max((k for k in per if k in KERNEL_FLOP_UNITS), key=lambda k: per[k])
+    base = w.tokens * w.heads * w.window * w.head_dim
+    fl = KERNEL_FLOP_UNITS[name] * base
+    achieved = fl / (per[name] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["fp32_mfma"]
+    return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 3), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+            "flops_per_launch": fl, "avg_launch_ms": round(per[name], 4)}
+
+
+def cpu_baseline(w, host, target_s, seed=1):
+    import oracle
+    q, k, v, dout = (t.float().numpy().astype(np.float64) for t in host)
+    units = w.tokens * w.heads
+    rng = np.random.default_rng(seed)
+
+    def run(n):
+        sel = np.sort(rng.integers(0, units, n))
+        t0 = time.perf_counter()
+        oracle.na_fwd(q, k, v, w.kernel, w.dilation, w.the_scale, sel=sel)
+        oracle.na_bwd(q, k, v, dout, w.kernel, w.dilation, w.the_scale, sel=sel)
+        return time.perf_counter() - t0
+
+    pilot_n = 256
+    t_pilot = run(pilot_n)
+    n = int(max(pilot_n, min(units, pilot_n * target_s / max(t_pilot, 1e-6))))
+    log(f"[bench] oracle pilot {pilot_n} units {t_pilot:.2f}s -> sample {n} units")
+    t = run(n)
+    f_fwd, f_bwd = flops(w)
+    full_s = t * units / n
+    return {"value": round((f_fwd + f_bwd) / full_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"{n} random (b, token, head) units of {w.name}: forward and dq at them "
+                       f"as queries, dk and dv at them as keys, fp64, {t:.1f} s; rate "
+                       f"extrapolated linearly to the whole workload ({full_s:.0f} s)"),
+            "est_full_ms": round(full_s * 1e3, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--variant", default="gather", choices=["gather", "kvparallel"])
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 3D workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: neighborhood attention here runs on a single "
+              "MI355X; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    na.load()
+
+    w = WORKLOADS[args.workload]
+    r = Runner(w, args.variant)
+    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
+    ms, wall, per = r.time(args.steps, args.warmup)
+    main_sum = summarize(w, ms, per)
+    log(f"[bench] {w.name}: {main_sum}")
+    f_fwd, f_bwd = flops(w)
+
+    result = {
+        "metric": METRIC,
+        "value": main_sum["tflops_total"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_sum["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "grid": list(w.grid),
+                   "heads": w.heads, "head_dim": w.head_dim, "kernel": list(w.kernel),
+                   "dilation": list(w.dilation), "backward": args.variant},
+        "wall_ms_per_step": round(wall, 4),
+        **{k: v for k, v in main_sum.items() if k != "ms_per_step"},
+        "roofline": roofline(w, per),
+    }
+
+    host = r.host
+    if not args.no_secondary and args.workload == HEADLINE:
+        w3 = WORKLOADS[HEADLINE_3D]
+        del r
+        torch.cuda.empty_cache()
+        r3 = Runner(w3, args.variant)
+        log(f"[bench] timing {w3.name}")
+        ms3, _, per3 = r3.time(args.steps, args.warmup)
+        s3 = summarize(w3, ms3, per3)
+        s3["roofline"] = roofline(w3, per3)
+        result["secondary"] = {"workload": w3.name, **s3}
+        log(f"[bench] {w3.name}: {s3}")
+        del r3
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+
+    result["host"] = {"cpu_count": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+                      "processor": platform.processor(),
+                      "gpu": torch.cuda.get_device_name(0)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

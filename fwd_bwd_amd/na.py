@@ -1,0 +1,259 @@
+"""Thin ctypes binding of libna (include/na.h): argument marshalling only.
+
+Every step of neighborhood attention runs in the library's HIP kernels; this
+module allocates the output tensors with torch (device memory and the current
+stream are the only things torch provides), passes raw pointers, and turns a
+non-OK status into an exception. There is no fallback: if libna.so is missing
+or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libna.so")
+
+NA_OK = 0
+NA_ERR_INVALID_ARG = 1
+NA_ERR_UNSUPPORTED = 2
+NA_ERR_WORKSPACE = 3
+NA_ERR_HIP = 4
+
+NA_F32 = 0
+NA_BF16 = 1
+
+NA_BWD_GATHER = 0
+NA_BWD_KVPARALLEL = 1
+VARIANTS = {"gather": NA_BWD_GATHER, "kvparallel": NA_BWD_KVPARALLEL}
+
+# every symbol include/na.h declares
+EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na_bwd_dq",
+           "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window")
+
+
+class NaProblem(ctypes.Structure):
+    """Mirror of na_problem."""
+    _fields_ = [
+        ("ndim", ctypes.c_int64),
+        ("dtype", ctypes.c_int64),
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("extent", ctypes.c_int64 * 3),
+        ("kernel", ctypes.c_int64 * 3),
+        ("dilation", ctypes.c_int64 * 3),
+        ("scale", ctypes.c_double),
+    ]
+
+
+class NaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libna.so (built in-tree by fwd_bwd_amd.build); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run fwd_bwd_amd.build.build() first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, P = ctypes.c_void_p, ctypes.POINTER(NaProblem)
+        i64 = ctypes.c_int64
+        lib.na_check_problem.argtypes = [P]
+        lib.na_check_problem.restype = ctypes.c_int
+        lib.na_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.na_fwd.restype = ctypes.c_int
+        lib.na_bwd_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        lib.na_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.na_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                               ctypes.c_int32, vp]
+        lib.na_bwd.restype = ctypes.c_int
+        lib.na_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_bwd_dq.restype = ctypes.c_int
+        lib.na_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_bwd_dkdv.restype = ctypes.c_int
+        lib.na_status_string.argtypes = [ctypes.c_int]
+        lib.na_status_string.restype = ctypes.c_char_p
+        lib.na_window_start.argtypes = [i64, i64, i64, i64]
+        lib.na_window_start.restype = i64
+        lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
+                                          ctypes.POINTER(i64)]
+        lib.na_inverse_window.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != NA_OK:
+        raise NaError(status, load().na_status_string(status).decode())
+
+
+def _tuple(v: Union[int, Sequence[int]], n: int) -> Tuple[int, ...]:
+    if isinstance(v, int):
+        return (v,) * n
+    v = tuple(int(a) for a in v)
+    if len(v) != n:
+        raise ValueError(f"expected {n} values, got {v}")
+    return v
+
+
+_DTYPES = {torch.float32: NA_F32, torch.bfloat16: NA_BF16}
+
+
+def make_problem(shape: Sequence[int], dtype: torch.dtype, kernel_size, dilation=1,
+                 scale: Optional[float] = None) -> NaProblem:
+    """na_problem for a token-major tensor shape [B, (T,) H, W, heads, head_dim]."""
+    ndim = len(shape) - 3
+    if ndim not in (2, 3):
+        raise ValueError(f"expected [B, (T,) H, W, heads, head_dim], got shape {tuple(shape)}")
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    p = NaProblem()
+    p.ndim = ndim
+    p.dtype = _DTYPES[dtype]
+    p.batch, p.heads, p.head_dim = int(shape[0]), int(shape[-2]), int(shape[-1])
+    ext = tuple(int(s) for s in shape[1:-2])
+    ks, ds = _tuple(kernel_size, ndim), _tuple(dilation, ndim)
+    for a in range(3):
+        p.extent[a] = ext[a] if a < ndim else 0
+        p.kernel[a] = ks[a] if a < ndim else 0
+        p.dilation[a] = ds[a] if a < ndim else 0
+    p.scale = float(shape[-1] ** -0.5 if scale is None else scale)
+    return p
+
+
+def check_problem(p: NaProblem) -> int:
+    return int(load().na_check_problem(ctypes.byref(p)))
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor):
+    for t in ts:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and out, dout) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (token-major layout)")
+    if ref.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+
+
+def na_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kernel_size, dilation=1,
+           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused NA forward. Returns (out, lse); lse is fp32 [B,(T,)H,W,heads]."""
+    _check_tensors(q, k, v)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check(load().na_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                         _stream_handle(q.device)))
+    return out, lse
+
+
+def bwd_workspace_bytes(p: NaProblem, variant: int) -> int:
+    return int(load().na_bwd_workspace_bytes(ctypes.byref(p), variant))
+
+
+def na_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+           dout: torch.Tensor, lse: torch.Tensor, kernel_size, dilation=1,
+           scale: Optional[float] = None, variant: str = "gather",
+           workspace: Optional[torch.Tensor] = None,
+           grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Fused NA backward of sum(out * dout). Returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, out, dout)
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:-1] or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor of shape q.shape[:-1]")
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    vid = VARIANTS[variant]
+    need = bwd_workspace_bytes(p, vid)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check(load().na_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                         _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), vid,
+                         _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def na_bwd_dq(q, k, v, out, dout, lse, kernel_size, dilation=1, scale=None, dq=None, delta=None):
+    """Query half of the gather backward: returns (dq, delta)."""
+    _check_tensors(q, k, v, out, dout)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if delta is None:
+        delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check(load().na_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                            _ptr(lse), _ptr(dq), _ptr(delta), _stream_handle(q.device)))
+    return dq, delta
+
+
+def na_bwd_dkdv(q, k, v, dout, lse, delta, kernel_size, dilation=1, scale=None, dk=None, dv=None):
+    """Key half of the gather backward: returns (dk, dv)."""
+    _check_tensors(q, k, v, dout)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _check(load().na_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                              _ptr(delta), _ptr(dk), _ptr(dv), _stream_handle(q.device)))
+    return dk, dv
+
+
+def window_start(extent: int, kernel: int, dilation: int, x: int) -> int:
+    return int(load().na_window_start(extent, kernel, dilation, x))
+
+
+def inverse_window(extent: int, kernel: int, dilation: int, y: int) -> Tuple[int, int]:
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().na_inverse_window(extent, kernel, dilation, y, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+class NeighborhoodAttention(torch.autograd.Function):
+    """Autograd wrapper: forward = na_fwd, backward = na_bwd (gather variant)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, kernel_size, dilation, scale):
+        out, lse = na_fwd(q.contiguous(), k.contiguous(), v.contiguous(), kernel_size, dilation,
+                          scale)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.cfg = (kernel_size, dilation, scale)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = na_bwd(q, k, v, out, dout.contiguous(), lse, *ctx.cfg)
+        return dq, dk, dv, None, None, None
+
+
+def neighborhood_attention(q, k, v, kernel_size, dilation=1, scale=None):
+    """Differentiable fused NA on token-major [B, (T,) H, W, heads, head_dim] tensors."""
+    return NeighborhoodAttention.apply(q, k, v, kernel_size, dilation, scale)

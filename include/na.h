@@ -1,0 +1,141 @@
+/*
+ * na.h -- C ABI of libna: fused neighborhood attention (NA) forward and
+ * backward over 2D and 3D token grids, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one discussed in NATTEN issue #161, "Backward pass is
+ * very slow towards much tokens and large kernels" (SHI-Labs/NATTEN): its
+ * benchmark script calls na2d / na3d(query, key, value, kernel_size) on
+ * token-major tensors [B, (T,) H, W, heads, head_dim] and drives the backward
+ * with loss = output.sum(); the unfused variant in the same script spells the
+ * computation out as window scores (na*_qk), a softmax over the window, and a
+ * weighted sum of values (na*_av); the maintainer's profiler tables split the
+ * backward into ComputeDelta (delta = rowsum(dO * O)) and the gradients of Q,
+ * K, V and of the attention weights.
+ *
+ * Definition implemented here. Along each axis of extent L with kernel k and
+ * dilation d, a query at coordinate x sees only coordinates of its own
+ * residue class x mod d. Inside that class (n positions, index i = x / d) its
+ * window starts at clamp(i - floor(k/2), 0, n - k) and holds k positions, so
+ * it is centered where it fits and shifted inward at the borders, and always
+ * has exactly k keys. The neighborhood N(x) is the product of the per-axis
+ * windows (prod(k) keys). With s_xy = scale * <q_x, k_y>:
+ *   lse_x = log sum_{y in N(x)} exp(s_xy)          (natural log)
+ *   out_x = sum_{y in N(x)} exp(s_xy - lse_x) v_y
+ * and the backward of sum(out * dout) gives
+ *   delta_x = <dout_x, out_x>,  dS_xy = P_xy (<dout_x, v_y> - delta_x),
+ *   dq_x = scale sum_{y in N(x)} dS_xy k_y,
+ *   dk_y = scale sum_{x: y in N(x)} dS_xy q_x,  dv_y = sum_{x: y in N(x)} P_xy dout_x.
+ *
+ * Layout. q, k, v, out, dout, dq, dk, dv are dense, contiguous, token-major
+ * arrays [B, (T,) H, W, heads, head_dim] of the problem's dtype; lse is a
+ * dense fp32 array [B, (T,) H, W, heads]. Device pointers must be 16-byte
+ * aligned. Every buffer is allocated and owned by the caller; the library
+ * never allocates, frees or synchronizes. Work is enqueued on the given HIP
+ * stream (a hipStream_t; NULL means the default stream) and completes
+ * asynchronously. Outputs are overwritten, never accumulated into.
+ *
+ * Errors. Argument errors are detected on the host before anything is
+ * enqueued and return NA_ERR_INVALID_ARG (or NA_ERR_UNSUPPORTED for a valid
+ * problem this build has no kernel for, NA_ERR_WORKSPACE for a workspace that
+ * is too small). A failed kernel launch returns NA_ERR_HIP. The library keeps
+ * no global state; calls on different streams may run concurrently.
+ */
+#ifndef NA_H
+#define NA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NA_OK = 0,
+    NA_ERR_INVALID_ARG = 1,  /* malformed problem, null or misaligned pointer */
+    NA_ERR_UNSUPPORTED = 2,  /* well-formed, but no kernel for it (head_dim, dtype) */
+    NA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than na_bwd_workspace_bytes */
+    NA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} na_status;
+
+typedef enum {
+    NA_F32 = 0,   /* fp32 tensors, fp32 arithmetic */
+    NA_BF16 = 1   /* bf16 tensors (round-to-nearest-even on output), fp32 arithmetic */
+} na_dtype;
+
+/* Backward strategies (the NATTEN issue's use_kv_parallelism_in_fused_na
+ * switch selects between query-parallel and KV-parallel fused backwards). */
+typedef enum {
+    NA_BWD_GATHER = 0,     /* dq by query tiles, then dk/dv by key tiles over the
+                              inverse neighborhood; no atomics, deterministic */
+    NA_BWD_KVPARALLEL = 1  /* one pass over key tiles producing dk, dv and fp32
+                              partial sums of dq in the workspace; dq is then
+                              finalized; uses atomics, not bitwise deterministic */
+} na_bwd_variant;
+
+typedef struct {
+    int64_t ndim;         /* 2 or 3 */
+    int64_t dtype;        /* na_dtype */
+    int64_t batch;        /* B >= 1 */
+    int64_t heads;        /* >= 1 */
+    int64_t head_dim;     /* 16, 32 or 64 in this build */
+    int64_t extent[3];    /* grid extents, outermost first: (T, H, W) for 3D, (H, W, -) for 2D */
+    int64_t kernel[3];    /* window size per axis, same order; 1 <= k <= floor(extent / dilation) */
+    int64_t dilation[3];  /* >= 1 per axis, same order */
+    double scale;         /* finite score multiplier; the usual choice is head_dim^-0.5 */
+} na_problem;
+
+/* Host-only validation of a problem description; enqueues nothing.
+ * Returns NA_OK, NA_ERR_INVALID_ARG or NA_ERR_UNSUPPORTED. */
+na_status na_check_problem(const na_problem *p);
+
+/* Forward: out (problem dtype) and lse (fp32, natural log) from q, k, v. */
+na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *v, void *out,
+                 float *lse, void *hip_stream);
+
+/* Bytes of device workspace na_bwd needs for the given variant (0 on an
+ * invalid problem or variant). NA_BWD_GATHER: the fp32 delta array
+ * [B,(T,)H,W,heads]. NA_BWD_KVPARALLEL: delta plus an fp32 dq accumulator
+ * [B,(T,)H,W,heads,head_dim]. Each region starts 256-byte aligned. */
+size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant);
+
+/* Backward of sum(out * dout): dq, dk, dv (problem dtype) from q, k, v, the
+ * forward's out and lse, and dout. workspace must be a device buffer of at
+ * least na_bwd_workspace_bytes(p, variant) bytes, 256-byte aligned; its
+ * contents on entry do not matter and are left undefined. */
+na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *v,
+                 const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                 void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                 void *hip_stream);
+
+/* The two halves of the NA_BWD_GATHER backward, for callers that want one of
+ * the gradients alone or time the kernels separately. na_bwd with
+ * NA_BWD_GATHER is exactly na_bwd_dq followed by na_bwd_dkdv on one stream.
+ * na_bwd_dq writes dq and the fp32 row array delta[B,(T,)H,W,heads] =
+ * <dout, out> (NATTEN's ComputeDelta); na_bwd_dkdv reads that delta and writes
+ * dk and dv. Same layout, alignment and error rules as na_bwd. */
+na_status na_bwd_dq(const na_problem *p, const void *q, const void *k, const void *v,
+                    const void *out, const void *dout, const float *lse, void *dq, float *delta,
+                    void *hip_stream);
+na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const void *v,
+                      const void *dout, const float *lse, const float *delta, void *dk, void *dv,
+                      void *hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char *na_status_string(na_status s);
+
+/* Host helpers exposing the window rule on one axis (absolute coordinates).
+ * na_window_start returns the first key coordinate of the window of query
+ * coordinate x (keys are start + d*j, j < k), or -1 on invalid arguments.
+ * na_inverse_window writes the first and last query coordinate (same residue
+ * class, step d) whose window contains key coordinate y; every class member
+ * between them attends y. Returns NA_ERR_INVALID_ARG on invalid arguments. */
+int64_t na_window_start(int64_t extent, int64_t kernel, int64_t dilation, int64_t x);
+na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, int64_t y,
+                            int64_t *first, int64_t *last);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NA_H */

@@ -1,0 +1,145 @@
+"""CPU-only checks of the C ABI (include/na.h): the library loads, exports every
+declared symbol, validates problems on the host, and its window helpers match
+brute force. No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from fwd_bwd_amd import na
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "na.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(na.lib_path()):
+        from fwd_bwd_amd import build
+        build.build()
+    return na.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(na_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_matches_binding_list():
+    assert declared_functions() == sorted(na.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", na.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.na_status_string(s).decode().startswith("NA_")
+
+
+def _p(shape=(1, 16, 16, 2, 16), dtype=None, kernel=(3, 3), dil=1, scale=None):
+    import torch
+    return na.make_problem(shape, dtype or torch.float32, kernel, dil, scale)
+
+
+def test_check_problem_accepts_workloads():
+    from fwd_bwd_amd.inputs import WORKLOADS
+    for w in WORKLOADS.values():
+        p = na.make_problem(w.shape, w.dtype, w.kernel, w.dilation, w.scale)
+        assert na.check_problem(p) == na.NA_OK, w.name
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda p: setattr(p, "ndim", 4), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "ndim", 1), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "dtype", 7), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "batch", 0), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "heads", 0), na.NA_ERR_INVALID_ARG),
+    (lambda p: p.kernel.__setitem__(0, 0), na.NA_ERR_INVALID_ARG),
+    (lambda p: p.kernel.__setitem__(1, 17), na.NA_ERR_INVALID_ARG),
+    (lambda p: p.dilation.__setitem__(0, 0), na.NA_ERR_INVALID_ARG),
+    (lambda p: p.dilation.__setitem__(0, 6), na.NA_ERR_INVALID_ARG),   # 16 // 6 = 2 < 3
+    (lambda p: p.extent.__setitem__(1, 0), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "scale", float("nan")), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "scale", float("inf")), na.NA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "head_dim", 24), na.NA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "head_dim", 128), na.NA_ERR_UNSUPPORTED),
+])
+def test_check_problem_rejects(mutate, expect):
+    p = _p()
+    assert na.check_problem(p) == na.NA_OK
+    mutate(p)
+    assert na.check_problem(p) == expect
+
+
+def test_dilated_kernel_limit():
+    p = _p(shape=(1, 9, 16, 1, 16), kernel=(3, 3), dil=(3, 1))   # 9 // 3 = 3: fits
+    assert na.check_problem(p) == na.NA_OK
+    p = _p(shape=(1, 8, 16, 1, 16), kernel=(3, 3), dil=(3, 1))   # class of 2 < 3
+    assert na.check_problem(p) == na.NA_ERR_INVALID_ARG
+
+
+def test_fwd_bwd_reject_null_pointers_before_launch(lib):
+    p = _p()
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 5
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert lib.na_fwd(ctypes.byref(p), *a, None) == na.NA_ERR_INVALID_ARG
+    # misaligned
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.na_fwd(ctypes.byref(p), mis, fake, fake, fake, fake, None) == na.NA_ERR_INVALID_ARG
+    ws = na.bwd_workspace_bytes(p, na.NA_BWD_GATHER)
+    bargs = [fake] * 9
+    for i in range(9):
+        a = list(bargs)
+        a[i] = None
+        assert lib.na_bwd(ctypes.byref(p), *a, fake, ws, 0, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_bwd(ctypes.byref(p), *bargs, None, ws, 0, None) == na.NA_ERR_WORKSPACE
+    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws - 1, 0, None) == na.NA_ERR_WORKSPACE
+    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws, 5, None) == na.NA_ERR_INVALID_ARG
+    bad = _p(kernel=(3, 19))
+    assert lib.na_fwd(ctypes.byref(bad), *args, None) == na.NA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes():
+    p = _p(shape=(2, 16, 16, 2, 16))
+    rows = 2 * 256 * 2
+    g = na.bwd_workspace_bytes(p, na.NA_BWD_GATHER)
+    kv = na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL)
+    assert g >= rows * 4 and g % 256 == 0
+    assert kv >= g + rows * 16 * 4 and kv % 256 == 0
+    assert na.bwd_workspace_bytes(p, 9) == 0
+
+
+def test_window_helpers_match_oracle_and_brute_force(lib):
+    for L in range(1, 21):
+        for d in range(1, 4):
+            if L // d < 1:
+                continue
+            for k in range(1, L // d + 1):
+                for x in range(L):
+                    s = na.window_start(L, k, d, x)
+                    assert s == oracle.window_start(L, k, d, x), (L, k, d, x)
+                for y in range(L):
+                    # brute force: every query whose window contains y
+                    att = [x for x in range(L) if x % d == y % d and
+                           y in range(oracle.window_start(L, k, d, x),
+                                      oracle.window_start(L, k, d, x) + d * k, d)]
+                    first, last = na.inverse_window(L, k, d, y)
+                    assert att == list(range(first, last + 1, d)), (L, k, d, y)
+    assert na.window_start(5, 6, 1, 0) == -1
+    with pytest.raises(na.NaError):
+        na.inverse_window(5, 6, 1, 0)

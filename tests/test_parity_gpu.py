@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs.
+
+Bar (per output tensor Y in {out, lse, dq, dk, dv}):
+    max |Y_gpu - Y_oracle| / max |Y_oracle| <= 1e-4 for fp32, 2e-2 for bf16.
+Small cases are compared element by element on every output; the full-size
+workloads are compared on sampled (b, token, head) units that include the grid
+corners and borders.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fwd_bwd_amd import na
+from fwd_bwd_amd.inputs import WORKLOADS, make_inputs, make_random
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    na.load()   # raises if the HIP library is not built: there is no fallback
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    return err / scale if scale > 0 else err
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def gpu_run(q, k, v, dout, kernel, dil, scale, variant="gather"):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
+    out, lse = na.na_fwd(qd, kd, vd, kernel, dil, scale)
+    dq, dk, dv = na.na_bwd(qd, kd, vd, out, dd, lse, kernel, dil, scale, variant=variant)
+    torch.cuda.synchronize()
+    return {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def oracle_full(q, k, v, dout, kernel, dil, scale):
+    args = [np64(t) for t in (q, k, v)]
+    out, lse = oracle.na_fwd(*args, kernel, dil, scale)
+    dq, dk, dv = oracle.na_bwd(*args, np64(dout), kernel, dil, scale)
+    return {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def compare(got, ref, dtype, label):
+    tol = TOL[dtype]
+    errs = {}
+    for name in ref:
+        errs[name] = rel_err(np64(got[name]), ref[name])
+    say(label, {k: f"{v:.2e}" for k, v in errs.items()})
+    for name, e in errs.items():
+        assert e <= tol, (label, name, e)
+    return errs
+
+
+# ----------------------------------------------------------------------------- small cases
+# shapes span several wave tiles (8x8 per wave) with ragged tails, both dtypes,
+# all head dims, dilation, batch > 1, k = 1, kernel = grid, windows of even size.
+SMALL = [
+    # (shape [B,(T,)H,W,h,D], kernel, dilation, dtype)
+    ((1, 16, 16, 2, 16), (3, 3), 1, torch.float32),
+    ((1, 19, 23, 2, 32), (5, 7), 1, torch.float32),
+    ((2, 13, 17, 3, 16), (3, 3), (2, 3), torch.float32),
+    ((1, 20, 20, 1, 64), (9, 9), 1, torch.float32),
+    ((1, 7, 9, 2, 32), (7, 9), 1, torch.float32),        # kernel = grid: dense attention
+    ((1, 11, 10, 2, 32), (1, 1), 1, torch.float32),      # k = 1
+    ((1, 12, 11, 1, 16), (4, 2), 1, torch.float32),      # even kernels
+    ((1, 3, 5, 1, 16), (3, 5), 1, torch.float32),        # grid smaller than a wave tile
+    ((1, 5, 11, 13, 2, 32), (3, 5, 5), 1, torch.float32),
+    ((1, 6, 9, 10, 2, 16), (3, 3, 3), (2, 1, 2), torch.float32),
+    ((2, 4, 9, 8, 1, 64), (3, 3, 3), 1, torch.float32),
+    ((1, 19, 23, 2, 32), (5, 7), 1, torch.bfloat16),
+    ((1, 6, 10, 9, 2, 32), (5, 7, 7), 1, torch.bfloat16),
+    ((2, 26, 27, 2, 64), (5, 5), 2, torch.bfloat16),
+]
+
+
+def _id(c):
+    shape, k, d, dt = c
+    return f"{'x'.join(map(str, shape))}-k{'x'.join(map(str, k))}-d{d}-{str(dt)[6:]}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+@pytest.mark.parametrize("variant", ["gather", "kvparallel"])
+def test_small_cases_match_oracle(case, variant):
+    shape, kernel, dil, dtype = case
+    say("case", _id(case), variant)
+    q, k, v, dout = make_random(shape, dtype, seed=zlib.crc32(_id(case).encode()) % 1000)
+    scale = shape[-1] ** -0.5
+    got = gpu_run(q, k, v, dout, kernel, dil, scale, variant)
+    ref = oracle_full(q, k, v, dout, kernel, dil, scale)
+    compare(got, ref, dtype, f"{_id(case)} {variant}")
+
+
+def test_first_workload_full_and_dout_ones():
+    """The 16x16 fp32 workload, every output, dout = ones as in the issue's script."""
+    w = WORKLOADS["2d_16x16_k3_h2_d16_f32"]
+    q, k, v, dout = make_inputs(w, seed=0)
+    for variant in ("gather", "kvparallel"):
+        got = gpu_run(q, k, v, dout, w.kernel, w.dilation, w.the_scale, variant)
+        ref = oracle_full(q, k, v, dout, w.kernel, w.dilation, w.the_scale)
+        compare(got, ref, w.dtype, f"{w.name} {variant}")
+
+
+def test_gather_backward_is_deterministic():
+    shape, kernel = (1, 2, 21, 19, 2, 32), (3, 5, 5)
+    q, k, v, dout = (t.cuda() for t in make_random(shape, torch.float32, seed=11))
+    out, lse = na.na_fwd(q, k, v, kernel)
+    a = na.na_bwd(q, k, v, out, dout, lse, kernel)
+    b = na.na_bwd(q, k, v, out, dout, lse, kernel)
+    out2, lse2 = na.na_fwd(q, k, v, kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_split_entry_points_equal_na_bwd():
+    shape, kernel = (1, 17, 18, 2, 32), (5, 5)
+    q, k, v, dout = (t.cuda() for t in make_random(shape, torch.float32, seed=12))
+    out, lse = na.na_fwd(q, k, v, kernel)
+    dq, dk, dv = na.na_bwd(q, k, v, out, dout, lse, kernel)
+    dq2, delta = na.na_bwd_dq(q, k, v, out, dout, lse, kernel)
+    dk2, dv2 = na.na_bwd_dkdv(q, k, v, dout, lse, delta, kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    ref_delta = (dout.double() * out.double()).sum(-1)
+    assert torch.allclose(delta.double(), ref_delta, rtol=1e-5, atol=1e-5)
+
+
+def test_kvparallel_matches_gather():
+    shape, kernel, dil = (2, 14, 15, 2, 32), (5, 7), (1, 2)
+    q, k, v, dout = (t.cuda() for t in make_random(shape, torch.float32, seed=13))
+    out, lse = na.na_fwd(q, k, v, kernel, dil)
+    a = na.na_bwd(q, k, v, out, dout, lse, kernel, dil, variant="gather")
+    b = na.na_bwd(q, k, v, out, dout, lse, kernel, dil, variant="kvparallel")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert rel_err(np64(x), np64(y)) < 1e-5
+
+
+def test_autograd_wrapper():
+    shape, kernel = (1, 10, 12, 2, 16), (3, 5)
+    q, k, v, dout = make_random(shape, torch.float32, seed=14)
+    qd, kd, vd = (t.cuda().requires_grad_() for t in (q, k, v))
+    o = na.neighborhood_attention(qd, kd, vd, kernel)
+    o.backward(dout.cuda())
+    ref = oracle_full(q, k, v, dout, kernel, 1, shape[-1] ** -0.5)
+    got = {"out": o, "dq": qd.grad, "dk": kd.grad, "dv": vd.grad}
+    compare(got, {n: ref[n] for n in got}, torch.float32, "autograd")
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def sample_units(w, n_random=96, seed=0):
+    """Flat (b, token, head) ids: every grid corner and edge midpoint, plus random ones."""
+    rng = np.random.default_rng(seed)
+    grid = w.grid
+    pts = set()
+    import itertools
+    for corner in itertools.product(*[(0, 1, g // 2, g - 2, g - 1) for g in grid]):
+        pts.add(tuple(corner))
+    pts = sorted(pts)
+    ids = []
+    ntok = int(np.prod(grid))
+    for i, p in enumerate(pts):
+        tok = int(np.ravel_multi_index(p, grid))
+        b = i % w.batch
+        h = (i * 7) % w.heads
+        ids.append((b * ntok + tok) * w.heads + h)
+    total = w.batch * ntok * w.heads
+    ids.extend(rng.integers(0, total, n_random).tolist())
+    return np.array(sorted(set(ids)), np.int64)
+
+
+FULL = ["2d_1024x1024_k9_h8_d32_f32", "3d_16x256x256_k3x5x5_h8_d32_f32",
+        "3d_b2_8x128x128_k5x7x7_h8_d32_bf16", "2d_b4_512x512_k13_d2_h4_d64_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled(name):
+    w = WORKLOADS[name]
+    say("full workload", name)
+    q, k, v, dout = make_inputs(w, seed=0)
+    got = gpu_run(q, k, v, dout, w.kernel, w.dilation, w.the_scale)
+    sel = sample_units(w)
+    D = w.head_dim
+    args = [np64(t) for t in (q, k, v)]
+    o_ref, l_ref = oracle.na_fwd(*args, w.kernel, w.dilation, w.the_scale, sel=sel)
+    dq_ref, dk_ref, dv_ref = oracle.na_bwd(*args, np64(dout), w.kernel, w.dilation, w.the_scale,
+                                           sel=sel)
+    pick = lambda t: np64(t).reshape(-1, D)[sel]  # noqa: E731
+    got_s = {"out": pick(got["out"]), "lse": np64(got["lse"]).reshape(-1)[sel],
+             "dq": pick(got["dq"]), "dk": pick(got["dk"]), "dv": pick(got["dv"])}
+    ref_s = {"out": o_ref, "lse": l_ref, "dq": dq_ref, "dk": dk_ref, "dv": dv_ref}
+    compare(got_s, ref_s, w.dtype, f"{name} sampled({sel.size})")
+    # properties that hold at any size, checked on the whole tensors
+    axes = tuple(range(1, 1 + w.ndim))
+    dv_sum = got["dv"].double().sum(axes)
+    do_sum = torch.as_tensor(dout).double().sum(axes).to(dv_sum.device)
+    assert rel_err(dv_sum.cpu().numpy(), do_sum.cpu().numpy()) < TOL[w.dtype]
+    assert torch.isfinite(got["dq"]).all() and torch.isfinite(got["dk"]).all()
