@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # hardware float atomics for the KV-parallel dq accumulator
     "-munsafe-fp-atomics",
+    # MFMA results in ordinary VGPRs: the accumulators are also touched by VALU
+    # code (softmax rescale), and AGPR residency costs a copy per use
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

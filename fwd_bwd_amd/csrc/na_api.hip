@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
 #include <initializer_list>
 
@@ -14,7 +15,7 @@ namespace {
 
 using na::bf16;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // elementwise kernels
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -69,31 +70,74 @@ na_status validate(const na_problem *p, Prob *out) {
     return NA_OK;
 }
 
-// Wave tiling of the class grids; false when the wave count overflows int32.
-bool geometry(const Prob &q, na::Geometry *g) {
-    int64_t n_waves = q.batch * q.heads;
+// Largest box, per axis, that any tile stages: the keys its queries' walks
+// read (forward, dq) or the queries its keys' walks read (dk/dv), over all
+// tiles and residue classes (the same plan the kernels compute per tile).
+// Also returns the longest walk (points along one axis a patch walks); the
+// kernels keep per-axis validity masks of that many bits.
+int max_union(const Prob &q, bool inverse, int (&mx)[3]) {
+    int walk = 1;
+    for (int a = 0; a < 3; ++a) {
+        mx[a] = 1;
+        const int k = q.ker[a], d = q.dil[a], tile = na::kTile[a], p = na::kPatch[a];
+        for (int r = 0; r < d && r < q.ext[a]; ++r) {
+            const int n = na::class_size(q.ext[a], d, r);
+            for (int f = 0; f < n; f += tile) {
+                int start, extent;
+                if (inverse) {
+                    const int cnt = na::tile_inverse_walk(f, tile, p, n, k);
+                    na::query_box(f, tile, p, n, k, cnt, &start, &extent);
+                    walk = std::max(walk, cnt * p);
+                } else {
+                    na::key_box(f, tile, p, n, k, &start, &extent);
+                    walk = std::max(walk, na::window_walk(k, p) * p);
+                }
+                mx[a] = std::max(mx[a], extent);
+            }
+        }
+    }
+    return walk;
+}
+
+// Target LDS bytes for one workgroup's staged chunk: two workgroups per CU.
+constexpr int kLdsTarget = 78 * 1024;
+constexpr int kLdsMax = 160 * 1024;
+
+// Tiling of the class grids and the LDS plan of one kernel kind; false when
+// the problem does not fit (wave count overflow or LDS).
+bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
+              na::Geometry *g, int *lds_bytes) {
+    int64_t n_tiles = q.batch * q.heads;
     int nres = 1;
     for (int a = 0; a < 3; ++a) {
         g->ext[a] = q.ext[a];
         g->ker[a] = q.ker[a];
         g->dil[a] = q.dil[a];
         const int nmax = na::class_size(q.ext[a], q.dil[a], 0);
-        g->tiles[a] = (nmax + na::kWaveTile[a] - 1) / na::kWaveTile[a];
-        n_waves *= g->tiles[a];
+        g->tiles[a] = (nmax + na::kTile[a] - 1) / na::kTile[a];
+        n_tiles *= g->tiles[a];
         nres *= q.dil[a];
     }
-    n_waves *= nres;
-    if (n_waves > INT32_MAX - 64) return false;
+    n_tiles *= nres;
+    if (n_tiles > INT32_MAX) return false;
     g->heads = (int)q.heads;
     g->batch = (int)q.batch;
     g->head_dim = (int)q.head_dim;
     g->nres = nres;
-    g->n_waves = (int)n_waves;
+    g->n_tiles = (int)n_tiles;
+    // chunks of a staged box are cut along the outermost axis that has extent
+    g->chunk_axis = q.ext[0] > 1 ? 0 : 1;
+    int mx[3];
+    if (max_union(q, inverse, mx) > 32) return false;  // 32-bit validity masks
+    const int64_t full = (int64_t)mx[0] * mx[1] * mx[2] * bytes_per_point;
+    const int64_t plane = full / mx[g->chunk_axis];
+    int64_t lds = std::min<int64_t>(full, kLdsTarget);
+    lds = std::max<int64_t>(lds, plane);
+    lds = std::max<int64_t>(lds, merge_bytes);
+    if (lds > kLdsMax) return false;
+    g->lds_budget = (int)lds;
+    *lds_bytes = (int)lds;
     return true;
-}
-
-dim3 wave_grid(const na::Geometry &g) {
-    return dim3((unsigned)((g.n_waves + na::kWavesPerBlock - 1) / na::kWavesPerBlock));
 }
 
 dim3 flat_grid(int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); }
@@ -101,8 +145,16 @@ dim3 flat_grid(int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads
 na_status launched() { return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP; }
 
 template <typename T, int D>
-na_status run_fwd(const na::FwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((na::fwd_kernel<T, D>), wave_grid(a.g), dim3(kThreads), 0, s, a);
+na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
+    constexpr int PB = D * (int)sizeof(T);
+    int lds;
+    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 2) * 4, &a.g, &lds))
+        return NA_ERR_UNSUPPORTED;
+    auto kern = na::fwd_kernel<T, D>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+        hipSuccess)
+        return NA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(a.g.n_tiles), dim3(na::kThreads), lds, s, a);
     return launched();
 }
 
@@ -110,27 +162,43 @@ na_status run_fwd(const na::FwdArgs &a, hipStream_t s) {
 enum Phase { kPhaseDq = 1, kPhaseDkdv = 2, kPhaseBoth = 3 };
 
 template <typename T, int D>
-na_status run_bwd(const na::BwdArgs &a, const Prob &q, int32_t variant, int phases, hipStream_t s) {
+na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hipStream_t s) {
+    constexpr int PB = D * (int)sizeof(T);
+    na::BwdArgs aq = a, ak = a;
+    int lds_q = 0, lds_k = 0;
+    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * D * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
+    if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * D * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
     if (variant == NA_BWD_GATHER) {
         if (phases & kPhaseDq) {
-            hipLaunchKernelGGL((na::dq_kernel<T, D>), wave_grid(a.g), dim3(kThreads), 0, s, a);
+            auto kern = na::dq_kernel<T, D>;
+            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds_q) != hipSuccess)
+                return NA_ERR_HIP;
+            hipLaunchKernelGGL(kern, dim3(aq.g.n_tiles), dim3(na::kThreads), lds_q, s, aq);
             if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
         }
         if (phases & kPhaseDkdv) {
-            hipLaunchKernelGGL((na::dkdv_kernel<T, D, false>), wave_grid(a.g), dim3(kThreads), 0,
-                               s, a);
+            auto kern = na::dkdv_kernel<T, D, false>;
+            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds_k) != hipSuccess)
+                return NA_ERR_HIP;
+            hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
             if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
         }
         return NA_OK;
     }
-    const int64_t n4 = q.rows * D / 4;
-    hipLaunchKernelGGL((na::delta_kernel<T, D>), flat_grid(q.rows), dim3(kThreads), 0, s,
+    const int64_t n4 = pr.rows * D / 4;
+    hipLaunchKernelGGL((na::delta_kernel<T, D>), flat_grid(pr.rows), dim3(kThreads), 0, s,
                        static_cast<const T *>(a.out), static_cast<const T *>(a.dout), a.delta,
-                       q.rows);
+                       pr.rows);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
     hipLaunchKernelGGL(na::zero_kernel, flat_grid(n4), dim3(kThreads), 0, s, a.dq_acc, n4);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
-    hipLaunchKernelGGL((na::dkdv_kernel<T, D, true>), wave_grid(a.g), dim3(kThreads), 0, s, a);
+    auto kern = na::dkdv_kernel<T, D, true>;
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lds_k) != hipSuccess)
+        return NA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
     hipLaunchKernelGGL((na::dq_finalize_kernel<T>), flat_grid(n4), dim3(kThreads), 0, s,
                        a.dq_acc, static_cast<T *>(a.dq), a.scale, n4);
@@ -188,7 +256,6 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
         return NA_ERR_INVALID_ARG;
     na::FwdArgs a{};
-    if (!geometry(pr, &a.g)) return NA_ERR_INVALID_ARG;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -198,9 +265,9 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const bool f32 = pr.dtype == NA_F32;
     switch (pr.head_dim) {
-        case 16: return f32 ? run_fwd<float, 16>(a, s) : run_fwd<bf16, 16>(a, s);
-        case 32: return f32 ? run_fwd<float, 32>(a, s) : run_fwd<bf16, 32>(a, s);
-        case 64: return f32 ? run_fwd<float, 64>(a, s) : run_fwd<bf16, 64>(a, s);
+        case 16: return f32 ? run_fwd<float, 16>(pr, a, s) : run_fwd<bf16, 16>(pr, a, s);
+        case 32: return f32 ? run_fwd<float, 32>(pr, a, s) : run_fwd<bf16, 32>(pr, a, s);
+        case 64: return f32 ? run_fwd<float, 64>(pr, a, s) : run_fwd<bf16, 64>(pr, a, s);
     }
     return NA_ERR_UNSUPPORTED;
 }
@@ -225,7 +292,6 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
     na::BwdArgs a{};
-    if (!geometry(pr, &a.g)) return NA_ERR_INVALID_ARG;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -243,14 +309,14 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     const bool f32 = pr.dtype == NA_F32;
     switch (pr.head_dim) {
         case 16:
-            return f32 ? run_bwd<float, 16>(a, pr, variant, phases, s)
-                       : run_bwd<bf16, 16>(a, pr, variant, phases, s);
+            return f32 ? run_bwd<float, 16>(pr, a, variant, phases, s)
+                       : run_bwd<bf16, 16>(pr, a, variant, phases, s);
         case 32:
-            return f32 ? run_bwd<float, 32>(a, pr, variant, phases, s)
-                       : run_bwd<bf16, 32>(a, pr, variant, phases, s);
+            return f32 ? run_bwd<float, 32>(pr, a, variant, phases, s)
+                       : run_bwd<bf16, 32>(pr, a, variant, phases, s);
         case 64:
-            return f32 ? run_bwd<float, 64>(a, pr, variant, phases, s)
-                       : run_bwd<bf16, 64>(a, pr, variant, phases, s);
+            return f32 ? run_bwd<float, 64>(pr, a, variant, phases, s)
+                       : run_bwd<bf16, 64>(pr, a, variant, phases, s);
     }
     return NA_ERR_UNSUPPORTED;
 }

@@ -1,5 +1,5 @@
-// na_common.hpp -- types, element I/O and per-wave geometry shared by the
-// neighborhood-attention kernels (gfx950, wave64).
+// na_common.hpp -- types, element I/O, tile geometry and LDS staging shared by
+// the neighborhood-attention kernels (gfx950, wave64).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,17 +11,17 @@ namespace na {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16;  // storage of a bfloat16 value
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ----------------------------------------------------------------------------
-// Element I/O. Tensors are fp32 or bf16; arithmetic is always fp32. A "chunk"
-// is 4 consecutive elements (16 bytes of fp32, 8 bytes of bf16).
+// Element I/O. Tensors are fp32 or bf16; arithmetic is always fp32.
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round to nearest, ties to even (inputs are finite).
+// Round to nearest, ties to even (values are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7fffu + ((u >> 16) & 1u);
@@ -33,6 +33,7 @@ struct Io;
 
 template <>
 struct Io<float> {
+    static constexpr int kPerChunk = 4;  // elements per 16-byte chunk
     __device__ __forceinline__ static void load4(const float *p, float *d) {
         float4 v = *reinterpret_cast<const float4 *>(p);
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
@@ -40,10 +41,18 @@ struct Io<float> {
     __device__ __forceinline__ static void store4(float *p, const float *s) {
         *reinterpret_cast<float4 *>(p) = make_float4(s[0], s[1], s[2], s[3]);
     }
+    // a 16-byte LDS chunk to fp32
+    __device__ __forceinline__ static void chunk(const char *lds, float *d) {
+        float4 v = *reinterpret_cast<const float4 *>(lds);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    // 4 elements (half chunk never needed for fp32)
+    __device__ __forceinline__ static void quad(const char *lds, float *d) { chunk(lds, d); }
 };
 
 template <>
 struct Io<bf16> {
+    static constexpr int kPerChunk = 8;
     __device__ __forceinline__ static void load4(const bf16 *p, float *d) {
         uint2 v = *reinterpret_cast<const uint2 *>(p);
         d[0] = bf16_to_f32(v.x & 0xffffu); d[1] = bf16_to_f32(v.x >> 16);
@@ -54,6 +63,20 @@ struct Io<bf16> {
         v.x = f32_to_bf16(s[0]) | (f32_to_bf16(s[1]) << 16);
         v.y = f32_to_bf16(s[2]) | (f32_to_bf16(s[3]) << 16);
         *reinterpret_cast<uint2 *>(p) = v;
+    }
+    __device__ __forceinline__ static void chunk(const char *lds, float *d) {
+        uint4 v = *reinterpret_cast<const uint4 *>(lds);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+            d[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+    __device__ __forceinline__ static void quad(const char *lds, float *d) {
+        uint2 v = *reinterpret_cast<const uint2 *>(lds);
+        d[0] = bf16_to_f32(v.x & 0xffffu); d[1] = bf16_to_f32(v.x >> 16);
+        d[2] = bf16_to_f32(v.y & 0xffffu); d[3] = bf16_to_f32(v.y >> 16);
     }
 };
 
@@ -70,34 +93,41 @@ __device__ __forceinline__ void load_row(const T *p, float (&d)[N]) {
 //   A_b[c] = a (lane 4b+c),  B_b[c] = b (lane 4b+c),
 //   D_b[i][c] = C_b[i][c] + A_b[i] * B_b[c], row i in result register i of
 //   lane 4b+c.
-// So with A = a key-indexed operand and B = a query-indexed one, lane 4b+c
-// ends up holding the products of its own query c with the 4 keys of its
-// block, one per register.
+// With A a key-indexed operand and B a query-indexed one, lane 4b+c ends up
+// holding the products of its own query c with the 4 keys of its block, one
+// per register.
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-// ----------------------------------------------------------------------------
-// Problem geometry, as the host hands it to every kernel. Axis 0 is T (1 for
-// 2D problems), axis 1 is H, axis 2 is W.
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
-// One wave covers a tile of 1 x 8 x 8 class coordinates, split into 16
-// patches of 1 x 2 x 2 (one patch per 4-lane MFMA block).
+// ----------------------------------------------------------------------------
+// Tiles. Axis 0 is T (1 for 2D problems), axis 1 is H, axis 2 is W, all in
+// class coordinates of one residue class (dilation). A workgroup of kWaves
+// waves owns a tile of 1 x 8 x 8 points (64: one per lane), split into sixteen
+// 1 x 2 x 2 patches, one per 4-lane MFMA block; all waves of the workgroup
+// hold the same 64 points and split the other side's patches between them.
+
 constexpr int kPatch[3] = {1, 2, 2};
-constexpr int kWaveTile[3] = {1, 8, 8};
-constexpr int kWavesPerBlock = 4;
+constexpr int kTile[3] = {1, 8, 8};
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 
 struct Geometry {
     int ext[3], ker[3], dil[3];
     int heads, batch, head_dim;
-    int tiles[3];     // wave tiles per axis, over the largest residue class
+    int tiles[3];     // tiles per axis, over the largest residue class
     int nres;         // dil[0] * dil[1] * dil[2]
-    int n_waves;      // batch * heads * nres * tiles[0] * tiles[1] * tiles[2]
+    int n_tiles;      // batch * heads * nres * tiles[0] * tiles[1] * tiles[2]
+    int chunk_axis;   // axis along which a staged box is split when it exceeds the budget
+    int lds_budget;   // bytes of LDS a staged chunk may use
 };
 
-// Where one wave works: batch element, head, residue class, tile origin, and
-// the address arithmetic of that class.
-struct WaveCtx {
+// Where a workgroup works: batch element, head, residue class, tile origin,
+// and the address arithmetic of that class.
+struct TileCtx {
     int n[3], k[3];     // class sizes and window sizes per axis
     int o[3];           // tile origin in class coordinates
     int64_t base;       // element offset of (b, class origin token, head, 0)
@@ -106,10 +136,20 @@ struct WaveCtx {
     int64_t lst[3];     // lse / delta offset of one class step per axis
 };
 
-// Decodes the wave id (tile fastest, then residue, head, batch). Returns false
-// when the tile lies past the end of this residue class (the whole wave exits).
-__device__ __forceinline__ bool decode_wave(const Geometry &g, int wave, WaveCtx &w) {
-    int rem = wave;
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2. Renumber them so that every XCD walks one contiguous run of tiles:
+// neighbouring tiles share most of their halo, which then hits in that XCD's
+// L2. The map is a bijection of [0, n).
+__device__ __forceinline__ int xcd_tile_id(int bid, int n) {
+    const int xcd = bid & 7, j = bid >> 3;
+    const int q = n >> 3, r = n & 7;
+    return xcd < r ? xcd * (q + 1) + j : r * (q + 1) + (xcd - r) * q + j;
+}
+
+// Decodes a tile id (tile fastest along W, then H, T, residue, head, batch).
+// Returns false when the tile lies past the end of its residue class.
+__device__ __forceinline__ bool decode_tile(const Geometry &g, int tile, TileCtx &w) {
+    int rem = tile;
     int tw = rem % g.tiles[2]; rem /= g.tiles[2];
     int th = rem % g.tiles[1]; rem /= g.tiles[1];
     int tt = rem % g.tiles[0]; rem /= g.tiles[0];
@@ -126,7 +166,7 @@ __device__ __forceinline__ bool decode_wave(const Geometry &g, int wave, WaveCtx
     for (int a = 0; a < 3; ++a) {
         w.n[a] = class_size(g.ext[a], g.dil[a], r[a]);
         w.k[a] = g.ker[a];
-        w.o[a] = t_idx[a] * kWaveTile[a];
+        w.o[a] = t_idx[a] * kTile[a];
         inside = inside && (w.o[a] < w.n[a]);
     }
     const int64_t HW = (int64_t)g.ext[1] * g.ext[2];
@@ -144,10 +184,10 @@ __device__ __forceinline__ bool decode_wave(const Geometry &g, int wave, WaveCtx
     return inside;
 }
 
-__device__ __forceinline__ int64_t elem_off(const WaveCtx &w, const int (&c)[3]) {
+__device__ __forceinline__ int64_t elem_off(const TileCtx &w, const int (&c)[3]) {
     return w.base + c[0] * w.st[0] + c[1] * w.st[1] + c[2] * w.st[2];
 }
-__device__ __forceinline__ int64_t row_off(const WaveCtx &w, const int (&c)[3]) {
+__device__ __forceinline__ int64_t row_off(const TileCtx &w, const int (&c)[3]) {
     return w.lbase + c[0] * w.lst[0] + c[1] * w.lst[1] + c[2] * w.lst[2];
 }
 
@@ -158,8 +198,160 @@ __device__ __forceinline__ void patch_point(const int (&f)[3], int c, int (&p)[3
     p[2] = f[2] + (c & 1);
 }
 
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
-__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+// The point a lane owns in its workgroup's tile, and its patch.
+struct LanePoint {
+    int f[3];     // first point of the lane's patch (clamped into the grid)
+    int l[3];     // last point of the lane's patch (clamped into the grid)
+    int p[3];     // the lane's own point (clamped into the grid)
+    bool active;  // the unclamped point lies inside the grid
+};
+
+__device__ __forceinline__ LanePoint lane_point(const TileCtx &w, int lane) {
+    const int grp = lane >> 2, c = lane & 3;
+    int f[3] = {w.o[0], w.o[1] + 2 * (grp >> 2), w.o[2] + 2 * (grp & 3)};
+    int p[3];
+    patch_point(f, c, p);
+    LanePoint lp;
+    lp.active = p[0] < w.n[0] && p[1] < w.n[1] && p[2] < w.n[2];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        lp.f[a] = imin(f[a], w.n[a] - 1);
+        lp.l[a] = imin(f[a] + kPatch[a] - 1, w.n[a] - 1);
+        lp.p[a] = imin(p[a], w.n[a] - 1);
+    }
+    return lp;
+}
+
+// Tile extent clamped to the grid: first and last point per axis.
+__device__ __forceinline__ void tile_span(const TileCtx &w, int (&f)[3], int (&l)[3]) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        f[a] = w.o[a];
+        l[a] = imin(w.o[a] + kTile[a] - 1, w.n[a] - 1);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// LDS staging of a box of points. A point (one (token, head) vector of D
+// elements) takes D * sizeof(T) bytes = NC 16-byte chunks, points in row-major
+// box order. Chunk s of a point sits at slot s ^ swz(point).
+//
+// Bank model (measured on gfx950): 16-byte reads of the 16 lanes of a quarter
+// wave conflict when two of them hit the same 16-byte slot modulo 256 bytes.
+// The swizzle keeps both read patterns of the kernels conflict-free for
+// fp32 (NC = 8) and D = 64 (NC = 16):
+//  * key-major: each lane reads chunk s of its own point; a quarter wave holds
+//    four 1x2x2 patches side by side, i.e. a 2x8 block of points;
+//  * d-major: the four lanes of a block read the four quarters of one point
+//    of their patch, and the blocks of a quarter wave visit that point's
+//    patch in orders differing in the w bit (see lds_quarter).
+struct Box {
+    int o[3];   // origin (class coordinates)
+    int e[3];   // extents
+};
+
+template <int NC>
+__device__ __forceinline__ int swz(int lh, int lw) {
+    if constexpr (NC == 16) return ((lw >> 1) & 3) | ((lw & 1) << 2) | ((lh & 1) << 3);
+    if constexpr (NC == 8) {
+        const int x = lw >> 1;
+        return ((x & 3) ^ ((x >> 1) & 1)) | ((lh & 1) << 2);
+    }
+    if constexpr (NC == 4) return ((lw >> 2) & 1) | ((lh & 1) << 1);
+    return (lw >> 1) & (NC - 1);
+}
+
+template <int NC>
+__device__ __forceinline__ constexpr int log2_of() {
+    return NC == 16 ? 4 : NC == 8 ? 3 : NC == 4 ? 2 : NC == 2 ? 1 : 0;
+}
+
+// All threads of the workgroup copy the box of tensor src into lds with
+// direct global-to-LDS loads, one box row at a time (16 bytes per lane, 64
+// consecutive slots per wave instruction). Box points past the end of the
+// grid (the box may overhang it by up to one patch) repeat the last grid
+// point; they are never used unmasked. Completion: stage_wait().
+template <typename T, int D>
+__device__ __forceinline__ void stage_box(const T *src, const TileCtx &w, const Box &b,
+                                          char *lds) {
+    constexpr int PB = D * (int)sizeof(T), NC = PB / 16, LNC = log2_of<NC>();
+    constexpr int EPC = 16 / (int)sizeof(T);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int rowchunks = b.e[2] * NC;
+    const int ipr = (rowchunks + 63) >> 6;
+    const int total = b.e[0] * b.e[1] * ipr;
+    for (int u = wave; u < total; u += kWaves) {
+        const int r = u / ipr, part = u - r * ipr;
+        const int lt = r / b.e[1], lh = r - lt * b.e[1];
+        const int j = part * 64 + lane;
+        const int c0 = imin(b.o[0] + lt, w.n[0] - 1), c1 = imin(b.o[1] + lh, w.n[1] - 1);
+        const int64_t rowbase = w.base + c0 * w.st[0] + c1 * w.st[1];
+        if (j < rowchunks) {
+            const int lw = j >> LNC, slot = j & (NC - 1);
+            const int s = slot ^ swz<NC>(lh, lw);
+            const int c2 = imin(b.o[2] + lw, w.n[2] - 1);
+            const T *gp = src + rowbase + c2 * w.st[2] + s * EPC;
+#if defined(__HIP_DEVICE_COMPILE__)
+            // the host pass of single-source HIP has no gfx950 builtins
+            __builtin_amdgcn_global_load_lds(gp, (lds_void *)(lds + (r * rowchunks + part * 64) * 16),
+                                             16, 0, 0);
+#else
+            (void)gp;
+#endif
+        }
+    }
+}
+
+// Per-point (logsumexp * log2(e), delta) pairs of a box, plain loads.
+__device__ __forceinline__ void stage_rows(const float *lse, const float *delta, const TileCtx &w,
+                                           const Box &b, float2 *lds) {
+    const int np = b.e[0] * b.e[1] * b.e[2];
+    const int e12 = b.e[1] * b.e[2];
+    for (int i = threadIdx.x; i < np; i += kThreads) {
+        const int lt = i / e12, rem = i - lt * e12;
+        const int lh = rem / b.e[2], lw = rem - lh * b.e[2];
+        const int c[3] = {imin(b.o[0] + lt, w.n[0] - 1), imin(b.o[1] + lh, w.n[1] - 1),
+                          imin(b.o[2] + lw, w.n[2] - 1)};
+        const int64_t ro = row_off(w, c);
+        lds[i] = make_float2(lse[ro] * kLog2e, delta[ro]);
+    }
+}
+
+__device__ __forceinline__ void stage_wait() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// Byte offset of point (lh, lw) relative coordinates already folded into pt.
+// Full point (D elements) from LDS, chunk by chunk.
+template <typename T, int D>
+__device__ __forceinline__ void lds_point(const char *lds, int pt, int sw, float (&d)[D]) {
+    constexpr int PB = D * (int)sizeof(T), NC = PB / 16, EPC = 16 / (int)sizeof(T);
+    const char *p = lds + pt * PB;
+#pragma unroll
+    for (int s = 0; s < NC; ++s) Io<T>::chunk(p + ((s ^ sw) << 4), d + s * EPC);
+}
+
+// Elements [c*G, c*G + G) (G = D / 4) of a point from LDS.
+template <typename T, int D>
+__device__ __forceinline__ void lds_quarter(const char *lds, int pt, int sw, int c,
+                                            float (&d)[D / 4]) {
+    constexpr int PB = D * (int)sizeof(T), EPC = 16 / (int)sizeof(T);
+    constexpr int G = D / 4;
+    const char *p = lds + pt * PB;
+    if constexpr (G >= EPC) {
+#pragma unroll
+        for (int s = 0; s < G / EPC; ++s) {
+            const int chunk = c * (G / EPC) + s;
+            Io<T>::chunk(p + ((chunk ^ sw) << 4), d + s * EPC);
+        }
+    } else {
+        // G = 4 < EPC = 8 (bf16, D = 16): half a chunk
+        const int chunk = (c * G) / EPC, half = (c * G) % EPC;
+        Io<T>::quad(p + ((chunk ^ sw) << 4) + half * (int)sizeof(T), d);
+    }
+}
 
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll

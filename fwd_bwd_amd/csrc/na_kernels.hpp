@@ -1,31 +1,36 @@
 // na_kernels.hpp -- neighborhood attention forward and backward kernels for
-// gfx950 (wave64, fp32 MFMA 4x4x1).
+// gfx950 (wave64, fp32 MFMA 4x4x1, LDS-staged operands).
 //
-// Work decomposition. Every kernel runs independent waves; a wave owns a
-// 1x8x8 tile of one residue class of one (batch, head), split into sixteen
-// 1x2x2 patches, one per 4-lane MFMA block. Inside a block each lane owns one
-// point of the patch (a query in the forward and dq kernels, a key in the dk/dv
-// kernel), and the block walks the other side's points in 1x2x2 patches that
-// cover the union of what its four points need. That union is at most one
-// position longer per axis than a single window, so the contraction over a
-// patch pair wastes little: a 9x9 window is covered by 5x5 patches of 4 keys
-// (100 computed vs 81 needed scores), a 3x5x5 window by 3x3x3 patches (108 vs
-// 75). Scores outside a point's window are masked by index arithmetic on the
-// window starts, never by padding (the NATTEN maintainer names software
-// predication of these bounds as the main overhead of 2D/3D fused kernels; here
-// it costs a few integer compares per score).
+// Work decomposition. A workgroup of four waves owns a 1x8x8 tile of one
+// residue class of one (batch, head): 64 points, one per lane, in sixteen 1x2x2
+// patches (one per 4-lane MFMA block). In the forward and dq kernels the points
+// are queries, in the dk/dv kernel keys. The workgroup stages, once, the box of
+// the other side's points its tile needs (the union of the windows, or of the
+// inverse windows) in LDS, then each block walks the 1x2x2 patches covering
+// what its own four points need; the four waves split those patches between
+// them and merge their partial results through LDS at the end.
 //
-// Softmax. Scores are kept in log2 units (q is pre-multiplied by
-// scale * log2(e)) so exp2 is a single hardware instruction; each lane keeps
-// the running maximum and sum of its own query, so no cross-lane reduction is
-// needed anywhere in the softmax.
+// Why these shapes. A 4x4 MFMA block contracts 4 points against 4 points, so a
+// 1x2x2 patch wastes little of a window: a 9x9 window is covered by 5x5 patches
+// (100 computed vs 81 needed scores), a 3x5x5 window by 3x3x3 (108 vs 75); a
+// 16-point tile (16x16 MFMA) would compute 144 resp. 192. The price is operand
+// traffic: every 4x4x1 MFMA needs one fresh register per lane, so operands come
+// from LDS (fast enough on gfx950), not from L1. Scores outside a point's
+// window are masked by index arithmetic on the window starts, never by padding
+// (software predication of these bounds is what the NATTEN maintainer names as
+// the main overhead of 2D/3D fused kernels; here it is a few integer compares).
 //
-// Backward (query-parallel + key-parallel gather): the dq kernel recomputes
-// P = exp2(S - lse) from the saved logsumexp, forms delta = <dout, out> for its
-// own queries (NATTEN's ComputeDelta, fused here), dS = P (dP - delta) and
-// dq. The dk/dv kernel walks each key's inverse neighborhood (a contiguous
-// range per axis, closed form in na_index.hpp) and writes dk, dv exactly once,
-// with no atomics.
+// Softmax. Scores are kept in log2 units (q pre-multiplied by scale*log2(e)) so
+// exp2 is one instruction; each lane keeps the running maximum and sum of its
+// own query, so no cross-lane reduction is needed in the softmax.
+//
+// Backward (the gather variant): the dq kernel recomputes P = exp2(S - lse)
+// from the saved logsumexp, forms delta = <dout, out> for its queries
+// (NATTEN's ComputeDelta, fused here), dS = P (dP - delta) and dq. The dk/dv
+// kernel walks every key's inverse neighborhood (one contiguous range per
+// axis, closed form in na_index.hpp) and writes dk, dv exactly once, with no
+// atomics. With KVPAR the dk/dv pass also forms each query's dq contribution
+// and adds it into an fp32 accumulator (the KV-parallel variant).
 #pragma once
 
 #include "na_common.hpp"
@@ -51,62 +56,170 @@ struct BwdArgs {
     float scale;
 };
 
-// Per-lane view of a patch-owning lane: the patch first point, the lane's
-// own point, and whether the point is inside the class grid.
-struct LanePoint {
-    int f[3];   // first point of the lane's patch (clamped into the grid)
-    int p[3];   // the lane's own point (clamped into the grid)
-    bool active;
-};
-
-__device__ __forceinline__ LanePoint lane_point(const WaveCtx &w, int grp, int c) {
-    LanePoint lp;
-    int f[3] = {w.o[0], w.o[1] + 2 * (grp >> 2), w.o[2] + 2 * (grp & 3)};
-    int p[3];
-    patch_point(f, c, p);
-    lp.active = p[0] < w.n[0] && p[1] < w.n[1] && p[2] < w.n[2];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        lp.f[a] = imin(f[a], w.n[a] - 1);
-        lp.p[a] = imin(p[a], w.n[a] - 1);
-    }
-    return lp;
+// Rows of axis A a chunk of the staged box may hold: as many as the LDS budget
+// allows for bytes_per_point, at least one.
+__device__ __forceinline__ int chunk_rows(const Box &b, int A, int bytes_per_point, int budget) {
+    const int plane = b.e[0] * b.e[1] * b.e[2] / b.e[A];
+    return imax(1, imin(b.e[A], budget / (plane * bytes_per_point)));
 }
 
-// Number of 1x2x2 patches per axis that cover the union of the windows of a
-// patch of queries: the union is at most k + patch - 1 long.
-__device__ __forceinline__ void key_patch_counts(const WaveCtx &w, int (&cnt)[3]) {
+// The chunk of box b starting at row r0 of axis A.
+__device__ __forceinline__ Box chunk_of(const Box &b, int A, int r0, int rows) {
+    Box c = b;
+    c.o[A] = b.o[A] + r0;
+    c.e[A] = imin(rows, b.e[A] - r0);
+    return c;
+}
+
+// A lane's addressing of a patch walk over a staged chunk. The walk starts at
+// class point `start` (the first patch of the lane's block); entry e (0..3) of
+// item (c0, c1, c2) is the point start + (c0, 2 c1 + e/2, 2 c2 + e%2). For a
+// fixed entry, the LDS point index moves by an amount that is the same for all
+// lanes (item_offset), and its swizzle only depends on c2 mod 4, so both are
+// prepared per entry once per chunk.
+struct Entry {
+    int pt;     // point index of the entry at item (0, 0, 0)
+    int tab;    // swizzle at c2 = j (mod 4) in bits [4j, 4j + 4)
+};
+
+template <int NC>
+__device__ __forceinline__ Entry make_entry(const Box &b, const int (&start)[3], int e) {
+    const int l0 = start[0] - b.o[0], l1 = start[1] - b.o[1] + (e >> 1);
+    const int l2 = start[2] - b.o[2] + (e & 1);
+    Entry en;
+    en.pt = (l0 * b.e[1] + l1) * b.e[2] + l2;
+    en.tab = 0;
 #pragma unroll
-    for (int a = 0; a < 3; ++a) cnt[a] = (w.k[a] + kPatch[a] - 1 + kPatch[a] - 1) / kPatch[a];
+    for (int j = 0; j < 4; ++j) en.tab |= swz<NC>(l1, l2 + 2 * j) << (4 * j);
+    return en;
+}
+
+// Item i of a walk of cnt patches per axis (row-major), and its point offset.
+struct Item {
+    int c0, c1, c2;
+    int off;        // point index offset of the item
+    int sh;         // 4 * (c2 mod 4): swizzle table shift
+};
+
+__device__ __forceinline__ Item make_item(int i, const int (&cnt)[3], const Box &b) {
+    Item it;
+    it.c2 = i % cnt[2];
+    it.c1 = (i / cnt[2]) % cnt[1];
+    it.c0 = i / (cnt[2] * cnt[1]);
+    it.off = (it.c0 * b.e[1] + 2 * it.c1) * b.e[2] + 2 * it.c2;
+    it.sh = 4 * (it.c2 & 3);
+    return it;
+}
+
+__device__ __forceinline__ unsigned umin(unsigned a, unsigned b) { return a < b ? a : b; }
+
+// LDS byte address of chunk 0 of the entry's point at this item, with the
+// swizzle folded in: chunk s is at  addr ^ (s << 4). lim clamps the point
+// into the staged chunk (walks over a chunk cut along H, masked entries).
+template <int PB>
+__device__ __forceinline__ int entry_addr(const Entry &en, const Item &it, unsigned lim) {
+    const unsigned pt = umin((unsigned)(en.pt + it.off), lim);
+    const int sw = (en.tab >> it.sh) & 15;
+    return (int)(pt * PB) | (sw << 4);
+}
+
+// Full point (D elements) at LDS byte address addr (see entry_addr).
+template <typename T, int D>
+__device__ __forceinline__ void lds_point_at(const char *lds, int addr, float (&d)[D]) {
+    constexpr int PB = D * (int)sizeof(T), NC = PB / 16, EPC = 16 / (int)sizeof(T);
+#pragma unroll
+    for (int s = 0; s < NC; ++s) Io<T>::chunk(lds + (addr ^ (s << 4)), d + s * EPC);
+}
+
+// Elements [c*G, c*G + G) (G = D / 4) of the point at LDS byte address addr.
+template <typename T, int D>
+__device__ __forceinline__ void lds_quarter_at(const char *lds, int addr, int c, float (&d)[D / 4]) {
+    constexpr int EPC = 16 / (int)sizeof(T), G = D / 4;
+    if constexpr (G >= EPC) {
+#pragma unroll
+        for (int s = 0; s < G / EPC; ++s)
+            Io<T>::chunk(lds + (addr ^ ((c * (G / EPC) + s) << 4)), d + s * EPC);
+    } else {
+        // G = 4 < EPC = 8 (bf16, D = 16): half a chunk
+        const int chunk = (c * G) / EPC, half = (c * G) % EPC;
+        Io<T>::quad(lds + (addr ^ (chunk << 4)) + half * (int)sizeof(T), d);
+    }
+}
+
+// Validity bits of the four entries of an item: bit e set when entry e lies in
+// the lane's window (or inverse window). m[a] has bit r set when relative
+// position r along axis a (from the walk start) is valid.
+__device__ __forceinline__ int entry_mask(const unsigned (&m)[3], const Item &it) {
+    const unsigned t = (m[0] >> it.c0) & 1u;
+    const unsigned row = (m[1] >> (2 * it.c1)) & (t ? 3u : 0u);
+    const unsigned col = m[2] >> (2 * it.c2);
+    // bit e = row bit (e >> 1) & col bit (e & 1)
+    return (int)(((row & col & 1u)) | (((row & (col >> 1)) & 1u) << 1) |
+                 ((((row >> 1) & col) & 1u) << 2) | ((((row & col) >> 1) & 1u) << 3));
+}
+
+// Bits [lo, lo + len) set (len >= 0, lo + len <= 32).
+__device__ __forceinline__ unsigned bit_range(int lo, int len) {
+    const unsigned ones = len >= 32 ? 0xffffffffu : ((1u << len) - 1u);
+    return ones << lo;
+}
+
+// Index of the block's patch along W inside the tile; blocks of one quarter
+// wave with odd index visit the entries of a patch in the order e ^ 1 in their
+// d-major reads (this is what makes those reads conflict-free, see swz).
+__device__ __forceinline__ int entry_flip(int lane) { return (lane >> 2) & 1; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Chunk bookkeeping shared by the kernels: the items of a walk over a chunk
+// cut along T are either wholly inside or outside it (all blocks of a tile
+// share their T start); a cut along H masks entries one by one.
+struct ChunkView {
+    unsigned lim;    // largest valid point index for clamped reads
+    bool chunked;    // the staged box is split
+    int A;           // cut axis
+};
+
+// 4-bit mask of the entries of an item whose cut-axis row lies in the chunk.
+__device__ __forceinline__ int chunk_mask(const ChunkView &cv, const Box &C, int start_a,
+                                          const Item &it) {
+    if (!cv.chunked) return 15;
+    if (cv.A == 0) {
+        const int r = start_a - C.o[0] + it.c0;
+        return (r >= 0 && r < C.e[0]) ? 15 : 0;
+    }
+    const int r = start_a - C.o[1] + 2 * it.c1;
+    const int lo = (r >= 0 && r < C.e[1]) ? 3 : 0, hi = (r + 1 >= 0 && r + 1 < C.e[1]) ? 12 : 0;
+    return lo | hi;
 }
 
 // ============================================================================
 // Forward: out, lse.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
-    constexpr int G = D / 4;
-    const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (wave >= a.g.n_waves) return;
-    WaveCtx w;
-    if (!decode_wave(a.g, wave, w)) return;
-    const int lane = threadIdx.x & 63, grp = lane >> 2, c = lane & 3;
-    const LanePoint lp = lane_point(w, grp, c);
+__global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
+    TileCtx w;
+    if (!decode_tile(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, flip = entry_flip(lane);
+    const LanePoint lp = lane_point(w, lane);
 
-    const T *Q = static_cast<const T *>(a.q);
-    const T *K = static_cast<const T *>(a.k);
-    const T *V = static_cast<const T *>(a.v);
-
-    // window of this lane's query, relative to the union start of its patch
-    int us[3], off[3], cnt[3];
+    // keys the tile needs (union of its queries' windows, padded to the walks)
+    Box U;
+    int us[3], cnt[3];
+    unsigned vm[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
+        key_box(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x], &U.o[x], &U.e[x]);
         us[x] = window_start(lp.f[x], w.n[x], w.k[x]);
-        off[x] = window_start(lp.p[x], w.n[x], w.k[x]) - us[x];
+        vm[x] = bit_range(window_start(lp.p[x], w.n[x], w.k[x]) - us[x], w.k[x]);
+        cnt[x] = window_walk(w.k[x], kPatch[x]);
     }
-    key_patch_counts(w, cnt);
+    const int ncount = cnt[0] * cnt[1] * cnt[2];
 
     float qr[D];
-    load_row<T, D>(Q + elem_off(w, lp.p), qr);
+    load_row<T, D>(static_cast<const T *>(a.q) + elem_off(w, lp.p), qr);
 #pragma unroll
     for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
 
@@ -115,102 +228,147 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int ct = 0; ct < cnt[0]; ++ct) {
-        for (int ch = 0; ch < cnt[1]; ++ch) {
-            for (int cw = 0; cw < cnt[2]; ++cw) {
-                const int kb[3] = {us[0] + ct * kPatch[0], us[1] + ch * kPatch[1],
-                                   us[2] + cw * kPatch[2]};
-                // S_b[i][c] = <k_i, q_c>: this lane supplies key c of the patch
-                int kc[3];
-                patch_point(kb, c, kc);
+    ChunkView cv;
+    cv.A = a.g.chunk_axis;
+    const int rows = chunk_rows(U, cv.A, 2 * PB, a.g.lds_budget);
+    cv.chunked = rows < U.e[cv.A];
+    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+        const Box C = chunk_of(U, cv.A, r0, rows);
+        const int np = C.e[0] * C.e[1] * C.e[2];
+        char *Ks = smem, *Vs = smem + np * PB;
+        if (r0 > 0) __syncthreads();
+        stage_box<T, D>(static_cast<const T *>(a.k), w, C, Ks);
+        stage_box<T, D>(static_cast<const T *>(a.v), w, C, Vs);
+        stage_wait();
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        const Entry own = make_entry<NC>(C, us, c);
+        Entry dm[4];
 #pragma unroll
-                for (int x = 0; x < 3; ++x) kc[x] = imin(kc[x], w.n[x] - 1);
-                float kr[D];
-                load_row<T, D>(K + elem_off(w, kc), kr);
-                f4 s = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int d = 0; d < D; ++d) s = mfma4(kr[d], qr[d], s);
+        for (int kap = 0; kap < 4; ++kap) dm[kap] = make_entry<NC>(C, us, kap ^ flip);
 
-                // mask keys outside this query's window
-                float sv[4];
+        for (int i = wave; i < ncount; i += kWaves) {
+            const Item it = make_item(i, cnt, C);
+            const int cm = chunk_mask(cv, C, us[cv.A], it);
+            if (cv.chunked && cv.A == 0 && cm == 0) continue;  // uniform along T
+            // S_b[i][c] = <k_i, q_c>: this lane supplies key c of the patch
+            f4 s;
+            {
+                float kr[D];
+                lds_point_at<T, D>(Ks, entry_addr<PB>(own, it, cv.lim), kr);
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rel[3] = {ct * kPatch[0], ch * kPatch[1] + (i >> 1),
-                                        cw * kPatch[2] + (i & 1)};
-                    bool ok = true;
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) ok = ok && rel[x] >= off[x] && rel[x] < off[x] + w.k[x];
-                    sv[i] = ok ? s[i] : -INFINITY;
+                for (int d = 0; d < D; d += 2) {
+                    s0 = mfma4(kr[d], qr[d], s0);
+                    s1 = mfma4(kr[d + 1], qr[d + 1], s1);
                 }
-                const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                const float mn = fmaxf(m, mx);
-                const float alpha = exp2f(m - mn);
-                float p[4];
+                s = s0 + s1;
+            }
+            const int mk = entry_mask(vm, it) & cm;
+            float sv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[i] = exp2f(sv[i] - mn);
-                l = l * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-                m = mn;
+            for (int e = 0; e < 4; ++e) sv[e] = (mk >> e) & 1 ? s[e] : -INFINITY;
+            // online softmax; the running maximum only moves (and the sums are
+            // rescaled) when a score exceeds it by more than 2^8, so exp2 stays
+            // below 256 and out = acc / l is unchanged
+            const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            if (__any(mx > m + 8.f)) {
+                const float mn = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
 #pragma unroll
                 for (int g = 0; g < G; ++g) acc[g] *= alpha;
+                m = mn;
+            }
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sv[e] - m);
+            l += (p[0] + p[1]) + (p[2] + p[3]);
 
-                // O_b[i][c] += v_kappa[i*G + g] * P[c][kappa]: this lane supplies
-                // the d-chunk c of every key of the patch
+            // O_b[i][c] += v_e[i*G + g] * P[c][e]: this lane supplies the
+            // quarter c of every key e of the patch (blocks visit e = kap ^ flip)
 #pragma unroll
-                for (int kap = 0; kap < 4; ++kap) {
-                    int vc[3];
-                    patch_point(kb, kap, vc);
+            for (int kap = 0; kap < 4; ++kap) {
+                float vr[G];
+                lds_quarter_at<T, D>(Vs, entry_addr<PB>(dm[kap], it, cv.lim), c, vr);
+                const float pe = flip ? p[kap ^ 1] : p[kap];
 #pragma unroll
-                    for (int x = 0; x < 3; ++x) vc[x] = imin(vc[x], w.n[x] - 1);
-                    float vr[G];
-                    load_row<T, G>(V + elem_off(w, vc) + c * G, vr);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) acc[g] = mfma4(vr[g], p[kap], acc[g]);
-                }
+                for (int g = 0; g < G; ++g) acc[g] = mfma4(vr[g], pe, acc[g]);
             }
         }
     }
 
-    if (!lp.active) return;
-    const float inv = 1.f / l;
-    T *O = static_cast<T *>(a.out) + elem_off(w, lp.p);
+    // merge the four waves' partial softmax states through LDS
+    __syncthreads();
+    float *mb = reinterpret_cast<float *>(smem);
+    {
+        float *mine = mb + (wave * 64 + lane) * (D + 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float o[G];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int g = 0; g < G; ++g) o[g] = acc[g][i] * inv;
-#pragma unroll
-        for (int g = 0; g < G; g += 4) Io<T>::store4(O + i * G + g, o + g);
+            for (int g = 0; g < G; ++g) mine[i * G + g] = acc[g][i];
+        mine[D] = m;
+        mine[D + 1] = l;
     }
-    a.lse[row_off(w, lp.p)] = (m + __log2f(l)) * kLn2;
+    __syncthreads();
+    {
+        const int L = threadIdx.x >> 2, qd = threadIdx.x & 3;
+        float mw[kWaves], M = -1e30f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            mw[v] = mb[(v * 64 + L) * (D + 2) + D];
+            M = fmaxf(M, mw[v]);
+        }
+        float Ls = 0.f, o[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) o[g] = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float sc = exp2f(mw[v] - M);
+            const float *src = mb + (v * 64 + L) * (D + 2);
+            Ls += src[D + 1] * sc;
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] += src[qd * G + g] * sc;
+        }
+        const LanePoint qp = lane_point(w, L);
+        if (qp.active) {
+            const float inv = 1.f / Ls;
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] *= inv;
+            T *O = static_cast<T *>(a.out) + elem_off(w, qp.p) + qd * G;
+#pragma unroll
+            for (int g = 0; g < G; g += 4) Io<T>::store4(O + g, o + g);
+            if (qd == 0) a.lse[row_off(w, qp.p)] = (M + __log2f(Ls)) * kLn2;
+        }
+    }
 }
 
 // ============================================================================
 // Backward, query side: delta and dq.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
-    constexpr int G = D / 4;
-    const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (wave >= a.g.n_waves) return;
-    WaveCtx w;
-    if (!decode_wave(a.g, wave, w)) return;
-    const int lane = threadIdx.x & 63, grp = lane >> 2, c = lane & 3;
-    const LanePoint lp = lane_point(w, grp, c);
+__global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
+    TileCtx w;
+    if (!decode_tile(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, flip = entry_flip(lane);
+    const LanePoint lp = lane_point(w, lane);
 
-    const T *Q = static_cast<const T *>(a.q);
-    const T *K = static_cast<const T *>(a.k);
-    const T *V = static_cast<const T *>(a.v);
-
-    int us[3], off[3], cnt[3];
+    Box U;
+    int us[3], cnt[3];
+    unsigned vm[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
+        key_box(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x], &U.o[x], &U.e[x]);
         us[x] = window_start(lp.f[x], w.n[x], w.k[x]);
-        off[x] = window_start(lp.p[x], w.n[x], w.k[x]) - us[x];
+        vm[x] = bit_range(window_start(lp.p[x], w.n[x], w.k[x]) - us[x], w.k[x]);
+        cnt[x] = window_walk(w.k[x], kPatch[x]);
     }
-    key_patch_counts(w, cnt);
+    const int ncount = cnt[0] * cnt[1] * cnt[2];
 
     const int64_t qo = elem_off(w, lp.p);
     float qr[D], dor[D];
-    load_row<T, D>(Q + qo, qr);
+    load_row<T, D>(static_cast<const T *>(a.q) + qo, qr);
     load_row<T, D>(static_cast<const T *>(a.dout) + qo, dor);
     float delta = 0.f;
     {
@@ -227,102 +385,151 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int ct = 0; ct < cnt[0]; ++ct) {
-        for (int ch = 0; ch < cnt[1]; ++ch) {
-            for (int cw = 0; cw < cnt[2]; ++cw) {
-                const int kb[3] = {us[0] + ct * kPatch[0], us[1] + ch * kPatch[1],
-                                   us[2] + cw * kPatch[2]};
-                int kc[3];
-                patch_point(kb, c, kc);
+    ChunkView cv;
+    cv.A = a.g.chunk_axis;
+    const int rows = chunk_rows(U, cv.A, 2 * PB, a.g.lds_budget);
+    cv.chunked = rows < U.e[cv.A];
+    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+        const Box C = chunk_of(U, cv.A, r0, rows);
+        const int np = C.e[0] * C.e[1] * C.e[2];
+        char *Ks = smem, *Vs = smem + np * PB;
+        if (r0 > 0) __syncthreads();
+        stage_box<T, D>(static_cast<const T *>(a.k), w, C, Ks);
+        stage_box<T, D>(static_cast<const T *>(a.v), w, C, Vs);
+        stage_wait();
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        const Entry own = make_entry<NC>(C, us, c);
+        Entry dm[4];
 #pragma unroll
-                for (int x = 0; x < 3; ++x) kc[x] = imin(kc[x], w.n[x] - 1);
-                const int64_t ko = elem_off(w, kc);
-                float kr[D], vr[D];
-                load_row<T, D>(K + ko, kr);
-                load_row<T, D>(V + ko, vr);
-                f4 s = f4{0.f, 0.f, 0.f, 0.f}, dp = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int d = 0; d < D; ++d) s = mfma4(kr[d], qr[d], s);
-#pragma unroll
-                for (int d = 0; d < D; ++d) dp = mfma4(vr[d], dor[d], dp);
+        for (int kap = 0; kap < 4; ++kap) dm[kap] = make_entry<NC>(C, us, kap ^ flip);
 
-                float ds[4];
+        for (int i = wave; i < ncount; i += kWaves) {
+            const Item it = make_item(i, cnt, C);
+            const int cm = chunk_mask(cv, C, us[cv.A], it);
+            if (cv.chunked && cv.A == 0 && cm == 0) continue;
+            const int ao = entry_addr<PB>(own, it, cv.lim);
+            f4 s, dp;
+            {
+                float kr[D];
+                lds_point_at<T, D>(Ks, ao, kr);
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rel[3] = {ct * kPatch[0], ch * kPatch[1] + (i >> 1),
-                                        cw * kPatch[2] + (i & 1)};
-                    bool ok = true;
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) ok = ok && rel[x] >= off[x] && rel[x] < off[x] + w.k[x];
-                    const float p = ok ? exp2f(s[i] - lse2) : 0.f;
-                    ds[i] = p * (dp[i] - delta);
+                for (int d = 0; d < D; d += 2) {
+                    s0 = mfma4(kr[d], qr[d], s0);
+                    s1 = mfma4(kr[d + 1], qr[d + 1], s1);
                 }
-                // dQ_b[i][c] += k_kappa[i*G + g] * dS[c][kappa]
+                s = s0 + s1;
+            }
+            {
+                float vr[D];
+                lds_point_at<T, D>(Vs, ao, vr);
+                f4 d0 = f4{0.f, 0.f, 0.f, 0.f}, d1 = d0;
 #pragma unroll
-                for (int kap = 0; kap < 4; ++kap) {
-                    int vc[3];
-                    patch_point(kb, kap, vc);
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) vc[x] = imin(vc[x], w.n[x] - 1);
-                    float kd[G];
-                    load_row<T, G>(K + elem_off(w, vc) + c * G, kd);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) acc[g] = mfma4(kd[g], ds[kap], acc[g]);
+                for (int d = 0; d < D; d += 2) {
+                    d0 = mfma4(vr[d], dor[d], d0);
+                    d1 = mfma4(vr[d + 1], dor[d + 1], d1);
                 }
+                dp = d0 + d1;
+            }
+            const int mk = entry_mask(vm, it) & cm;
+            float ds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = (mk >> e) & 1 ? fast_exp2(s[e] - lse2) : 0.f;
+                ds[e] = p * (dp[e] - delta);
+            }
+            // dQ_b[i][c] += k_e[i*G + g] * dS[c][e]
+#pragma unroll
+            for (int kap = 0; kap < 4; ++kap) {
+                float kd[G];
+                lds_quarter_at<T, D>(Ks, entry_addr<PB>(dm[kap], it, cv.lim), c, kd);
+                const float dse = flip ? ds[kap ^ 1] : ds[kap];
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g] = mfma4(kd[g], dse, acc[g]);
             }
         }
     }
 
-    if (!lp.active) return;
-    a.delta[row_off(w, lp.p)] = delta;
-    T *DQ = static_cast<T *>(a.dq) + qo;
+    // sum the four waves' partial dq through LDS
+    __syncthreads();
+    float *mb = reinterpret_cast<float *>(smem);
+    {
+        float *mine = mb + (wave * 64 + lane) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) mine[i * G + g] = acc[g][i];
+    }
+    __syncthreads();
+    {
+        const int L = threadIdx.x >> 2, qd = threadIdx.x & 3;
         float o[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) o[g] = acc[g][i] * a.scale;
+        for (int g = 0; g < G; ++g) o[g] = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; g += 4) Io<T>::store4(DQ + i * G + g, o + g);
+        for (int v = 0; v < kWaves; ++v) {
+            const float *src = mb + (v * 64 + L) * D + qd * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] += src[g];
+        }
+        const LanePoint qp = lane_point(w, L);
+        if (qp.active) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] *= a.scale;
+            T *DQ = static_cast<T *>(a.dq) + elem_off(w, qp.p) + qd * G;
+#pragma unroll
+            for (int g = 0; g < G; g += 4) Io<T>::store4(DQ + g, o + g);
+        }
     }
+    if (wave == 0 && lp.active) a.delta[row_off(w, lp.p)] = delta;
 }
 
 // ============================================================================
-// Backward, key side: dk and dv by inverse-neighborhood gather. With
-// KVPAR the same pass also produces each query's dq contributions from this
-// key patch and adds them into the fp32 accumulator dq_acc.
+// Backward, key side: dk and dv by inverse-neighborhood gather. With KVPAR the
+// same pass also produces each query's dq contributions from this tile's keys
+// and adds them into the fp32 accumulator dq_acc.
 template <typename T, int D, bool KVPAR>
-__global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
-    constexpr int G = D / 4;
-    const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (wave >= a.g.n_waves) return;
-    WaveCtx w;
-    if (!decode_wave(a.g, wave, w)) return;
-    const int lane = threadIdx.x & 63, grp = lane >> 2, c = lane & 3;
-    const LanePoint lp = lane_point(w, grp, c);  // here: this lane's key
+__global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
+    TileCtx w;
+    if (!decode_tile(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, flip = entry_flip(lane);
+    const LanePoint lp = lane_point(w, lane);  // here: this lane's key
 
-    const T *Q = static_cast<const T *>(a.q);
-    const T *K = static_cast<const T *>(a.k);
-    const T *V = static_cast<const T *>(a.v);
-    const T *DO = static_cast<const T *>(a.dout);
-
-    // queries of the patch's inverse neighborhood, and of this lane's key
-    int lo[3], ilo[3], ihi[3], cnt[3];
+    // queries the tile needs: the union of its keys' inverse windows
+    Box U;
+    int lo[3], cnt[3];
+    unsigned vm[3];
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-        int last = imin(lp.f[x] + kPatch[x] - 1, w.n[x] - 1);
+        cnt[x] = tile_inverse_walk(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x]);
+        query_box(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x], cnt[x], &U.o[x], &U.e[x]);
         lo[x] = inverse_first(lp.f[x], w.n[x], w.k[x]);
-        int hi = inverse_last(last, w.n[x], w.k[x]);
-        ilo[x] = inverse_first(lp.p[x], w.n[x], w.k[x]);
-        ihi[x] = inverse_last(lp.p[x], w.n[x], w.k[x]);
-        cnt[x] = wave_max((hi - lo[x] + kPatch[x]) / kPatch[x]);
+        const int ilo = inverse_first(lp.p[x], w.n[x], w.k[x]);
+        vm[x] = bit_range(ilo - lo[x], inverse_last(lp.p[x], w.n[x], w.k[x]) - ilo + 1);
     }
+    const int ncount = cnt[0] * cnt[1] * cnt[2];
 
     const int64_t ko = elem_off(w, lp.p);
     float kr[D], vr[D];
-    load_row<T, D>(K + ko, kr);
-    load_row<T, D>(V + ko, vr);
+    load_row<T, D>(static_cast<const T *>(a.k) + ko, kr);
+    load_row<T, D>(static_cast<const T *>(a.v) + ko, vr);
 #pragma unroll
     for (int d = 0; d < D; ++d) kr[d] *= a.qscale;
+    // KV-parallel: the block's four keys, quarter c of each, for dq += dS k
+    float kq[KVPAR ? 4 : 1][KVPAR ? G : 1];
+    if constexpr (KVPAR) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int kj[3];
+            patch_point(lp.f, j, kj);
+#pragma unroll
+            for (int x = 0; x < 3; ++x) kj[x] = imin(kj[x], w.n[x] - 1);
+            load_row<T, G>(static_cast<const T *>(a.k) + elem_off(w, kj) + c * G, kq[j]);
+        }
+    }
 
     f4 dk[G], dv[G];
 #pragma unroll
@@ -331,121 +538,152 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
         dv[g] = f4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int ct = 0; ct < cnt[0]; ++ct) {
-        for (int ch = 0; ch < cnt[1]; ++ch) {
-            for (int cw = 0; cw < cnt[2]; ++cw) {
-                const int qb[3] = {lo[0] + ct * kPatch[0], lo[1] + ch * kPatch[1],
-                                   lo[2] + cw * kPatch[2]};
-                // S_b[i][c] = <q_i, k_c>: this lane supplies query c of the patch
-                int qc[3];
-                patch_point(qb, c, qc);
+    ChunkView cv;
+    cv.A = a.g.chunk_axis;
+    const int rows = chunk_rows(U, cv.A, 2 * PB + 8, a.g.lds_budget);
+    cv.chunked = rows < U.e[cv.A];
+    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+        const Box C = chunk_of(U, cv.A, r0, rows);
+        const int np = C.e[0] * C.e[1] * C.e[2];
+        char *Qs = smem, *Os = smem + np * PB;
+        float2 *Rs = reinterpret_cast<float2 *>(smem + 2 * np * PB);
+        if (r0 > 0) __syncthreads();
+        stage_box<T, D>(static_cast<const T *>(a.q), w, C, Qs);
+        stage_box<T, D>(static_cast<const T *>(a.dout), w, C, Os);
+        stage_rows(a.lse, a.delta, w, C, Rs);
+        stage_wait();
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        const Entry own = make_entry<NC>(C, lo, c);
+        Entry dm[4], row[4];
 #pragma unroll
-                for (int x = 0; x < 3; ++x) qc[x] = imin(qc[x], w.n[x] - 1);
-                const int64_t qo = elem_off(w, qc);
-                float qr[D], dor[D];
-                load_row<T, D>(Q + qo, qr);
-                load_row<T, D>(DO + qo, dor);
-                f4 s = f4{0.f, 0.f, 0.f, 0.f}, dp = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int d = 0; d < D; ++d) s = mfma4(qr[d], kr[d], s);
-#pragma unroll
-                for (int d = 0; d < D; ++d) dp = mfma4(dor[d], vr[d], dp);
+        for (int kap = 0; kap < 4; ++kap) {
+            dm[kap] = make_entry<NC>(C, lo, kap ^ flip);
+            row[kap] = make_entry<NC>(C, lo, kap);
+        }
 
-                float p[4], ds[4];
+        for (int i = wave; i < ncount; i += kWaves) {
+            const Item it = make_item(i, cnt, C);
+            const int cm = chunk_mask(cv, C, lo[cv.A], it);
+            if (cv.chunked && cv.A == 0 && cm == 0) continue;
+            // S_b[i][c] = <q_i, k_c>: this lane supplies query c of the patch
+            const int ao = entry_addr<PB>(own, it, cv.lim);
+            f4 s, dp;
+            {
+                float q_[D];
+                lds_point_at<T, D>(Qs, ao, q_);
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    int qi[3];
-                    patch_point(qb, i, qi);
-                    bool ok = true;
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) ok = ok && qi[x] >= ilo[x] && qi[x] <= ihi[x];
-                    int qcl[3];
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) qcl[x] = imin(qi[x], w.n[x] - 1);
-                    const int64_t ro = row_off(w, qcl);
-                    const float l2 = a.lse[ro] * kLog2e;
-                    const float dl = a.delta[ro];
-                    p[i] = ok ? exp2f(s[i] - l2) : 0.f;
-                    ds[i] = p[i] * (dp[i] - dl);
+                for (int d = 0; d < D; d += 2) {
+                    s0 = mfma4(q_[d], kr[d], s0);
+                    s1 = mfma4(q_[d + 1], kr[d + 1], s1);
                 }
-                // dV_b[i][c] += dout_kappa[i*G + g] * P[kappa][c];
-                // dK_b[i][c] += q_kappa[i*G + g] * dS[kappa][c]
+                s = s0 + s1;
+            }
+            {
+                float o_[D];
+                lds_point_at<T, D>(Os, ao, o_);
+                f4 d0 = f4{0.f, 0.f, 0.f, 0.f}, d1 = d0;
 #pragma unroll
-                for (int kap = 0; kap < 4; ++kap) {
-                    int qi[3];
-                    patch_point(qb, kap, qi);
-#pragma unroll
-                    for (int x = 0; x < 3; ++x) qi[x] = imin(qi[x], w.n[x] - 1);
-                    const int64_t o2 = elem_off(w, qi) + c * G;
-                    float dod[G], qd[G];
-                    load_row<T, G>(DO + o2, dod);
-                    load_row<T, G>(Q + o2, qd);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) dv[g] = mfma4(dod[g], p[kap], dv[g]);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) dk[g] = mfma4(qd[g], ds[kap], dk[g]);
+                for (int d = 0; d < D; d += 2) {
+                    d0 = mfma4(o_[d], vr[d], d0);
+                    d1 = mfma4(o_[d + 1], vr[d + 1], d1);
                 }
+                dp = d0 + d1;
+            }
+            const int mk = entry_mask(vm, it) & cm;
+            float p[4], ds[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 ld = Rs[umin((unsigned)(row[e].pt + it.off), cv.lim)];
+                p[e] = (mk >> e) & 1 ? fast_exp2(s[e] - ld.x) : 0.f;
+                ds[e] = p[e] * (dp[e] - ld.y);
+            }
+            // dV_b[i][c] += dout_e[i*G + g] * P[e][c];
+            // dK_b[i][c] += q_e[i*G + g] * dS[e][c]
+#pragma unroll
+            for (int kap = 0; kap < 4; ++kap) {
+                const int ad = entry_addr<PB>(dm[kap], it, cv.lim);
+                float od[G], qd[G];
+                lds_quarter_at<T, D>(Os, ad, c, od);
+                lds_quarter_at<T, D>(Qs, ad, c, qd);
+                const float pe = flip ? p[kap ^ 1] : p[kap];
+                const float dse = flip ? ds[kap ^ 1] : ds[kap];
+#pragma unroll
+                for (int g = 0; g < G; ++g) dv[g] = mfma4(od[g], pe, dv[g]);
+#pragma unroll
+                for (int g = 0; g < G; ++g) dk[g] = mfma4(qd[g], dse, dk[g]);
+            }
 
-                if constexpr (KVPAR) {
-                    // A lane whose key lies past the grid edge was clamped onto a
-                    // real key; it must not add that key's contribution twice.
-                    float dsk[4];
+            if constexpr (KVPAR) {
+                // A lane whose key lies past the grid edge was clamped onto a
+                // real key; it must not add that key's contribution twice.
+                float dsk[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dsk[i] = lp.active ? ds[i] : 0.f;
-                    // transpose dS inside the block: lane 4b+c gets
-                    // tr[j] = dS[query c][key j] (held by lane 4b+j, register c)
-                    float tr[4];
+                for (int j = 0; j < 4; ++j) dsk[j] = lp.active ? ds[j] : 0.f;
+                // transpose dS inside the block: lane 4b+c gets
+                // tr[j] = dS[query c][key j] (held by lane 4b+j, register c)
+                float tr[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int src = (lane & ~3) | j;
-                        float x0 = __shfl(dsk[0], src), x1 = __shfl(dsk[1], src);
-                        float x2 = __shfl(dsk[2], src), x3 = __shfl(dsk[3], src);
-                        tr[j] = c == 0 ? x0 : c == 1 ? x1 : c == 2 ? x2 : x3;
-                    }
-                    // dQ_b[i][c] = sum_j k_j[i*G + g] * dS[c][j]
-                    f4 dq[G];
+                for (int j = 0; j < 4; ++j) {
+                    const int src = (lane & ~3) | j;
+                    const float x0 = __shfl(dsk[0], src), x1 = __shfl(dsk[1], src);
+                    const float x2 = __shfl(dsk[2], src), x3 = __shfl(dsk[3], src);
+                    tr[j] = c == 0 ? x0 : c == 1 ? x1 : c == 2 ? x2 : x3;
+                }
+                // dQ_b[i][c] = sum_j k_j[i*G + g] * dS[c][j]
+                f4 dq[G];
 #pragma unroll
-                    for (int g = 0; g < G; ++g) dq[g] = f4{0.f, 0.f, 0.f, 0.f};
+                for (int g = 0; g < G; ++g) dq[g] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        int kj[3];
-                        patch_point(lp.f, j, kj);
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                        for (int x = 0; x < 3; ++x) kj[x] = imin(kj[x], w.n[x] - 1);
-                        float kd[G];
-                        load_row<T, G>(K + elem_off(w, kj) + c * G, kd);
+                    for (int g = 0; g < G; ++g) dq[g] = mfma4(kq[j][g], tr[j], dq[g]);
+                const int qq[3] = {lo[0] + it.c0, lo[1] + 2 * it.c1 + (c >> 1),
+                                   lo[2] + 2 * it.c2 + (c & 1)};
+                const bool inside = qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2] &&
+                                    ((cm >> c) & 1);
+                if (inside) {
+                    float *accp = a.dq_acc + elem_off(w, qq);
 #pragma unroll
-                        for (int g = 0; g < G; ++g) dq[g] = mfma4(kd[g], tr[j], dq[g]);
-                    }
-                    int qq[3];
-                    patch_point(qb, c, qq);
-                    if (qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2]) {
-                        float *acc = a.dq_acc + elem_off(w, qq);
+                    for (int i2 = 0; i2 < 4; ++i2)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int g = 0; g < G; ++g) atomicAdd(acc + i * G + g, dq[g][i]);
-                    }
+                        for (int g = 0; g < G; ++g) atomicAdd(accp + i2 * G + g, dq[g][i2]);
                 }
             }
         }
     }
 
-    if (!lp.active) return;
-    T *DK = static_cast<T *>(a.dk) + ko;
-    T *DV = static_cast<T *>(a.dv) + ko;
+    // sum the four waves' partial dk, then dv, through LDS
+    float *mb = reinterpret_cast<float *>(smem);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float ok_[G], ov[G];
+    for (int round = 0; round < 2; ++round) {
+        __syncthreads();
+        {
+            float *mine = mb + (wave * 64 + lane) * D;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            ok_[g] = dk[g][i] * a.scale;
-            ov[g] = dv[g][i];
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g) mine[i * G + g] = round == 0 ? dk[g][i] : dv[g][i];
         }
+        __syncthreads();
+        const int L = threadIdx.x >> 2, qd = threadIdx.x & 3;
+        float o[G];
 #pragma unroll
-        for (int g = 0; g < G; g += 4) {
-            Io<T>::store4(DK + i * G + g, ok_ + g);
-            Io<T>::store4(DV + i * G + g, ov + g);
+        for (int g = 0; g < G; ++g) o[g] = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const float *src = mb + (v * 64 + L) * D + qd * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] += src[g];
+        }
+        const LanePoint kp = lane_point(w, L);
+        if (kp.active) {
+            const float mul = round == 0 ? a.scale : 1.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g] *= mul;
+            T *dst = static_cast<T *>(round == 0 ? a.dk : a.dv) + elem_off(w, kp.p) + qd * G;
+#pragma unroll
+            for (int g = 0; g < G; g += 4) Io<T>::store4(dst + g, o + g);
         }
     }
 }
@@ -468,7 +706,7 @@ __global__ void __launch_bounds__(256) delta_kernel(const T *out, const T *dout,
     delta[r] = s;
 }
 
-// Zero n floats (n a multiple of 4), four per thread.
+// Zero n4 float4s.
 __global__ void __launch_bounds__(256) zero_kernel(float *p, int64_t n4) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n4) reinterpret_cast<float4 *>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
