@@ -59,6 +59,9 @@ na_status validate(const na_problem *p, Prob *out) {
     // every offset fits comfortably in int64; keep batch*heads bounded for the wave id
     if (p->batch > INT32_MAX || p->heads > INT32_MAX) return NA_ERR_INVALID_ARG;
     if (p->head_dim != 16 && p->head_dim != 32 && p->head_dim != 64) return NA_ERR_UNSUPPORTED;
+    // byte offsets within one row of tokens are 32-bit in the kernels
+    const int64_t esize = p->dtype == NA_F32 ? 4 : 2;
+    if (p->extent[nd - 1] * p->heads * p->head_dim * esize > INT32_MAX) return NA_ERR_UNSUPPORTED;
     q.batch = p->batch;
     q.heads = p->heads;
     q.head_dim = p->head_dim;
@@ -148,7 +151,7 @@ template <typename T, int D>
 na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
     int lds;
-    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 2) * 4, &a.g, &lds))
+    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 3) * 4, &a.g, &lds))
         return NA_ERR_UNSUPPORTED;
     auto kern = na::fwd_kernel<T, D>;
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
@@ -166,8 +169,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
     constexpr int PB = D * (int)sizeof(T);
     na::BwdArgs aq = a, ak = a;
     int lds_q = 0, lds_k = 0;
-    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * D * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
-    if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * D * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
+    if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 1) * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
+    if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * (D + 1) * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
     if (variant == NA_BWD_GATHER) {
         if (phases & kPhaseDq) {
             auto kern = na::dq_kernel<T, D>;

@@ -271,33 +271,42 @@ __device__ __forceinline__ constexpr int log2_of() {
 // consecutive slots per wave instruction). Box points past the end of the
 // grid (the box may overhang it by up to one patch) repeat the last grid
 // point; they are never used unmasked. Completion: stage_wait().
+//
+// The per-lane part of an address (column, chunk, swizzle) only depends on
+// the lane's slot in a row, so it is computed once per slot group ("part");
+// the row only contributes a uniform base pointer and the parity of its H
+// coordinate, which flips one swizzle bit.
 template <typename T, int D>
 __device__ __forceinline__ void stage_box(const T *src, const TileCtx &w, const Box &b,
                                           char *lds) {
     constexpr int PB = D * (int)sizeof(T), NC = PB / 16, LNC = log2_of<NC>();
-    constexpr int EPC = 16 / (int)sizeof(T);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int rowchunks = b.e[2] * NC;
     const int ipr = (rowchunks + 63) >> 6;
-    const int total = b.e[0] * b.e[1] * ipr;
-    for (int u = wave; u < total; u += kWaves) {
-        const int r = u / ipr, part = u - r * ipr;
-        const int lt = r / b.e[1], lh = r - lt * b.e[1];
+    const int rows = b.e[0] * b.e[1];
+    const int hbit = swz<NC>(1, 0) << 4;   // byte offset flip of odd H rows
+    const char *gsrc = reinterpret_cast<const char *>(src);
+    for (int part = 0; part < ipr; ++part) {
         const int j = part * 64 + lane;
-        const int c0 = imin(b.o[0] + lt, w.n[0] - 1), c1 = imin(b.o[1] + lh, w.n[1] - 1);
-        const int64_t rowbase = w.base + c0 * w.st[0] + c1 * w.st[1];
-        if (j < rowchunks) {
-            const int lw = j >> LNC, slot = j & (NC - 1);
-            const int s = slot ^ swz<NC>(lh, lw);
-            const int c2 = imin(b.o[2] + lw, w.n[2] - 1);
-            const T *gp = src + rowbase + c2 * w.st[2] + s * EPC;
+        const int lw = j >> LNC, slot = j & (NC - 1);
+        if (lw >= b.e[2]) continue;
+        const int c2 = imin(b.o[2] + lw, w.n[2] - 1);
+        // byte offset of the lane's chunk within its row (even H rows)
+        const int col = (int)(c2 * w.st[2]) * (int)sizeof(T) + ((slot ^ swz<NC>(0, lw)) << 4);
+        for (int r = wave; r < rows; r += kWaves) {
+            const int lt = r / b.e[1], lh = r - lt * b.e[1];
+            const int c0 = imin(b.o[0] + lt, w.n[0] - 1), c1 = imin(b.o[1] + lh, w.n[1] - 1);
+            const char *rowp = gsrc + (w.base + c0 * w.st[0] + c1 * w.st[1]) * (int64_t)sizeof(T);
+            const int voff = col ^ ((lh & 1) ? hbit : 0);
 #if defined(__HIP_DEVICE_COMPILE__)
             // the host pass of single-source HIP has no gfx950 builtins
-            __builtin_amdgcn_global_load_lds(gp, (lds_void *)(lds + (r * rowchunks + part * 64) * 16),
+            __builtin_amdgcn_global_load_lds(rowp + voff,
+                                             (lds_void *)(lds + (r * rowchunks + part * 64) * 16),
                                              16, 0, 0);
 #else
-            (void)gp;
+            (void)rowp;
+            (void)voff;
 #endif
         }
     }

@@ -78,35 +78,40 @@ __device__ __forceinline__ Box chunk_of(const Box &b, int A, int r0, int rows) {
 // lanes (item_offset), and its swizzle only depends on c2 mod 4, so both are
 // prepared per entry once per chunk.
 struct Entry {
-    int pt;     // point index of the entry at item (0, 0, 0)
+    int ptb;    // LDS byte offset of the entry's point at item (0, 0, 0)
     int tab;    // swizzle at c2 = j (mod 4) in bits [4j, 4j + 4)
 };
 
 template <int NC>
 __device__ __forceinline__ Entry make_entry(const Box &b, const int (&start)[3], int e) {
+    constexpr int PB = NC * 16;
     const int l0 = start[0] - b.o[0], l1 = start[1] - b.o[1] + (e >> 1);
     const int l2 = start[2] - b.o[2] + (e & 1);
     Entry en;
-    en.pt = (l0 * b.e[1] + l1) * b.e[2] + l2;
+    en.ptb = ((l0 * b.e[1] + l1) * b.e[2] + l2) * PB;
     en.tab = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) en.tab |= swz<NC>(l1, l2 + 2 * j) << (4 * j);
+    // keep the prepared values in registers (no re-derivation inside the walk)
+    asm volatile("" : "+v"(en.ptb), "+v"(en.tab));
     return en;
 }
 
-// Item i of a walk of cnt patches per axis (row-major), and its point offset.
+// Item i of a walk of cnt patches per axis (row-major); all fields are the
+// same for every lane.
 struct Item {
     int c0, c1, c2;
-    int off;        // point index offset of the item
+    int offb;       // LDS byte offset of the item relative to item (0, 0, 0)
     int sh;         // 4 * (c2 mod 4): swizzle table shift
 };
 
+template <int PB>
 __device__ __forceinline__ Item make_item(int i, const int (&cnt)[3], const Box &b) {
     Item it;
     it.c2 = i % cnt[2];
     it.c1 = (i / cnt[2]) % cnt[1];
     it.c0 = i / (cnt[2] * cnt[1]);
-    it.off = (it.c0 * b.e[1] + 2 * it.c1) * b.e[2] + 2 * it.c2;
+    it.offb = ((it.c0 * b.e[1] + 2 * it.c1) * b.e[2] + 2 * it.c2) * PB;
     it.sh = 4 * (it.c2 & 3);
     return it;
 }
@@ -114,13 +119,12 @@ __device__ __forceinline__ Item make_item(int i, const int (&cnt)[3], const Box 
 __device__ __forceinline__ unsigned umin(unsigned a, unsigned b) { return a < b ? a : b; }
 
 // LDS byte address of chunk 0 of the entry's point at this item, with the
-// swizzle folded in: chunk s is at  addr ^ (s << 4). lim clamps the point
-// into the staged chunk (walks over a chunk cut along H, masked entries).
-template <int PB>
-__device__ __forceinline__ int entry_addr(const Entry &en, const Item &it, unsigned lim) {
-    const unsigned pt = umin((unsigned)(en.pt + it.off), lim);
-    const int sw = (en.tab >> it.sh) & 15;
-    return (int)(pt * PB) | (sw << 4);
+// swizzle folded in: chunk s is at  addr ^ (s << 4). limb (a byte offset)
+// clamps the point into the staged chunk (walks over a chunk cut along H,
+// masked entries; negative offsets wrap to large unsigned values).
+__device__ __forceinline__ int entry_addr(const Entry &en, const Item &it, unsigned limb) {
+    const unsigned pa = umin((unsigned)(en.ptb + it.offb), limb);
+    return (int)pa | (((en.tab >> it.sh) & 15) << 4);
 }
 
 // Full point (D elements) at LDS byte address addr (see entry_addr).
@@ -151,11 +155,10 @@ __device__ __forceinline__ void lds_quarter_at(const char *lds, int addr, int c,
 // position r along axis a (from the walk start) is valid.
 __device__ __forceinline__ int entry_mask(const unsigned (&m)[3], const Item &it) {
     const unsigned t = (m[0] >> it.c0) & 1u;
-    const unsigned row = (m[1] >> (2 * it.c1)) & (t ? 3u : 0u);
-    const unsigned col = m[2] >> (2 * it.c2);
-    // bit e = row bit (e >> 1) & col bit (e & 1)
-    return (int)(((row & col & 1u)) | (((row & (col >> 1)) & 1u) << 1) |
-                 ((((row >> 1) & col) & 1u) << 2) | ((((row & col) >> 1) & 1u) << 3));
+    const unsigned row = (m[1] >> (2 * it.c1)) & (3u * t);
+    const unsigned col = (m[2] >> (2 * it.c2)) & 3u;
+    // bit e = row bit (e >> 1) & col bit (e & 1): col spread by the row bits
+    return (int)(col * (row + (row & 2u)));
 }
 
 // Bits [lo, lo + len) set (len >= 0, lo + len <= 32).
@@ -170,6 +173,15 @@ __device__ __forceinline__ unsigned bit_range(int lo, int len) {
 __device__ __forceinline__ int entry_flip(int lane) { return (lane >> 2) & 1; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reorder a 4-vector indexed by entry into the block's visiting order
+// (entries e ^ flip): swap the members of each pair when flip is set.
+__device__ __forceinline__ void swap_pairs(float (&v)[4], int flip) {
+    const bool f = flip != 0;
+    const float a0 = f ? v[1] : v[0], a1 = f ? v[0] : v[1];
+    const float a2 = f ? v[3] : v[2], a3 = f ? v[2] : v[3];
+    v[0] = a0; v[1] = a1; v[2] = a2; v[3] = a3;
+}
 
 // Chunk bookkeeping shared by the kernels: the items of a walk over a chunk
 // cut along T are either wholly inside or outside it (all blocks of a tile
@@ -240,21 +252,21 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
         stage_box<T, D>(static_cast<const T *>(a.k), w, C, Ks);
         stage_box<T, D>(static_cast<const T *>(a.v), w, C, Vs);
         stage_wait();
-        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)((np - 1) * PB) : 0xffffffffu;
         const Entry own = make_entry<NC>(C, us, c);
         Entry dm[4];
 #pragma unroll
         for (int kap = 0; kap < 4; ++kap) dm[kap] = make_entry<NC>(C, us, kap ^ flip);
 
         for (int i = wave; i < ncount; i += kWaves) {
-            const Item it = make_item(i, cnt, C);
+            const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, us[cv.A], it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;  // uniform along T
             // S_b[i][c] = <k_i, q_c>: this lane supplies key c of the patch
             f4 s;
             {
                 float kr[D];
-                lds_point_at<T, D>(Ks, entry_addr<PB>(own, it, cv.lim), kr);
+                lds_point_at<T, D>(Ks, entry_addr(own, it, cv.lim), kr);
                 f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
                 for (int d = 0; d < D; d += 2) {
@@ -283,16 +295,16 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sv[e] - m);
             l += (p[0] + p[1]) + (p[2] + p[3]);
+            swap_pairs(p, flip);
 
             // O_b[i][c] += v_e[i*G + g] * P[c][e]: this lane supplies the
             // quarter c of every key e of the patch (blocks visit e = kap ^ flip)
 #pragma unroll
             for (int kap = 0; kap < 4; ++kap) {
                 float vr[G];
-                lds_quarter_at<T, D>(Vs, entry_addr<PB>(dm[kap], it, cv.lim), c, vr);
-                const float pe = flip ? p[kap ^ 1] : p[kap];
+                lds_quarter_at<T, D>(Vs, entry_addr(dm[kap], it, cv.lim), c, vr);
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g] = mfma4(vr[g], pe, acc[g]);
+                for (int g = 0; g < G; ++g) acc[g] = mfma4(vr[g], p[kap], acc[g]);
             }
         }
     }
@@ -301,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
     __syncthreads();
     float *mb = reinterpret_cast<float *>(smem);
     {
-        float *mine = mb + (wave * 64 + lane) * (D + 2);
+        float *mine = mb + (wave * 64 + lane) * (D + 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -315,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
         float mw[kWaves], M = -1e30f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            mw[v] = mb[(v * 64 + L) * (D + 2) + D];
+            mw[v] = mb[(v * 64 + L) * (D + 3) + D];
             M = fmaxf(M, mw[v]);
         }
         float Ls = 0.f, o[G];
@@ -324,7 +336,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const float sc = exp2f(mw[v] - M);
-            const float *src = mb + (v * 64 + L) * (D + 2);
+            const float *src = mb + (v * 64 + L) * (D + 3);
             Ls += src[D + 1] * sc;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] += src[qd * G + g] * sc;
@@ -397,17 +409,17 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
         stage_box<T, D>(static_cast<const T *>(a.k), w, C, Ks);
         stage_box<T, D>(static_cast<const T *>(a.v), w, C, Vs);
         stage_wait();
-        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)((np - 1) * PB) : 0xffffffffu;
         const Entry own = make_entry<NC>(C, us, c);
         Entry dm[4];
 #pragma unroll
         for (int kap = 0; kap < 4; ++kap) dm[kap] = make_entry<NC>(C, us, kap ^ flip);
 
         for (int i = wave; i < ncount; i += kWaves) {
-            const Item it = make_item(i, cnt, C);
+            const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, us[cv.A], it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
-            const int ao = entry_addr<PB>(own, it, cv.lim);
+            const int ao = entry_addr(own, it, cv.lim);
             f4 s, dp;
             {
                 float kr[D];
@@ -439,13 +451,13 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
                 ds[e] = p * (dp[e] - delta);
             }
             // dQ_b[i][c] += k_e[i*G + g] * dS[c][e]
+            swap_pairs(ds, flip);
 #pragma unroll
             for (int kap = 0; kap < 4; ++kap) {
                 float kd[G];
-                lds_quarter_at<T, D>(Ks, entry_addr<PB>(dm[kap], it, cv.lim), c, kd);
-                const float dse = flip ? ds[kap ^ 1] : ds[kap];
+                lds_quarter_at<T, D>(Ks, entry_addr(dm[kap], it, cv.lim), c, kd);
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g] = mfma4(kd[g], dse, acc[g]);
+                for (int g = 0; g < G; ++g) acc[g] = mfma4(kd[g], ds[kap], acc[g]);
             }
         }
     }
@@ -454,7 +466,7 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
     __syncthreads();
     float *mb = reinterpret_cast<float *>(smem);
     {
-        float *mine = mb + (wave * 64 + lane) * D;
+        float *mine = mb + (wave * 64 + lane) * (D + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -468,7 +480,7 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
         for (int g = 0; g < G; ++g) o[g] = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *src = mb + (v * 64 + L) * D + qd * G;
+            const float *src = mb + (v * 64 + L) * (D + 1) + qd * G;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] += src[g];
         }
@@ -552,7 +564,7 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
         stage_box<T, D>(static_cast<const T *>(a.dout), w, C, Os);
         stage_rows(a.lse, a.delta, w, C, Rs);
         stage_wait();
-        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)(np - 1) : 0xffffffffu;
+        cv.lim = (cv.chunked && cv.A != 0) ? (unsigned)((np - 1) * PB) : 0xffffffffu;
         const Entry own = make_entry<NC>(C, lo, c);
         Entry dm[4], row[4];
 #pragma unroll
@@ -562,11 +574,11 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
         }
 
         for (int i = wave; i < ncount; i += kWaves) {
-            const Item it = make_item(i, cnt, C);
+            const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, lo[cv.A], it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
             // S_b[i][c] = <q_i, k_c>: this lane supplies query c of the patch
-            const int ao = entry_addr<PB>(own, it, cv.lim);
+            const int ao = entry_addr(own, it, cv.lim);
             f4 s, dp;
             {
                 float q_[D];
@@ -594,24 +606,25 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float2 ld = Rs[umin((unsigned)(row[e].pt + it.off), cv.lim)];
+                const float2 ld = Rs[umin((unsigned)(row[e].ptb + it.offb), cv.lim) / PB];
                 p[e] = (mk >> e) & 1 ? fast_exp2(s[e] - ld.x) : 0.f;
                 ds[e] = p[e] * (dp[e] - ld.y);
             }
             // dV_b[i][c] += dout_e[i*G + g] * P[e][c];
             // dK_b[i][c] += q_e[i*G + g] * dS[e][c]
+            float pf[4] = {p[0], p[1], p[2], p[3]}, dsf[4] = {ds[0], ds[1], ds[2], ds[3]};
+            swap_pairs(pf, flip);
+            swap_pairs(dsf, flip);
 #pragma unroll
             for (int kap = 0; kap < 4; ++kap) {
-                const int ad = entry_addr<PB>(dm[kap], it, cv.lim);
+                const int ad = entry_addr(dm[kap], it, cv.lim);
                 float od[G], qd[G];
                 lds_quarter_at<T, D>(Os, ad, c, od);
                 lds_quarter_at<T, D>(Qs, ad, c, qd);
-                const float pe = flip ? p[kap ^ 1] : p[kap];
-                const float dse = flip ? ds[kap ^ 1] : ds[kap];
 #pragma unroll
-                for (int g = 0; g < G; ++g) dv[g] = mfma4(od[g], pe, dv[g]);
+                for (int g = 0; g < G; ++g) dv[g] = mfma4(od[g], pf[kap], dv[g]);
 #pragma unroll
-                for (int g = 0; g < G; ++g) dk[g] = mfma4(qd[g], dse, dk[g]);
+                for (int g = 0; g < G; ++g) dk[g] = mfma4(qd[g], dsf[kap], dk[g]);
             }
 
             if constexpr (KVPAR) {
@@ -659,7 +672,7 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
     for (int round = 0; round < 2; ++round) {
         __syncthreads();
         {
-            float *mine = mb + (wave * 64 + lane) * D;
+            float *mine = mb + (wave * 64 + lane) * (D + 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -672,7 +685,7 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
         for (int g = 0; g < G; ++g) o[g] = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *src = mb + (v * 64 + L) * D + qd * G;
+            const float *src = mb + (v * 64 + L) * (D + 1) + qd * G;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] += src[g];
         }
