@@ -19,9 +19,11 @@ progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -46,6 +48,35 @@ KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "fwd_bwd_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources; a recorded traffic figure is only
+    reported while the kernels it was measured on are unchanged."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary profiles/traffic_<kernel>_<workload>.md, or None
+    when there is none or it was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
 
 
 def flops(w):
@@ -153,7 +184,8 @@ def roofline(w, per):
     achieved = fl / (per[name] * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp32_mfma"]
     return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 3), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(name, w.name),
             "flops_per_launch": fl, "avg_launch_ms": round(per[name], 4)}
 
 
@@ -195,7 +227,13 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the 3D workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: neighborhood attention here runs on a single "
@@ -205,6 +243,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     na.load()
+
+    if args.calibrate_copy:
+        # a plain copy of known size: 1 GiB read, 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 3}))
+        return
 
     w = WORKLOADS[args.workload]
     r = Runner(w, args.variant)
