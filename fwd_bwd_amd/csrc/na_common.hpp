@@ -146,12 +146,22 @@ __device__ __forceinline__ int xcd_tile_id(int bid, int n) {
     return xcd < r ? xcd * (q + 1) + j : r * (q + 1) + (xcd - r) * q + j;
 }
 
-// Decodes a tile id (tile fastest along W, then H, T, residue, head, batch).
+// Decodes a tile id. Within one (batch, head, residue, T-tile) plane the
+// tiles are walked in bands kBand tiles wide along W, row by row inside a
+// band, so a tile's upper neighbour was staged at most kBand tiles earlier
+// (its halo is then still in L2); then T, residue, head, batch.
 // Returns false when the tile lies past the end of its residue class.
+constexpr int kBand = 32;
+
 __device__ __forceinline__ bool decode_tile(const Geometry &g, int tile, TileCtx &w) {
-    int rem = tile;
-    int tw = rem % g.tiles[2]; rem /= g.tiles[2];
-    int th = rem % g.tiles[1]; rem /= g.tiles[1];
+    const int plane = g.tiles[1] * g.tiles[2];
+    int rem = tile / plane;
+    int in = tile - rem * plane;
+    const int band = in / (kBand * g.tiles[1]);
+    const int bw = imin(kBand, g.tiles[2] - band * kBand);   // width of this band
+    in -= band * kBand * g.tiles[1];
+    int th = in / bw;
+    int tw = band * kBand + (in - th * bw);
     int tt = rem % g.tiles[0]; rem /= g.tiles[0];
     int res = rem % g.nres; rem /= g.nres;
     int head = rem % g.heads; rem /= g.heads;

@@ -56,18 +56,30 @@ struct BwdArgs {
     float scale;
 };
 
+// Element `i` of a 3-array chosen by value: a runtime index into a small
+// array would put the array in (slow, memory-backed) scratch.
+__device__ __forceinline__ int get3(const int (&a)[3], int i) {
+    return i == 0 ? a[0] : (i == 1 ? a[1] : a[2]);
+}
+
 // Rows of axis A a chunk of the staged box may hold: as many as the LDS budget
 // allows for bytes_per_point, at least one.
 __device__ __forceinline__ int chunk_rows(const Box &b, int A, int bytes_per_point, int budget) {
-    const int plane = b.e[0] * b.e[1] * b.e[2] / b.e[A];
-    return imax(1, imin(b.e[A], budget / (plane * bytes_per_point)));
+    const int ea = get3(b.e, A);
+    const int plane = b.e[0] * b.e[1] * b.e[2] / ea;
+    return imax(1, imin(ea, budget / (plane * bytes_per_point)));
 }
 
 // The chunk of box b starting at row r0 of axis A.
 __device__ __forceinline__ Box chunk_of(const Box &b, int A, int r0, int rows) {
     Box c = b;
-    c.o[A] = b.o[A] + r0;
-    c.e[A] = imin(rows, b.e[A] - r0);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        if (x == A) {
+            c.o[x] = b.o[x] + r0;
+            c.e[x] = imin(rows, b.e[x] - r0);
+        }
+    }
     return c;
 }
 
@@ -174,6 +186,19 @@ __device__ __forceinline__ int entry_flip(int lane) { return (lane >> 2) & 1; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Output of the merged results: thread qd (0..3) of a point writes G = D / 4
+// elements as 16-byte (or, for bf16 D = 16, 8-byte) pieces, piece j at element
+// (4 j + qd) * W, so the four threads of a point write contiguous bytes in
+// every store instruction (no partially written lines).
+template <typename T, int D>
+__device__ __forceinline__ constexpr int piece_elems() {
+    return (D / 4) >= (16 / (int)sizeof(T)) ? 16 / (int)sizeof(T) : D / 4;
+}
+template <typename T, int D>
+__device__ __forceinline__ int piece_offset(int j, int qd) {
+    return (4 * j + qd) * piece_elems<T, D>();
+}
+
 // Reorder a 4-vector indexed by entry into the block's visiting order
 // (entries e ^ flip): swap the members of each pair when flip is set.
 __device__ __forceinline__ void swap_pairs(float (&v)[4], int flip) {
@@ -208,7 +233,7 @@ __device__ __forceinline__ int chunk_mask(const ChunkView &cv, const Box &C, int
 // ============================================================================
 // Forward: out, lse.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -243,8 +268,8 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
     ChunkView cv;
     cv.A = a.g.chunk_axis;
     const int rows = chunk_rows(U, cv.A, 2 * PB, a.g.lds_budget);
-    cv.chunked = rows < U.e[cv.A];
-    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+    cv.chunked = rows < get3(U.e, cv.A);
+    for (int r0 = 0; r0 < get3(U.e, cv.A); r0 += rows) {
         const Box C = chunk_of(U, cv.A, r0, rows);
         const int np = C.e[0] * C.e[1] * C.e[2];
         char *Ks = smem, *Vs = smem + np * PB;
@@ -260,7 +285,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
 
         for (int i = wave; i < ncount; i += kWaves) {
             const Item it = make_item<PB>(i, cnt, C);
-            const int cm = chunk_mask(cv, C, us[cv.A], it);
+            const int cm = chunk_mask(cv, C, get3(us, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;  // uniform along T
             // S_b[i][c] = <k_i, q_c>: this lane supplies key c of the patch
             f4 s;
@@ -333,22 +358,29 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
         float Ls = 0.f, o[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) o[g] = 0.f;
+        constexpr int PE = piece_elems<T, D>();
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const float sc = exp2f(mw[v] - M);
             const float *src = mb + (v * 64 + L) * (D + 3);
             Ls += src[D + 1] * sc;
 #pragma unroll
-            for (int g = 0; g < G; ++g) o[g] += src[qd * G + g] * sc;
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; ++x)
+                    o[j * PE + x] += src[piece_offset<T, D>(j, qd) + x] * sc;
         }
         const LanePoint qp = lane_point(w, L);
         if (qp.active) {
             const float inv = 1.f / Ls;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] *= inv;
-            T *O = static_cast<T *>(a.out) + elem_off(w, qp.p) + qd * G;
+            T *O = static_cast<T *>(a.out) + elem_off(w, qp.p);
 #pragma unroll
-            for (int g = 0; g < G; g += 4) Io<T>::store4(O + g, o + g);
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; x += 4)
+                    Io<T>::store4(O + piece_offset<T, D>(j, qd) + x, o + j * PE + x);
             if (qd == 0) a.lse[row_off(w, qp.p)] = (M + __log2f(Ls)) * kLn2;
         }
     }
@@ -357,7 +389,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(FwdArgs a) {
 // ============================================================================
 // Backward, query side: delta and dq.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -400,8 +432,8 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
     ChunkView cv;
     cv.A = a.g.chunk_axis;
     const int rows = chunk_rows(U, cv.A, 2 * PB, a.g.lds_budget);
-    cv.chunked = rows < U.e[cv.A];
-    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+    cv.chunked = rows < get3(U.e, cv.A);
+    for (int r0 = 0; r0 < get3(U.e, cv.A); r0 += rows) {
         const Box C = chunk_of(U, cv.A, r0, rows);
         const int np = C.e[0] * C.e[1] * C.e[2];
         char *Ks = smem, *Vs = smem + np * PB;
@@ -417,7 +449,7 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
 
         for (int i = wave; i < ncount; i += kWaves) {
             const Item it = make_item<PB>(i, cnt, C);
-            const int cm = chunk_mask(cv, C, us[cv.A], it);
+            const int cm = chunk_mask(cv, C, get3(us, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
             const int ao = entry_addr(own, it, cv.lim);
             f4 s, dp;
@@ -478,19 +510,25 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
         float o[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) o[g] = 0.f;
+        constexpr int PE = piece_elems<T, D>();
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *src = mb + (v * 64 + L) * (D + 1) + qd * G;
+            const float *src = mb + (v * 64 + L) * (D + 1);
 #pragma unroll
-            for (int g = 0; g < G; ++g) o[g] += src[g];
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; ++x) o[j * PE + x] += src[piece_offset<T, D>(j, qd) + x];
         }
         const LanePoint qp = lane_point(w, L);
         if (qp.active) {
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] *= a.scale;
-            T *DQ = static_cast<T *>(a.dq) + elem_off(w, qp.p) + qd * G;
+            T *DQ = static_cast<T *>(a.dq) + elem_off(w, qp.p);
 #pragma unroll
-            for (int g = 0; g < G; g += 4) Io<T>::store4(DQ + g, o + g);
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; x += 4)
+                    Io<T>::store4(DQ + piece_offset<T, D>(j, qd) + x, o + j * PE + x);
         }
     }
     if (wave == 0 && lp.active) a.delta[row_off(w, lp.p)] = delta;
@@ -501,7 +539,7 @@ __global__ void __launch_bounds__(kThreads) dq_kernel(BwdArgs a) {
 // same pass also produces each query's dq contributions from this tile's keys
 // and adds them into the fp32 accumulator dq_acc.
 template <typename T, int D, bool KVPAR>
-__global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -553,8 +591,8 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
     ChunkView cv;
     cv.A = a.g.chunk_axis;
     const int rows = chunk_rows(U, cv.A, 2 * PB + 8, a.g.lds_budget);
-    cv.chunked = rows < U.e[cv.A];
-    for (int r0 = 0; r0 < U.e[cv.A]; r0 += rows) {
+    cv.chunked = rows < get3(U.e, cv.A);
+    for (int r0 = 0; r0 < get3(U.e, cv.A); r0 += rows) {
         const Box C = chunk_of(U, cv.A, r0, rows);
         const int np = C.e[0] * C.e[1] * C.e[2];
         char *Qs = smem, *Os = smem + np * PB;
@@ -575,7 +613,7 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
 
         for (int i = wave; i < ncount; i += kWaves) {
             const Item it = make_item<PB>(i, cnt, C);
-            const int cm = chunk_mask(cv, C, lo[cv.A], it);
+            const int cm = chunk_mask(cv, C, get3(lo, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
             // S_b[i][c] = <q_i, k_c>: this lane supplies query c of the patch
             const int ao = entry_addr(own, it, cv.lim);
@@ -683,20 +721,26 @@ __global__ void __launch_bounds__(kThreads) dkdv_kernel(BwdArgs a) {
         float o[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) o[g] = 0.f;
+        constexpr int PE = piece_elems<T, D>();
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *src = mb + (v * 64 + L) * (D + 1) + qd * G;
+            const float *src = mb + (v * 64 + L) * (D + 1);
 #pragma unroll
-            for (int g = 0; g < G; ++g) o[g] += src[g];
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; ++x) o[j * PE + x] += src[piece_offset<T, D>(j, qd) + x];
         }
         const LanePoint kp = lane_point(w, L);
         if (kp.active) {
             const float mul = round == 0 ? a.scale : 1.f;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] *= mul;
-            T *dst = static_cast<T *>(round == 0 ? a.dk : a.dv) + elem_off(w, kp.p) + qd * G;
+            T *dst = static_cast<T *>(round == 0 ? a.dk : a.dv) + elem_off(w, kp.p);
 #pragma unroll
-            for (int g = 0; g < G; g += 4) Io<T>::store4(dst + g, o + g);
+            for (int j = 0; j < G / PE; ++j)
+#pragma unroll
+                for (int x = 0; x < PE; x += 4)
+                    Io<T>::store4(dst + piece_offset<T, D>(j, qd) + x, o + j * PE + x);
         }
     }
 }
