@@ -9,6 +9,7 @@
 #include <initializer_list>
 
 #include "na.h"
+#include "na_fast.hpp"
 #include "na_kernels.hpp"
 
 namespace {
@@ -143,6 +144,155 @@ bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
     return true;
 }
 
+// ----------------------------------------------------------------------------
+// Register-resident kernels (na_fast.hpp): fp32, head_dim 16 or 32, square
+// walks of C x C patches along H and W, one box plane within the LDS share of
+// two workgroups per CU.
+
+constexpr int kFastLdsMax = 80 * 1024;
+
+struct FastPlan {
+    na::fast::Geom g;
+    int lds;
+    int c;        // walk length per axis the kernel is compiled for
+    bool t3;      // more than one plane along T
+    bool border;  // dk/dv: some tiles need a longer inverse walk (left to the split kernel)
+};
+
+// Smallest compiled walk length >= need (0: none). Grids with several planes
+// along T keep fewer scores per lane (the other operands stay live across the
+// plane loop).
+int fast_walk(int need, bool t3) {
+    const int cmax = t3 ? 4 : 5;
+    for (int c = 2; c <= cmax; ++c)
+        if (c >= need) return c;
+    return 0;
+}
+
+// kind 0: forward / dq (key boxes), 1: dk/dv (query boxes)
+bool fast_plan(const Prob &q, int kind, FastPlan *pl) {
+    if (q.dtype != NA_F32 || (q.head_dim != 16 && q.head_dim != 32)) return false;
+    const int PB = (int)q.head_dim * 4;
+    const bool t3 = q.ext[0] > 1;
+    // walk lengths
+    int need = 0, interior = 0;
+    for (int a = 1; a < 3; ++a) interior = std::max(interior, na::window_walk(q.ker[a], 2));
+    if (kind == 0) {
+        if (na::window_walk(q.ker[1], 2) != na::window_walk(q.ker[2], 2)) return false;
+        need = interior;
+    } else {
+        for (int a = 1; a < 3; ++a)
+            for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
+                const int n = na::class_size(q.ext[a], q.dil[a], r);
+                for (int f = 0; f < n; f += 16)
+                    need = std::max(need, na::tile_inverse_walk(f, 16, 2, n, q.ker[a]));
+            }
+    }
+    int c = fast_walk(need, t3);
+    pl->border = false;
+    if (c == 0 && kind == 1) {
+        // the split kernel takes the border tiles
+        c = fast_walk(interior, t3);
+        pl->border = true;
+    }
+    if (c == 0) return false;
+    if (kind == 0 && c != need) return false;  // the edge masks assume the exact walk
+    // largest plane box per axis over the tiles this kernel runs
+    int mx[3] = {1, 1, 1};
+    for (int a = 1; a < 3; ++a)
+        for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
+            const int n = na::class_size(q.ext[a], q.dil[a], r);
+            for (int f = 0; f < n; f += 16) {
+                int start, extent;
+                if (kind == 0) {
+                    na::key_box(f, 16, 2, n, q.ker[a], &start, &extent);
+                } else {
+                    const int cnt = na::tile_inverse_walk(f, 16, 2, n, q.ker[a]);
+                    if (cnt > c) continue;
+                    na::query_box(f, 16, 2, n, q.ker[a], cnt, &start, &extent);
+                }
+                mx[a] = std::max(mx[a], extent);
+            }
+        }
+    // row pitches: an odd number of 16-byte slots (A), 2 mod 4 slots (B)
+    const int slots = mx[2] * PB / 16;
+    const int ra = (slots | 1) * 16;
+    const int rb = (slots + ((2 - slots % 4) + 4) % 4) * 16;
+    int64_t lds = (int64_t)mx[1] * std::max(ra, rb);
+    na::fast::Geom &g = pl->g;
+    g.rows_off = (int)lds;
+    g.rows_pitch = mx[2];
+    if (kind == 1) lds += (int64_t)mx[1] * mx[2] * 8;
+    if (lds > kFastLdsMax) return false;
+    int64_t n_tiles = q.batch * q.heads;
+    int nres = 1;
+    for (int a = 0; a < 3; ++a) {
+        g.ext[a] = q.ext[a];
+        g.ker[a] = q.ker[a];
+        g.dil[a] = q.dil[a];
+        const int nmax = na::class_size(q.ext[a], q.dil[a], 0);
+        g.tiles[a] = a == 0 ? nmax : (nmax + 15) / 16;
+        n_tiles *= g.tiles[a];
+        nres *= q.dil[a];
+    }
+    n_tiles *= nres;
+    if (n_tiles > INT32_MAX) return false;
+    g.heads = (int)q.heads;
+    g.batch = (int)q.batch;
+    g.head_dim = (int)q.head_dim;
+    g.nres = nres;
+    g.n_tiles = (int)n_tiles;
+    g.ra = ra;
+    g.rb = rb;
+    pl->lds = (int)lds;
+    pl->c = c;
+    pl->t3 = t3;
+    return true;
+}
+
+template <typename Kern, typename Args>
+na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t s) {
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            pl.lds) != hipSuccess)
+        return NA_ERR_HIP;
+    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
+    return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
+}
+
+// The compiled (head_dim, walk, several planes) combinations.
+#define NA_FAST_CASES(X)                                                                  \
+    X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)                      \
+    X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
+    X(16, 2, true) X(16, 3, true) X(16, 4, true)                                         \
+    X(32, 2, true) X(32, 3, true) X(32, 4, true)
+
+na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgs &a, hipStream_t s) {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return launch_fast(na::fast::fwd_kernel<D, C, C, T3>, pl, a, s);
+    NA_FAST_CASES(X)
+#undef X
+    return NA_ERR_UNSUPPORTED;
+}
+
+na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return launch_fast(na::fast::dq_kernel<D, C, C, T3>, pl, a, s);
+    NA_FAST_CASES(X)
+#undef X
+    return NA_ERR_UNSUPPORTED;
+}
+
+na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return launch_fast(na::fast::dkdv_kernel<D, C, C, T3>, pl, a, s);
+    NA_FAST_CASES(X)
+#undef X
+    return NA_ERR_UNSUPPORTED;
+}
+
 dim3 flat_grid(int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); }
 
 na_status launched() { return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP; }
@@ -150,6 +300,18 @@ na_status launched() { return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_H
 template <typename T, int D>
 na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
+    FastPlan pl;
+    if (fast_plan(pr, 0, &pl)) {
+        na::fast::FwdArgs fa{};
+        fa.g = pl.g;
+        fa.q = static_cast<const float *>(a.q);
+        fa.k = static_cast<const float *>(a.k);
+        fa.v = static_cast<const float *>(a.v);
+        fa.out = static_cast<float *>(a.out);
+        fa.lse = a.lse;
+        fa.qscale = a.qscale;
+        return fast_fwd(pl, fa, s);
+    }
     int lds;
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 3) * 4, &a.g, &lds))
         return NA_ERR_UNSUPPORTED;
@@ -172,21 +334,55 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 1) * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
     if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * (D + 1) * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
     if (variant == NA_BWD_GATHER) {
+        na::fast::BwdArgs fa{};
+        fa.q = static_cast<const float *>(a.q);
+        fa.k = static_cast<const float *>(a.k);
+        fa.v = static_cast<const float *>(a.v);
+        fa.out = static_cast<const float *>(a.out);
+        fa.dout = static_cast<const float *>(a.dout);
+        fa.lse = a.lse;
+        fa.delta = a.delta;
+        fa.dq = static_cast<float *>(a.dq);
+        fa.dk = static_cast<float *>(a.dk);
+        fa.dv = static_cast<float *>(a.dv);
+        fa.qscale = a.qscale;
+        fa.scale = a.scale;
+        // dq (which also writes delta) strictly before dk/dv, which reads it
+        FastPlan pq, pk;
         if (phases & kPhaseDq) {
-            auto kern = na::dq_kernel<T, D>;
-            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    lds_q) != hipSuccess)
-                return NA_ERR_HIP;
-            hipLaunchKernelGGL(kern, dim3(aq.g.n_tiles), dim3(na::kThreads), lds_q, s, aq);
-            if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+            if (fast_plan(pr, 0, &pq)) {
+                fa.g = pq.g;
+                const na_status st = fast_dq(pq, fa, s);
+                if (st != NA_OK) return st;
+            } else {
+                auto kern = na::dq_kernel<T, D>;
+                if (hipFuncSetAttribute((const void *)kern,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        lds_q) != hipSuccess)
+                    return NA_ERR_HIP;
+                hipLaunchKernelGGL(kern, dim3(aq.g.n_tiles), dim3(na::kThreads), lds_q, s, aq);
+                if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+            }
         }
         if (phases & kPhaseDkdv) {
-            auto kern = na::dkdv_kernel<T, D, false>;
-            if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    lds_k) != hipSuccess)
-                return NA_ERR_HIP;
-            hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
-            if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+            bool split = true;
+            if (fast_plan(pr, 1, &pk)) {
+                fa.g = pk.g;
+                const na_status st = fast_dkdv(pk, fa, s);
+                if (st != NA_OK) return st;
+                split = pk.border;
+                ak.skip_ch = pk.c;  // the split kernel only takes the tiles left over
+                ak.skip_cw = pk.c;
+            }
+            if (split) {
+                auto kern = na::dkdv_kernel<T, D, false>;
+                if (hipFuncSetAttribute((const void *)kern,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        lds_k) != hipSuccess)
+                    return NA_ERR_HIP;
+                hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
+                if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+            }
         }
         return NA_OK;
     }

@@ -103,6 +103,14 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
+// Bits [lo, lo + len) set (len >= 0, lo + len <= 32).
+__device__ __forceinline__ unsigned bit_range(int lo, int len) {
+    const unsigned ones = len >= 32 ? 0xffffffffu : ((1u << len) - 1u);
+    return ones << lo;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ----------------------------------------------------------------------------
 // Tiles. Axis 0 is T (1 for 2D problems), axis 1 is H, axis 2 is W, all in
 // class coordinates of one residue class (dilation). A workgroup of kWaves
@@ -153,6 +161,38 @@ __device__ __forceinline__ int xcd_tile_id(int bid, int n) {
 // Returns false when the tile lies past the end of its residue class.
 constexpr int kBand = 32;
 
+// Fills w for batch element b, head, residue class res and tile origin o
+// (class coordinates); false when the origin lies past the end of its class.
+__device__ __forceinline__ bool fill_ctx(const int (&ext)[3], const int (&ker)[3],
+                                         const int (&dil)[3], int heads, int head_dim, int b,
+                                         int head, int res, const int (&o)[3], TileCtx &w) {
+    int r[3];
+    r[2] = res % dil[2];
+    r[1] = (res / dil[2]) % dil[1];
+    r[0] = res / (dil[2] * dil[1]);
+    bool inside = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        w.n[a] = class_size(ext[a], dil[a], r[a]);
+        w.k[a] = ker[a];
+        w.o[a] = o[a];
+        inside = inside && (o[a] < w.n[a]);
+    }
+    const int64_t HW = (int64_t)ext[1] * ext[2];
+    const int64_t ntok = HW * ext[0];
+    const int64_t hd = (int64_t)heads * head_dim;
+    const int64_t origin_tok = r[0] * HW + (int64_t)r[1] * ext[2] + r[2];
+    w.base = ((int64_t)b * ntok + origin_tok) * hd + (int64_t)head * head_dim;
+    w.st[0] = dil[0] * HW * hd;
+    w.st[1] = (int64_t)dil[1] * ext[2] * hd;
+    w.st[2] = (int64_t)dil[2] * hd;
+    w.lbase = ((int64_t)b * ntok + origin_tok) * heads + head;
+    w.lst[0] = dil[0] * HW * heads;
+    w.lst[1] = (int64_t)dil[1] * ext[2] * heads;
+    w.lst[2] = (int64_t)dil[2] * heads;
+    return inside;
+}
+
 __device__ __forceinline__ bool decode_tile(const Geometry &g, int tile, TileCtx &w) {
     const int plane = g.tiles[1] * g.tiles[2];
     int rem = tile / plane;
@@ -160,38 +200,16 @@ __device__ __forceinline__ bool decode_tile(const Geometry &g, int tile, TileCtx
     const int band = in / (kBand * g.tiles[1]);
     const int bw = imin(kBand, g.tiles[2] - band * kBand);   // width of this band
     in -= band * kBand * g.tiles[1];
-    int th = in / bw;
-    int tw = band * kBand + (in - th * bw);
-    int tt = rem % g.tiles[0]; rem /= g.tiles[0];
-    int res = rem % g.nres; rem /= g.nres;
-    int head = rem % g.heads; rem /= g.heads;
-    int b = rem;
-    int r[3];
-    r[2] = res % g.dil[2];
-    r[1] = (res / g.dil[2]) % g.dil[1];
-    r[0] = res / (g.dil[2] * g.dil[1]);
-    const int t_idx[3] = {tt, th, tw};
-    bool inside = true;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        w.n[a] = class_size(g.ext[a], g.dil[a], r[a]);
-        w.k[a] = g.ker[a];
-        w.o[a] = t_idx[a] * kTile[a];
-        inside = inside && (w.o[a] < w.n[a]);
-    }
-    const int64_t HW = (int64_t)g.ext[1] * g.ext[2];
-    const int64_t ntok = HW * g.ext[0];
-    const int64_t hd = (int64_t)g.heads * g.head_dim;
-    const int64_t origin_tok = r[0] * HW + (int64_t)r[1] * g.ext[2] + r[2];
-    w.base = ((int64_t)b * ntok + origin_tok) * hd + (int64_t)head * g.head_dim;
-    w.st[0] = g.dil[0] * HW * hd;
-    w.st[1] = (int64_t)g.dil[1] * g.ext[2] * hd;
-    w.st[2] = (int64_t)g.dil[2] * hd;
-    w.lbase = ((int64_t)b * ntok + origin_tok) * g.heads + head;
-    w.lst[0] = g.dil[0] * HW * g.heads;
-    w.lst[1] = (int64_t)g.dil[1] * g.ext[2] * g.heads;
-    w.lst[2] = (int64_t)g.dil[2] * g.heads;
-    return inside;
+    const int th = in / bw;
+    const int tw = band * kBand + (in - th * bw);
+    const int tt = rem % g.tiles[0];
+    rem /= g.tiles[0];
+    const int res = rem % g.nres;
+    rem /= g.nres;
+    const int head = rem % g.heads;
+    const int b = rem / g.heads;
+    const int o[3] = {tt * kTile[0], th * kTile[1], tw * kTile[2]};
+    return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, b, head, res, o, w);
 }
 
 __device__ __forceinline__ int64_t elem_off(const TileCtx &w, const int (&c)[3]) {

@@ -1,0 +1,609 @@
+// na_fast.hpp -- neighborhood attention kernels with register-resident scores,
+// for fp32 tensors and small windows (gfx950, wave64, MFMA 4x4x1 f32).
+//
+// Work decomposition. A workgroup of four waves owns a 1 x 16 x 16 tile of one
+// residue class of one (batch, head); each wave owns an 8 x 8 quarter of it,
+// one point per lane, in sixteen 1 x 2 x 2 patches (one per 4-lane MFMA
+// block). Every wave walks the whole window (forward, dq) or inverse window
+// (dk/dv) of its own points, so no partial results are merged between waves.
+// The walk along H and W has a compile-time length (CH x CW patches of the
+// other side per block), which lets each lane keep the scores of its point for
+// the whole walk in registers: the kernels run in phases that each need one
+// staged tensor only, and the LDS holds one box plane of one tensor at a time.
+//
+//   forward, per key plane:  K -> S and its maximum;  V -> P = exp2(S - m), O += P V
+//   dq, per key plane:       V -> dP;  K -> S, dS = P (dP - delta);  K -> dQ += dS K
+//   dk/dv, per query plane:  Q -> P;  dO -> dV += P dO;  dO -> dS;  Q -> dK += dS Q
+//
+// (NATTEN issue #161, "Backward pass is very slow towards much tokens and large
+// kernels": the backward recomputes the attention weights from the saved
+// logsumexp, uses delta = rowsum(dO * O), and forms dK and dV by gathering
+// over each key's inverse neighborhood.)
+//
+// LDS layouts. A staged point takes D * 4 bytes (NC 16-byte chunks), points of
+// a box row contiguous, rows at a padded pitch. The 16 lanes of a quarter wave
+// hold four patches stacked along H (an 8 x 2 block of points), and read
+//  * key-major (A): chunk s of each lane's own point; conflict-free when the
+//    row pitch is an odd number of 16-byte slots;
+//  * d-major (B): the four lanes of a block read chunks c, c + 4, ... of the
+//    same point, all blocks the same entry of their patch; conflict-free when
+//    the row pitch is 2 (mod 4) slots.
+// Within a point every chunk offset is a compile-time immediate, and a walk
+// item only adds a wave-uniform row offset, so LDS addressing costs about one
+// VALU add per item row.
+//
+// Softmax (forward). The exact maximum of a plane's scores is known before any
+// exponential is taken, so the sums are rescaled at most once per key plane (2D
+// grids: never).
+#pragma once
+
+#include "na_common.hpp"
+
+namespace na {
+namespace fast {
+
+constexpr int kTH = 16, kTW = 16;  // tile extent along H and W (T: 1)
+
+struct Geom {
+    int ext[3], ker[3], dil[3];
+    int heads, batch, head_dim;
+    int tiles[3];      // tiles per axis over the largest residue class
+    int nres, n_tiles;
+    int ra, rb;        // LDS row pitch in bytes of the key-major (A) and d-major (B) layouts
+    int rows_off;      // dk/dv: byte offset of the per-point (lse, delta) rows in LDS
+    int rows_pitch;    // dk/dv: points per row of those rows
+};
+
+struct FwdArgs {
+    Geom g;
+    const float *q, *k, *v;
+    float *out, *lse;
+    float qscale;  // scale * log2(e)
+};
+
+struct BwdArgs {
+    Geom g;
+    const float *q, *k, *v, *out, *dout, *lse;
+    float *delta;
+    float *dq, *dk, *dv;
+    float qscale, scale;
+};
+
+// Tile id -> tile. T varies fastest (the tiles of one (H, W) column share two
+// of every three key planes of a 3-plane window, which then hit in L2), then
+// (H, W) in bands of kBand tiles along W, then residue class, head, batch.
+__device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
+    int rem = tile;
+    const int tt = rem % g.tiles[0];
+    rem /= g.tiles[0];
+    const int plane = g.tiles[1] * g.tiles[2];
+    int in = rem % plane;
+    rem /= plane;
+    const int band = in / (kBand * g.tiles[1]);
+    const int bw = imin(kBand, g.tiles[2] - band * kBand);
+    in -= band * kBand * g.tiles[1];
+    const int th = in / bw;
+    const int tw = band * kBand + (in - th * bw);
+    const int res = rem % g.nres;
+    rem /= g.nres;
+    const int head = rem % g.heads;
+    const int b = rem / g.heads;
+    const int o[3] = {tt, th * kTH, tw * kTW};
+    return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, b, head, res, o, w);
+}
+
+// The lane's point and its patch (first point) in the tile, clamped into the
+// grid. Wave v owns the 8 x 8 quarter at (8 (v >> 1), 8 (v & 1)); lane l is
+// entry l % 4 of patch l / 4, patches stacked four along H per quarter wave.
+struct Lane {
+    int f[3], p[3];
+    bool active;
+};
+
+__device__ __forceinline__ Lane lane_geom(const TileCtx &w, int wave, int lane) {
+    const int c = lane & 3, grp = lane >> 2;
+    Lane L;
+    L.f[0] = L.p[0] = w.o[0];
+    L.f[1] = w.o[1] + 8 * (wave >> 1) + 2 * (grp & 3);
+    L.f[2] = w.o[2] + 8 * (wave & 1) + 2 * (grp >> 2);
+    L.p[1] = L.f[1] + (c >> 1);
+    L.p[2] = L.f[2] + (c & 1);
+    L.active = L.p[1] < w.n[1] && L.p[2] < w.n[2];
+#pragma unroll
+    for (int a = 1; a < 3; ++a) {
+        L.f[a] = imin(L.f[a], w.n[a] - 1);
+        L.p[a] = imin(L.p[a], w.n[a] - 1);
+    }
+    return L;
+}
+
+// Copy one plane (class T coordinate tk) of the box [U1, U1 + E1) x [U2, U2 + E2)
+// of src into lds, box row r at byte r * rowb, with direct global-to-LDS loads
+// (16 bytes per lane, 64 consecutive slots per wave instruction). Points past
+// the grid repeat the last grid point; they are only ever read masked.
+// Completion: stage_wait().
+template <int D>
+__device__ __forceinline__ void stage_plane(const float *src, const TileCtx &w, int tk, int U1,
+                                            int E1, int U2, int E2, int rowb, char *lds) {
+    constexpr int PB = D * 4, NC = PB / 16, LNC = log2_of<NC>();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int parts = (E2 * NC + 63) >> 6;
+    const char *plane = reinterpret_cast<const char *>(src) + (w.base + tk * w.st[0]) * 4;
+    for (int part = 0; part < parts; ++part) {
+        const int j = part * 64 + lane;
+        const int col = j >> LNC;
+        if (col >= E2) continue;
+        const int c2 = imin(U2 + col, w.n[2] - 1);
+        const int colb = (int)(c2 * w.st[2]) * 4 + ((j & (NC - 1)) << 4);
+        for (int r = wave; r < E1; r += kWaves) {
+            const int c1 = imin(U1 + r, w.n[1] - 1);
+            const char *rowp = plane + c1 * w.st[1] * 4;
+#if defined(__HIP_DEVICE_COMPILE__)
+            __builtin_amdgcn_global_load_lds(rowp + colb, (lds_void *)(lds + r * rowb + part * 1024),
+                                             16, 0, 0);
+#else
+            (void)rowp;
+            (void)colb;
+#endif
+        }
+    }
+}
+
+// (logsumexp * log2(e), delta) of every point of one box plane, as float2 at
+// rows + (r * pitch + col).
+__device__ __forceinline__ void stage_rows_plane(const float *lse, const float *delta,
+                                                 const TileCtx &w, int tk, int U1, int E1, int U2,
+                                                 int E2, int pitch, float2 *rows) {
+    for (int i = threadIdx.x; i < E1 * E2; i += kThreads) {
+        const int r = i / E2, col = i - r * E2;
+        const int c[3] = {tk, imin(U1 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1)};
+        const int64_t ro = row_off(w, c);
+        rows[r * pitch + col] = make_float2(lse[ro] * kLog2e, delta[ro]);
+    }
+}
+
+// Chunk j (0 .. NC - 1) of a point at LDS byte address base + off.
+__device__ __forceinline__ f4 lds_chunk(const char *base, int off) {
+    return *reinterpret_cast<const f4 *>(base + off);
+}
+
+// acc += sum over the point's D elements of a (from LDS, key-major: this
+// lane's own entry) times b (registers), one 4x4x1 MFMA per element.
+template <int D>
+__device__ __forceinline__ f4 dot_keymajor(const char *pt, const float (&b)[D], f4 acc) {
+    constexpr int NC = D / 4;
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+        const f4 x = lds_chunk(pt, s * 16);
+        acc = mfma4(x[0], b[4 * s + 0], acc);
+        acc = mfma4(x[1], b[4 * s + 1], acc);
+        acc = mfma4(x[2], b[4 * s + 2], acc);
+        acc = mfma4(x[3], b[4 * s + 3], acc);
+    }
+    return acc;
+}
+
+// acc[g] += point[dim(i, g)] * w for the chunks c, c + 4, ... of a point read
+// d-major (pt already offset by c * 16): lane 4b+i supplies dims
+// 4 (i + 4 j) + x as element g = 4 j + x.
+template <int D>
+__device__ __forceinline__ void axpy_dmajor(const char *pt, float wgt, f4 (&acc)[D / 4]) {
+    constexpr int NQ = D / 16;  // chunks per lane
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const f4 x = lds_chunk(pt, j * 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * j + e] = mfma4(x[e], wgt, acc[4 * j + e]);
+    }
+}
+
+// Store a per-lane accumulator (dims as in axpy_dmajor) times mul to the
+// lane's own row.
+template <int D>
+__device__ __forceinline__ void store_row(float *dst, const f4 (&acc)[D / 4], float mul) {
+    constexpr int NQ = D / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const float o[4] = {acc[4 * j][i] * mul, acc[4 * j + 1][i] * mul,
+                                acc[4 * j + 2][i] * mul, acc[4 * j + 3][i] * mul};
+            Io<float>::store4(dst + 4 * (i + 4 * j), o);
+        }
+}
+
+// Whether walk row r (0 .. 2C - 1, relative to the block's walk start) lies
+// in the window of a point whose window starts lo (0 or 1) rows after the walk
+// start: rows 1 .. 2C - 3 always do (k >= 2C - 2 for a walk of C patches).
+template <int C>
+__device__ __forceinline__ bool walk_row_valid(int r, int lo, int k) {
+    if (r >= 1 && r <= 2 * C - 3) return true;
+    return (unsigned)(r - lo) < (unsigned)k;
+}
+
+template <int CH, int CW>
+struct Edge {
+    // validity of this lane's entries in walk rows / columns that can be
+    // outside its window
+    bool h[2 * CH], w[2 * CW];
+};
+
+// ============================================================================
+// Forward.
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int PB = D * 4, G = D / 4;
+    TileCtx w;
+    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3;
+    const Lane L = lane_geom(w, wave, lane);
+
+    int us[3], lo[3], U[3], E[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        us[x] = window_start(L.f[x], w.n[x], w.k[x]);
+        lo[x] = window_start(L.p[x], w.n[x], w.k[x]) - us[x];
+        key_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], &U[x], &E[x]);
+    }
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    Edge<CH, CW> ed;
+#pragma unroll
+    for (int r = 0; r < 2 * CH; ++r) ed.h[r] = walk_row_valid<CH>(r, lo[1], w.k[1]);
+#pragma unroll
+    for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
+
+    const int ra = a.g.ra, rb = a.g.rb;
+    // key-major: this lane supplies entry c of its block's patch
+    const int offA = (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
+    // d-major: this lane supplies chunks c, c + 4, ... of the block's entry
+    const int offB = (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+
+    float qr[D];
+    load_row<float, D>(a.q + elem_off(w, L.p), qr);
+#pragma unroll
+    for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+
+    float m = -1e30f, l = 0.f;
+    f4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nplanes = T3 ? w.k[0] : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tk = t0 + j;
+        if (j > 0) __syncthreads();
+        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_wait();
+
+        // S_b[i][c] = <k_i, q_c>, masked; plane maximum
+        float s[CH][CW][4];
+        float mj = -1e30f;
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            const char *row = smem + offA + 2 * c1 * ra;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, qr, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                    s[c1][c2][e] = ok ? z[e] : -INFINITY;
+                }
+                mj = fmaxf(mj, fmaxf(fmaxf(s[c1][c2][0], s[c1][c2][1]),
+                                     fmaxf(s[c1][c2][2], s[c1][c2][3])));
+            }
+        }
+        if constexpr (T3) {
+            const float mn = fmaxf(m, mj);
+            const float alpha = fast_exp2(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] *= alpha;
+            m = mn;
+        } else {
+            m = mj;
+        }
+        __syncthreads();
+        stage_plane<D>(a.v, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // O_b[i][c] += v_e[dim(i, g)] * P[c][e]
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            const char *row0 = smem + offB + 2 * c1 * rb;
+            const char *row1 = row0 + rb;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[c1][c2][e] - m);
+                l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, p[e], acc);
+            }
+        }
+    }
+
+    if (L.active) {
+        store_row<D>(a.out + elem_off(w, L.p), acc, 1.f / l);
+        a.lse[row_off(w, L.p)] = (m + __log2f(l)) * kLn2;
+    }
+}
+
+// ============================================================================
+// Backward, query side: delta and dq.
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int PB = D * 4, G = D / 4;
+    TileCtx w;
+    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3;
+    const Lane L = lane_geom(w, wave, lane);
+
+    int us[3], lo[3], U[3], E[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        us[x] = window_start(L.f[x], w.n[x], w.k[x]);
+        lo[x] = window_start(L.p[x], w.n[x], w.k[x]) - us[x];
+        key_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], &U[x], &E[x]);
+    }
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    Edge<CH, CW> ed;
+#pragma unroll
+    for (int r = 0; r < 2 * CH; ++r) ed.h[r] = walk_row_valid<CH>(r, lo[1], w.k[1]);
+#pragma unroll
+    for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
+
+    const int ra = a.g.ra, rb = a.g.rb;
+    const int offA = (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
+    const int offB = (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+
+    const int64_t qo = elem_off(w, L.p);
+    const int64_t ro = row_off(w, L.p);
+    float dor[D];
+    load_row<float, D>(a.dout + qo, dor);
+    float delta = 0.f;
+    {
+        float orow[D];
+        load_row<float, D>(a.out + qo, orow);
+#pragma unroll
+        for (int d = 0; d < D; ++d) delta += dor[d] * orow[d];
+    }
+    if (L.active) a.delta[ro] = delta;
+    const float lse2 = a.lse[ro] * kLog2e;
+    float qr[D];
+    if constexpr (T3) {
+        load_row<float, D>(a.q + qo, qr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+    }
+
+    f4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nplanes = T3 ? w.k[0] : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tk = t0 + j;
+        if (j > 0) __syncthreads();
+        stage_plane<D>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_wait();
+
+        // dP_b[i][c] = <v_i, dout_c>
+        float s[CH][CW][4];
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            const char *row = smem + offA + 2 * c1 * ra;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, dor, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[c1][c2][e] = z[e];
+            }
+        }
+        if constexpr (!T3) {
+            load_row<float, D>(a.q + qo, qr);
+#pragma unroll
+            for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+        }
+        __syncthreads();
+        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_wait();
+
+        // P = exp2(S - lse), dS = P (dP - delta)
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            const char *row = smem + offA + 2 * c1 * ra;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, qr, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                    const float p = ok ? fast_exp2(z[e] - lse2) : 0.f;
+                    s[c1][c2][e] = p * (s[c1][c2][e] - delta);
+                }
+            }
+        }
+        __syncthreads();
+        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // dQ_b[i][c] += k_e[dim(i, g)] * dS[c][e]
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            const char *row0 = smem + offB + 2 * c1 * rb;
+            const char *row1 = row0 + rb;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
+                                   acc);
+        }
+    }
+
+    if (L.active) store_row<D>(a.dq + qo, acc, a.scale);
+}
+
+// ============================================================================
+// Backward, key side: dk and dv by inverse-neighborhood gather, without
+// atomics. Tiles whose inverse walk is longer than CH x CW patches (keys near
+// a grid border, where the window shift makes inverse neighborhoods longer)
+// are left to the split kernel.
+__device__ __forceinline__ bool fits_inverse_walk(const TileCtx &w, int ch, int cw) {
+    return tile_inverse_walk(w.o[1], kTH, 2, w.n[1], w.k[1]) <= ch &&
+           tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]) <= cw;
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int PB = D * 4, G = D / 4;
+    TileCtx w;
+    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    if (!fits_inverse_walk(w, CH, CW)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3;
+    const Lane L = lane_geom(w, wave, lane);  // keys
+
+    int lo[3], U[3], E[3], cnt[3];
+    unsigned vm[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        cnt[x] = tile_inverse_walk(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x]);
+        query_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], cnt[x], &U[x], &E[x]);
+        lo[x] = inverse_first(L.f[x], w.n[x], w.k[x]);
+        const int ilo = inverse_first(L.p[x], w.n[x], w.k[x]);
+        vm[x] = bit_range(ilo - lo[x], inverse_last(L.p[x], w.n[x], w.k[x]) - ilo + 1);
+    }
+    const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
+    const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
+
+    const int ra = a.g.ra, rb = a.g.rb;
+    const int offA = (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PB;
+    const int offB = (lo[1] - U[1]) * rb + (lo[2] - U[2]) * PB + c * 16;
+    const int rp = a.g.rows_pitch;
+    const float2 *rows = reinterpret_cast<const float2 *>(smem + a.g.rows_off);
+    const int offR = (lo[1] - U[1] + (c >> 1)) * rp + (lo[2] - U[2] + (c & 1));
+
+    const int64_t ko = elem_off(w, L.p);
+    float kr[D];
+    load_row<float, D>(a.k + ko, kr);
+#pragma unroll
+    for (int d = 0; d < D; ++d) kr[d] *= a.qscale;
+    float vr[D];
+    if constexpr (T3) load_row<float, D>(a.v + ko, vr);
+
+    f4 dk[G], dv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        dk[g] = f4{0.f, 0.f, 0.f, 0.f};
+        dv[g] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nplanes = T3 ? tq1 - tq0 + 1 : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tq = tq0 + j;
+        if (j > 0) __syncthreads();
+        stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,
+                         reinterpret_cast<float2 *>(smem + a.g.rows_off));
+        stage_wait();
+
+        // S_b[i][c] = <q_i, k_c> - lse_i (the lse term as one more MFMA step:
+        // lane 4b+i supplies -lse of its entry, every lane 1); P masked
+        float s[CH][CW][4];
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            if (c1 >= cnt[1]) continue;
+            const char *row = smem + offA + 2 * c1 * ra;
+            const float2 *rrow = rows + offR + 2 * c1 * rp;
+            const unsigned hb = vm[1] >> (2 * c1);
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                if (c2 >= cnt[2]) continue;
+                f4 z = mfma4(-rrow[2 * c2].x, 1.f, f4{0.f, 0.f, 0.f, 0.f});
+                z = dot_keymajor<D>(row + 2 * c2 * PB, kr, z);
+                const unsigned wb = vm[2] >> (2 * c2);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = ((hb >> (e >> 1)) & (wb >> (e & 1)) & 1u) != 0;
+                    s[c1][c2][e] = ok ? fast_exp2(z[e]) : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+        stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // dV_b[i][c] += dout_e[dim(i, g)] * P[c][e]
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            if (c1 >= cnt[1]) continue;
+            const char *row0 = smem + offB + 2 * c1 * rb;
+            const char *row1 = row0 + rb;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                if (c2 >= cnt[2]) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
+                                   dv);
+            }
+        }
+        if constexpr (!T3) load_row<float, D>(a.v + ko, vr);
+        __syncthreads();
+        stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        stage_wait();
+
+        // dP_b[i][c] = <dout_i, v_c> - delta_i;  dS = P dP
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            if (c1 >= cnt[1]) continue;
+            const char *row = smem + offA + 2 * c1 * ra;
+            const float2 *rrow = rows + offR + 2 * c1 * rp;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                if (c2 >= cnt[2]) continue;
+                f4 z = mfma4(-rrow[2 * c2].y, 1.f, f4{0.f, 0.f, 0.f, 0.f});
+                z = dot_keymajor<D>(row + 2 * c2 * PB, vr, z);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[c1][c2][e] *= z[e];
+            }
+        }
+        __syncthreads();
+        stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // dK_b[i][c] += q_e[dim(i, g)] * dS[c][e]
+#pragma unroll
+        for (int c1 = 0; c1 < CH; ++c1) {
+            if (c1 >= cnt[1]) continue;
+            const char *row0 = smem + offB + 2 * c1 * rb;
+            const char *row1 = row0 + rb;
+#pragma unroll
+            for (int c2 = 0; c2 < CW; ++c2) {
+                if (c2 >= cnt[2]) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
+                                   dk);
+            }
+        }
+    }
+
+    if (L.active) {
+        store_row<D>(a.dk + ko, dk, a.scale);
+        store_row<D>(a.dv + ko, dv, 1.f);
+    }
+}
+
+}  // namespace fast
+}  // namespace na

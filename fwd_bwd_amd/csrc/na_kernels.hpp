@@ -54,6 +54,10 @@ struct BwdArgs {
     float *dq_acc;  // KV-parallel variant only
     float qscale;   // scale * log2(e)
     float scale;
+    // dk/dv: when skip_ch > 0, skip the tiles whose 16 x 16 super-tile has an
+    // inverse walk of at most skip_ch x skip_cw patches (the register-resident
+    // dk/dv kernel covers those)
+    int skip_ch, skip_cw;
 };
 
 // Element `i` of a 3-array chosen by value: a runtime index into a small
@@ -173,18 +177,12 @@ __device__ __forceinline__ int entry_mask(const unsigned (&m)[3], const Item &it
     return (int)(col * (row + (row & 2u)));
 }
 
-// Bits [lo, lo + len) set (len >= 0, lo + len <= 32).
-__device__ __forceinline__ unsigned bit_range(int lo, int len) {
-    const unsigned ones = len >= 32 ? 0xffffffffu : ((1u << len) - 1u);
-    return ones << lo;
-}
 
 // Index of the block's patch along W inside the tile; blocks of one quarter
 // wave with odd index visit the entries of a patch in the order e ^ 1 in their
 // d-major reads (this is what makes those reads conflict-free, see swz).
 __device__ __forceinline__ int entry_flip(int lane) { return (lane >> 2) & 1; }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Output of the merged results: thread qd (0..3) of a point writes G = D / 4
 // elements as 16-byte (or, for bf16 D = 16, 8-byte) pieces, piece j at element
@@ -544,6 +542,12 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
     if (!decode_tile(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    if (a.skip_ch > 0) {
+        const int o1 = w.o[1] & ~15, o2 = w.o[2] & ~15;
+        if (tile_inverse_walk(o1, 16, 2, w.n[1], w.k[1]) <= a.skip_ch &&
+            tile_inverse_walk(o2, 16, 2, w.n[2], w.k[2]) <= a.skip_cw)
+            return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 3, flip = entry_flip(lane);
     const LanePoint lp = lane_point(w, lane);  // here: this lane's key

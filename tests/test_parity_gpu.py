@@ -94,6 +94,12 @@ SMALL = [
     ((1, 19, 23, 2, 32), (5, 7), 1, torch.bfloat16),
     ((1, 6, 10, 9, 2, 32), (5, 7, 7), 1, torch.bfloat16),
     ((2, 26, 27, 2, 64), (5, 5), 2, torch.bfloat16),
+    # several 16 x 16 tiles with ragged tails (register-resident kernels; for
+    # k = 9 the tiles at the grid border take the split dk/dv kernel)
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.float32),
+    ((1, 35, 33, 2, 16), (5, 5), (1, 2), torch.float32),
+    ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float32),
+    ((1, 7, 18, 20, 2, 16), (5, 3, 3), (1, 2, 1), torch.float32),
 ]
 
 
