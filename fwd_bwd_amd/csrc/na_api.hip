@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <initializer_list>
+#include <vector>
 
 #include "na.h"
 #include "na_fast.hpp"
@@ -156,48 +157,62 @@ struct FastPlan {
     int lds;
     int c;        // walk length per axis the kernel is compiled for
     bool t3;      // more than one plane along T
-    bool border;  // dk/dv: some tiles need a longer inverse walk (left to the split kernel)
+    int walk_lo;  // dk/dv: the launch takes tiles whose inverse walk lies in (walk_lo, c]
 };
 
-// Smallest compiled walk length >= need (0: none). Grids with several planes
-// along T keep fewer scores per lane (the other operands stay live across the
-// plane loop).
-int fast_walk(int need, bool t3) {
-    const int cmax = t3 ? 4 : 5;
-    for (int c = 2; c <= cmax; ++c)
-        if (c >= need) return c;
-    return 0;
+// Compiled walk lengths: 2 .. 5 patches per axis on single-plane grids, 2 .. 4
+// with several planes along T (the per-lane rows and accumulators stay live
+// across the plane loop there).
+bool fast_walk_compiled(int c, bool t3) { return c >= 2 && c <= (t3 ? 4 : 5); }
+
+// Longest inverse walk (patches) of any 16 x 16 tile of any residue class.
+int max_tile_walk(const Prob &q) {
+    int m = 0;
+    for (int a = 1; a < 3; ++a)
+        for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
+            const int n = na::class_size(q.ext[a], q.dil[a], r);
+            for (int f = 0; f < n; f += 16)
+                m = std::max(m, na::tile_inverse_walk(f, 16, 2, n, q.ker[a]));
+        }
+    return m;
 }
 
-// kind 0: forward / dq (key boxes), 1: dk/dv (query boxes)
-bool fast_plan(const Prob &q, int kind, FastPlan *pl) {
+// The 16 x 16 tiles whose inverse walk exceeds `done`, as border rows and
+// columns (na::Border); false when they are not such a frame (dilation > 1
+// has several residue classes of different sizes: launches then cover every
+// tile and the others exit early).
+bool border_of(const Prob &q, int done, na::Border *bd) {
+    for (int a = 0; a < 3; ++a)
+        if (q.dil[a] != 1) return false;
+    int lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
+    for (int a = 1; a < 3; ++a) {
+        const int n = q.ext[a], T = (n + 15) / 16;
+        std::vector<int> big(T);
+        for (int t = 0; t < T; ++t) big[t] = na::tile_inverse_walk(16 * t, 16, 2, n, q.ker[a]) > done;
+        while (lo[a] < T && big[lo[a]]) ++lo[a];
+        while (hi[a] < T - lo[a] && big[T - 1 - hi[a]]) ++hi[a];
+        for (int t = lo[a]; t < T - hi[a]; ++t)
+            if (big[t]) return false;
+    }
+    const int R = (q.ext[1] + 15) / 16, C = (q.ext[2] + 15) / 16;
+    bd->on = 1;
+    bd->rows_lo = lo[1];
+    bd->rows_hi = hi[1];
+    bd->cols_lo = lo[2];
+    bd->cols_hi = hi[2];
+    const int rb = lo[1] + hi[1], cb = lo[2] + hi[2];
+    bd->per_plane = rb * C + (R - rb) * cb;
+    return true;
+}
+
+// kind 0: forward / dq (walk c = the window walk, exact);
+// kind 1: dk/dv over the tiles whose inverse walk lies in (walk_lo, c].
+bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl) {
     if (q.dtype != NA_F32 || (q.head_dim != 16 && q.head_dim != 32)) return false;
-    const int PB = (int)q.head_dim * 4;
     const bool t3 = q.ext[0] > 1;
-    // walk lengths
-    int need = 0, interior = 0;
-    for (int a = 1; a < 3; ++a) interior = std::max(interior, na::window_walk(q.ker[a], 2));
-    if (kind == 0) {
-        if (na::window_walk(q.ker[1], 2) != na::window_walk(q.ker[2], 2)) return false;
-        need = interior;
-    } else {
-        for (int a = 1; a < 3; ++a)
-            for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
-                const int n = na::class_size(q.ext[a], q.dil[a], r);
-                for (int f = 0; f < n; f += 16)
-                    need = std::max(need, na::tile_inverse_walk(f, 16, 2, n, q.ker[a]));
-            }
-    }
-    int c = fast_walk(need, t3);
-    pl->border = false;
-    if (c == 0 && kind == 1) {
-        // the split kernel takes the border tiles
-        c = fast_walk(interior, t3);
-        pl->border = true;
-    }
-    if (c == 0) return false;
-    if (kind == 0 && c != need) return false;  // the edge masks assume the exact walk
-    // largest plane box per axis over the tiles this kernel runs
+    if (!fast_walk_compiled(c, t3)) return false;
+    const int PB = (int)q.head_dim * 4;
+    // largest plane box per axis over the tiles this launch runs
     int mx[3] = {1, 1, 1};
     for (int a = 1; a < 3; ++a)
         for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
@@ -207,9 +222,8 @@ bool fast_plan(const Prob &q, int kind, FastPlan *pl) {
                 if (kind == 0) {
                     na::key_box(f, 16, 2, n, q.ker[a], &start, &extent);
                 } else {
-                    const int cnt = na::tile_inverse_walk(f, 16, 2, n, q.ker[a]);
-                    if (cnt > c) continue;
-                    na::query_box(f, 16, 2, n, q.ker[a], cnt, &start, &extent);
+                    if (na::tile_inverse_walk(f, 16, 2, n, q.ker[a]) > c) continue;
+                    na::query_box(f, 16, 2, n, q.ker[a], c, &start, &extent);
                 }
                 mx[a] = std::max(mx[a], extent);
             }
@@ -220,6 +234,7 @@ bool fast_plan(const Prob &q, int kind, FastPlan *pl) {
     const int rb = (slots + ((2 - slots % 4) + 4) % 4) * 16;
     int64_t lds = (int64_t)mx[1] * std::max(ra, rb);
     na::fast::Geom &g = pl->g;
+    g = na::fast::Geom{};
     g.rows_off = (int)lds;
     g.rows_pitch = mx[2];
     if (kind == 1) lds += (int64_t)mx[1] * mx[2] * 8;
@@ -247,7 +262,15 @@ bool fast_plan(const Prob &q, int kind, FastPlan *pl) {
     pl->lds = (int)lds;
     pl->c = c;
     pl->t3 = t3;
+    pl->walk_lo = walk_lo;
     return true;
+}
+
+// Forward / dq: the register-resident kernels need a square walk.
+bool fast_plan_fwd(const Prob &q, FastPlan *pl) {
+    const int c = na::window_walk(q.ker[1], 2);
+    if (na::window_walk(q.ker[2], 2) != c) return false;
+    return fast_plan(q, 0, c, 0, pl);
 }
 
 template <typename Kern, typename Args>
@@ -255,7 +278,8 @@ na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t 
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             pl.lds) != hipSuccess)
         return NA_ERR_HIP;
-    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
+    if (a.g.n_tiles == 0) return NA_OK;
+    hipLaunchKernelGGL(kern, dim3(a.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
     return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
 }
 
@@ -284,10 +308,11 @@ na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s)
     return NA_ERR_UNSUPPORTED;
 }
 
-na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
+na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s, bool border) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return launch_fast(na::fast::dkdv_kernel<D, C, C, T3>, pl, a, s);
+        return border ? launch_fast(na::fast::dkdv_border_kernel<D, C, C, T3>, pl, a, s)  \
+                      : launch_fast(na::fast::dkdv_kernel<D, C, C, T3>, pl, a, s);
     NA_FAST_CASES(X)
 #undef X
     return NA_ERR_UNSUPPORTED;
@@ -301,7 +326,7 @@ template <typename T, int D>
 na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
     FastPlan pl;
-    if (fast_plan(pr, 0, &pl)) {
+    if (fast_plan_fwd(pr, &pl)) {
         na::fast::FwdArgs fa{};
         fa.g = pl.g;
         fa.q = static_cast<const float *>(a.q);
@@ -350,7 +375,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
         if (phases & kPhaseDq) {
-            if (fast_plan(pr, 0, &pq)) {
+            if (fast_plan_fwd(pr, &pq)) {
                 fa.g = pq.g;
                 const na_status st = fast_dq(pq, fa, s);
                 if (st != NA_OK) return st;
@@ -365,16 +390,34 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
             }
         }
         if (phases & kPhaseDkdv) {
-            bool split = true;
-            if (fast_plan(pr, 1, &pk)) {
+            // the interior walk c (the window walk) over every tile, then
+            // c + 1 over the border tiles that need more; the split kernel
+            // takes whatever is longer
+            const int need = max_tile_walk(pr);
+            const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
+            int done = 0;  // tiles with inverse walk <= done are covered
+            if (fast_plan(pr, 1, c, 0, &pk)) {
                 fa.g = pk.g;
-                const na_status st = fast_dkdv(pk, fa, s);
+                fa.walk_lo = 0;
+                const na_status st = fast_dkdv(pk, fa, s, false);
                 if (st != NA_OK) return st;
-                split = pk.border;
-                ak.skip_ch = pk.c;  // the split kernel only takes the tiles left over
-                ak.skip_cw = pk.c;
+                done = c;
             }
-            if (split) {
+            if (done > 0 && done < need && fast_plan(pr, 1, c + 1, done, &pk)) {
+                fa.g = pk.g;
+                fa.walk_lo = done;
+                if (border_of(pr, done, &fa.g.border))
+                    fa.g.n_tiles = (int)(pr.batch * pr.heads * fa.g.tiles[0] * fa.g.border.per_plane);
+                const na_status st = fast_dkdv(pk, fa, s, true);
+                if (st != NA_OK) return st;
+                done = c + 1;
+            }
+            if (done < need) {
+                ak.skip_ch = done;  // 0: the split kernel takes every tile
+                ak.skip_cw = done;
+                if (done > 0 && border_of(pr, done, &ak.g.border))
+                    ak.g.n_tiles = (int)(4 * pr.batch * pr.heads * ak.g.tiles[0] *
+                                         ak.g.border.per_plane);
                 auto kern = na::dkdv_kernel<T, D, false>;
                 if (hipFuncSetAttribute((const void *)kern,
                                         hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -123,14 +123,42 @@ constexpr int kTile[3] = {1, 8, 8};
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
+// The 16 x 16 (H, W) tiles near the borders of a dilation-1 grid: tile rows
+// [0, rows_lo) and [R - rows_hi, R), tile columns [0, cols_lo) and
+// [C - cols_hi, C), of R x C tiles per plane. Near a border the window shift
+// makes inverse neighborhoods longer, and only these tiles need the kernels for
+// longer inverse walks; a launch over them enumerates them directly instead of
+// starting (and ending) a workgroup for every tile.
+struct Border {
+    int on;                          // the launch covers the border tiles only
+    int rows_lo, rows_hi, cols_lo, cols_hi;
+    int per_plane;                   // border tiles per (batch, head, T) plane
+};
+
+// Border tile i (0 .. per_plane - 1) of a plane of R x C tiles: (row, col).
+__device__ __forceinline__ void border_tile(const Border &bd, int R, int C, int i, int &r, int &c) {
+    const int rb = bd.rows_lo + bd.rows_hi, cb = bd.cols_lo + bd.cols_hi;
+    if (i < rb * C) {
+        const int rr = i / C;
+        c = i - rr * C;
+        r = rr < bd.rows_lo ? rr : R - bd.rows_hi + (rr - bd.rows_lo);
+    } else {
+        i -= rb * C;
+        const int q = i / cb, cc = i - q * cb;
+        r = bd.rows_lo + q;
+        c = cc < bd.cols_lo ? cc : C - bd.cols_hi + (cc - bd.cols_lo);
+    }
+}
+
 struct Geometry {
     int ext[3], ker[3], dil[3];
     int heads, batch, head_dim;
     int tiles[3];     // tiles per axis, over the largest residue class
     int nres;         // dil[0] * dil[1] * dil[2]
-    int n_tiles;      // batch * heads * nres * tiles[0] * tiles[1] * tiles[2]
+    int n_tiles;      // batch * heads * nres * tiles[0] * tiles[1] * tiles[2] (or the border tiles)
     int chunk_axis;   // axis along which a staged box is split when it exceeds the budget
     int lds_budget;   // bytes of LDS a staged chunk may use
+    Border border;    // when on: the 8 x 8 tiles of the border 16 x 16 tiles only
 };
 
 // Where a workgroup works: batch element, head, residue class, tile origin,
@@ -194,6 +222,21 @@ __device__ __forceinline__ bool fill_ctx(const int (&ext)[3], const int (&ker)[3
 }
 
 __device__ __forceinline__ bool decode_tile(const Geometry &g, int tile, TileCtx &w) {
+    if (g.border.on) {
+        // four 8 x 8 tiles per border 16 x 16 tile, then head, T, batch
+        const int sub = tile & 3;
+        int rem = tile >> 2;
+        const int head = rem % g.heads;
+        rem /= g.heads;
+        const int tt = rem % g.tiles[0];
+        rem /= g.tiles[0];
+        const int R = (g.tiles[1] + 1) >> 1, C = (g.tiles[2] + 1) >> 1;
+        int r, c;
+        border_tile(g.border, R, C, rem % g.border.per_plane, r, c);
+        const int b = rem / g.border.per_plane;
+        const int o[3] = {tt * kTile[0], 16 * r + 8 * (sub >> 1), 16 * c + 8 * (sub & 1)};
+        return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, b, head, 0, o, w);
+    }
     const int plane = g.tiles[1] * g.tiles[2];
     int rem = tile / plane;
     int in = tile - rem * plane;

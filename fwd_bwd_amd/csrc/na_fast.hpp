@@ -52,6 +52,7 @@ struct Geom {
     int ra, rb;        // LDS row pitch in bytes of the key-major (A) and d-major (B) layouts
     int rows_off;      // dk/dv: byte offset of the per-point (lse, delta) rows in LDS
     int rows_pitch;    // dk/dv: points per row of those rows
+    Border border;     // when on: the border tiles only
 };
 
 struct FwdArgs {
@@ -67,27 +68,40 @@ struct BwdArgs {
     float *delta;
     float *dq, *dk, *dv;
     float qscale, scale;
+    int walk_lo;  // dk/dv: this launch takes the tiles whose inverse walk exceeds walk_lo
 };
 
-// Tile id -> tile. T varies fastest (the tiles of one (H, W) column share two
-// of every three key planes of a 3-plane window, which then hit in L2), then
-// (H, W) in bands of kBand tiles along W, then residue class, head, batch.
+// Tile id -> tile. The head varies fastest: consecutive tiles (and so the
+// workgroups one XCD runs at a time) cover all heads of one position, whose
+// rows of one token are adjacent in memory (measured faster than one head at
+// a time over twice as many positions). Then T (the tiles of one (H, W)
+// column share two of every three key planes of a 3-plane window), then (H,
+// W) in bands kFastBand tiles wide along W, residue class, batch.
+constexpr int kFastBand = 8;
+
 __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
     int rem = tile;
+    const int head = rem % g.heads;
+    rem /= g.heads;
     const int tt = rem % g.tiles[0];
     rem /= g.tiles[0];
+    if (g.border.on) {
+        int r, c;
+        border_tile(g.border, g.tiles[1], g.tiles[2], rem % g.border.per_plane, r, c);
+        const int o[3] = {tt, r * kTH, c * kTW};
+        return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, rem / g.border.per_plane, head,
+                        0, o, w);
+    }
     const int plane = g.tiles[1] * g.tiles[2];
     int in = rem % plane;
     rem /= plane;
-    const int band = in / (kBand * g.tiles[1]);
-    const int bw = imin(kBand, g.tiles[2] - band * kBand);
-    in -= band * kBand * g.tiles[1];
+    const int band = in / (kFastBand * g.tiles[1]);
+    const int bw = imin(kFastBand, g.tiles[2] - band * kFastBand);
+    in -= band * kFastBand * g.tiles[1];
     const int th = in / bw;
-    const int tw = band * kBand + (in - th * bw);
+    const int tw = band * kFastBand + (in - th * bw);
     const int res = rem % g.nres;
-    rem /= g.nres;
-    const int head = rem % g.heads;
-    const int b = rem / g.heads;
+    const int b = rem / g.nres;
     const int o[3] = {tt, th * kTH, tw * kTW};
     return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, b, head, res, o, w);
 }
@@ -163,42 +177,139 @@ __device__ __forceinline__ void stage_rows_plane(const float *lse, const float *
     }
 }
 
-// Chunk j (0 .. NC - 1) of a point at LDS byte address base + off.
+// A 16-byte chunk at LDS byte address base + off.
 __device__ __forceinline__ f4 lds_chunk(const char *base, int off) {
     return *reinterpret_cast<const f4 *>(base + off);
 }
 
-// acc += sum over the point's D elements of a (from LDS, key-major: this
-// lane's own entry) times b (registers), one 4x4x1 MFMA per element.
-template <int D>
-__device__ __forceinline__ f4 dot_keymajor(const char *pt, const float (&b)[D], f4 acc) {
-    constexpr int NC = D / 4;
+// Software pipeline over the N items of a fully unrolled walk: the LDS reads
+// of item i + 1 (into register buffer (i + 1) & 1) are issued before the MFMAs
+// of item i, and scheduling barriers keep the compiler from pulling them back
+// next to their uses (it otherwise trades this overlap for registers).
+template <int N, typename Load, typename Compute>
+__device__ __forceinline__ void pipelined(Load &&load, Compute &&compute) {
+    load(0, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (i + 1 < N) load(i + 1, (i + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i, i & 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Keeps the four values of an item in registers at this point: otherwise the
+// compiler may sink their last arithmetic into the next phase and hold its
+// inputs (twice the registers) across the staging in between.
+__device__ __forceinline__ void pin4(float (&x)[4]) {
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+}
+
+// A zero the compiler cannot see through: added to the address of a row that
+// is reloaded inside the plane loop, it keeps the load there instead of
+// hoisting it (and its registers) across the loop.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+// The NC chunks of a point read key-major (this lane's own entry).
+template <int NC>
+__device__ __forceinline__ void load_point(const char *pt, f4 (&x)[NC]) {
+#pragma unroll
+    for (int s = 0; s < NC; ++s) x[s] = lds_chunk(pt, s * 16);
+}
+
+// sum over d of x[d] (this lane's entry) times b[d] (registers), as two
+// independent MFMA chains.
+template <int NC>
+__device__ __forceinline__ f4 dot_chunks(const f4 (&x)[NC], const float (&b)[4 * NC], f4 z0) {
+    f4 z1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NC; ++s) {
-        const f4 x = lds_chunk(pt, s * 16);
-        acc = mfma4(x[0], b[4 * s + 0], acc);
-        acc = mfma4(x[1], b[4 * s + 1], acc);
-        acc = mfma4(x[2], b[4 * s + 2], acc);
-        acc = mfma4(x[3], b[4 * s + 3], acc);
+        z0 = mfma4(x[s][0], b[4 * s + 0], z0);
+        z1 = mfma4(x[s][1], b[4 * s + 1], z1);
+        z0 = mfma4(x[s][2], b[4 * s + 2], z0);
+        z1 = mfma4(x[s][3], b[4 * s + 3], z1);
     }
-    return acc;
+    return z0 + z1;
 }
 
-// acc[g] += point[dim(i, g)] * w for the chunks c, c + 4, ... of a point read
-// d-major (pt already offset by c * 16): lane 4b+i supplies dims
-// 4 (i + 4 j) + x as element g = 4 j + x.
+// Half-item pipelining: step j of a walk covers item j / 2, half j % 2 (half
+// of a point's chunks key-major, or one row of the patch d-major), so the
+// register buffer of the next step holds half an item.
+template <int NH>
+__device__ __forceinline__ void load_chunks(const char *pt, f4 (&x)[NH]) {
+#pragma unroll
+    for (int s = 0; s < NH; ++s) x[s] = lds_chunk(pt, s * 16);
+}
+
+// z0, z1 += the chunks x (elements from chunk c0 on) times b, as two chains.
+template <int NH, int N>
+__device__ __forceinline__ void dot_half(const f4 (&x)[NH], const float (&b)[N], int c0, f4 &z0,
+                                         f4 &z1) {
+#pragma unroll
+    for (int s = 0; s < NH; ++s) {
+        const int d = 4 * (c0 + s);
+        z0 = mfma4(x[s][0], b[d + 0], z0);
+        z1 = mfma4(x[s][1], b[d + 1], z1);
+        z0 = mfma4(x[s][2], b[d + 2], z0);
+        z1 = mfma4(x[s][3], b[d + 3], z1);
+    }
+}
+
+// One row (entries 2h, 2h + 1) of a patch read d-major.
 template <int D>
-__device__ __forceinline__ void axpy_dmajor(const char *pt, float wgt, f4 (&acc)[D / 4]) {
-    constexpr int NQ = D / 16;  // chunks per lane
+__device__ __forceinline__ void load_row_dmajor(const char *row, int col, f4 (&x)[2][D / 16]) {
+    constexpr int PB = D * 4;
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        const f4 x = lds_chunk(pt, j * 64);
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * j + e] = mfma4(x[e], wgt, acc[4 * j + e]);
-    }
+        for (int j = 0; j < D / 16; ++j) x[e][j] = lds_chunk(row + col + e * PB, j * 64);
 }
 
-// Store a per-lane accumulator (dims as in axpy_dmajor) times mul to the
+// acc[g] += entry[dim(i, g)] * w[e] over the two entries of a patch row.
+template <int D>
+__device__ __forceinline__ void axpy_row(const f4 (&x)[2][D / 16], float w0, float w1,
+                                         f4 (&acc)[D / 4]) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[4 * j + t] = mfma4(x[0][j][t], w0, acc[4 * j + t]);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[4 * j + t] = mfma4(x[1][j][t], w1, acc[4 * j + t]);
+}
+
+// The chunks c, c + 4, ... of the four entries of a patch read d-major: entry
+// e at row (e >> 1 ? row1 : row0), column offset col + (e & 1) * PB.
+template <int D>
+__device__ __forceinline__ void load_patch_dmajor(const char *row0, const char *row1, int col,
+                                                  f4 (&x)[4][D / 16]) {
+    constexpr int PB = D * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+            x[e][j] = lds_chunk((e >> 1 ? row1 : row0) + col + (e & 1) * PB, j * 64);
+}
+
+// acc[g] += entry_e[dim(i, g)] * w[e] over the four entries: lane 4b+i
+// supplies dims 4 (i + 4 j) + x as element g = 4 j + x.
+template <int D>
+__device__ __forceinline__ void axpy_patch(const f4 (&x)[4][D / 16], const float (&w)[4],
+                                           f4 (&acc)[D / 4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[4 * j + t] = mfma4(x[e][j][t], w[e], acc[4 * j + t]);
+}
+
+// Store a per-lane accumulator (dims as in axpy_patch) times mul to the
 // lane's own row.
 template <int D>
 __device__ __forceinline__ void store_row(float *dst, const f4 (&acc)[D / 4], float mul) {
@@ -232,11 +343,10 @@ struct Edge {
 // ============================================================================
 // Forward.
 template <int D, int CH, int CW, bool T3>
-__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int PB = D * 4, G = D / 4;
+__device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem) {
+    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
-    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    if (!decode(a.g, tile, w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 3;
     const Lane L = lane_geom(w, wave, lane);
@@ -257,15 +367,11 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
 
     const int ra = a.g.ra, rb = a.g.rb;
     // key-major: this lane supplies entry c of its block's patch
-    const int offA = (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
-    // d-major: this lane supplies chunks c, c + 4, ... of the block's entry
-    const int offB = (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
+    // d-major: this lane supplies chunks c, c + 4, ... of the block's entries
+    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
 
-    float qr[D];
-    load_row<float, D>(a.q + elem_off(w, L.p), qr);
-#pragma unroll
-    for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
-
+    const int64_t qo = elem_off(w, L.p);
     float m = -1e30f, l = 0.f;
     f4 acc[G];
 #pragma unroll
@@ -276,25 +382,38 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
         stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        float qr[D];
+        load_row<float, D>(a.q + qo + opaque_zero(), qr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
         stage_wait();
 
         // S_b[i][c] = <k_i, q_c>, masked; plane maximum
-        float s[CH][CW][4];
+        float s[NI][4];
         float mj = -1e30f;
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                                            (j & 1) * (NC / 2) * 16, kb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, c1 = i / CW, c2 = i % CW;
+                    if ((j & 1) == 0) z0 = z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    dot_half<NC / 2>(kb[b], qr, (j & 1) * (NC / 2), z0, z1);
+                    if ((j & 1) == 0) return;
+                    const f4 z = z0 + z1;
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            const char *row = smem + offA + 2 * c1 * ra;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, qr, f4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
-                    s[c1][c2][e] = ok ? z[e] : -INFINITY;
-                }
-                mj = fmaxf(mj, fmaxf(fmaxf(s[c1][c2][0], s[c1][c2][1]),
-                                     fmaxf(s[c1][c2][2], s[c1][c2][3])));
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        s[i][e] = ok ? z[e] : -INFINITY;
+                    }
+                    mj = fmaxf(mj, fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3])));
+                    pin4(s[i]);
+                    asm volatile("" : "+v"(mj));
+                });
         }
         if constexpr (T3) {
             const float mn = fmaxf(m, mj);
@@ -311,25 +430,29 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
         stage_wait();
 
         // O_b[i][c] += v_e[dim(i, g)] * P[c][e]
+        {
+            f4 vb[2][2][D / 16];
+            float p[4];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                                       vb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, h = j & 1;
+                    if (h == 0) {
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            const char *row0 = smem + offB + 2 * c1 * rb;
-            const char *row1 = row0 + rb;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[c1][c2][e] - m);
-                l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, p[e], acc);
-            }
+                        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[i][e] - m);
+                        l += (p[0] + p[1]) + (p[2] + p[3]);
+                    }
+                    axpy_row<D>(vb[b], p[2 * h], p[2 * h + 1], acc);
+                });
         }
     }
 
     if (L.active) {
-        store_row<D>(a.out + elem_off(w, L.p), acc, 1.f / l);
+        store_row<D>(a.out + qo, acc, 1.f / l);
         a.lse[row_off(w, L.p)] = (m + __log2f(l)) * kLn2;
     }
 }
@@ -337,11 +460,10 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
 // ============================================================================
 // Backward, query side: delta and dq.
 template <int D, int CH, int CW, bool T3>
-__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int PB = D * 4, G = D / 4;
+__device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) {
+    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
-    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    if (!decode(a.g, tile, w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 3;
     const Lane L = lane_geom(w, wave, lane);
@@ -361,28 +483,21 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
 
     const int ra = a.g.ra, rb = a.g.rb;
-    const int offA = (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
-    const int offB = (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
+    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
 
     const int64_t qo = elem_off(w, L.p);
     const int64_t ro = row_off(w, L.p);
-    float dor[D];
-    load_row<float, D>(a.dout + qo, dor);
     float delta = 0.f;
     {
-        float orow[D];
+        float dor[D], orow[D];
+        load_row<float, D>(a.dout + qo, dor);
         load_row<float, D>(a.out + qo, orow);
 #pragma unroll
         for (int d = 0; d < D; ++d) delta += dor[d] * orow[d];
     }
     if (L.active) a.delta[ro] = delta;
     const float lse2 = a.lse[ro] * kLog2e;
-    float qr[D];
-    if constexpr (T3) {
-        load_row<float, D>(a.q + qo, qr);
-#pragma unroll
-        for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
-    }
 
     f4 acc[G];
 #pragma unroll
@@ -393,59 +508,80 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
         stage_plane<D>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        float dor[D];
+        load_row<float, D>(a.dout + qo + opaque_zero(), dor);
         stage_wait();
 
         // dP_b[i][c] = <v_i, dout_c>
-        float s[CH][CW][4];
+        float s[NI][4];
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                                            (j & 1) * (NC / 2) * 16, kb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    if ((j & 1) == 0) z0 = z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    dot_half<NC / 2>(kb[b], dor, (j & 1) * (NC / 2), z0, z1);
+                    if ((j & 1) == 0) return;
+                    const f4 z = z0 + z1;
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            const char *row = smem + offA + 2 * c1 * ra;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, dor, f4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[c1][c2][e] = z[e];
-            }
-        }
-        if constexpr (!T3) {
-            load_row<float, D>(a.q + qo, qr);
-#pragma unroll
-            for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+                    for (int e = 0; e < 4; ++e) s[i][e] = z[e];
+                    pin4(s[i]);
+                });
         }
         __syncthreads();
         stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        float qr[D];
+        load_row<float, D>(a.q + qo + opaque_zero(), qr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
         stage_wait();
 
         // P = exp2(S - lse), dS = P (dP - delta)
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                                            (j & 1) * (NC / 2) * 16, kb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, c1 = i / CW, c2 = i % CW;
+                    if ((j & 1) == 0) z0 = z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    dot_half<NC / 2>(kb[b], qr, (j & 1) * (NC / 2), z0, z1);
+                    if ((j & 1) == 0) return;
+                    const f4 z = z0 + z1;
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            const char *row = smem + offA + 2 * c1 * ra;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                const f4 z = dot_keymajor<D>(row + 2 * c2 * PB, qr, f4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
-                    const float p = ok ? fast_exp2(z[e] - lse2) : 0.f;
-                    s[c1][c2][e] = p * (s[c1][c2][e] - delta);
-                }
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        const float p = ok ? fast_exp2(z[e] - lse2) : 0.f;
+                        s[i][e] = p * (s[i][e] - delta);
+                    }
+                    pin4(s[i]);
+                });
         }
         __syncthreads();
         stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dQ_b[i][c] += k_e[dim(i, g)] * dS[c][e]
-#pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            const char *row0 = smem + offB + 2 * c1 * rb;
-            const char *row1 = row0 + rb;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
-                                   acc);
+        {
+            f4 vb[2][2][D / 16];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                                       vb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, h = j & 1;
+                    axpy_row<D>(vb[b], s[i][2 * h], s[i][2 * h + 1], acc);
+                });
         }
     }
 
@@ -454,31 +590,35 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
 
 // ============================================================================
 // Backward, key side: dk and dv by inverse-neighborhood gather, without
-// atomics. Tiles whose inverse walk is longer than CH x CW patches (keys near
-// a grid border, where the window shift makes inverse neighborhoods longer)
-// are left to the split kernel.
-__device__ __forceinline__ bool fits_inverse_walk(const TileCtx &w, int ch, int cw) {
-    return tile_inverse_walk(w.o[1], kTH, 2, w.n[1], w.k[1]) <= ch &&
-           tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]) <= cw;
+// atomics. Every block walks CH x CW query patches; entries outside a key's
+// inverse window are masked, and the staged box covers the whole walk of
+// every block (points past the grid repeat real data), so masked reads are
+// always finite. Near a grid border the window shift makes inverse
+// neighborhoods longer: a launch takes the tiles whose longest inverse walk
+// lies in (walk_lo, C]; longer ones are left to another launch.
+__device__ __forceinline__ int tile_walk(const TileCtx &w) {
+    return imax(tile_inverse_walk(w.o[1], kTH, 2, w.n[1], w.k[1]),
+                tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]));
 }
 
 template <int D, int CH, int CW, bool T3>
-__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int PB = D * 4, G = D / 4;
+__device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem) {
+    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
-    if (!decode(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
-    if (!fits_inverse_walk(w, CH, CW)) return;
+    if (!decode(a.g, tile, w)) return;
+    {
+        const int tw = tile_walk(w);
+        if (tw <= a.walk_lo || tw > (CH > CW ? CH : CW)) return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 3;
     const Lane L = lane_geom(w, wave, lane);  // keys
 
-    int lo[3], U[3], E[3], cnt[3];
+    int lo[3], U[3], E[3];
     unsigned vm[3];
 #pragma unroll
     for (int x = 1; x < 3; ++x) {
-        cnt[x] = tile_inverse_walk(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x]);
-        query_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], cnt[x], &U[x], &E[x]);
+        query_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], x == 1 ? CH : CW, &U[x], &E[x]);
         lo[x] = inverse_first(L.f[x], w.n[x], w.k[x]);
         const int ilo = inverse_first(L.p[x], w.n[x], w.k[x]);
         vm[x] = bit_range(ilo - lo[x], inverse_last(L.p[x], w.n[x], w.k[x]) - ilo + 1);
@@ -487,19 +627,13 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
     const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
 
     const int ra = a.g.ra, rb = a.g.rb;
-    const int offA = (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PB;
-    const int offB = (lo[1] - U[1]) * rb + (lo[2] - U[2]) * PB + c * 16;
+    const char *baseA = smem + (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PB;
+    const char *baseB = smem + (lo[1] - U[1]) * rb + (lo[2] - U[2]) * PB + c * 16;
     const int rp = a.g.rows_pitch;
-    const float2 *rows = reinterpret_cast<const float2 *>(smem + a.g.rows_off);
-    const int offR = (lo[1] - U[1] + (c >> 1)) * rp + (lo[2] - U[2] + (c & 1));
+    const float2 *baseR = reinterpret_cast<const float2 *>(smem + a.g.rows_off) +
+                          (lo[1] - U[1] + (c >> 1)) * rp + (lo[2] - U[2] + (c & 1));
 
     const int64_t ko = elem_off(w, L.p);
-    float kr[D];
-    load_row<float, D>(a.k + ko, kr);
-#pragma unroll
-    for (int d = 0; d < D; ++d) kr[d] *= a.qscale;
-    float vr[D];
-    if constexpr (T3) load_row<float, D>(a.v + ko, vr);
 
     f4 dk[G], dv[G];
 #pragma unroll
@@ -515,94 +649,147 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
         stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,
                          reinterpret_cast<float2 *>(smem + a.g.rows_off));
+        float kr[D];
+        load_row<float, D>(a.k + ko + opaque_zero(), kr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) kr[d] *= a.qscale;
         stage_wait();
 
-        // S_b[i][c] = <q_i, k_c> - lse_i (the lse term as one more MFMA step:
-        // lane 4b+i supplies -lse of its entry, every lane 1); P masked
-        float s[CH][CW][4];
+        // S_b[i][c] = <q_i, k_c> - lse_i (the lse term is one more MFMA step:
+        // lane 4b+i supplies -lse of its entry, every lane 1); P, masked
+        float s[NI][4];
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            float lr[2];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                                            (j & 1) * (NC / 2) * 16, kb[b]);
+                    if ((j & 1) == 0) lr[b] = baseR[2 * (i / CW) * rp + 2 * (i % CW)].x;
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, c1 = i / CW, c2 = i % CW;
+                    if ((j & 1) == 0) {
+                        z0 = mfma4(-lr[b], 1.f, f4{0.f, 0.f, 0.f, 0.f});
+                        z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    dot_half<NC / 2>(kb[b], kr, (j & 1) * (NC / 2), z0, z1);
+                    if ((j & 1) == 0) return;
+                    const f4 z = z0 + z1;
+                    const unsigned hb = vm[1] >> (2 * c1), wb = vm[2] >> (2 * c2);
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            if (c1 >= cnt[1]) continue;
-            const char *row = smem + offA + 2 * c1 * ra;
-            const float2 *rrow = rows + offR + 2 * c1 * rp;
-            const unsigned hb = vm[1] >> (2 * c1);
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                if (c2 >= cnt[2]) continue;
-                f4 z = mfma4(-rrow[2 * c2].x, 1.f, f4{0.f, 0.f, 0.f, 0.f});
-                z = dot_keymajor<D>(row + 2 * c2 * PB, kr, z);
-                const unsigned wb = vm[2] >> (2 * c2);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = ((hb >> (e >> 1)) & (wb >> (e & 1)) & 1u) != 0;
-                    s[c1][c2][e] = ok ? fast_exp2(z[e]) : 0.f;
-                }
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = ((hb >> (e >> 1)) & (wb >> (e & 1)) & 1u) != 0;
+                        s[i][e] = ok ? fast_exp2(z[e]) : 0.f;
+                    }
+                    pin4(s[i]);
+                });
         }
         __syncthreads();
         stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dV_b[i][c] += dout_e[dim(i, g)] * P[c][e]
-#pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            if (c1 >= cnt[1]) continue;
-            const char *row0 = smem + offB + 2 * c1 * rb;
-            const char *row1 = row0 + rb;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                if (c2 >= cnt[2]) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
-                                   dv);
-            }
+        {
+            f4 vb[2][2][D / 16];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                                       vb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, h = j & 1;
+                    axpy_row<D>(vb[b], s[i][2 * h], s[i][2 * h + 1], dv);
+                });
         }
-        if constexpr (!T3) load_row<float, D>(a.v + ko, vr);
+        // one plane: dv is final here; storing it now frees its registers
+        if constexpr (!T3)
+            if (L.active) store_row<D>(a.dv + ko, dv, 1.f);
         __syncthreads();
         stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        float vr[D];
+        load_row<float, D>(a.v + ko + opaque_zero(), vr);
         stage_wait();
 
         // dP_b[i][c] = <dout_i, v_c> - delta_i;  dS = P dP
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            float dr[2];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                                            (j & 1) * (NC / 2) * 16, kb[b]);
+                    if ((j & 1) == 0) dr[b] = baseR[2 * (i / CW) * rp + 2 * (i % CW)].y;
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    if ((j & 1) == 0) {
+                        z0 = mfma4(-dr[b], 1.f, f4{0.f, 0.f, 0.f, 0.f});
+                        z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    dot_half<NC / 2>(kb[b], vr, (j & 1) * (NC / 2), z0, z1);
+                    if ((j & 1) == 0) return;
+                    const f4 z = z0 + z1;
 #pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            if (c1 >= cnt[1]) continue;
-            const char *row = smem + offA + 2 * c1 * ra;
-            const float2 *rrow = rows + offR + 2 * c1 * rp;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                if (c2 >= cnt[2]) continue;
-                f4 z = mfma4(-rrow[2 * c2].y, 1.f, f4{0.f, 0.f, 0.f, 0.f});
-                z = dot_keymajor<D>(row + 2 * c2 * PB, vr, z);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[c1][c2][e] *= z[e];
-            }
+                    for (int e = 0; e < 4; ++e) s[i][e] *= z[e];
+                    pin4(s[i]);
+                });
         }
         __syncthreads();
         stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dK_b[i][c] += q_e[dim(i, g)] * dS[c][e]
-#pragma unroll
-        for (int c1 = 0; c1 < CH; ++c1) {
-            if (c1 >= cnt[1]) continue;
-            const char *row0 = smem + offB + 2 * c1 * rb;
-            const char *row1 = row0 + rb;
-#pragma unroll
-            for (int c2 = 0; c2 < CW; ++c2) {
-                if (c2 >= cnt[2]) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    axpy_dmajor<D>((e >> 1 ? row1 : row0) + (2 * c2 + (e & 1)) * PB, s[c1][c2][e],
-                                   dk);
-            }
+        {
+            f4 vb[2][2][D / 16];
+            pipelined<2 * NI>(
+                [&](int j, int b) {
+                    const int i = j >> 1;
+                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                                       vb[b]);
+                },
+                [&](int j, int b) {
+                    const int i = j >> 1, h = j & 1;
+                    axpy_row<D>(vb[b], s[i][2 * h], s[i][2 * h + 1], dk);
+                });
         }
     }
 
     if (L.active) {
         store_row<D>(a.dk + ko, dk, a.scale);
-        store_row<D>(a.dv + ko, dv, 1.f);
+        if constexpr (T3) store_row<D>(a.dv + ko, dv, 1.f);
     }
+}
+
+// ============================================================================
+// Kernels: one workgroup per tile.
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    fwd_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    dq_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    dkdv_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+// The same for the few border tiles with a longer walk: one workgroup per CU,
+// so that the longer walk never spills registers.
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 1) dkdv_border_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    dkdv_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 }  // namespace fast
