@@ -157,6 +157,7 @@ struct FastPlan {
     int lds;
     int c;        // walk length per axis the kernel is compiled for
     bool t3;      // more than one plane along T
+    bool pad;     // dq, dk/dv: padded points, one staging per tensor serves both read patterns
     int walk_lo;  // dk/dv: the launch takes tiles whose inverse walk lies in (walk_lo, c]
 };
 
@@ -164,6 +165,13 @@ struct FastPlan {
 // with several planes along T (the per-lane rows and accumulators stay live
 // across the plane loop there).
 bool fast_walk_compiled(int c, bool t3) { return c >= 2 && c <= (t3 ? 4 : 5); }
+
+// Border-only dk/dv kernels for longer walks, one workgroup per CU (single
+// plane grids, head_dim 32): the whole LDS and register file of a CU.
+constexpr int kBorderLdsMax = 160 * 1024;
+bool border_walk_compiled(int c, bool t3, int head_dim) {
+    return !t3 && head_dim == 32 && (c == 6 || c == 7);
+}
 
 // Longest inverse walk (patches) of any 16 x 16 tile of any residue class.
 int max_tile_walk(const Prob &q) {
@@ -205,13 +213,34 @@ bool border_of(const Prob &q, int done, na::Border *bd) {
     return true;
 }
 
+// Divisors of the fast tile decode (na::fast::decode), from the geometry and
+// the border set; call again after changing either.
+void set_divisors(na::fast::Geom &g) {
+    const int band = na::fast::kFastBand, last = g.tiles[2] % band;
+    g.f_heads = na::make_fastdiv(g.heads);
+    g.f_t = na::make_fastdiv(g.tiles[0]);
+    g.f_plane = na::make_fastdiv(g.border.on ? g.border.per_plane : g.tiles[1] * g.tiles[2]);
+    g.f_bandrows = na::make_fastdiv(band * g.tiles[1]);
+    g.f_band = na::make_fastdiv(band);
+    g.f_lastband = na::make_fastdiv(last ? last : band);
+    g.f_nres = na::make_fastdiv(g.nres);
+    g.f_c = na::make_fastdiv(g.tiles[2]);
+    g.f_cb = na::make_fastdiv(std::max(1, g.border.cols_lo + g.border.cols_hi));
+    for (int a = 0; a < 3; ++a) g.f_dil[a] = na::make_fastdiv(g.dil[a]);
+    g.f_dil21 = na::make_fastdiv(g.dil[2] * g.dil[1]);
+}
+
 // kind 0: forward / dq (walk c = the window walk, exact);
 // kind 1: dk/dv over the tiles whose inverse walk lies in (walk_lo, c].
-bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl) {
+// pad: points one 16-byte slot apart (see dq_tile), for grids with several
+// planes along T, whose plane boxes leave room for it.
+bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false) {
     if (q.dtype != NA_F32 || (q.head_dim != 16 && q.head_dim != 32)) return false;
     const bool t3 = q.ext[0] > 1;
-    if (!fast_walk_compiled(c, t3)) return false;
-    const int PB = (int)q.head_dim * 4;
+    const bool wide = kind == 1 && border_walk_compiled(c, t3, (int)q.head_dim);
+    if (!fast_walk_compiled(c, t3) && !wide) return false;
+    if (pad && !t3) return false;
+    const int PB = (int)q.head_dim * 4 + (pad ? 16 : 0);
     // largest plane box per axis over the tiles this launch runs
     int mx[3] = {1, 1, 1};
     for (int a = 1; a < 3; ++a)
@@ -228,17 +257,18 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl) {
                 mx[a] = std::max(mx[a], extent);
             }
         }
-    // row pitches: an odd number of 16-byte slots (A), 2 mod 4 slots (B)
+    // row pitches: an odd number of 16-byte slots (A), 2 mod 4 slots (B; both
+    // patterns when padded)
     const int slots = mx[2] * PB / 16;
-    const int ra = (slots | 1) * 16;
     const int rb = (slots + ((2 - slots % 4) + 4) % 4) * 16;
+    const int ra = pad ? rb : (slots | 1) * 16;
     int64_t lds = (int64_t)mx[1] * std::max(ra, rb);
     na::fast::Geom &g = pl->g;
     g = na::fast::Geom{};
     g.rows_off = (int)lds;
     g.rows_pitch = mx[2];
     if (kind == 1) lds += (int64_t)mx[1] * mx[2] * 8;
-    if (lds > kFastLdsMax) return false;
+    if (lds > (wide ? kBorderLdsMax : kFastLdsMax)) return false;
     int64_t n_tiles = q.batch * q.heads;
     int nres = 1;
     for (int a = 0; a < 3; ++a) {
@@ -259,18 +289,21 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl) {
     g.n_tiles = (int)n_tiles;
     g.ra = ra;
     g.rb = rb;
+    set_divisors(g);
     pl->lds = (int)lds;
     pl->c = c;
     pl->t3 = t3;
+    pl->pad = pad;
     pl->walk_lo = walk_lo;
     return true;
 }
 
-// Forward / dq: the register-resident kernels need a square walk.
-bool fast_plan_fwd(const Prob &q, FastPlan *pl) {
+// Forward / dq: the register-resident kernels need a square walk. dq takes
+// the padded layout where it fits.
+bool fast_plan_fwd(const Prob &q, FastPlan *pl, bool try_pad = false) {
     const int c = na::window_walk(q.ker[1], 2);
     if (na::window_walk(q.ker[2], 2) != c) return false;
-    return fast_plan(q, 0, c, 0, pl);
+    return (try_pad && fast_plan(q, 0, c, 0, pl, true)) || fast_plan(q, 0, c, 0, pl);
 }
 
 template <typename Kern, typename Args>
@@ -302,18 +335,24 @@ na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgs &a, hipStream_t s
 na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return launch_fast(na::fast::dq_kernel<D, C, C, T3>, pl, a, s);
+        return pl.pad ? launch_fast(na::fast::dq_kernel<D, C, C, T3, T3>, pl, a, s)       \
+                      : launch_fast(na::fast::dq_kernel<D, C, C, T3, false>, pl, a, s);
     NA_FAST_CASES(X)
 #undef X
     return NA_ERR_UNSUPPORTED;
 }
 
-na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s, bool border) {
+na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return border ? launch_fast(na::fast::dkdv_border_kernel<D, C, C, T3>, pl, a, s)  \
-                      : launch_fast(na::fast::dkdv_kernel<D, C, C, T3>, pl, a, s);
+        return pl.pad ? launch_fast(na::fast::dkdv_kernel<D, C, C, T3, T3>, pl, a, s)     \
+                      : launch_fast(na::fast::dkdv_kernel<D, C, C, T3, false>, pl, a, s);
     NA_FAST_CASES(X)
+#undef X
+#define X(D, C)                                                                          \
+    if (a.g.head_dim == D && pl.c == C && !pl.t3)                                        \
+        return launch_fast(na::fast::dkdv_border_kernel<D, C, C, false>, pl, a, s);
+    X(32, 6) X(32, 7)
 #undef X
     return NA_ERR_UNSUPPORTED;
 }
@@ -375,7 +414,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
         if (phases & kPhaseDq) {
-            if (fast_plan_fwd(pr, &pq)) {
+            if (fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;
                 const na_status st = fast_dq(pq, fa, s);
                 if (st != NA_OK) return st;
@@ -390,27 +429,31 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
             }
         }
         if (phases & kPhaseDkdv) {
-            // the interior walk c (the window walk) over every tile, then
-            // c + 1 over the border tiles that need more; the split kernel
-            // takes whatever is longer
+            // the interior walk c (the window walk) over every tile, then the
+            // shortest compiled longer walk over the border tiles that need
+            // more; the split kernel takes whatever is left
             const int need = max_tile_walk(pr);
             const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
             int done = 0;  // tiles with inverse walk <= done are covered
-            if (fast_plan(pr, 1, c, 0, &pk)) {
+            if (fast_plan(pr, 1, c, 0, &pk, true) || fast_plan(pr, 1, c, 0, &pk)) {
                 fa.g = pk.g;
                 fa.walk_lo = 0;
-                const na_status st = fast_dkdv(pk, fa, s, false);
+                const na_status st = fast_dkdv(pk, fa, s);
                 if (st != NA_OK) return st;
                 done = c;
             }
-            if (done > 0 && done < need && fast_plan(pr, 1, c + 1, done, &pk)) {
+            for (int cb = c + 1; done > 0 && done < need && cb <= need; ++cb) {
+                if (!fast_plan(pr, 1, cb, done, &pk, true) && !fast_plan(pr, 1, cb, done, &pk))
+                    continue;
                 fa.g = pk.g;
                 fa.walk_lo = done;
-                if (border_of(pr, done, &fa.g.border))
+                if (border_of(pr, done, &fa.g.border)) {
                     fa.g.n_tiles = (int)(pr.batch * pr.heads * fa.g.tiles[0] * fa.g.border.per_plane);
-                const na_status st = fast_dkdv(pk, fa, s, true);
+                    set_divisors(fa.g);
+                }
+                const na_status st = fast_dkdv(pk, fa, s);
                 if (st != NA_OK) return st;
-                done = c + 1;
+                done = cb;
             }
             if (done < need) {
                 ak.skip_ch = done;  // 0: the split kernel takes every tile

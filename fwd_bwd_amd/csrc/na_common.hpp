@@ -112,6 +112,27 @@ __device__ __forceinline__ unsigned bit_range(int lo, int len) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
+// Division by a launch constant: m = ceil(2^32 / d) makes floor(n * m / 2^32)
+// either floor(n / d) or one more (for 0 <= n < 2^31), which one comparison
+// corrects; a few scalar instructions instead of a full integer division.
+struct FastDiv {
+    uint32_t d, m;  // m = 0: d = 1
+};
+
+NA_HD FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.m = d <= 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d);
+    return f;
+}
+
+__device__ __forceinline__ int fdiv(int n, const FastDiv &f) {
+    if (f.m == 0) return n;
+    const uint32_t q = __umulhi((uint32_t)n, f.m);
+    return (int)(q - (q * f.d > (uint32_t)n));
+}
+
+// ----------------------------------------------------------------------------
 // Tiles. Axis 0 is T (1 for 2D problems), axis 1 is H, axis 2 is W, all in
 // class coordinates of one residue class (dilation). A workgroup of kWaves
 // waves owns a tile of 1 x 8 x 8 points (64: one per lane), split into sixteen

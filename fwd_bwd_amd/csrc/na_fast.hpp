@@ -53,6 +53,9 @@ struct Geom {
     int rows_off;      // dk/dv: byte offset of the per-point (lse, delta) rows in LDS
     int rows_pitch;    // dk/dv: points per row of those rows
     Border border;     // when on: the border tiles only
+    // divisors of the tile decode
+    FastDiv f_heads, f_t, f_plane, f_bandrows, f_band, f_lastband, f_nres, f_c, f_cb;
+    FastDiv f_dil[3], f_dil21;
 };
 
 struct FwdArgs {
@@ -80,30 +83,73 @@ struct BwdArgs {
 constexpr int kFastBand = 8;
 
 __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
-    int rem = tile;
-    const int head = rem % g.heads;
-    rem /= g.heads;
-    const int tt = rem % g.tiles[0];
-    rem /= g.tiles[0];
+    int rem = tile, q;
+    q = fdiv(rem, g.f_heads);
+    const int head = rem - q * g.heads;
+    rem = q;
+    q = fdiv(rem, g.f_t);
+    const int tt = rem - q * g.tiles[0];
+    rem = q;
+    int th, tw, res = 0;
     if (g.border.on) {
-        int r, c;
-        border_tile(g.border, g.tiles[1], g.tiles[2], rem % g.border.per_plane, r, c);
-        const int o[3] = {tt, r * kTH, c * kTW};
-        return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, rem / g.border.per_plane, head,
-                        0, o, w);
+        q = fdiv(rem, g.f_plane);  // f_plane: border tiles per plane here
+        int i = rem - q * g.border.per_plane;
+        rem = q;
+        const int rb = g.border.rows_lo + g.border.rows_hi;
+        if (i < rb * g.tiles[2]) {
+            const int rr = fdiv(i, g.f_c);
+            tw = i - rr * g.tiles[2];
+            th = rr < g.border.rows_lo ? rr : g.tiles[1] - g.border.rows_hi + (rr - g.border.rows_lo);
+        } else {
+            i -= rb * g.tiles[2];
+            const int cb = g.border.cols_lo + g.border.cols_hi;
+            const int qq = fdiv(i, g.f_cb), cc = i - qq * cb;
+            th = g.border.rows_lo + qq;
+            tw = cc < g.border.cols_lo ? cc : g.tiles[2] - g.border.cols_hi + (cc - g.border.cols_lo);
+        }
+    } else {
+        q = fdiv(rem, g.f_plane);
+        int in = rem - q * (g.tiles[1] * g.tiles[2]);
+        rem = q;
+        const int band = fdiv(in, g.f_bandrows);
+        const int bw = imin(kFastBand, g.tiles[2] - band * kFastBand);
+        in -= band * kFastBand * g.tiles[1];
+        th = fdiv(in, bw == kFastBand ? g.f_band : g.f_lastband);
+        tw = band * kFastBand + (in - th * bw);
+        q = fdiv(rem, g.f_nres);
+        res = rem - q * g.nres;
+        rem = q;
     }
-    const int plane = g.tiles[1] * g.tiles[2];
-    int in = rem % plane;
-    rem /= plane;
-    const int band = in / (kFastBand * g.tiles[1]);
-    const int bw = imin(kFastBand, g.tiles[2] - band * kFastBand);
-    in -= band * kFastBand * g.tiles[1];
-    const int th = in / bw;
-    const int tw = band * kFastBand + (in - th * bw);
-    const int res = rem % g.nres;
-    const int b = rem / g.nres;
+    const int b = rem;
+    // residue class of each axis, its size and the tile origin
+    int r[3];
+    q = fdiv(res, g.f_dil[2]);
+    r[2] = res - q * g.dil[2];
+    const int q1 = fdiv(q, g.f_dil[1]);
+    r[1] = q - q1 * g.dil[1];
+    r[0] = fdiv(res, g.f_dil21);
     const int o[3] = {tt, th * kTH, tw * kTW};
-    return fill_ctx(g.ext, g.ker, g.dil, g.heads, g.head_dim, b, head, res, o, w);
+    bool inside = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        w.n[a] = fdiv(g.ext[a] - r[a] + g.dil[a] - 1, g.f_dil[a]);
+        w.k[a] = g.ker[a];
+        w.o[a] = o[a];
+        inside = inside && (o[a] < w.n[a]);
+    }
+    const int64_t HW = (int64_t)g.ext[1] * g.ext[2];
+    const int64_t ntok = HW * g.ext[0];
+    const int64_t hd = (int64_t)g.heads * g.head_dim;
+    const int64_t origin_tok = r[0] * HW + (int64_t)r[1] * g.ext[2] + r[2];
+    w.base = ((int64_t)b * ntok + origin_tok) * hd + (int64_t)head * g.head_dim;
+    w.st[0] = g.dil[0] * HW * hd;
+    w.st[1] = (int64_t)g.dil[1] * g.ext[2] * hd;
+    w.st[2] = (int64_t)g.dil[2] * hd;
+    w.lbase = ((int64_t)b * ntok + origin_tok) * g.heads + head;
+    w.lst[0] = g.dil[0] * HW * g.heads;
+    w.lst[1] = (int64_t)g.dil[1] * g.ext[2] * g.heads;
+    w.lst[2] = (int64_t)g.dil[2] * g.heads;
+    return inside;
 }
 
 // The lane's point and its patch (first point) in the tile, clamped into the
@@ -132,24 +178,25 @@ __device__ __forceinline__ Lane lane_geom(const TileCtx &w, int wave, int lane) 
 }
 
 // Copy one plane (class T coordinate tk) of the box [U1, U1 + E1) x [U2, U2 + E2)
-// of src into lds, box row r at byte r * rowb, with direct global-to-LDS loads
-// (16 bytes per lane, 64 consecutive slots per wave instruction). Points past
-// the grid repeat the last grid point; they are only ever read masked.
-// Completion: stage_wait().
-template <int D>
+// of src into lds, box row r at byte r * rowb, points PS bytes apart (D * 4,
+// or one 16-byte slot more), with direct global-to-LDS loads (16 bytes per
+// lane, 64 consecutive slots per wave instruction; lanes on padding slots are
+// idle). Points past the grid repeat the last grid point; they are only ever
+// read masked. Completion: stage_wait().
+template <int D, int PS>
 __device__ __forceinline__ void stage_plane(const float *src, const TileCtx &w, int tk, int U1,
                                             int E1, int U2, int E2, int rowb, char *lds) {
-    constexpr int PB = D * 4, NC = PB / 16, LNC = log2_of<NC>();
+    constexpr int NC = D / 4, SP = PS / 16;  // chunks of data, slots per point
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int parts = (E2 * NC + 63) >> 6;
+    const int parts = (E2 * SP + 63) >> 6;
     const char *plane = reinterpret_cast<const char *>(src) + (w.base + tk * w.st[0]) * 4;
     for (int part = 0; part < parts; ++part) {
         const int j = part * 64 + lane;
-        const int col = j >> LNC;
-        if (col >= E2) continue;
+        const int col = j / SP, chunk = j - col * SP;
+        if (col >= E2 || chunk >= NC) continue;
         const int c2 = imin(U2 + col, w.n[2] - 1);
-        const int colb = (int)(c2 * w.st[2]) * 4 + ((j & (NC - 1)) << 4);
+        const int colb = (int)(c2 * w.st[2]) * 4 + (chunk << 4);
         for (int r = wave; r < E1; r += kWaves) {
             const int c1 = imin(U1 + r, w.n[1] - 1);
             const char *rowp = plane + c1 * w.st[1] * 4;
@@ -214,28 +261,6 @@ __device__ __forceinline__ int opaque_zero() {
     return z;
 }
 
-// The NC chunks of a point read key-major (this lane's own entry).
-template <int NC>
-__device__ __forceinline__ void load_point(const char *pt, f4 (&x)[NC]) {
-#pragma unroll
-    for (int s = 0; s < NC; ++s) x[s] = lds_chunk(pt, s * 16);
-}
-
-// sum over d of x[d] (this lane's entry) times b[d] (registers), as two
-// independent MFMA chains.
-template <int NC>
-__device__ __forceinline__ f4 dot_chunks(const f4 (&x)[NC], const float (&b)[4 * NC], f4 z0) {
-    f4 z1 = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NC; ++s) {
-        z0 = mfma4(x[s][0], b[4 * s + 0], z0);
-        z1 = mfma4(x[s][1], b[4 * s + 1], z1);
-        z0 = mfma4(x[s][2], b[4 * s + 2], z0);
-        z1 = mfma4(x[s][3], b[4 * s + 3], z1);
-    }
-    return z0 + z1;
-}
-
 // Half-item pipelining: step j of a walk covers item j / 2, half j % 2 (half
 // of a point's chunks key-major, or one row of the patch d-major), so the
 // register buffer of the next step holds half an item.
@@ -259,14 +284,13 @@ __device__ __forceinline__ void dot_half(const f4 (&x)[NH], const float (&b)[N],
     }
 }
 
-// One row (entries 2h, 2h + 1) of a patch read d-major.
-template <int D>
+// One row (entries 2h, 2h + 1, points PS bytes apart) of a patch read d-major.
+template <int D, int PS>
 __device__ __forceinline__ void load_row_dmajor(const char *row, int col, f4 (&x)[2][D / 16]) {
-    constexpr int PB = D * 4;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) x[e][j] = lds_chunk(row + col + e * PB, j * 64);
+        for (int j = 0; j < D / 16; ++j) x[e][j] = lds_chunk(row + col + e * PS, j * 64);
 }
 
 // acc[g] += entry[dim(i, g)] * w[e] over the two entries of a patch row.
@@ -281,32 +305,6 @@ __device__ __forceinline__ void axpy_row(const f4 (&x)[2][D / 16], float w0, flo
     for (int j = 0; j < D / 16; ++j)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[4 * j + t] = mfma4(x[1][j][t], w1, acc[4 * j + t]);
-}
-
-// The chunks c, c + 4, ... of the four entries of a patch read d-major: entry
-// e at row (e >> 1 ? row1 : row0), column offset col + (e & 1) * PB.
-template <int D>
-__device__ __forceinline__ void load_patch_dmajor(const char *row0, const char *row1, int col,
-                                                  f4 (&x)[4][D / 16]) {
-    constexpr int PB = D * 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j)
-            x[e][j] = lds_chunk((e >> 1 ? row1 : row0) + col + (e & 1) * PB, j * 64);
-}
-
-// acc[g] += entry_e[dim(i, g)] * w[e] over the four entries: lane 4b+i
-// supplies dims 4 (i + 4 j) + x as element g = 4 j + x.
-template <int D>
-__device__ __forceinline__ void axpy_patch(const f4 (&x)[4][D / 16], const float (&w)[4],
-                                           f4 (&acc)[D / 4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[4 * j + t] = mfma4(x[e][j][t], w[e], acc[4 * j + t]);
 }
 
 // Store a per-lane accumulator (dims as in axpy_patch) times mul to the
@@ -344,7 +342,7 @@ struct Edge {
 // Forward.
 template <int D, int CH, int CW, bool T3>
 __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem) {
-    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
+    constexpr int PS = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -367,9 +365,9 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
 
     const int ra = a.g.ra, rb = a.g.rb;
     // key-major: this lane supplies entry c of its block's patch
-    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PS;
     // d-major: this lane supplies chunks c, c + 4, ... of the block's entries
-    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PS + c * 16;
 
     const int64_t qo = elem_off(w, L.p);
     float m = -1e30f, l = 0.f;
@@ -381,7 +379,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
         load_row<float, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
@@ -396,7 +394,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
                                             (j & 1) * (NC / 2) * 16, kb[b]);
                 },
                 [&](int j, int b) {
@@ -426,7 +424,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
             m = mj;
         }
         __syncthreads();
-        stage_plane<D>(a.v, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // O_b[i][c] += v_e[dim(i, g)] * P[c][e]
@@ -436,7 +434,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PS,
                                        vb[b]);
                 },
                 [&](int j, int b) {
@@ -459,9 +457,12 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
 
 // ============================================================================
 // Backward, query side: delta and dq.
-template <int D, int CH, int CW, bool T3>
+// PAD: points one 16-byte slot apart in LDS (row pitch 2 mod 4 slots), which
+// makes key-major and d-major reads both conflict-free, so K is staged once
+// for both of its uses; without it K is staged twice, in each layout.
+template <int D, int CH, int CW, bool T3, bool PAD>
 __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) {
-    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
+    constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -483,8 +484,8 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
     for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
 
     const int ra = a.g.ra, rb = a.g.rb;
-    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PB;
-    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PB + c * 16;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PS;
+    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PS + c * 16;
 
     const int64_t qo = elem_off(w, L.p);
     const int64_t ro = row_off(w, L.p);
@@ -507,7 +508,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float dor[D];
         load_row<float, D>(a.dout + qo + opaque_zero(), dor);
         stage_wait();
@@ -519,7 +520,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
                                             (j & 1) * (NC / 2) * 16, kb[b]);
                 },
                 [&](int j, int b) {
@@ -534,7 +535,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
                 });
         }
         __syncthreads();
-        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
         load_row<float, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
@@ -547,7 +548,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
                                             (j & 1) * (NC / 2) * 16, kb[b]);
                 },
                 [&](int j, int b) {
@@ -565,9 +566,11 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
                     pin4(s[i]);
                 });
         }
-        __syncthreads();
-        stage_plane<D>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
-        stage_wait();
+        if constexpr (!PAD) {
+            __syncthreads();
+            stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+            stage_wait();
+        }
 
         // dQ_b[i][c] += k_e[dim(i, g)] * dS[c][e]
         {
@@ -575,7 +578,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PS,
                                        vb[b]);
                 },
                 [&](int j, int b) {
@@ -601,9 +604,10 @@ __device__ __forceinline__ int tile_walk(const TileCtx &w) {
                 tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]));
 }
 
-template <int D, int CH, int CW, bool T3>
+// PAD: as for dq_tile; dout is then staged once for dV and dS.
+template <int D, int CH, int CW, bool T3, bool PAD>
 __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem) {
-    constexpr int PB = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
+    constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
     {
@@ -627,8 +631,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
     const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
 
     const int ra = a.g.ra, rb = a.g.rb;
-    const char *baseA = smem + (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PB;
-    const char *baseB = smem + (lo[1] - U[1]) * rb + (lo[2] - U[2]) * PB + c * 16;
+    const char *baseA = smem + (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PS;
+    const char *baseB = smem + (lo[1] - U[1]) * rb + (lo[2] - U[2]) * PS + c * 16;
     const int rp = a.g.rows_pitch;
     const float2 *baseR = reinterpret_cast<const float2 *>(smem + a.g.rows_off) +
                           (lo[1] - U[1] + (c >> 1)) * rp + (lo[2] - U[2] + (c & 1));
@@ -646,7 +650,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
     for (int j = 0; j < nplanes; ++j) {
         const int tq = tq0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,
                          reinterpret_cast<float2 *>(smem + a.g.rows_off));
         float kr[D];
@@ -664,7 +668,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
                                             (j & 1) * (NC / 2) * 16, kb[b]);
                     if ((j & 1) == 0) lr[b] = baseR[2 * (i / CW) * rp + 2 * (i % CW)].x;
                 },
@@ -687,7 +691,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
                 });
         }
         __syncthreads();
-        stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dV_b[i][c] += dout_e[dim(i, g)] * P[c][e]
@@ -696,7 +700,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PS,
                                        vb[b]);
                 },
                 [&](int j, int b) {
@@ -707,11 +711,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
         // one plane: dv is final here; storing it now frees its registers
         if constexpr (!T3)
             if (L.active) store_row<D>(a.dv + ko, dv, 1.f);
-        __syncthreads();
-        stage_plane<D>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         float vr[D];
+        if constexpr (!PAD) {
+            __syncthreads();
+            stage_plane<D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        }
         load_row<float, D>(a.v + ko + opaque_zero(), vr);
-        stage_wait();
+        if constexpr (!PAD) stage_wait();
 
         // dP_b[i][c] = <dout_i, v_c> - delta_i;  dS = P dP
         {
@@ -720,7 +726,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PB +
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
                                             (j & 1) * (NC / 2) * 16, kb[b]);
                     if ((j & 1) == 0) dr[b] = baseR[2 * (i / CW) * rp + 2 * (i % CW)].y;
                 },
@@ -739,7 +745,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
                 });
         }
         __syncthreads();
-        stage_plane<D>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dK_b[i][c] += q_e[dim(i, g)] * dS[c][e]
@@ -748,7 +754,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
             pipelined<2 * NI>(
                 [&](int j, int b) {
                     const int i = j >> 1;
-                    load_row_dmajor<D>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PB,
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (j & 1)) * rb, 2 * (i % CW) * PS,
                                        vb[b]);
                 },
                 [&](int j, int b) {
@@ -772,16 +778,16 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
     fwd_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <int D, int CH, int CW, bool T3>
+template <int D, int CH, int CW, bool T3, bool PAD>
 __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
-    dq_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dq_tile<D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <int D, int CH, int CW, bool T3>
+template <int D, int CH, int CW, bool T3, bool PAD>
 __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 // The same for the few border tiles with a longer walk: one workgroup per CU,
@@ -789,7 +795,7 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
 template <int D, int CH, int CW, bool T3>
 __global__ void __launch_bounds__(kThreads, 1) dkdv_border_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<D, CH, CW, T3, false>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 }  // namespace fast
