@@ -100,6 +100,12 @@ SMALL = [
     ((1, 35, 33, 2, 16), (5, 5), (1, 2), torch.float32),
     ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float32),
     ((1, 7, 18, 20, 2, 16), (5, 3, 3), (1, 2, 1), torch.float32),
+    # longer inverse walks at the borders: 3D walk 4 whose border tiles need 5
+    # (split kernel), 2D head_dim 16 with k = 9 (split kernel for walks 6, 7),
+    # 2D k = 7 (a border launch of walk 5), batch 2
+    ((1, 5, 40, 36, 1, 32), (3, 7, 7), 1, torch.float32),
+    ((1, 34, 35, 2, 16), (9, 9), 1, torch.float32),
+    ((2, 33, 30, 1, 32), (7, 7), 1, torch.float32),
 ]
 
 
