@@ -54,11 +54,15 @@ CSRC = os.path.join(ROOT, "fwd_bwd_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# the sources the fused kernels (the bench phases) are built from
+FUSED_SOURCES = ("na_api.hip", "na_common.hpp", "na_fast.hpp", "na_index.hpp", "na_kernels.hpp")
+
+
 def kernel_source_hash():
-    """sha256 over the kernel sources; a recorded traffic figure is only
-    reported while the kernels it was measured on are unchanged."""
+    """sha256 over the fused kernels' sources; a recorded traffic figure is
+    only reported while the kernels it was measured on are unchanged."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(FUSED_SOURCES):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
