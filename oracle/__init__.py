@@ -62,6 +62,12 @@ def _bind(path):
     lib.oracle_na_weights.restype = None
     lib.oracle_na_bwd.argtypes = [P, dp, dp, dp, dp, ctypes.c_int64, ip, dp, dp, dp]
     lib.oracle_na_bwd.restype = None
+    lib.oracle_na_qk.argtypes = [P, dp, dp, ctypes.c_double, ctypes.c_int64, ip, dp]
+    lib.oracle_na_qk.restype = None
+    lib.oracle_na_av.argtypes = [P, dp, dp, ctypes.c_double, ctypes.c_int64, ip, dp]
+    lib.oracle_na_av.restype = None
+    lib.oracle_na_av_inverse.argtypes = [P, dp, dp, ctypes.c_double, ctypes.c_int64, ip, dp]
+    lib.oracle_na_av_inverse.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -200,6 +206,128 @@ def na_bwd(q, k, v, dout, kernel, dilation=1, scale=None, sel=None, want=("dq", 
     return res["dq"], res["dk"], res["dv"]
 
 
+# ----------------------------------------------------------------------------- unfused ops
+# The unfused formulation of the benchmark script (method = 'unfused'): na*_qk,
+# a softmax over the window axis, na*_av, on head-major tensors
+# [B, heads, (T,) H, W, C] (C = head_dim, or K = prod(kernel) for the attention
+# array). The C oracle works token-major; these wrappers only move the heads
+# axis (and translate selected unit ids) around the call. Selected units are
+# flat ids of (b, head, token) in head-major order.
+
+def _to_tm(x):
+    """[B, heads, (T,) H, W, C] -> [B, (T,) H, W, heads, C]."""
+    return np.ascontiguousarray(np.moveaxis(_f64(x), 1, -2))
+
+
+def _to_hm(x):
+    return np.ascontiguousarray(np.moveaxis(x, -2, 1))
+
+
+def _sel_tm(sel, shape_hm):
+    """Head-major unit ids -> token-major unit ids."""
+    n, s = _sel(sel)
+    if s is None:
+        return n, None
+    heads = shape_hm[1]
+    tokens = int(np.prod(shape_hm[2:-1]))
+    b, rest = np.divmod(s, heads * tokens)
+    h, tok = np.divmod(rest, tokens)
+    return n, np.ascontiguousarray((b * tokens + tok) * heads + h, dtype=np.int64)
+
+
+def _problem_hm(shape_hm, kernel, dilation, head_dim):
+    tm = (shape_hm[0],) + tuple(shape_hm[2:-1]) + (shape_hm[1], head_dim)
+    return _problem(tm, kernel, dilation, 1.0)
+
+
+def na_qk(a, b, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
+    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> (the script's na*_qk times alpha).
+
+    a, b: [B, heads, (T,) H, W, D]. Returns [B, heads, (T,) H, W, K], or [n, K]
+    for the selected query units.
+    """
+    a_tm, b_tm = _to_tm(a), _to_tm(b)
+    p = _problem_hm(a.shape, kernel, dilation, a.shape[-1])
+    K = int(np.prod(list(p.kernel)))
+    n, s = _sel_tm(sel, a.shape)
+    units = n if s is not None else int(np.prod(a.shape[:-1]))
+    attn = np.empty((units, K), np.float64)
+    (lib or _load()).oracle_na_qk(ctypes.byref(p), _dptr(a_tm), _dptr(b_tm), float(alpha), n,
+                                  None if s is None else _iptr(s), _dptr(attn))
+    if s is not None:
+        return attn
+    return _to_hm(attn.reshape(a_tm.shape[:-1] + (K,)))
+
+
+def na_av(attn, b, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
+    """out_x = alpha * sum_j attn[x, j] b_{N(x)_j} (the script's na*_av times alpha).
+
+    attn: [B, heads, (T,) H, W, K]; b: [B, heads, (T,) H, W, D]. Returns the
+    shape of b, or [n, D] for the selected query units.
+    """
+    at_tm, b_tm = _to_tm(attn), _to_tm(b)
+    p = _problem_hm(b.shape, kernel, dilation, b.shape[-1])
+    if attn.shape[:-1] != b.shape[:-1] or attn.shape[-1] != int(np.prod(list(p.kernel))):
+        raise ValueError("attn must be [B, heads, (T,) H, W, prod(kernel)]")
+    n, s = _sel_tm(sel, b.shape)
+    out = np.empty(b_tm.shape if s is None else (n, b.shape[-1]), np.float64)
+    (lib or _load()).oracle_na_av(ctypes.byref(p), _dptr(at_tm), _dptr(b_tm), float(alpha), n,
+                                  None if s is None else _iptr(s), _dptr(out))
+    return out if s is not None else _to_hm(out)
+
+
+def na_av_inverse(attn, a, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
+    """out_y = alpha * sum over the queries x whose window holds y of attn[x, j] a_x.
+
+    The map behind the gradients of the keys of na*_qk and of the values of
+    na*_av (KGRAD, VGRAD). Shapes as in na_av; selected units are keys.
+    """
+    at_tm, a_tm = _to_tm(attn), _to_tm(a)
+    p = _problem_hm(a.shape, kernel, dilation, a.shape[-1])
+    if attn.shape[:-1] != a.shape[:-1] or attn.shape[-1] != int(np.prod(list(p.kernel))):
+        raise ValueError("attn must be [B, heads, (T,) H, W, prod(kernel)]")
+    n, s = _sel_tm(sel, a.shape)
+    out = np.empty(a_tm.shape if s is None else (n, a.shape[-1]), np.float64)
+    (lib or _load()).oracle_na_av_inverse(ctypes.byref(p), _dptr(at_tm), _dptr(a_tm),
+                                          float(alpha), n, None if s is None else _iptr(s),
+                                          _dptr(out))
+    return out if s is not None else _to_hm(out)
+
+
+def softmax(x):
+    """Softmax over the last (window) axis, as the script's F.softmax(attn, dim=-1):
+    exp(x - max) / sum exp(x - max), in float64."""
+    x = _f64(x)
+    e = np.exp(x - np.max(x, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def softmax_bwd(p, dp):
+    """Backward of the window softmax: dS = P * (dP - sum_j P dP) over the last axis."""
+    p, dp = _f64(p), _f64(dp)
+    return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+
+
+def unfused_fwd(q, k, v, kernel, dilation=1, scale=None, lib=None):
+    """The unfused forward on head-major tensors: P = softmax(scale * na_qk(q, k)),
+    out = na_av(P, v). Returns (P, out)."""
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    P = softmax(na_qk(q, k, kernel, dilation, scale, lib=lib))
+    return P, na_av(P, v, kernel, dilation, 1.0, lib=lib)
+
+
+def unfused_bwd(q, k, v, P, dout, kernel, dilation=1, scale=None, lib=None):
+    """Backward of sum(out * dout) through the unfused ops (AGRAD, softmax
+    backward, QGRAD, KGRAD, VGRAD). Returns (dq, dk, dv)."""
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    dP = na_qk(dout, v, kernel, dilation, 1.0, lib=lib)             # AGRAD
+    dv = na_av_inverse(P, dout, kernel, dilation, 1.0, lib=lib)      # VGRAD
+    dS = softmax_bwd(P, dP)
+    dq = na_av(dS, k, kernel, dilation, scale, lib=lib)              # QGRAD
+    dk = na_av_inverse(dS, q, kernel, dilation, scale, lib=lib)      # KGRAD
+    return dq, dk, dv
+
+
 class Bound:
     """The oracle's functions bound to one compiled library (the default build
     unless a path is given). Lets a check run against another build of the
@@ -219,3 +347,18 @@ class Bound:
 
     def na_bwd(self, *a, **kw):
         return na_bwd(*a, lib=self.lib, **kw)
+
+    def na_qk(self, *a, **kw):
+        return na_qk(*a, lib=self.lib, **kw)
+
+    def na_av(self, *a, **kw):
+        return na_av(*a, lib=self.lib, **kw)
+
+    def na_av_inverse(self, *a, **kw):
+        return na_av_inverse(*a, lib=self.lib, **kw)
+
+    def unfused_fwd(self, *a, **kw):
+        return unfused_fwd(*a, lib=self.lib, **kw)
+
+    def unfused_bwd(self, *a, **kw):
+        return unfused_bwd(*a, lib=self.lib, **kw)

@@ -300,6 +300,120 @@ void oracle_na_bwd(const oracle_problem *p, const double *q, const double *k, co
     }
 }
 
+/*
+ * The unfused formulation (the benchmark script's method = 'unfused'): the
+ * window scores are materialized as an array attn[unit][K] by na*_qk, a
+ * softmax runs over its last axis, and na*_av takes the weighted sum of the
+ * values over the same windows. The maintainer's profiler tables list the
+ * backward kernels of these two ops: AGRAD and VGRAD (backward of na*_av),
+ * QGRAD and KGRAD (backward of na*_qk). Every one of them is one of the three
+ * maps below with some pair of operands:
+ *   qk:          attn[x][j] = alpha * <a_x, b_{N(x)_j}>           (QK, AGRAD)
+ *   av:          out_x = alpha * sum_j attn[x][j] b_{N(x)_j}      (AV, QGRAD)
+ *   av_inverse:  out_y = alpha * sum_{x: y in N(x)} attn[x][j] a_x,
+ *                with j the position of y in the window of x      (KGRAD, VGRAD)
+ * attn rows are indexed by unit (b, token, head) in token-major order, window
+ * positions j in the neighborhood's row-major order (as neighborhood() lists
+ * them).
+ */
+
+/* attn[s][j] for each selected unit s (all units when sel == NULL); attn is [n_sel, K]. */
+void oracle_na_qk(const oracle_problem *p, const double *a, const double *b, double alpha,
+                  int64_t n_sel, const int64_t *sel, double *attn)
+{
+    int64_t K = window_size(p), D = p->head_dim;
+    if (!sel) n_sel = p->batch * tokens(p) * p->heads;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t s = 0; s < n_sel; ++s) {
+            int64_t bb, tok, h;
+            decode_unit(p, sel ? sel[s] : s, &bb, &tok, &h);
+            neighborhood(p, tok, keys);
+            const double *ax = vec(p, a, bb, tok, h);
+            for (int64_t j = 0; j < K; ++j)
+                attn[s * K + j] = alpha * dot(ax, vec(p, b, bb, keys[j], h), D);
+        }
+        free(keys);
+    }
+}
+
+/* out[s] (D values) for each selected query unit; attn is the full [units, K] array. */
+void oracle_na_av(const oracle_problem *p, const double *attn, const double *b, double alpha,
+                  int64_t n_sel, const int64_t *sel, double *out)
+{
+    int64_t K = window_size(p), D = p->head_dim;
+    if (!sel) n_sel = p->batch * tokens(p) * p->heads;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t s = 0; s < n_sel; ++s) {
+            int64_t u = sel ? sel[s] : s, bb, tok, h;
+            decode_unit(p, u, &bb, &tok, &h);
+            neighborhood(p, tok, keys);
+            double *o = out + s * D;
+            for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+            for (int64_t j = 0; j < K; ++j) {
+                const double *bv = vec(p, b, bb, keys[j], h);
+                for (int64_t c = 0; c < D; ++c) o[c] += attn[u * K + j] * bv[c];
+            }
+            for (int64_t c = 0; c < D; ++c) o[c] *= alpha;
+        }
+        free(keys);
+    }
+}
+
+/*
+ * out[s] (D values) for each selected key unit y: the sum over every query x
+ * whose window holds y. Candidates are found by brute force exactly as in
+ * oracle_na_bwd (same residue class, within (k-1)*d on every axis), the
+ * candidate's window is rebuilt and y is looked up in it, which gives j.
+ */
+void oracle_na_av_inverse(const oracle_problem *p, const double *attn, const double *a,
+                          double alpha, int64_t n_sel, const int64_t *sel, double *out)
+{
+    int64_t K = window_size(p), D = p->head_dim;
+    int64_t T = p->extent[0], H = p->extent[1], W = p->extent[2];
+    if (!sel) n_sel = p->batch * tokens(p) * p->heads;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t s = 0; s < n_sel; ++s) {
+            int64_t bb, tok, h;
+            decode_unit(p, sel ? sel[s] : s, &bb, &tok, &h);
+            int64_t ctr[3] = {tok / (H * W), (tok / W) % H, tok % W}, lo[3], hi[3];
+            for (int ax = 0; ax < 3; ++ax) {
+                lo[ax] = ctr[ax] - (p->kernel[ax] - 1) * p->dilation[ax];
+                hi[ax] = ctr[ax] + (p->kernel[ax] - 1) * p->dilation[ax];
+            }
+            double *o = out + s * D;
+            for (int64_t c = 0; c < D; ++c) o[c] = 0.0;
+            for (int64_t xt = lo[0]; xt <= hi[0]; ++xt) {
+                if (xt < 0 || xt >= T || (xt - ctr[0]) % p->dilation[0]) continue;
+                for (int64_t xy = lo[1]; xy <= hi[1]; ++xy) {
+                    if (xy < 0 || xy >= H || (xy - ctr[1]) % p->dilation[1]) continue;
+                    for (int64_t xx = lo[2]; xx <= hi[2]; ++xx) {
+                        if (xx < 0 || xx >= W || (xx - ctr[2]) % p->dilation[2]) continue;
+                        int64_t xtok = token_index(p, xt, xy, xx);
+                        neighborhood(p, xtok, keys);
+                        int64_t j = 0;
+                        while (j < K && keys[j] != tok) ++j;
+                        if (j == K) continue; /* y is not in the window of x */
+                        int64_t xu = (bb * tokens(p) + xtok) * p->heads + h;
+                        const double *ax = vec(p, a, bb, xtok, h);
+                        for (int64_t c = 0; c < D; ++c) o[c] += attn[xu * K + j] * ax[c];
+                    }
+                }
+            }
+            for (int64_t c = 0; c < D; ++c) o[c] *= alpha;
+        }
+        free(keys);
+    }
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void)
 {

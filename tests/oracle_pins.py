@@ -282,6 +282,111 @@ def check_selection(orc, seed=10):
         assert np.array_equal(a.reshape(-1, D)[sel], b)
 
 
+# --------------------------------------------------------------------------- unfused ops
+# The unfused ops (na_qk, softmax, na_av and the inverse-neighborhood sum
+# behind KGRAD / VGRAD) on head-major tensors [B, heads, (T,) H, W, C].
+
+def _hm(shape_tm_grid, heads, C, seed, B=1):
+    r = _rng(seed)
+    return r.standard_normal((B, heads) + tuple(shape_tm_grid) + (C,))
+
+
+def check_unfused_dense(orc, seed=11):
+    """kernel = whole grid: every window is the whole grid in row-major order,
+    so na_qk is alpha * a b^T, na_av is alpha * attn b and the inverse sum is
+    alpha * attn^T a (numpy matmul per (batch, head))."""
+    for grid in [(4, 5), (2, 3, 4)]:
+        B, heads, D = 2, 2, 3
+        a = _hm(grid, heads, D, seed, B)
+        b = _hm(grid, heads, D, seed + 1, B)
+        N = int(np.prod(grid))
+        G = _hm(grid, heads, N, seed + 2, B)
+        alpha = 0.8
+        af, bf, Gf = (x.reshape(B, heads, N, -1) for x in (a, b, G))
+        attn = orc.na_qk(a, b, grid, 1, alpha).reshape(B, heads, N, N)
+        assert np.max(np.abs(attn - alpha * af @ bf.transpose(0, 1, 3, 2))) < 1e-12
+        out = orc.na_av(G, b, grid, 1, alpha).reshape(B, heads, N, D)
+        assert np.max(np.abs(out - alpha * Gf @ bf)) < 1e-12
+        inv = orc.na_av_inverse(G, a, grid, 1, alpha).reshape(B, heads, N, D)
+        assert np.max(np.abs(inv - alpha * Gf.transpose(0, 1, 3, 2) @ af)) < 1e-12
+
+
+UNFUSED_CASES = [((7, 6), (3, 5), (1, 1)), ((9, 8), (3, 3), (2, 2)), ((5, 10), (4, 3), (1, 3)),
+                 ((4, 6, 6), (3, 3, 5), (1, 2, 1)), ((5, 4, 7), (2, 3, 3), (2, 1, 2))]
+
+
+def check_unfused_adjoint(orc, seed=12):
+    """na_av and the inverse sum are the two adjoints of na_qk:
+    <na_qk(a, b), G> = <a, na_av(G, b)> = <b, na_av_inverse(G, a)> for every G.
+    A wrong window position, a transposed index or a wrong membership in any of
+    the three breaks one of the equalities."""
+    for i, (grid, kernel, dil) in enumerate(UNFUSED_CASES):
+        heads, D = 2, 3
+        K = int(np.prod(kernel))
+        a = _hm(grid, heads, D, seed + 3 * i)
+        b = _hm(grid, heads, D, seed + 3 * i + 1)
+        G = _hm(grid, heads, K, seed + 3 * i + 2)
+        lhs = np.sum(orc.na_qk(a, b, kernel, dil, 1.3) * G)
+        mid = np.sum(a * orc.na_av(G, b, kernel, dil, 1.3))
+        rhs = np.sum(b * orc.na_av_inverse(G, a, kernel, dil, 1.3))
+        assert abs(lhs - mid) < 1e-10 * max(1.0, abs(lhs)), (grid, kernel, dil, lhs, mid)
+        assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(lhs)), (grid, kernel, dil, lhs, rhs)
+
+
+def check_unfused_matches_fused(orc, seed=13):
+    """softmax(scale * na_qk) is the fused path's window weights, na_av of
+    them its output, and the five backward ops compose to its gradients (the
+    fused functions are pinned on their own by the dense, finite-difference
+    and identity checks above)."""
+    for i, (grid, kernel, dil) in enumerate(UNFUSED_CASES):
+        heads, D = 2, 3
+        q, k, v, dout = (_hm(grid, heads, D, seed + 4 * i + j) for j in range(4))
+        scale = 0.6
+        P, out = orc.unfused_fwd(q, k, v, kernel, dil, scale)
+        dq, dk, dv = orc.unfused_bwd(q, k, v, P, dout, kernel, dil, scale)
+        tm = lambda x: np.moveaxis(x, 1, -2)
+        o_ref, _ = orc.na_fwd(tm(q), tm(k), tm(v), kernel, dil, scale)
+        w_ref, _ = orc.na_weights(tm(q), tm(k), kernel, dil, scale)
+        g_ref = orc.na_bwd(tm(q), tm(k), tm(v), tm(dout), kernel, dil, scale)
+        assert np.max(np.abs(tm(out) - o_ref)) < 1e-12
+        assert np.max(np.abs(tm(P).reshape(w_ref.shape) - w_ref)) < 1e-12
+        for got, ref in zip((dq, dk, dv), g_ref):
+            assert np.max(np.abs(tm(got) - ref)) < 1e-12
+
+
+def check_softmax(orc, seed=14):
+    """The window softmax and its backward against torch (float64, CPU) and its autograd."""
+    import oracle as _o   # the numpy softmax is module-level, not per build
+    r = _rng(seed)
+    x = 4.0 * r.standard_normal((3, 5, 25))
+    g = r.standard_normal(x.shape)
+    tx = torch.tensor(x, requires_grad=True)
+    tp = torch.softmax(tx, dim=-1)
+    tp.backward(torch.tensor(g))
+    p = _o.softmax(x)
+    assert np.max(np.abs(p - tp.detach().numpy())) < 1e-14
+    assert np.max(np.abs(_o.softmax_bwd(p, g) - tx.grad.numpy())) < 1e-14
+    # large scores: no overflow, rows still sum to one
+    big = _o.softmax(x * 300.0)
+    assert np.all(np.isfinite(big)) and np.max(np.abs(big.sum(-1) - 1.0)) < 1e-12
+
+
+def check_unfused_selection(orc, seed=15):
+    """Sampled evaluation (head-major unit ids) returns the full evaluation's rows."""
+    grid, kernel, dil = (5, 6), (3, 3), (1, 2)
+    heads, D, K = 3, 4, 9
+    a = _hm(grid, heads, D, seed, B=2)
+    b = _hm(grid, heads, D, seed + 1, B=2)
+    G = _hm(grid, heads, K, seed + 2, B=2)
+    sel = np.array([0, 7, 31, 59, 100, 179])
+    full = [orc.na_qk(a, b, kernel, dil, 0.5), orc.na_av(G, b, kernel, dil, 0.5),
+            orc.na_av_inverse(G, a, kernel, dil, 0.5)]
+    part = [orc.na_qk(a, b, kernel, dil, 0.5, sel=sel), orc.na_av(G, b, kernel, dil, 0.5, sel=sel),
+            orc.na_av_inverse(G, a, kernel, dil, 0.5, sel=sel)]
+    for f, p in zip(full, part):
+        assert np.array_equal(f.reshape(-1, f.shape[-1])[sel], p)
+
+
 ALL_CHECKS = [
     ("windows", lambda o: check_windows(o)),
     ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
@@ -295,6 +400,11 @@ ALL_CHECKS = [
     ("reflection", check_reflection),
     ("scale", check_scale),
     ("selection", check_selection),
+    ("unfused_dense", check_unfused_dense),
+    ("unfused_adjoint", check_unfused_adjoint),
+    ("unfused_matches_fused", check_unfused_matches_fused),
+    ("softmax", check_softmax),
+    ("unfused_selection", check_unfused_selection),
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 

@@ -29,6 +29,17 @@ MUTATIONS = {
                         "w[j] = dot(qv, vec(p, k, b, keys[j], h), D);", 0),
     "values_from_keys": ("const double *vv = vec(p, v, b, keys[j], h);",
                          "const double *vv = vec(p, k, b, keys[j], h);", 0),
+    "qk_drops_alpha": ("attn[s * K + j] = alpha * dot(", "attn[s * K + j] = dot(", 0),
+    "qk_wrong_operand": ("dot(ax, vec(p, b, bb, keys[j], h), D)", "dot(ax, vec(p, a, bb, keys[j], h), D)", 0),
+    "av_transposed_index": ("o[c] += attn[u * K + j] * bv[c];", "o[c] += attn[j * K + u] * bv[c];", 0),
+    "av_drops_alpha": ("o[c] *= alpha;", "o[c] *= 1.0;", 0),
+    "inverse_drops_alpha": ("o[c] *= alpha;", "o[c] *= 1.0;", 1),
+    "inverse_wrong_operand": ("const double *ax = vec(p, a, bb, xtok, h);",
+                              "const double *ax = vec(p, a, bb, tok, h);", 0),
+    "inverse_own_row": ("o[c] += attn[xu * K + j] * ax[c];",
+                        "o[c] += attn[((bb * tokens(p) + tok) * p->heads + h) * K + j] * ax[c];", 0),
+    "inverse_short_reach": ("lo[ax] = ctr[ax] - (p->kernel[ax] - 1) * p->dilation[ax];",
+                            "lo[ax] = ctr[ax] - (p->kernel[ax] / 2) * p->dilation[ax];", 0),
 }
 
 
