@@ -31,7 +31,9 @@ VARIANTS = {"gather": NA_BWD_GATHER, "kvparallel": NA_BWD_KVPARALLEL}
 
 # every symbol include/na.h declares
 EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na_bwd_dq",
-           "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window")
+           "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
+           "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
+           "na_unfused_bwd")
 
 
 class NaProblem(ctypes.Structure):
@@ -91,6 +93,17 @@ def load() -> ctypes.CDLL:
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
                                           ctypes.POINTER(i64)]
         lib.na_inverse_window.restype = ctypes.c_int
+        dbl = ctypes.c_double
+        lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp]
+        lib.na_av.argtypes = [P, vp, vp, dbl, vp, vp]
+        lib.na_av_inverse.argtypes = [P, vp, vp, dbl, vp, vp]
+        lib.na_softmax.argtypes = [P, vp, vp, vp]
+        lib.na_softmax_bwd.argtypes = [P, vp, vp, vp, vp]
+        lib.na_unfused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.na_unfused_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for name in ("na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd",
+                     "na_unfused_fwd", "na_unfused_bwd"):
+            getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -257,3 +270,153 @@ class NeighborhoodAttention(torch.autograd.Function):
 def neighborhood_attention(q, k, v, kernel_size, dilation=1, scale=None):
     """Differentiable fused NA on token-major [B, (T,) H, W, heads, head_dim] tensors."""
     return NeighborhoodAttention.apply(q, k, v, kernel_size, dilation, scale)
+
+
+# ----------------------------------------------------------------------------- unfused ops
+# Head-major tensors [B, heads, (T,) H, W, head_dim] and fp32 attention arrays
+# [B, heads, (T,) H, W, K], as the benchmark script's unfused method uses them.
+
+def make_problem_hm(shape: Sequence[int], head_dim: int, kernel_size, dilation=1,
+                    scale: Optional[float] = None) -> NaProblem:
+    """fp32 na_problem for a head-major shape [B, heads, (T,) H, W, C] (C is
+    head_dim for vectors, K for attention arrays; head_dim is given apart)."""
+    ndim = len(shape) - 3
+    tm = (shape[0],) + tuple(shape[2:-1]) + (shape[1], head_dim)
+    if ndim not in (2, 3):
+        raise ValueError(f"expected [B, heads, (T,) H, W, C], got shape {tuple(shape)}")
+    return make_problem(tm, torch.float32, kernel_size, dilation, scale)
+
+
+def _window_size(kernel_size, ndim):
+    n = 1
+    for k in _tuple(kernel_size, ndim):
+        n *= k
+    return n
+
+
+def _check_hm(*ts: torch.Tensor):
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise ValueError("the unfused ops take fp32 tensors")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (head-major layout)")
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on the GPU")
+
+
+def _attn_like(x: torch.Tensor, K: int) -> torch.Tensor:
+    return torch.empty(x.shape[:-1] + (K,), dtype=torch.float32, device=x.device)
+
+
+def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
+          attn: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> (na*_qk; AGRAD with a = dout, b = v)."""
+    _check_hm(a, b)
+    ndim = a.dim() - 3
+    K = _window_size(kernel_size, ndim)
+    p = make_problem_hm(a.shape, a.shape[-1], kernel_size, dilation)
+    if b.shape != a.shape:
+        raise ValueError("a and b must share their shape")
+    if attn is None:
+        attn = _attn_like(a, K)
+    _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), _ptr(attn),
+                        _stream_handle(a.device)))
+    return attn
+
+
+def na_av(attn: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
+          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out_x = alpha * sum_j attn[x, j] b_{N(x)_j} (na*_av; QGRAD with attn = dS, b = k)."""
+    _check_hm(attn, b)
+    K = _window_size(kernel_size, b.dim() - 3)
+    if attn.shape != b.shape[:-1] + (K,):
+        raise ValueError("attn must be [B, heads, (T,) H, W, prod(kernel_size)]")
+    p = make_problem_hm(b.shape, b.shape[-1], kernel_size, dilation)
+    if out is None:
+        out = torch.empty_like(b)
+    _check(load().na_av(ctypes.byref(p), _ptr(attn), _ptr(b), float(alpha), _ptr(out),
+                        _stream_handle(b.device)))
+    return out
+
+
+def na_av_inverse(attn: torch.Tensor, a: torch.Tensor, kernel_size, dilation=1,
+                  alpha: float = 1.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out_y = alpha * sum over the queries x whose window holds y of attn[x, j] a_x
+    (KGRAD with attn = dS, a = q; VGRAD with attn = P, a = dout)."""
+    _check_hm(attn, a)
+    K = _window_size(kernel_size, a.dim() - 3)
+    if attn.shape != a.shape[:-1] + (K,):
+        raise ValueError("attn must be [B, heads, (T,) H, W, prod(kernel_size)]")
+    p = make_problem_hm(a.shape, a.shape[-1], kernel_size, dilation)
+    if out is None:
+        out = torch.empty_like(a)
+    _check(load().na_av_inverse(ctypes.byref(p), _ptr(attn), _ptr(a), float(alpha), _ptr(out),
+                                _stream_handle(a.device)))
+    return out
+
+
+def na_softmax(attn: torch.Tensor, kernel_size, dilation=1,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Softmax of attn over its window axis (out may be attn itself)."""
+    _check_hm(attn)
+    p = make_problem_hm(attn.shape, 16, kernel_size, dilation)
+    if attn.shape[-1] != _window_size(kernel_size, attn.dim() - 3):
+        raise ValueError("the last axis of attn must hold prod(kernel_size) entries")
+    if out is None:
+        out = torch.empty_like(attn)
+    _check(load().na_softmax(ctypes.byref(p), _ptr(attn), _ptr(out), _stream_handle(attn.device)))
+    return out
+
+
+def na_softmax_bwd(probs: torch.Tensor, dprobs: torch.Tensor, kernel_size, dilation=1,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """probs * (dprobs - rowsum(probs * dprobs)) over the window axis (out may be dprobs)."""
+    _check_hm(probs, dprobs)
+    if probs.shape != dprobs.shape:
+        raise ValueError("probs and dprobs must share their shape")
+    p = make_problem_hm(probs.shape, 16, kernel_size, dilation)
+    if probs.shape[-1] != _window_size(kernel_size, probs.dim() - 3):
+        raise ValueError("the last axis must hold prod(kernel_size) entries")
+    if out is None:
+        out = torch.empty_like(probs)
+    _check(load().na_softmax_bwd(ctypes.byref(p), _ptr(probs), _ptr(dprobs), _ptr(out),
+                                 _stream_handle(probs.device)))
+    return out
+
+
+def na_unfused_fwd(q, k, v, kernel_size, dilation=1, scale: Optional[float] = None,
+                   probs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Unfused forward on head-major fp32 tensors: returns (probs, out)."""
+    _check_hm(q, k, v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must share their shape")
+    K = _window_size(kernel_size, q.dim() - 3)
+    p = make_problem_hm(q.shape, q.shape[-1], kernel_size, dilation, scale)
+    if probs is None:
+        probs = _attn_like(q, K)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(probs),
+                                 _ptr(out), _stream_handle(q.device)))
+    return probs, out
+
+
+def na_unfused_bwd(q, k, v, probs, dout, kernel_size, dilation=1, scale: Optional[float] = None,
+                   dscores: Optional[torch.Tensor] = None, grads=None):
+    """Unfused backward of sum(out * dout): returns (dq, dk, dv)."""
+    _check_hm(q, k, v, probs, dout)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout must share their shape")
+    K = _window_size(kernel_size, q.dim() - 3)
+    if probs.shape != q.shape[:-1] + (K,):
+        raise ValueError("probs must be [B, heads, (T,) H, W, prod(kernel_size)]")
+    p = make_problem_hm(q.shape, q.shape[-1], kernel_size, dilation, scale)
+    if dscores is None:
+        dscores = _attn_like(q, K)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check(load().na_unfused_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(probs),
+                                 _ptr(dout), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _stream_handle(q.device)))
+    return dq, dk, dv

@@ -134,6 +134,68 @@ int64_t na_window_start(int64_t extent, int64_t kernel, int64_t dilation, int64_
 na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, int64_t y,
                             int64_t *first, int64_t *last);
 
+/* ------------------------------------------------------------------------
+ * Unfused ops (NATTEN issue #161: the benchmark script's method = 'unfused'
+ * materializes the window scores with na2d_qk / na3d_qk, applies a softmax
+ * over the window axis, and forms the output with na2d_av / na3d_av; the
+ * maintainer's profiler tables list their backward kernels AGRAD, QGRAD,
+ * KGRAD and VGRAD).
+ *
+ * Layout. As in that script these ops take head-major tensors: a, b, q, k, v,
+ * out, dout, dq, dk, dv are dense [B, heads, (T,) H, W, head_dim] arrays and
+ * the attention arrays (attn, probs, dprobs, dscores) are dense fp32
+ * [B, heads, (T,) H, W, K], K = prod(kernel), entry j of a row being the key
+ * at window offset j in row-major (t, h, w) order; the window and the
+ * dilation rule are those of the fused ops above. Only NA_F32 problems are
+ * supported (others return NA_ERR_UNSUPPORTED); problem->scale is used only
+ * by na_unfused_fwd / na_unfused_bwd, and na_softmax / na_softmax_bwd accept
+ * any head_dim >= 1 (they never read a head_dim-long vector). Pointers must be non-null and 16-byte
+ * aligned; buffers are caller-owned, outputs are overwritten, work is
+ * enqueued on hip_stream and nothing is allocated or synchronized. Errors as
+ * for the fused ops.
+ */
+
+/* attn[x][j] = alpha * <a_x, b_{N(x)_j}>: the window scores (na*_qk with
+ * a = q, b = k, alpha = scale) and the gradient of the weights of na*_av
+ * (AGRAD: a = dout, b = v, alpha = 1). attn must not overlap a or b. */
+na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, float *attn,
+                void *hip_stream);
+
+/* out_x = alpha * sum_j attn[x][j] * b_{N(x)_j}: na*_av (b = v, alpha = 1) and
+ * the query gradient of na*_qk (QGRAD: attn = dscores, b = k, alpha = scale). */
+na_status na_av(const na_problem *p, const float *attn, const void *b, double alpha, void *out,
+                void *hip_stream);
+
+/* out_y = alpha * sum over the queries x whose window holds y of attn[x][j] * a_x,
+ * j being the offset of y in the window of x: the key gradient of na*_qk
+ * (KGRAD: attn = dscores, a = q, alpha = scale) and the value gradient of
+ * na*_av (VGRAD: attn = probs, a = dout, alpha = 1). Each output row is
+ * written once by its owner; no atomics. */
+na_status na_av_inverse(const na_problem *p, const float *attn, const void *a, double alpha,
+                        void *out, void *hip_stream);
+
+/* probs = softmax of attn over the window axis (rows of K); in place allowed. */
+na_status na_softmax(const na_problem *p, const float *attn, float *probs, void *hip_stream);
+
+/* Softmax backward over rows of K: dscores = probs * (dprobs - rowsum(probs * dprobs));
+ * dscores may alias dprobs. */
+na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *dprobs,
+                         float *dscores, void *hip_stream);
+
+/* The unfused forward: probs = softmax(scale * na_qk(q, k)), out = na_av(probs, v).
+ * probs ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward. */
+na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
+                         float *probs, void *out, void *hip_stream);
+
+/* The unfused backward of sum(out * dout), from the forward's probs:
+ * dprobs = na_qk(dout, v) (AGRAD), dv = na_av_inverse(probs, dout) (VGRAD),
+ * dscores = softmax backward, dq = scale * na_av(dscores, k) (QGRAD),
+ * dk = scale * na_av_inverse(dscores, q) (KGRAD). dscores is a caller-owned
+ * fp32 [B, heads, (T,) H, W, K] scratch array, left holding dscores. */
+na_status na_unfused_bwd(const na_problem *p, const void *q, const void *k, const void *v,
+                         const float *probs, const void *dout, float *dscores, void *dq,
+                         void *dk, void *dv, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,193 @@
+"""GPU parity of the unfused ops (na_qk, window softmax, na_av, the inverse
+sum and their forward / backward compositions), through the C ABI, against
+the fp64 CPU oracle on the same seeded head-major inputs.
+
+Bar: max |Y_gpu - Y_oracle| / max |Y_oracle| <= 1e-4 per output (fp32).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fwd_bwd_amd import na
+from fwd_bwd_amd.inputs import make_random
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    na.load()
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    return err / scale if scale > 0 else err
+
+
+def np64(t):
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, label, tol=TOL):
+    errs = {n: rel_err(np64(got[n]), ref[n]) for n in ref}
+    say(label, {n: f"{e:.2e}" for n, e in errs.items()})
+    for n, e in errs.items():
+        assert e <= tol, (label, n, e)
+
+
+# (head-major shape [B, heads, (T,) H, W, D], kernel, dilation)
+SMALL = [
+    ((1, 2, 16, 16, 16), (3, 3), 1),
+    ((1, 2, 19, 23, 32), (5, 7), 1),
+    ((2, 3, 13, 17, 16), (3, 3), (2, 3)),
+    ((1, 1, 20, 20, 64), (9, 9), 1),
+    ((1, 2, 7, 9, 32), (7, 9), 1),           # kernel = grid
+    ((1, 2, 11, 10, 32), (1, 1), 1),         # k = 1
+    ((1, 1, 12, 11, 16), (4, 2), 1),         # even kernels
+    ((1, 2, 40, 37, 32), (9, 9), 1),
+    ((1, 2, 35, 33, 16), (5, 5), (1, 2)),
+    ((1, 1, 70, 68, 32), (9, 9), 1),
+    ((1, 2, 5, 11, 13, 32), (3, 5, 5), 1),
+    ((1, 2, 6, 9, 10, 16), (3, 3, 3), (2, 1, 2)),
+    ((1, 1, 3, 37, 35, 32), (3, 5, 5), 1),
+    ((1, 1, 5, 40, 36, 32), (3, 7, 7), 1),
+    ((2, 1, 4, 9, 8, 64), (3, 3, 3), 1),
+]
+
+
+def _id(c):
+    shape, k, d = c
+    return f"{'x'.join(map(str, shape))}-k{'x'.join(map(str, k))}-d{d}"
+
+
+def _seed(c):
+    return zlib.crc32(_id(c).encode()) % 1000
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_unfused_fwd_bwd_matches_oracle(case):
+    shape, kernel, dil = case
+    say("case", _id(case))
+    q, k, v, dout = make_random(shape, torch.float32, seed=_seed(case))
+    scale = shape[-1] ** -0.5
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
+    probs, out = na.na_unfused_fwd(qd, kd, vd, kernel, dil, scale)
+    dq, dk, dv = na.na_unfused_bwd(qd, kd, vd, probs, dd, kernel, dil, scale)
+    torch.cuda.synchronize()
+    args = [np64(t) for t in (q, k, v)]
+    P, o = oracle.unfused_fwd(*args, kernel, dil, scale)
+    gq, gk, gv = oracle.unfused_bwd(*args, P, np64(dout), kernel, dil, scale)
+    check({"probs": probs, "out": out, "dq": dq, "dk": dk, "dv": dv},
+          {"probs": P, "out": o, "dq": gq, "dk": gk, "dv": gv}, _id(case))
+
+
+@pytest.mark.parametrize("case", SMALL[:4] + SMALL[10:12], ids=[_id(c) for c in SMALL[:4] + SMALL[10:12]])
+def test_unfused_ops_on_arbitrary_operands(case):
+    """Each op alone, with alpha != 1 and attention arrays that are not softmax
+    rows (seeded normals), so a wrong window position cannot hide behind
+    normalization."""
+    shape, kernel, dil = case
+    say("ops", _id(case))
+    K = int(np.prod(kernel))
+    a, b, _, _ = make_random(shape, torch.float32, seed=_seed(case) + 1)
+    attn, g, _, _ = make_random(shape[:-1] + (K,), torch.float32, seed=_seed(case) + 2)
+    dev = torch.device("cuda:0")
+    ad, bd, atd, gd = (t.to(dev) for t in (a, b, attn, g))
+    s = na.na_qk(ad, bd, kernel, dil, alpha=0.7)
+    o = na.na_av(atd, bd, kernel, dil, alpha=-1.3)
+    oi = na.na_av_inverse(atd, ad, kernel, dil, alpha=0.4)
+    p = na.na_softmax(atd, kernel, dil)
+    ds = na.na_softmax_bwd(p, gd, kernel, dil)
+    torch.cuda.synchronize()
+    A, B, AT, G = (np64(t) for t in (a, b, attn, g))
+    Pref = oracle.softmax(AT)
+    check({"qk": s, "av": o, "av_inverse": oi, "softmax": p, "softmax_bwd": ds},
+          {"qk": oracle.na_qk(A, B, kernel, dil, 0.7),
+           "av": oracle.na_av(AT, B, kernel, dil, -1.3),
+           "av_inverse": oracle.na_av_inverse(AT, A, kernel, dil, 0.4),
+           "softmax": Pref, "softmax_bwd": oracle.softmax_bwd(Pref, G)}, "ops " + _id(case))
+
+
+def test_softmax_in_place_and_large_rows():
+    """In-place softmax / softmax backward, and rows longer than the register
+    path holds (K = 441 > 384 entries: the multi-pass kernel)."""
+    dev = torch.device("cuda:0")
+    for shape, kernel in [((1, 2, 9, 10, 16), (3, 5)), ((1, 1, 22, 23, 16), (21, 21))]:
+        K = int(np.prod(kernel))
+        x, g, _, _ = make_random(shape[:-1] + (K,), torch.float32, seed=K)
+        x = 3.0 * x
+        xd, gd = x.to(dev), g.to(dev)
+        p = na.na_softmax(xd, kernel)
+        xd2 = xd.clone()
+        na.na_softmax(xd2, kernel, out=xd2)
+        gd2 = gd.clone()
+        na.na_softmax_bwd(p, gd2, kernel, out=gd2)
+        torch.cuda.synchronize()
+        Pref = oracle.softmax(np64(x))
+        check({"p": p, "p_inplace": xd2, "ds_inplace": gd2},
+              {"p": Pref, "p_inplace": Pref, "ds_inplace": oracle.softmax_bwd(Pref, np64(g))},
+              f"softmax K={K}")
+
+
+def test_unfused_matches_fused_path():
+    """The unfused composition and the fused kernels compute the same function
+    (same window rule): compared on one 2D and one 3D problem, the fused path
+    fed the token-major copies of the same tensors."""
+    dev = torch.device("cuda:0")
+    for shape, kernel, dil in [((1, 2, 33, 35, 32), (7, 7), 1), ((1, 2, 5, 20, 18, 32), (3, 5, 5), 1)]:
+        q, k, v, dout = (t.to(dev) for t in make_random(shape, torch.float32, seed=21))
+        probs, out = na.na_unfused_fwd(q, k, v, kernel, dil)
+        dq, dk, dv = na.na_unfused_bwd(q, k, v, probs, dout, kernel, dil)
+        tm = lambda t: t.movedim(1, -2).contiguous()  # noqa: E731
+        out2, lse = na.na_fwd(tm(q), tm(k), tm(v), kernel, dil)
+        dq2, dk2, dv2 = na.na_bwd(tm(q), tm(k), tm(v), out2, tm(dout), lse, kernel, dil)
+        torch.cuda.synchronize()
+        for a, b in ((out, out2), (dq, dq2), (dk, dk2), (dv, dv2)):
+            assert rel_err(np64(tm(a)), np64(b)) < 2e-4
+
+
+def test_unfused_is_deterministic():
+    dev = torch.device("cuda:0")
+    shape, kernel = (1, 2, 4, 21, 19, 32), (3, 5, 5)
+    q, k, v, dout = (t.to(dev) for t in make_random(shape, torch.float32, seed=22))
+    p1, o1 = na.na_unfused_fwd(q, k, v, kernel)
+    g1 = na.na_unfused_bwd(q, k, v, p1, dout, kernel)
+    p2, o2 = na.na_unfused_fwd(q, k, v, kernel)
+    g2 = na.na_unfused_bwd(q, k, v, p2, dout, kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(o1, o2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_unfused_rejects_bf16_and_bad_shapes():
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 2, 8, 8, 16), device=dev)
+    p = na.make_problem_hm(q.shape, 16, (3, 3))
+    p.dtype = na.NA_BF16
+    attn = torch.zeros((1, 2, 8, 8, 9), device=dev)
+    status = na.load().na_qk(na.ctypes.byref(p), q.data_ptr(), q.data_ptr(), 1.0, attn.data_ptr(),
+                             None)
+    assert status == na.NA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        na.na_av(torch.zeros((1, 2, 8, 8, 8), device=dev), q, (3, 3))
+    with pytest.raises(na.NaError):
+        na.na_qk(q, q, (9, 3))   # window larger than the grid
