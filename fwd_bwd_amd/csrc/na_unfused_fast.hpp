@@ -1,10 +1,35 @@
 // na_unfused_fast.hpp -- geometry of the unfused ops and their register-tiled
-// kernels (fp32).
+// kernels (fp32, head_dim 16 and 32).
+//
+// The unfused ops reuse the tile machinery of the fused kernels (na_fast.hpp):
+// a workgroup of four waves owns a 16 x 16 tile of one residue class of one
+// (batch, head) plane, one point per lane, the other side read from one
+// staged box plane in LDS through the 4 x 4 x 1 MFMA blocks. A head-major
+// tensor [B, heads, (T,) H, W, C] is the token-major layout of that machinery
+// with one head and B * heads batch elements, so its decode and addressing
+// apply unchanged. What differs is the attention array, which these ops read
+// or write: its rows (K entries per point) pass through an LDS buffer so that
+// global memory sees whole contiguous rows.
+//
+//   qk (QK, AGRAD): per window plane, scores of the lane's point against
+//     its window (as the fused forward), then the plane's slice of the
+//     attention rows of each wave's 8 x 8 points goes out through LDS;
+//   av (AV, QGRAD): the slice comes in through LDS into the lane's registers,
+//     then the weighted sum over the window (as the fused forward's P V);
+//   av_inverse (KGRAD, VGRAD): the lane is a key; the attention entries of
+//     the queries of its inverse window come in through LDS in chunks of box
+//     rows, then the weighted sum over those queries (as the fused dk/dv).
+//     Keys near the grid border have longer inverse windows: the compiled
+//     walk covers them in several passes (offset walks), each adding to the
+//     output of the previous one.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
+#include "na_fast.hpp"
 #include "na_index.hpp"
 
 namespace nu {
@@ -18,19 +43,618 @@ struct Geo {
     int khw;     // ker[1] * ker[2]
 };
 
+using namespace na;
+using namespace na::fast;
+
+struct UArgs {
+    Geom g;
+    const float *a;      // qk: the points' own vectors; av_inverse: the summed vectors
+    const float *b;      // qk: the window vectors; av: the summed vectors
+    const float *attn;   // av, av_inverse: the attention rows
+    float *attn_out;     // qk: the attention rows
+    float *out;          // av, av_inverse
+    float alpha;
+    int K, KP, kw;       // row length, one window plane's slice of it, window width
+    FastDiv fKP;
+    int rows_round;      // qk, av: rows of a wave's 8 x 8 points per LDS round (8, 4, 2, 1)
+    int chunk_rows;      // av_inverse: box rows per attention chunk in LDS
+    int oh, ow;          // av_inverse: walk offset of this pass, in patches
+    int accumulate;      // av_inverse: add to out (passes after the first)
+};
+
+// One window plane's slice (KP entries per point) of the attention rows of
+// quarter rows [r0, r0 + rows_round) of a wave's 8 x 8 points, as one LDS
+// array: point (row, col) of the round at buf + ((row - r0) * 8 + col) * KP.
+// One quarter row at a time (its global base is wave-uniform), its 8 * KP
+// elements taken by consecutive lanes; element e is entry e % KP of point
+// column e / KP. With unit stride along W and a single window plane the
+// row's slice is one contiguous run of global memory.
+struct RowRun {
+    int64_t base;     // global index of entry 0 of the row's first point
+    int64_t cstride;  // global elements from one point of the row to the next
+    int n;            // elements of the row inside the grid
+    bool contiguous;
+};
+
+__device__ __forceinline__ RowRun row_run(const UArgs &a, const TileCtx &w, int t, int row,
+                                          int col0, int cols, int it) {
+    RowRun rr;
+    const int c[3] = {t, row, col0};
+    rr.base = row_off(w, c) * a.K + it * a.KP;
+    rr.cstride = w.lst[2] * a.K;
+    rr.n = imax(0, imin(cols, w.n[2] - col0)) * a.KP;
+    rr.contiguous = rr.cstride == a.KP;
+    return rr;
+}
+
+__device__ __forceinline__ int64_t run_index(const UArgs &a, const RowRun &rr, int e) {
+    if (rr.contiguous) return rr.base + e;
+    const int col = fdiv(e, a.fKP);
+    return rr.base + col * rr.cstride + (e - col * a.KP);
+}
+
+// global -> LDS with direct loads (no register round trip, all in flight at
+// once); completion: stage_wait().
+__device__ __forceinline__ void load_round(const UArgs &a, const TileCtx &w, int wave, int r0,
+                                           int it, float *buf, const float *src) {
+    const int lane = threadIdx.x & 63;
+    const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
+    for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
+        const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
+        float *brow = buf + row * 8 * a.KP;
+        for (int e0 = 0; e0 < rr.n; e0 += 64) {
+            if (e0 + lane < rr.n) {
+                const float *g = src + run_index(a, rr, e0 + lane);
+#if defined(__HIP_DEVICE_COMPILE__)
+                __builtin_amdgcn_global_load_lds(g, (lds_void *)(brow + e0), 4, 0, 0);
+#else
+                (void)g;
+                (void)brow;
+#endif
+            }
+        }
+    }
+}
+
+// LDS -> global.
+__device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, int wave, int r0,
+                                            int it, const float *buf, float *dst) {
+    const int lane = threadIdx.x & 63;
+    const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
+    for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
+        const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
+        const float *brow = buf + row * 8 * a.KP;
+        for (int e0 = 0; e0 < rr.n; e0 += 4 * 64) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                v[u] = e < rr.n ? brow[e] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                if (e < rr.n) dst[run_index(a, rr, e)] = v[u];
+            }
+        }
+    }
+}
+
+// ============================================================================
+// qk: attn[x][j] = alpha <a_x, b_{N(x)_j}>
+template <int D, int CH, int CW, bool T3>
+__device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
+    constexpr int PS = D * 4, NC = D / 4, NI = CH * CW;
+    TileCtx w;
+    if (!decode(a.g, tile, w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, grp = lane >> 2;
+    const Lane L = lane_geom(w, wave, lane);
+
+    int us[3], lo[3], U[3], E[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        us[x] = window_start(L.f[x], w.n[x], w.k[x]);
+        lo[x] = window_start(L.p[x], w.n[x], w.k[x]) - us[x];
+        key_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], &U[x], &E[x]);
+    }
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    const int ra = a.g.ra;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PS;
+    const int64_t qo = elem_off(w, L.p);
+    // the lane's point in its wave's 8 x 8 quarter, and the wave's LDS buffer
+    const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
+    float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
+
+    const int nplanes = T3 ? w.k[0] : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tk = t0 + j;
+        if (j > 0) __syncthreads();
+        stage_plane<D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        float qr[D];
+        load_row<float, D>(a.a + qo + opaque_zero(), qr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) qr[d] *= a.alpha;
+        stage_wait();
+
+        // S_b[i][c] = <b_i, a_c> over the walk
+        float s[NI][4];
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            pipelined<2 * NI>(
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
+                                            (jj & 1) * (NC / 2) * 16, kb[bb]);
+                },
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    if ((jj & 1) == 0) z0 = z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    dot_half<NC / 2>(kb[bb], qr, (jj & 1) * (NC / 2), z0, z1);
+                    if ((jj & 1) == 0) return;
+                    const f4 z = z0 + z1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[i][e] = z[e];
+                    pin4(s[i]);
+                });
+        }
+        __syncthreads();  // the staged plane is read no more: its LDS takes the rows
+        for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
+            if (lr >= r0 && lr < r0 + a.rows_round) {
+                float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jh = 2 * (i / CW) + (e >> 1) - lo[1];
+                        const int jw = 2 * (i % CW) + (e & 1) - lo[2];
+                        if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2])
+                            slot[jh * a.kw + jw] = s[i][e];
+                    }
+            }
+            __syncthreads();
+            store_round(a, w, wave, r0, j, buf, a.attn_out);
+            __syncthreads();
+        }
+    }
+}
+
+// ============================================================================
+// av: out_x = alpha sum_j attn[x][j] b_{N(x)_j}
+template <int D, int CH, int CW, bool T3>
+__device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
+    constexpr int PS = D * 4, G = D / 4, NI = CH * CW;
+    TileCtx w;
+    if (!decode(a.g, tile, w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, grp = lane >> 2;
+    const Lane L = lane_geom(w, wave, lane);
+
+    int us[3], lo[3], U[3], E[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        us[x] = window_start(L.f[x], w.n[x], w.k[x]);
+        lo[x] = window_start(L.p[x], w.n[x], w.k[x]) - us[x];
+        key_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], &U[x], &E[x]);
+    }
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    const int rb = a.g.rb;
+    const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PS + c * 16;
+    const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
+    float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
+
+    f4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nplanes = T3 ? w.k[0] : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tk = t0 + j;
+        if (j > 0) __syncthreads();
+        // this plane's weights into the registers of the walk (0 off the window)
+        float s[NI][4];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[i][e] = 0.f;
+        for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
+            load_round(a, w, wave, r0, j, buf, a.attn);
+            stage_wait();
+            if (L.active && lr >= r0 && lr < r0 + a.rows_round) {
+                const float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jh = 2 * (i / CW) + (e >> 1) - lo[1];
+                        const int jw = 2 * (i % CW) + (e & 1) - lo[2];
+                        if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2])
+                            s[i][e] = slot[jh * a.kw + jw];
+                    }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) pin4(s[i]);
+        stage_plane<D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // O_b[i][c] += b_e[dim(i, g)] * attn[c][e]
+        {
+            f4 vb[2][2][D / 16];
+            pipelined<2 * NI>(
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (jj & 1)) * rb,
+                                           2 * (i % CW) * PS, vb[bb]);
+                },
+                [&](int jj, int bb) {
+                    const int i = jj >> 1, h = jj & 1;
+                    axpy_row<D>(vb[bb], s[i][2 * h], s[i][2 * h + 1], acc);
+                });
+        }
+    }
+    if (L.active) store_row<D>(a.out + elem_off(w, L.p), acc, a.alpha);
+}
+
+// ============================================================================
+// av_inverse: out_y = alpha sum_{x : y in N(x)} attn[x][j(x, y)] a_x
+template <int D, int CH, int CW, bool T3>
+__device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
+    constexpr int PS = D * 4, G = D / 4, NI = CH * CW;
+    TileCtx w;
+    if (!decode(a.g, tile, w)) return;
+    // this pass walks patches [oh, oh + CH) x [ow, ow + CW) of the inverse walks
+    if (tile_inverse_walk(w.o[1], kTH, 2, w.n[1], w.k[1]) <= a.oh ||
+        tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]) <= a.ow)
+        return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3;
+    const Lane L = lane_geom(w, wave, lane);  // keys
+
+    int lo[3], U[3], E[3];
+    unsigned vm[3];
+    const int off[3] = {0, 2 * a.oh, 2 * a.ow};
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        const int cnt = off[x] / 2 + (x == 1 ? CH : CW);
+        query_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], cnt, &U[x], &E[x]);
+        U[x] += off[x];
+        E[x] -= off[x];
+        lo[x] = inverse_first(L.f[x], w.n[x], w.k[x]) + off[x];
+        const int s0 = imax(0, inverse_first(L.p[x], w.n[x], w.k[x]) - lo[x]);
+        const int s1 = imin(2 * (x == 1 ? CH : CW), inverse_last(L.p[x], w.n[x], w.k[x]) - lo[x] + 1);
+        vm[x] = s1 > s0 ? bit_range(s0, s1 - s0) : 0u;
+    }
+    // LDS offsets (relative to the lane's first walk point) of the entry of
+    // this lane's key in the attention row of walk row h / column wc: the
+    // point's place in the box plus the key's offset in that query's window
+    int rowt[2 * CH], colt[2 * CW];
+#pragma unroll
+    for (int h = 0; h < 2 * CH; ++h)
+        rowt[h] = h * E[2] * a.KP +
+                  (L.p[1] - window_start(imin(lo[1] + h, w.n[1] - 1), w.n[1], w.k[1])) * a.kw;
+#pragma unroll
+    for (int h = 0; h < 2 * CW; ++h)
+        colt[h] = h * a.KP + L.p[2] - window_start(imin(lo[2] + h, w.n[2] - 1), w.n[2], w.k[2]);
+    const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
+    const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
+
+    const int rb = a.g.rb;
+    const int rel1 = lo[1] - U[1], rel2 = lo[2] - U[2];
+    const char *baseB = smem + rel1 * rb + rel2 * PS + c * 16;
+    float *abuf = reinterpret_cast<float *>(smem);
+
+    f4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nplanes = T3 ? tq1 - tq0 + 1 : 1;
+    for (int j = 0; j < nplanes; ++j) {
+        const int tq = tq0 + j;
+        const int it = w.o[0] - window_start(tq, w.n[0], w.k[0]);  // window plane of the key
+        float s[NI][4];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[i][e] = 0.f;
+        // the box's attention entries of window plane it, a chunk of box rows
+        // at a time: LDS element e = entry jj of box point pt = r * E2 + col
+        for (int r0 = 0; r0 < E[1]; r0 += a.chunk_rows) {
+            const int rows = imin(a.chunk_rows, E[1] - r0);
+            if (j > 0 || r0 > 0) __syncthreads();
+            {
+                const int wave = threadIdx.x >> 6;
+                for (int r = 0; r < rows && U[1] + r0 + r < w.n[1]; ++r) {
+                    const RowRun rr = row_run(a, w, tq, U[1] + r0 + r, U[2], E[2], it);
+                    float *brow = abuf + r * E[2] * a.KP;
+                    for (int e0 = 64 * wave; e0 < rr.n; e0 += kThreads) {
+                        if (e0 + lane < rr.n) {
+                            const float *g = a.attn + run_index(a, rr, e0 + lane);
+#if defined(__HIP_DEVICE_COMPILE__)
+                            __builtin_amdgcn_global_load_lds(g, (lds_void *)(brow + e0), 4, 0, 0);
+#else
+                            (void)g;
+                            (void)brow;
+#endif
+                        }
+                    }
+                }
+            }
+            stage_wait();
+            // walk rows of this lane inside the chunk
+            const int h0 = imax(0, r0 - rel1), h1 = imin(32, r0 - rel1 + rows);
+            const unsigned rm = h1 > h0 ? vm[1] & bit_range(h0, h1 - h0) : 0u;
+            const float *cb = abuf + ((rel1 - r0) * E[2] + rel2) * a.KP;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
+                    if ((rm >> h) & (vm[2] >> wc) & 1u) s[i][e] = cb[rowt[h] + colt[wc]];
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) pin4(s[i]);
+        __syncthreads();
+        stage_plane<D, PS>(a.a, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_wait();
+
+        // Out_b[i][c] += a_e[dim(i, g)] * attn[e][c]
+        {
+            f4 vb[2][2][D / 16];
+            pipelined<2 * NI>(
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    load_row_dmajor<D, PS>(baseB + (2 * (i / CW) + (jj & 1)) * rb,
+                                           2 * (i % CW) * PS, vb[bb]);
+                },
+                [&](int jj, int bb) {
+                    const int i = jj >> 1, h = jj & 1;
+                    axpy_row<D>(vb[bb], s[i][2 * h], s[i][2 * h + 1], acc);
+                });
+        }
+        __syncthreads();
+    }
+    if (L.active) {
+        float *dst = a.out + elem_off(w, L.p);
+        if (a.accumulate) {
+            // add the output of the earlier passes (same layout as store_row)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j) {
+                    float o[4];
+                    Io<float>::load4(dst + 4 * (i + 4 * j), o);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[4 * j + t][i] = acc[4 * j + t][i] * a.alpha + o[t];
+                }
+            store_row<D>(dst, acc, 1.f);
+        } else {
+            store_row<D>(dst, acc, a.alpha);
+        }
+    }
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) qk_kernel(UArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    qk_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) av_kernel(UArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    av_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+template <int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) avi_kernel(UArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    avi_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+}
+
+// ============================================================================
+// Host planning.
+
+constexpr int kLdsCap = 80 * 1024;  // two workgroups per CU
+
+// Compiled walks: 2 .. 5 patches per axis on single-plane grids, 2 .. 4 with
+// several planes along T, as for the fused kernels.
+inline bool walk_compiled(int c, bool t3) { return c >= 2 && c <= (t3 ? 4 : 5); }
+
+inline void set_divisors(Geom &g) {
+    const int band = kFastBand, last = g.tiles[2] % band;
+    g.f_heads = na::make_fastdiv(g.heads);
+    g.f_t = na::make_fastdiv(g.tiles[0]);
+    g.f_plane = na::make_fastdiv(g.tiles[1] * g.tiles[2]);
+    g.f_bandrows = na::make_fastdiv(band * g.tiles[1]);
+    g.f_band = na::make_fastdiv(band);
+    g.f_lastband = na::make_fastdiv(last ? last : band);
+    g.f_nres = na::make_fastdiv(g.nres);
+    g.f_c = na::make_fastdiv(g.tiles[2]);
+    g.f_cb = na::make_fastdiv(1);
+    for (int a = 0; a < 3; ++a) g.f_dil[a] = na::make_fastdiv(g.dil[a]);
+    g.f_dil21 = na::make_fastdiv(g.dil[2] * g.dil[1]);
+}
+
+struct UPlan {
+    UArgs a;
+    int lds;
+    int c;
+    bool t3;
+};
+
+// kind 0: qk / av; kind 1: av_inverse, one pass at walk offset (oh, ow).
+inline bool plan(const Geo &geo, int64_t bh, int D, int kind, int oh, int ow, UPlan *pl) {
+    if (D != 16 && D != 32) return false;
+    const bool t3 = geo.ext[0] > 1;
+    const int c = na::window_walk(geo.ker[1], 2);
+    if (na::window_walk(geo.ker[2], 2) != c || !walk_compiled(c, t3)) return false;
+    const int PB = D * 4;
+    const int off[3] = {0, 2 * oh, 2 * ow};
+    int mx[3] = {1, 1, 1};
+    for (int a = 1; a < 3; ++a)
+        for (int r = 0; r < geo.dil[a] && r < geo.ext[a]; ++r) {
+            const int n = na::class_size(geo.ext[a], geo.dil[a], r);
+            for (int f = 0; f < n; f += 16) {
+                int start, extent;
+                if (kind == 0) {
+                    na::key_box(f, 16, 2, n, geo.ker[a], &start, &extent);
+                } else {
+                    if (na::tile_inverse_walk(f, 16, 2, n, geo.ker[a]) <= off[a] / 2) continue;
+                    na::query_box(f, 16, 2, n, geo.ker[a], off[a] / 2 + c, &start, &extent);
+                    extent -= off[a];
+                }
+                mx[a] = std::max(mx[a], extent);
+            }
+        }
+    // row pitches as for the fused kernels: odd slot count (key-major reads),
+    // 2 mod 4 slots (d-major reads)
+    const int slots = mx[2] * PB / 16;
+    const int rb = (slots + ((2 - slots % 4) + 4) % 4) * 16;
+    const int ra = (slots | 1) * 16;
+    int64_t lds = (int64_t)mx[1] * (kind == 0 ? std::max(ra, rb) : rb);
+    UArgs &u = pl->a;
+    u = UArgs{};
+    u.K = geo.K;
+    u.KP = geo.khw;
+    u.fKP = na::make_fastdiv(geo.khw);
+    u.kw = geo.kw;
+    if (kind == 0) {
+        // rows per LDS round of the wave buffers (four waves)
+        int R = 8;
+        while (R > 1 && (int64_t)4 * R * 8 * u.KP * 4 > std::max<int64_t>(lds, kLdsCap)) R /= 2;
+        if ((int64_t)4 * R * 8 * u.KP * 4 > kLdsCap) return false;
+        u.rows_round = R;
+        lds = std::max<int64_t>(lds, (int64_t)4 * R * 8 * u.KP * 4);
+    } else {
+        const int64_t row_bytes = (int64_t)mx[2] * u.KP * 4;
+        const int64_t room = std::max<int64_t>(lds, kLdsCap);
+        if (row_bytes > room) return false;
+        u.chunk_rows = (int)std::min<int64_t>(mx[1], room / row_bytes);
+        lds = std::max<int64_t>(lds, u.chunk_rows * row_bytes);
+    }
+    if (lds > kLdsCap) return false;
+    Geom &g = u.g;
+    int64_t n_tiles = bh;
+    int nres = 1;
+    for (int a = 0; a < 3; ++a) {
+        g.ext[a] = geo.ext[a];
+        g.ker[a] = geo.ker[a];
+        g.dil[a] = geo.dil[a];
+        const int nmax = na::class_size(geo.ext[a], geo.dil[a], 0);
+        g.tiles[a] = a == 0 ? nmax : (nmax + 15) / 16;
+        n_tiles *= g.tiles[a];
+        nres *= geo.dil[a];
+    }
+    n_tiles *= nres;
+    if (n_tiles > INT32_MAX || bh > INT32_MAX) return false;
+    g.heads = 1;  // head-major tensors: (batch, head) planes are batch elements
+    g.batch = (int)bh;
+    g.head_dim = D;
+    g.nres = nres;
+    g.n_tiles = (int)n_tiles;
+    g.ra = ra;
+    g.rb = rb;
+    set_divisors(g);
+    u.oh = oh;
+    u.ow = ow;
+    pl->lds = (int)lds;
+    pl->c = c;
+    pl->t3 = t3;
+    return true;
+}
+
+template <typename Kern>
+inline bool launch(Kern kern, const UPlan &pl, hipStream_t s) {
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            pl.lds) != hipSuccess)
+        return false;
+    if (pl.a.g.n_tiles > 0)
+        hipLaunchKernelGGL(kern, dim3(pl.a.g.n_tiles), dim3(kThreads), pl.lds, s, pl.a);
+    return true;
+}
+
+#define NU_CASES(X)                                                          \
+    X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)          \
+    X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)          \
+    X(16, 2, true) X(16, 3, true) X(16, 4, true)                             \
+    X(32, 2, true) X(32, 3, true) X(32, 4, true)
+
 // Register-tiled paths; each returns false (launching nothing) when the
-// problem is outside what it covers.
-inline bool fast_qk(const Geo &, int64_t, int, const float *, const float *, float, float *,
-                    hipStream_t) {
+// problem is outside what they cover.
+inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const float *b, float alpha,
+                    float *attn, hipStream_t s) {
+    UPlan pl;
+    if (!plan(geo, bh, D, 0, 0, 0, &pl)) return false;
+    pl.a.a = a;
+    pl.a.b = b;
+    pl.a.attn_out = attn;
+    pl.a.alpha = alpha;
+#define X(DD, C, T3) \
+    if (D == DD && pl.c == C && pl.t3 == T3) return launch(qk_kernel<DD, C, C, T3>, pl, s);
+    NU_CASES(X)
+#undef X
     return false;
 }
-inline bool fast_av(const Geo &, int64_t, int, const float *, const float *, float, float *,
-                    hipStream_t) {
+
+inline bool fast_av(const Geo &geo, int64_t bh, int D, const float *attn, const float *b,
+                    float alpha, float *out, hipStream_t s) {
+    UPlan pl;
+    if (!plan(geo, bh, D, 0, 0, 0, &pl)) return false;
+    pl.a.b = b;
+    pl.a.attn = attn;
+    pl.a.out = out;
+    pl.a.alpha = alpha;
+#define X(DD, C, T3) \
+    if (D == DD && pl.c == C && pl.t3 == T3) return launch(av_kernel<DD, C, C, T3>, pl, s);
+    NU_CASES(X)
+#undef X
     return false;
 }
-inline bool fast_av_inverse(const Geo &, int64_t, int, const float *, const float *, float,
-                            float *, hipStream_t) {
-    return false;
+
+// Longest inverse walk (patches) along axis a over every tile of every class.
+inline int max_inverse_walk(const Geo &geo, int a) {
+    int m = 1;
+    for (int r = 0; r < geo.dil[a] && r < geo.ext[a]; ++r) {
+        const int n = na::class_size(geo.ext[a], geo.dil[a], r);
+        for (int f = 0; f < n; f += 16) m = std::max(m, na::tile_inverse_walk(f, 16, 2, n, geo.ker[a]));
+    }
+    return m;
+}
+
+inline bool fast_av_inverse(const Geo &geo, int64_t bh, int D, const float *attn, const float *a,
+                            float alpha, float *out, hipStream_t s) {
+    UPlan pl;
+    if (!plan(geo, bh, D, 1, 0, 0, &pl)) return false;
+    const int c = pl.c;
+    const int wh = max_inverse_walk(geo, 1), ww = max_inverse_walk(geo, 2);
+    // plan every pass first: launch nothing unless all of them fit
+    const int ph = (wh + c - 1) / c, pw = (ww + c - 1) / c;
+    if (ph * pw > 16) return false;
+    UPlan plans[16];
+    for (int i = 0; i < ph; ++i)
+        for (int j = 0; j < pw; ++j)
+            if (!plan(geo, bh, D, 1, i * c, j * c, &plans[i * pw + j])) return false;
+    for (int p = 0; p < ph * pw; ++p) {
+        UPlan &q = plans[p];
+        q.a.a = a;
+        q.a.attn = attn;
+        q.a.out = out;
+        q.a.alpha = alpha;
+        q.a.accumulate = p > 0;
+        bool ok = false;
+#define X(DD, C, T3)                                                               \
+    if (!ok && D == DD && q.c == C && q.t3 == T3) {                                \
+        if (!launch(avi_kernel<DD, C, C, T3>, q, s)) return false;                 \
+        ok = true;                                                                 \
+    }
+        NU_CASES(X)
+#undef X
+        if (!ok) return false;
+    }
+    return true;
 }
 
 }  // namespace nu
