@@ -15,6 +15,12 @@ window is measured in the same run and reported beside it.
 Effective FLOPs (the metric's convention): forward 4*N*heads*K*D, backward
 2.5x that, with N tokens and K = prod(kernel). Prints one JSON line on stdout;
 progress goes to stderr.
+
+The same function is also timed through the unfused ops (the script's method
+= 'unfused': window scores, softmax, weighted sum, and their backward AGRAD,
+VGRAD, softmax backward, QGRAD, KGRAD, on head-major copies of the same
+inputs) and reported under "unfused", with each op's share of the HBM
+roofline: the fused-versus-unfused comparison the issue is about.
 """
 from __future__ import annotations
 
@@ -162,6 +168,77 @@ class Runner:
         return start.elapsed_time(end) / steps, wall, per
 
 
+# ----------------------------------------------------------------------------- unfused leg
+# The same function through the unfused ops on head-major tensors (the issue's
+# method = 'unfused': na_qk, softmax, na_av and, in the backward, AGRAD, VGRAD,
+# the softmax backward, QGRAD and KGRAD), one kernel launch per op.
+
+def unfused_bytes(w):
+    """Algorithmic HBM bytes of each unfused op (every operand read once, every
+    result written once): vectors N*heads*D*4, attention arrays N*heads*K*4."""
+    t = w.tokens * w.heads * w.head_dim * 4
+    a = w.tokens * w.heads * w.window * 4
+    return {"qk": 2 * t + a, "softmax": 2 * a, "av": a + 2 * t, "agrad": 2 * t + a,
+            "vgrad": a + 2 * t, "softmax_bwd": 3 * a, "qgrad": a + 2 * t, "kgrad": a + 2 * t}
+
+
+class UnfusedRunner:
+    def __init__(self, w, host):
+        self.w = w
+        dev = torch.device("cuda:0")
+        hm = lambda t: t.movedim(-2, 1).contiguous().to(dev)  # noqa: E731
+        self.q, self.k, self.v, self.dout = (hm(t) for t in host)
+        self.probs = torch.empty(self.q.shape[:-1] + (w.window,), dtype=torch.float32, device=dev)
+        self.ds = torch.empty_like(self.probs)
+        self.out, self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(4))
+        kk, dd, sc = w.kernel, w.dilation, w.the_scale
+        self.ops = [
+            ("qk", lambda: na.na_qk(self.q, self.k, kk, dd, sc, attn=self.probs)),
+            ("softmax", lambda: na.na_softmax(self.probs, kk, dd, out=self.probs)),
+            ("av", lambda: na.na_av(self.probs, self.v, kk, dd, 1.0, out=self.out)),
+            ("agrad", lambda: na.na_qk(self.dout, self.v, kk, dd, 1.0, attn=self.ds)),
+            ("vgrad", lambda: na.na_av_inverse(self.probs, self.dout, kk, dd, 1.0, out=self.dv)),
+            ("softmax_bwd", lambda: na.na_softmax_bwd(self.probs, self.ds, kk, dd, out=self.ds)),
+            ("qgrad", lambda: na.na_av(self.ds, self.k, kk, dd, sc, out=self.dq)),
+            ("kgrad", lambda: na.na_av_inverse(self.ds, self.q, kk, dd, sc, out=self.dk)),
+        ]
+
+    def time(self, steps, warmup):
+        for _ in range(warmup):
+            for _, f in self.ops:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.ops) + 1)]
+              for _ in range(steps)]
+        for s in range(steps):
+            ev[s][0].record()
+            for i, (_, f) in enumerate(self.ops):
+                f()
+                ev[s][i + 1].record()
+        torch.cuda.synchronize()
+        per = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+               for i, (name, _) in enumerate(self.ops)}
+        step = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]))
+        return step, per
+
+
+def unfused_summary(w, step, per):
+    f_fwd, f_bwd = flops(w)
+    by = unfused_bytes(w)
+    name = max(per, key=per.get)
+    gbs = by[name] / (per[name] * 1e-3) / 1e9
+    return {"ms_per_step": round(step, 4),
+            "fwd_ms": round(sum(per[k] for k in ("qk", "softmax", "av")), 4),
+            "bwd_ms": round(sum(v for k, v in per.items() if k not in ("qk", "softmax", "av")), 4),
+            "tflops_total": round((f_fwd + f_bwd) / step / 1e9, 3),
+            "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+            "hbm_frac": {k: round(by[k] / (per[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k in per},
+            "roofline": {"bound": "hbm", "kernel": name, "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None, "bytes_per_launch": by[name],
+                         "avg_launch_ms": round(per[name], 4)}}
+
+
 def summarize(w, ms_step, per):
     f_fwd, f_bwd = flops(w)
     b_fwd, b_bwd, b_kern = algorithmic_bytes(w)
@@ -230,6 +307,7 @@ def main():
     ap.add_argument("--variant", default="gather", choices=["gather", "kvparallel"])
     ap.add_argument("--no-secondary", action="store_true", help="skip the 3D workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -288,10 +366,24 @@ def main():
     }
 
     host = r.host
+    del r
+    torch.cuda.empty_cache()
+    unfused = {}
+
+    def run_unfused(wl, h):
+        if args.no_unfused or wl.dtype != torch.float32:
+            return
+        u = UnfusedRunner(wl, h)
+        log(f"[bench] timing the unfused ops on {wl.name}")
+        step, per_u = u.time(args.steps, args.warmup)
+        unfused[wl.name] = unfused_summary(wl, step, per_u)
+        log(f"[bench] unfused {wl.name}: {unfused[wl.name]}")
+        del u
+        torch.cuda.empty_cache()
+
+    run_unfused(w, host)
     if not args.no_secondary and args.workload == HEADLINE:
         w3 = WORKLOADS[HEADLINE_3D]
-        del r
-        torch.cuda.empty_cache()
         r3 = Runner(w3, args.variant)
         log(f"[bench] timing {w3.name}")
         ms3, _, per3 = r3.time(args.steps, args.warmup)
@@ -299,8 +391,13 @@ def main():
         s3["roofline"] = roofline(w3, per3)
         result["secondary"] = {"workload": w3.name, **s3}
         log(f"[bench] {w3.name}: {s3}")
+        h3 = r3.host
         del r3
         torch.cuda.empty_cache()
+        run_unfused(w3, h3)
+        del h3
+    if unfused:
+        result["unfused"] = unfused
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

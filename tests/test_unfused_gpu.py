@@ -191,3 +191,47 @@ def test_unfused_rejects_bf16_and_bad_shapes():
         na.na_av(torch.zeros((1, 2, 8, 8, 8), device=dev), q, (3, 3))
     with pytest.raises(na.NaError):
         na.na_qk(q, q, (9, 3))   # window larger than the grid
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["2d_1024x1024_k9_h8_d32_f32", "3d_16x256x256_k3x5x5_h8_d32_f32"])
+def test_unfused_full_workload_sampled(name):
+    """The two fp32 benchmark workloads through the unfused path (head-major
+    copies of the benchmark's inputs, launched as bench.py launches them),
+    checked at sampled units: attention rows against softmax(scale * na_qk)
+    of the oracle, out and the gradients against the oracle's fused functions
+    (equal to the unfused composition by the oracle's own pins)."""
+    from fwd_bwd_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    say("unfused full workload", name)
+    q, k, v, dout = make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    hm = lambda t: t.movedim(-2, 1).contiguous().to(dev)  # noqa: E731
+    qd, kd, vd, dd = (hm(t) for t in (q, k, v, dout))
+    probs, out = na.na_unfused_fwd(qd, kd, vd, w.kernel, w.dilation, w.the_scale)
+    dq, dk, dv = na.na_unfused_bwd(qd, kd, vd, probs, dd, w.kernel, w.dilation, w.the_scale)
+    torch.cuda.synchronize()
+    # sampled units: head-major ids (b, head, token), grid corners and edges plus random ones
+    import itertools
+    rng = np.random.default_rng(0)
+    ntok = int(np.prod(w.grid))
+    pts = sorted(set(itertools.product(*[(0, 1, g // 2, g - 2, g - 1) for g in w.grid])))
+    ids = [((i % w.batch) * w.heads + (i * 7) % w.heads) * ntok + int(np.ravel_multi_index(p, w.grid))
+           for i, p in enumerate(pts)]
+    ids += rng.integers(0, w.batch * w.heads * ntok, 64).tolist()
+    sel_hm = np.array(sorted(set(ids)), np.int64)
+    b, rest = np.divmod(sel_hm, w.heads * ntok)
+    h, tok = np.divmod(rest, ntok)
+    sel_tm = (b * ntok + tok) * w.heads + h
+    D = w.head_dim
+    pick = lambda t, c: np64(t.reshape(-1, c)[torch.as_tensor(sel_hm, device=t.device)])  # noqa: E731
+    Q, K_, V, DO = (np64(t) for t in (q, k, v, dout))
+    qm, km = np.moveaxis(Q, -2, 1), np.moveaxis(K_, -2, 1)
+    P_ref = oracle.softmax(oracle.na_qk(qm, km, w.kernel, w.dilation, w.the_scale, sel=sel_hm))
+    o_ref, _ = oracle.na_fwd(Q, K_, V, w.kernel, w.dilation, w.the_scale, sel=sel_tm)
+    g_ref = oracle.na_bwd(Q, K_, V, DO, w.kernel, w.dilation, w.the_scale, sel=sel_tm)
+    check({"probs": pick(probs, w.window), "out": pick(out, D), "dq": pick(dq, D),
+           "dk": pick(dk, D), "dv": pick(dv, D)},
+          {"probs": P_ref, "out": o_ref, "dq": g_ref[0], "dk": g_ref[1], "dv": g_ref[2]},
+          f"unfused {name} sampled({sel_hm.size})")
