@@ -222,10 +222,124 @@ __global__ __launch_bounds__(256) void av_inverse_plain(Geo g, const float *__re
 }
 
 // ----------------------------------------------------------------------------
-// Window softmax and its backward over rows of K entries: sixteen lanes per
-// row, sixteen rows per workgroup; a row lives in registers (NR entries per
-// lane) when K <= 16 NR, otherwise it is read in passes (NR = 0).
+// Window softmax and its backward over rows of K entries. A workgroup takes 64
+// consecutive rows, one contiguous run of 64 K floats starting 16-byte aligned
+// (64 K is a multiple of 4), moved between HBM and LDS with 16-byte accesses;
+// four lanes share a row and reduce it with two shuffles. Rows of more than
+// kRowMax entries take the plain path below (sixteen lanes per row, read in
+// passes).
 
+constexpr int kRowsPerBlock = 64;
+constexpr int kRowMax = 160;   // 64 rows x 160 entries x 4 bytes = 40 KB of LDS per array
+
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, 4));
+    return fmaxf(v, __shfl_xor(v, 2, 4));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __shfl_xor(v, 1, 4);
+    return v + __shfl_xor(v, 2, 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy the first n & ~3 floats (global offset 16-byte aligned) global -> LDS
+// with direct 16-byte loads, all in flight at once; completion: waitcnt + barrier.
+__device__ __forceinline__ void block_in(const float *g, float *l, int n) {
+    const int lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < (n >> 2); i += 256) {
+        // lanes of a wave hold consecutive i: LDS base l + 4 (i - lane) is wave-uniform
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_global_load_lds(g + 4 * i, (lds_void *)(l + 4 * (i - lane)), 16, 0, 0);
+#else
+        (void)g; (void)l; (void)lane;
+#endif
+    }
+}
+__device__ __forceinline__ void block_out(const float *l, float *g, int n) {
+    const int n4 = n >> 2;
+    const float4 *l4 = reinterpret_cast<const float4 *>(l);
+    float4 *g4 = reinterpret_cast<float4 *>(g);
+    int i = threadIdx.x;
+    for (; i + 768 < n4; i += 1024) {
+        const float4 a = l4[i], b = l4[i + 256], c = l4[i + 512], d = l4[i + 768];
+        g4[i] = a;
+        g4[i + 256] = b;
+        g4[i + 512] = c;
+        g4[i + 768] = d;
+    }
+    for (; i < n4; i += 256) g4[i] = l4[i];
+}
+
+// Rows [row0, row0 + nr) of one block; nr = 64 except for the last block,
+// whose tail (nr * K not a multiple of 4) is moved with 4-byte accesses.
+__device__ __forceinline__ void tail_in(const float *g, float *l, int n) {
+    for (int i = (n & ~3) + (int)threadIdx.x; i < n; i += 256) l[i] = g[i];
+}
+__device__ __forceinline__ void tail_out(const float *l, float *g, int n) {
+    for (int i = (n & ~3) + (int)threadIdx.x; i < n; i += 256) g[i] = l[i];
+}
+
+__global__ __launch_bounds__(256) void softmax_blocks(const float *x, float *y, int64_t rows,
+                                                      int K) {
+    __shared__ __align__(16) float xs[kRowsPerBlock * kRowMax];
+    const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock;
+    const int nr = (int)(rows - row0 < kRowsPerBlock ? rows - row0 : kRowsPerBlock);
+    const int n = nr * K;
+    const float *xg = x + row0 * K;
+    float *yg = y + row0 * K;
+    block_in(xg, xs, n);
+    tail_in(xg, xs, n);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int r = threadIdx.x >> 2, l = threadIdx.x & 3;
+    float *xr = xs + r * K;
+    const bool ok = r < nr;
+    float m = -INFINITY;
+    for (int i = l; ok && i < K; i += 4) m = fmaxf(m, xr[i]);
+    m = quad_max(m);
+    float sum = 0.f;
+    for (int i = l; ok && i < K; i += 4) {
+        const float e = __expf(xr[i] - m);
+        xr[i] = e;
+        sum += e;
+    }
+    const float inv = 1.f / quad_sum(sum);
+    for (int i = l; ok && i < K; i += 4) xr[i] *= inv;
+    __syncthreads();
+    block_out(xs, yg, n);
+    tail_out(xs, yg, n);
+}
+
+// dS = P (dP - sum_j P dP); ds may alias dp.
+__global__ __launch_bounds__(256) void softmax_bwd_blocks(const float *p, const float *dp, float *ds,
+                                                          int64_t rows, int K) {
+    __shared__ __align__(16) float ps[kRowsPerBlock * kRowMax];
+    __shared__ __align__(16) float gs[kRowsPerBlock * kRowMax];
+    const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock;
+    const int nr = (int)(rows - row0 < kRowsPerBlock ? rows - row0 : kRowsPerBlock);
+    const int n = nr * K;
+    block_in(p + row0 * K, ps, n);
+    block_in(dp + row0 * K, gs, n);
+    tail_in(p + row0 * K, ps, n);
+    tail_in(dp + row0 * K, gs, n);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int r = threadIdx.x >> 2, l = threadIdx.x & 3;
+    const bool ok = r < nr;
+    const float *pr = ps + r * K;
+    float *gr = gs + r * K;
+    float sum = 0.f;
+    for (int i = l; ok && i < K; i += 4) sum += pr[i] * gr[i];
+    sum = quad_sum(sum);
+    for (int i = l; ok && i < K; i += 4) gr[i] = pr[i] * (gr[i] - sum);
+    __syncthreads();
+    block_out(gs, ds + row0 * K, n);
+    tail_out(gs, ds + row0 * K, n);
+}
+
+// Rows longer than kRowMax: sixteen lanes per row, sixteen rows per
+// workgroup, each row read in passes.
 __device__ __forceinline__ float row_max16(float v) {
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
@@ -237,75 +351,31 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-template <int NR>
-__global__ __launch_bounds__(256) void softmax_rows(const float *__restrict__ x, float *y,
-                                                    int64_t rows, int K) {
+__global__ __launch_bounds__(256) void softmax_rows(const float *x, float *y, int64_t rows, int K) {
     const int64_t row = blockIdx.x * 16ll + (threadIdx.x >> 4);
     const int l = threadIdx.x & 15;
     const bool ok = row < rows;   // every lane takes part in the shuffles
     const float *xr = x + (ok ? row : 0) * K;
     float *yr = y + (ok ? row : 0) * K;
-    if constexpr (NR > 0) {
-        float v[NR];
-        float m = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int idx = l + 16 * i;
-            v[i] = (ok && idx < K) ? xr[idx] : -INFINITY;
-            m = fmaxf(m, v[i]);
-        }
-        m = row_max16(m);
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            v[i] = (l + 16 * i < K) ? __expf(v[i] - m) : 0.f;
-            s += v[i];
-        }
-        const float inv = 1.f / row_sum16(s);
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-            if (ok && l + 16 * i < K) yr[l + 16 * i] = v[i] * inv;
-    } else {
-        float m = -INFINITY;
-        for (int idx = l; ok && idx < K; idx += 16) m = fmaxf(m, xr[idx]);
-        m = row_max16(m);
-        float s = 0.f;
-        for (int idx = l; ok && idx < K; idx += 16) s += __expf(xr[idx] - m);
-        const float inv = 1.f / row_sum16(s);
-        for (int idx = l; ok && idx < K; idx += 16) yr[idx] = __expf(xr[idx] - m) * inv;
-    }
+    float m = -INFINITY;
+    for (int idx = l; ok && idx < K; idx += 16) m = fmaxf(m, xr[idx]);
+    m = row_max16(m);
+    float s = 0.f;
+    for (int idx = l; ok && idx < K; idx += 16) s += __expf(xr[idx] - m);
+    const float inv = 1.f / row_sum16(s);
+    for (int idx = l; ok && idx < K; idx += 16) yr[idx] = __expf(xr[idx] - m) * inv;
 }
 
-// dS = P (dP - sum_j P dP); ds may alias dp.
-template <int NR>
-__global__ __launch_bounds__(256) void softmax_bwd_rows(const float *__restrict__ p,
-                                                        const float *dp, float *ds, int64_t rows,
-                                                        int K) {
+__global__ __launch_bounds__(256) void softmax_bwd_rows(const float *p, const float *dp, float *ds,
+                                                        int64_t rows, int K) {
     const int64_t row = blockIdx.x * 16ll + (threadIdx.x >> 4);
     const int l = threadIdx.x & 15;
     const bool ok = row < rows;
     const int64_t off = (ok ? row : 0) * K;
-    if constexpr (NR > 0) {
-        float pv[NR], gv[NR];
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int idx = l + 16 * i;
-            const bool in = ok && idx < K;
-            pv[i] = in ? p[off + idx] : 0.f;
-            gv[i] = in ? dp[off + idx] : 0.f;
-            s += pv[i] * gv[i];
-        }
-        s = row_sum16(s);
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-            if (ok && l + 16 * i < K) ds[off + l + 16 * i] = pv[i] * (gv[i] - s);
-    } else {
-        float s = 0.f;
-        for (int idx = l; ok && idx < K; idx += 16) s += p[off + idx] * dp[off + idx];
-        s = row_sum16(s);
-        for (int idx = l; ok && idx < K; idx += 16) ds[off + idx] = p[off + idx] * (dp[off + idx] - s);
-    }
+    float s = 0.f;
+    for (int idx = l; ok && idx < K; idx += 16) s += p[off + idx] * dp[off + idx];
+    s = row_sum16(s);
+    for (int idx = l; ok && idx < K; idx += 16) ds[off + idx] = p[off + idx] * (dp[off + idx] - s);
 }
 
 // ----------------------------------------------------------------------------
@@ -346,33 +416,36 @@ na_status run_av_inverse(const UProb &q, const float *attn, const float *a, floa
     return launched();
 }
 
-// Launch a row kernel with the smallest register row that holds K entries.
-#define NA_LAUNCH_ROWS(KERN, K, rows, st, ...)                                     \
-    do {                                                                           \
-        const dim3 grid_((unsigned)(((rows) + 15) / 16)), block_(256);             \
-        const int need_ = ((K) + 15) / 16;                                         \
-        if (need_ <= 2) KERN<2><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K);   \
-        else if (need_ <= 4) KERN<4><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K);   \
-        else if (need_ <= 6) KERN<6><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K);   \
-        else if (need_ <= 8) KERN<8><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K);   \
-        else if (need_ <= 12) KERN<12><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K); \
-        else if (need_ <= 16) KERN<16><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K); \
-        else if (need_ <= 24) KERN<24><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K); \
-        else KERN<0><<<grid_, block_, 0, st>>>(__VA_ARGS__, rows, K);             \
-    } while (0)
-
 na_status run_softmax(const UProb &q, const float *x, float *y, hipStream_t st) {
     if (q.units == 0) return NA_OK;
-    if ((q.units + 15) / 16 > INT32_MAX) return NA_ERR_UNSUPPORTED;
-    NA_LAUNCH_ROWS(softmax_rows, q.g.K, q.units, st, x, y);
+    if (q.g.K <= kRowMax) {
+        const int64_t blocks = (q.units + kRowsPerBlock - 1) / kRowsPerBlock;
+        if (blocks > INT32_MAX) return NA_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(softmax_blocks, dim3((unsigned)blocks), dim3(256), 0, st, x, y, q.units,
+                           q.g.K);
+    } else {
+        const int64_t blocks = (q.units + 15) / 16;
+        if (blocks > INT32_MAX) return NA_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(softmax_rows, dim3((unsigned)blocks), dim3(256), 0, st, x, y, q.units,
+                           q.g.K);
+    }
     return launched();
 }
 
 na_status run_softmax_bwd(const UProb &q, const float *p, const float *dp, float *ds,
                           hipStream_t st) {
     if (q.units == 0) return NA_OK;
-    if ((q.units + 15) / 16 > INT32_MAX) return NA_ERR_UNSUPPORTED;
-    NA_LAUNCH_ROWS(softmax_bwd_rows, q.g.K, q.units, st, p, dp, ds);
+    if (q.g.K <= kRowMax) {
+        const int64_t blocks = (q.units + kRowsPerBlock - 1) / kRowsPerBlock;
+        if (blocks > INT32_MAX) return NA_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(softmax_bwd_blocks, dim3((unsigned)blocks), dim3(256), 0, st, p, dp, ds,
+                           q.units, q.g.K);
+    } else {
+        const int64_t blocks = (q.units + 15) / 16;
+        if (blocks > INT32_MAX) return NA_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(softmax_bwd_rows, dim3((unsigned)blocks), dim3(256), 0, st, p, dp, ds,
+                           q.units, q.g.K);
+    }
     return launched();
 }
 

@@ -93,37 +93,108 @@ __device__ __forceinline__ int64_t run_index(const UArgs &a, const RowRun &rr, i
     return rr.base + col * rr.cstride + (e - col * a.KP);
 }
 
-// global -> LDS with direct loads (no register round trip, all in flight at
-// once); completion: stage_wait().
-__device__ __forceinline__ void load_round(const UArgs &a, const TileCtx &w, int wave, int r0,
-                                           int it, float *buf, const float *src) {
+// Per-lane offsets of the elements e = lane + 64 m (m < kRunSteps) of a row
+// run of `cols` points relative to its base: every row of a box has the same
+// shape, so they are computed once per tile instead of once per element.
+constexpr int kRunSteps = 16;
+
+struct RunOffs {
+    int off[kRunSteps];
+    bool ok;  // the run fits kRunSteps steps of 64 lanes
+};
+
+__device__ __forceinline__ RunOffs run_offs(const UArgs &a, const TileCtx &w, int cols) {
+    RunOffs ro;
     const int lane = threadIdx.x & 63;
+    const int n = cols * a.KP;
+    ro.ok = n <= 64 * kRunSteps;
+    const int cstride = (int)(w.lst[2] * a.K);
+#pragma unroll
+    for (int m = 0; m < kRunSteps; ++m) {
+        const int e = lane + 64 * m;
+        const int col = fdiv(e, a.fKP);
+        ro.off[m] = col * cstride + (e - col * a.KP);
+    }
+    return ro;
+}
+
+// One row run, global -> LDS with direct loads (no register round trip, all in
+// flight at once), by waves wv, wv + nw, ... of the workgroup, 64 lanes per
+// step: 16-byte pieces when the run is contiguous and both ends are 16-byte
+// aligned (vec), else 4-byte ones. Completion: stage_wait().
+__device__ __forceinline__ void load_run(const UArgs &a, const RowRun &rr, const float *src,
+                                         float *l, bool vec, int wv, int nw,
+                                         const RunOffs *ro = nullptr) {
+    const int lane = threadIdx.x & 63;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (vec) {
+        const float *g = src + rr.base;
+        const int n4 = rr.n >> 2;
+        for (int b = 64 * wv; b < n4; b += 64 * nw)
+            if (b + lane < n4)
+                __builtin_amdgcn_global_load_lds(g + 4 * (b + lane), (lds_void *)(l + 4 * b), 16, 0, 0);
+        for (int b = 4 * n4 + 64 * wv; b < rr.n; b += 64 * nw)
+            if (b + lane < rr.n)
+                __builtin_amdgcn_global_load_lds(g + b + lane, (lds_void *)(l + b), 4, 0, 0);
+    } else if (ro && ro->ok && nw == 1) {
+        const float *g = src + rr.base;
+#pragma unroll
+        for (int m = 0; m < kRunSteps; ++m)
+            if (64 * m + lane < rr.n)
+                __builtin_amdgcn_global_load_lds(g + ro->off[m], (lds_void *)(l + 64 * m), 4, 0, 0);
+    } else {
+        for (int b = 64 * wv; b < rr.n; b += 64 * nw)
+            if (b + lane < rr.n)
+                __builtin_amdgcn_global_load_lds(src + run_index(a, rr, b + lane), (lds_void *)(l + b),
+                                                 4, 0, 0);
+    }
+#else
+    (void)a; (void)rr; (void)src; (void)l; (void)vec; (void)wv; (void)nw; (void)lane; (void)ro;
+#endif
+}
+
+__device__ __forceinline__ bool run_vec(const RowRun &rr, int lds_off) {
+    return rr.contiguous && (rr.base & 3) == 0 && (lds_off & 3) == 0;
+}
+
+__device__ __forceinline__ void load_round(const UArgs &a, const TileCtx &w, int wave, int r0,
+                                           int it, float *buf, const float *src,
+                                           const RunOffs &ro) {
     const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
     for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
         const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
-        float *brow = buf + row * 8 * a.KP;
-        for (int e0 = 0; e0 < rr.n; e0 += 64) {
-            if (e0 + lane < rr.n) {
-                const float *g = src + run_index(a, rr, e0 + lane);
-#if defined(__HIP_DEVICE_COMPILE__)
-                __builtin_amdgcn_global_load_lds(g, (lds_void *)(brow + e0), 4, 0, 0);
-#else
-                (void)g;
-                (void)brow;
-#endif
-            }
-        }
+        load_run(a, rr, src, buf + row * 8 * a.KP, run_vec(rr, row * 8 * a.KP), 0, 1, &ro);
     }
 }
 
-// LDS -> global.
+// LDS -> global, one wave: 16-byte pieces where aligned, else 4-byte ones,
+// four LDS reads in flight per lane.
 __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, int wave, int r0,
-                                            int it, const float *buf, float *dst) {
+                                            int it, const float *buf, float *dst,
+                                            const RunOffs &ro) {
     const int lane = threadIdx.x & 63;
     const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
     for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
         const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
         const float *brow = buf + row * 8 * a.KP;
+        if (run_vec(rr, row * 8 * a.KP)) {
+            const int n4 = rr.n >> 2;
+            const float4 *l4 = reinterpret_cast<const float4 *>(brow);
+            float4 *g4 = reinterpret_cast<float4 *>(dst + rr.base);
+            for (int b = lane; b < n4; b += 64) g4[b] = l4[b];
+            for (int e = 4 * n4 + lane; e < rr.n; e += 64) dst[rr.base + e] = brow[e];
+            continue;
+        }
+        if (ro.ok) {
+            float v[kRunSteps];
+#pragma unroll
+            for (int m = 0; m < kRunSteps; ++m)
+                v[m] = 64 * m + lane < rr.n ? brow[64 * m + lane] : 0.f;
+#pragma unroll
+            for (int m = 0; m < kRunSteps; ++m)
+                if (64 * m + lane < rr.n) dst[rr.base + ro.off[m]] = v[m];
+            continue;
+        }
         for (int e0 = 0; e0 < rr.n; e0 += 4 * 64) {
             float v[4];
 #pragma unroll
@@ -165,6 +236,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     // the lane's point in its wave's 8 x 8 quarter, and the wave's LDS buffer
     const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
     float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
+    const RunOffs ro = run_offs(a, w, 8);
 
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
@@ -213,7 +285,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     }
             }
             __syncthreads();
-            store_round(a, w, wave, r0, j, buf, a.attn_out);
+            store_round(a, w, wave, r0, j, buf, a.attn_out, ro);
             __syncthreads();
         }
     }
@@ -242,6 +314,7 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
     const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PS + c * 16;
     const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
     float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
+    const RunOffs ro = run_offs(a, w, 8);
 
     f4 acc[G];
 #pragma unroll
@@ -258,7 +331,7 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[i][e] = 0.f;
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
-            load_round(a, w, wave, r0, j, buf, a.attn);
+            load_round(a, w, wave, r0, j, buf, a.attn, ro);
             stage_wait();
             if (L.active && lr >= r0 && lr < r0 + a.rows_round) {
                 const float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
@@ -344,6 +417,7 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
     const int rel1 = lo[1] - U[1], rel2 = lo[2] - U[2];
     const char *baseB = smem + rel1 * rb + rel2 * PS + c * 16;
     float *abuf = reinterpret_cast<float *>(smem);
+    const RunOffs aro = run_offs(a, w, E[2]);
 
     f4 acc[G];
 #pragma unroll
@@ -363,36 +437,25 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
         for (int r0 = 0; r0 < E[1]; r0 += a.chunk_rows) {
             const int rows = imin(a.chunk_rows, E[1] - r0);
             if (j > 0 || r0 > 0) __syncthreads();
-            {
-                const int wave = threadIdx.x >> 6;
-                for (int r = 0; r < rows && U[1] + r0 + r < w.n[1]; ++r) {
-                    const RowRun rr = row_run(a, w, tq, U[1] + r0 + r, U[2], E[2], it);
-                    float *brow = abuf + r * E[2] * a.KP;
-                    for (int e0 = 64 * wave; e0 < rr.n; e0 += kThreads) {
-                        if (e0 + lane < rr.n) {
-                            const float *g = a.attn + run_index(a, rr, e0 + lane);
-#if defined(__HIP_DEVICE_COMPILE__)
-                            __builtin_amdgcn_global_load_lds(g, (lds_void *)(brow + e0), 4, 0, 0);
-#else
-                            (void)g;
-                            (void)brow;
-#endif
-                        }
-                    }
-                }
+            for (int r = wave; r < rows && U[1] + r0 + r < w.n[1]; r += kWaves) {
+                const RowRun rr = row_run(a, w, tq, U[1] + r0 + r, U[2], E[2], it);
+                const int off = r * E[2] * a.KP;
+                load_run(a, rr, a.attn, abuf + off, run_vec(rr, off), 0, 1, &aro);
             }
             stage_wait();
             // walk rows of this lane inside the chunk
             const int h0 = imax(0, r0 - rel1), h1 = imin(32, r0 - rel1 + rows);
             const unsigned rm = h1 > h0 ? vm[1] & bit_range(h0, h1 - h0) : 0u;
             const float *cb = abuf + ((rel1 - r0) * E[2] + rel2) * a.KP;
+            if (rm) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
-                    if ((rm >> h) & (vm[2] >> wc) & 1u) s[i][e] = cb[rowt[h] + colt[wc]];
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
+                        if ((rm >> h) & (vm[2] >> wc) & 1u) s[i][e] = cb[rowt[h] + colt[wc]];
+                    }
+            }
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) pin4(s[i]);
