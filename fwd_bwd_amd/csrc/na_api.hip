@@ -16,6 +16,7 @@
 namespace {
 
 using na::bf16;
+using na::f16;
 
 constexpr int kThreads = 256;  // elementwise kernels
 
@@ -34,7 +35,7 @@ struct Prob {
 na_status validate(const na_problem *p, Prob *out) {
     if (!p) return NA_ERR_INVALID_ARG;
     if (p->ndim != 2 && p->ndim != 3) return NA_ERR_INVALID_ARG;
-    if (p->dtype != NA_F32 && p->dtype != NA_BF16) return NA_ERR_INVALID_ARG;
+    if (p->dtype != NA_F32 && p->dtype != NA_BF16 && p->dtype != NA_F16) return NA_ERR_INVALID_ARG;
     if (p->batch < 1 || p->heads < 1 || p->head_dim < 1) return NA_ERR_INVALID_ARG;
     if (!std::isfinite(p->scale)) return NA_ERR_INVALID_ARG;
     const int nd = (int)p->ndim;
@@ -548,12 +549,13 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     a.lse = lse;
     a.qscale = pr.scale * na::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const bool f32 = pr.dtype == NA_F32;
-    switch (pr.head_dim) {
-        case 16: return f32 ? run_fwd<float, 16>(pr, a, s) : run_fwd<bf16, 16>(pr, a, s);
-        case 32: return f32 ? run_fwd<float, 32>(pr, a, s) : run_fwd<bf16, 32>(pr, a, s);
-        case 64: return f32 ? run_fwd<float, 64>(pr, a, s) : run_fwd<bf16, 64>(pr, a, s);
-    }
+#define NA_FWD_D(D)                                                   \
+    case D:                                                           \
+        if (pr.dtype == NA_F32) return run_fwd<float, D>(pr, a, s);   \
+        if (pr.dtype == NA_BF16) return run_fwd<bf16, D>(pr, a, s);   \
+        return run_fwd<f16, D>(pr, a, s);
+    switch (pr.head_dim) { NA_FWD_D(16) NA_FWD_D(32) NA_FWD_D(64) }
+#undef NA_FWD_D
     return NA_ERR_UNSUPPORTED;
 }
 
@@ -591,18 +593,13 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     a.qscale = pr.scale * na::kLog2e;
     a.scale = pr.scale;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const bool f32 = pr.dtype == NA_F32;
-    switch (pr.head_dim) {
-        case 16:
-            return f32 ? run_bwd<float, 16>(pr, a, variant, phases, s)
-                       : run_bwd<bf16, 16>(pr, a, variant, phases, s);
-        case 32:
-            return f32 ? run_bwd<float, 32>(pr, a, variant, phases, s)
-                       : run_bwd<bf16, 32>(pr, a, variant, phases, s);
-        case 64:
-            return f32 ? run_bwd<float, 64>(pr, a, variant, phases, s)
-                       : run_bwd<bf16, 64>(pr, a, variant, phases, s);
-    }
+#define NA_BWD_D(D)                                                                 \
+    case D:                                                                         \
+        if (pr.dtype == NA_F32) return run_bwd<float, D>(pr, a, variant, phases, s); \
+        if (pr.dtype == NA_BF16) return run_bwd<bf16, D>(pr, a, variant, phases, s); \
+        return run_bwd<f16, D>(pr, a, variant, phases, s);
+    switch (pr.head_dim) { NA_BWD_D(16) NA_BWD_D(32) NA_BWD_D(64) }
+#undef NA_BWD_D
     return NA_ERR_UNSUPPORTED;
 }
 

@@ -11,6 +11,7 @@ namespace na {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16;  // storage of a bfloat16 value
+typedef _Float16 f16;   // IEEE binary16
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -77,6 +78,43 @@ struct Io<bf16> {
         uint2 v = *reinterpret_cast<const uint2 *>(lds);
         d[0] = bf16_to_f32(v.x & 0xffffu); d[1] = bf16_to_f32(v.x >> 16);
         d[2] = bf16_to_f32(v.y & 0xffffu); d[3] = bf16_to_f32(v.y >> 16);
+    }
+};
+
+template <>
+struct Io<f16> {
+    static constexpr int kPerChunk = 8;
+    __device__ __forceinline__ static float cvt(uint32_t h) {
+        return (float)__builtin_bit_cast(f16, (uint16_t)h);
+    }
+    // round to nearest, ties to even (the default rounding mode of the conversion)
+    __device__ __forceinline__ static uint32_t bits(float f) {
+        return __builtin_bit_cast(uint16_t, (f16)f);
+    }
+    __device__ __forceinline__ static void load4(const f16 *p, float *d) {
+        uint2 v = *reinterpret_cast<const uint2 *>(p);
+        d[0] = cvt(v.x & 0xffffu); d[1] = cvt(v.x >> 16);
+        d[2] = cvt(v.y & 0xffffu); d[3] = cvt(v.y >> 16);
+    }
+    __device__ __forceinline__ static void store4(f16 *p, const float *s) {
+        uint2 v;
+        v.x = bits(s[0]) | (bits(s[1]) << 16);
+        v.y = bits(s[2]) | (bits(s[3]) << 16);
+        *reinterpret_cast<uint2 *>(p) = v;
+    }
+    __device__ __forceinline__ static void chunk(const char *lds, float *d) {
+        uint4 v = *reinterpret_cast<const uint4 *>(lds);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[2 * i] = cvt(w[i] & 0xffffu);
+            d[2 * i + 1] = cvt(w[i] >> 16);
+        }
+    }
+    __device__ __forceinline__ static void quad(const char *lds, float *d) {
+        uint2 v = *reinterpret_cast<const uint2 *>(lds);
+        d[0] = cvt(v.x & 0xffffu); d[1] = cvt(v.x >> 16);
+        d[2] = cvt(v.y & 0xffffu); d[3] = cvt(v.y >> 16);
     }
 };
 

@@ -9,7 +9,8 @@ standard normal, token-major [B, (T,) H, W, heads, head_dim], and the backward
 driven by loss = output.sum(), i.e. dout = ones. The two headline shapes are
 the issue's 2D 1024x1024 grid with a 9x9 kernel and 3D 16x256x256 grid with a
 (3, 5, 5) kernel, both with 8 heads of dimension 32 in fp32. The bf16 cases
-draw dout from a standard normal as well.
+draw dout from a standard normal as well. The same two shapes in fp16 follow
+the maintainer's fp16 profile of the fused op (same script, dout = ones).
 
 Draw order from one CPU torch.Generator seeded with `seed`: q, k, v, then dout
 (when it is random), each in fp32, then cast to the workload dtype with
@@ -77,6 +78,11 @@ WORKLOADS: Dict[str, Workload] = {
     "2d_b4_512x512_k13_d2_h4_d64_bf16": Workload("2d_b4_512x512_k13_d2_h4_d64_bf16", 4,
                                                  (512, 512), 4, 64, (13, 13), (2, 2),
                                                  torch.bfloat16, False, 64 ** -0.5),
+    "2d_1024x1024_k9_h8_d32_f16": Workload("2d_1024x1024_k9_h8_d32_f16", 1, (1024, 1024), 8, 32,
+                                           (9, 9), (1, 1), torch.float16, True, 32 ** -0.5),
+    "3d_16x256x256_k3x5x5_h8_d32_f16": Workload("3d_16x256x256_k3x5x5_h8_d32_f16", 1,
+                                                (16, 256, 256), 8, 32, (3, 5, 5), (1, 1, 1),
+                                                torch.float16, True, 32 ** -0.5),
 }
 
 # the configuration the benchmark's headline number is quoted on, and the 3D one beside it

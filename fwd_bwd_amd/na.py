@@ -24,6 +24,7 @@ NA_ERR_HIP = 4
 
 NA_F32 = 0
 NA_BF16 = 1
+NA_F16 = 2
 
 NA_BWD_GATHER = 0
 NA_BWD_KVPARALLEL = 1
@@ -122,7 +123,7 @@ def _tuple(v: Union[int, Sequence[int]], n: int) -> Tuple[int, ...]:
     return v
 
 
-_DTYPES = {torch.float32: NA_F32, torch.bfloat16: NA_BF16}
+_DTYPES = {torch.float32: NA_F32, torch.bfloat16: NA_BF16, torch.float16: NA_F16}
 
 
 def make_problem(shape: Sequence[int], dtype: torch.dtype, kernel_size, dilation=1,

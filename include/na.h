@@ -60,7 +60,9 @@ typedef enum {
 
 typedef enum {
     NA_F32 = 0,   /* fp32 tensors, fp32 arithmetic */
-    NA_BF16 = 1   /* bf16 tensors (round-to-nearest-even on output), fp32 arithmetic */
+    NA_BF16 = 1,  /* bf16 tensors (round-to-nearest-even on output), fp32 arithmetic */
+    NA_F16 = 2    /* IEEE fp16 tensors (round-to-nearest-even on output), fp32 arithmetic
+                     (the issue's maintainer profiles the fused op at fp16 beside fp32) */
 } na_dtype;
 
 /* Backward strategies (the NATTEN issue's use_kv_parallelism_in_fused_na

@@ -20,7 +20,9 @@ from fwd_bwd_amd.inputs import WORKLOADS, make_inputs, make_random
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# fp16: outputs are rounded to binary16 (relative step 2^-11 ~ 4.9e-4) after fp32
+# accumulation; four rounding steps of the largest output is the bar.
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-3}
 
 
 def say(*a):
@@ -106,6 +108,11 @@ SMALL = [
     ((1, 5, 40, 36, 1, 32), (3, 7, 7), 1, torch.float32),
     ((1, 34, 35, 2, 16), (9, 9), 1, torch.float32),
     ((2, 33, 30, 1, 32), (7, 7), 1, torch.float32),
+    # fp16 (binary16 storage, fp32 arithmetic): 2D, 3D, dilation, every head_dim
+    ((1, 19, 23, 2, 32), (5, 7), 1, torch.float16),
+    ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
+    ((2, 26, 27, 2, 64), (5, 5), 2, torch.float16),
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.float16),
 ]
 
 
@@ -208,7 +215,8 @@ def sample_units(w, n_random=96, seed=0):
 
 
 FULL = ["2d_1024x1024_k9_h8_d32_f32", "3d_16x256x256_k3x5x5_h8_d32_f32",
-        "3d_b2_8x128x128_k5x7x7_h8_d32_bf16", "2d_b4_512x512_k13_d2_h4_d64_bf16"]
+        "3d_b2_8x128x128_k5x7x7_h8_d32_bf16", "2d_b4_512x512_k13_d2_h4_d64_bf16",
+        "2d_1024x1024_k9_h8_d32_f16", "3d_16x256x256_k3x5x5_h8_d32_f16"]
 
 
 @pytest.mark.parametrize("name", FULL)
