@@ -68,6 +68,10 @@ def _bind(path):
     lib.oracle_na_av.restype = None
     lib.oracle_na_av_inverse.argtypes = [P, dp, dp, ctypes.c_double, ctypes.c_int64, ip, dp]
     lib.oracle_na_av_inverse.restype = None
+    lib.oracle_na_qk_rpb.argtypes = [P, dp, dp, ctypes.c_double, dp, ctypes.c_int64, ip, dp]
+    lib.oracle_na_qk_rpb.restype = None
+    lib.oracle_na_rpb_grad.argtypes = [P, dp, dp]
+    lib.oracle_na_rpb_grad.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -240,8 +244,15 @@ def _problem_hm(shape_hm, kernel, dilation, head_dim):
     return _problem(tm, kernel, dilation, 1.0)
 
 
-def na_qk(a, b, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
-    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> (the script's na*_qk times alpha).
+def rpb_shape(kernel, heads):
+    """Shape of a relative positional bias table: [heads, 2k-1 per axis]."""
+    return (heads,) + tuple(2 * int(k) - 1 for k in kernel)
+
+
+def na_qk(a, b, kernel, dilation=1, alpha=1.0, sel=None, rpb=None, lib=None):
+    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> (the script's na*_qk times alpha),
+    plus rpb[head][offset of the key from the query] when a bias table is given
+    (shape rpb_shape(kernel, heads)).
 
     a, b: [B, heads, (T,) H, W, D]. Returns [B, heads, (T,) H, W, K], or [n, K]
     for the selected query units.
@@ -252,8 +263,17 @@ def na_qk(a, b, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
     n, s = _sel_tm(sel, a.shape)
     units = n if s is not None else int(np.prod(a.shape[:-1]))
     attn = np.empty((units, K), np.float64)
-    (lib or _load()).oracle_na_qk(ctypes.byref(p), _dptr(a_tm), _dptr(b_tm), float(alpha), n,
-                                  None if s is None else _iptr(s), _dptr(attn))
+    if rpb is None:
+        (lib or _load()).oracle_na_qk(ctypes.byref(p), _dptr(a_tm), _dptr(b_tm), float(alpha), n,
+                                      None if s is None else _iptr(s), _dptr(attn))
+    else:
+        rp = _f64(rpb)
+        if rp.shape != rpb_shape(kernel if not np.isscalar(kernel) else (kernel,) * (a.ndim - 3),
+                                 a.shape[1]):
+            raise ValueError("rpb must have shape rpb_shape(kernel, heads)")
+        (lib or _load()).oracle_na_qk_rpb(ctypes.byref(p), _dptr(a_tm), _dptr(b_tm), float(alpha),
+                                          _dptr(rp), n, None if s is None else _iptr(s),
+                                          _dptr(attn))
     if s is not None:
         return attn
     return _to_hm(attn.reshape(a_tm.shape[:-1] + (K,)))
@@ -294,6 +314,18 @@ def na_av_inverse(attn, a, kernel, dilation=1, alpha=1.0, sel=None, lib=None):
     return out if s is not None else _to_hm(out)
 
 
+def rpb_grad(dattn, kernel, dilation=1, lib=None):
+    """Gradient of the bias table: for every head and relative offset, the sum
+    of dattn over all batch elements, queries and window entries at that
+    offset. dattn: [B, heads, (T,) H, W, K]. Returns rpb_shape(kernel, heads)."""
+    at_tm = _to_tm(dattn)
+    kern = (kernel,) * (dattn.ndim - 3) if np.isscalar(kernel) else tuple(kernel)
+    p = _problem_hm(dattn.shape, kern, dilation, 1)
+    out = np.empty(rpb_shape(kern, dattn.shape[1]), np.float64)
+    (lib or _load()).oracle_na_rpb_grad(ctypes.byref(p), _dptr(at_tm), _dptr(out))
+    return out
+
+
 def softmax(x):
     """Softmax over the last (window) axis, as the script's F.softmax(attn, dim=-1):
     exp(x - max) / sum exp(x - max), in float64."""
@@ -308,23 +340,26 @@ def softmax_bwd(p, dp):
     return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
 
 
-def unfused_fwd(q, k, v, kernel, dilation=1, scale=None, lib=None):
-    """The unfused forward on head-major tensors: P = softmax(scale * na_qk(q, k)),
-    out = na_av(P, v). Returns (P, out)."""
+def unfused_fwd(q, k, v, kernel, dilation=1, scale=None, rpb=None, lib=None):
+    """The unfused forward on head-major tensors: P = softmax(scale * na_qk(q, k)
+    [+ rpb]), out = na_av(P, v). Returns (P, out)."""
     scale = q.shape[-1] ** -0.5 if scale is None else scale
-    P = softmax(na_qk(q, k, kernel, dilation, scale, lib=lib))
+    P = softmax(na_qk(q, k, kernel, dilation, scale, rpb=rpb, lib=lib))
     return P, na_av(P, v, kernel, dilation, 1.0, lib=lib)
 
 
-def unfused_bwd(q, k, v, P, dout, kernel, dilation=1, scale=None, lib=None):
+def unfused_bwd(q, k, v, P, dout, kernel, dilation=1, scale=None, want_rpb=False, lib=None):
     """Backward of sum(out * dout) through the unfused ops (AGRAD, softmax
-    backward, QGRAD, KGRAD, VGRAD). Returns (dq, dk, dv)."""
+    backward, QGRAD, KGRAD, VGRAD). Returns (dq, dk, dv), and the bias
+    gradient as a fourth value when want_rpb."""
     scale = q.shape[-1] ** -0.5 if scale is None else scale
     dP = na_qk(dout, v, kernel, dilation, 1.0, lib=lib)             # AGRAD
     dv = na_av_inverse(P, dout, kernel, dilation, 1.0, lib=lib)      # VGRAD
     dS = softmax_bwd(P, dP)
     dq = na_av(dS, k, kernel, dilation, scale, lib=lib)              # QGRAD
     dk = na_av_inverse(dS, q, kernel, dilation, scale, lib=lib)      # KGRAD
+    if want_rpb:
+        return dq, dk, dv, rpb_grad(dS, kernel, dilation, lib=lib)
     return dq, dk, dv
 
 
@@ -356,6 +391,9 @@ class Bound:
 
     def na_av_inverse(self, *a, **kw):
         return na_av_inverse(*a, lib=self.lib, **kw)
+
+    def rpb_grad(self, *a, **kw):
+        return rpb_grad(*a, lib=self.lib, **kw)
 
     def unfused_fwd(self, *a, **kw):
         return unfused_fwd(*a, lib=self.lib, **kw)

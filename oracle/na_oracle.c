@@ -414,6 +414,73 @@ void oracle_na_av_inverse(const oracle_problem *p, const double *attn, const dou
     }
 }
 
+/*
+ * Relative positional bias (the maintainer's profile names the unfused score
+ * kernel QKRPB: scores plus a bias that depends only on where the key sits
+ * relative to the query). Reading taken: per head, one learned value per
+ * relative offset key - query, counted per axis in steps of the dilation
+ * (so in class units), over the full range a shifted window can reach,
+ * -(k-1) .. k-1. Table layout [heads][2kt-1][2kh-1][2kw-1]; offset delta
+ * on an axis sits at index delta + k - 1.
+ */
+static int64_t rpb_size(const oracle_problem *p)
+{
+    return (2 * p->kernel[0] - 1) * (2 * p->kernel[1] - 1) * (2 * p->kernel[2] - 1);
+}
+
+/* Index in one head's table of the offset from query token x to key token y. */
+static int64_t rpb_index(const oracle_problem *p, int64_t x, int64_t y)
+{
+    int64_t W = p->extent[2], H = p->extent[1];
+    int64_t xc[3] = {x / (H * W), (x / W) % H, x % W};
+    int64_t yc[3] = {y / (H * W), (y / W) % H, y % W};
+    int64_t idx = 0;
+    for (int a = 0; a < 3; ++a) {
+        int64_t delta = (yc[a] - xc[a]) / p->dilation[a]; /* same class: exact */
+        idx = idx * (2 * p->kernel[a] - 1) + delta + p->kernel[a] - 1;
+    }
+    return idx;
+}
+
+/* attn[s][j] = alpha * <a_x, b_{N(x)_j}> + rpb[head][offset(x, N(x)_j)]. */
+void oracle_na_qk_rpb(const oracle_problem *p, const double *a, const double *b, double alpha,
+                      const double *rpb, int64_t n_sel, const int64_t *sel, double *attn)
+{
+    int64_t K = window_size(p), D = p->head_dim, R = rpb_size(p);
+    if (!sel) n_sel = p->batch * tokens(p) * p->heads;
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t s = 0; s < n_sel; ++s) {
+            int64_t bb, tok, h;
+            decode_unit(p, sel ? sel[s] : s, &bb, &tok, &h);
+            neighborhood(p, tok, keys);
+            const double *ax = vec(p, a, bb, tok, h);
+            for (int64_t j = 0; j < K; ++j)
+                attn[s * K + j] = alpha * dot(ax, vec(p, b, bb, keys[j], h), D) +
+                                  rpb[h * R + rpb_index(p, tok, keys[j])];
+        }
+        free(keys);
+    }
+}
+
+/* Gradient of the bias: drpb[head][o] = sum over every batch element, query
+ * and window entry whose offset is o of dattn (the full [units, K] array). */
+void oracle_na_rpb_grad(const oracle_problem *p, const double *dattn, double *drpb)
+{
+    int64_t K = window_size(p), R = rpb_size(p), n = p->batch * tokens(p) * p->heads;
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * K);
+    for (int64_t i = 0; i < p->heads * R; ++i) drpb[i] = 0.0;
+    for (int64_t u = 0; u < n; ++u) {
+        int64_t bb, tok, h;
+        decode_unit(p, u, &bb, &tok, &h);
+        neighborhood(p, tok, keys);
+        for (int64_t j = 0; j < K; ++j) drpb[h * R + rpb_index(p, tok, keys[j])] += dattn[u * K + j];
+    }
+    free(keys);
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void)
 {

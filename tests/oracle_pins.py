@@ -387,6 +387,65 @@ def check_unfused_selection(orc, seed=15):
         assert np.array_equal(f.reshape(-1, f.shape[-1])[sel], p)
 
 
+# --------------------------------------------------------------------------- relative positional bias
+
+def check_rpb_worked_examples(orc):
+    """q = k = 0 so the scores are the bias alone, bias values 10 + index:
+    worked out by hand from the reading (offset key - query in class units,
+    stored at offset + k - 1) for a 1 x 5 row with k = 3 (windows shifted at
+    both ends) and a 1 x 6 row at dilation 2 (two classes of three)."""
+    rpb = np.array([10., 11, 12, 13, 14]).reshape(1, 1, 5)
+    z = np.zeros((1, 1, 1, 5, 1))
+    got = orc.na_qk(z, z, (1, 3), 1, 1.0, rpb=rpb)[0, 0, 0]
+    want = [[12, 13, 14], [11, 12, 13], [11, 12, 13], [11, 12, 13], [10, 11, 12]]
+    assert np.array_equal(got, np.array(want, float)), got
+    z = np.zeros((1, 1, 1, 6, 1))
+    got = orc.na_qk(z, z, (1, 3), (1, 2), 1.0, rpb=rpb)[0, 0, 0]
+    want = [[12, 13, 14], [12, 13, 14], [11, 12, 13], [11, 12, 13], [10, 11, 12], [10, 11, 12]]
+    assert np.array_equal(got, np.array(want, float)), got
+
+
+def check_rpb_adjoint(orc, seed=16):
+    """Adding the bias and its gradient are adjoint maps:
+    <qk(a, b, rpb) - qk(a, b), G> = <rpb, rpb_grad(G)> for every rpb and G, and
+    a zero table adds nothing."""
+    import oracle as _o
+    for i, (grid, kernel, dil) in enumerate(UNFUSED_CASES):
+        heads, D = 2, 3
+        K = int(np.prod(kernel))
+        a = _hm(grid, heads, D, seed + 3 * i)
+        b = _hm(grid, heads, D, seed + 3 * i + 1)
+        G = _hm(grid, heads, K, seed + 3 * i + 2)
+        rpb = _rng(seed + i).standard_normal(_o.rpb_shape(kernel, heads))
+        base = orc.na_qk(a, b, kernel, dil, 0.9)
+        assert np.array_equal(orc.na_qk(a, b, kernel, dil, 0.9, rpb=np.zeros_like(rpb)), base)
+        lhs = np.sum((orc.na_qk(a, b, kernel, dil, 0.9, rpb=rpb) - base) * G)
+        rhs = np.sum(rpb * orc.rpb_grad(G, kernel, dil))
+        assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(lhs)), (grid, kernel, dil, lhs, rhs)
+
+
+def check_rpb_fd(orc, seed=17, h=1e-6, tol=2e-7):
+    """Central finite differences of sum(out * dout) through the unfused forward
+    with a bias fix the bias gradient of the unfused backward."""
+    import oracle as _o
+    for grid, kernel, dil in [((5, 6), (3, 3), (1, 2)), ((3, 4, 5), (3, 3, 3), 1)]:
+        heads, D = 2, 3
+        q, k, v, dout = (_hm(grid, heads, D, seed + j) for j in range(4))
+        rpb = 0.5 * _rng(seed).standard_normal(_o.rpb_shape(kernel, heads))
+        P, _ = orc.unfused_fwd(q, k, v, kernel, dil, 0.7, rpb=rpb)
+        g = orc.unfused_bwd(q, k, v, P, dout, kernel, dil, 0.7, want_rpb=True)[3]
+        flat = rpb.reshape(-1)
+        for idx in _rng(seed + 1).choice(flat.size, 6, replace=False):
+            vals = []
+            for sgn in (1, -1):
+                r2 = flat.copy()
+                r2[idx] += sgn * h
+                _, o2 = orc.unfused_fwd(q, k, v, kernel, dil, 0.7, rpb=r2.reshape(rpb.shape))
+                vals.append(np.sum(o2 * dout))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert abs(fd - g.reshape(-1)[idx]) < tol * max(1.0, abs(fd)), (grid, idx, fd)
+
+
 ALL_CHECKS = [
     ("windows", lambda o: check_windows(o)),
     ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
@@ -405,6 +464,9 @@ ALL_CHECKS = [
     ("unfused_matches_fused", check_unfused_matches_fused),
     ("softmax", check_softmax),
     ("unfused_selection", check_unfused_selection),
+    ("rpb_worked_examples", check_rpb_worked_examples),
+    ("rpb_adjoint", check_rpb_adjoint),
+    ("rpb_fd", check_rpb_fd),
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 

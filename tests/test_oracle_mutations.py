@@ -40,6 +40,14 @@ MUTATIONS = {
                         "o[c] += attn[((bb * tokens(p) + tok) * p->heads + h) * K + j] * ax[c];", 0),
     "inverse_short_reach": ("lo[ax] = ctr[ax] - (p->kernel[ax] - 1) * p->dilation[ax];",
                             "lo[ax] = ctr[ax] - (p->kernel[ax] / 2) * p->dilation[ax];", 0),
+    "rpb_offset_sign": ("int64_t delta = (yc[a] - xc[a]) / p->dilation[a];",
+                        "int64_t delta = (xc[a] - yc[a]) / p->dilation[a];", 0),
+    "rpb_ignores_dilation": ("int64_t delta = (yc[a] - xc[a]) / p->dilation[a];",
+                             "int64_t delta = (yc[a] - xc[a]);", 0),
+    "rpb_off_center": ("idx = idx * (2 * p->kernel[a] - 1) + delta + p->kernel[a] - 1;",
+                       "idx = idx * (2 * p->kernel[a] - 1) + delta + p->kernel[a] / 2;", 0),
+    "rpb_grad_wrong_head": ("drpb[h * R + rpb_index(p, tok, keys[j])] += dattn[u * K + j];",
+                            "drpb[rpb_index(p, tok, keys[j])] += dattn[u * K + j];", 0),
 }
 
 
