@@ -35,6 +35,7 @@ namespace {
 
 struct UProb {
     nu::Geo g;
+    int64_t heads;
     int64_t bh;     // batch * heads
     int64_t units;  // bh * tokens
     int D;
@@ -74,6 +75,7 @@ na_status uvalidate(const na_problem *p, UProb *out, bool need_dim = true) {
     q.g.K = (int)K;
     q.g.kw = q.g.ker[2];
     q.g.khw = q.g.ker[1] * q.g.ker[2];
+    q.heads = p->heads;
     q.bh = p->batch * p->heads;
     q.units = q.bh * tokens;
     q.D = (int)p->head_dim;
@@ -113,9 +115,25 @@ __device__ __forceinline__ int64_t token_of(const Geo &g, int t, int y, int x) {
     return ((int64_t)t * g.ext[1] + y) * g.ext[2] + x;
 }
 
+// Index in one head's bias table of the key at window offsets (jt, jh, jw) of
+// the query at coordinates c: the offset key - query in class units plus k - 1
+// per axis.
+__device__ __forceinline__ int rpb_entry(const Geo &g, const int (&c)[3], int jt, int jh, int jw) {
+    const int j3[3] = {jt, jh, jw};
+    int idx = 0;
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        const int d = g.dil[ax], i = c[ax] / d;
+        const int s = na::window_start(i, na::class_size(g.ext[ax], d, c[ax] % d), g.ker[ax]);
+        idx = idx * (2 * g.ker[ax] - 1) + (s + j3[ax] - i) + g.ker[ax] - 1;
+    }
+    return idx;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void qk_plain(Geo g, const float *__restrict__ a,
                                                 const float *__restrict__ b, float alpha,
+                                                const float *__restrict__ rpb, int heads,
                                                 float *__restrict__ attn, int64_t total) {
     for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < total; e += gridDim.x * 256ll) {
         const int64_t u = e / g.K;
@@ -136,7 +154,13 @@ __global__ __launch_bounds__(256) void qk_plain(Geo g, const float *__restrict__
             const float4 x = pa[i], y = pb[i];
             s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
         }
-        attn[e] = alpha * s;
+        if (rpb) {
+            const int R = (2 * g.ker[0] - 1) * (2 * g.ker[1] - 1) * (2 * g.ker[2] - 1);
+            s = alpha * s + rpb[(int64_t)(bh % heads) * R + rpb_entry(g, c, jt, jh, jw)];
+            attn[e] = s;
+        } else {
+            attn[e] = alpha * s;
+        }
     }
 }
 
@@ -219,6 +243,92 @@ __global__ __launch_bounds__(256) void av_inverse_plain(Geo g, const float *__re
         reinterpret_cast<float4 *>(out)[e] =
             make_float4(alpha * acc.x, alpha * acc.y, alpha * acc.z, alpha * acc.w);
     }
+}
+
+// ----------------------------------------------------------------------------
+// Gradient of the relative positional bias: drpb[head][o] = sum of dscores over
+// every (batch, query, window entry) whose key sits at offset o from the
+// query. Deterministic two-stage sum, no atomics: a workgroup takes one chunk
+// of kRpbChunk queries of one (batch, head) plane, keeps its rows in LDS
+// kRpbSub at a time, and each thread sums the entries of a few offsets
+// (every query has at most one entry per offset) into a partial per chunk;
+// a second kernel adds the partials of every chunk of every batch element in
+// a fixed order.
+
+constexpr int kRpbChunk = 256;        // queries per workgroup
+constexpr int kRpbSub = 16;           // queries in LDS at a time
+constexpr int kRpbMaxK = 512;         // window entries (LDS: kRpbSub * K floats)
+constexpr int kRpbPerThread = 8;      // offsets per thread: R <= 2048
+
+__global__ __launch_bounds__(256) void rpb_partial_kernel(Geo g, const float *__restrict__ ds,
+                                                          float *__restrict__ partial, int chunks) {
+    __shared__ float rows[kRpbSub * kRpbMaxK];
+    __shared__ int rel[kRpbSub][3];   // query's place in its window per axis (class units)
+    const int plane = blockIdx.x / chunks, chunk = blockIdx.x - plane * chunks;
+    const int R1 = 2 * g.ker[1] - 1, R2 = 2 * g.ker[2] - 1;
+    const int R = (2 * g.ker[0] - 1) * R1 * R2;
+    // this thread's offsets: o = threadIdx.x + 256 m, as (dt, dh, dw) from k - 1
+    int dt[kRpbPerThread], dh[kRpbPerThread], dw[kRpbPerThread];
+    float acc[kRpbPerThread];
+#pragma unroll
+    for (int m = 0; m < kRpbPerThread; ++m) {
+        const int o = threadIdx.x + 256 * m;
+        dt[m] = o / (R1 * R2) - (g.ker[0] - 1);
+        dh[m] = (o / R2) % R1 - (g.ker[1] - 1);
+        dw[m] = o % R2 - (g.ker[2] - 1);
+        acc[m] = 0.f;
+    }
+    const int q0 = chunk * kRpbChunk;
+    const int nq = min(kRpbChunk, g.tokens - q0);
+    const float *base = ds + ((int64_t)plane * g.tokens + q0) * g.K;
+    for (int s0 = 0; s0 < nq; s0 += kRpbSub) {
+        const int ns = min(kRpbSub, nq - s0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < ns * g.K; i += 256) rows[i] = base[(int64_t)s0 * g.K + i];
+        if (threadIdx.x < ns) {
+            int tok = q0 + s0 + threadIdx.x;
+            int c[3];
+            c[2] = tok % g.ext[2];
+            tok /= g.ext[2];
+            c[1] = tok % g.ext[1];
+            c[0] = tok / g.ext[1];
+#pragma unroll
+            for (int ax = 0; ax < 3; ++ax) {
+                const int d = g.dil[ax], i = c[ax] / d;
+                rel[threadIdx.x][ax] = i - na::window_start(i, na::class_size(g.ext[ax], d, c[ax] % d),
+                                                            g.ker[ax]);
+            }
+        }
+        __syncthreads();
+        for (int q = 0; q < ns; ++q) {
+            const int rt = rel[q][0], rh = rel[q][1], rw = rel[q][2];
+#pragma unroll
+            for (int m = 0; m < kRpbPerThread; ++m) {
+                const int jt = dt[m] + rt, jh = dh[m] + rh, jw = dw[m] + rw;
+                if (threadIdx.x + 256 * m < R && (unsigned)jt < (unsigned)g.ker[0] &&
+                    (unsigned)jh < (unsigned)g.ker[1] && (unsigned)jw < (unsigned)g.ker[2])
+                    acc[m] += rows[q * g.K + (jt * g.ker[1] + jh) * g.kw + jw];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kRpbPerThread; ++m)
+        if (threadIdx.x + 256 * m < R) partial[(int64_t)blockIdx.x * R + threadIdx.x + 256 * m] = acc[m];
+}
+
+// drpb[h][o] = sum over batch elements b, then chunks, of partial[(b * heads + h) * chunks + c][o].
+__global__ __launch_bounds__(256) void rpb_reduce_kernel(const float *__restrict__ partial,
+                                                         float *__restrict__ drpb, int batch,
+                                                         int heads, int chunks, int R) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= heads * R) return;
+    const int h = idx / R, o = idx - h * R;
+    float s = 0.f;
+    for (int b = 0; b < batch; ++b) {
+        const float *p = partial + ((int64_t)(b * heads + h) * chunks) * R + o;
+        for (int c = 0; c < chunks; ++c) s += p[(int64_t)c * R];
+    }
+    drpb[idx] = s;
 }
 
 // ----------------------------------------------------------------------------
@@ -388,13 +498,39 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows(const float *p, const fl
     default: { constexpr int kD = 64; CALL; } break; \
     }
 
-na_status run_qk(const UProb &q, const float *a, const float *b, float alpha, float *attn,
-                 hipStream_t st) {
+na_status run_qk(const UProb &q, const float *a, const float *b, float alpha, const float *rpb,
+                 float *attn, hipStream_t st) {
     if (q.units == 0) return NA_OK;
-    if (nu::fast_qk(q.g, q.bh, q.D, a, b, alpha, attn, st)) return launched();
+    if (nu::fast_qk(q.g, q.bh, q.D, a, b, alpha, rpb, q.heads, attn, st)) return launched();
     const int64_t total = q.units * q.g.K;
     NA_FOR_D(q.D, hipLaunchKernelGGL(qk_plain<kD>, dim3(grid_for(total, 256)), dim3(256), 0, st,
-                                     q.g, a, b, alpha, attn, total));
+                                     q.g, a, b, alpha, rpb, q.heads, attn, total));
+    return launched();
+}
+
+int rpb_size(const UProb &q) {
+    return (2 * q.g.ker[0] - 1) * (2 * q.g.ker[1] - 1) * (2 * q.g.ker[2] - 1);
+}
+
+int64_t rpb_chunks(const UProb &q) { return (q.g.tokens + kRpbChunk - 1) / kRpbChunk; }
+
+size_t rpb_workspace(const UProb &q) {
+    return (size_t)(q.bh * rpb_chunks(q) * rpb_size(q)) * sizeof(float);
+}
+
+na_status run_rpb_grad(const UProb &q, const float *ds, float *drpb, void *ws, size_t ws_bytes,
+                       hipStream_t st) {
+    const int R = rpb_size(q);
+    if (R > 256 * kRpbPerThread || q.g.K > kRpbMaxK) return NA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < rpb_workspace(q)) return NA_ERR_WORKSPACE;
+    const int64_t blocks = q.bh * rpb_chunks(q);
+    if (blocks > INT32_MAX) return NA_ERR_UNSUPPORTED;
+    float *partial = static_cast<float *>(ws);
+    hipLaunchKernelGGL(rpb_partial_kernel, dim3((unsigned)blocks), dim3(256), 0, st, q.g, ds,
+                       partial, (int)rpb_chunks(q));
+    const int n = (int)q.heads * R;
+    hipLaunchKernelGGL(rpb_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       partial, drpb, (int)(q.bh / q.heads), (int)q.heads, (int)rpb_chunks(q), R);
     return launched();
 }
 
@@ -461,14 +597,32 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, float *attn,
-                void *hip_stream) {
+na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, const float *rpb,
+                float *attn, void *hip_stream) {
     UProb q;
     na_status s = uvalidate(p, &q);
     if (s != NA_OK) return s;
     if (!std::isfinite(alpha)) return NA_ERR_INVALID_ARG;
     if ((s = check_ptrs({a, b, attn})) != NA_OK) return s;
-    return run_qk(q, (const float *)a, (const float *)b, (float)alpha, attn, as_stream(hip_stream));
+    if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
+    return run_qk(q, (const float *)a, (const float *)b, (float)alpha, rpb, attn,
+                  as_stream(hip_stream));
+}
+
+size_t na_rpb_grad_workspace_bytes(const na_problem *p) {
+    UProb q;
+    if (uvalidate(p, &q, false) != NA_OK) return 0;
+    return rpb_workspace(q);
+}
+
+na_status na_rpb_grad(const na_problem *p, const float *dscores, float *drpb, void *workspace,
+                      size_t workspace_bytes, void *hip_stream) {
+    UProb q;
+    na_status s = uvalidate(p, &q, false);
+    if (s != NA_OK) return s;
+    if ((s = check_ptrs({dscores, drpb})) != NA_OK) return s;
+    if (q.units == 0) return NA_OK;
+    return run_rpb_grad(q, dscores, drpb, workspace, workspace_bytes, as_stream(hip_stream));
 }
 
 na_status na_av(const na_problem *p, const float *attn, const void *b, double alpha, void *out,
@@ -510,13 +664,15 @@ na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *d
 }
 
 na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
-                         float *probs, void *out, void *hip_stream) {
+                         const float *rpb, float *probs, void *out, void *hip_stream) {
     UProb u;
     na_status s = uvalidate(p, &u);
     if (s != NA_OK) return s;
     if ((s = check_ptrs({q, k, v, probs, out})) != NA_OK) return s;
+    if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
     const hipStream_t st = as_stream(hip_stream);
-    if ((s = run_qk(u, (const float *)q, (const float *)k, (float)p->scale, probs, st)) != NA_OK)
+    if ((s = run_qk(u, (const float *)q, (const float *)k, (float)p->scale, rpb, probs, st)) !=
+        NA_OK)
         return s;
     if ((s = run_softmax(u, probs, probs, st)) != NA_OK) return s;
     return run_av(u, probs, (const float *)v, 1.f, (float *)out, st);
@@ -524,19 +680,28 @@ na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, cons
 
 na_status na_unfused_bwd(const na_problem *p, const void *q, const void *k, const void *v,
                          const float *probs, const void *dout, float *dscores, void *dq, void *dk,
-                         void *dv, void *hip_stream) {
+                         void *dv, float *drpb, void *workspace, size_t workspace_bytes,
+                         void *hip_stream) {
     UProb u;
     na_status s = uvalidate(p, &u);
     if (s != NA_OK) return s;
     if ((s = check_ptrs({q, k, v, probs, dout, dscores, dq, dk, dv})) != NA_OK) return s;
+    if (drpb) {
+        if (!aligned16(drpb)) return NA_ERR_INVALID_ARG;
+        if (rpb_size(u) > 256 * kRpbPerThread || u.g.K > kRpbMaxK) return NA_ERR_UNSUPPORTED;
+        if (!workspace || workspace_bytes < rpb_workspace(u)) return NA_ERR_WORKSPACE;
+    }
     const hipStream_t st = as_stream(hip_stream);
     const float scale = (float)p->scale;
     // AGRAD: dP = dout . v over the window; VGRAD: dv = inverse sum of P dout
-    if ((s = run_qk(u, (const float *)dout, (const float *)v, 1.f, dscores, st)) != NA_OK) return s;
+    if ((s = run_qk(u, (const float *)dout, (const float *)v, 1.f, nullptr, dscores, st)) != NA_OK)
+        return s;
     if ((s = run_av_inverse(u, probs, (const float *)dout, 1.f, (float *)dv, st)) != NA_OK)
         return s;
-    // softmax backward in place: dS = P (dP - rowsum(P dP))
+    // softmax backward in place: dS = P (dP - rowsum(P dP)); the bias gradient sums dS
     if ((s = run_softmax_bwd(u, probs, dscores, dscores, st)) != NA_OK) return s;
+    if (drpb && (s = run_rpb_grad(u, dscores, drpb, workspace, workspace_bytes, st)) != NA_OK)
+        return s;
     // QGRAD and KGRAD
     if ((s = run_av(u, dscores, (const float *)k, scale, (float *)dq, st)) != NA_OK) return s;
     return run_av_inverse(u, dscores, (const float *)q, scale, (float *)dk, st);

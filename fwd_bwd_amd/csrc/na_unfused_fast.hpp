@@ -60,7 +60,16 @@ struct UArgs {
     int chunk_rows;      // av_inverse: box rows per attention chunk in LDS
     int oh, ow;          // av_inverse: walk offset of this pass, in patches
     int accumulate;      // av_inverse: add to out (passes after the first)
+    const float *rpb;    // qk: relative positional bias [heads][2kt-1][2kh-1][2kw-1], or null
+    int heads;           // qk with a bias: heads per batch element
 };
+
+// Head of a tile's (batch, head) plane: planes are the batch elements of the
+// head-major layout, base = plane * (tokens * head_dim) + class origin.
+__device__ __forceinline__ int tile_head(const UArgs &a, const TileCtx &w) {
+    const int64_t plane_elems = (int64_t)a.g.ext[0] * a.g.ext[1] * a.g.ext[2] * a.g.head_dim;
+    return (int)((w.base / plane_elems) % a.heads);
+}
 
 // One window plane's slice (KP entries per point) of the attention rows of
 // quarter rows [r0, r0 + rows_round) of a wave's 8 x 8 points, as one LDS
@@ -270,6 +279,17 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     pin4(s[i]);
                 });
         }
+        // bias: entry (offset key - query + k - 1 per axis) of this head's table
+        const float *tb = nullptr;
+        int rowb[2 * CH], colb[2 * CW];
+        if (a.rpb) {
+            const int RH = 2 * w.k[1] - 1, RW = 2 * w.k[2] - 1;
+            tb = a.rpb + ((int64_t)tile_head(a, w) * (2 * w.k[0] - 1) + tk - w.o[0] + w.k[0] - 1) * RH * RW;
+#pragma unroll
+            for (int h = 0; h < 2 * CH; ++h) rowb[h] = (us[1] + h - L.p[1] + w.k[1] - 1) * RW;
+#pragma unroll
+            for (int h = 0; h < 2 * CW; ++h) colb[h] = us[2] + h - L.p[2] + w.k[2] - 1;
+        }
         __syncthreads();  // the staged plane is read no more: its LDS takes the rows
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
             if (lr >= r0 && lr < r0 + a.rows_round) {
@@ -278,10 +298,10 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                 for (int i = 0; i < NI; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int jh = 2 * (i / CW) + (e >> 1) - lo[1];
-                        const int jw = 2 * (i % CW) + (e & 1) - lo[2];
+                        const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
+                        const int jh = h - lo[1], jw = wc - lo[2];
                         if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2])
-                            slot[jh * a.kw + jw] = s[i][e];
+                            slot[jh * a.kw + jw] = tb ? s[i][e] + tb[rowb[h] + colb[wc]] : s[i][e];
                     }
             }
             __syncthreads();
@@ -648,13 +668,15 @@ inline bool launch(Kern kern, const UPlan &pl, hipStream_t s) {
 // Register-tiled paths; each returns false (launching nothing) when the
 // problem is outside what they cover.
 inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const float *b, float alpha,
-                    float *attn, hipStream_t s) {
+                    const float *rpb, int heads, float *attn, hipStream_t s) {
     UPlan pl;
     if (!plan(geo, bh, D, 0, 0, 0, &pl)) return false;
     pl.a.a = a;
     pl.a.b = b;
     pl.a.attn_out = attn;
     pl.a.alpha = alpha;
+    pl.a.rpb = rpb;
+    pl.a.heads = heads;
 #define X(DD, C, T3) \
     if (D == DD && pl.c == C && pl.t3 == T3) return launch(qk_kernel<DD, C, C, T3>, pl, s);
     NU_CASES(X)

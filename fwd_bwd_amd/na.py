@@ -34,7 +34,7 @@ VARIANTS = {"gather": NA_BWD_GATHER, "kvparallel": NA_BWD_KVPARALLEL}
 EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na_bwd_dq",
            "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
-           "na_unfused_bwd")
+           "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad")
 
 
 class NaProblem(ctypes.Structure):
@@ -95,13 +95,18 @@ def load() -> ctypes.CDLL:
                                           ctypes.POINTER(i64)]
         lib.na_inverse_window.restype = ctypes.c_int
         dbl = ctypes.c_double
-        lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp]
+        lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp, vp]
+        lib.na_rpb_grad_workspace_bytes.argtypes = [P]
+        lib.na_rpb_grad_workspace_bytes.restype = ctypes.c_size_t
+        lib.na_rpb_grad.argtypes = [P, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.na_rpb_grad.restype = ctypes.c_int
         lib.na_av.argtypes = [P, vp, vp, dbl, vp, vp]
         lib.na_av_inverse.argtypes = [P, vp, vp, dbl, vp, vp]
         lib.na_softmax.argtypes = [P, vp, vp, vp]
         lib.na_softmax_bwd.argtypes = [P, vp, vp, vp, vp]
-        lib.na_unfused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
-        lib.na_unfused_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_unfused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_unfused_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
         for name in ("na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd",
                      "na_unfused_fwd", "na_unfused_bwd"):
             getattr(lib, name).restype = ctypes.c_int
@@ -309,20 +314,54 @@ def _attn_like(x: torch.Tensor, K: int) -> torch.Tensor:
     return torch.empty(x.shape[:-1] + (K,), dtype=torch.float32, device=x.device)
 
 
+def rpb_shape(kernel_size, heads: int, ndim: int) -> Tuple[int, ...]:
+    """Shape of a relative positional bias table: [heads, 2k - 1 per axis]."""
+    return (heads,) + tuple(2 * k - 1 for k in _tuple(kernel_size, ndim))
+
+
+def _check_rpb(rpb, kernel_size, heads, ndim, ref):
+    if rpb is None:
+        return None
+    _check_hm(rpb)
+    if tuple(rpb.shape) != rpb_shape(kernel_size, heads, ndim) or rpb.device != ref.device:
+        raise ValueError(f"rpb must be an fp32 tensor of shape {rpb_shape(kernel_size, heads, ndim)}")
+    return _ptr(rpb)
+
+
 def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
-          attn: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> (na*_qk; AGRAD with a = dout, b = v)."""
+          attn: Optional[torch.Tensor] = None, rpb: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> [+ rpb[head, offset]] (na*_qk, QKRPB;
+    AGRAD with a = dout, b = v)."""
     _check_hm(a, b)
     ndim = a.dim() - 3
     K = _window_size(kernel_size, ndim)
     p = make_problem_hm(a.shape, a.shape[-1], kernel_size, dilation)
     if b.shape != a.shape:
         raise ValueError("a and b must share their shape")
+    rp = _check_rpb(rpb, kernel_size, a.shape[1], ndim, a)
     if attn is None:
         attn = _attn_like(a, K)
-    _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), _ptr(attn),
+    _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, _ptr(attn),
                         _stream_handle(a.device)))
     return attn
+
+
+def na_rpb_grad(dscores: torch.Tensor, kernel_size, dilation=1,
+                drpb: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient of the bias table from dscores [B, heads, (T,) H, W, K]."""
+    _check_hm(dscores)
+    ndim = dscores.dim() - 3
+    p = make_problem_hm(dscores.shape, 16, kernel_size, dilation)
+    need = int(load().na_rpb_grad_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dscores.device)
+    if drpb is None:
+        drpb = torch.empty(rpb_shape(kernel_size, dscores.shape[1], ndim), dtype=torch.float32,
+                           device=dscores.device)
+    _check(load().na_rpb_grad(ctypes.byref(p), _ptr(dscores), _ptr(drpb), _ptr(workspace),
+                              workspace.numel(), _stream_handle(dscores.device)))
+    return drpb
 
 
 def na_av(attn: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
@@ -386,25 +425,29 @@ def na_softmax_bwd(probs: torch.Tensor, dprobs: torch.Tensor, kernel_size, dilat
 
 
 def na_unfused_fwd(q, k, v, kernel_size, dilation=1, scale: Optional[float] = None,
-                   probs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+                   probs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   rpb: Optional[torch.Tensor] = None):
     """Unfused forward on head-major fp32 tensors: returns (probs, out)."""
     _check_hm(q, k, v)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v must share their shape")
     K = _window_size(kernel_size, q.dim() - 3)
     p = make_problem_hm(q.shape, q.shape[-1], kernel_size, dilation, scale)
+    rp = _check_rpb(rpb, kernel_size, q.shape[1], q.dim() - 3, q)
     if probs is None:
         probs = _attn_like(q, K)
     if out is None:
         out = torch.empty_like(q)
-    _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(probs),
+    _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), rp, _ptr(probs),
                                  _ptr(out), _stream_handle(q.device)))
     return probs, out
 
 
 def na_unfused_bwd(q, k, v, probs, dout, kernel_size, dilation=1, scale: Optional[float] = None,
-                   dscores: Optional[torch.Tensor] = None, grads=None):
-    """Unfused backward of sum(out * dout): returns (dq, dk, dv)."""
+                   dscores: Optional[torch.Tensor] = None, grads=None, want_rpb: bool = False,
+                   workspace: Optional[torch.Tensor] = None):
+    """Unfused backward of sum(out * dout): returns (dq, dk, dv), and the bias
+    gradient as a fourth value when want_rpb."""
     _check_hm(q, k, v, probs, dout)
     if not (q.shape == k.shape == v.shape == dout.shape):
         raise ValueError("q, k, v, dout must share their shape")
@@ -417,7 +460,16 @@ def na_unfused_bwd(q, k, v, probs, dout, kernel_size, dilation=1, scale: Optiona
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
+    drpb, ws_ptr, ws_n = None, None, 0
+    if want_rpb:
+        need = int(load().na_rpb_grad_workspace_bytes(ctypes.byref(p)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        drpb = torch.empty(rpb_shape(kernel_size, q.shape[1], q.dim() - 3), dtype=torch.float32,
+                           device=q.device)
+        ws_ptr, ws_n = _ptr(workspace), workspace.numel()
     _check(load().na_unfused_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(probs),
                                  _ptr(dout), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 None if drpb is None else _ptr(drpb), ws_ptr, ws_n,
                                  _stream_handle(q.device)))
-    return dq, dk, dv
+    return (dq, dk, dv, drpb) if want_rpb else (dq, dk, dv)

@@ -157,11 +157,30 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
  * for the fused ops.
  */
 
-/* attn[x][j] = alpha * <a_x, b_{N(x)_j}>: the window scores (na*_qk with
- * a = q, b = k, alpha = scale) and the gradient of the weights of na*_av
- * (AGRAD: a = dout, b = v, alpha = 1). attn must not overlap a or b. */
-na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, float *attn,
-                void *hip_stream);
+/* attn[x][j] = alpha * <a_x, b_{N(x)_j}> [+ rpb[head][offset]]: the window
+ * scores (na*_qk with a = q, b = k, alpha = scale) and the gradient of the
+ * weights of na*_av (AGRAD: a = dout, b = v, alpha = 1, rpb = NULL). attn must
+ * not overlap a or b.
+ * rpb (may be NULL): relative positional bias, the QKRPB of the maintainer's
+ * unfused profile. A dense fp32 table [heads][2kt-1][2kh-1][2kw-1] (2D:
+ * [heads][2kh-1][2kw-1]); the entry added to the score of query x and key y
+ * sits at (y - x) / dilation + (k - 1) along each axis, i.e. it depends only
+ * on the offset of the key from the query in class units, over the full
+ * range -(k-1) .. k-1 a border-shifted window can reach. */
+na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, const float *rpb,
+                float *attn, void *hip_stream);
+
+/* Bytes of device workspace na_rpb_grad needs (0 on an invalid problem). */
+size_t na_rpb_grad_workspace_bytes(const na_problem *p);
+
+/* Gradient of the bias table: drpb[head][o] = the sum of dscores over every
+ * batch element, query and window entry whose key sits at offset o from the
+ * query (layout of rpb in na_qk). Deterministic (fixed summation order, no
+ * atomics); uses a caller-owned workspace of na_rpb_grad_workspace_bytes.
+ * Windows of more than 512 entries or tables of more than 2048 offsets
+ * return NA_ERR_UNSUPPORTED. */
+na_status na_rpb_grad(const na_problem *p, const float *dscores, float *drpb, void *workspace,
+                      size_t workspace_bytes, void *hip_stream);
 
 /* out_x = alpha * sum_j attn[x][j] * b_{N(x)_j}: na*_av (b = v, alpha = 1) and
  * the query gradient of na*_qk (QGRAD: attn = dscores, b = k, alpha = scale). */
@@ -184,19 +203,24 @@ na_status na_softmax(const na_problem *p, const float *attn, float *probs, void 
 na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *dprobs,
                          float *dscores, void *hip_stream);
 
-/* The unfused forward: probs = softmax(scale * na_qk(q, k)), out = na_av(probs, v).
- * probs ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward. */
+/* The unfused forward: probs = softmax(scale * na_qk(q, k) [+ rpb]),
+ * out = na_av(probs, v). rpb may be NULL (no bias). probs
+ * ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward. */
 na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
-                         float *probs, void *out, void *hip_stream);
+                         const float *rpb, float *probs, void *out, void *hip_stream);
 
 /* The unfused backward of sum(out * dout), from the forward's probs:
  * dprobs = na_qk(dout, v) (AGRAD), dv = na_av_inverse(probs, dout) (VGRAD),
  * dscores = softmax backward, dq = scale * na_av(dscores, k) (QGRAD),
- * dk = scale * na_av_inverse(dscores, q) (KGRAD). dscores is a caller-owned
- * fp32 [B, heads, (T,) H, W, K] scratch array, left holding dscores. */
+ * dk = scale * na_av_inverse(dscores, q) (KGRAD), and, when drpb is not
+ * NULL, the bias gradient drpb = na_rpb_grad(dscores) (workspace of
+ * na_rpb_grad_workspace_bytes; ignored when drpb is NULL). dscores is a
+ * caller-owned fp32 [B, heads, (T,) H, W, K] scratch array, left holding
+ * dscores. */
 na_status na_unfused_bwd(const na_problem *p, const void *q, const void *k, const void *v,
                          const float *probs, const void *dout, float *dscores, void *dq,
-                         void *dk, void *dv, void *hip_stream);
+                         void *dk, void *dv, float *drpb, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
 
 #ifdef __cplusplus
 }

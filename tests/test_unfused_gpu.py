@@ -184,8 +184,8 @@ def test_unfused_rejects_bf16_and_bad_shapes():
     p = na.make_problem_hm(q.shape, 16, (3, 3))
     p.dtype = na.NA_BF16
     attn = torch.zeros((1, 2, 8, 8, 9), device=dev)
-    status = na.load().na_qk(na.ctypes.byref(p), q.data_ptr(), q.data_ptr(), 1.0, attn.data_ptr(),
-                             None)
+    status = na.load().na_qk(na.ctypes.byref(p), q.data_ptr(), q.data_ptr(), 1.0, None,
+                             attn.data_ptr(), None)
     assert status == na.NA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         na.na_av(torch.zeros((1, 2, 8, 8, 8), device=dev), q, (3, 3))
@@ -235,3 +235,51 @@ def test_unfused_full_workload_sampled(name):
            "dk": pick(dk, D), "dv": pick(dv, D)},
           {"probs": P_ref, "out": o_ref, "dq": g_ref[0], "dk": g_ref[1], "dv": g_ref[2]},
           f"unfused {name} sampled({sel_hm.size})")
+
+
+# ----------------------------------------------------------------------------- relative positional bias
+
+RPB_CASES = [((1, 2, 19, 23, 32), (5, 7), 1), ((2, 3, 13, 17, 16), (3, 3), (2, 3)),
+             ((1, 2, 40, 37, 32), (9, 9), 1), ((1, 1, 20, 20, 64), (9, 9), 1),
+             ((1, 2, 5, 11, 13, 32), (3, 5, 5), 1), ((1, 2, 6, 9, 10, 16), (3, 3, 3), (2, 1, 2))]
+
+
+@pytest.mark.parametrize("case", RPB_CASES, ids=[_id(c) for c in RPB_CASES])
+def test_unfused_with_rpb_matches_oracle(case):
+    """Scores plus a relative positional bias (register-tiled and plain score
+    kernels), the whole unfused forward and backward with it, and the bias
+    gradient, against the oracle."""
+    shape, kernel, dil = case
+    say("rpb", _id(case))
+    q, k, v, dout = make_random(shape, torch.float32, seed=_seed(case) + 5)
+    ndim = len(shape) - 3
+    g = torch.Generator(device="cpu").manual_seed(_seed(case) + 6)
+    rpb = torch.randn(na.rpb_shape(kernel, shape[1], ndim), generator=g)
+    scale = shape[-1] ** -0.5
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd, rd = (t.to(dev) for t in (q, k, v, dout, rpb))
+    s = na.na_qk(qd, kd, kernel, dil, alpha=0.8, rpb=rd)
+    probs, out = na.na_unfused_fwd(qd, kd, vd, kernel, dil, scale, rpb=rd)
+    dq, dk, dv, drpb = na.na_unfused_bwd(qd, kd, vd, probs, dd, kernel, dil, scale, want_rpb=True)
+    torch.cuda.synchronize()
+    Q, K_, V, DO, RP = (np64(t) for t in (q, k, v, dout, rpb))
+    P, o = oracle.unfused_fwd(Q, K_, V, kernel, dil, scale, rpb=RP)
+    gq, gk, gv, gr = oracle.unfused_bwd(Q, K_, V, P, DO, kernel, dil, scale, want_rpb=True)
+    check({"qk_rpb": s, "probs": probs, "out": out, "dq": dq, "dk": dk, "dv": dv, "drpb": drpb},
+          {"qk_rpb": oracle.na_qk(Q, K_, kernel, dil, 0.8, rpb=RP), "probs": P, "out": o,
+           "dq": gq, "dk": gk, "dv": gv, "drpb": gr}, "rpb " + _id(case))
+
+
+def test_rpb_grad_of_arbitrary_scores_and_determinism():
+    """na_rpb_grad alone on seeded normals (not a softmax gradient), twice:
+    equal to the oracle and bitwise equal between runs."""
+    dev = torch.device("cuda:0")
+    for shape, kernel, dil in [((2, 3, 33, 35, 16), (7, 5), (1, 2)), ((1, 2, 6, 20, 18, 32), (3, 5, 5), 1)]:
+        K = int(np.prod(kernel))
+        x, _, _, _ = make_random(shape[:-1] + (K,), torch.float32, seed=31)
+        xd = x.to(dev)
+        a = na.na_rpb_grad(xd, kernel, dil)
+        b = na.na_rpb_grad(xd, kernel, dil)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        check({"drpb": a}, {"drpb": oracle.rpb_grad(np64(x), kernel, dil)}, f"rpb_grad {shape}")
