@@ -245,31 +245,38 @@ __global__ __launch_bounds__(256) void av_inverse_plain(Geo g, const float *__re
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // ----------------------------------------------------------------------------
 // Gradient of the relative positional bias: drpb[head][o] = sum of dscores over
 // every (batch, query, window entry) whose key sits at offset o from the
 // query. Deterministic two-stage sum, no atomics: a workgroup takes one chunk
-// of kRpbChunk queries of one (batch, head) plane, keeps its rows in LDS
-// kRpbSub at a time, and each thread sums the entries of a few offsets
+// of kRpbChunk queries of one (batch, head) plane, keeps as many of their rows
+// in LDS as fit at a time, and each thread sums the entries of a few offsets
 // (every query has at most one entry per offset) into a partial per chunk;
 // a second kernel adds the partials of every chunk of every batch element in
 // a fixed order.
 
 constexpr int kRpbChunk = 256;        // queries per workgroup
-constexpr int kRpbSub = 16;           // queries in LDS at a time
-constexpr int kRpbMaxK = 512;         // window entries (LDS: kRpbSub * K floats)
+constexpr int kRpbLds = 8192;         // floats of LDS for rows (32 KB)
+constexpr int kRpbMaxK = 512;         // window entries (two per thread at most)
 constexpr int kRpbPerThread = 8;      // offsets per thread: R <= 2048
 
 __global__ __launch_bounds__(256) void rpb_partial_kernel(Geo g, const float *__restrict__ ds,
                                                           float *__restrict__ partial, int chunks) {
-    __shared__ float rows[kRpbSub * kRpbMaxK];
-    __shared__ int rel[kRpbSub][3];   // query's place in its window per axis (class units)
+    __shared__ __align__(16) float rows[kRpbLds];
+    __shared__ int rel[kRpbChunk][3];   // query's place in its window per axis (class units)
+    __shared__ float colsum[kRpbMaxK];
+    __shared__ unsigned long long refmask[kRpbChunk / 64];
     const int plane = blockIdx.x / chunks, chunk = blockIdx.x - plane * chunks;
     const int R1 = 2 * g.ker[1] - 1, R2 = 2 * g.ker[2] - 1;
     const int R = (2 * g.ker[0] - 1) * R1 * R2;
+    const int nm = (R + 255) / 256, nj = (g.K + 255) / 256;
+    const int G = g.K <= 128 ? 256 / g.K : 1;   // column groups summing in parallel
+    const int lane = threadIdx.x & 63;
     // this thread's offsets: o = threadIdx.x + 256 m, as (dt, dh, dw) from k - 1
     int dt[kRpbPerThread], dh[kRpbPerThread], dw[kRpbPerThread];
-    float acc[kRpbPerThread];
+    float acc[kRpbPerThread], cs[2] = {0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < kRpbPerThread; ++m) {
         const int o = threadIdx.x + 256 * m;
@@ -280,55 +287,162 @@ __global__ __launch_bounds__(256) void rpb_partial_kernel(Geo g, const float *__
     }
     const int q0 = chunk * kRpbChunk;
     const int nq = min(kRpbChunk, g.tokens - q0);
-    const float *base = ds + ((int64_t)plane * g.tokens + q0) * g.K;
-    for (int s0 = 0; s0 < nq; s0 += kRpbSub) {
-        const int ns = min(kRpbSub, nq - s0);
-        __syncthreads();
-        for (int i = threadIdx.x; i < ns * g.K; i += 256) rows[i] = base[(int64_t)s0 * g.K + i];
-        if (threadIdx.x < ns) {
-            int tok = q0 + s0 + threadIdx.x;
-            int c[3];
-            c[2] = tok % g.ext[2];
-            tok /= g.ext[2];
-            c[1] = tok % g.ext[1];
-            c[0] = tok / g.ext[1];
+    if (threadIdx.x < nq) {
+        int tok = q0 + threadIdx.x;
+        int c[3];
+        c[2] = tok % g.ext[2];
+        tok /= g.ext[2];
+        c[1] = tok % g.ext[1];
+        c[0] = tok / g.ext[1];
 #pragma unroll
-            for (int ax = 0; ax < 3; ++ax) {
-                const int d = g.dil[ax], i = c[ax] / d;
-                rel[threadIdx.x][ax] = i - na::window_start(i, na::class_size(g.ext[ax], d, c[ax] % d),
-                                                            g.ker[ax]);
-            }
-        }
-        __syncthreads();
-        for (int q = 0; q < ns; ++q) {
-            const int rt = rel[q][0], rh = rel[q][1], rw = rel[q][2];
-#pragma unroll
-            for (int m = 0; m < kRpbPerThread; ++m) {
-                const int jt = dt[m] + rt, jh = dh[m] + rh, jw = dw[m] + rw;
-                if (threadIdx.x + 256 * m < R && (unsigned)jt < (unsigned)g.ker[0] &&
-                    (unsigned)jh < (unsigned)g.ker[1] && (unsigned)jw < (unsigned)g.ker[2])
-                    acc[m] += rows[q * g.K + (jt * g.ker[1] + jh) * g.kw + jw];
-            }
+        for (int ax = 0; ax < 3; ++ax) {
+            const int d = g.dil[ax], i = c[ax] / d;
+            rel[threadIdx.x][ax] =
+                i - na::window_start(i, na::class_size(g.ext[ax], d, c[ax] % d), g.ker[ax]);
         }
     }
+    __syncthreads();
+    // Most queries of a chunk sit at the same place in their windows (the
+    // chunk's middle query's): for those the offset of entry j is fixed, so
+    // their part is a column sum; the others are summed offset by offset.
+    // refmask bit q: query q is such a query.
+    const int ref0 = rel[nq / 2][0], ref1 = rel[nq / 2][1], ref2 = rel[nq / 2][2];
+    {
+        const int t = threadIdx.x;
+        const bool isref = t < nq && rel[t][0] == ref0 && rel[t][1] == ref1 && rel[t][2] == ref2;
+        const unsigned long long bal = __ballot(isref);
+        if (lane == 0) refmask[t >> 6] = bal;
+    }
+    const int sub = (kRpbLds / g.K) & ~3;   // rows per LDS fill (a multiple of 4)
+    const float *base = ds + ((int64_t)plane * g.tokens + q0) * g.K;
+    const bool vec = ((((int64_t)plane * g.tokens + q0) * g.K) & 3) == 0;
+    for (int s0 = 0; s0 < nq; s0 += sub) {
+        const int ns = min(sub, nq - s0);
+        __syncthreads();
+        // direct loads, all in flight; lanes of a wave take consecutive pieces
+        // (16 bytes when the rows start 16-byte aligned: s0 K is a multiple of 4)
+        const int n = ns * g.K, n4 = vec ? n >> 2 : 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+        for (int i = threadIdx.x; i < n4; i += 256)
+            __builtin_amdgcn_global_load_lds(base + (int64_t)s0 * g.K + 4 * i,
+                                             (lds_void *)(rows + 4 * (i - lane)), 16, 0, 0);
+        for (int i = 4 * n4 + (int)threadIdx.x; i < n; i += 256)
+            __builtin_amdgcn_global_load_lds(base + (int64_t)s0 * g.K + i,
+                                             (lds_void *)(rows + (i - lane)), 4, 0, 0);
+#else
+        (void)base; (void)lane; (void)n4;
+#endif
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int q = 0; q < ns;) {
+            const int gq = s0 + q;
+            const int run = min(64 - (gq & 63), ns - q);   // queries left in this mask word
+            const unsigned long long live = run == 64 ? ~0ull : ((1ull << run) - 1);
+            const unsigned long long word = (refmask[gq >> 6] >> (gq & 63)) & live;
+            // column sums over the reference queries: thread (group gi, column
+            // j) takes the queries u = gi, gi + G, ... of the run
+            if (G > 1) {
+                const int gi = threadIdx.x / g.K, j = threadIdx.x - gi * g.K;
+                if (gi < G) {
+                    const float *col = rows + q * g.K + j;
+                    float sum = 0.f;
+#pragma unroll 4
+                    for (int u = gi; u < run; u += G) sum += ((word >> u) & 1ull) ? col[u * g.K] : 0.f;
+                    cs[0] += sum;
+                }
+            } else {
+                for (int m = 0; m < nj; ++m) {
+                    const int j = threadIdx.x + 256 * m;
+                    if (j >= g.K) continue;
+                    const float *col = rows + q * g.K + j;
+                    float sum = 0.f;
+#pragma unroll 8
+                    for (int u = 0; u < run; ++u) sum += ((word >> u) & 1ull) ? col[u * g.K] : 0.f;
+                    cs[m] += sum;
+                }
+            }
+            // the other queries, offset by offset
+            for (unsigned long long other = ~word & live; other; other &= other - 1) {
+                const int u = __ffsll((long long)other) - 1;
+                const int rt = rel[gq + u][0], rh = rel[gq + u][1], rw = rel[gq + u][2];
+                const float *row = rows + (q + u) * g.K;
+                for (int m = 0; m < nm; ++m) {
+                    const int jt = dt[m] + rt, jh = dh[m] + rh, jw = dw[m] + rw;
+                    if (threadIdx.x + 256 * m < R && (unsigned)jt < (unsigned)g.ker[0] &&
+                        (unsigned)jh < (unsigned)g.ker[1] && (unsigned)jw < (unsigned)g.ker[2])
+                        acc[m] += row[(jt * g.ker[1] + jh) * g.kw + jw];
+                }
+            }
+            q += run;
+        }
+    }
+    if (G > 1) {
+        // groups in order: colsum[j] = group 0 + group 1 + ...
+        __syncthreads();
+        const int gi = threadIdx.x / g.K, j = threadIdx.x - gi * g.K;
+        if (gi < G) rows[gi * g.K + j] = cs[0];
+        __syncthreads();
+        if (threadIdx.x < g.K) {
+            float sum = 0.f;
+            for (int k2 = 0; k2 < G; ++k2) sum += rows[k2 * g.K + threadIdx.x];
+            colsum[threadIdx.x] = sum;
+        }
+    } else {
+        for (int m = 0; m < nj; ++m)
+            if (threadIdx.x + 256 * m < g.K) colsum[threadIdx.x + 256 * m] = cs[m];
+    }
+    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kRpbPerThread; ++m)
-        if (threadIdx.x + 256 * m < R) partial[(int64_t)blockIdx.x * R + threadIdx.x + 256 * m] = acc[m];
+    for (int m = 0; m < kRpbPerThread; ++m) {
+        if (threadIdx.x + 256 * m >= R) continue;
+        const int jt = dt[m] + ref0, jh = dh[m] + ref1, jw = dw[m] + ref2;
+        float v = acc[m];
+        if ((unsigned)jt < (unsigned)g.ker[0] && (unsigned)jh < (unsigned)g.ker[1] &&
+            (unsigned)jw < (unsigned)g.ker[2])
+            v += colsum[(jt * g.ker[1] + jh) * g.kw + jw];
+        partial[(int64_t)blockIdx.x * R + threadIdx.x + 256 * m] = v;
+    }
 }
 
-// drpb[h][o] = sum over batch elements b, then chunks, of partial[(b * heads + h) * chunks + c][o].
+// drpb[h][o] = sum over batch elements b and chunks c of
+// partial[(b * heads + h) * chunks + c][o]. A workgroup takes 16 offsets of
+// one head; its 16 slices of 16 threads each sum every 16th (b, c) partial
+// (eight loads in flight per thread), then the 16 slice sums are added in
+// slice order: a fixed summation order, so the result is deterministic.
 __global__ __launch_bounds__(256) void rpb_reduce_kernel(const float *__restrict__ partial,
                                                          float *__restrict__ drpb, int batch,
                                                          int heads, int chunks, int R) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= heads * R) return;
-    const int h = idx / R, o = idx - h * R;
-    float s = 0.f;
-    for (int b = 0; b < batch; ++b) {
-        const float *p = partial + ((int64_t)(b * heads + h) * chunks) * R + o;
-        for (int c = 0; c < chunks; ++c) s += p[(int64_t)c * R];
+    __shared__ float slice_sum[16][17];
+    const int oblocks = (R + 15) / 16;
+    const int h = blockIdx.x / oblocks, ob = blockIdx.x - h * oblocks;
+    const int oo = threadIdx.x & 15, sl = threadIdx.x >> 4;
+    const int o = ob * 16 + oo;
+    const int n = batch * chunks;   // partials per (head, offset)
+    float sum = 0.f;
+    if (o < R) {
+        for (int i0 = sl; i0 < n; i0 += 16 * 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 16 * u;
+                if (i < n) {
+                    const int b = i / chunks, c = i - b * chunks;
+                    v[u] = partial[((int64_t)(b * heads + h) * chunks + c) * R + o];
+                } else {
+                    v[u] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
     }
-    drpb[idx] = s;
+    slice_sum[sl][oo] = sum;
+    __syncthreads();
+    if (sl == 0 && o < R) {
+        float t = 0.f;
+        for (int k2 = 0; k2 < 16; ++k2) t += slice_sum[k2][oo];
+        drpb[(int64_t)h * R + o] = t;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -351,7 +465,6 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v + __shfl_xor(v, 2, 4);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy the first n & ~3 floats (global offset 16-byte aligned) global -> LDS
 // with direct 16-byte loads, all in flight at once; completion: waitcnt + barrier.
@@ -528,9 +641,8 @@ na_status run_rpb_grad(const UProb &q, const float *ds, float *drpb, void *ws, s
     float *partial = static_cast<float *>(ws);
     hipLaunchKernelGGL(rpb_partial_kernel, dim3((unsigned)blocks), dim3(256), 0, st, q.g, ds,
                        partial, (int)rpb_chunks(q));
-    const int n = (int)q.heads * R;
-    hipLaunchKernelGGL(rpb_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       partial, drpb, (int)(q.bh / q.heads), (int)q.heads, (int)rpb_chunks(q), R);
+    hipLaunchKernelGGL(rpb_reduce_kernel, dim3((unsigned)(q.heads * ((R + 15) / 16))), dim3(256), 0,
+                       st, partial, drpb, (int)(q.bh / q.heads), (int)q.heads, (int)rpb_chunks(q), R);
     return launched();
 }
 

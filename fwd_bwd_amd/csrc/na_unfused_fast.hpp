@@ -62,6 +62,7 @@ struct UArgs {
     int accumulate;      // av_inverse: add to out (passes after the first)
     const float *rpb;    // qk: relative positional bias [heads][2kt-1][2kh-1][2kw-1], or null
     int heads;           // qk with a bias: heads per batch element
+    int rpb_off;         // qk with a bias: LDS byte offset of the bias table plane
 };
 
 // Head of a tile's (batch, head) plane: planes are the batch elements of the
@@ -222,7 +223,7 @@ __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, in
 
 // ============================================================================
 // qk: attn[x][j] = alpha <a_x, b_{N(x)_j}>
-template <int D, int CH, int CW, bool T3>
+template <int D, int CH, int CW, bool T3, bool RPB>
 __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     constexpr int PS = D * 4, NC = D / 4, NI = CH * CW;
     TileCtx w;
@@ -279,16 +280,17 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     pin4(s[i]);
                 });
         }
-        // bias: entry (offset key - query + k - 1 per axis) of this head's table
-        const float *tb = nullptr;
-        int rowb[2 * CH], colb[2 * CW];
-        if (a.rpb) {
+        // bias: this head's table plane for the key plane tk in LDS (past the
+        // staging area); the lane's entry for walk row h, column wc sits at
+        // tbl + h * RW + wc (offset key - query + k - 1 per axis)
+        const float *tbl = nullptr;
+        if constexpr (RPB) {
             const int RH = 2 * w.k[1] - 1, RW = 2 * w.k[2] - 1;
-            tb = a.rpb + ((int64_t)tile_head(a, w) * (2 * w.k[0] - 1) + tk - w.o[0] + w.k[0] - 1) * RH * RW;
-#pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) rowb[h] = (us[1] + h - L.p[1] + w.k[1] - 1) * RW;
-#pragma unroll
-            for (int h = 0; h < 2 * CW; ++h) colb[h] = us[2] + h - L.p[2] + w.k[2] - 1;
+            const float *src = a.rpb + ((int64_t)tile_head(a, w) * (2 * w.k[0] - 1) + tk - w.o[0] +
+                                        w.k[0] - 1) * RH * RW;
+            float *dstl = reinterpret_cast<float *>(smem + a.rpb_off);
+            for (int i = threadIdx.x; i < RH * RW; i += kThreads) dstl[i] = src[i];
+            tbl = dstl + (us[1] - L.p[1] + w.k[1] - 1) * RW + (us[2] - L.p[2] + w.k[2] - 1);
         }
         __syncthreads();  // the staged plane is read no more: its LDS takes the rows
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
@@ -300,8 +302,12 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     for (int e = 0; e < 4; ++e) {
                         const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
                         const int jh = h - lo[1], jw = wc - lo[2];
-                        if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2])
-                            slot[jh * a.kw + jw] = tb ? s[i][e] + tb[rowb[h] + colb[wc]] : s[i][e];
+                        if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2]) {
+                            if constexpr (RPB)
+                                slot[jh * a.kw + jw] = s[i][e] + tbl[h * (2 * w.k[2] - 1) + wc];
+                            else
+                                slot[jh * a.kw + jw] = s[i][e];
+                        }
                     }
             }
             __syncthreads();
@@ -519,10 +525,10 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
     }
 }
 
-template <int D, int CH, int CW, bool T3>
+template <int D, int CH, int CW, bool T3, bool RPB>
 __global__ void __launch_bounds__(kThreads, 2) qk_kernel(UArgs a) {
     extern __shared__ __align__(16) char smem[];
-    qk_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    qk_tile<D, CH, CW, T3, RPB>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 template <int D, int CH, int CW, bool T3>
@@ -677,8 +683,16 @@ inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const flo
     pl.a.alpha = alpha;
     pl.a.rpb = rpb;
     pl.a.heads = heads;
-#define X(DD, C, T3) \
-    if (D == DD && pl.c == C && pl.t3 == T3) return launch(qk_kernel<DD, C, C, T3>, pl, s);
+    if (rpb) {
+        // the bias table plane after the staging area
+        pl.a.rpb_off = (pl.lds + 15) & ~15;
+        pl.lds = pl.a.rpb_off + (2 * geo.ker[1] - 1) * (2 * geo.ker[2] - 1) * 4;
+        if (pl.lds > kLdsCap) return false;
+    }
+#define X(DD, C, T3)                                                                          \
+    if (D == DD && pl.c == C && pl.t3 == T3)                                                  \
+        return rpb ? launch(qk_kernel<DD, C, C, T3, true>, pl, s)                             \
+                   : launch(qk_kernel<DD, C, C, T3, false>, pl, s);
     NU_CASES(X)
 #undef X
     return false;
