@@ -328,10 +328,42 @@ def rpb_grad(dattn, kernel, dilation=1, lib=None):
 
 def softmax(x):
     """Softmax over the last (window) axis, as the script's F.softmax(attn, dim=-1):
-    exp(x - max) / sum exp(x - max), in float64."""
+    exp(x - max) / sum exp(x - max), in float64. A row whose entries are all
+    -inf (every key masked out) gets zero weights."""
     x = _f64(x)
-    e = np.exp(x - np.max(x, axis=-1, keepdims=True))
-    return e / np.sum(e, axis=-1, keepdims=True)
+    m = np.max(x, axis=-1, keepdims=True)
+    dead = np.isneginf(m)
+    e = np.exp(x - np.where(dead, 0.0, m))
+    s = np.sum(e, axis=-1, keepdims=True)
+    return np.where(dead, 0.0, e / np.where(dead, 1.0, s))
+
+
+def mask_scores(attn, mask):
+    """Masked windows (the issue's requester masks the result of na3d_qk to get
+    per-frame window sizes): score entries whose mask is 0 become -inf, so the
+    window softmax gives them zero weight. mask: [(T,) H, W, K] per token,
+    shared by every batch element and head (broadcast)."""
+    attn = _f64(attn)
+    return np.where(np.asarray(mask) != 0, attn, -np.inf)
+
+
+def frame_window_mask(grid, kernel, frame_kernel):
+    """Mask [T, H, W, K] keeping, for every query of frame t, only the keys
+    whose frame lies in the window of size frame_kernel[t] around t (the same
+    centered-and-shifted rule along T), inside the kernel[0]-frame window the
+    scores are computed over: the requester's time kernel that varies per
+    frame. Undilated grids."""
+    T, H, W = grid
+    kt, kh, kw = kernel
+    mask = np.zeros((T, H, W, kt * kh * kw), np.uint8)
+    for t in range(T):
+        s_max = window_start(T, kt, 1, t)
+        s_own = window_start(T, int(frame_kernel[t]), 1, t)
+        for it in range(kt):
+            f = s_max + it
+            if s_own <= f < s_own + int(frame_kernel[t]):
+                mask[t, :, :, it * kh * kw:(it + 1) * kh * kw] = 1
+    return mask
 
 
 def softmax_bwd(p, dp):
@@ -340,11 +372,14 @@ def softmax_bwd(p, dp):
     return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
 
 
-def unfused_fwd(q, k, v, kernel, dilation=1, scale=None, rpb=None, lib=None):
+def unfused_fwd(q, k, v, kernel, dilation=1, scale=None, rpb=None, mask=None, lib=None):
     """The unfused forward on head-major tensors: P = softmax(scale * na_qk(q, k)
-    [+ rpb]), out = na_av(P, v). Returns (P, out)."""
+    [+ rpb], masked), out = na_av(P, v). Returns (P, out)."""
     scale = q.shape[-1] ** -0.5 if scale is None else scale
-    P = softmax(na_qk(q, k, kernel, dilation, scale, rpb=rpb, lib=lib))
+    s = na_qk(q, k, kernel, dilation, scale, rpb=rpb, lib=lib)
+    if mask is not None:
+        s = mask_scores(s, mask)
+    P = softmax(s)
     return P, na_av(P, v, kernel, dilation, 1.0, lib=lib)
 
 

@@ -446,6 +446,40 @@ def check_rpb_fd(orc, seed=17, h=1e-6, tol=2e-7):
             assert abs(fd - g.reshape(-1)[idx]) < tol * max(1.0, abs(fd)), (grid, idx, fd)
 
 
+# --------------------------------------------------------------------------- masked windows
+
+def check_masked_windows(orc, seed=18):
+    """Masking the scores of a larger window down to a smaller one gives
+    neighborhood attention with the smaller window (windows of the same
+    centered-and-shifted rule are nested): the masked unfused forward with a
+    constant per-frame time kernel equals the fused oracle at that kernel,
+    and the backward through it (masked weights are zero) equals its
+    gradients. A mask of ones changes nothing; a fully masked query gets a
+    zero output."""
+    import oracle as _o
+    grid, kernel, heads, D = (6, 5, 4), (5, 3, 3), 2, 3
+    q, k, v, dout = (_hm(grid, heads, D, seed + j) for j in range(4))
+    for kt in (1, 3):
+        mask = _o.frame_window_mask(grid, kernel, [kt] * grid[0])
+        P, out = orc.unfused_fwd(q, k, v, kernel, 1, 0.8, mask=mask)
+        dq, dk, dv = orc.unfused_bwd(q, k, v, P, dout, kernel, 1, 0.8)
+        small = (kt,) + kernel[1:]
+        tm = lambda x: np.moveaxis(x, 1, -2)  # noqa: E731
+        o_ref, _ = orc.na_fwd(tm(q), tm(k), tm(v), small, 1, 0.8)
+        g_ref = orc.na_bwd(tm(q), tm(k), tm(v), tm(dout), small, 1, 0.8)
+        assert np.max(np.abs(tm(out) - o_ref)) < 1e-12, kt
+        for got, ref in zip((dq, dk, dv), g_ref):
+            assert np.max(np.abs(tm(got) - ref)) < 1e-12, kt
+    ones = np.ones(grid + (int(np.prod(kernel)),), np.uint8)
+    P1, o1 = orc.unfused_fwd(q, k, v, kernel, 1, 0.8, mask=ones)
+    P0, o0 = orc.unfused_fwd(q, k, v, kernel, 1, 0.8)
+    assert np.array_equal(P1, P0) and np.array_equal(o1, o0)
+    dead = ones.copy()
+    dead[2, 1, 3, :] = 0
+    Pd, od = orc.unfused_fwd(q, k, v, kernel, 1, 0.8, mask=dead)
+    assert np.all(Pd[:, :, 2, 1, 3] == 0) and np.all(od[:, :, 2, 1, 3] == 0)
+
+
 ALL_CHECKS = [
     ("windows", lambda o: check_windows(o)),
     ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
@@ -467,6 +501,7 @@ ALL_CHECKS = [
     ("rpb_worked_examples", check_rpb_worked_examples),
     ("rpb_adjoint", check_rpb_adjoint),
     ("rpb_fd", check_rpb_fd),
+    ("masked_windows", check_masked_windows),
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 
