@@ -134,6 +134,7 @@ template <int D>
 __global__ __launch_bounds__(256) void qk_plain(Geo g, const float *__restrict__ a,
                                                 const float *__restrict__ b, float alpha,
                                                 const float *__restrict__ rpb, int heads,
+                                                const uint8_t *__restrict__ mask,
                                                 float *__restrict__ attn, int64_t total) {
     for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < total; e += gridDim.x * 256ll) {
         const int64_t u = e / g.K;
@@ -157,10 +158,12 @@ __global__ __launch_bounds__(256) void qk_plain(Geo g, const float *__restrict__
         if (rpb) {
             const int R = (2 * g.ker[0] - 1) * (2 * g.ker[1] - 1) * (2 * g.ker[2] - 1);
             s = alpha * s + rpb[(int64_t)(bh % heads) * R + rpb_entry(g, c, jt, jh, jw)];
-            attn[e] = s;
         } else {
-            attn[e] = alpha * s;
+            s = alpha * s;
         }
+        // a masked-out entry: -inf, no weight after the softmax
+        if (mask && !mask[(u - bh * g.tokens) * g.K + j]) s = -INFINITY;
+        attn[e] = s;
     }
 }
 
@@ -521,13 +524,15 @@ __global__ __launch_bounds__(256) void softmax_blocks(const float *x, float *y, 
     float m = -INFINITY;
     for (int i = l; ok && i < K; i += 4) m = fmaxf(m, xr[i]);
     m = quad_max(m);
+    if (m == -INFINITY) m = 0.f;   // every entry masked out: zero weights
     float sum = 0.f;
     for (int i = l; ok && i < K; i += 4) {
         const float e = __expf(xr[i] - m);
         xr[i] = e;
         sum += e;
     }
-    const float inv = 1.f / quad_sum(sum);
+    sum = quad_sum(sum);
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
     for (int i = l; ok && i < K; i += 4) xr[i] *= inv;
     __syncthreads();
     block_out(xs, yg, n);
@@ -583,9 +588,11 @@ __global__ __launch_bounds__(256) void softmax_rows(const float *x, float *y, in
     float m = -INFINITY;
     for (int idx = l; ok && idx < K; idx += 16) m = fmaxf(m, xr[idx]);
     m = row_max16(m);
+    if (m == -INFINITY) m = 0.f;   // every entry masked out: zero weights
     float s = 0.f;
     for (int idx = l; ok && idx < K; idx += 16) s += __expf(xr[idx] - m);
-    const float inv = 1.f / row_sum16(s);
+    s = row_sum16(s);
+    const float inv = s > 0.f ? 1.f / s : 0.f;
     for (int idx = l; ok && idx < K; idx += 16) yr[idx] = __expf(xr[idx] - m) * inv;
 }
 
@@ -612,12 +619,12 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows(const float *p, const fl
     }
 
 na_status run_qk(const UProb &q, const float *a, const float *b, float alpha, const float *rpb,
-                 float *attn, hipStream_t st) {
+                 const uint8_t *mask, float *attn, hipStream_t st) {
     if (q.units == 0) return NA_OK;
-    if (nu::fast_qk(q.g, q.bh, q.D, a, b, alpha, rpb, q.heads, attn, st)) return launched();
+    if (nu::fast_qk(q.g, q.bh, q.D, a, b, alpha, rpb, mask, q.heads, attn, st)) return launched();
     const int64_t total = q.units * q.g.K;
     NA_FOR_D(q.D, hipLaunchKernelGGL(qk_plain<kD>, dim3(grid_for(total, 256)), dim3(256), 0, st,
-                                     q.g, a, b, alpha, rpb, q.heads, attn, total));
+                                     q.g, a, b, alpha, rpb, q.heads, mask, attn, total));
     return launched();
 }
 
@@ -710,14 +717,14 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 extern "C" {
 
 na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, const float *rpb,
-                float *attn, void *hip_stream) {
+                const uint8_t *mask, float *attn, void *hip_stream) {
     UProb q;
     na_status s = uvalidate(p, &q);
     if (s != NA_OK) return s;
     if (!std::isfinite(alpha)) return NA_ERR_INVALID_ARG;
     if ((s = check_ptrs({a, b, attn})) != NA_OK) return s;
     if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
-    return run_qk(q, (const float *)a, (const float *)b, (float)alpha, rpb, attn,
+    return run_qk(q, (const float *)a, (const float *)b, (float)alpha, rpb, mask, attn,
                   as_stream(hip_stream));
 }
 
@@ -776,15 +783,16 @@ na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *d
 }
 
 na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
-                         const float *rpb, float *probs, void *out, void *hip_stream) {
+                         const float *rpb, const uint8_t *mask, float *probs, void *out,
+                         void *hip_stream) {
     UProb u;
     na_status s = uvalidate(p, &u);
     if (s != NA_OK) return s;
     if ((s = check_ptrs({q, k, v, probs, out})) != NA_OK) return s;
     if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
     const hipStream_t st = as_stream(hip_stream);
-    if ((s = run_qk(u, (const float *)q, (const float *)k, (float)p->scale, rpb, probs, st)) !=
-        NA_OK)
+    if ((s = run_qk(u, (const float *)q, (const float *)k, (float)p->scale, rpb, mask, probs,
+                    st)) != NA_OK)
         return s;
     if ((s = run_softmax(u, probs, probs, st)) != NA_OK) return s;
     return run_av(u, probs, (const float *)v, 1.f, (float *)out, st);
@@ -806,7 +814,8 @@ na_status na_unfused_bwd(const na_problem *p, const void *q, const void *k, cons
     const hipStream_t st = as_stream(hip_stream);
     const float scale = (float)p->scale;
     // AGRAD: dP = dout . v over the window; VGRAD: dv = inverse sum of P dout
-    if ((s = run_qk(u, (const float *)dout, (const float *)v, 1.f, nullptr, dscores, st)) != NA_OK)
+    if ((s = run_qk(u, (const float *)dout, (const float *)v, 1.f, nullptr, nullptr, dscores, st)) !=
+        NA_OK)
         return s;
     if ((s = run_av_inverse(u, probs, (const float *)dout, 1.f, (float *)dv, st)) != NA_OK)
         return s;

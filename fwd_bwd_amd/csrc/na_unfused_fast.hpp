@@ -63,6 +63,7 @@ struct UArgs {
     const float *rpb;    // qk: relative positional bias [heads][2kt-1][2kh-1][2kw-1], or null
     int heads;           // qk with a bias: heads per batch element
     int rpb_off;         // qk with a bias: LDS byte offset of the bias table plane
+    const uint8_t *mask; // qk: window mask [tokens][K] shared by every (batch, head) plane, or null
 };
 
 // Head of a tile's (batch, head) plane: planes are the batch elements of the
@@ -177,22 +178,45 @@ __device__ __forceinline__ void load_round(const UArgs &a, const TileCtx &w, int
     }
 }
 
+// A masked-out window entry: its score is -inf, so the softmax gives it no weight.
+__device__ __forceinline__ float masked(const uint8_t *m, int64_t i, float v) {
+    return m[i] ? v : -INFINITY;
+}
+
 // LDS -> global, one wave: 16-byte pieces where aligned, else 4-byte ones,
-// four LDS reads in flight per lane.
+// four LDS reads in flight per lane. With a window mask, entry i of the
+// attention array takes mask[i - mbase] (the mask indexes one plane).
 __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, int wave, int r0,
                                             int it, const float *buf, float *dst,
-                                            const RunOffs &ro) {
+                                            const RunOffs &ro, int64_t mbase) {
     const int lane = threadIdx.x & 63;
     const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
+    const uint8_t *mk = a.mask ? a.mask - mbase : nullptr;
     for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
         const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
         const float *brow = buf + row * 8 * a.KP;
-        if (run_vec(rr, row * 8 * a.KP)) {
+        if (run_vec(rr, row * 8 * a.KP) &&
+            (!mk || ((reinterpret_cast<uintptr_t>(mk + rr.base) & 3) == 0))) {
             const int n4 = rr.n >> 2;
             const float4 *l4 = reinterpret_cast<const float4 *>(brow);
             float4 *g4 = reinterpret_cast<float4 *>(dst + rr.base);
-            for (int b = lane; b < n4; b += 64) g4[b] = l4[b];
-            for (int e = 4 * n4 + lane; e < rr.n; e += 64) dst[rr.base + e] = brow[e];
+            if (mk) {
+                const uchar4 *m4 = reinterpret_cast<const uchar4 *>(mk + rr.base);
+                for (int b = lane; b < n4; b += 64) {
+                    float4 v = l4[b];
+                    const uchar4 m = m4[b];
+                    v.x = m.x ? v.x : -INFINITY;
+                    v.y = m.y ? v.y : -INFINITY;
+                    v.z = m.z ? v.z : -INFINITY;
+                    v.w = m.w ? v.w : -INFINITY;
+                    g4[b] = v;
+                }
+                for (int e = 4 * n4 + lane; e < rr.n; e += 64)
+                    dst[rr.base + e] = masked(mk, rr.base + e, brow[e]);
+            } else {
+                for (int b = lane; b < n4; b += 64) g4[b] = l4[b];
+                for (int e = 4 * n4 + lane; e < rr.n; e += 64) dst[rr.base + e] = brow[e];
+            }
             continue;
         }
         if (ro.ok) {
@@ -202,7 +226,10 @@ __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, in
                 v[m] = 64 * m + lane < rr.n ? brow[64 * m + lane] : 0.f;
 #pragma unroll
             for (int m = 0; m < kRunSteps; ++m)
-                if (64 * m + lane < rr.n) dst[rr.base + ro.off[m]] = v[m];
+                if (64 * m + lane < rr.n) {
+                    const int64_t gi = rr.base + ro.off[m];
+                    dst[gi] = mk ? masked(mk, gi, v[m]) : v[m];
+                }
             continue;
         }
         for (int e0 = 0; e0 < rr.n; e0 += 4 * 64) {
@@ -215,7 +242,10 @@ __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, in
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = e0 + 64 * u + lane;
-                if (e < rr.n) dst[run_index(a, rr, e)] = v[u];
+                if (e < rr.n) {
+                    const int64_t gi = run_index(a, rr, e);
+                    dst[gi] = mk ? masked(mk, gi, v[u]) : v[u];
+                }
             }
         }
     }
@@ -247,6 +277,9 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
     float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
     const RunOffs ro = run_offs(a, w, 8);
+    // first attention entry of this tile's (batch, head) plane (the mask spans one plane)
+    const int64_t plane_tokens = (int64_t)a.g.ext[0] * a.g.ext[1] * a.g.ext[2];
+    const int64_t mbase = a.mask ? (w.lbase / plane_tokens) * plane_tokens * a.K : 0;
 
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
@@ -311,7 +344,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     }
             }
             __syncthreads();
-            store_round(a, w, wave, r0, j, buf, a.attn_out, ro);
+            store_round(a, w, wave, r0, j, buf, a.attn_out, ro, mbase);
             __syncthreads();
         }
     }
@@ -674,7 +707,7 @@ inline bool launch(Kern kern, const UPlan &pl, hipStream_t s) {
 // Register-tiled paths; each returns false (launching nothing) when the
 // problem is outside what they cover.
 inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const float *b, float alpha,
-                    const float *rpb, int heads, float *attn, hipStream_t s) {
+                    const float *rpb, const uint8_t *mask, int heads, float *attn, hipStream_t s) {
     UPlan pl;
     if (!plan(geo, bh, D, 0, 0, 0, &pl)) return false;
     pl.a.a = a;
@@ -682,6 +715,7 @@ inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const flo
     pl.a.attn_out = attn;
     pl.a.alpha = alpha;
     pl.a.rpb = rpb;
+    pl.a.mask = mask;
     pl.a.heads = heads;
     if (rpb) {
         // the bias table plane after the staging area

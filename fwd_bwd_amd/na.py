@@ -95,7 +95,7 @@ def load() -> ctypes.CDLL:
                                           ctypes.POINTER(i64)]
         lib.na_inverse_window.restype = ctypes.c_int
         dbl = ctypes.c_double
-        lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp, vp]
+        lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp]
         lib.na_rpb_grad_workspace_bytes.argtypes = [P]
         lib.na_rpb_grad_workspace_bytes.restype = ctypes.c_size_t
         lib.na_rpb_grad.argtypes = [P, vp, vp, vp, ctypes.c_size_t, vp]
@@ -104,7 +104,7 @@ def load() -> ctypes.CDLL:
         lib.na_av_inverse.argtypes = [P, vp, vp, dbl, vp, vp]
         lib.na_softmax.argtypes = [P, vp, vp, vp]
         lib.na_softmax_bwd.argtypes = [P, vp, vp, vp, vp]
-        lib.na_unfused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_unfused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.na_unfused_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
         for name in ("na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd",
@@ -328,10 +328,22 @@ def _check_rpb(rpb, kernel_size, heads, ndim, ref):
     return _ptr(rpb)
 
 
+def _check_mask(mask, ref, K):
+    """A window mask: uint8 [(T,) H, W, K] per token, on the device of ref."""
+    if mask is None:
+        return None
+    if mask.dtype != torch.uint8 or not mask.is_contiguous() or mask.device != ref.device:
+        raise ValueError("mask must be a contiguous uint8 tensor on the tensors' device")
+    if tuple(mask.shape) != tuple(ref.shape[2:-1]) + (K,):
+        raise ValueError(f"mask must have shape {tuple(ref.shape[2:-1]) + (K,)}")
+    return _ptr(mask)
+
+
 def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
-          attn: Optional[torch.Tensor] = None, rpb: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> [+ rpb[head, offset]] (na*_qk, QKRPB;
-    AGRAD with a = dout, b = v)."""
+          attn: Optional[torch.Tensor] = None, rpb: Optional[torch.Tensor] = None,
+          mask: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """attn[x, j] = alpha * <a_x, b_{N(x)_j}> [+ rpb[head, offset]], -inf where the
+    window mask is 0 (na*_qk, QKRPB; AGRAD with a = dout, b = v)."""
     _check_hm(a, b)
     ndim = a.dim() - 3
     K = _window_size(kernel_size, ndim)
@@ -339,9 +351,10 @@ def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: floa
     if b.shape != a.shape:
         raise ValueError("a and b must share their shape")
     rp = _check_rpb(rpb, kernel_size, a.shape[1], ndim, a)
+    mp = _check_mask(mask, a, K)
     if attn is None:
         attn = _attn_like(a, K)
-    _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, _ptr(attn),
+    _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, mp, _ptr(attn),
                         _stream_handle(a.device)))
     return attn
 
@@ -426,7 +439,7 @@ def na_softmax_bwd(probs: torch.Tensor, dprobs: torch.Tensor, kernel_size, dilat
 
 def na_unfused_fwd(q, k, v, kernel_size, dilation=1, scale: Optional[float] = None,
                    probs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                   rpb: Optional[torch.Tensor] = None):
+                   rpb: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None):
     """Unfused forward on head-major fp32 tensors: returns (probs, out)."""
     _check_hm(q, k, v)
     if not (q.shape == k.shape == v.shape):
@@ -434,12 +447,13 @@ def na_unfused_fwd(q, k, v, kernel_size, dilation=1, scale: Optional[float] = No
     K = _window_size(kernel_size, q.dim() - 3)
     p = make_problem_hm(q.shape, q.shape[-1], kernel_size, dilation, scale)
     rp = _check_rpb(rpb, kernel_size, q.shape[1], q.dim() - 3, q)
+    mp = _check_mask(mask, q, K)
     if probs is None:
         probs = _attn_like(q, K)
     if out is None:
         out = torch.empty_like(q)
-    _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), rp, _ptr(probs),
-                                 _ptr(out), _stream_handle(q.device)))
+    _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), rp, mp,
+                                 _ptr(probs), _ptr(out), _stream_handle(q.device)))
     return probs, out
 
 

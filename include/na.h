@@ -159,8 +159,13 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
 
 /* attn[x][j] = alpha * <a_x, b_{N(x)_j}> [+ rpb[head][offset]]: the window
  * scores (na*_qk with a = q, b = k, alpha = scale) and the gradient of the
- * weights of na*_av (AGRAD: a = dout, b = v, alpha = 1, rpb = NULL). attn must
- * not overlap a or b.
+ * weights of na*_av (AGRAD: a = dout, b = v, alpha = 1, rpb = mask = NULL).
+ * attn must not overlap a or b.
+ * mask (may be NULL): masked windows, as the issue's requester masks the
+ * result of na3d_qk to give each frame its own window: a byte array
+ * [(T,) H, W, K] per token, shared by every batch element and head; entries
+ * whose byte is 0 get the score -inf, so na_softmax gives them zero weight (a
+ * query with every entry masked gets all-zero weights and a zero output).
  * rpb (may be NULL): relative positional bias, the QKRPB of the maintainer's
  * unfused profile. A dense fp32 table [heads][2kt-1][2kh-1][2kw-1] (2D:
  * [heads][2kh-1][2kw-1]); the entry added to the score of query x and key y
@@ -168,7 +173,7 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
  * on the offset of the key from the query in class units, over the full
  * range -(k-1) .. k-1 a border-shifted window can reach. */
 na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, const float *rpb,
-                float *attn, void *hip_stream);
+                const uint8_t *mask, float *attn, void *hip_stream);
 
 /* Bytes of device workspace na_rpb_grad needs (0 on an invalid problem). */
 size_t na_rpb_grad_workspace_bytes(const na_problem *p);
@@ -203,11 +208,13 @@ na_status na_softmax(const na_problem *p, const float *attn, float *probs, void 
 na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *dprobs,
                          float *dscores, void *hip_stream);
 
-/* The unfused forward: probs = softmax(scale * na_qk(q, k) [+ rpb]),
- * out = na_av(probs, v). rpb may be NULL (no bias). probs
- * ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward. */
+/* The unfused forward: probs = softmax(scale * na_qk(q, k) [+ rpb], masked),
+ * out = na_av(probs, v). rpb and mask may be NULL (as in na_qk). probs
+ * ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward, which
+ * needs no mask: masked entries have zero weight in probs. */
 na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
-                         const float *rpb, float *probs, void *out, void *hip_stream);
+                         const float *rpb, const uint8_t *mask, float *probs, void *out,
+                         void *hip_stream);
 
 /* The unfused backward of sum(out * dout), from the forward's probs:
  * dprobs = na_qk(dout, v) (AGRAD), dv = na_av_inverse(probs, dout) (VGRAD),

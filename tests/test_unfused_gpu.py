@@ -184,7 +184,7 @@ def test_unfused_rejects_bf16_and_bad_shapes():
     p = na.make_problem_hm(q.shape, 16, (3, 3))
     p.dtype = na.NA_BF16
     attn = torch.zeros((1, 2, 8, 8, 9), device=dev)
-    status = na.load().na_qk(na.ctypes.byref(p), q.data_ptr(), q.data_ptr(), 1.0, None,
+    status = na.load().na_qk(na.ctypes.byref(p), q.data_ptr(), q.data_ptr(), 1.0, None, None,
                              attn.data_ptr(), None)
     assert status == na.NA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
@@ -283,3 +283,41 @@ def test_rpb_grad_of_arbitrary_scores_and_determinism():
         torch.cuda.synchronize()
         assert torch.equal(a, b)
         check({"drpb": a}, {"drpb": oracle.rpb_grad(np64(x), kernel, dil)}, f"rpb_grad {shape}")
+
+
+# ----------------------------------------------------------------------------- masked windows
+
+MASK_CASES = [((1, 2, 6, 20, 18, 32), (5, 3, 3), [1, 3, 3, 5, 5, 5]),   # register-tiled
+              ((1, 2, 5, 11, 13, 32), (3, 5, 5), [1, 1, 3, 3, 3]),
+              ((1, 1, 4, 9, 8, 64), (3, 3, 3), [3, 1, 1, 3])]            # plain kernels
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"{c[0]}-k{c[1]}" for c in MASK_CASES])
+def test_unfused_masked_windows_match_oracle(case):
+    """Per-frame time windows (the requester's masked na3d_qk): scores masked to
+    -inf outside each frame's own window, then the whole unfused forward and
+    backward, against the oracle; one query fully masked (zero weights)."""
+    shape, kernel, frame_k = case
+    say("mask", shape, kernel, frame_k)
+    q, k, v, dout = make_random(shape, torch.float32, seed=41)
+    mask = oracle.frame_window_mask(shape[2:-1], kernel, frame_k)
+    mask[1, 2, 3, :] = 0
+    scale = shape[-1] ** -0.5
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
+    md = torch.from_numpy(mask).to(dev)
+    s = na.na_qk(qd, kd, kernel, 1, alpha=scale, mask=md)
+    probs, out = na.na_unfused_fwd(qd, kd, vd, kernel, 1, scale, mask=md)
+    dq, dk, dv = na.na_unfused_bwd(qd, kd, vd, probs, dd, kernel, 1, scale)
+    torch.cuda.synchronize()
+    Q, K_, V, DO = (np64(t) for t in (q, k, v, dout))
+    P, o = oracle.unfused_fwd(Q, K_, V, kernel, 1, scale, mask=mask)
+    gq, gk, gv = oracle.unfused_bwd(Q, K_, V, P, DO, kernel, 1, scale)
+    s_ref = oracle.mask_scores(oracle.na_qk(Q, K_, kernel, 1, scale), mask)
+    s_gpu = np64(s)
+    assert np.array_equal(np.isneginf(s_gpu), np.isneginf(s_ref))
+    fin = np.isfinite(s_ref)
+    check({"scores": s_gpu[fin], "probs": probs, "out": out, "dq": dq, "dk": dk, "dv": dv},
+          {"scores": s_ref[fin], "probs": P, "out": o, "dq": gq, "dk": gk, "dv": gv},
+          f"mask {shape}")
+    assert torch.all(probs[:, :, 1, 2, 3] == 0) and torch.all(out[:, :, 1, 2, 3] == 0)
