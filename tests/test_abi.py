@@ -143,3 +143,48 @@ def test_window_helpers_match_oracle_and_brute_force(lib):
     assert na.window_start(5, 6, 1, 0) == -1
     with pytest.raises(na.NaError):
         na.inverse_window(5, 6, 1, 0)
+
+
+# ----------------------------------------------------------------------------- unfused ops
+
+def _hm_problem(shape=(2, 2, 16, 16, 16), kernel=(3, 3), dil=1):
+    return na.make_problem_hm(shape, shape[-1], kernel, dil)
+
+
+def test_unfused_entry_points_validate_on_host(lib):
+    """Argument errors of the unfused ops come back before anything is launched."""
+    p = _hm_problem()
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    # null / misaligned operands, non-finite alpha, misaligned bias table
+    assert lib.na_qk(ctypes.byref(p), None, fake, 1.0, None, None, fake, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_qk(ctypes.byref(p), fake, fake, 1.0, None, None, mis, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_qk(ctypes.byref(p), fake, fake, float("nan"), None, None, fake, None) == \
+        na.NA_ERR_INVALID_ARG
+    assert lib.na_qk(ctypes.byref(p), fake, fake, 1.0, mis, None, fake, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_av(ctypes.byref(p), fake, None, 1.0, fake, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_av_inverse(ctypes.byref(p), fake, fake, 1.0, None, None) == na.NA_ERR_INVALID_ARG
+    # the unfused ops are fp32 only
+    b16 = _hm_problem()
+    b16.dtype = na.NA_BF16
+    assert lib.na_qk(ctypes.byref(b16), fake, fake, 1.0, None, None, fake, None) == na.NA_ERR_UNSUPPORTED
+    # head_dim outside {16, 32, 64}: unsupported for the contractions
+    odd = _hm_problem(shape=(1, 2, 16, 16, 24))
+    assert lib.na_av(ctypes.byref(odd), fake, fake, 1.0, fake, None) == na.NA_ERR_UNSUPPORTED
+    bad = _hm_problem(kernel=(3, 17))
+    assert lib.na_softmax(ctypes.byref(bad), fake, fake, None) == na.NA_ERR_INVALID_ARG
+    # the bias gradient needs its workspace
+    need = lib.na_rpb_grad_workspace_bytes(ctypes.byref(p))
+    assert lib.na_rpb_grad(ctypes.byref(p), fake, fake, None, need, None) == na.NA_ERR_WORKSPACE
+    assert lib.na_rpb_grad(ctypes.byref(p), fake, fake, fake, need - 1, None) == na.NA_ERR_WORKSPACE
+    args = [fake] * 9
+    assert lib.na_unfused_bwd(ctypes.byref(p), *args, fake, fake, need - 1, None) == na.NA_ERR_WORKSPACE
+
+
+def test_rpb_workspace_bytes(lib):
+    # (batch 2 x heads 2) planes x one chunk of 256 tokens x (2*3-1)^2 offsets, fp32
+    assert lib.na_rpb_grad_workspace_bytes(ctypes.byref(_hm_problem())) == 2 * 2 * 1 * 25 * 4
+    # 3D, 3 chunks of a 600-token plane, offsets 5 * 9 * 9
+    p = _hm_problem(shape=(1, 3, 4, 10, 15, 32), kernel=(3, 5, 5))
+    assert lib.na_rpb_grad_workspace_bytes(ctypes.byref(p)) == 3 * 3 * 5 * 9 * 9 * 4
+    assert na.rpb_shape((3, 5, 5), 3, 3) == (3, 5, 9, 9)
