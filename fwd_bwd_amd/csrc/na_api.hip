@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <initializer_list>
+#include <type_traits>
 #include <vector>
 
 #include "na.h"
@@ -236,7 +237,13 @@ void set_divisors(na::fast::Geom &g) {
 // pad: points one 16-byte slot apart (see dq_tile), for grids with several
 // planes along T, whose plane boxes leave room for it.
 bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false) {
-    if (q.dtype != NA_F32 || (q.head_dim != 16 && q.head_dim != 32)) return false;
+    // fp32 with head_dim 16 or 32; bf16 / fp16 (converted to fp32 while staged)
+    // with head_dim 32
+    if (q.dtype == NA_F32) {
+        if (q.head_dim != 16 && q.head_dim != 32) return false;
+    } else if (q.head_dim != 32) {
+        return false;
+    }
     const bool t3 = q.ext[0] > 1;
     const bool wide = kind == 1 && border_walk_compiled(c, t3, (int)q.head_dim);
     if (!fast_walk_compiled(c, t3) && !wide) return false;
@@ -317,42 +324,71 @@ na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t 
     return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
 }
 
-// The compiled (head_dim, walk, several planes) combinations.
+// The compiled (head_dim, walk, several planes) combinations: fp32 below;
+// the 16-bit types take the head_dim 32 ones.
 #define NA_FAST_CASES(X)                                                                  \
     X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)                      \
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(16, 2, true) X(16, 3, true) X(16, 4, true)                                         \
     X(32, 2, true) X(32, 3, true) X(32, 4, true)
+#define NA_FAST_CASES16(X)                                                                \
+    X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
+    X(32, 2, true) X(32, 3, true) X(32, 4, true)
 
-na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgs &a, hipStream_t s) {
+template <typename T>
+na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgsT<T> &a, hipStream_t s) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return launch_fast(na::fast::fwd_kernel<D, C, C, T3>, pl, a, s);
-    NA_FAST_CASES(X)
+        return launch_fast(na::fast::fwd_kernel<T, D, C, C, T3>, pl, a, s);
+    if constexpr (std::is_same<T, float>::value) {
+        NA_FAST_CASES(X)
+    } else {
+        NA_FAST_CASES16(X)
+    }
 #undef X
     return NA_ERR_UNSUPPORTED;
 }
 
-na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
+template <typename T>
+na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
+    if constexpr (std::is_same<T, float>::value) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return pl.pad ? launch_fast(na::fast::dq_kernel<D, C, C, T3, T3>, pl, a, s)       \
-                      : launch_fast(na::fast::dq_kernel<D, C, C, T3, false>, pl, a, s);
-    NA_FAST_CASES(X)
+        return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3>, pl, a, s)    \
+                      : launch_fast(na::fast::dq_kernel<T, D, C, C, T3, false>, pl, a, s);
+        NA_FAST_CASES(X)
 #undef X
+    } else {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3>, pl, a, s)    \
+                      : launch_fast(na::fast::dq_kernel<T, D, C, C, T3, false>, pl, a, s);
+        NA_FAST_CASES16(X)
+#undef X
+    }
     return NA_ERR_UNSUPPORTED;
 }
 
-na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgs &a, hipStream_t s) {
+template <typename T>
+na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
+    if constexpr (std::is_same<T, float>::value) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
-        return pl.pad ? launch_fast(na::fast::dkdv_kernel<D, C, C, T3, T3>, pl, a, s)     \
-                      : launch_fast(na::fast::dkdv_kernel<D, C, C, T3, false>, pl, a, s);
-    NA_FAST_CASES(X)
+        return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, T3>, pl, a, s)  \
+                      : launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, false>, pl, a, s);
+        NA_FAST_CASES(X)
 #undef X
+    } else {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, T3>, pl, a, s)  \
+                      : launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, false>, pl, a, s);
+        NA_FAST_CASES16(X)
+#undef X
+    }
 #define X(D, C)                                                                          \
     if (a.g.head_dim == D && pl.c == C && !pl.t3)                                        \
-        return launch_fast(na::fast::dkdv_border_kernel<D, C, C, false>, pl, a, s);
+        return launch_fast(na::fast::dkdv_border_kernel<T, D, C, C, false>, pl, a, s);
     X(32, 6) X(32, 7)
 #undef X
     return NA_ERR_UNSUPPORTED;
@@ -367,15 +403,15 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
     FastPlan pl;
     if (fast_plan_fwd(pr, &pl)) {
-        na::fast::FwdArgs fa{};
+        na::fast::FwdArgsT<T> fa{};
         fa.g = pl.g;
-        fa.q = static_cast<const float *>(a.q);
-        fa.k = static_cast<const float *>(a.k);
-        fa.v = static_cast<const float *>(a.v);
-        fa.out = static_cast<float *>(a.out);
+        fa.q = static_cast<const T *>(a.q);
+        fa.k = static_cast<const T *>(a.k);
+        fa.v = static_cast<const T *>(a.v);
+        fa.out = static_cast<T *>(a.out);
         fa.lse = a.lse;
         fa.qscale = a.qscale;
-        return fast_fwd(pl, fa, s);
+        return fast_fwd<T>(pl, fa, s);
     }
     int lds;
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 3) * 4, &a.g, &lds))
@@ -399,17 +435,17 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 1) * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
     if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * (D + 1) * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
     if (variant == NA_BWD_GATHER) {
-        na::fast::BwdArgs fa{};
-        fa.q = static_cast<const float *>(a.q);
-        fa.k = static_cast<const float *>(a.k);
-        fa.v = static_cast<const float *>(a.v);
-        fa.out = static_cast<const float *>(a.out);
-        fa.dout = static_cast<const float *>(a.dout);
+        na::fast::BwdArgsT<T> fa{};
+        fa.q = static_cast<const T *>(a.q);
+        fa.k = static_cast<const T *>(a.k);
+        fa.v = static_cast<const T *>(a.v);
+        fa.out = static_cast<const T *>(a.out);
+        fa.dout = static_cast<const T *>(a.dout);
         fa.lse = a.lse;
         fa.delta = a.delta;
-        fa.dq = static_cast<float *>(a.dq);
-        fa.dk = static_cast<float *>(a.dk);
-        fa.dv = static_cast<float *>(a.dv);
+        fa.dq = static_cast<T *>(a.dq);
+        fa.dk = static_cast<T *>(a.dk);
+        fa.dv = static_cast<T *>(a.dv);
         fa.qscale = a.qscale;
         fa.scale = a.scale;
         // dq (which also writes delta) strictly before dk/dv, which reads it
@@ -417,7 +453,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
         if (phases & kPhaseDq) {
             if (fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;
-                const na_status st = fast_dq(pq, fa, s);
+                const na_status st = fast_dq<T>(pq, fa, s);
                 if (st != NA_OK) return st;
             } else {
                 auto kern = na::dq_kernel<T, D>;
@@ -439,7 +475,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
             if (fast_plan(pr, 1, c, 0, &pk, true) || fast_plan(pr, 1, c, 0, &pk)) {
                 fa.g = pk.g;
                 fa.walk_lo = 0;
-                const na_status st = fast_dkdv(pk, fa, s);
+                const na_status st = fast_dkdv<T>(pk, fa, s);
                 if (st != NA_OK) return st;
                 done = c;
             }
@@ -452,7 +488,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                     fa.g.n_tiles = (int)(pr.batch * pr.heads * fa.g.tiles[0] * fa.g.border.per_plane);
                     set_divisors(fa.g);
                 }
-                const na_status st = fast_dkdv(pk, fa, s);
+                const na_status st = fast_dkdv<T>(pk, fa, s);
                 if (st != NA_OK) return st;
                 done = cb;
             }

@@ -39,6 +39,8 @@
 
 #include "na_common.hpp"
 
+#include <type_traits>
+
 namespace na {
 namespace fast {
 
@@ -58,21 +60,29 @@ struct Geom {
     FastDiv f_dil[3], f_dil21;
 };
 
-struct FwdArgs {
+// T: the tensors' element type (float, or bf16 / f16, which the staging
+// converts to fp32 on the way into LDS); lse and delta are fp32.
+template <typename T>
+struct FwdArgsT {
     Geom g;
-    const float *q, *k, *v;
-    float *out, *lse;
+    const T *q, *k, *v;
+    T *out;
+    float *lse;
     float qscale;  // scale * log2(e)
 };
+using FwdArgs = FwdArgsT<float>;
 
-struct BwdArgs {
+template <typename T>
+struct BwdArgsT {
     Geom g;
-    const float *q, *k, *v, *out, *dout, *lse;
+    const T *q, *k, *v, *out, *dout;
+    const float *lse;
     float *delta;
-    float *dq, *dk, *dv;
+    T *dq, *dk, *dv;
     float qscale, scale;
     int walk_lo;  // dk/dv: this launch takes the tiles whose inverse walk exceeds walk_lo
 };
+using BwdArgs = BwdArgsT<float>;
 
 // Tile id -> tile. The head varies fastest: consecutive tiles (and so the
 // workgroups one XCD runs at a time) cover all heads of one position, whose
@@ -183,13 +193,32 @@ __device__ __forceinline__ Lane lane_geom(const TileCtx &w, int wave, int lane) 
 // lane, 64 consecutive slots per wave instruction; lanes on padding slots are
 // idle). Points past the grid repeat the last grid point; they are only ever
 // read masked. Completion: stage_wait().
-template <int D, int PS>
-__device__ __forceinline__ void stage_plane(const float *src, const TileCtx &w, int tk, int U1,
+template <typename T, int D, int PS>
+__device__ __forceinline__ void stage_plane(const T *src, const TileCtx &w, int tk, int U1,
                                             int E1, int U2, int E2, int rowb, char *lds) {
     constexpr int NC = D / 4, SP = PS / 16;  // chunks of data, slots per point
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int parts = (E2 * SP + 63) >> 6;
+    if constexpr (!std::is_same<T, float>::value) {
+        // 16-bit elements: the same fp32 layout, four elements (8 bytes) per
+        // 16-byte slot, loaded into registers and converted on the way
+        const T *plane = src + w.base + tk * w.st[0];
+        for (int part = 0; part < parts; ++part) {
+            const int j = part * 64 + lane;
+            const int col = j / SP, chunk = j - col * SP;
+            if (col >= E2 || chunk >= NC) continue;
+            const T *colp = plane + imin(U2 + col, w.n[2] - 1) * w.st[2] + chunk * 4;
+            char *dst = lds + part * 1024 + lane * 16;
+#pragma unroll 4
+            for (int r = wave; r < E1; r += kWaves) {
+                float d[4];
+                Io<T>::load4(colp + imin(U1 + r, w.n[1] - 1) * w.st[1], d);
+                *reinterpret_cast<f4 *>(dst + r * rowb) = f4{d[0], d[1], d[2], d[3]};
+            }
+        }
+        return;
+    }
     const char *plane = reinterpret_cast<const char *>(src) + (w.base + tk * w.st[0]) * 4;
     for (int part = 0; part < parts; ++part) {
         const int j = part * 64 + lane;
@@ -309,8 +338,8 @@ __device__ __forceinline__ void axpy_row(const f4 (&x)[2][D / 16], float w0, flo
 
 // Store a per-lane accumulator (dims as in axpy_patch) times mul to the
 // lane's own row.
-template <int D>
-__device__ __forceinline__ void store_row(float *dst, const f4 (&acc)[D / 4], float mul) {
+template <typename T, int D>
+__device__ __forceinline__ void store_row(T *dst, const f4 (&acc)[D / 4], float mul) {
     constexpr int NQ = D / 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -318,7 +347,7 @@ __device__ __forceinline__ void store_row(float *dst, const f4 (&acc)[D / 4], fl
         for (int j = 0; j < NQ; ++j) {
             const float o[4] = {acc[4 * j][i] * mul, acc[4 * j + 1][i] * mul,
                                 acc[4 * j + 2][i] * mul, acc[4 * j + 3][i] * mul};
-            Io<float>::store4(dst + 4 * (i + 4 * j), o);
+            Io<T>::store4(dst + 4 * (i + 4 * j), o);
         }
 }
 
@@ -340,8 +369,8 @@ struct Edge {
 
 // ============================================================================
 // Forward.
-template <int D, int CH, int CW, bool T3>
-__device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem) {
+template <typename T, int D, int CH, int CW, bool T3>
+__device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
@@ -379,9 +408,9 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
-        load_row<float, D>(a.q + qo + opaque_zero(), qr);
+        load_row<T, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
         for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
         stage_wait();
@@ -424,7 +453,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
             m = mj;
         }
         __syncthreads();
-        stage_plane<D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<T, D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // O_b[i][c] += v_e[dim(i, g)] * P[c][e]
@@ -450,7 +479,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
     }
 
     if (L.active) {
-        store_row<D>(a.out + qo, acc, 1.f / l);
+        store_row<T, D>(a.out + qo, acc, 1.f / l);
         a.lse[row_off(w, L.p)] = (m + __log2f(l)) * kLn2;
     }
 }
@@ -460,8 +489,8 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs &a, int tile, char *smem)
 // PAD: points one 16-byte slot apart in LDS (row pitch 2 mod 4 slots), which
 // makes key-major and d-major reads both conflict-free, so K is staged once
 // for both of its uses; without it K is staged twice, in each layout.
-template <int D, int CH, int CW, bool T3, bool PAD>
-__device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) {
+template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+__device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
@@ -492,8 +521,8 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
     float delta = 0.f;
     {
         float dor[D], orow[D];
-        load_row<float, D>(a.dout + qo, dor);
-        load_row<float, D>(a.out + qo, orow);
+        load_row<T, D>(a.dout + qo, dor);
+        load_row<T, D>(a.out + qo, orow);
 #pragma unroll
         for (int d = 0; d < D; ++d) delta += dor[d] * orow[d];
     }
@@ -508,9 +537,9 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<T, D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float dor[D];
-        load_row<float, D>(a.dout + qo + opaque_zero(), dor);
+        load_row<T, D>(a.dout + qo + opaque_zero(), dor);
         stage_wait();
 
         // dP_b[i][c] = <v_i, dout_c>
@@ -535,9 +564,9 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
                 });
         }
         __syncthreads();
-        stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
-        load_row<float, D>(a.q + qo + opaque_zero(), qr);
+        load_row<T, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
         for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
         stage_wait();
@@ -568,7 +597,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
         }
         if constexpr (!PAD) {
             __syncthreads();
-            stage_plane<D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+            stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
             stage_wait();
         }
 
@@ -588,7 +617,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgs &a, int tile, char *smem) 
         }
     }
 
-    if (L.active) store_row<D>(a.dq + qo, acc, a.scale);
+    if (L.active) store_row<T, D>(a.dq + qo, acc, a.scale);
 }
 
 // ============================================================================
@@ -605,8 +634,8 @@ __device__ __forceinline__ int tile_walk(const TileCtx &w) {
 }
 
 // PAD: as for dq_tile; dout is then staged once for dV and dS.
-template <int D, int CH, int CW, bool T3, bool PAD>
-__device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem) {
+template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+__device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
@@ -650,11 +679,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
     for (int j = 0; j < nplanes; ++j) {
         const int tq = tq0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<T, D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,
                          reinterpret_cast<float2 *>(smem + a.g.rows_off));
         float kr[D];
-        load_row<float, D>(a.k + ko + opaque_zero(), kr);
+        load_row<T, D>(a.k + ko + opaque_zero(), kr);
 #pragma unroll
         for (int d = 0; d < D; ++d) kr[d] *= a.qscale;
         stage_wait();
@@ -691,7 +720,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
                 });
         }
         __syncthreads();
-        stage_plane<D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<T, D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dV_b[i][c] += dout_e[dim(i, g)] * P[c][e]
@@ -710,13 +739,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
         }
         // one plane: dv is final here; storing it now frees its registers
         if constexpr (!T3)
-            if (L.active) store_row<D>(a.dv + ko, dv, 1.f);
+            if (L.active) store_row<T, D>(a.dv + ko, dv, 1.f);
         float vr[D];
         if constexpr (!PAD) {
             __syncthreads();
-            stage_plane<D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
+            stage_plane<T, D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         }
-        load_row<float, D>(a.v + ko + opaque_zero(), vr);
+        load_row<T, D>(a.v + ko + opaque_zero(), vr);
         if constexpr (!PAD) stage_wait();
 
         // dP_b[i][c] = <dout_i, v_c> - delta_i;  dS = P dP
@@ -745,7 +774,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
                 });
         }
         __syncthreads();
-        stage_plane<D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<T, D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // dK_b[i][c] += q_e[dim(i, g)] * dS[c][e]
@@ -765,37 +794,37 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int tile, char *smem
     }
 
     if (L.active) {
-        store_row<D>(a.dk + ko, dk, a.scale);
-        if constexpr (T3) store_row<D>(a.dv + ko, dv, 1.f);
+        store_row<T, D>(a.dk + ko, dk, a.scale);
+        if constexpr (T3) store_row<T, D>(a.dv + ko, dv, 1.f);
     }
 }
 
 // ============================================================================
 // Kernels: one workgroup per tile.
-template <int D, int CH, int CW, bool T3>
-__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
+template <typename T, int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    fwd_tile<D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    fwd_tile<T, D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <int D, int CH, int CW, bool T3, bool PAD>
-__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
+template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dq_tile<D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dq_tile<T, D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <int D, int CH, int CW, bool T3, bool PAD>
-__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<T, D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 // The same for the few border tiles with a longer walk: one workgroup per CU,
 // so that the longer walk never spills registers.
-template <int D, int CH, int CW, bool T3>
-__global__ void __launch_bounds__(kThreads, 1) dkdv_border_kernel(BwdArgs a) {
+template <typename T, int D, int CH, int CW, bool T3>
+__global__ void __launch_bounds__(kThreads, 1) dkdv_border_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<D, CH, CW, T3, false>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<T, D, CH, CW, T3, false>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 }  // namespace fast

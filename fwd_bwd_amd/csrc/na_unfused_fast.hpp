@@ -285,7 +285,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
         if (j > 0) __syncthreads();
-        stage_plane<D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        stage_plane<float, D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
         load_row<float, D>(a.a + qo + opaque_zero(), qr);
 #pragma unroll
@@ -408,7 +408,7 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) pin4(s[i]);
-        stage_plane<D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<float, D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // O_b[i][c] += b_e[dim(i, g)] * attn[c][e]
@@ -426,7 +426,7 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
                 });
         }
     }
-    if (L.active) store_row<D>(a.out + elem_off(w, L.p), acc, a.alpha);
+    if (L.active) store_row<float, D>(a.out + elem_off(w, L.p), acc, a.alpha);
 }
 
 // ============================================================================
@@ -519,7 +519,7 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) pin4(s[i]);
         __syncthreads();
-        stage_plane<D, PS>(a.a, w, tq, U[1], E[1], U[2], E[2], rb, smem);
+        stage_plane<float, D, PS>(a.a, w, tq, U[1], E[1], U[2], E[2], rb, smem);
         stage_wait();
 
         // Out_b[i][c] += a_e[dim(i, g)] * attn[e][c]
@@ -551,9 +551,9 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) acc[4 * j + t][i] = acc[4 * j + t][i] * a.alpha + o[t];
                 }
-            store_row<D>(dst, acc, 1.f);
+            store_row<float, D>(dst, acc, 1.f);
         } else {
-            store_row<D>(dst, acc, a.alpha);
+            store_row<float, D>(dst, acc, a.alpha);
         }
     }
 }

@@ -113,6 +113,12 @@ SMALL = [
     ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
     ((2, 26, 27, 2, 64), (5, 5), 2, torch.float16),
     ((1, 40, 37, 2, 32), (9, 9), 1, torch.float16),
+    # 16-bit tensors on the register-resident kernels (head_dim 32, square walks):
+    # 2D with border launches, 3D, dilation
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.bfloat16),
+    ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float16),
+    ((1, 5, 40, 36, 1, 32), (3, 7, 7), 1, torch.bfloat16),
+    ((1, 35, 33, 2, 32), (5, 5), (1, 2), torch.float16),
 ]
 
 
