@@ -16,6 +16,10 @@ Effective FLOPs (the metric's convention): forward 4*N*heads*K*D, backward
 2.5x that, with N tokens and K = prod(kernel). Prints one JSON line on stdout;
 progress goes to stderr.
 
+Beside the headline step the same run times the KV-parallel backward variant
+on the same inputs ("kvparallel") and the headline shape with fp16 tensors
+("fp16").
+
 The same function is also timed through the unfused ops (the script's method
 = 'unfused': window scores, softmax, weighted sum, and their backward AGRAD,
 VGRAD, softmax backward, QGRAD, KGRAD, on head-major copies of the same
@@ -308,6 +312,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the 3D workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path leg")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the KV-parallel backward and fp16 legs of the headline shape")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -382,6 +388,28 @@ def main():
         torch.cuda.empty_cache()
 
     run_unfused(w, host)
+    if not args.no_extra and args.workload == HEADLINE:
+        # the KV-parallel backward (atomic dq accumulation) on the same inputs, and the
+        # same shape with fp16 tensors (the maintainer's second profiled precision)
+        extra = {}
+        if args.variant == "gather":
+            rk = Runner(w, "kvparallel")
+            log(f"[bench] timing {w.name} with the KV-parallel backward")
+            msk, _, perk = rk.time(args.steps, args.warmup)
+            extra["kvparallel"] = summarize(w, msk, perk)
+            log(f"[bench] kvparallel {w.name}: {extra['kvparallel']}")
+            del rk
+            torch.cuda.empty_cache()
+        w16 = WORKLOADS.get(w.name.replace("_f32", "_f16"))
+        if w16 is not None:
+            r16 = Runner(w16, args.variant)
+            log(f"[bench] timing {w16.name}")
+            ms16, _, per16 = r16.time(args.steps, args.warmup)
+            extra["fp16"] = {"workload": w16.name, **summarize(w16, ms16, per16)}
+            log(f"[bench] {w16.name}: {extra['fp16']}")
+            del r16
+            torch.cuda.empty_cache()
+        result.update(extra)
     if not args.no_secondary and args.workload == HEADLINE:
         w3 = WORKLOADS[HEADLINE_3D]
         r3 = Runner(w3, args.variant)
