@@ -225,6 +225,27 @@ class UnfusedRunner:
         step = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]))
         return step, per
 
+    def time_chain(self, steps, warmup):
+        """na_unfused_fwd + na_unfused_bwd: the same ops, with the window softmax and
+        its backward taken inside the score kernels where a query's window fits."""
+        w = self.w
+        kk, dd, sc = w.kernel, w.dilation, w.the_scale
+
+        def step():
+            na.na_unfused_fwd(self.q, self.k, self.v, kk, dd, sc, probs=self.probs, out=self.out)
+            na.na_unfused_bwd(self.q, self.k, self.v, self.probs, self.dout, kk, dd, sc,
+                              dscores=self.ds, grads=(self.dq, self.dk, self.dv))
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
 
 def unfused_summary(w, step, per):
     f_fwd, f_bwd = flops(w)
@@ -383,6 +404,7 @@ def main():
         log(f"[bench] timing the unfused ops on {wl.name}")
         step, per_u = u.time(args.steps, args.warmup)
         unfused[wl.name] = unfused_summary(wl, step, per_u)
+        unfused[wl.name]["chain_ms_per_step"] = round(u.time_chain(args.steps, args.warmup), 4)
         log(f"[bench] unfused {wl.name}: {unfused[wl.name]}")
         del u
         torch.cuda.empty_cache()

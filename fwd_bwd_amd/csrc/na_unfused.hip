@@ -653,6 +653,32 @@ na_status run_rpb_grad(const UProb &q, const float *ds, float *drpb, void *ws, s
     return launched();
 }
 
+// Scores and the window softmax: one kernel where the whole window of a query
+// fits the lane's registers (single-plane grids), else scores then softmax.
+na_status run_qk_softmax(const UProb &q, const float *a, const float *b, float alpha,
+                         const float *rpb, const uint8_t *mask, float *probs, hipStream_t st);
+na_status run_softmax(const UProb &q, const float *x, float *y, hipStream_t st);
+na_status run_softmax_bwd(const UProb &q, const float *p, const float *dp, float *ds,
+                          hipStream_t st);
+
+na_status run_qk_softmax(const UProb &q, const float *a, const float *b, float alpha,
+                         const float *rpb, const uint8_t *mask, float *probs, hipStream_t st) {
+    if (q.units == 0) return NA_OK;
+    if (nu::fast_qk_softmax(q.g, q.bh, q.D, a, b, alpha, rpb, mask, (int)q.heads, probs, st))
+        return launched();
+    na_status s = run_qk(q, a, b, alpha, rpb, mask, probs, st);
+    return s != NA_OK ? s : run_softmax(q, probs, probs, st);
+}
+
+// AGRAD and the softmax backward: one kernel on single-plane grids, else dP then dS.
+na_status run_qk_softmax_bwd(const UProb &q, const float *dout, const float *v,
+                             const float *probs, float *dscores, hipStream_t st) {
+    if (q.units == 0) return NA_OK;
+    if (nu::fast_qk_softmax_bwd(q.g, q.bh, q.D, dout, v, probs, dscores, st)) return launched();
+    na_status s = run_qk(q, dout, v, 1.f, nullptr, nullptr, dscores, st);
+    return s != NA_OK ? s : run_softmax_bwd(q, probs, dscores, dscores, st);
+}
+
 na_status run_av(const UProb &q, const float *attn, const float *b, float alpha, float *out,
                  hipStream_t st) {
     if (nu::fast_av(q.g, q.bh, q.D, attn, b, alpha, out, st)) return launched();
@@ -728,6 +754,28 @@ na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha,
                   as_stream(hip_stream));
 }
 
+na_status na_qk_softmax(const na_problem *p, const void *a, const void *b, double alpha,
+                        const float *rpb, const uint8_t *mask, float *probs, void *hip_stream) {
+    UProb q;
+    na_status s = uvalidate(p, &q);
+    if (s != NA_OK) return s;
+    if (!std::isfinite(alpha)) return NA_ERR_INVALID_ARG;
+    if ((s = check_ptrs({a, b, probs})) != NA_OK) return s;
+    if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
+    return run_qk_softmax(q, (const float *)a, (const float *)b, (float)alpha, rpb, mask, probs,
+                          as_stream(hip_stream));
+}
+
+na_status na_qk_softmax_bwd(const na_problem *p, const void *dout, const void *v,
+                            const float *probs, float *dscores, void *hip_stream) {
+    UProb q;
+    na_status s = uvalidate(p, &q);
+    if (s != NA_OK) return s;
+    if ((s = check_ptrs({dout, v, probs, dscores})) != NA_OK) return s;
+    return run_qk_softmax_bwd(q, (const float *)dout, (const float *)v, probs, dscores,
+                              as_stream(hip_stream));
+}
+
 size_t na_rpb_grad_workspace_bytes(const na_problem *p) {
     UProb q;
     if (uvalidate(p, &q, false) != NA_OK) return 0;
@@ -791,10 +839,9 @@ na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, cons
     if ((s = check_ptrs({q, k, v, probs, out})) != NA_OK) return s;
     if (rpb && !aligned16(rpb)) return NA_ERR_INVALID_ARG;
     const hipStream_t st = as_stream(hip_stream);
-    if ((s = run_qk(u, (const float *)q, (const float *)k, (float)p->scale, rpb, mask, probs,
-                    st)) != NA_OK)
+    if ((s = run_qk_softmax(u, (const float *)q, (const float *)k, (float)p->scale, rpb, mask,
+                            probs, st)) != NA_OK)
         return s;
-    if ((s = run_softmax(u, probs, probs, st)) != NA_OK) return s;
     return run_av(u, probs, (const float *)v, 1.f, (float *)out, st);
 }
 
@@ -813,14 +860,13 @@ na_status na_unfused_bwd(const na_problem *p, const void *q, const void *k, cons
     }
     const hipStream_t st = as_stream(hip_stream);
     const float scale = (float)p->scale;
-    // AGRAD: dP = dout . v over the window; VGRAD: dv = inverse sum of P dout
-    if ((s = run_qk(u, (const float *)dout, (const float *)v, 1.f, nullptr, nullptr, dscores, st)) !=
+    // AGRAD and the softmax backward: dS = P (dP - rowsum(P dP)), dP = dout . v over
+    // the window; VGRAD: dv = inverse sum of P dout; the bias gradient sums dS
+    if ((s = run_qk_softmax_bwd(u, (const float *)dout, (const float *)v, probs, dscores, st)) !=
         NA_OK)
         return s;
     if ((s = run_av_inverse(u, probs, (const float *)dout, 1.f, (float *)dv, st)) != NA_OK)
         return s;
-    // softmax backward in place: dS = P (dP - rowsum(P dP)); the bias gradient sums dS
-    if ((s = run_softmax_bwd(u, probs, dscores, dscores, st)) != NA_OK) return s;
     if (drpb && (s = run_rpb_grad(u, dscores, drpb, workspace, workspace_bytes, st)) != NA_OK)
         return s;
     // QGRAD and KGRAD

@@ -188,10 +188,10 @@ __device__ __forceinline__ float masked(const uint8_t *m, int64_t i, float v) {
 // attention array takes mask[i - mbase] (the mask indexes one plane).
 __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, int wave, int r0,
                                             int it, const float *buf, float *dst,
-                                            const RunOffs &ro, int64_t mbase) {
+                                            const RunOffs &ro, int64_t mbase, bool use_mask) {
     const int lane = threadIdx.x & 63;
     const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
-    const uint8_t *mk = a.mask ? a.mask - mbase : nullptr;
+    const uint8_t *mk = use_mask && a.mask ? a.mask - mbase : nullptr;
     for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
         const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
         const float *brow = buf + row * 8 * a.KP;
@@ -253,8 +253,14 @@ __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, in
 
 // ============================================================================
 // qk: attn[x][j] = alpha <a_x, b_{N(x)_j}>
-template <int D, int CH, int CW, bool T3, bool RPB>
+// MODE 0: the scores. MODE 1 (single-plane grids): the window softmax of the
+// scores, computed in the lane's registers (the whole window is there), so
+// the probabilities leave instead of the scores. MODE 2 (single-plane grids):
+// the scores are dP = <dout, v> (AGRAD); the lane's probabilities come in
+// through LDS and dS = P (dP - sum_j P dP) leaves (the softmax backward).
+template <int D, int CH, int CW, bool T3, bool RPB, int MODE>
 __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
+    static_assert(MODE == 0 || !T3, "the fused softmax needs the whole window in one plane");
     constexpr int PS = D * 4, NC = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
@@ -325,10 +331,75 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
             for (int i = threadIdx.x; i < RH * RW; i += kThreads) dstl[i] = src[i];
             tbl = dstl + (us[1] - L.p[1] + w.k[1] - 1) * RW + (us[2] - L.p[2] + w.k[2] - 1);
         }
+        if constexpr (MODE == 1) {
+            // window softmax in registers: bias, window and mask decide the
+            // entries; the others get zero weight
+            const uint8_t *mrow = nullptr;
+            if (a.mask) {
+                const int c0[3] = {w.o[0], L.p[1], L.p[2]};
+                mrow = a.mask + (row_off(w, c0) - (w.lbase / plane_tokens) * plane_tokens) * a.K;
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
+                    const int jh = h - lo[1], jw = wc - lo[2];
+                    bool ok = (unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2];
+                    if (ok && mrow) ok = mrow[jh * a.kw + jw] != 0;
+                    float v = s[i][e];
+                    if constexpr (RPB) v += tbl[h * (2 * w.k[2] - 1) + wc];
+                    s[i][e] = ok ? v : -INFINITY;
+                    m = fmaxf(m, s[i][e]);
+                }
+            if (m == -INFINITY) m = 0.f;   // every entry masked out: zero weights
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[i][e] = __expf(s[i][e] - m);
+                    l += s[i][e];
+                }
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[i][e] *= inv;
+        }
         __syncthreads();  // the staged plane is read no more: its LDS takes the rows
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
-            if (lr >= r0 && lr < r0 + a.rows_round) {
-                float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
+            const bool mine = lr >= r0 && lr < r0 + a.rows_round;
+            float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
+            if constexpr (MODE == 2) {
+                // this round's probabilities into the slots, then dS in place
+                load_round(a, w, wave, r0, j, buf, a.attn, ro);
+                stage_wait();
+                if (mine) {
+                    float rs = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int jh = 2 * (i / CW) + (e >> 1) - lo[1];
+                            const int jw = 2 * (i % CW) + (e & 1) - lo[2];
+                            if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2])
+                                rs += slot[jh * a.kw + jw] * s[i][e];
+                        }
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int jh = 2 * (i / CW) + (e >> 1) - lo[1];
+                            const int jw = 2 * (i % CW) + (e & 1) - lo[2];
+                            if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2]) {
+                                float *q = slot + jh * a.kw + jw;
+                                *q = *q * (s[i][e] - rs);
+                            }
+                        }
+                }
+            } else if (mine) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -336,7 +407,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                         const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
                         const int jh = h - lo[1], jw = wc - lo[2];
                         if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2]) {
-                            if constexpr (RPB)
+                            if constexpr (RPB && MODE == 0)
                                 slot[jh * a.kw + jw] = s[i][e] + tbl[h * (2 * w.k[2] - 1) + wc];
                             else
                                 slot[jh * a.kw + jw] = s[i][e];
@@ -344,7 +415,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                     }
             }
             __syncthreads();
-            store_round(a, w, wave, r0, j, buf, a.attn_out, ro, mbase);
+            store_round(a, w, wave, r0, j, buf, a.attn_out, ro, mbase, MODE == 0);
             __syncthreads();
         }
     }
@@ -558,10 +629,10 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
     }
 }
 
-template <int D, int CH, int CW, bool T3, bool RPB>
+template <int D, int CH, int CW, bool T3, bool RPB, int MODE>
 __global__ void __launch_bounds__(kThreads, 2) qk_kernel(UArgs a) {
     extern __shared__ __align__(16) char smem[];
-    qk_tile<D, CH, CW, T3, RPB>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    qk_tile<D, CH, CW, T3, RPB, MODE>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 template <int D, int CH, int CW, bool T3>
@@ -725,9 +796,59 @@ inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const flo
     }
 #define X(DD, C, T3)                                                                          \
     if (D == DD && pl.c == C && pl.t3 == T3)                                                  \
-        return rpb ? launch(qk_kernel<DD, C, C, T3, true>, pl, s)                             \
-                   : launch(qk_kernel<DD, C, C, T3, false>, pl, s);
+        return rpb ? launch(qk_kernel<DD, C, C, T3, true, 0>, pl, s)                          \
+                   : launch(qk_kernel<DD, C, C, T3, false, 0>, pl, s);
     NU_CASES(X)
+#undef X
+    return false;
+}
+
+// The single-plane compiled cases (the fused softmax needs the whole window
+// of a query in one plane).
+#define NU_CASES2D(X)                                                        \
+    X(16, 2) X(16, 3) X(16, 4) X(16, 5) X(32, 2) X(32, 3) X(32, 4) X(32, 5)
+
+// Scores plus the window softmax in one kernel: probs (2D only).
+inline bool fast_qk_softmax(const Geo &geo, int64_t bh, int D, const float *a, const float *b,
+                            float alpha, const float *rpb, const uint8_t *mask, int heads,
+                            float *probs, hipStream_t s) {
+    UPlan pl;
+    if (!plan(geo, bh, D, 0, 0, 0, &pl) || pl.t3) return false;
+    pl.a.a = a;
+    pl.a.b = b;
+    pl.a.attn_out = probs;
+    pl.a.alpha = alpha;
+    pl.a.rpb = rpb;
+    pl.a.mask = mask;
+    pl.a.heads = heads;
+    if (rpb) {
+        pl.a.rpb_off = (pl.lds + 15) & ~15;
+        pl.lds = pl.a.rpb_off + (2 * geo.ker[1] - 1) * (2 * geo.ker[2] - 1) * 4;
+        if (pl.lds > kLdsCap) return false;
+    }
+#define X(DD, C)                                                                              \
+    if (D == DD && pl.c == C)                                                                 \
+        return rpb ? launch(qk_kernel<DD, C, C, false, true, 1>, pl, s)                       \
+                   : launch(qk_kernel<DD, C, C, false, false, 1>, pl, s);
+    NU_CASES2D(X)
+#undef X
+    return false;
+}
+
+// AGRAD plus the softmax backward in one kernel: dscores from dout, v, probs (2D only).
+inline bool fast_qk_softmax_bwd(const Geo &geo, int64_t bh, int D, const float *dout,
+                                const float *v, const float *probs, float *dscores,
+                                hipStream_t s) {
+    UPlan pl;
+    if (!plan(geo, bh, D, 0, 0, 0, &pl) || pl.t3) return false;
+    pl.a.a = dout;
+    pl.a.b = v;
+    pl.a.attn = probs;
+    pl.a.attn_out = dscores;
+    pl.a.alpha = 1.f;
+#define X(DD, C) \
+    if (D == DD && pl.c == C) return launch(qk_kernel<DD, C, C, false, false, 2>, pl, s);
+    NU_CASES2D(X)
 #undef X
     return false;
 }

@@ -34,7 +34,8 @@ VARIANTS = {"gather": NA_BWD_GATHER, "kvparallel": NA_BWD_KVPARALLEL}
 EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na_bwd_dq",
            "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
-           "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad")
+           "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
+           "na_qk_softmax_bwd")
 
 
 class NaProblem(ctypes.Structure):
@@ -96,6 +97,10 @@ def load() -> ctypes.CDLL:
         lib.na_inverse_window.restype = ctypes.c_int
         dbl = ctypes.c_double
         lib.na_qk.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp]
+        lib.na_qk_softmax.argtypes = [P, vp, vp, dbl, vp, vp, vp, vp]
+        lib.na_qk_softmax.restype = ctypes.c_int
+        lib.na_qk_softmax_bwd.argtypes = [P, vp, vp, vp, vp, vp]
+        lib.na_qk_softmax_bwd.restype = ctypes.c_int
         lib.na_rpb_grad_workspace_bytes.argtypes = [P]
         lib.na_rpb_grad_workspace_bytes.restype = ctypes.c_size_t
         lib.na_rpb_grad.argtypes = [P, vp, vp, vp, ctypes.c_size_t, vp]
@@ -357,6 +362,40 @@ def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: floa
     _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, mp, _ptr(attn),
                         _stream_handle(a.device)))
     return attn
+
+
+def na_qk_softmax(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: float = 1.0,
+                  probs: Optional[torch.Tensor] = None, rpb: Optional[torch.Tensor] = None,
+                  mask: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """softmax(na_qk(a, b, alpha, rpb, mask)) over the window axis."""
+    _check_hm(a, b)
+    ndim = a.dim() - 3
+    K = _window_size(kernel_size, ndim)
+    if b.shape != a.shape:
+        raise ValueError("a and b must share their shape")
+    p = make_problem_hm(a.shape, a.shape[-1], kernel_size, dilation)
+    rp = _check_rpb(rpb, kernel_size, a.shape[1], ndim, a)
+    mp = _check_mask(mask, a, K)
+    if probs is None:
+        probs = _attn_like(a, K)
+    _check(load().na_qk_softmax(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, mp,
+                                _ptr(probs), _stream_handle(a.device)))
+    return probs
+
+
+def na_qk_softmax_bwd(dout: torch.Tensor, v: torch.Tensor, probs: torch.Tensor, kernel_size,
+                      dilation=1, dscores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dS = probs * (dP - rowsum(probs * dP)) with dP = na_qk(dout, v)."""
+    _check_hm(dout, v, probs)
+    K = _window_size(kernel_size, dout.dim() - 3)
+    if probs.shape != dout.shape[:-1] + (K,) or v.shape != dout.shape:
+        raise ValueError("probs must be [B, heads, (T,) H, W, prod(kernel_size)], v like dout")
+    p = make_problem_hm(dout.shape, dout.shape[-1], kernel_size, dilation)
+    if dscores is None:
+        dscores = _attn_like(dout, K)
+    _check(load().na_qk_softmax_bwd(ctypes.byref(p), _ptr(dout), _ptr(v), _ptr(probs),
+                                    _ptr(dscores), _stream_handle(dout.device)))
+    return dscores
 
 
 def na_rpb_grad(dscores: torch.Tensor, kernel_size, dilation=1,

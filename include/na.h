@@ -175,6 +175,19 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
 na_status na_qk(const na_problem *p, const void *a, const void *b, double alpha, const float *rpb,
                 const uint8_t *mask, float *attn, void *hip_stream);
 
+/* na_qk (with a = q, b = k, alpha = scale, optional rpb and mask) followed by
+ * na_softmax, writing only the probabilities: on single-plane grids one
+ * kernel takes each query's whole window softmax in registers, elsewhere the
+ * two ops run in turn. Same layouts and rules as na_qk. */
+na_status na_qk_softmax(const na_problem *p, const void *a, const void *b, double alpha,
+                        const float *rpb, const uint8_t *mask, float *probs, void *hip_stream);
+
+/* AGRAD followed by the softmax backward: dscores = probs * (dP - rowsum(probs * dP))
+ * with dP[x][j] = <dout_x, v_{N(x)_j}>; one kernel on single-plane grids, else
+ * na_qk then na_softmax_bwd. dscores must not overlap probs. */
+na_status na_qk_softmax_bwd(const na_problem *p, const void *dout, const void *v,
+                            const float *probs, float *dscores, void *hip_stream);
+
 /* Bytes of device workspace na_rpb_grad needs (0 on an invalid problem). */
 size_t na_rpb_grad_workspace_bytes(const na_problem *p);
 
@@ -208,8 +221,8 @@ na_status na_softmax(const na_problem *p, const float *attn, float *probs, void 
 na_status na_softmax_bwd(const na_problem *p, const float *probs, const float *dprobs,
                          float *dscores, void *hip_stream);
 
-/* The unfused forward: probs = softmax(scale * na_qk(q, k) [+ rpb], masked),
- * out = na_av(probs, v). rpb and mask may be NULL (as in na_qk). probs
+/* The unfused forward: probs = softmax(scale * na_qk(q, k) [+ rpb], masked)
+ * (na_qk_softmax), out = na_av(probs, v). rpb and mask may be NULL (as in na_qk). probs
  * ([B, heads, (T,) H, W, K] fp32) is an output, kept for the backward, which
  * needs no mask: masked entries have zero weight in probs. */
 na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, const void *v,
@@ -217,8 +230,8 @@ na_status na_unfused_fwd(const na_problem *p, const void *q, const void *k, cons
                          void *hip_stream);
 
 /* The unfused backward of sum(out * dout), from the forward's probs:
- * dprobs = na_qk(dout, v) (AGRAD), dv = na_av_inverse(probs, dout) (VGRAD),
- * dscores = softmax backward, dq = scale * na_av(dscores, k) (QGRAD),
+ * dscores = softmax backward of dprobs = na_qk(dout, v) (AGRAD; together
+ * na_qk_softmax_bwd), dv = na_av_inverse(probs, dout) (VGRAD), dq = scale * na_av(dscores, k) (QGRAD),
  * dk = scale * na_av_inverse(dscores, q) (KGRAD), and, when drpb is not
  * NULL, the bias gradient drpb = na_rpb_grad(dscores) (workspace of
  * na_rpb_grad_workspace_bytes; ignored when drpb is NULL). dscores is a

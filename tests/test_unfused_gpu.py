@@ -321,3 +321,38 @@ def test_unfused_masked_windows_match_oracle(case):
           {"scores": s_ref[fin], "probs": P, "out": o, "dq": gq, "dk": gk, "dv": gv},
           f"mask {shape}")
     assert torch.all(probs[:, :, 1, 2, 3] == 0) and torch.all(out[:, :, 1, 2, 3] == 0)
+
+
+# ----------------------------------------------------------------------------- softmax fused into the score kernels
+
+SMX_CASES = [((1, 2, 40, 37, 32), (9, 9), 1), ((2, 3, 13, 17, 16), (3, 3), (2, 3)),
+             ((1, 2, 19, 23, 32), (5, 5), 1), ((1, 2, 5, 11, 13, 32), (3, 5, 5), 1)]
+
+
+@pytest.mark.parametrize("case", SMX_CASES, ids=[_id(c) for c in SMX_CASES])
+def test_qk_softmax_and_its_backward(case):
+    """The window softmax taken inside the score kernel (single-plane grids;
+    3D grids run the two ops in turn), with a bias and a mask, and AGRAD with
+    the softmax backward in one kernel, against the oracle."""
+    shape, kernel, dil = case
+    say("qk_softmax", _id(case))
+    ndim = len(shape) - 3
+    a, b, g, _ = make_random(shape, torch.float32, seed=_seed(case) + 9)
+    gen = torch.Generator(device="cpu").manual_seed(_seed(case) + 10)
+    rpb = torch.randn(na.rpb_shape(kernel, shape[1], ndim), generator=gen)
+    K = int(np.prod(kernel))
+    mask = (torch.rand(shape[2:-1] + (K,), generator=gen) > 0.2).to(torch.uint8)
+    mask[(0,) * ndim] = 0                      # one query with every entry masked
+    dev = torch.device("cuda:0")
+    ad, bd, gd, rd, md = (t.to(dev) for t in (a, b, g, rpb, mask))
+    p = na.na_qk_softmax(ad, bd, kernel, dil, alpha=0.6, rpb=rd, mask=md)
+    p2 = na.na_qk_softmax(ad, bd, kernel, dil, alpha=0.6)
+    ds = na.na_qk_softmax_bwd(gd, bd, p2, kernel, dil)
+    torch.cuda.synchronize()
+    A, B, G, RP = (np64(t) for t in (a, b, g, rpb))
+    P_ref = oracle.softmax(oracle.mask_scores(oracle.na_qk(A, B, kernel, dil, 0.6, rpb=RP),
+                                              mask.numpy()))
+    P2_ref = oracle.softmax(oracle.na_qk(A, B, kernel, dil, 0.6))
+    dS_ref = oracle.softmax_bwd(np64(p2), oracle.na_qk(G, B, kernel, dil, 1.0))
+    check({"probs": p, "probs_plain": p2, "dscores": ds},
+          {"probs": P_ref, "probs_plain": P2_ref, "dscores": dS_ref}, "qk_softmax " + _id(case))
