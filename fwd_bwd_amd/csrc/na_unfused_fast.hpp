@@ -282,7 +282,11 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     // the lane's point in its wave's 8 x 8 quarter, and the wave's LDS buffer
     const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
     float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
-    const RunOffs ro = run_offs(a, w, 8);
+    // row-run offsets: formed once per tile for the plain scores; the softmax
+    // modes form them after the window's scores, which they would otherwise
+    // share the registers with (the bias variant spilled)
+    RunOffs ro;
+    if constexpr (MODE == 0) ro = run_offs(a, w, 8);
     // first attention entry of this tile's (batch, head) plane (the mask spans one plane)
     const int64_t plane_tokens = (int64_t)a.g.ext[0] * a.g.ext[1] * a.g.ext[2];
     const int64_t mbase = a.mask ? (w.lbase / plane_tokens) * plane_tokens * a.K : 0;
@@ -369,6 +373,7 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
                 for (int e = 0; e < 4; ++e) s[i][e] *= inv;
         }
         __syncthreads();  // the staged plane is read no more: its LDS takes the rows
+        if constexpr (MODE != 0) ro = run_offs(a, w, 8);
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
             const bool mine = lr >= r0 && lr < r0 + a.rows_round;
             float *slot = buf + ((lr - r0) * 8 + lc) * a.KP;
@@ -444,7 +449,6 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
     const char *baseB = smem + (us[1] - U[1]) * rb + (us[2] - U[2]) * PS + c * 16;
     const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
     float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_round * 8 * a.KP);
-    const RunOffs ro = run_offs(a, w, 8);
 
     f4 acc[G];
 #pragma unroll
@@ -460,6 +464,9 @@ __device__ __forceinline__ void av_tile(const UArgs &a, int tile, char *smem) {
         for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[i][e] = 0.f;
+        // row-run offsets: formed per plane so that they hold no registers
+        // across the products
+        const RunOffs ro = run_offs(a, w, 8);
         for (int r0 = 0; r0 < 8; r0 += a.rows_round) {
             load_round(a, w, wave, r0, j, buf, a.attn, ro);
             stage_wait();
@@ -529,17 +536,6 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
         const int s1 = imin(2 * (x == 1 ? CH : CW), inverse_last(L.p[x], w.n[x], w.k[x]) - lo[x] + 1);
         vm[x] = s1 > s0 ? bit_range(s0, s1 - s0) : 0u;
     }
-    // LDS offsets (relative to the lane's first walk point) of the entry of
-    // this lane's key in the attention row of walk row h / column wc: the
-    // point's place in the box plus the key's offset in that query's window
-    int rowt[2 * CH], colt[2 * CW];
-#pragma unroll
-    for (int h = 0; h < 2 * CH; ++h)
-        rowt[h] = h * E[2] * a.KP +
-                  (L.p[1] - window_start(imin(lo[1] + h, w.n[1] - 1), w.n[1], w.k[1])) * a.kw;
-#pragma unroll
-    for (int h = 0; h < 2 * CW; ++h)
-        colt[h] = h * a.KP + L.p[2] - window_start(imin(lo[2] + h, w.n[2] - 1), w.n[2], w.k[2]);
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
     const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
 
@@ -547,7 +543,6 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
     const int rel1 = lo[1] - U[1], rel2 = lo[2] - U[2];
     const char *baseB = smem + rel1 * rb + rel2 * PS + c * 16;
     float *abuf = reinterpret_cast<float *>(smem);
-    const RunOffs aro = run_offs(a, w, E[2]);
 
     f4 acc[G];
 #pragma unroll
@@ -562,6 +557,20 @@ __device__ __forceinline__ void avi_tile(const UArgs &a, int tile, char *smem) {
         for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[i][e] = 0.f;
+        // Formed per plane so that they hold no registers across the products:
+        // the row-run offsets, and the LDS offsets (relative to the lane's
+        // first walk point) of the entry of this lane's key in the attention
+        // row of walk row h / column wc (the point's place in the box plus the
+        // key's offset in that query's window)
+        const RunOffs aro = run_offs(a, w, E[2]);
+        int rowt[2 * CH], colt[2 * CW];
+#pragma unroll
+        for (int h = 0; h < 2 * CH; ++h)
+            rowt[h] = h * E[2] * a.KP +
+                      (L.p[1] - window_start(imin(lo[1] + h, w.n[1] - 1), w.n[1], w.k[1])) * a.kw;
+#pragma unroll
+        for (int h = 0; h < 2 * CW; ++h)
+            colt[h] = h * a.KP + L.p[2] - window_start(imin(lo[2] + h, w.n[2] - 1), w.n[2], w.k[2]);
         // the box's attention entries of window plane it, a chunk of box rows
         // at a time: LDS element e = entry jj of box point pt = r * E2 + col
         for (int r0 = 0; r0 < E[1]; r0 += a.chunk_rows) {
