@@ -505,12 +505,15 @@ ALL_CHECKS = [
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 
-def failing_checks(orc):
-    """Names of the checks the given oracle build fails."""
+def failing_checks(orc, first_only=False):
+    """Names of the checks the given oracle build fails (cheapest checks first;
+    with first_only, stop at the first failure)."""
     bad = []
     for name, fn in ALL_CHECKS:
         try:
             fn(orc)
         except (AssertionError, IndexError, ValueError, FloatingPointError):
             bad.append(name)
+            if first_only:
+                break
     return bad
