@@ -157,7 +157,8 @@ constexpr int kFastLdsMax = 80 * 1024;
 struct FastPlan {
     na::fast::Geom g;
     int lds;
-    int c;        // walk length per axis the kernel is compiled for
+    int c;        // walk length the kernel is compiled for (along H; along W too when square)
+    int cw;       // walk length along W
     bool t3;      // more than one plane along T
     bool pad;     // dq, dk/dv: padded points, one staging per tensor serves both read patterns
     int walk_lo;  // dk/dv: the launch takes tiles whose inverse walk lies in (walk_lo, c]
@@ -173,6 +174,30 @@ bool fast_walk_compiled(int c, bool t3) { return c >= 2 && c <= (t3 ? 4 : 5); }
 constexpr int kBorderLdsMax = 160 * 1024;
 bool border_walk_compiled(int c, bool t3, int head_dim) {
     return !t3 && head_dim == 32 && (c == 6 || c == 7);
+}
+
+// dk/dv walks of ch x cw patches with ch != cw, for the border tiles that need
+// the longer walk along one axis only: single-plane grids (one workgroup per
+// CU, head_dim 32, fp32 and fp16) for windows of 7 and 9; grids with several
+// planes (fp32, head_dim 32) for a window of 5.
+bool rect_walk_compiled(int ch, int cw, bool t3, int head_dim, int dtype) {
+    if (head_dim != 32) return false;
+    if (!t3)
+        return (dtype == NA_F32 || dtype == NA_F16) &&
+               ((ch == 7 && cw == 5) || (ch == 5 && cw == 7) || (ch == 6 && cw == 4) ||
+                (ch == 4 && cw == 6));
+    return dtype == NA_F32 && ((ch == 4 && cw == 3) || (ch == 3 && cw == 4));
+}
+
+// Longest inverse walk (patches) along one axis (1: H, 2: W) of any 16-point
+// tile of any residue class.
+int max_axis_walk(const Prob &q, int a) {
+    int m = 0;
+    for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
+        const int n = na::class_size(q.ext[a], q.dil[a], r);
+        for (int f = 0; f < n; f += 16) m = std::max(m, na::tile_inverse_walk(f, 16, 2, n, q.ker[a]));
+    }
+    return m;
 }
 
 // Longest inverse walk (patches) of any 16 x 16 tile of any residue class.
@@ -206,6 +231,7 @@ bool border_of(const Prob &q, int done, na::Border *bd) {
     }
     const int R = (q.ext[1] + 15) / 16, C = (q.ext[2] + 15) / 16;
     bd->on = 1;
+    bd->cls = 0;
     bd->rows_lo = lo[1];
     bd->rows_hi = hi[1];
     bd->cols_lo = lo[2];
@@ -226,17 +252,22 @@ void set_divisors(na::fast::Geom &g) {
     g.f_band = na::make_fastdiv(band);
     g.f_lastband = na::make_fastdiv(last ? last : band);
     g.f_nres = na::make_fastdiv(g.nres);
-    g.f_c = na::make_fastdiv(g.tiles[2]);
+    const int cb = g.border.cols_lo + g.border.cols_hi;
+    g.f_c = na::make_fastdiv(!g.border.on || g.border.cls == 0 ? g.tiles[2]
+                             : (g.border.cls & 2)               ? std::max(1, cb)
+                                                                : std::max(1, g.tiles[2] - cb));
     g.f_cb = na::make_fastdiv(std::max(1, g.border.cols_lo + g.border.cols_hi));
     for (int a = 0; a < 3; ++a) g.f_dil[a] = na::make_fastdiv(g.dil[a]);
     g.f_dil21 = na::make_fastdiv(g.dil[2] * g.dil[1]);
 }
 
 // kind 0: forward / dq (walk c = the window walk, exact);
-// kind 1: dk/dv over the tiles whose inverse walk lies in (walk_lo, c].
+// kind 1: dk/dv over the tiles whose inverse walk lies in (walk_lo, c], or
+// with cw > 0 a walk of c patches along H and cw along W (border classes).
 // pad: points one 16-byte slot apart (see dq_tile), for grids with several
 // planes along T, whose plane boxes leave room for it.
-bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false) {
+bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false,
+               int cw = 0) {
     // fp32 with head_dim 16 or 32; bf16 / fp16 (converted to fp32 while staged)
     // with head_dim 32
     if (q.dtype == NA_F32) {
@@ -245,8 +276,15 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
         return false;
     }
     const bool t3 = q.ext[0] > 1;
-    const bool wide = kind == 1 && border_walk_compiled(c, t3, (int)q.head_dim);
-    if (!fast_walk_compiled(c, t3) && !wide) return false;
+    if (cw <= 0) cw = c;
+    bool wide;
+    if (cw == c) {
+        wide = kind == 1 && border_walk_compiled(c, t3, (int)q.head_dim);
+        if (!fast_walk_compiled(c, t3) && !wide) return false;
+    } else {
+        if (kind != 1 || !rect_walk_compiled(c, cw, t3, (int)q.head_dim, q.dtype)) return false;
+        wide = !t3;
+    }
     if (pad && !t3) return false;
     const int PB = (int)q.head_dim * 4 + (pad ? 16 : 0);
     // largest plane box per axis over the tiles this launch runs
@@ -259,8 +297,9 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
                 if (kind == 0) {
                     na::key_box(f, 16, 2, n, q.ker[a], &start, &extent);
                 } else {
-                    if (na::tile_inverse_walk(f, 16, 2, n, q.ker[a]) > c) continue;
-                    na::query_box(f, 16, 2, n, q.ker[a], c, &start, &extent);
+                    const int ca = a == 1 ? c : cw;
+                    if (na::tile_inverse_walk(f, 16, 2, n, q.ker[a]) > ca) continue;
+                    na::query_box(f, 16, 2, n, q.ker[a], ca, &start, &extent);
                 }
                 mx[a] = std::max(mx[a], extent);
             }
@@ -300,6 +339,7 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
     set_divisors(g);
     pl->lds = (int)lds;
     pl->c = c;
+    pl->cw = cw;
     pl->t3 = t3;
     pl->pad = pad;
     pl->walk_lo = walk_lo;
@@ -371,6 +411,25 @@ na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_
 
 template <typename T>
 na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
+    if (pl.cw != pl.c) {
+        // border classes with a longer walk along one axis (rect_walk_compiled)
+        if constexpr (!std::is_same<T, bf16>::value) {
+#define X(CH, CW)                                                                        \
+    if (a.g.head_dim == 32 && pl.c == CH && pl.cw == CW && !pl.t3)                       \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false>, pl, a, s);
+            X(7, 5) X(5, 7) X(6, 4) X(4, 6)
+#undef X
+        }
+        if constexpr (std::is_same<T, float>::value) {
+#define X(CH, CW)                                                                        \
+    if (a.g.head_dim == 32 && pl.c == CH && pl.cw == CW && pl.t3)                        \
+        return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, 32, CH, CW, true, true>, pl, a, s) \
+                      : launch_fast(na::fast::dkdv_kernel<T, 32, CH, CW, true, false>, pl, a, s);
+            X(4, 3) X(3, 4)
+#undef X
+        }
+        return NA_ERR_UNSUPPORTED;
+    }
     if constexpr (std::is_same<T, float>::value) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
@@ -448,6 +507,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
         fa.dv = static_cast<T *>(a.dv);
         fa.qscale = a.qscale;
         fa.scale = a.scale;
+        fa.edge = -1;  // dk/dv tiles by walk_lo (border classes set it per launch)
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
         if (phases & kPhaseDq) {
@@ -478,6 +538,44 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                 const na_status st = fast_dkdv<T>(pk, fa, s);
                 if (st != NA_OK) return st;
                 done = c;
+            }
+            // border tiles by class: a longer walk along H only, along W only,
+            // or along both (corners), each with the walk it needs, when all
+            // the classes that occur have a compiled kernel
+            if (done > 0 && done < need) {
+                const int hm = max_axis_walk(pr, 1), wm = max_axis_walk(pr, 2);
+                FastPlan cls[4];
+                bool use[4] = {false, false, false, false}, all = true;
+                for (int e = 1; e <= 3; ++e) {
+                    if (((e & 1) && hm <= done) || ((e & 2) && wm <= done)) continue;  // no such tile
+                    const int ch = (e & 1) ? hm : done, cw = (e & 2) ? wm : done;
+                    use[e] = fast_plan(pr, 1, ch, done, &cls[e], true, cw) ||
+                             fast_plan(pr, 1, ch, done, &cls[e], false, cw);
+                    all = all && use[e];
+                }
+                if (all) {
+                    for (int e = 1; e <= 3; ++e) {
+                        if (!use[e]) continue;
+                        fa.g = cls[e].g;
+                        fa.edge = e;
+                        fa.walk_c = done;
+                        na::Border &bd = fa.g.border;
+                        if (border_of(pr, done, &bd)) {
+                            // this class's tiles only, so every workgroup has work
+                            const int rb = bd.rows_lo + bd.rows_hi, cb = bd.cols_lo + bd.cols_hi;
+                            bd.cls = e;
+                            bd.per_plane = ((e & 1) ? rb : fa.g.tiles[1] - rb) *
+                                           ((e & 2) ? cb : fa.g.tiles[2] - cb);
+                            fa.g.n_tiles =
+                                (int)(pr.batch * pr.heads * fa.g.tiles[0] * bd.per_plane);
+                            set_divisors(fa.g);
+                        }
+                        const na_status st = fast_dkdv<T>(cls[e], fa, s);
+                        if (st != NA_OK) return st;
+                    }
+                    fa.edge = -1;
+                    done = need;
+                }
             }
             for (int cb = c + 1; done > 0 && done < need && cb <= need; ++cb) {
                 if (!fast_plan(pr, 1, cb, done, &pk, true) && !fast_plan(pr, 1, cb, done, &pk))

@@ -192,6 +192,9 @@ struct Border {
     int on;                          // the launch covers the border tiles only
     int rows_lo, rows_hi, cols_lo, cols_hi;
     int per_plane;                   // border tiles per (batch, head, T) plane
+    // 0: every tile of the frame; otherwise one class of it: rows from the
+    // bands (bit 0 set) or between them, columns likewise (bit 1)
+    int cls;
 };
 
 // Border tile i (0 .. per_plane - 1) of a plane of R x C tiles: (row, col).

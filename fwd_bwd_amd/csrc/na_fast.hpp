@@ -81,6 +81,10 @@ struct BwdArgsT {
     T *dq, *dk, *dv;
     float qscale, scale;
     int walk_lo;  // dk/dv: this launch takes the tiles whose inverse walk exceeds walk_lo
+    // dk/dv border classes (when edge >= 0, instead of walk_lo): the launch
+    // takes the tiles whose inverse walk along H exceeds walk_c exactly when
+    // bit 0 of edge is set, and along W exactly when bit 1 is set
+    int edge, walk_c;
 };
 using BwdArgs = BwdArgsT<float>;
 
@@ -106,7 +110,17 @@ __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
         int i = rem - q * g.border.per_plane;
         rem = q;
         const int rb = g.border.rows_lo + g.border.rows_hi;
-        if (i < rb * g.tiles[2]) {
+        const int cls = g.border.cls;
+        if (cls != 0) {
+            // one class: f_c divides by its number of columns
+            const int ncol = (cls & 2) ? g.border.cols_lo + g.border.cols_hi
+                                       : g.tiles[2] - g.border.cols_lo - g.border.cols_hi;
+            const int rr = fdiv(i, g.f_c), cc = i - rr * ncol;
+            th = !(cls & 1) ? g.border.rows_lo + rr
+                 : rr < g.border.rows_lo ? rr : g.tiles[1] - g.border.rows_hi + (rr - g.border.rows_lo);
+            tw = !(cls & 2) ? g.border.cols_lo + cc
+                 : cc < g.border.cols_lo ? cc : g.tiles[2] - g.border.cols_hi + (cc - g.border.cols_lo);
+        } else if (i < rb * g.tiles[2]) {
             const int rr = fdiv(i, g.f_c);
             tw = i - rr * g.tiles[2];
             th = rr < g.border.rows_lo ? rr : g.tiles[1] - g.border.rows_hi + (rr - g.border.rows_lo);
@@ -639,7 +653,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
-    {
+    if (a.edge >= 0) {
+        const int wh = tile_inverse_walk(w.o[1], kTH, 2, w.n[1], w.k[1]);
+        const int ww = tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]);
+        if ((wh > a.walk_c) != ((a.edge & 1) != 0) || (ww > a.walk_c) != ((a.edge & 2) != 0) ||
+            wh > CH || ww > CW)
+            return;
+    } else {
         const int tw = tile_walk(w);
         if (tw <= a.walk_lo || tw > (CH > CW ? CH : CW)) return;
     }

@@ -108,6 +108,11 @@ SMALL = [
     ((1, 5, 40, 36, 1, 32), (3, 7, 7), 1, torch.float32),
     ((1, 34, 35, 2, 16), (9, 9), 1, torch.float32),
     ((2, 33, 30, 1, 32), (7, 7), 1, torch.float32),
+    # border tiles by class next to interior tiles: a longer inverse walk along
+    # H only, along W only, and along both (corners), each its own launch
+    ((1, 64, 56, 1, 32), (9, 9), 1, torch.float32),
+    ((1, 64, 56, 1, 32), (9, 9), 1, torch.float16),
+    ((1, 4, 48, 40, 1, 32), (3, 5, 5), 1, torch.float32),
     # fp16 (binary16 storage, fp32 arithmetic): 2D, 3D, dilation, every head_dim
     ((1, 19, 23, 2, 32), (5, 7), 1, torch.float16),
     ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
