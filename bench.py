@@ -17,8 +17,8 @@ Effective FLOPs (the metric's convention): forward 4*N*heads*K*D, backward
 progress goes to stderr.
 
 Beside the headline step the same run times the KV-parallel backward variant
-on the same inputs ("kvparallel") and the headline shape with fp16 tensors
-("fp16").
+on the same inputs ("kvparallel"), the headline shape with fp16 tensors
+("fp16") and the two bf16 workloads ("bf16").
 
 The same function is also timed through the unfused ops (the script's method
 = 'unfused': window scores, softmax, weighted sum, and their backward AGRAD,
@@ -54,6 +54,10 @@ PEAK_HBM_GBS = 8000.0
 # without tile waste: fwd = QK^T + PV; dq = QK^T + dO V^T + dS K;
 # dk/dv = QK^T + dO V^T + P^T dO + dS^T Q
 KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+
+# the bf16 workloads (3D 2x8x128x128 with a 5x7x7 window; 2D 4x512x512, 13x13, dilation 2,
+# head_dim 64), timed beside the headline for their roofline fractions
+BF16_WORKLOADS = ("3d_b2_8x128x128_k5x7x7_h8_d32_bf16", "2d_b4_512x512_k13_d2_h4_d64_bf16")
 
 
 def log(*a):
@@ -334,7 +338,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path leg")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the KV-parallel backward and fp16 legs of the headline shape")
+                    help="skip the KV-parallel backward, fp16 and bf16 legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -449,6 +453,26 @@ def main():
         del h3
     if unfused:
         result["unfused"] = unfused
+    if not args.no_extra and args.workload == HEADLINE:
+        # the two bf16 workloads (fp32 accumulate): timed for their roofline fractions;
+        # the contractions run on fp32 MFMA after conversion, so the fp32 peak is the
+        # one they are measured against, and the bf16 MFMA fraction is given beside it
+        bf16 = {}
+        for name in BF16_WORKLOADS:
+            wb = WORKLOADS[name]
+            rb = Runner(wb, args.variant)
+            nb = min(args.steps, 5)
+            log(f"[bench] timing {wb.name}")
+            msb, _, perb = rb.time(nb, min(args.warmup, 2))
+            sb = summarize(wb, msb, perb)
+            f_fwd, f_bwd = flops(wb)
+            sb["bf16_mfma_frac_total"] = round((f_fwd + f_bwd) / msb / 1e9 /
+                                               PEAK_TFLOPS["bf16_mfma"], 5)
+            bf16[name] = {"steps": nb, **sb}
+            log(f"[bench] {wb.name}: {sb}")
+            del rb
+            torch.cuda.empty_cache()
+        result["bf16"] = bf16
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
