@@ -108,6 +108,7 @@ int max_union(const Prob &q, bool inverse, int (&mx)[3]) {
 
 // Target LDS bytes for one workgroup's staged chunk: two workgroups per CU.
 constexpr int kLdsTarget = 78 * 1024;
+constexpr int kLdsTargetWide = 156 * 1024;
 constexpr int kLdsMax = 160 * 1024;
 
 // Tiling of the class grids and the LDS plan of one kernel kind; false when
@@ -138,7 +139,8 @@ bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
     if (max_union(q, inverse, mx) > 32) return false;  // 32-bit validity masks
     const int64_t full = (int64_t)mx[0] * mx[1] * mx[2] * bytes_per_point;
     const int64_t plane = full / mx[g->chunk_axis];
-    int64_t lds = std::min<int64_t>(full, kLdsTarget);
+    // head_dim 64 kernels run one workgroup per CU (kSplitOccupancy): the CU's LDS
+    int64_t lds = std::min<int64_t>(full, q.head_dim >= 64 ? kLdsTargetWide : kLdsTarget);
     lds = std::max<int64_t>(lds, plane);
     lds = std::max<int64_t>(lds, merge_bytes);
     if (lds > kLdsMax) return false;

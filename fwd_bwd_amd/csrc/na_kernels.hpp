@@ -60,6 +60,13 @@ struct BwdArgs {
     int skip_ch, skip_cw;
 };
 
+// Workgroups per CU the split kernels are compiled for: at head_dim 64 the
+// per-lane rows and accumulators need more than the 256 registers of two
+// workgroups per CU, so one workgroup takes the CU's whole register file and
+// LDS (no scratch spills, boxes staged in one chunk).
+template <int D>
+constexpr int kSplitOccupancy = D >= 64 ? 1 : 2;
+
 // Element `i` of a 3-array chosen by value: a runtime index into a small
 // array would put the array in (slow, memory-backed) scratch.
 __device__ __forceinline__ int get3(const int (&a)[3], int i) {
@@ -231,7 +238,7 @@ __device__ __forceinline__ int chunk_mask(const ChunkView &cv, const Box &C, int
 // ============================================================================
 // Forward: out, lse.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -387,7 +394,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgs a) {
 // ============================================================================
 // Backward, query side: delta and dq.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -537,7 +544,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgs a) {
 // same pass also produces each query's dq contributions from this tile's keys
 // and adds them into the fp32 accumulator dq_acc.
 template <typename T, int D, bool KVPAR>
-__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dkdv_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
