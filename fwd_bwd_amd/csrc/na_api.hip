@@ -171,24 +171,27 @@ struct FastPlan {
 // across the plane loop there).
 bool fast_walk_compiled(int c, bool t3) { return c >= 2 && c <= (t3 ? 4 : 5); }
 
-// Border-only dk/dv kernels for longer walks, one workgroup per CU (single
-// plane grids, head_dim 32): the whole LDS and register file of a CU.
+// Border-only dk/dv kernels for longer walks, one workgroup per CU (head_dim
+// 32; walks 6 and 7 on single-plane grids, 6 with the padded layout on grids
+// with several planes): the whole LDS and register file of a CU.
 constexpr int kBorderLdsMax = 160 * 1024;
 bool border_walk_compiled(int c, bool t3, int head_dim) {
-    return !t3 && head_dim == 32 && (c == 6 || c == 7);
+    return head_dim == 32 && (t3 ? c == 6 : (c == 6 || c == 7));
 }
 
 // dk/dv walks of ch x cw patches with ch != cw, for the border tiles that need
 // the longer walk along one axis only: single-plane grids (one workgroup per
 // CU, head_dim 32, fp32 and fp16) for windows of 7 and 9; grids with several
-// planes (fp32, head_dim 32) for a window of 5.
+// planes (head_dim 32) for a window of 5 (fp32, two workgroups per CU) and of
+// 7 (every type, one workgroup per CU, padded layout).
 bool rect_walk_compiled(int ch, int cw, bool t3, int head_dim, int dtype) {
     if (head_dim != 32) return false;
     if (!t3)
         return (dtype == NA_F32 || dtype == NA_F16) &&
                ((ch == 7 && cw == 5) || (ch == 5 && cw == 7) || (ch == 6 && cw == 4) ||
                 (ch == 4 && cw == 6));
-    return dtype == NA_F32 && ((ch == 4 && cw == 3) || (ch == 3 && cw == 4));
+    return (dtype == NA_F32 && ((ch == 4 && cw == 3) || (ch == 3 && cw == 4))) ||
+           (ch == 6 && cw == 4) || (ch == 4 && cw == 6);
 }
 
 // Longest inverse walk (patches) along one axis (1: H, 2: W) of any 16-point
@@ -285,9 +288,10 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
         if (!fast_walk_compiled(c, t3) && !wide) return false;
     } else {
         if (kind != 1 || !rect_walk_compiled(c, cw, t3, (int)q.head_dim, q.dtype)) return false;
-        wide = !t3;
+        wide = !t3 || std::max(c, cw) > 4;
     }
     if (pad && !t3) return false;
+    if (wide && t3 && !pad) return false;  // the border kernels of such grids are padded
     const int PB = (int)q.head_dim * 4 + (pad ? 16 : 0);
     // largest plane box per axis over the tiles this launch runs
     int mx[3] = {1, 1, 1};
@@ -418,10 +422,15 @@ na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStrea
         if constexpr (!std::is_same<T, bf16>::value) {
 #define X(CH, CW)                                                                        \
     if (a.g.head_dim == 32 && pl.c == CH && pl.cw == CW && !pl.t3)                       \
-        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false>, pl, a, s);
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false, false>, pl, a, s);
             X(7, 5) X(5, 7) X(6, 4) X(4, 6)
 #undef X
         }
+#define X(CH, CW)                                                                        \
+    if (a.g.head_dim == 32 && pl.c == CH && pl.cw == CW && pl.t3 && pl.pad)              \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true>, pl, a, s);
+        X(6, 4) X(4, 6)
+#undef X
         if constexpr (std::is_same<T, float>::value) {
 #define X(CH, CW)                                                                        \
     if (a.g.head_dim == 32 && pl.c == CH && pl.cw == CW && pl.t3)                        \
@@ -449,9 +458,11 @@ na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStrea
     }
 #define X(D, C)                                                                          \
     if (a.g.head_dim == D && pl.c == C && !pl.t3)                                        \
-        return launch_fast(na::fast::dkdv_border_kernel<T, D, C, C, false>, pl, a, s);
+        return launch_fast(na::fast::dkdv_border_kernel<T, D, C, C, false, false>, pl, a, s);
     X(32, 6) X(32, 7)
 #undef X
+    if (a.g.head_dim == 32 && pl.c == 6 && pl.t3 && pl.pad)
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, 6, 6, true, true>, pl, a, s);
     return NA_ERR_UNSUPPORTED;
 }
 

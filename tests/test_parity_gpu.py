@@ -113,6 +113,10 @@ SMALL = [
     ((1, 64, 56, 1, 32), (9, 9), 1, torch.float32),
     ((1, 64, 56, 1, 32), (9, 9), 1, torch.float16),
     ((1, 4, 48, 40, 1, 32), (3, 5, 5), 1, torch.float32),
+    # the same on grids with several planes and a 7-wide window (walk 6 at the
+    # border, one workgroup per CU)
+    ((1, 3, 64, 56, 1, 32), (3, 7, 7), 1, torch.float32),
+    ((1, 3, 64, 56, 1, 32), (3, 7, 7), 1, torch.bfloat16),
     # fp16 (binary16 storage, fp32 arithmetic): 2D, 3D, dilation, every head_dim
     ((1, 19, 23, 2, 32), (5, 7), 1, torch.float16),
     ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
