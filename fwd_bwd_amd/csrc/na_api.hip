@@ -271,8 +271,10 @@ void set_divisors(na::fast::Geom &g) {
 // with cw > 0 a walk of c patches along H and cw along W (border classes).
 // pad: points one 16-byte slot apart (see dq_tile), for grids with several
 // planes along T, whose plane boxes leave room for it.
+// edge >= 0: the box only over the tiles of that border class (inverse walk
+// along H above walk_lo exactly when bit 0 is set, along W when bit 1 is).
 bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false,
-               int cw = 0) {
+               int cw = 0, int edge = -1) {
     // fp32 with head_dim 16 or 32; bf16 / fp16 (converted to fp32 while staged)
     // with head_dim 32
     if (q.dtype == NA_F32) {
@@ -304,7 +306,9 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
                     na::key_box(f, 16, 2, n, q.ker[a], &start, &extent);
                 } else {
                     const int ca = a == 1 ? c : cw;
-                    if (na::tile_inverse_walk(f, 16, 2, n, q.ker[a]) > ca) continue;
+                    const int wt = na::tile_inverse_walk(f, 16, 2, n, q.ker[a]);
+                    if (wt > ca) continue;
+                    if (edge >= 0 && (wt > walk_lo) != (((edge >> (a - 1)) & 1) != 0)) continue;
                     na::query_box(f, 16, 2, n, q.ker[a], ca, &start, &extent);
                 }
                 mx[a] = std::max(mx[a], extent);
@@ -562,8 +566,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                 for (int e = 1; e <= 3; ++e) {
                     if (((e & 1) && hm <= done) || ((e & 2) && wm <= done)) continue;  // no such tile
                     const int ch = (e & 1) ? hm : done, cw = (e & 2) ? wm : done;
-                    use[e] = fast_plan(pr, 1, ch, done, &cls[e], true, cw) ||
-                             fast_plan(pr, 1, ch, done, &cls[e], false, cw);
+                    use[e] = fast_plan(pr, 1, ch, done, &cls[e], true, cw, e) ||
+                             fast_plan(pr, 1, ch, done, &cls[e], false, cw, e);
                     all = all && use[e];
                 }
                 if (all) {
