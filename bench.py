@@ -312,11 +312,18 @@ def cpu_baseline(w, host, target_s, seed=1):
         oracle.na_bwd(q, k, v, dout, w.kernel, w.dilation, w.the_scale, sel=sel)
         return time.perf_counter() - t0
 
-    pilot_n = 256
+    # a warm-up call (thread team start-up), then a pilot long enough to time,
+    # sizes the sample to about target_s of work; one resize if it came out short
+    run(256)
+    pilot_n = 8192
     t_pilot = run(pilot_n)
     n = int(max(pilot_n, min(units, pilot_n * target_s / max(t_pilot, 1e-6))))
     log(f"[bench] oracle pilot {pilot_n} units {t_pilot:.2f}s -> sample {n} units")
     t = run(n)
+    if t < 0.5 * target_s and n < units:
+        n = int(min(units, n * target_s / max(t, 1e-6)))
+        log(f"[bench] oracle sample short ({t:.1f}s) -> {n} units")
+        t = run(n)
     f_fwd, f_bwd = flops(w)
     full_s = t * units / n
     return {"value": round((f_fwd + f_bwd) / full_s / 1e12, 6), "unit": "TFLOP/s",
