@@ -145,6 +145,7 @@ bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
     lds = std::max<int64_t>(lds, merge_bytes);
     if (lds > kLdsMax) return false;
     g->lds_budget = (int)lds;
+    g->dq_lds_off = 0;
     *lds_bytes = (int)lds;
     return true;
 }
@@ -631,6 +632,19 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
     hipLaunchKernelGGL(na::zero_kernel, flat_grid(n4), dim3(kThreads), 0, s, a.dq_acc, n4);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+    // dq contributions summed per workgroup in LDS over its query box when the
+    // largest box fits beside the staging (one global atomic per box point and
+    // channel instead of one per key block, query and channel)
+    {
+        int mx[3];
+        max_union(pr, true, mx);
+        const int64_t acc = (int64_t)mx[0] * mx[1] * mx[2] * (D + 1) * 4;
+        const int off = (lds_k + 15) & ~15;
+        if (off + acc <= kLdsMax) {
+            ak.g.dq_lds_off = off;
+            lds_k = (int)(off + acc);
+        }
+    }
     auto kern = na::dkdv_kernel<T, D, true>;
     if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             lds_k) != hipSuccess)

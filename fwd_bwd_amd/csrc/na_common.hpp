@@ -221,6 +221,7 @@ struct Geometry {
     int chunk_axis;   // axis along which a staged box is split when it exceeds the budget
     int lds_budget;   // bytes of LDS a staged chunk may use
     Border border;    // when on: the 8 x 8 tiles of the border 16 x 16 tiles only
+    int dq_lds_off;   // KV-parallel dk/dv: byte offset of the LDS dq accumulator (0: none)
 };
 
 // Where a workgroup works: batch element, head, residue class, tile origin,

@@ -543,8 +543,10 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
 // Backward, key side: dk and dv by inverse-neighborhood gather. With KVPAR the
 // same pass also produces each query's dq contributions from this tile's keys
 // and adds them into the fp32 accumulator dq_acc.
+// The KV-parallel pass keeps the block's keys for dq besides everything else
+// and, with its LDS dq accumulator, runs one workgroup per CU anyway.
 template <typename T, int D, bool KVPAR>
-__global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
@@ -597,6 +599,18 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dkdv_kernel(BwdA
     for (int g = 0; g < G; ++g) {
         dk[g] = f4{0.f, 0.f, 0.f, 0.f};
         dv[g] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    // KV-parallel with an LDS accumulator: the tile's dq contributions are
+    // summed over its query box U in LDS (points D + 1 floats apart), then
+    // added to the global accumulator once per point and channel. Zeroed here;
+    // the barrier of the first staging orders it before any addition.
+    float *qacc = nullptr;
+    if constexpr (KVPAR) {
+        if (a.g.dq_lds_off > 0) {
+            qacc = reinterpret_cast<float *>(smem + a.g.dq_lds_off);
+            const int n = U.e[0] * U.e[1] * U.e[2] * (D + 1);
+            for (int i = threadIdx.x; i < n; i += kThreads) qacc[i] = 0.f;
+        }
     }
 
     ChunkView cv;
@@ -704,13 +718,37 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dkdv_kernel(BwdA
                                    lo[2] + 2 * it.c2 + (c & 1)};
                 const bool inside = qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2] &&
                                     ((cm >> c) & 1);
-                if (inside) {
+                if (inside && qacc) {
+                    float *ap = qacc + (((qq[0] - U.o[0]) * U.e[1] + (qq[1] - U.o[1])) * U.e[2] +
+                                        (qq[2] - U.o[2])) * (D + 1);
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+                        for (int g = 0; g < G; ++g) atomicAdd(ap + i2 * G + g, dq[g][i2]);
+                } else if (inside) {
                     float *accp = a.dq_acc + elem_off(w, qq);
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2)
 #pragma unroll
                         for (int g = 0; g < G; ++g) atomicAdd(accp + i2 * G + g, dq[g][i2]);
                 }
+            }
+        }
+    }
+
+    if constexpr (KVPAR) {
+        if (qacc) {
+            // the box's sums into the global accumulator (points past the grid
+            // never received any)
+            __syncthreads();
+            const int plane = U.e[1] * U.e[2], n = U.e[0] * plane * D;
+            for (int i = threadIdx.x; i < n; i += kThreads) {
+                const int pt = i / D, d = i - pt * D;
+                const int z = pt / plane, r = pt - z * plane, y = r / U.e[2], x = r - y * U.e[2];
+                const int qq[3] = {U.o[0] + z, U.o[1] + y, U.o[2] + x};
+                const float v = qacc[pt * (D + 1) + d];
+                if (qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2] && v != 0.f)
+                    atomicAdd(a.dq_acc + elem_off(w, qq) + d, v);
             }
         }
     }
