@@ -117,6 +117,12 @@ SMALL = [
     # border, one workgroup per CU)
     ((1, 3, 64, 56, 1, 32), (3, 7, 7), 1, torch.float32),
     ((1, 3, 64, 56, 1, 32), (3, 7, 7), 1, torch.bfloat16),
+    # degenerate shapes: a 3D grid of one plane (k_t = 1), a window spanning the
+    # whole extent along one axis only, a dilation that leaves every residue
+    # class exactly one window long
+    ((1, 1, 40, 37, 2, 32), (1, 9, 9), 1, torch.float32),
+    ((1, 9, 30, 1, 32), (9, 5), 1, torch.float32),
+    ((1, 18, 18, 1, 16), (3, 3), 6, torch.float32),
     # fp16 (binary16 storage, fp32 arithmetic): 2D, 3D, dilation, every head_dim
     ((1, 19, 23, 2, 32), (5, 7), 1, torch.float16),
     ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
