@@ -56,3 +56,14 @@ def test_traffic_only_reported_for_current_sources(tmp_path, monkeypatch):
     (tmp_path / "traffic_k_w.md").write_text(
         "source_sha256: " + bench.kernel_source_hash() + "\nhbm_bytes_per_launch: 5e9\n")
     assert bench.recorded_traffic("k", "w") == 5e9
+
+
+def test_bench_side_workloads_exist():
+    """The workloads the bench times beside the headline are defined, with
+    the types their legs assume."""
+    import torch
+    for name in bench.BF16_WORKLOADS:
+        assert name in WORKLOADS and WORKLOADS[name].dtype == torch.bfloat16, name
+    assert WORKLOADS[bench.HEADLINE].dtype == torch.float32
+    assert WORKLOADS[bench.HEADLINE_3D].dtype == torch.float32
+    assert bench.HEADLINE.replace("_f32", "_f16") in WORKLOADS
