@@ -16,6 +16,13 @@ Effective FLOPs (the metric's convention): forward 4*N*heads*K*D, backward
 2.5x that, with N tokens and K = prod(kernel). Prints one JSON line on stdout;
 progress goes to stderr.
 
+Timing protocol: before each pass (forward; backward) a 1 GiB buffer is
+overwritten, which evicts the inputs from the L2 caches and the 256 MB
+Infinity Cache, so every pass starts cold as it would inside a model; the
+flush itself is outside the timed events. Per pass the median, minimum and
+mean over the timed steps are reported; the headline value uses the medians.
+The same steps without the flush are reported beside it ("warm").
+
 Beside the headline step the same run times the KV-parallel backward variant
 on the same inputs ("kvparallel"), the headline shape with fp16 tensors
 ("fp16") and the two bf16 workloads ("bf16").
@@ -49,6 +56,20 @@ from fwd_bwd_amd.inputs import HEADLINE, HEADLINE_3D, WORKLOADS, make_inputs  # 
 METRIC = "NA fwd+bwd ms & TFLOP/s (% roofline): 2D 1024² k9×9, 3D 16×256² k3×5×5"
 PEAK_TFLOPS = {"fp32_mfma": 157.3, "bf16_mfma": 2516.6}
 PEAK_HBM_GBS = 8000.0
+DTYPE_LABEL = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+FLUSH_BYTES = 1 << 30
+
+
+def mfma_peak(dtype):
+    """Dense MFMA peak (TFLOP/s) of the workload's arithmetic type: fp32 for
+    fp32 tensors; the 16-bit MFMA rate (bf16 and fp16 alike) for 16-bit ones."""
+    return PEAK_TFLOPS["fp32_mfma"] if dtype == torch.float32 else PEAK_TFLOPS["bf16_mfma"]
+
+
+def stats(xs):
+    xs = [float(x) for x in xs]
+    return {"median": round(float(np.median(xs)), 4), "min": round(min(xs), 4),
+            "mean": round(float(np.mean(xs)), 4)}
 
 # contraction FLOPs each kernel performs per (query or key) x window entry x channel,
 # without tile waste: fwd = QK^T + PV; dq = QK^T + dO V^T + dS K;
@@ -150,30 +171,32 @@ class Runner:
             return [("fwd", self.fwd), ("bwd_dq", self.bwd_dq), ("bwd_dkdv", self.bwd_dkdv)]
         return [("fwd", self.fwd), ("bwd_kvparallel", self.bwd_kvpar)]
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, flush=None):
+        """Per-phase kernel durations (ms lists over `steps`) and the wall time
+        per step. With a flush buffer, it is overwritten before the forward
+        and before the backward pass (outside the timed events)."""
         ph = self.phases()
         for _ in range(warmup):
             for _, f in ph:
                 f()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ph) + 1)]
-              for _ in range(steps)]
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+        n = len(ph)
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        start.record()
         for s in range(steps):
-            ev[s][0].record()
-            for i, (_, f) in enumerate(ph):
+            for i, (name, f) in enumerate(ph):
+                if flush is not None and (name == "fwd" or i == 1):
+                    flush.fill_((s + i) & 0xff)
+                ev[s][i][0].record()
                 f()
-                ev[s][i + 1].record()
-        end.record()
+                ev[s][i][1].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
-        per = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+        per = {name: [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]
                for i, (name, _) in enumerate(ph)}
-        return start.elapsed_time(end) / steps, wall, per
+        return per, wall
 
 
 # ----------------------------------------------------------------------------- unfused leg
@@ -268,35 +291,75 @@ def unfused_summary(w, step, per):
                          "avg_launch_ms": round(per[name], 4)}}
 
 
-def summarize(w, ms_step, per):
+def summarize(w, per):
+    """Times, effective TFLOP/s and roofline fractions of one workload from
+    per-phase duration lists; fractions against the MFMA peak of the
+    workload's arithmetic type and against HBM."""
     f_fwd, f_bwd = flops(w)
-    b_fwd, b_bwd, b_kern = algorithmic_bytes(w)
-    fwd_ms = per["fwd"]
-    bwd_ms = sum(v for k, v in per.items() if k != "fwd")
-    peak = PEAK_TFLOPS["fp32_mfma"]   # every contraction runs on fp32 MFMA
+    b_fwd, b_bwd, _ = algorithmic_bytes(w)
+    steps = len(per["fwd"])
+    bwd = [sum(per[k][s] for k in per if k != "fwd") for s in range(steps)]
+    step = [per["fwd"][s] + bwd[s] for s in range(steps)]
+    fwd_ms = float(np.median(per["fwd"]))
+    bwd_ms = float(np.median(bwd))
+    ms_step = float(np.median(step))
+    peak = mfma_peak(w.dtype)
     return {
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(ms_step, 4),
+        "fwd_ms_stats": stats(per["fwd"]), "bwd_ms_stats": stats(bwd), "step_ms_stats": stats(step),
         "tflops_fwd": round(f_fwd / fwd_ms / 1e9, 3), "tflops_bwd": round(f_bwd / bwd_ms / 1e9, 3),
         "tflops_total": round((f_fwd + f_bwd) / ms_step / 1e9, 3),
-        "mfma_frac_fwd": round(f_fwd / fwd_ms / 1e9 / peak, 4),
-        "mfma_frac_bwd": round(f_bwd / bwd_ms / 1e9 / peak, 4),
-        "mfma_frac_total": round((f_fwd + f_bwd) / ms_step / 1e9 / peak, 4),
+        "mfma_peak_tflops": peak,
+        "mfma_frac_fwd": round(f_fwd / fwd_ms / 1e9 / peak, 5),
+        "mfma_frac_bwd": round(f_bwd / bwd_ms / 1e9 / peak, 5),
+        "mfma_frac_total": round((f_fwd + f_bwd) / ms_step / 1e9 / peak, 5),
         "hbm_frac_fwd": round(b_fwd / fwd_ms / 1e6 / PEAK_HBM_GBS, 4),
         "hbm_frac_bwd": round(b_bwd / bwd_ms / 1e6 / PEAK_HBM_GBS, 4),
-        "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "hbm_frac_total": round((b_fwd + b_bwd) / ms_step / 1e6 / PEAK_HBM_GBS, 4),
+        "roofline_ms": round(max((f_fwd + f_bwd) / peak / 1e9,
+                                 (b_fwd + b_bwd) / PEAK_HBM_GBS / 1e6), 4),
+        "kernel_ms": {k: stats(v) for k, v in per.items()},
     }
 
 
 def roofline(w, per):
-    name = max((k for k in per if k in KERNEL_FLOP_UNITS), key=lambda k: per[k])
+    """Roofline entry of the longest kernel (by median duration): its
+    contraction FLOPs and algorithmic bytes per launch; bound by whichever of
+    the MFMA peak of the workload's type and HBM its intensity puts it under."""
+    med = {k: float(np.median(v)) for k, v in per.items() if k in KERNEL_FLOP_UNITS}
+    name = max(med, key=med.get)
     base = w.tokens * w.heads * w.window * w.head_dim
     fl = KERNEL_FLOP_UNITS[name] * base
-    achieved = fl / (per[name] * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["fp32_mfma"]
-    return {"bound": "mfma", "kernel": name, "achieved": round(achieved, 3), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": recorded_traffic(name, w.name),
-            "flops_per_launch": fl, "avg_launch_ms": round(per[name], 4)}
+    by = algorithmic_bytes(w)[2][name]
+    peak = mfma_peak(w.dtype)
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    t = med[name] * 1e-3
+    out = {"kernel": name, "flops_per_launch": fl, "bytes_per_launch": by,
+           "intensity_flop_per_byte": round(fl / by, 2), "ridge_flop_per_byte": round(ridge, 2),
+           "avg_launch_ms": round(med[name], 4), "dtype": DTYPE_LABEL[w.dtype]}
+    if fl / by >= ridge:
+        achieved = fl / t / 1e12
+        out.update({"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4)})
+    else:
+        achieved = by / t / 1e9
+        out.update({"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)})
+    out["traffic"] = recorded_traffic(name, w.name)
+    return out
+
+
+def leg(w, per, wall=None, warm=None):
+    """Summary of one timed workload: cold (flushed) medians, the roofline of
+    its longest kernel, and the warm medians beside them."""
+    out = summarize(w, per)
+    out["roofline"] = roofline(w, per)
+    if wall is not None:
+        out["wall_ms_per_step"] = round(wall, 4)
+    if warm is not None:
+        ws = summarize(w, warm)
+        out["warm"] = {k: ws[k] for k in ("fwd_ms", "bwd_ms", "ms_per_step", "tflops_total")}
+    return out
 
 
 def cpu_baseline(w, host, target_s, seed=1):
@@ -334,6 +397,33 @@ def cpu_baseline(w, host, target_s, seed=1):
             "est_full_ms": round(full_s * 1e3, 1)}
 
 
+def host_info():
+    """Where the numbers were taken: host CPU, GPU, ROCm and the library build."""
+    model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    from fwd_bwd_amd import build as hipbuild
+    lib_sha = na.source_sha256()
+    return {"cpu_count": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "cpu_model": model, "gpu": torch.cuda.get_device_name(0),
+            "gpu_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+            "rocm": rocm, "torch_hip": torch.version.hip, "torch": torch.__version__,
+            "libna_source_sha256": lib_sha,
+            "libna_matches_tree": lib_sha == hipbuild.source_sha256()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +436,8 @@ def main():
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path leg")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the KV-parallel backward, fp16 and bf16 legs")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time warm passes only (no cache flush between passes)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -374,33 +466,43 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 3}))
         return
 
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8,
+                                                   device="cuda:0")
+
+    def timed(wl, variant, steps, warmup):
+        r = Runner(wl, variant)
+        log(f"[bench] timing {wl.name} ({variant}): warmup {warmup}, steps {steps}")
+        per, wall = r.time(steps, warmup, flush)
+        warm = None
+        if flush is not None:
+            warm, _ = r.time(steps, 0, None)
+        out = leg(wl, per, wall, warm)
+        log(f"[bench] {wl.name} ({variant}): step {out['ms_per_step']} ms, "
+            f"fwd {out['fwd_ms']} ms, bwd {out['bwd_ms']} ms, {out['tflops_total']} TFLOP/s")
+        return r, out
+
     w = WORKLOADS[args.workload]
-    r = Runner(w, args.variant)
-    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, wall, per = r.time(args.steps, args.warmup)
-    main_sum = summarize(w, ms, per)
-    log(f"[bench] {w.name}: {main_sum}")
-    f_fwd, f_bwd = flops(w)
+    r, main_leg = timed(w, args.variant, args.steps, args.warmup)
 
     result = {
         "metric": METRIC,
-        "value": main_sum["tflops_total"],
+        "value": main_leg["tflops_total"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_sum["ms_per_step"],
+        "ms_per_step": main_leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+        "dtype": DTYPE_LABEL[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "grid": list(w.grid),
                    "heads": w.heads, "head_dim": w.head_dim, "kernel": list(w.kernel),
-                   "dilation": list(w.dilation), "backward": args.variant},
-        "wall_ms_per_step": round(wall, 4),
-        **{k: v for k, v in main_sum.items() if k != "ms_per_step"},
-        "roofline": roofline(w, per),
+                   "dilation": list(w.dilation), "backward": args.variant,
+                   "timing": "median of cold passes (1 GiB flush before each pass)"
+                   if flush is not None else "median of warm passes"},
+        **{k: v for k, v in main_leg.items() if k != "ms_per_step"},
     }
 
     host = r.host
@@ -422,61 +524,42 @@ def main():
 
     run_unfused(w, host)
     if not args.no_extra and args.workload == HEADLINE:
-        # the KV-parallel backward (atomic dq accumulation) on the same inputs, and the
-        # same shape with fp16 tensors (the maintainer's second profiled precision)
+        # the KV-parallel backward on the same inputs, and the same shape with fp16
+        # tensors (the maintainer's second profiled precision)
         extra = {}
         if args.variant == "gather":
-            # atomic dq accumulation makes it ~50x slower than the gather: two steps suffice
-            rk = Runner(w, "kvparallel")
-            log(f"[bench] timing {w.name} with the KV-parallel backward")
-            msk, _, perk = rk.time(min(args.steps, 2), min(args.warmup, 1))
-            extra["kvparallel"] = {"steps": min(args.steps, 2), **summarize(w, msk, perk)}
-            log(f"[bench] kvparallel {w.name}: {extra['kvparallel']}")
+            nk = min(args.steps, 2)
+            rk, extra["kvparallel"] = timed(w, "kvparallel", nk, min(args.warmup, 1))
+            extra["kvparallel"]["steps"] = nk
             del rk
             torch.cuda.empty_cache()
         w16 = WORKLOADS.get(w.name.replace("_f32", "_f16"))
         if w16 is not None:
-            r16 = Runner(w16, args.variant)
-            log(f"[bench] timing {w16.name}")
-            ms16, _, per16 = r16.time(args.steps, args.warmup)
-            extra["fp16"] = {"workload": w16.name, **summarize(w16, ms16, per16)}
-            log(f"[bench] {w16.name}: {extra['fp16']}")
+            r16, s16 = timed(w16, args.variant, args.steps, args.warmup)
+            extra["fp16"] = {"workload": w16.name, **s16}
             del r16
             torch.cuda.empty_cache()
         result.update(extra)
+    h3 = None
     if not args.no_secondary and args.workload == HEADLINE:
         w3 = WORKLOADS[HEADLINE_3D]
-        r3 = Runner(w3, args.variant)
-        log(f"[bench] timing {w3.name}")
-        ms3, _, per3 = r3.time(args.steps, args.warmup)
-        s3 = summarize(w3, ms3, per3)
-        s3["roofline"] = roofline(w3, per3)
+        r3, s3 = timed(w3, args.variant, args.steps, args.warmup)
         result["secondary"] = {"workload": w3.name, **s3}
-        log(f"[bench] {w3.name}: {s3}")
         h3 = r3.host
         del r3
         torch.cuda.empty_cache()
         run_unfused(w3, h3)
-        del h3
     if unfused:
         result["unfused"] = unfused
     if not args.no_extra and args.workload == HEADLINE:
-        # the two bf16 workloads (fp32 accumulate): timed for their roofline fractions;
-        # the contractions run on fp32 MFMA after conversion, so the fp32 peak is the
-        # one they are measured against, and the bf16 MFMA fraction is given beside it
+        # the two bf16 workloads (fp32 accumulate), each against the roofline of its
+        # own type: 16-bit MFMA or HBM, whichever its arithmetic intensity binds
         bf16 = {}
         for name in BF16_WORKLOADS:
             wb = WORKLOADS[name]
-            rb = Runner(wb, args.variant)
             nb = min(args.steps, 5)
-            log(f"[bench] timing {wb.name}")
-            msb, _, perb = rb.time(nb, min(args.warmup, 2))
-            sb = summarize(wb, msb, perb)
-            f_fwd, f_bwd = flops(wb)
-            sb["bf16_mfma_frac_total"] = round((f_fwd + f_bwd) / msb / 1e9 /
-                                               PEAK_TFLOPS["bf16_mfma"], 5)
+            rb, sb = timed(wb, args.variant, nb, min(args.warmup, 2))
             bf16[name] = {"steps": nb, **sb}
-            log(f"[bench] {wb.name}: {sb}")
             del rb
             torch.cuda.empty_cache()
         result["bf16"] = bf16
@@ -484,12 +567,13 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+        if h3 is not None:
+            result["secondary"]["cpu_baseline"] = cpu_baseline(WORKLOADS[HEADLINE_3D], h3,
+                                                               args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
 
-    result["host"] = {"cpu_count": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
-                      "processor": platform.processor(),
-                      "gpu": torch.cuda.get_device_name(0)}
+    result["host"] = host_info()
     print(json.dumps(result), flush=True)
 
 

@@ -1,6 +1,7 @@
 """Build libna.so (the HIP kernels and the C ABI of include/na.h) for gfx950, in-tree."""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 
@@ -27,11 +28,31 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_files():
+    """Every file libna.so is built from: the kernel and ABI sources and the
+    public header, sorted by name."""
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp"))]
+    files.append(os.path.join(ROOT, "include", "na.h"))
+    return sorted(files, key=os.path.basename)
+
+
+def source_sha256() -> str:
+    """sha256 over (name, contents) of source_files(); the build embeds it in
+    the library (na_source_sha256), so a loaded library can be matched with
+    the tree it came from."""
+    h = hashlib.sha256()
+    for path in source_files():
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source to an object (in parallel), then link libna.so."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     os.makedirs(OBJDIR, exist_ok=True)
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           f'-DNA_SOURCE_SHA256="{source_sha256()}"']
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(OBJDIR, os.path.splitext(os.path.basename(src))[0] + ".o")

@@ -8,10 +8,11 @@
 #include <cstdint>
 #include <initializer_list>
 #include <type_traits>
-#include <vector>
+#include <mutex>
 
 #include "na.h"
 #include "na_fast.hpp"
+#include "na_host.hpp"
 #include "na_kernels.hpp"
 
 namespace {
@@ -20,6 +21,10 @@ using na::bf16;
 using na::f16;
 
 constexpr int kThreads = 256;  // elementwise kernels
+
+#ifndef NA_SOURCE_SHA256
+#define NA_SOURCE_SHA256 "unknown"
+#endif
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -32,6 +37,8 @@ struct Prob {
     na_dtype dtype;
     float scale;
 };
+
+int max_union(const Prob &q, bool inverse, int (&mx)[3]);
 
 na_status validate(const na_problem *p, Prob *out) {
     if (!p) return NA_ERR_INVALID_ARG;
@@ -73,6 +80,13 @@ na_status validate(const na_problem *p, Prob *out) {
     q.rows = p->batch * tokens * p->heads;
     q.dtype = (na_dtype)p->dtype;
     q.scale = (float)p->scale;
+    // the kernels keep per-axis validity masks of 32 bits over a patch walk.
+    // The forward walk along an axis spans k + 1 or k + 2 points; the inverse
+    // walk of a key near a border is longer (up to 2k points on short axes).
+    // Windows up to 16 fit every extent, 17 to 21 all but a few class extents
+    // between 33 and 42, and from 22 on only class extents below 33.
+    int mx[3];
+    if (max_union(q, false, mx) > 32 || max_union(q, true, mx) > 32) return NA_ERR_UNSUPPORTED;
     if (out) *out = q;
     return NA_OK;
 }
@@ -228,12 +242,11 @@ bool border_of(const Prob &q, int done, na::Border *bd) {
     int lo[3] = {0, 0, 0}, hi[3] = {0, 0, 0};
     for (int a = 1; a < 3; ++a) {
         const int n = q.ext[a], T = (n + 15) / 16;
-        std::vector<int> big(T);
-        for (int t = 0; t < T; ++t) big[t] = na::tile_inverse_walk(16 * t, 16, 2, n, q.ker[a]) > done;
-        while (lo[a] < T && big[lo[a]]) ++lo[a];
-        while (hi[a] < T - lo[a] && big[T - 1 - hi[a]]) ++hi[a];
+        auto big = [&](int t) { return na::tile_inverse_walk(16 * t, 16, 2, n, q.ker[a]) > done; };
+        while (lo[a] < T && big(lo[a])) ++lo[a];
+        while (hi[a] < T - lo[a] && big(T - 1 - hi[a])) ++hi[a];
         for (int t = lo[a]; t < T - hi[a]; ++t)
-            if (big[t]) return false;
+            if (big(t)) return false;
     }
     const int R = (q.ext[1] + 15) / 16, C = (q.ext[2] + 15) / 16;
     bd->on = 1;
@@ -367,9 +380,7 @@ bool fast_plan_fwd(const Prob &q, FastPlan *pl, bool try_pad = false) {
 
 template <typename Kern, typename Args>
 na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t s) {
-    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            pl.lds) != hipSuccess)
-        return NA_ERR_HIP;
+    if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
     if (a.g.n_tiles == 0) return NA_OK;
     hipLaunchKernelGGL(kern, dim3(a.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
     return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
@@ -494,9 +505,7 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 3) * 4, &a.g, &lds))
         return NA_ERR_UNSUPPORTED;
     auto kern = na::fwd_kernel<T, D>;
-    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
-        hipSuccess)
-        return NA_ERR_HIP;
+    if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3(a.g.n_tiles), dim3(na::kThreads), lds, s, a);
     return launched();
 }
@@ -535,10 +544,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                 if (st != NA_OK) return st;
             } else {
                 auto kern = na::dq_kernel<T, D>;
-                if (hipFuncSetAttribute((const void *)kern,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        lds_q) != hipSuccess)
-                    return NA_ERR_HIP;
+                if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
                 hipLaunchKernelGGL(kern, dim3(aq.g.n_tiles), dim3(na::kThreads), lds_q, s, aq);
                 if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
             }
@@ -615,10 +621,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                     ak.g.n_tiles = (int)(4 * pr.batch * pr.heads * ak.g.tiles[0] *
                                          ak.g.border.per_plane);
                 auto kern = na::dkdv_kernel<T, D, false>;
-                if (hipFuncSetAttribute((const void *)kern,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        lds_k) != hipSuccess)
-                    return NA_ERR_HIP;
+                if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
                 hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
                 if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
             }
@@ -646,9 +649,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
         }
     }
     auto kern = na::dkdv_kernel<T, D, true>;
-    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            lds_k) != hipSuccess)
-        return NA_ERR_HIP;
+    if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
     hipLaunchKernelGGL((na::dq_finalize_kernel<T>), flat_grid(n4), dim3(kThreads), 0, s,
@@ -668,12 +669,16 @@ const char *na_status_string(na_status s) {
     switch (s) {
         case NA_OK: return "NA_OK";
         case NA_ERR_INVALID_ARG: return "NA_ERR_INVALID_ARG: invalid problem or pointer";
-        case NA_ERR_UNSUPPORTED: return "NA_ERR_UNSUPPORTED: no kernel for this head_dim or dtype";
+        case NA_ERR_UNSUPPORTED:
+            return "NA_ERR_UNSUPPORTED: no kernel for this problem (head_dim not 16, 32 or 64, a "
+                   "window whose walk near a border exceeds 32 points, or a token row over 2 GiB)";
         case NA_ERR_WORKSPACE: return "NA_ERR_WORKSPACE: workspace missing or too small";
         case NA_ERR_HIP: return "NA_ERR_HIP: HIP runtime error at launch";
     }
     return "unknown na_status";
 }
+
+const char *na_source_sha256(void) { return NA_SOURCE_SHA256; }
 
 int64_t na_window_start(int64_t extent, int64_t kernel, int64_t dilation, int64_t x) {
     if (extent < 1 || kernel < 1 || dilation < 1 || x < 0 || x >= extent || extent > INT32_MAX)

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "na_fast.hpp"
+#include "na_host.hpp"
 #include "na_index.hpp"
 
 namespace nu {
@@ -770,9 +771,7 @@ inline bool plan(const Geo &geo, int64_t bh, int D, int kind, int oh, int ow, UP
 
 template <typename Kern>
 inline bool launch(Kern kern, const UPlan &pl, hipStream_t s) {
-    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            pl.lds) != hipSuccess)
-        return false;
+    if (!na_host::lds_limit_once((const void *)kern)) return false;
     if (pl.a.g.n_tiles > 0)
         hipLaunchKernelGGL(kern, dim3(pl.a.g.n_tiles), dim3(kThreads), pl.lds, s, pl.a);
     return true;

@@ -35,7 +35,7 @@ EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na
            "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
            "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
-           "na_qk_softmax_bwd")
+           "na_qk_softmax_bwd", "na_source_sha256")
 
 
 class NaProblem(ctypes.Structure):
@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
         lib.na_bwd_dkdv.restype = ctypes.c_int
         lib.na_status_string.argtypes = [ctypes.c_int]
         lib.na_status_string.restype = ctypes.c_char_p
+        lib.na_source_sha256.argtypes = []
+        lib.na_source_sha256.restype = ctypes.c_char_p
         lib.na_window_start.argtypes = [i64, i64, i64, i64]
         lib.na_window_start.restype = i64
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
@@ -180,6 +182,25 @@ def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor):
         raise ValueError("tensors must live on the GPU")
 
 
+def _check_buf(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device: torch.device):
+    """A caller-supplied output or workspace buffer: the C ABI cannot see sizes,
+    so a wrong one would be written out of bounds; reject it here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws: torch.Tensor, need: int, device: torch.device):
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
+
+
 def na_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kernel_size, dilation=1,
            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -188,8 +209,10 @@ def na_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kernel_size, dilat
     p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
     if out is None:
         out = torch.empty_like(q)
+    _check_buf(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
     _check(load().na_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                          _stream_handle(q.device)))
     return out, lse
@@ -214,9 +237,12 @@ def na_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     need = bwd_workspace_bytes(p, vid)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(g, name, q.shape, q.dtype, q.device)
     _check(load().na_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), vid,
@@ -227,11 +253,14 @@ def na_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
 def na_bwd_dq(q, k, v, out, dout, lse, kernel_size, dilation=1, scale=None, dq=None, delta=None):
     """Query half of the gather backward: returns (dq, delta)."""
     _check_tensors(q, k, v, out, dout)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
     p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
     if dq is None:
         dq = torch.empty_like(q)
+    _check_buf(dq, "dq", q.shape, q.dtype, q.device)
     if delta is None:
         delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_buf(delta, "delta", q.shape[:-1], torch.float32, q.device)
     _check(load().na_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                             _ptr(lse), _ptr(dq), _ptr(delta), _stream_handle(q.device)))
     return dq, delta
@@ -240,14 +269,23 @@ def na_bwd_dq(q, k, v, out, dout, lse, kernel_size, dilation=1, scale=None, dq=N
 def na_bwd_dkdv(q, k, v, dout, lse, delta, kernel_size, dilation=1, scale=None, dk=None, dv=None):
     """Key half of the gather backward: returns (dk, dv)."""
     _check_tensors(q, k, v, dout)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    _check_buf(delta, "delta", q.shape[:-1], torch.float32, q.device)
     p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
     if dk is None:
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
+    _check_buf(dk, "dk", q.shape, q.dtype, q.device)
+    _check_buf(dv, "dv", q.shape, q.dtype, q.device)
     _check(load().na_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                               _ptr(delta), _ptr(dk), _ptr(dv), _stream_handle(q.device)))
     return dk, dv
+
+
+def source_sha256() -> str:
+    """sha256 of the sources the loaded library was built from."""
+    return load().na_source_sha256().decode()
 
 
 def window_start(extent: int, kernel: int, dilation: int, x: int) -> int:
@@ -265,8 +303,10 @@ class NeighborhoodAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, kernel_size, dilation, scale):
-        out, lse = na_fwd(q.contiguous(), k.contiguous(), v.contiguous(), kernel_size, dilation,
-                          scale)
+        # views (e.g. q, k, v split from one fused projection) become contiguous
+        # copies here, and the backward gets those same copies
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, lse = na_fwd(q, k, v, kernel_size, dilation, scale)
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.cfg = (kernel_size, dilation, scale)
         return out
@@ -315,6 +355,13 @@ def _check_hm(*ts: torch.Tensor):
             raise ValueError("tensors must live on the GPU")
 
 
+def _check_hm_buf(t, name: str, shape, ref: torch.Tensor):
+    """A caller-supplied fp32 buffer of the unfused ops: right shape, on ref's device."""
+    _check_hm(t)
+    if tuple(t.shape) != tuple(shape) or t.device != ref.device:
+        raise ValueError(f"{name} must be an fp32 tensor of shape {tuple(shape)} on {ref.device}")
+
+
 def _attn_like(x: torch.Tensor, K: int) -> torch.Tensor:
     return torch.empty(x.shape[:-1] + (K,), dtype=torch.float32, device=x.device)
 
@@ -359,6 +406,7 @@ def na_qk(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: floa
     mp = _check_mask(mask, a, K)
     if attn is None:
         attn = _attn_like(a, K)
+    _check_hm_buf(attn, "attn", a.shape[:-1] + (K,), a)
     _check(load().na_qk(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, mp, _ptr(attn),
                         _stream_handle(a.device)))
     return attn
@@ -378,6 +426,7 @@ def na_qk_softmax(a: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alp
     mp = _check_mask(mask, a, K)
     if probs is None:
         probs = _attn_like(a, K)
+    _check_hm_buf(probs, "probs", a.shape[:-1] + (K,), a)
     _check(load().na_qk_softmax(ctypes.byref(p), _ptr(a), _ptr(b), float(alpha), rp, mp,
                                 _ptr(probs), _stream_handle(a.device)))
     return probs
@@ -393,6 +442,7 @@ def na_qk_softmax_bwd(dout: torch.Tensor, v: torch.Tensor, probs: torch.Tensor, 
     p = make_problem_hm(dout.shape, dout.shape[-1], kernel_size, dilation)
     if dscores is None:
         dscores = _attn_like(dout, K)
+    _check_hm_buf(dscores, "dscores", dout.shape[:-1] + (K,), dout)
     _check(load().na_qk_softmax_bwd(ctypes.byref(p), _ptr(dout), _ptr(v), _ptr(probs),
                                     _ptr(dscores), _stream_handle(dout.device)))
     return dscores
@@ -408,11 +458,14 @@ def na_rpb_grad(dscores: torch.Tensor, kernel_size, dilation=1,
     need = int(load().na_rpb_grad_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dscores.device)
+    _check_workspace(workspace, need, dscores.device)
     if drpb is None:
         drpb = torch.empty(rpb_shape(kernel_size, dscores.shape[1], ndim), dtype=torch.float32,
                            device=dscores.device)
+    _check_hm_buf(drpb, "drpb", rpb_shape(kernel_size, dscores.shape[1], ndim), dscores)
     _check(load().na_rpb_grad(ctypes.byref(p), _ptr(dscores), _ptr(drpb), _ptr(workspace),
-                              workspace.numel(), _stream_handle(dscores.device)))
+                              workspace.numel() * workspace.element_size(),
+                              _stream_handle(dscores.device)))
     return drpb
 
 
@@ -426,6 +479,7 @@ def na_av(attn: torch.Tensor, b: torch.Tensor, kernel_size, dilation=1, alpha: f
     p = make_problem_hm(b.shape, b.shape[-1], kernel_size, dilation)
     if out is None:
         out = torch.empty_like(b)
+    _check_hm_buf(out, "out", b.shape, b)
     _check(load().na_av(ctypes.byref(p), _ptr(attn), _ptr(b), float(alpha), _ptr(out),
                         _stream_handle(b.device)))
     return out
@@ -442,6 +496,7 @@ def na_av_inverse(attn: torch.Tensor, a: torch.Tensor, kernel_size, dilation=1,
     p = make_problem_hm(a.shape, a.shape[-1], kernel_size, dilation)
     if out is None:
         out = torch.empty_like(a)
+    _check_hm_buf(out, "out", a.shape, a)
     _check(load().na_av_inverse(ctypes.byref(p), _ptr(attn), _ptr(a), float(alpha), _ptr(out),
                                 _stream_handle(a.device)))
     return out
@@ -456,6 +511,7 @@ def na_softmax(attn: torch.Tensor, kernel_size, dilation=1,
         raise ValueError("the last axis of attn must hold prod(kernel_size) entries")
     if out is None:
         out = torch.empty_like(attn)
+    _check_hm_buf(out, "out", attn.shape, attn)
     _check(load().na_softmax(ctypes.byref(p), _ptr(attn), _ptr(out), _stream_handle(attn.device)))
     return out
 
@@ -471,6 +527,7 @@ def na_softmax_bwd(probs: torch.Tensor, dprobs: torch.Tensor, kernel_size, dilat
         raise ValueError("the last axis must hold prod(kernel_size) entries")
     if out is None:
         out = torch.empty_like(probs)
+    _check_hm_buf(out, "out", probs.shape, probs)
     _check(load().na_softmax_bwd(ctypes.byref(p), _ptr(probs), _ptr(dprobs), _ptr(out),
                                  _stream_handle(probs.device)))
     return out
@@ -491,6 +548,8 @@ def na_unfused_fwd(q, k, v, kernel_size, dilation=1, scale: Optional[float] = No
         probs = _attn_like(q, K)
     if out is None:
         out = torch.empty_like(q)
+    _check_hm_buf(probs, "probs", q.shape[:-1] + (K,), q)
+    _check_hm_buf(out, "out", q.shape, q)
     _check(load().na_unfused_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), rp, mp,
                                  _ptr(probs), _ptr(out), _stream_handle(q.device)))
     return probs, out
@@ -510,17 +569,21 @@ def na_unfused_bwd(q, k, v, probs, dout, kernel_size, dilation=1, scale: Optiona
     p = make_problem_hm(q.shape, q.shape[-1], kernel_size, dilation, scale)
     if dscores is None:
         dscores = _attn_like(q, K)
+    _check_hm_buf(dscores, "dscores", q.shape[:-1] + (K,), q)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = grads
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_hm_buf(g, name, q.shape, q)
     drpb, ws_ptr, ws_n = None, None, 0
     if want_rpb:
         need = int(load().na_rpb_grad_workspace_bytes(ctypes.byref(p)))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, need, q.device)
         drpb = torch.empty(rpb_shape(kernel_size, q.shape[1], q.dim() - 3), dtype=torch.float32,
                            device=q.device)
-        ws_ptr, ws_n = _ptr(workspace), workspace.numel()
+        ws_ptr, ws_n = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(load().na_unfused_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(probs),
                                  _ptr(dout), _ptr(dscores), _ptr(dq), _ptr(dk), _ptr(dv),
                                  None if drpb is None else _ptr(drpb), ws_ptr, ws_n,

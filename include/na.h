@@ -38,7 +38,16 @@
  * enqueued and return NA_ERR_INVALID_ARG (or NA_ERR_UNSUPPORTED for a valid
  * problem this build has no kernel for, NA_ERR_WORKSPACE for a workspace that
  * is too small). A failed kernel launch returns NA_ERR_HIP. The library keeps
- * no global state; calls on different streams may run concurrently.
+ * no state between calls besides a once-per-kernel raise of the dynamic-LDS
+ * limit; calls on different streams may run concurrently.
+ *
+ * Window limit. The kernels keep 32-bit validity masks over a patch walk
+ * along each axis; the walk of a key near a grid border is longer than the
+ * window (up to 2k points on short axes). Windows up to 16 per axis work for
+ * every extent, 17 to 21 for all class extents (extent / dilation) except a
+ * few between 33 and 42, and 22 or more only for class extents below 33;
+ * na_check_problem and every entry point return NA_ERR_UNSUPPORTED for the
+ * rest, before anything is enqueued.
  */
 #ifndef NA_H
 #define NA_H
@@ -53,7 +62,7 @@ extern "C" {
 typedef enum {
     NA_OK = 0,
     NA_ERR_INVALID_ARG = 1,  /* malformed problem, null or misaligned pointer */
-    NA_ERR_UNSUPPORTED = 2,  /* well-formed, but no kernel for it (head_dim, dtype) */
+    NA_ERR_UNSUPPORTED = 2,  /* well-formed, but no kernel for it (head_dim, window limit) */
     NA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than na_bwd_workspace_bytes */
     NA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
 } na_status;
@@ -82,7 +91,8 @@ typedef struct {
     int64_t heads;        /* >= 1 */
     int64_t head_dim;     /* 16, 32 or 64 in this build */
     int64_t extent[3];    /* grid extents, outermost first: (T, H, W) for 3D, (H, W, -) for 2D */
-    int64_t kernel[3];    /* window size per axis, same order; 1 <= k <= floor(extent / dilation) */
+    int64_t kernel[3];    /* window size per axis, same order; 1 <= k <= floor(extent / dilation)
+                             (and the window limit above) */
     int64_t dilation[3];  /* >= 1 per axis, same order */
     double scale;         /* finite score multiplier; the usual choice is head_dim^-0.5 */
 } na_problem;
@@ -125,6 +135,11 @@ na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const v
 
 /* Static, human-readable name of a status code. */
 const char *na_status_string(na_status s);
+
+/* Static string: the sha256 (hex) of the sources this library was built
+ * from (every file of the kernel and ABI sources and this header, in name
+ * order, as fwd_bwd_amd/build.py hashes them), or "unknown". */
+const char *na_source_sha256(void);
 
 /* Host helpers exposing the window rule on one axis (absolute coordinates).
  * na_window_start returns the first key coordinate of the window of query

@@ -26,7 +26,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(na_[a-z_]+)\s*\(", text)
+    names = re.findall(r"\b(na_[a-z0-9_]+)\s*\(", text)
     return sorted(set(names))
 
 
@@ -188,3 +188,26 @@ def test_rpb_workspace_bytes(lib):
     p = _hm_problem(shape=(1, 3, 4, 10, 15, 32), kernel=(3, 5, 5))
     assert lib.na_rpb_grad_workspace_bytes(ctypes.byref(p)) == 3 * 3 * 5 * 9 * 9 * 4
     assert na.rpb_shape((3, 5, 5), 3, 3) == (3, 5, 9, 9)
+
+
+@pytest.mark.parametrize("extent,kernel,expect", [
+    (40, 16, na.NA_OK),            # windows up to 16 fit every extent
+    (33, 16, na.NA_OK),
+    (33, 17, na.NA_ERR_UNSUPPORTED),  # a border walk of 34 points
+    (64, 17, na.NA_OK),
+    (100, 23, na.NA_ERR_UNSUPPORTED),
+    (30, 23, na.NA_OK),            # class extents below 33 always fit
+])
+def test_window_limit(lib, extent, kernel, expect):
+    """Windows whose walk near a border exceeds the kernels' 32-bit validity
+    masks are rejected on the host, by na_check_problem and by the entry points."""
+    p = _p(shape=(1, extent, 48, 1, 32), kernel=(kernel, 3))
+    assert na.check_problem(p) == expect
+    if expect != na.NA_OK:
+        fake = ctypes.c_void_p(4096)
+        assert lib.na_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, None) == expect
+
+
+def test_source_hash_matches_tree(lib):
+    from fwd_bwd_amd import build
+    assert na.source_sha256() == build.source_sha256()

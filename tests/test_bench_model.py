@@ -67,3 +67,40 @@ def test_bench_side_workloads_exist():
     assert WORKLOADS[bench.HEADLINE].dtype == torch.float32
     assert WORKLOADS[bench.HEADLINE_3D].dtype == torch.float32
     assert bench.HEADLINE.replace("_f32", "_f16") in WORKLOADS
+
+
+def _per(ms):
+    return {k: [v, v, v] for k, v in ms.items()}
+
+
+def test_roofline_picks_the_bound_of_each_workloads_type():
+    """fp32 kernels with intensity above the fp32 ridge are priced against the
+    fp32 MFMA peak; the 16-bit workloads sit below the 16-bit MFMA ridge
+    (2516.6 TFLOP/s over 8 TB/s) and are priced against HBM."""
+    import torch
+    w = WORKLOADS[bench.HEADLINE]
+    r = bench.roofline(w, _per({"fwd": 1.0, "bwd_dq": 2.0, "bwd_dkdv": 3.0}))
+    assert r["kernel"] == "bwd_dkdv" and r["bound"] == "mfma" and r["peak"] == 157.3
+    base = w.tokens * w.heads * w.window * w.head_dim
+    assert r["achieved"] == pytest.approx(8 * base / 3e-3 / 1e12, rel=1e-3)
+    for name in bench.BF16_WORKLOADS:
+        wb = WORKLOADS[name]
+        rb = bench.roofline(wb, _per({"fwd": 1.0, "bwd_dq": 2.0, "bwd_dkdv": 3.0}))
+        assert rb["bound"] == "hbm" and rb["unit"] == "GB/s" and rb["peak"] == bench.PEAK_HBM_GBS
+        assert rb["intensity_flop_per_byte"] < rb["ridge_flop_per_byte"]
+        by = bench.algorithmic_bytes(wb)[2]["bwd_dkdv"]
+        assert rb["achieved"] == pytest.approx(by / 3e-3 / 1e9, rel=1e-3)
+        s = bench.summarize(wb, _per({"fwd": 1.0, "bwd_dq": 2.0, "bwd_dkdv": 3.0}))
+        assert s["mfma_peak_tflops"] == bench.PEAK_TFLOPS["bf16_mfma"]
+    assert bench.mfma_peak(torch.float16) == bench.PEAK_TFLOPS["bf16_mfma"]
+    assert bench.DTYPE_LABEL[torch.float16] == "f16"
+    assert bench.DTYPE_LABEL[torch.bfloat16] == "bf16"
+
+
+def test_summarize_reports_medians_and_the_step_sum():
+    w = WORKLOADS[bench.HEADLINE]
+    per = {"fwd": [1.0, 5.0, 2.0], "bwd_dq": [2.0, 2.0, 9.0], "bwd_dkdv": [3.0, 3.0, 3.0]}
+    s = bench.summarize(w, per)
+    assert s["fwd_ms"] == 2.0 and s["fwd_ms_stats"]["min"] == 1.0
+    # per step: 6, 10, 14 -> median 10; backward per step 5, 5, 12 -> median 5
+    assert s["ms_per_step"] == 10.0 and s["bwd_ms"] == 5.0

@@ -212,6 +212,25 @@ def test_autograd_wrapper():
     compare(got, {n: ref[n] for n in got}, torch.float32, "autograd")
 
 
+def test_autograd_on_views_of_a_fused_projection():
+    """q, k, v as non-contiguous views of one [.., 3, heads, D] projection: the
+    forward makes contiguous copies and the backward must use the same ones."""
+    shape, kernel = (1, 10, 12, 2, 32), (3, 5)
+    g = torch.Generator().manual_seed(15)
+    qkv = torch.randn(shape[:-2] + (3,) + shape[-2:], generator=g)
+    dout = torch.randn(shape, generator=g)
+    x = qkv.cuda().requires_grad_()
+    q, k, v = x.unbind(-3)
+    assert not q.is_contiguous()
+    o = na.neighborhood_attention(q, k, v, kernel)
+    o.backward(dout.cuda())
+    ref = oracle_full(*(t.contiguous() for t in qkv.unbind(-3)), dout, kernel, 1,
+                      shape[-1] ** -0.5)
+    got = {"out": o, "dq": x.grad[..., 0, :, :], "dk": x.grad[..., 1, :, :],
+           "dv": x.grad[..., 2, :, :]}
+    compare(got, {n: ref[n] for n in got}, torch.float32, "autograd on views")
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 
 def sample_units(w, n_random=96, seed=0):
