@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <initializer_list>
 #include <type_traits>
+#include <map>
 #include <mutex>
 
 #include "na.h"
@@ -21,6 +22,10 @@ using na::bf16;
 using na::f16;
 
 constexpr int kThreads = 256;  // elementwise kernels
+
+// (token, head) rows the static delta array of na_bwd_noalloc holds: 2^23
+// fp32 values, 32 MiB per device.
+constexpr int64_t kNoallocRows = NA_NOALLOC_MAX_ROWS;
 
 #ifndef NA_SOURCE_SHA256
 #define NA_SOURCE_SHA256 "unknown"
@@ -821,6 +826,56 @@ na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const v
     if (!ptrs_ok({q, k, v, dout, lse, delta, dk, dv})) return NA_ERR_INVALID_ARG;
     return bwd_common(p, q, k, v, nullptr, dout, lse, nullptr, dk, dv, const_cast<float *>(delta),
                       nullptr, NA_BWD_GATHER, kPhaseDkdv, hip_stream);
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------------------
+// Backward without a caller workspace, for callers that cannot allocate device
+// memory. Its one scratch buffer, the fp32 delta rows, is this file-scope
+// array: every GPU the library runs on holds its own copy until the process
+// ends. In host code the name `scratch` is only a host-side stand-in; the
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+
+namespace {
+
+static __device__ __align__(256) float scratch[kNoallocRows];
+
+// Device address of `scratch` on the current device (nullptr on a HIP error).
+float *noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    static std::mutex mu;
+    static std::map<int, float *> ptrs;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = ptrs.find(dev);
+    if (it != ptrs.end()) return it->second;
+    float *ptr = nullptr;
+    if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return nullptr;
+    ptrs[dev] = ptr;
+    return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+na_status na_bwd_noalloc(const na_problem *p, const void *q, const void *k, const void *v,
+                         const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                         void *dv, void *hip_stream) {
+    Prob pr;
+    na_status st = validate(p, &pr);
+    if (st != NA_OK) return st;
+    if (!ptrs_ok({q, k, v, out, dout, lse, dq, dk, dv})) return NA_ERR_INVALID_ARG;
+    if (pr.rows > kNoallocRows) return NA_ERR_WORKSPACE;
+    float *delta = noalloc_scratch();
+    if (!delta) return NA_ERR_HIP;
+    // delta is written in full by the dq kernel before dk/dv reads it: nothing
+    // needs clearing between calls
+    return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, NA_BWD_GATHER,
+                      kPhaseBoth, hip_stream);
 }
 
 }  // extern "C"

@@ -35,7 +35,10 @@ EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na
            "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
            "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
-           "na_qk_softmax_bwd", "na_source_sha256")
+           "na_qk_softmax_bwd", "na_source_sha256", "na_bwd_noalloc")
+
+# rows (batch * tokens * heads) the static delta array of na_bwd_noalloc holds
+NOALLOC_MAX_ROWS = 8388608
 
 
 class NaProblem(ctypes.Structure):
@@ -92,6 +95,8 @@ def load() -> ctypes.CDLL:
         lib.na_status_string.restype = ctypes.c_char_p
         lib.na_source_sha256.argtypes = []
         lib.na_source_sha256.restype = ctypes.c_char_p
+        lib.na_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_bwd_noalloc.restype = ctypes.c_int
         lib.na_window_start.argtypes = [i64, i64, i64, i64]
         lib.na_window_start.restype = i64
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
@@ -281,6 +286,24 @@ def na_bwd_dkdv(q, k, v, dout, lse, delta, kernel_size, dilation=1, scale=None, 
     _check(load().na_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                               _ptr(delta), _ptr(dk), _ptr(dv), _stream_handle(q.device)))
     return dk, dv
+
+
+def na_bwd_noalloc(q, k, v, out, dout, lse, kernel_size, dilation=1, scale=None, grads=None):
+    """The gather backward with its delta rows in the library's static device
+    array instead of a workspace (the C entry point allocates nothing; pass
+    grads to allocate nothing here either). Returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, out, dout)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(g, name, q.shape, q.dtype, q.device)
+    _check(load().na_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _stream_handle(q.device)))
+    return dq, dk, dv
 
 
 def source_sha256() -> str:

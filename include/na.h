@@ -37,9 +37,10 @@
  * Errors. Argument errors are detected on the host before anything is
  * enqueued and return NA_ERR_INVALID_ARG (or NA_ERR_UNSUPPORTED for a valid
  * problem this build has no kernel for, NA_ERR_WORKSPACE for a workspace that
- * is too small). A failed kernel launch returns NA_ERR_HIP. The library keeps
- * no state between calls besides a once-per-kernel raise of the dynamic-LDS
- * limit; calls on different streams may run concurrently.
+ * is too small). A failed kernel launch returns NA_ERR_HIP. Apart from the
+ * static delta array of na_bwd_noalloc, the library keeps no state between
+ * calls besides a once-per-kernel raise of the dynamic-LDS limit; calls on
+ * different streams may run concurrently.
  *
  * Window limit. The kernels keep 32-bit validity masks over a patch walk
  * along each axis; the walk of a key near a grid border is longer than the
@@ -140,6 +141,26 @@ const char *na_status_string(na_status s);
  * from (every file of the kernel and ABI sources and this header, in name
  * order, as fwd_bwd_amd/build.py hashes them), or "unknown". */
 const char *na_source_sha256(void);
+
+/* ------------------------------------------------------------------------
+ * Backward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Exactly na_bwd with NA_BWD_GATHER (the same kernels, bitwise the same
+ * dq, dk, dv), except that the delta rows live in a static device array of
+ * the library instead of a caller workspace: NA_NOALLOC_MAX_ROWS fp32 values
+ * (32 MiB), held on every GPU the library runs on until the process ends.
+ * Problems with more than NA_NOALLOC_MAX_ROWS (token, head) rows, i.e.
+ * batch * prod(extent) * heads, return NA_ERR_WORKSPACE before anything is
+ * enqueued. Nothing is allocated, freed or synchronized; inputs and outputs
+ * are the caller's, as for na_bwd. All calls on one GPU share that GPU's
+ * array (it keeps the last call's contents, which the next call overwrites
+ * before reading): calls that overlap in time on one GPU, e.g. on two
+ * streams, race and must be ordered by the caller. */
+#define NA_NOALLOC_MAX_ROWS 8388608
+na_status na_bwd_noalloc(const na_problem *p, const void *q, const void *k, const void *v,
+                         const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                         void *dv, void *hip_stream);
 
 /* Host helpers exposing the window rule on one axis (absolute coordinates).
  * na_window_start returns the first key coordinate of the window of query

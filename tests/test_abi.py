@@ -211,3 +211,17 @@ def test_window_limit(lib, extent, kernel, expect):
 def test_source_hash_matches_tree(lib):
     from fwd_bwd_amd import build
     assert na.source_sha256() == build.source_sha256()
+
+
+def test_noalloc_rejects_problems_beyond_its_array(lib):
+    """na_bwd_noalloc keeps delta in a static array of NA_NOALLOC_MAX_ROWS rows:
+    larger problems are refused on the host, before any HIP call."""
+    assert na.NOALLOC_MAX_ROWS == 1 << 23
+    p = _p(shape=(1, 1024, 1024, 9, 16), kernel=(3, 3))   # 9 * 2^20 rows
+    fake = ctypes.c_void_p(4096)
+    args = [ctypes.byref(p)] + [fake] * 9 + [None]
+    assert lib.na_bwd_noalloc(*args) == na.NA_ERR_WORKSPACE
+    p = _p(shape=(1, 1024, 1024, 8, 16), kernel=(3, 3))   # exactly 2^23 rows: accepted sizes
+    assert na.check_problem(p) == na.NA_OK
+    bad = [ctypes.byref(p)] + [fake] * 8 + [None, None]   # dv missing
+    assert lib.na_bwd_noalloc(*bad) == na.NA_ERR_INVALID_ARG
