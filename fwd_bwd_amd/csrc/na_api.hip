@@ -15,6 +15,7 @@
 #include "na_fast.hpp"
 #include "na_host.hpp"
 #include "na_kernels.hpp"
+#include "na_mfma16.hpp"
 
 namespace {
 
@@ -487,6 +488,89 @@ na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStrea
     return NA_ERR_UNSUPPORTED;
 }
 
+// ----------------------------------------------------------------------------
+// 16-bit MFMA kernels (na_mfma16.hpp): bf16 and fp16 tensors with head_dim 32
+// or 64. kind 0: forward, 1: dq, 2: dk/dv.
+
+struct M16Plan {
+    na::m16::Geom g;
+    int lds;
+};
+
+// Columns a slab row must hold: the end of the last block any wave of any
+// 16-column tile walks, relative to its tile's box start (the same formulas
+// the kernels evaluate), rounded to groups of four.
+int m16_box_w(const Prob &q, bool inverse) {
+    int bw = 4;
+    const int k = q.ker[2];
+    for (int r = 0; r < q.dil[2] && r < q.ext[2]; ++r) {
+        const int n = na::class_size(q.ext[2], q.dil[2], r);
+        for (int w0 = 0; w0 < n; w0 += na::m16::kTW) {
+            const int U2 = inverse ? na::inverse_first(w0, n, k) : na::window_start(w0, n, k);
+            for (int j = 0; j < 4 && w0 + 4 * j < n; ++j) {
+                const int p0 = w0 + 4 * j, p1 = std::min(p0 + 3, n - 1);
+                const int s0 = inverse ? na::inverse_first(p0, n, k) : na::window_start(p0, n, k);
+                const int e1 = inverse ? na::inverse_last(p1, n, k) + 1
+                                       : na::window_start(p1, n, k) + k;
+                const int aw = (s0 - U2) & ~3;
+                const int nbw = (e1 - U2 - aw + 3) >> 2;
+                bw = std::max(bw, aw + 4 * nbw);
+            }
+        }
+    }
+    return bw;
+}
+
+bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
+    if (q.dtype != NA_BF16 && q.dtype != NA_F16) return false;
+    if (q.head_dim != 32 && q.head_dim != 64) return false;
+    na::m16::Geom &g = pl->g;
+    g = na::m16::Geom{};
+    int64_t n_tiles = q.batch * q.heads;
+    int nres = 1;
+    for (int a = 0; a < 3; ++a) {
+        g.ext[a] = q.ext[a];
+        g.ker[a] = q.ker[a];
+        g.dil[a] = q.dil[a];
+        const int nmax = na::class_size(q.ext[a], q.dil[a], 0);
+        const int t = a == 0 ? 1 : a == 1 ? na::m16::kTH : na::m16::kTW;
+        g.tiles[a] = (nmax + t - 1) / t;
+        n_tiles *= g.tiles[a];
+        nres *= q.dil[a];
+    }
+    n_tiles *= nres;
+    if (n_tiles > INT32_MAX) return false;
+    g.heads = (int)q.heads;
+    g.batch = (int)q.batch;
+    g.nres = nres;
+    g.n_tiles = (int)n_tiles;
+    g.box_w = m16_box_w(q, kind == 2);
+    const int NC = (int)q.head_dim * 2 / 16;
+    g.km_pitch = ((g.box_w * NC) | 1) * 16;                 // odd number of 16-byte chunks
+    g.tr_pitch = g.box_w * 2 * (int)q.head_dim + 128;       // 128 bytes off a multiple of 256
+    const int64_t lds = kind == 0   ? 4LL * g.km_pitch + 4LL * g.tr_pitch
+                        : kind == 1 ? 8LL * g.km_pitch + 4LL * g.tr_pitch
+                                    : 8LL * g.km_pitch + 8LL * g.tr_pitch + 32LL * g.box_w;
+    if (lds > kLdsMax) return false;
+    pl->lds = (int)lds;
+    g.f_heads = na::make_fastdiv(g.heads);
+    g.f_tw = na::make_fastdiv(g.tiles[2]);
+    g.f_th = na::make_fastdiv(g.tiles[1]);
+    g.f_t = na::make_fastdiv(g.tiles[0]);
+    g.f_nres = na::make_fastdiv(g.nres);
+    for (int a = 0; a < 3; ++a) g.f_dil[a] = na::make_fastdiv(g.dil[a]);
+    g.f_dil21 = na::make_fastdiv(g.dil[2] * g.dil[1]);
+    return true;
+}
+
+template <typename Kern, typename Args>
+na_status launch_m16(Kern kern, const M16Plan &pl, const Args &a, hipStream_t s) {
+    if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
+    if (pl.g.n_tiles == 0) return NA_OK;
+    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
+    return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
+}
+
 dim3 flat_grid(int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); }
 
 na_status launched() { return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP; }
@@ -494,6 +578,20 @@ na_status launched() { return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_H
 template <typename T, int D>
 na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
+    if constexpr (!std::is_same<T, float>::value && (D == 32 || D == 64)) {
+        M16Plan mp;
+        if (m16_plan(pr, 0, &mp)) {
+            na::m16::Args<T> ma{};
+            ma.g = mp.g;
+            ma.q = static_cast<const T *>(a.q);
+            ma.k = static_cast<const T *>(a.k);
+            ma.v = static_cast<const T *>(a.v);
+            ma.o = static_cast<T *>(a.out);
+            ma.lse_out = a.lse;
+            ma.qscale = a.qscale;
+            return launch_m16(na::m16::fwd_kernel<T, D>, mp, ma, s);
+        }
+    }
     FastPlan pl;
     if (fast_plan_fwd(pr, &pl)) {
         na::fast::FwdArgsT<T> fa{};
@@ -525,6 +623,35 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
     int lds_q = 0, lds_k = 0;
     if (!geometry(pr, false, 2 * PB, na::kWaves * 64 * (D + 1) * 4, &aq.g, &lds_q)) return NA_ERR_UNSUPPORTED;
     if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * (D + 1) * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
+    if constexpr (!std::is_same<T, float>::value && (D == 32 || D == 64)) {
+        M16Plan mq, mk;
+        if (variant == NA_BWD_GATHER && m16_plan(pr, 1, &mq) && m16_plan(pr, 2, &mk)) {
+            na::m16::Args<T> ma{};
+            ma.q = static_cast<const T *>(a.q);
+            ma.k = static_cast<const T *>(a.k);
+            ma.v = static_cast<const T *>(a.v);
+            ma.out = static_cast<const T *>(a.out);
+            ma.dout = static_cast<const T *>(a.dout);
+            ma.lse = a.lse;
+            ma.delta = a.delta;
+            ma.dq = static_cast<T *>(a.dq);
+            ma.dk = static_cast<T *>(a.dk);
+            ma.dv = static_cast<T *>(a.dv);
+            ma.qscale = a.qscale;
+            ma.scale = a.scale;
+            // dq (which also writes delta) strictly before dk/dv, which reads it
+            if (phases & kPhaseDq) {
+                ma.g = mq.g;
+                const na_status st = launch_m16(na::m16::dq_kernel<T, D>, mq, ma, s);
+                if (st != NA_OK) return st;
+            }
+            if (phases & kPhaseDkdv) {
+                ma.g = mk.g;
+                return launch_m16(na::m16::dkdv_kernel<T, D>, mk, ma, s);
+            }
+            return NA_OK;
+        }
+    }
     if (variant == NA_BWD_GATHER) {
         na::fast::BwdArgsT<T> fa{};
         fa.q = static_cast<const T *>(a.q);

@@ -1,0 +1,663 @@
+// na_mfma16.hpp -- neighborhood attention forward and backward for 16-bit
+// tensors (bf16, fp16) on the gfx950 16-bit MFMA v_mfma_f32_16x16x32_{bf16,f16}
+// (fp32 accumulation).
+//
+// The operation is that of NATTEN issue #161, "Backward pass is very slow
+// towards much tokens and large kernels": per query a softmax over the scores
+// scale * <q, k> of its window of keys, weighted sum of values; the backward
+// recomputes the weights from the saved logsumexp, uses delta = rowsum(dO * O)
+// (the maintainer's ComputeDelta) and forms dK, dV over each key's inverse
+// neighborhood. The maintainer notes that fused attention is compute bound only
+// at 16-bit precision; this is the path for those tensors.
+//
+// Work decomposition. A wave owns a patch of 16 points (1 x 4 x 4 along T, H,
+// W in class coordinates of one residue class): queries in the forward and dq
+// kernels, keys in the dk/dv kernel. A workgroup of four waves owns a 1 x 4 x
+// 16 tile (its waves side by side along W), so all its waves share the same
+// rows along T and H and need the same rows of the other side's box: the box
+// is staged one 4-row slab at a time (one plane along T), and every wave walks
+// the 4 x 4 blocks of its own patch's window union (or inverse union) inside
+// the slab. One MFMA contracts 16 points of one side with a 4 x 4 block of the
+// other over 32 channels; pairs of blocks (32 points) form the 32-deep
+// reductions of the weighted sums.
+//
+// Operand layouts (lane l, lane group g = l / 16, n = l % 16):
+//  * A (16 x 32) and B (32 x 16) operands: lane l holds row / column n and
+//    reduction entries 8g .. 8g + 7; result C (16 x 16): lane l holds rows
+//    4g .. 4g + 3 of column n.
+//  * Scores are formed transposed, S^T = K Q^T: A = a 4 x 4 key block (key n at
+//    block row n / 4, column n % 4, channels from LDS), B = the wave's queries
+//    (registers). Lane l then holds the scores of query n against the keys of
+//    block row g, columns 0..3 -- exactly the B operand a weighted sum over a
+//    pair of blocks needs when its reduction entries 8g .. 8g + 3 are block
+//    row g of the first block and 8g + 4 .. 8g + 7 block row g of the second:
+//    O^T += V^T P^T with A = V^T read as four keys at one channel.
+//  * LDS: "key-major" slabs hold each point's channels contiguously (16-byte
+//    chunks, XOR-swizzled at 64 channels, odd row pitch in chunks: the A reads
+//    of 16 keys at one chunk hit 16 different bank groups); "transposed" slabs
+//    hold each group of four W-consecutive points as channel-major 8-byte
+//    entries (4 points x 16 bits), rows 128 bytes off a multiple of 256, so the
+//    two 8-byte reads of an A operand come from 64 different banks.
+//  * Row sums of the weights come out of the MFMA as well: one more product
+//    against an all-ones A operand gives every lane the sum for its query.
+//
+// Windows are clamped by index arithmetic only: a score is kept when the key
+// lies in the query's window (equivalently the query in the key's inverse
+// window), which also rejects every point a slab holds past the grid (those
+// repeat the last grid point, so they are finite).
+#pragma once
+
+#include "na_common.hpp"
+
+namespace na {
+namespace m16 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct Mf;
+
+template <>
+struct Mf<bf16> {
+    __device__ __forceinline__ static f4 mma(uint4 a, uint4 b, f4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // two fp32 values to two bf16 (round to nearest even), low half first
+    __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ __forceinline__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ __forceinline__ static float hi(uint32_t w) {
+        return __uint_as_float(w & 0xffff0000u);
+    }
+    static constexpr uint32_t kOne2 = 0x3f803f80u;  // (1.0, 1.0)
+};
+
+template <>
+struct Mf<f16> {
+    __device__ __forceinline__ static f4 mma(uint4 a, uint4 b, f4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ __forceinline__ static float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    __device__ __forceinline__ static float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+    static constexpr uint32_t kOne2 = 0x3c003c00u;
+};
+
+constexpr int kTH = 4, kTW = 16;  // tile rows (H) and columns (W); T: one plane
+
+struct Geom {
+    int ext[3], ker[3], dil[3];
+    int heads, batch;
+    int tiles[3];  // per axis over the largest residue class: planes, 4-row tiles, 16-column tiles
+    int nres, n_tiles;
+    int box_w;     // points per slab row (a multiple of 4)
+    int km_pitch;  // bytes per slab row, key-major layout
+    int tr_pitch;  // bytes per slab row, transposed layout
+    FastDiv f_heads, f_tw, f_th, f_t, f_nres;
+    FastDiv f_dil[3], f_dil21;
+};
+
+template <typename T>
+struct Args {
+    Geom g;
+    const T *q, *k, *v, *out, *dout;
+    const float *lse;
+    float *lse_out;  // forward: logsumexp output
+    float *delta;    // dq: written; dk/dv: read
+    T *o, *dq, *dk, *dv;
+    float qscale;  // scale * log2(e)
+    float scale;
+};
+
+// Tile id -> batch, head, residue class and tile origin (class coordinates).
+// The head varies fastest (the heads of one token are adjacent in memory),
+// then W, H, T tiles, residue class, batch.
+__device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
+    int rem = tile, q;
+    q = fdiv(rem, g.f_heads);
+    const int head = rem - q * g.heads;
+    rem = q;
+    q = fdiv(rem, g.f_tw);
+    const int tw = rem - q * g.tiles[2];
+    rem = q;
+    q = fdiv(rem, g.f_th);
+    const int th = rem - q * g.tiles[1];
+    rem = q;
+    q = fdiv(rem, g.f_t);
+    const int tt = rem - q * g.tiles[0];
+    rem = q;
+    q = fdiv(rem, g.f_nres);
+    const int res = rem - q * g.nres;
+    const int b = q;
+    int r[3];
+    q = fdiv(res, g.f_dil[2]);
+    r[2] = res - q * g.dil[2];
+    const int q1 = fdiv(q, g.f_dil[1]);
+    r[1] = q - q1 * g.dil[1];
+    r[0] = fdiv(res, g.f_dil21);
+    const int o[3] = {tt, th * kTH, tw * kTW};
+    bool inside = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        w.n[a] = fdiv(g.ext[a] - r[a] + g.dil[a] - 1, g.f_dil[a]);
+        w.k[a] = g.ker[a];
+        w.o[a] = o[a];
+        inside = inside && (o[a] < w.n[a]);
+    }
+    // (token, head) row offsets; element offsets are these times head_dim
+    const int64_t HW = (int64_t)g.ext[1] * g.ext[2];
+    const int64_t ntok = HW * g.ext[0];
+    const int64_t origin_tok = r[0] * HW + (int64_t)r[1] * g.ext[2] + r[2];
+    w.lbase = ((int64_t)b * ntok + origin_tok) * g.heads + head;
+    w.lst[0] = g.dil[0] * HW * g.heads;
+    w.lst[1] = (int64_t)g.dil[1] * g.ext[2] * g.heads;
+    w.lst[2] = (int64_t)g.dil[2] * g.heads;
+    return inside;
+}
+
+// Element offset of class point c: (row offset) * D.
+template <int D>
+__device__ __forceinline__ int64_t eoff(const TileCtx &w, int c0, int c1, int c2) {
+    return (w.lbase + c0 * w.lst[0] + c1 * w.lst[1] + c2 * w.lst[2]) * D;
+}
+__device__ __forceinline__ int64_t roff(const TileCtx &w, int c0, int c1, int c2) {
+    return w.lbase + c0 * w.lst[0] + c1 * w.lst[1] + c2 * w.lst[2];
+}
+
+// Chunk swizzle of the key-major layout: at 8 chunks per point (64 channels)
+// the chunk index flips bit 2 on every other pair of columns.
+template <int NC>
+__device__ __forceinline__ int kswz(int col) {
+    return NC == 8 ? ((col >> 1) & 1) << 2 : 0;
+}
+
+// Key-major slab: rows [r0, r0 + 4) of plane tk (class coordinates), columns
+// [U2, U2 + box_w), of src; row r at lds + r * pitch, chunk s of column c at
+// 16 * (c * NC + (s ^ kswz(c))). Direct global-to-LDS loads, 64 consecutive
+// chunks per wave instruction; wave v stages row v. Points past the grid repeat
+// the last grid point. Completion: stage_wait().
+template <typename T, int D>
+__device__ __forceinline__ void stage_km(const T *src, const TileCtx &w, int tk, int r0, int U2,
+                                         int box_w, int pitch, char *lds) {
+    constexpr int NC = D * 2 / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int nch = box_w * NC;
+    const int c1 = imin(r0 + wave, w.n[1] - 1);
+    const char *rowp =
+        reinterpret_cast<const char *>(src) + eoff<D>(w, tk, c1, 0) * (int64_t)sizeof(T);
+    char *dst = lds + wave * pitch;
+    for (int part = 0; part * 64 < nch; ++part) {
+        const int s = part * 64 + lane;
+        if (s >= nch) continue;
+        const int col = s / NC, pos = s - col * NC;
+        const int c2 = imin(U2 + col, w.n[2] - 1);
+        const int goff = (int)(c2 * w.lst[2]) * D * 2 + ((pos ^ kswz<NC>(col)) << 4);
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_global_load_lds(rowp + goff, (lds_void *)(dst + part * 1024), 16, 0, 0);
+#else
+        (void)goff;
+        (void)dst;
+        (void)rowp;
+#endif
+    }
+}
+
+// Transposed slab: the same points, each group of four W-consecutive points
+// (columns 4G .. 4G + 3) stored channel-major: channel d of the group is the
+// 8 bytes at lds + r * pitch + G * 8 * D + 8 * d (the four points' values in
+// column order). Staged through registers: a thread loads one 16-byte chunk
+// (8 channels) of each of the four points and writes 64 bytes.
+template <typename T, int D>
+__device__ __forceinline__ void stage_tr(const T *src, const TileCtx &w, int tk, int r0, int U2,
+                                         int box_w, int pitch, char *lds) {
+    constexpr int NC = D * 2 / 16;
+    const int groups = box_w >> 2;
+    const int tasks = 4 * groups * NC;
+    for (int t = threadIdx.x; t < tasks; t += kThreads) {
+        const int c = t % NC;
+        const int rg = t / NC;
+        const int G = rg % groups, r = rg / groups;
+        const int c1 = imin(r0 + r, w.n[1] - 1);
+        const T *rowp = src + eoff<D>(w, tk, c1, 0) + c * 8;
+        uint4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c2 = imin(U2 + 4 * G + j, w.n[2] - 1);
+            x[j] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)c2 * w.lst[2] * D);
+        }
+        char *dst = lds + r * pitch + G * 8 * D + c * 64;
+        const uint32_t a0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
+        const uint32_t a1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
+        const uint32_t a2[4] = {x[2].x, x[2].y, x[2].z, x[2].w};
+        const uint32_t a3[4] = {x[3].x, x[3].y, x[3].z, x[3].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint4 o;
+            o.x = (a0[i] & 0xffffu) | (a1[i] << 16);
+            o.y = (a2[i] & 0xffffu) | (a3[i] << 16);
+            o.z = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
+            o.w = (a2[i] >> 16) | (a3[i] & 0xffff0000u);
+            *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
+        }
+    }
+}
+
+// (logsumexp * log2(e), delta) of every point of a slab, as float2 at
+// rows[r * box_w + col].
+__device__ __forceinline__ void stage_rows16(const float *lse, const float *delta,
+                                             const TileCtx &w, int tk, int r0, int U2, int box_w,
+                                             float2 *rows) {
+    for (int i = threadIdx.x; i < 4 * box_w; i += kThreads) {
+        const int r = i / box_w, col = i - r * box_w;
+        const int64_t ro = roff(w, tk, imin(r0 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1));
+        rows[i] = make_float2(lse[ro] * kLog2e, delta[ro]);
+    }
+}
+
+// A operand of the S^T (or S) MFMA: point n of the block at column `col0` of
+// the key-major slab, chunk `ch` (channels 8 ch .. 8 ch + 7).
+template <int NC>
+__device__ __forceinline__ uint4 km_read(const char *lds, int pitch, int n, int col0, int ch) {
+    const int row = n >> 2, col = col0 + (n & 3);
+    return *reinterpret_cast<const uint4 *>(lds + row * pitch + ((col * NC + (ch ^ kswz<NC>(col))) << 4));
+}
+
+// A operand of a weighted sum over blocks at group columns G0, G1 (block
+// columns / 4) of the transposed slab: channel d, slab row g (lane group).
+template <int D>
+__device__ __forceinline__ uint4 tr_read(const char *lds, int pitch, int g, int G0, int G1, int d) {
+    const char *base = lds + g * pitch + 8 * d;
+    const uint2 a = *reinterpret_cast<const uint2 *>(base + G0 * 8 * D);
+    const uint2 b = *reinterpret_cast<const uint2 *>(base + G1 * 8 * D);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+__device__ __forceinline__ float xmax4(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+// The lane's point of the wave's patch: patch origin (class) + (n / 4, n % 4).
+struct Pt {
+    int h, w;       // clamped into the grid
+    bool active;    // unclamped point inside the grid
+};
+__device__ __forceinline__ Pt patch_point(const TileCtx &w, int wave, int n) {
+    const int h = w.o[1] + (n >> 2), c = w.o[2] + 4 * wave + (n & 3);
+    Pt p;
+    p.active = h < w.n[1] && c < w.n[2];
+    p.h = imin(h, w.n[1] - 1);
+    p.w = imin(c, w.n[2] - 1);
+    return p;
+}
+
+// ============================================================================
+// Forward: out, lse.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    const Geom &g = a.g;
+    TileCtx w;
+    if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
+    const int nh = w.n[1], nw = w.n[2];
+    char *Kl = smem;
+    char *Vl = smem + 4 * g.km_pitch;
+
+    // the workgroup's box: planes, rows (shared by all waves) and columns
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    const int Uh = window_start(w.o[1], nh, w.k[1]);
+    const int Hend = window_start(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + w.k[1];
+    const int U2 = window_start(w.o[2], nw, w.k[2]);
+    // this wave's blocks: from its patch's first window start (aligned down to
+    // a group of four columns of the box) to its last window end
+    const bool wave_on = w.o[2] + 4 * wave < nw;
+    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
+    const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
+
+    const Pt P = patch_point(w, wave, n);
+    const int wh = window_start(P.h, nh, w.k[1]);
+    const int ww = window_start(P.w, nw, w.k[2]) - U2;  // relative to the box
+    uint4 qv[NH];
+    {
+        const T *qp = a.q + eoff<D>(w, w.o[0], P.h, P.w) + 8 * lg;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) qv[h] = *reinterpret_cast<const uint4 *>(qp + 32 * h);
+    }
+    const float c = a.qscale;
+    const uint4 ones = make_uint4(Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2);
+
+    f4 acc[ND], lsum = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = -1e30f;
+
+    const int nslab = (Hend - Uh + 3) >> 2;
+    for (int j = 0; j < w.k[0]; ++j) {
+        const int tk = t0 + j;
+        for (int sl = 0; sl < nslab; ++sl) {
+            const int r0 = Uh + 4 * sl;
+            __syncthreads();
+            stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kl);
+            stage_tr<T, D>(a.v, w, tk, r0, U2, g.box_w, g.tr_pitch, Vl);
+            stage_wait();
+            if (!wave_on) continue;
+            // key row of this lane group's scores in the slab, and whether it is
+            // inside the lane's query window
+            const bool row_ok = (unsigned)(r0 + lg - wh) < (unsigned)w.k[1];
+            for (int b = 0; b < nbw; b += 2) {
+                const bool two = b + 1 < nbw;
+                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    s0 = Mf<T>::mma(km_read<NC>(Kl, g.km_pitch, n, col0, lg + 4 * h), qv[h], s0);
+                if (two) {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        s1 = Mf<T>::mma(km_read<NC>(Kl, g.km_pitch, n, col1, lg + 4 * h), qv[h], s1);
+                }
+                float x[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok0 = row_ok && (unsigned)(col0 + r - ww) < (unsigned)w.k[2];
+                    const bool ok1 = two && row_ok && (unsigned)(col1 + r - ww) < (unsigned)w.k[2];
+                    x[r] = ok0 ? s0[r] * c : -INFINITY;
+                    x[4 + r] = ok1 ? s1[r] * c : -INFINITY;
+                }
+                float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                const float mn = fmaxf(m, xmax4(mx));
+                const float alpha = fast_exp2(m - mn);
+                m = mn;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+                lsum *= alpha;
+                uint4 pb;
+                pb.x = Mf<T>::pack(fast_exp2(x[0] - m), fast_exp2(x[1] - m));
+                pb.y = Mf<T>::pack(fast_exp2(x[2] - m), fast_exp2(x[3] - m));
+                pb.z = Mf<T>::pack(fast_exp2(x[4] - m), fast_exp2(x[5] - m));
+                pb.w = Mf<T>::pack(fast_exp2(x[6] - m), fast_exp2(x[7] - m));
+                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    acc[d] = Mf<T>::mma(tr_read<D>(Vl, g.tr_pitch, lg, G0, G1, 16 * d + n), pb, acc[d]);
+                lsum = Mf<T>::mma(ones, pb, lsum);
+            }
+        }
+    }
+    if (!wave_on || !P.active) return;
+    const float inv = 1.f / lsum[0];
+    T *op = a.o + eoff<D>(w, w.o[0], P.h, P.w) + 4 * lg;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const float o4[4] = {acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv};
+        Io<T>::store4(op + 16 * d, o4);
+    }
+    if (lg == 0) a.lse_out[roff(w, w.o[0], P.h, P.w)] = (m + __log2f(lsum[0])) * kLn2;
+}
+
+// ============================================================================
+// Backward, query side: delta = <dout, out> and dq.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    const Geom &g = a.g;
+    TileCtx w;
+    if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
+    const int nh = w.n[1], nw = w.n[2];
+    char *Vk = smem;
+    char *Kk = smem + 4 * g.km_pitch;
+    char *Kt = smem + 8 * g.km_pitch;
+
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    const int Uh = window_start(w.o[1], nh, w.k[1]);
+    const int Hend = window_start(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + w.k[1];
+    const int U2 = window_start(w.o[2], nw, w.k[2]);
+    const bool wave_on = w.o[2] + 4 * wave < nw;
+    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
+    const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
+
+    const Pt P = patch_point(w, wave, n);
+    const int wh = window_start(P.h, nh, w.k[1]);
+    const int ww = window_start(P.w, nw, w.k[2]) - U2;
+    const int64_t qo = eoff<D>(w, w.o[0], P.h, P.w);
+    const int64_t ro = roff(w, w.o[0], P.h, P.w);
+    uint4 qv[NH], dv[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        qv[h] = *reinterpret_cast<const uint4 *>(a.q + qo + 8 * lg + 32 * h);
+        dv[h] = *reinterpret_cast<const uint4 *>(a.dout + qo + 8 * lg + 32 * h);
+    }
+    // delta of the lane's query: its lane group's 8 (or 16) channels, summed
+    // over the four lane groups
+    float delta = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const uint4 ov = *reinterpret_cast<const uint4 *>(a.out + qo + 8 * lg + 32 * h);
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, dw[4] = {dv[h].x, dv[h].y, dv[h].z, dv[h].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            delta += Mf<T>::lo(ow[i]) * Mf<T>::lo(dw[i]) + Mf<T>::hi(ow[i]) * Mf<T>::hi(dw[i]);
+    }
+    delta += __shfl_xor(delta, 16);
+    delta += __shfl_xor(delta, 32);
+    if (wave_on && P.active && lg == 0) a.delta[ro] = delta;
+    const float lse2 = a.lse[ro] * kLog2e;
+    const float c = a.qscale;
+
+    f4 acc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nslab = (Hend - Uh + 3) >> 2;
+    for (int j = 0; j < w.k[0]; ++j) {
+        const int tk = t0 + j;
+        for (int sl = 0; sl < nslab; ++sl) {
+            const int r0 = Uh + 4 * sl;
+            __syncthreads();
+            stage_km<T, D>(a.v, w, tk, r0, U2, g.box_w, g.km_pitch, Vk);
+            stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kk);
+            stage_tr<T, D>(a.k, w, tk, r0, U2, g.box_w, g.tr_pitch, Kt);
+            stage_wait();
+            if (!wave_on) continue;
+            const bool row_ok = (unsigned)(r0 + lg - wh) < (unsigned)w.k[1];
+            for (int b = 0; b < nbw; b += 2) {
+                const bool two = b + 1 < nbw;
+                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    s0 = Mf<T>::mma(km_read<NC>(Kk, g.km_pitch, n, col0, lg + 4 * h), qv[h], s0);
+                    p0 = Mf<T>::mma(km_read<NC>(Vk, g.km_pitch, n, col0, lg + 4 * h), dv[h], p0);
+                }
+                if (two) {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) {
+                        s1 = Mf<T>::mma(km_read<NC>(Kk, g.km_pitch, n, col1, lg + 4 * h), qv[h], s1);
+                        p1 = Mf<T>::mma(km_read<NC>(Vk, g.km_pitch, n, col1, lg + 4 * h), dv[h], p1);
+                    }
+                }
+                float ds[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok0 = row_ok && (unsigned)(col0 + r - ww) < (unsigned)w.k[2];
+                    const bool ok1 = two && row_ok && (unsigned)(col1 + r - ww) < (unsigned)w.k[2];
+                    const float e0 = ok0 ? fast_exp2(s0[r] * c - lse2) : 0.f;
+                    const float e1 = ok1 ? fast_exp2(s1[r] * c - lse2) : 0.f;
+                    ds[r] = e0 * (p0[r] - delta);
+                    ds[4 + r] = e1 * (p1[r] - delta);
+                }
+                uint4 db;
+                db.x = Mf<T>::pack(ds[0], ds[1]);
+                db.y = Mf<T>::pack(ds[2], ds[3]);
+                db.z = Mf<T>::pack(ds[4], ds[5]);
+                db.w = Mf<T>::pack(ds[6], ds[7]);
+                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    acc[d] = Mf<T>::mma(tr_read<D>(Kt, g.tr_pitch, lg, G0, G1, 16 * d + n), db, acc[d]);
+            }
+        }
+    }
+    if (!wave_on || !P.active) return;
+    T *dp = a.dq + qo + 4 * lg;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const float o4[4] = {acc[d][0] * a.scale, acc[d][1] * a.scale, acc[d][2] * a.scale,
+                             acc[d][3] * a.scale};
+        Io<T>::store4(dp + 16 * d, o4);
+    }
+}
+
+// ============================================================================
+// Backward, key side: dk and dv by inverse-neighborhood gather (no atomics).
+// The wave's patch holds keys; it walks the 4 x 4 query blocks of its keys'
+// inverse windows: S = Q K^T (A = a query block, key-major; B = the wave's
+// keys), P = exp2(S c - lse), dP = dO V^T, dS = P (dP - delta); then
+// dV^T += dO^T P and dK^T += Q^T dS over pairs of query blocks.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    const Geom &g = a.g;
+    TileCtx w;
+    if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
+    const int nh = w.n[1], nw = w.n[2];
+    char *Qk = smem;
+    char *Ok = smem + 4 * g.km_pitch;
+    char *Qt = smem + 8 * g.km_pitch;
+    char *Ot = Qt + 4 * g.tr_pitch;
+    float2 *Rw = reinterpret_cast<float2 *>(Ot + 4 * g.tr_pitch);
+
+    // the workgroup's query box: planes, rows, columns of the inverse windows
+    const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
+    const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
+    const int Uh = inverse_first(w.o[1], nh, w.k[1]);
+    const int Hend = inverse_last(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + 1;
+    const int U2 = inverse_first(w.o[2], nw, w.k[2]);
+    const bool wave_on = w.o[2] + 4 * wave < nw;
+    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const int aw = (inverse_first(pw0, nw, w.k[2]) - U2) & ~3;
+    const int nbw = (inverse_last(pw1, nw, w.k[2]) + 1 - U2 - aw + 3) >> 2;
+
+    const Pt P = patch_point(w, wave, n);  // the lane's key
+    const int ih0 = inverse_first(P.h, nh, w.k[1]), ih1 = inverse_last(P.h, nh, w.k[1]);
+    const int iw0 = inverse_first(P.w, nw, w.k[2]) - U2, iw1 = inverse_last(P.w, nw, w.k[2]) - U2;
+    const int64_t ko = eoff<D>(w, w.o[0], P.h, P.w);
+    uint4 kv[NH], vv[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        kv[h] = *reinterpret_cast<const uint4 *>(a.k + ko + 8 * lg + 32 * h);
+        vv[h] = *reinterpret_cast<const uint4 *>(a.v + ko + 8 * lg + 32 * h);
+    }
+    const float c = a.qscale;
+
+    f4 dka[ND], dva[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        dka[d] = f4{0.f, 0.f, 0.f, 0.f};
+        dva[d] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nslab = (Hend - Uh + 3) >> 2;
+    for (int tq = tq0; tq <= tq1; ++tq) {
+        for (int sl = 0; sl < nslab; ++sl) {
+            const int r0 = Uh + 4 * sl;
+            __syncthreads();
+            stage_km<T, D>(a.q, w, tq, r0, U2, g.box_w, g.km_pitch, Qk);
+            stage_km<T, D>(a.dout, w, tq, r0, U2, g.box_w, g.km_pitch, Ok);
+            stage_tr<T, D>(a.q, w, tq, r0, U2, g.box_w, g.tr_pitch, Qt);
+            stage_tr<T, D>(a.dout, w, tq, r0, U2, g.box_w, g.tr_pitch, Ot);
+            stage_rows16(a.lse, a.delta, w, tq, r0, U2, g.box_w, Rw);
+            stage_wait();
+            if (!wave_on) continue;
+            // query row of this lane group in the slab, inside the key's inverse window?
+            const bool row_ok = (unsigned)(r0 + lg - ih0) <= (unsigned)(ih1 - ih0);
+            const float2 *rrow = Rw + lg * g.box_w;
+            for (int b = 0; b < nbw; b += 2) {
+                const bool two = b + 1 < nbw;
+                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    s0 = Mf<T>::mma(km_read<NC>(Qk, g.km_pitch, n, col0, lg + 4 * h), kv[h], s0);
+                    p0 = Mf<T>::mma(km_read<NC>(Ok, g.km_pitch, n, col0, lg + 4 * h), vv[h], p0);
+                }
+                if (two) {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) {
+                        s1 = Mf<T>::mma(km_read<NC>(Qk, g.km_pitch, n, col1, lg + 4 * h), kv[h], s1);
+                        p1 = Mf<T>::mma(km_read<NC>(Ok, g.km_pitch, n, col1, lg + 4 * h), vv[h], p1);
+                    }
+                }
+                float pr[8], ds[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float2 l0 = rrow[col0 + r];
+                    const float2 l1 = rrow[imin(col1 + r, g.box_w - 1)];
+                    const bool ok0 = row_ok && (unsigned)(col0 + r - iw0) <= (unsigned)(iw1 - iw0);
+                    const bool ok1 =
+                        two && row_ok && (unsigned)(col1 + r - iw0) <= (unsigned)(iw1 - iw0);
+                    pr[r] = ok0 ? fast_exp2(s0[r] * c - l0.x) : 0.f;
+                    pr[4 + r] = ok1 ? fast_exp2(s1[r] * c - l1.x) : 0.f;
+                    ds[r] = pr[r] * (p0[r] - l0.y);
+                    ds[4 + r] = pr[4 + r] * (p1[r] - l1.y);
+                }
+                uint4 pb, db;
+                pb.x = Mf<T>::pack(pr[0], pr[1]);
+                pb.y = Mf<T>::pack(pr[2], pr[3]);
+                pb.z = Mf<T>::pack(pr[4], pr[5]);
+                pb.w = Mf<T>::pack(pr[6], pr[7]);
+                db.x = Mf<T>::pack(ds[0], ds[1]);
+                db.y = Mf<T>::pack(ds[2], ds[3]);
+                db.z = Mf<T>::pack(ds[4], ds[5]);
+                db.w = Mf<T>::pack(ds[6], ds[7]);
+                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    dva[d] = Mf<T>::mma(tr_read<D>(Ot, g.tr_pitch, lg, G0, G1, 16 * d + n), pb, dva[d]);
+                    dka[d] = Mf<T>::mma(tr_read<D>(Qt, g.tr_pitch, lg, G0, G1, 16 * d + n), db, dka[d]);
+                }
+            }
+        }
+    }
+    if (!wave_on || !P.active) return;
+    T *kp = a.dk + ko + 4 * lg;
+    T *vp = a.dv + ko + 4 * lg;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const float k4[4] = {dka[d][0] * a.scale, dka[d][1] * a.scale, dka[d][2] * a.scale,
+                             dka[d][3] * a.scale};
+        const float v4[4] = {dva[d][0], dva[d][1], dva[d][2], dva[d][3]};
+        Io<T>::store4(kp + 16 * d, k4);
+        Io<T>::store4(vp + 16 * d, v4);
+    }
+}
+
+}  // namespace m16
+}  // namespace na
