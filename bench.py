@@ -24,8 +24,9 @@ mean over the timed steps are reported; the headline value uses the medians.
 The same steps without the flush are reported beside it ("warm").
 
 Beside the headline step the same run times the KV-parallel backward variant
-on the same inputs ("kvparallel"), the headline shape with fp16 tensors
-("fp16") and the two bf16 workloads ("bf16").
+on the same inputs ("kvparallel", per kv_splits: 0 = float atomics, 1 and 4 =
+bounded accumulator copies, bitwise reproducible), the headline shape with
+fp16 tensors ("fp16") and the two bf16 workloads ("bf16").
 
 The same function is also timed through the unfused ops (the script's method
 = 'unfused': window scores, softmax, weighted sum, and their backward AGRAD,
@@ -134,9 +135,10 @@ def algorithmic_bytes(w):
 
 
 class Runner:
-    def __init__(self, w, variant, seed=0):
+    def __init__(self, w, variant, seed=0, kv_splits=0):
         self.w = w
         self.variant = variant
+        self.kv_splits = kv_splits
         dev = torch.device("cuda:0")
         log(f"[bench] generating inputs for {w.name}")
         q, k, v, dout = make_inputs(w, seed)
@@ -147,7 +149,7 @@ class Runner:
         self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
         self.delta = torch.empty_like(self.lse)
         p = na.make_problem(w.shape, w.dtype, w.kernel, w.dilation, w.the_scale)
-        ws = na.bwd_workspace_bytes(p, na.VARIANTS[variant])
+        ws = na.bwd_workspace_bytes(p, na.VARIANTS[variant], kv_splits)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.args = (w.kernel, w.dilation, w.the_scale)
 
@@ -164,7 +166,8 @@ class Runner:
 
     def bwd_kvpar(self):
         na.na_bwd(self.q, self.k, self.v, self.out, self.dout, self.lse, *self.args,
-                  variant="kvparallel", workspace=self.ws, grads=(self.dq, self.dk, self.dv))
+                  variant="kvparallel", workspace=self.ws, grads=(self.dq, self.dk, self.dv),
+                  kv_splits=self.kv_splits)
 
     def phases(self):
         if self.variant == "gather":
@@ -469,9 +472,10 @@ def main():
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8,
                                                    device="cuda:0")
 
-    def timed(wl, variant, steps, warmup):
-        r = Runner(wl, variant)
-        log(f"[bench] timing {wl.name} ({variant}): warmup {warmup}, steps {steps}")
+    def timed(wl, variant, steps, warmup, kv_splits=0):
+        r = Runner(wl, variant, kv_splits=kv_splits)
+        log(f"[bench] timing {wl.name} ({variant}, kv_splits {kv_splits}): warmup {warmup}, "
+            f"steps {steps}")
         per, wall = r.time(steps, warmup, flush)
         warm = None
         if flush is not None:
@@ -528,11 +532,17 @@ def main():
         # tensors (the maintainer's second profiled precision)
         extra = {}
         if args.variant == "gather":
+            # kv_splits 0: float atomics into one accumulator; 1 and 4: bounded copies of the
+            # accumulator, bitwise reproducible (the memory-preference cap)
             nk = min(args.steps, 2)
-            rk, extra["kvparallel"] = timed(w, "kvparallel", nk, min(args.warmup, 1))
-            extra["kvparallel"]["steps"] = nk
-            del rk
-            torch.cuda.empty_cache()
+            kvp = {}
+            for splits in (0, 1, 4):
+                rk, kvp[f"kv_splits_{splits}"] = timed(w, "kvparallel", nk, min(args.warmup, 1),
+                                                       splits)
+                kvp[f"kv_splits_{splits}"]["steps"] = nk
+                del rk
+                torch.cuda.empty_cache()
+            extra["kvparallel"] = kvp
         w16 = WORKLOADS.get(w.name.replace("_f32", "_f16"))
         if w16 is not None:
             r16, s16 = timed(w16, args.variant, args.steps, args.warmup)

@@ -133,8 +133,10 @@ constexpr int kLdsMax = 160 * 1024;
 
 // Tiling of the class grids and the LDS plan of one kernel kind; false when
 // the problem does not fit (wave count overflow or LDS).
+// h_chunks: when one plane along T of a box exceeds the LDS, cut chunks along
+// H instead (all planes of a few rows at a time).
 bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
-              na::Geometry *g, int *lds_bytes) {
+              na::Geometry *g, int *lds_bytes, int target = 0, bool h_chunks = false) {
     int64_t n_tiles = q.batch * q.heads;
     int nres = 1;
     for (int a = 0; a < 3; ++a) {
@@ -158,9 +160,11 @@ bool geometry(const Prob &q, bool inverse, int bytes_per_point, int merge_bytes,
     int mx[3];
     if (max_union(q, inverse, mx) > 32) return false;  // 32-bit validity masks
     const int64_t full = (int64_t)mx[0] * mx[1] * mx[2] * bytes_per_point;
+    if (h_chunks && g->chunk_axis == 0 && full / mx[0] > kLdsMax) g->chunk_axis = 1;
     const int64_t plane = full / mx[g->chunk_axis];
     // head_dim 64 kernels run one workgroup per CU (kSplitOccupancy): the CU's LDS
-    int64_t lds = std::min<int64_t>(full, q.head_dim >= 64 ? kLdsTargetWide : kLdsTarget);
+    if (target <= 0) target = q.head_dim >= 64 ? kLdsTargetWide : kLdsTarget;
+    int64_t lds = std::min<int64_t>(full, target);
     lds = std::max<int64_t>(lds, plane);
     lds = std::max<int64_t>(lds, merge_bytes);
     if (lds > kLdsMax) return false;
@@ -616,8 +620,44 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
 // Which kernels of the backward a call runs.
 enum Phase { kPhaseDq = 1, kPhaseDkdv = 2, kPhaseBoth = 3 };
 
+// Tile classes of the deterministic KV-parallel backward: per axis the
+// smallest m such that any two tiles m (or more) apart along it have disjoint
+// query boxes (box starts do not decrease along an axis, so checking tiles
+// exactly m apart suffices). A tile's class is its tile index modulo m per
+// axis; tiles of one class never add into the same element.
+int kv_classes(const Prob &q, int (&m)[3]) {
+    for (int a = 0; a < 3; ++a) {
+        const int tile = na::kTile[a], p = na::kPatch[a], k = q.ker[a];
+        auto box = [&](int n, int t, int *st, int *en) {
+            const int f = t * tile;
+            const int cnt = na::tile_inverse_walk(f, tile, p, n, k);
+            int ex;
+            na::query_box(f, tile, p, n, k, cnt, st, &ex);
+            *en = *st + ex;
+        };
+        m[a] = 1;
+        for (int r = 0; r < q.dil[a] && r < q.ext[a]; ++r) {
+            const int n = na::class_size(q.ext[a], q.dil[a], r), T = (n + tile - 1) / tile;
+            for (bool again = true; again;) {
+                again = false;
+                for (int t = 0; t + m[a] < T && !again; ++t) {
+                    int s0, e0, s1, e1;
+                    box(n, t, &s0, &e0);
+                    box(n, t + m[a], &s1, &e1);
+                    if (s1 < e0) {
+                        ++m[a];
+                        again = true;
+                    }
+                }
+            }
+        }
+    }
+    return m[0] * m[1] * m[2];
+}
+
 template <typename T, int D>
-na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hipStream_t s) {
+na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_splits, int phases,
+                  hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
     na::BwdArgs aq = a, ak = a;
     int lds_q = 0, lds_k = 0;
@@ -752,7 +792,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                 if (done > 0 && border_of(pr, done, &ak.g.border))
                     ak.g.n_tiles = (int)(4 * pr.batch * pr.heads * ak.g.tiles[0] *
                                          ak.g.border.per_plane);
-                auto kern = na::dkdv_kernel<T, D, false>;
+                auto kern = na::dkdv_kernel<T, D, 0>;
                 if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
                 hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
                 if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
@@ -765,6 +805,36 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
                        static_cast<const T *>(a.out), static_cast<const T *>(a.dout), a.delta,
                        pr.rows);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+    if (kv_splits > 0) {
+        // deterministic: classes of tiles with disjoint query boxes, run in rounds
+        // of kv_splits classes, each class of a round adding into its own copy of
+        // the accumulator; the copies are summed in order at the end
+        int m[3];
+        const int ncls = kv_classes(pr, m);
+        const int ncopies = std::min<int>(kv_splits, ncls);
+        const int64_t stride = (int64_t)pr.rows * D;
+        const int64_t z4 = ncopies * stride / 4;
+        hipLaunchKernelGGL(na::zero_kernel, flat_grid(z4), dim3(kThreads), 0, s, a.dq_acc, z4);
+        if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+        na::BwdArgs ad = a;
+        int lds_d = 0;
+        if (!geometry(pr, true, 2 * PB + 8 + 8 * D, na::kWaves * 64 * (D + 1) * 4, &ad.g, &lds_d,
+                      kLdsMax, true))
+            return NA_ERR_UNSUPPORTED;
+        auto kern = na::dkdv_kernel<T, D, 2>;
+        if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
+        for (int a0 = 0; a0 < 3; ++a0) ad.cls_m[a0] = m[a0];
+        ad.copy_stride = stride;
+        for (int lo = 0; lo < ncls; lo += ncopies) {
+            ad.cls_lo = lo;
+            ad.cls_n = std::min(ncopies, ncls - lo);
+            hipLaunchKernelGGL(kern, dim3(ad.g.n_tiles), dim3(na::kThreads), lds_d, s, ad);
+            if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
+        }
+        hipLaunchKernelGGL((na::dq_copies_finalize_kernel<T>), flat_grid(n4), dim3(kThreads), 0, s,
+                           a.dq_acc, ncopies, stride, static_cast<T *>(a.dq), a.scale, n4);
+        return launched();
+    }
     hipLaunchKernelGGL(na::zero_kernel, flat_grid(n4), dim3(kThreads), 0, s, a.dq_acc, n4);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
     // dq contributions summed per workgroup in LDS over its query box when the
@@ -780,7 +850,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int phases, hi
             lds_k = (int)(off + acc);
         }
     }
-    auto kern = na::dkdv_kernel<T, D, true>;
+    auto kern = na::dkdv_kernel<T, D, 1>;
     if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
     hipLaunchKernelGGL(kern, dim3(ak.g.n_tiles), dim3(na::kThreads), lds_k, s, ak);
     if (hipGetLastError() != hipSuccess) return NA_ERR_HIP;
@@ -861,13 +931,15 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     return NA_ERR_UNSUPPORTED;
 }
 
-size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant) {
+size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant, int32_t kv_splits) {
     Prob pr;
-    if (validate(p, &pr) != NA_OK) return 0;
+    if (validate(p, &pr) != NA_OK || kv_splits < 0) return 0;
     const size_t delta = round256((size_t)pr.rows * sizeof(float));
     if (variant == NA_BWD_GATHER) return delta;
-    if (variant == NA_BWD_KVPARALLEL)
-        return delta + round256((size_t)pr.rows * pr.head_dim * sizeof(float));
+    if (variant == NA_BWD_KVPARALLEL) {
+        const size_t acc = (size_t)pr.rows * pr.head_dim * sizeof(float);
+        return delta + round256(acc * (size_t)std::max(kv_splits, 1));
+    }
     return 0;
 }
 
@@ -875,8 +947,8 @@ namespace {
 
 na_status bwd_common(const na_problem *p, const void *q, const void *k, const void *v,
                      const void *out, const void *dout, const float *lse, void *dq, void *dk,
-                     void *dv, float *delta, float *dq_acc, int32_t variant, int phases,
-                     void *hip_stream) {
+                     void *dv, float *delta, float *dq_acc, int32_t variant, int32_t kv_splits,
+                     int phases, void *hip_stream) {
     Prob pr;
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
@@ -897,9 +969,9 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define NA_BWD_D(D)                                                                 \
     case D:                                                                         \
-        if (pr.dtype == NA_F32) return run_bwd<float, D>(pr, a, variant, phases, s); \
-        if (pr.dtype == NA_BF16) return run_bwd<bf16, D>(pr, a, variant, phases, s); \
-        return run_bwd<f16, D>(pr, a, variant, phases, s);
+        if (pr.dtype == NA_F32) return run_bwd<float, D>(pr, a, variant, kv_splits, phases, s); \
+        if (pr.dtype == NA_BF16) return run_bwd<bf16, D>(pr, a, variant, kv_splits, phases, s); \
+        return run_bwd<f16, D>(pr, a, variant, kv_splits, phases, s);
     switch (pr.head_dim) { NA_BWD_D(16) NA_BWD_D(32) NA_BWD_D(64) }
 #undef NA_BWD_D
     return NA_ERR_UNSUPPORTED;
@@ -916,12 +988,13 @@ bool ptrs_ok(std::initializer_list<const void *> ptrs) {
 na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *v,
                  const void *out, const void *dout, const float *lse, void *dq, void *dk,
                  void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
-                 void *hip_stream) {
+                 int32_t kv_splits, void *hip_stream) {
     na_status st = validate(p, nullptr);
     if (st != NA_OK) return st;
     if (variant != NA_BWD_GATHER && variant != NA_BWD_KVPARALLEL) return NA_ERR_INVALID_ARG;
+    if (kv_splits < 0) return NA_ERR_INVALID_ARG;
     if (!ptrs_ok({q, k, v, out, dout, lse, dq, dk, dv})) return NA_ERR_INVALID_ARG;
-    const size_t need = na_bwd_workspace_bytes(p, variant);
+    const size_t need = na_bwd_workspace_bytes(p, variant, kv_splits);
     if (!workspace || workspace_bytes < need) return NA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NA_ERR_WORKSPACE;
     Prob pr;
@@ -931,8 +1004,8 @@ na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *
                         ? reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                                     round256((size_t)pr.rows * sizeof(float)))
                         : nullptr;
-    return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, dq_acc, variant, kPhaseBoth,
-                      hip_stream);
+    return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, dq_acc, variant, kv_splits,
+                      kPhaseBoth, hip_stream);
 }
 
 na_status na_bwd_dq(const na_problem *p, const void *q, const void *k, const void *v,
@@ -942,7 +1015,7 @@ na_status na_bwd_dq(const na_problem *p, const void *q, const void *k, const voi
     if (st != NA_OK) return st;
     if (!ptrs_ok({q, k, v, out, dout, lse, dq, delta})) return NA_ERR_INVALID_ARG;
     return bwd_common(p, q, k, v, out, dout, lse, dq, nullptr, nullptr, delta, nullptr,
-                      NA_BWD_GATHER, kPhaseDq, hip_stream);
+                      NA_BWD_GATHER, 0, kPhaseDq, hip_stream);
 }
 
 na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const void *v,
@@ -952,7 +1025,7 @@ na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const v
     if (st != NA_OK) return st;
     if (!ptrs_ok({q, k, v, dout, lse, delta, dk, dv})) return NA_ERR_INVALID_ARG;
     return bwd_common(p, q, k, v, nullptr, dout, lse, nullptr, dk, dv, const_cast<float *>(delta),
-                      nullptr, NA_BWD_GATHER, kPhaseDkdv, hip_stream);
+                      nullptr, NA_BWD_GATHER, 0, kPhaseDkdv, hip_stream);
 }
 
 }  // extern "C"
@@ -1001,7 +1074,7 @@ na_status na_bwd_noalloc(const na_problem *p, const void *q, const void *k, cons
     if (!delta) return NA_ERR_HIP;
     // delta is written in full by the dq kernel before dk/dv reads it: nothing
     // needs clearing between calls
-    return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, NA_BWD_GATHER,
+    return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, nullptr, NA_BWD_GATHER, 0,
                       kPhaseBoth, hip_stream);
 }
 

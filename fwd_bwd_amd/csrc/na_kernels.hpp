@@ -58,7 +58,19 @@ struct BwdArgs {
     // inverse walk of at most skip_ch x skip_cw patches (the register-resident
     // dk/dv kernel covers those)
     int skip_ch, skip_cw;
+    // KV-parallel with bounded copies: this launch runs the tiles of classes
+    // [cls_lo, cls_lo + cls_n); a tile's class is its tile index along each
+    // axis modulo cls_m (tiles of one class have disjoint query boxes), and
+    // it adds its box into copy (class - cls_lo), copy_stride floats apart
+    int cls_lo, cls_n, cls_m[3];
+    int64_t copy_stride;
 };
+
+// dq contributions of a KV-parallel workgroup are summed exactly in LDS as
+// 64-bit fixed point with 32 fraction bits: integer additions do not depend on
+// their order, so the sums are the same on every run (|partial sums| < 2^31).
+constexpr float kFixOne = 4294967296.0f;  // 2^32
+constexpr float kFixInv = 1.0f / 4294967296.0f;
 
 // Workgroups per CU the split kernels are compiled for: at head_dim 64 the
 // per-lane rows and accumulators need more than the 256 registers of two
@@ -540,17 +552,31 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
 }
 
 // ============================================================================
-// Backward, key side: dk and dv by inverse-neighborhood gather. With KVPAR the
-// same pass also produces each query's dq contributions from this tile's keys
-// and adds them into the fp32 accumulator dq_acc.
+// Backward, key side: dk and dv by inverse-neighborhood gather. MODE 0: only
+// that. MODE 1 (KV-parallel): the same pass also produces each query's dq
+// contributions from this tile's keys and adds them into the fp32 accumulator
+// dq_acc with float atomics (not bitwise reproducible). MODE 2 (KV-parallel,
+// deterministic): the contributions of each staged chunk of the query box are
+// summed exactly in LDS (fixed point), then added with plain stores into the
+// tile's class copy of the accumulator; no two tiles of one launch touch the
+// same element of a copy.
 // The KV-parallel pass keeps the block's keys for dq besides everything else
 // and, with its LDS dq accumulator, runs one workgroup per CU anyway.
-template <typename T, int D, bool KVPAR>
-__global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv_kernel(BwdArgs a) {
+template <typename T, int D, int MODE>
+__global__ void __launch_bounds__(kThreads, MODE != 0 ? 1 : kSplitOccupancy<D>) dkdv_kernel(BwdArgs a) {
     extern __shared__ __align__(16) char smem[];
+    constexpr bool KVPAR = MODE != 0;
     constexpr int G = D / 4, PB = D * (int)sizeof(T), NC = PB / 16;
     TileCtx w;
     if (!decode_tile(a.g, xcd_tile_id(blockIdx.x, a.g.n_tiles), w)) return;
+    float *copy = nullptr;
+    if constexpr (MODE == 2) {
+        const int cls = ((w.o[0] / kTile[0]) % a.cls_m[0] * a.cls_m[1] +
+                         (w.o[1] / kTile[1]) % a.cls_m[1]) * a.cls_m[2] +
+                        (w.o[2] / kTile[2]) % a.cls_m[2];
+        if (cls < a.cls_lo || cls >= a.cls_lo + a.cls_n) return;
+        copy = a.dq_acc + (int64_t)(cls - a.cls_lo) * a.copy_stride;
+    }
     if (a.skip_ch > 0) {
         const int o1 = w.o[1] & ~15, o2 = w.o[2] & ~15;
         if (tile_inverse_walk(o1, 16, 2, w.n[1], w.k[1]) <= a.skip_ch &&
@@ -605,7 +631,7 @@ __global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv
     // added to the global accumulator once per point and channel. Zeroed here;
     // the barrier of the first staging orders it before any addition.
     float *qacc = nullptr;
-    if constexpr (KVPAR) {
+    if constexpr (MODE == 1) {
         if (a.g.dq_lds_off > 0) {
             qacc = reinterpret_cast<float *>(smem + a.g.dq_lds_off);
             const int n = U.e[0] * U.e[1] * U.e[2] * (D + 1);
@@ -615,14 +641,20 @@ __global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv
 
     ChunkView cv;
     cv.A = a.g.chunk_axis;
-    const int rows = chunk_rows(U, cv.A, 2 * PB + 8, a.g.lds_budget);
+    // MODE 2 keeps a 64-bit accumulator per point and channel of the chunk
+    const int rows = chunk_rows(U, cv.A, 2 * PB + 8 + (MODE == 2 ? 8 * D : 0), a.g.lds_budget);
     cv.chunked = rows < get3(U.e, cv.A);
     for (int r0 = 0; r0 < get3(U.e, cv.A); r0 += rows) {
         const Box C = chunk_of(U, cv.A, r0, rows);
         const int np = C.e[0] * C.e[1] * C.e[2];
         char *Qs = smem, *Os = smem + np * PB;
         float2 *Rs = reinterpret_cast<float2 *>(smem + 2 * np * PB);
+        unsigned long long *fix = reinterpret_cast<unsigned long long *>(smem + 2 * np * PB + 8 * np);
         if (r0 > 0) __syncthreads();
+        if constexpr (MODE == 2) {
+            // the barrier of this chunk's staging orders the clearing before any addition
+            for (int i = threadIdx.x; i < np * D; i += kThreads) fix[i] = 0ull;
+        }
         stage_box<T, D>(static_cast<const T *>(a.q), w, C, Qs);
         stage_box<T, D>(static_cast<const T *>(a.dout), w, C, Os);
         stage_rows(a.lse, a.delta, w, C, Rs);
@@ -718,7 +750,19 @@ __global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv
                                    lo[2] + 2 * it.c2 + (c & 1)};
                 const bool inside = qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2] &&
                                     ((cm >> c) & 1);
-                if (inside && qacc) {
+                if constexpr (MODE == 2) {
+                    if (inside) {
+                        unsigned long long *fp =
+                            fix + (((qq[0] - C.o[0]) * C.e[1] + (qq[1] - C.o[1])) * C.e[2] +
+                                   (qq[2] - C.o[2])) * D;
+#pragma unroll
+                        for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+                            for (int g = 0; g < G; ++g)
+                                atomicAdd(fp + i2 * G + g,
+                                          (unsigned long long)__float2ll_rn(dq[g][i2] * kFixOne));
+                    }
+                } else if (inside && qacc) {
                     float *ap = qacc + (((qq[0] - U.o[0]) * U.e[1] + (qq[1] - U.o[1])) * U.e[2] +
                                         (qq[2] - U.o[2])) * (D + 1);
 #pragma unroll
@@ -734,9 +778,23 @@ __global__ void __launch_bounds__(kThreads, KVPAR ? 1 : kSplitOccupancy<D>) dkdv
                 }
             }
         }
+        if constexpr (MODE == 2) {
+            // the chunk's exact sums into the tile's copy, one thread per element
+            __syncthreads();
+            const int plane = C.e[1] * C.e[2];
+            for (int i = threadIdx.x; i < np * D; i += kThreads) {
+                const int pt = i / D, d = i - pt * D;
+                const int z = pt / plane, r = pt - z * plane, y = r / C.e[2], x = r - y * C.e[2];
+                const int qq[3] = {C.o[0] + z, C.o[1] + y, C.o[2] + x};
+                if (qq[0] < w.n[0] && qq[1] < w.n[1] && qq[2] < w.n[2]) {
+                    float *dst = copy + elem_off(w, qq) + d;
+                    *dst += (float)(long long)fix[i] * kFixInv;
+                }
+            }
+        }
     }
 
-    if constexpr (KVPAR) {
+    if constexpr (MODE == 1) {
         if (qacc) {
             // the box's sums into the global accumulator (points past the grid
             // never received any)
@@ -816,6 +874,26 @@ __global__ void __launch_bounds__(256) delta_kernel(const T *out, const T *dout,
 __global__ void __launch_bounds__(256) zero_kernel(float *p, int64_t n4) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n4) reinterpret_cast<float4 *>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// dq = scale * (copy 0 + copy 1 + ... + copy n-1), summed in that order, cast
+// to the tensor type; four elements per thread.
+template <typename T>
+__global__ void __launch_bounds__(256) dq_copies_finalize_kernel(const float *acc, int ncopies,
+                                                                 int64_t stride, T *dq, float scale,
+                                                                 int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < ncopies; ++c) {
+        float x[4];
+        Io<float>::load4(acc + c * stride + 4 * i, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= scale;
+    Io<T>::store4(dq + 4 * i, v);
 }
 
 // dq = scale * dq_acc, cast to the tensor type, four elements per thread.

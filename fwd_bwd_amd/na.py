@@ -82,10 +82,10 @@ def load() -> ctypes.CDLL:
         lib.na_check_problem.restype = ctypes.c_int
         lib.na_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
         lib.na_fwd.restype = ctypes.c_int
-        lib.na_bwd_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        lib.na_bwd_workspace_bytes.argtypes = [P, ctypes.c_int32, ctypes.c_int32]
         lib.na_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.na_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                               ctypes.c_int32, vp]
+                               ctypes.c_int32, ctypes.c_int32, vp]
         lib.na_bwd.restype = ctypes.c_int
         lib.na_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.na_bwd_dq.restype = ctypes.c_int
@@ -223,23 +223,27 @@ def na_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kernel_size, dilat
     return out, lse
 
 
-def bwd_workspace_bytes(p: NaProblem, variant: int) -> int:
-    return int(load().na_bwd_workspace_bytes(ctypes.byref(p), variant))
+def bwd_workspace_bytes(p: NaProblem, variant: int, kv_splits: int = 0) -> int:
+    return int(load().na_bwd_workspace_bytes(ctypes.byref(p), variant, kv_splits))
 
 
 def na_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
            dout: torch.Tensor, lse: torch.Tensor, kernel_size, dilation=1,
            scale: Optional[float] = None, variant: str = "gather",
            workspace: Optional[torch.Tensor] = None,
-           grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
-           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Fused NA backward of sum(out * dout). Returns (dq, dk, dv)."""
+           grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+           kv_splits: int = 0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Fused NA backward of sum(out * dout). Returns (dq, dk, dv). kv_splits
+    (KV-parallel only): 0 = float atomics into one accumulator; S >= 1 = at most
+    S accumulator copies, bitwise reproducible."""
     _check_tensors(q, k, v, out, dout)
     if lse.dtype != torch.float32 or lse.shape != q.shape[:-1] or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 tensor of shape q.shape[:-1]")
     p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
     vid = VARIANTS[variant]
-    need = bwd_workspace_bytes(p, vid)
+    if kv_splits < 0:
+        raise ValueError("kv_splits must be >= 0")
+    need = bwd_workspace_bytes(p, vid, kv_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, need, q.device)
@@ -250,7 +254,7 @@ def na_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         _check_buf(g, name, q.shape, q.dtype, q.device)
     _check(load().na_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), vid,
+                         workspace.numel() * workspace.element_size(), vid, kv_splits,
                          _stream_handle(q.device)))
     return dq, dk, dv
 

@@ -76,13 +76,23 @@ typedef enum {
 } na_dtype;
 
 /* Backward strategies (the NATTEN issue's use_kv_parallelism_in_fused_na
- * switch selects between query-parallel and KV-parallel fused backwards). */
+ * switch selects between query-parallel and KV-parallel fused backwards; its
+ * set_memory_usage_preference caps how far KV parallelism may go, here the
+ * kv_splits argument of na_bwd). */
 typedef enum {
     NA_BWD_GATHER = 0,     /* dq by query tiles, then dk/dv by key tiles over the
                               inverse neighborhood; no atomics, deterministic */
     NA_BWD_KVPARALLEL = 1  /* one pass over key tiles producing dk, dv and fp32
                               partial sums of dq in the workspace; dq is then
-                              finalized; uses atomics, not bitwise deterministic */
+                              finalized. kv_splits = 0: one accumulator, float
+                              atomics, not bitwise reproducible. kv_splits = S
+                              >= 1: at most S accumulator copies; each key tile
+                              sums its contributions exactly (64-bit fixed point,
+                              32 fraction bits, partial sums below 2^31 in
+                              magnitude) and adds them to one copy with plain
+                              stores, tiles of one copy never overlapping within
+                              a launch (tile classes run in rounds of S); the
+                              copies are summed in order: bitwise reproducible */
 } na_bwd_variant;
 
 typedef struct {
@@ -106,20 +116,22 @@ na_status na_check_problem(const na_problem *p);
 na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *v, void *out,
                  float *lse, void *hip_stream);
 
-/* Bytes of device workspace na_bwd needs for the given variant (0 on an
- * invalid problem or variant). NA_BWD_GATHER: the fp32 delta array
- * [B,(T,)H,W,heads]. NA_BWD_KVPARALLEL: delta plus an fp32 dq accumulator
- * [B,(T,)H,W,heads,head_dim]. Each region starts 256-byte aligned. */
-size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant);
+/* Bytes of device workspace na_bwd needs for the given variant and kv_splits
+ * (0 on an invalid problem, variant or a negative kv_splits). NA_BWD_GATHER:
+ * the fp32 delta array [B,(T,)H,W,heads] (kv_splits ignored).
+ * NA_BWD_KVPARALLEL: delta plus max(kv_splits, 1) fp32 dq accumulators
+ * [B,(T,)H,W,heads,head_dim] back to back. Regions start 256-byte aligned. */
+size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant, int32_t kv_splits);
 
 /* Backward of sum(out * dout): dq, dk, dv (problem dtype) from q, k, v, the
  * forward's out and lse, and dout. workspace must be a device buffer of at
- * least na_bwd_workspace_bytes(p, variant) bytes, 256-byte aligned; its
- * contents on entry do not matter and are left undefined. */
+ * least na_bwd_workspace_bytes(p, variant, kv_splits) bytes, 256-byte
+ * aligned; its contents on entry do not matter and are left undefined.
+ * kv_splits (>= 0; see na_bwd_variant) only matters for NA_BWD_KVPARALLEL. */
 na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *v,
                  const void *out, const void *dout, const float *lse, void *dq, void *dk,
                  void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
-                 void *hip_stream);
+                 int32_t kv_splits, void *hip_stream);
 
 /* The two halves of the NA_BWD_GATHER backward, for callers that want one of
  * the gradients alone or time the kernels separately. na_bwd with

@@ -106,10 +106,13 @@ def test_fwd_bwd_reject_null_pointers_before_launch(lib):
     for i in range(9):
         a = list(bargs)
         a[i] = None
-        assert lib.na_bwd(ctypes.byref(p), *a, fake, ws, 0, None) == na.NA_ERR_INVALID_ARG
-    assert lib.na_bwd(ctypes.byref(p), *bargs, None, ws, 0, None) == na.NA_ERR_WORKSPACE
-    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws - 1, 0, None) == na.NA_ERR_WORKSPACE
-    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws, 5, None) == na.NA_ERR_INVALID_ARG
+        assert lib.na_bwd(ctypes.byref(p), *a, fake, ws, 0, 0, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_bwd(ctypes.byref(p), *bargs, None, ws, 0, 0, None) == na.NA_ERR_WORKSPACE
+    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws - 1, 0, 0, None) == na.NA_ERR_WORKSPACE
+    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, ws, 5, 0, None) == na.NA_ERR_INVALID_ARG
+    # a KV-parallel workspace grows with kv_splits
+    wk = na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL, 3)
+    assert lib.na_bwd(ctypes.byref(p), *bargs, fake, wk - 1, 1, 3, None) == na.NA_ERR_WORKSPACE
     bad = _p(kernel=(3, 19))
     assert lib.na_fwd(ctypes.byref(bad), *args, None) == na.NA_ERR_INVALID_ARG
 
@@ -225,3 +228,22 @@ def test_noalloc_rejects_problems_beyond_its_array(lib):
     assert na.check_problem(p) == na.NA_OK
     bad = [ctypes.byref(p)] + [fake] * 8 + [None, None]   # dv missing
     assert lib.na_bwd_noalloc(*bad) == na.NA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes_per_variant_and_copies(lib):
+    """Gather: the delta rows; KV-parallel: delta plus max(kv_splits, 1) fp32
+    accumulators, each region 256-byte aligned; a negative kv_splits is 0."""
+    p = _p(shape=(2, 13, 17, 3, 32), kernel=(3, 5))
+    rows = 2 * 13 * 17 * 3
+    r256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    delta, acc = r256(rows * 4), rows * 32 * 4
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_GATHER, 0) == delta
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_GATHER, 5) == delta
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL, 0) == delta + r256(acc)
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL, 1) == delta + r256(acc)
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL, 4) == delta + r256(4 * acc)
+    assert na.bwd_workspace_bytes(p, na.NA_BWD_KVPARALLEL, -1) == 0
+    fake = ctypes.c_void_p(4096)
+    args = [ctypes.byref(p)] + [fake] * 9 + [fake, ctypes.c_size_t(1 << 40), na.NA_BWD_KVPARALLEL,
+                                             -1, None]
+    assert lib.na_bwd(*args) == na.NA_ERR_INVALID_ARG

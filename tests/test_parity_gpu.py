@@ -50,11 +50,18 @@ def np64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+# backward variants under test: (na_bwd variant, kv_splits); "kvdet" is the
+# KV-parallel backward with bounded, bitwise-reproducible accumulator copies
+VARIANTS = {"gather": ("gather", 0), "kvparallel": ("kvparallel", 0), "kvdet": ("kvparallel", 2)}
+
+
 def gpu_run(q, k, v, dout, kernel, dil, scale, variant="gather"):
     dev = torch.device("cuda:0")
     qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
     out, lse = na.na_fwd(qd, kd, vd, kernel, dil, scale)
-    dq, dk, dv = na.na_bwd(qd, kd, vd, out, dd, lse, kernel, dil, scale, variant=variant)
+    var, splits = VARIANTS[variant]
+    dq, dk, dv = na.na_bwd(qd, kd, vd, out, dd, lse, kernel, dil, scale, variant=var,
+                           kv_splits=splits)
     torch.cuda.synchronize()
     return {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
@@ -143,7 +150,7 @@ def _id(c):
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
-@pytest.mark.parametrize("variant", ["gather", "kvparallel"])
+@pytest.mark.parametrize("variant", ["gather", "kvparallel", "kvdet"])
 def test_small_cases_match_oracle(case, variant):
     shape, kernel, dil, dtype = case
     say("case", _id(case), variant)
@@ -199,6 +206,26 @@ def test_kvparallel_matches_gather():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert rel_err(np64(x), np64(y)) < 1e-5
+
+
+@pytest.mark.parametrize("case", [((1, 40, 37, 2, 32), (9, 9), 1, torch.float32),
+                                  ((1, 5, 21, 19, 2, 32), (3, 5, 5), 1, torch.float32),
+                                  ((2, 26, 27, 2, 64), (5, 5), 2, torch.bfloat16)],
+                         ids=lambda c: _id(c))
+def test_kvparallel_with_copies_is_bitwise_reproducible(case):
+    """kv_splits >= 1: exact per-tile sums and ordered copies give the same
+    bits on every run, for any number of copies, and match the gather."""
+    shape, kernel, dil, dtype = case
+    q, k, v, dout = (t.cuda() for t in make_random(shape, dtype, seed=16))
+    out, lse = na.na_fwd(q, k, v, kernel, dil)
+    ref = na.na_bwd(q, k, v, out, dout, lse, kernel, dil)
+    for splits in (1, 3, 64):
+        a = na.na_bwd(q, k, v, out, dout, lse, kernel, dil, variant="kvparallel", kv_splits=splits)
+        b = na.na_bwd(q, k, v, out, dout, lse, kernel, dil, variant="kvparallel", kv_splits=splits)
+        torch.cuda.synchronize()
+        for name, x, y, r in zip(("dq", "dk", "dv"), a, b, ref):
+            assert torch.equal(x, y), (splits, name)
+            assert rel_err(np64(x), np64(r)) <= TOL[dtype], (splits, name)
 
 
 def test_autograd_wrapper():
@@ -259,12 +286,15 @@ FULL = ["2d_1024x1024_k9_h8_d32_f32", "3d_16x256x256_k3x5x5_h8_d32_f32",
         "2d_1024x1024_k9_h8_d32_f16", "3d_16x256x256_k3x5x5_h8_d32_f16"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_workload_sampled(name):
+FULL_CASES = [(n, "gather") for n in FULL] + [("2d_1024x1024_k9_h8_d32_f32", "kvdet")]
+
+
+@pytest.mark.parametrize("name,variant", FULL_CASES, ids=[f"{n}-{v}" for n, v in FULL_CASES])
+def test_full_workload_sampled(name, variant):
     w = WORKLOADS[name]
-    say("full workload", name)
+    say("full workload", name, variant)
     q, k, v, dout = make_inputs(w, seed=0)
-    got = gpu_run(q, k, v, dout, w.kernel, w.dilation, w.the_scale)
+    got = gpu_run(q, k, v, dout, w.kernel, w.dilation, w.the_scale, variant)
     sel = sample_units(w)
     D = w.head_dim
     args = [np64(t) for t in (q, k, v)]
