@@ -504,8 +504,8 @@ struct M16Plan {
 // Columns a slab row must hold: the end of the last block any wave of any
 // 16-column tile walks, relative to its tile's box start (the same formulas
 // the kernels evaluate), rounded to groups of four.
-int m16_box_w(const Prob &q, bool inverse) {
-    int bw = 4;
+int m16_box_w(const Prob &q, bool inverse, int *max_blocks = nullptr) {
+    int bw = 4, mb = 1;
     const int k = q.ker[2];
     for (int r = 0; r < q.dil[2] && r < q.ext[2]; ++r) {
         const int n = na::class_size(q.ext[2], q.dil[2], r);
@@ -519,9 +519,11 @@ int m16_box_w(const Prob &q, bool inverse) {
                 const int aw = (s0 - U2) & ~3;
                 const int nbw = (e1 - U2 - aw + 3) >> 2;
                 bw = std::max(bw, aw + 4 * nbw);
+                mb = std::max(mb, nbw);
             }
         }
     }
+    if (max_blocks) *max_blocks = mb;
     return bw;
 }
 
@@ -551,10 +553,11 @@ bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
     g.box_w = m16_box_w(q, kind == 2);
     const int NC = (int)q.head_dim * 2 / 16;
     g.km_pitch = ((g.box_w * NC) | 1) * 16;                 // odd number of 16-byte chunks
-    g.tr_pitch = g.box_w * 2 * (int)q.head_dim + 128;       // 128 bytes off a multiple of 256
-    const int64_t lds = kind == 0   ? 4LL * g.km_pitch + 4LL * g.tr_pitch
-                        : kind == 1 ? 8LL * g.km_pitch + 4LL * g.tr_pitch
-                                    : 8LL * g.km_pitch + 8LL * g.tr_pitch + 32LL * g.box_w;
+    // transposed slab: one column of four rows per 8 * head_dim + 128 bytes
+    g.tr_pitch = g.box_w * (8 * (int)q.head_dim + 128);
+    const int64_t lds = kind == 0   ? 4LL * g.km_pitch + g.tr_pitch
+                        : kind == 1 ? 8LL * g.km_pitch + g.tr_pitch
+                                    : 8LL * g.km_pitch + 2LL * g.tr_pitch + 32LL * g.box_w;
     if (lds > kLdsMax) return false;
     pl->lds = (int)lds;
     g.f_heads = na::make_fastdiv(g.heads);

@@ -25,19 +25,22 @@
 //  * A (16 x 32) and B (32 x 16) operands: lane l holds row / column n and
 //    reduction entries 8g .. 8g + 7; result C (16 x 16): lane l holds rows
 //    4g .. 4g + 3 of column n.
-//  * Scores are formed transposed, S^T = K Q^T: A = a 4 x 4 key block (key n at
-//    block row n / 4, column n % 4, channels from LDS), B = the wave's queries
-//    (registers). Lane l then holds the scores of query n against the keys of
-//    block row g, columns 0..3 -- exactly the B operand a weighted sum over a
-//    pair of blocks needs when its reduction entries 8g .. 8g + 3 are block
-//    row g of the first block and 8g + 4 .. 8g + 7 block row g of the second:
-//    O^T += V^T P^T with A = V^T read as four keys at one channel.
+//  * A block is 4 slab rows by 4 columns; its point m sits at row m % 4,
+//    column m / 4. Scores are formed transposed, S^T = K Q^T: A = a key block
+//    (point n's channels from LDS), B = the wave's queries (registers). Lane l
+//    then holds the scores of query n against column g of the block, rows
+//    0..3 -- exactly the B operand of a weighted sum over a pair of blocks
+//    whose reduction entries 8g .. 8g + 3 are column g of the first block and
+//    8g + 4 .. 8g + 7 column g of the second: O^T += V^T P^T, with A = V^T
+//    read as the four rows of one column at one channel. One lane's four
+//    scores share their column: the window test along W is one compare per
+//    block, the test along H one per slab row.
 //  * LDS: "key-major" slabs hold each point's channels contiguously (16-byte
 //    chunks, XOR-swizzled at 64 channels, odd row pitch in chunks: the A reads
-//    of 16 keys at one chunk hit 16 different bank groups); "transposed" slabs
-//    hold each group of four W-consecutive points as channel-major 8-byte
-//    entries (4 points x 16 bits), rows 128 bytes off a multiple of 256, so the
-//    two 8-byte reads of an A operand come from 64 different banks.
+//    of 16 points at one chunk hit 16 different bank groups); "transposed"
+//    slabs hold, per column and channel, the 8 bytes of the column's four rows,
+//    columns 128 bytes off a multiple of 256 apart, so the 8-byte reads of an
+//    A operand come from 64 different banks.
 //  * Row sums of the weights come out of the MFMA as well: one more product
 //    against an all-ones A operand gives every lane the sum for its query.
 //
@@ -106,7 +109,7 @@ struct Geom {
     int nres, n_tiles;
     int box_w;     // points per slab row (a multiple of 4)
     int km_pitch;  // bytes per slab row, key-major layout
-    int tr_pitch;  // bytes per slab row, transposed layout
+    int tr_pitch;  // bytes of a transposed slab (all four rows)
     FastDiv f_heads, f_tw, f_th, f_t, f_nres;
     FastDiv f_dil[3], f_dil21;
 };
@@ -217,79 +220,75 @@ __device__ __forceinline__ void stage_km(const T *src, const TileCtx &w, int tk,
     }
 }
 
-// Transposed slab: the same points, each group of four W-consecutive points
-// (columns 4G .. 4G + 3) stored channel-major: channel d of the group is the
-// 8 bytes at lds + r * pitch + G * 8 * D + 8 * d (the four points' values in
-// column order). Staged through registers: a thread loads one 16-byte chunk
-// (8 channels) of each of the four points and writes 64 bytes.
+// Transposed slab: channel-major by slab column. Column w of the slab holds,
+// for each channel d, the 8 bytes of its four rows (row 0 first) at
+// lds + w * tr_col<D>() + 8 * d. Columns are 8 * D + 128 bytes apart (128 off
+// a multiple of 256), so the two lane groups of a half wave, reading
+// neighbouring columns, hit different banks. Staged through registers: a
+// thread loads one 16-byte chunk (8 channels) of each of the column's four
+// rows and writes 64 bytes.
+template <int D>
+__device__ __forceinline__ constexpr int tr_col() {
+    return 8 * D + 128;
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void stage_tr(const T *src, const TileCtx &w, int tk, int r0, int U2,
-                                         int box_w, int pitch, char *lds) {
+                                         int box_w, char *lds) {
     constexpr int NC = D * 2 / 16;
-    const int groups = box_w >> 2;
-    const int tasks = 4 * groups * NC;
+    const int tasks = box_w * NC;
+    const int rows[4] = {imin(r0, w.n[1] - 1), imin(r0 + 1, w.n[1] - 1), imin(r0 + 2, w.n[1] - 1),
+                         imin(r0 + 3, w.n[1] - 1)};
     for (int t = threadIdx.x; t < tasks; t += kThreads) {
-        const int c = t % NC;
-        const int rg = t / NC;
-        const int G = rg % groups, r = rg / groups;
-        const int c1 = imin(r0 + r, w.n[1] - 1);
-        const T *rowp = src + eoff<D>(w, tk, c1, 0) + c * 8;
+        const int c = t % NC, col = t / NC;
+        const int c2 = imin(U2 + col, w.n[2] - 1);
         uint4 x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c2 = imin(U2 + 4 * G + j, w.n[2] - 1);
-            x[j] = *reinterpret_cast<const uint4 *>(rowp + (int64_t)c2 * w.lst[2] * D);
-        }
-        char *dst = lds + r * pitch + G * 8 * D + c * 64;
+        for (int r = 0; r < 4; ++r)
+            x[r] = *reinterpret_cast<const uint4 *>(src + eoff<D>(w, tk, rows[r], c2) + c * 8);
+        char *dst = lds + col * tr_col<D>() + c * 64;
         const uint32_t a0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
         const uint32_t a1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
         const uint32_t a2[4] = {x[2].x, x[2].y, x[2].z, x[2].w};
         const uint32_t a3[4] = {x[3].x, x[3].y, x[3].z, x[3].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 o;
-            o.x = (a0[i] & 0xffffu) | (a1[i] << 16);
-            o.y = (a2[i] & 0xffffu) | (a3[i] << 16);
-            o.z = (a0[i] >> 16) | (a1[i] & 0xffff0000u);
-            o.w = (a2[i] >> 16) | (a3[i] & 0xffff0000u);
-            *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
+        for (int e = 0; e < 4; ++e) {
+            uint4 o;  // channels 2e and 2e + 1, rows 0..3 each
+            o.x = (a0[e] & 0xffffu) | (a1[e] << 16);
+            o.y = (a2[e] & 0xffffu) | (a3[e] << 16);
+            o.z = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+            o.w = (a2[e] >> 16) | (a3[e] & 0xffff0000u);
+            *reinterpret_cast<uint4 *>(dst + 16 * e) = o;
         }
     }
 }
 
-// (logsumexp * log2(e), delta) of every point of a slab, as float2 at
-// rows[r * box_w + col].
+// (logsumexp * log2(e), delta) of every point of a slab, column-major: the
+// four rows of column w at rows[4 w .. 4 w + 3].
 __device__ __forceinline__ void stage_rows16(const float *lse, const float *delta,
                                              const TileCtx &w, int tk, int r0, int U2, int box_w,
                                              float2 *rows) {
     for (int i = threadIdx.x; i < 4 * box_w; i += kThreads) {
-        const int r = i / box_w, col = i - r * box_w;
+        const int col = i >> 2, r = i & 3;
         const int64_t ro = roff(w, tk, imin(r0 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1));
         rows[i] = make_float2(lse[ro] * kLog2e, delta[ro]);
     }
 }
 
-// A operand of the S^T (or S) MFMA: point n of the block at column `col0` of
-// the key-major slab, chunk `ch` (channels 8 ch .. 8 ch + 7).
-template <int NC>
-__device__ __forceinline__ uint4 km_read(const char *lds, int pitch, int n, int col0, int ch) {
-    const int row = n >> 2, col = col0 + (n & 3);
-    return *reinterpret_cast<const uint4 *>(lds + row * pitch + ((col * NC + (ch ^ kswz<NC>(col))) << 4));
-}
-
-// A operand of a weighted sum over blocks at group columns G0, G1 (block
-// columns / 4) of the transposed slab: channel d, slab row g (lane group).
-template <int D>
-__device__ __forceinline__ uint4 tr_read(const char *lds, int pitch, int g, int G0, int G1, int d) {
-    const char *base = lds + g * pitch + 8 * d;
-    const uint2 a = *reinterpret_cast<const uint2 *>(base + G0 * 8 * D);
-    const uint2 b = *reinterpret_cast<const uint2 *>(base + G1 * 8 * D);
-    return make_uint4(a.x, a.y, b.x, b.y);
-}
-
+// Maximum and sum over the four lanes n, n + 16, n + 32, n + 48 (the lane
+// groups holding one query's scores): each lane swap returns the lane's own
+// value and that of its partner (lane ^ 32, then lane ^ 16), VALU only.
 __device__ __forceinline__ float xmax4(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum4(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // The lane's point of the wave's patch: patch origin (class) + (n / 4, n % 4).
@@ -305,6 +304,46 @@ __device__ __forceinline__ Pt patch_point(const TileCtx &w, int wave, int n) {
     p.w = imin(c, w.n[2] - 1);
     return p;
 }
+
+// Per-lane LDS addressing of the A operands. A block of 16 points is four
+// slab rows by four columns [col0, col0 + 4) (col0 a multiple of 4), point m
+// at row m % 4, column col0 + m / 4; so lane group g of an MFMA result holds
+// column col0 + g, one row per register.
+//  * key-major: lane n supplies point n, chunk (lg + 4h): base km(h) plus
+//    col0 * NC * 16 (the swizzle only depends on the column within the block);
+//  * transposed: lane (g, n) supplies channel n + 16 d of column col0 + g
+//    (block one of a pair) or col0 + 4 + g (block two): base tr plus
+//    col0 * tr_col, channel blocks 128 bytes apart.
+template <int D>
+struct LaneAddr {
+    static constexpr int NC = D * 2 / 16, NH = D / 32;
+    int km[NH];
+    int tr;
+    __device__ __forceinline__ LaneAddr(int km_pitch, int lg, int n) {
+        const int col = n >> 2, row = n & 3;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            km[h] = row * km_pitch + ((col * NC + ((lg + 4 * h) ^ kswz<NC>(col))) << 4);
+        tr = lg * tr_col<D>() + 8 * n;
+    }
+};
+
+__device__ __forceinline__ uint4 km_at(const char *lds, int addr) {
+    return *reinterpret_cast<const uint4 *>(lds + addr);
+}
+
+// A operand of a weighted sum over a pair of blocks: channel 16 d + n of the
+// lane group's column in block one (t0) and block two (t1).
+__device__ __forceinline__ uint4 tr_at(const char *t0, const char *t1, int d) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(t0 + 128 * d);
+    const uint2 b = *reinterpret_cast<const uint2 *>(t1 + 128 * d);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Weights are rescaled only when a score exceeds the running maximum by more
+// than this (log2 units): weights then stay below 2^8, harmless in fp32 sums
+// and in the 16-bit operands, and the rescale is rare.
+constexpr float kLazyRescale = 8.f;
 
 // ============================================================================
 // Forward: out, lse.
@@ -335,20 +374,30 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
 
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
-    const int ww = window_start(P.w, nw, w.k[2]) - U2;  // relative to the box
+    // column of this lane group in a block relative to the lane's window start
+    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - U2);
+    // scores are kept unscaled; a negative scale flips the query's sign instead.
+    // A zero scale becomes the tiniest normal one (every weight still exp2(0)
+    // in fp32), so that masked scores (-inf) times it stay -inf.
+    const bool neg = a.qscale < 0.f;
+    const float c = fmaxf(neg ? -a.qscale : a.qscale, 1.1754944e-38f);
     uint4 qv[NH];
     {
         const T *qp = a.q + eoff<D>(w, w.o[0], P.h, P.w) + 8 * lg;
+        const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) qv[h] = *reinterpret_cast<const uint4 *>(qp + 32 * h);
+        for (int h = 0; h < NH; ++h) {
+            qv[h] = *reinterpret_cast<const uint4 *>(qp + 32 * h);
+            qv[h].x ^= flip; qv[h].y ^= flip; qv[h].z ^= flip; qv[h].w ^= flip;
+        }
     }
-    const float c = a.qscale;
+    const LaneAddr<D> la(g.km_pitch, lg, n);
     const uint4 ones = make_uint4(Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2);
 
     f4 acc[ND], lsum = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
-    float m = -1e30f;
+    float m = -1e30f;  // running maximum, scaled (log2 units)
 
     const int nslab = (Hend - Uh + 3) >> 2;
     for (int j = 0; j < w.k[0]; ++j) {
@@ -357,49 +406,53 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
             const int r0 = Uh + 4 * sl;
             __syncthreads();
             stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kl);
-            stage_tr<T, D>(a.v, w, tk, r0, U2, g.box_w, g.tr_pitch, Vl);
+            stage_tr<T, D>(a.v, w, tk, r0, U2, g.box_w, Vl);
             stage_wait();
             if (!wave_on) continue;
-            // key row of this lane group's scores in the slab, and whether it is
-            // inside the lane's query window
-            const bool row_ok = (unsigned)(r0 + lg - wh) < (unsigned)w.k[1];
+            // key rows of the slab inside the lane's query window
+            bool hr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1];
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                const int col0 = aw + 4 * b;
                 f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
                 for (int h = 0; h < NH; ++h)
-                    s0 = Mf<T>::mma(km_read<NC>(Kl, g.km_pitch, n, col0, lg + 4 * h), qv[h], s0);
+                    s0 = Mf<T>::mma(km_at(Kl + col0 * NC * 16, la.km[h]), qv[h], s0);
                 if (two) {
 #pragma unroll
                     for (int h = 0; h < NH; ++h)
-                        s1 = Mf<T>::mma(km_read<NC>(Kl, g.km_pitch, n, col1, lg + 4 * h), qv[h], s1);
+                        s1 = Mf<T>::mma(km_at(Kl + (col0 + 4) * NC * 16, la.km[h]), qv[h], s1);
                 }
+                const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
+                const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
                 float x[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool ok0 = row_ok && (unsigned)(col0 + r - ww) < (unsigned)w.k[2];
-                    const bool ok1 = two && row_ok && (unsigned)(col1 + r - ww) < (unsigned)w.k[2];
-                    x[r] = ok0 ? s0[r] * c : -INFINITY;
-                    x[4 + r] = ok1 ? s1[r] * c : -INFINITY;
+                    x[r] = (w0 && hr[r]) ? s0[r] : -INFINITY;
+                    x[4 + r] = (w1 && hr[r]) ? s1[r] : -INFINITY;
                 }
-                float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-                const float mn = fmaxf(m, xmax4(mx));
-                const float alpha = fast_exp2(m - mn);
-                m = mn;
+                const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                const float ms = xmax4(mx) * c;
+                if (__any(ms > m + kLazyRescale)) {
+                    const float mn = ms > m + kLazyRescale ? ms : m;
+                    const float alpha = fast_exp2(m - mn);
+                    m = mn;
 #pragma unroll
-                for (int d = 0; d < ND; ++d) acc[d] *= alpha;
-                lsum *= alpha;
+                    for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+                    lsum *= alpha;
+                }
                 uint4 pb;
-                pb.x = Mf<T>::pack(fast_exp2(x[0] - m), fast_exp2(x[1] - m));
-                pb.y = Mf<T>::pack(fast_exp2(x[2] - m), fast_exp2(x[3] - m));
-                pb.z = Mf<T>::pack(fast_exp2(x[4] - m), fast_exp2(x[5] - m));
-                pb.w = Mf<T>::pack(fast_exp2(x[6] - m), fast_exp2(x[7] - m));
-                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+                pb.x = Mf<T>::pack(fast_exp2(fmaf(x[0], c, -m)), fast_exp2(fmaf(x[1], c, -m)));
+                pb.y = Mf<T>::pack(fast_exp2(fmaf(x[2], c, -m)), fast_exp2(fmaf(x[3], c, -m)));
+                pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
+                pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
+                const char *t0p = Vl + la.tr + col0 * tr_col<D>();
+                const char *t1p = two ? t0p + 4 * tr_col<D>() : t0p;
 #pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    acc[d] = Mf<T>::mma(tr_read<D>(Vl, g.tr_pitch, lg, G0, G1, 16 * d + n), pb, acc[d]);
+                for (int d = 0; d < ND; ++d) acc[d] = Mf<T>::mma(tr_at(t0p, t1p, d), pb, acc[d]);
                 lsum = Mf<T>::mma(ones, pb, lsum);
             }
         }
@@ -442,7 +495,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
 
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
-    const int ww = window_start(P.w, nw, w.k[2]) - U2;
+    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - U2);
     const int64_t qo = eoff<D>(w, w.o[0], P.h, P.w);
     const int64_t ro = roff(w, w.o[0], P.h, P.w);
     uint4 qv[NH], dv[NH];
@@ -462,11 +515,11 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
         for (int i = 0; i < 4; ++i)
             delta += Mf<T>::lo(ow[i]) * Mf<T>::lo(dw[i]) + Mf<T>::hi(ow[i]) * Mf<T>::hi(dw[i]);
     }
-    delta += __shfl_xor(delta, 16);
-    delta += __shfl_xor(delta, 32);
+    delta = xsum4(delta);
     if (wave_on && P.active && lg == 0) a.delta[ro] = delta;
-    const float lse2 = a.lse[ro] * kLog2e;
+    const float nlse2 = -a.lse[ro] * kLog2e;
     const float c = a.qscale;
+    const LaneAddr<D> la(g.km_pitch, lg, n);
 
     f4 acc[ND];
 #pragma unroll
@@ -480,33 +533,35 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
             __syncthreads();
             stage_km<T, D>(a.v, w, tk, r0, U2, g.box_w, g.km_pitch, Vk);
             stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kk);
-            stage_tr<T, D>(a.k, w, tk, r0, U2, g.box_w, g.tr_pitch, Kt);
+            stage_tr<T, D>(a.k, w, tk, r0, U2, g.box_w, Kt);
             stage_wait();
             if (!wave_on) continue;
-            const bool row_ok = (unsigned)(r0 + lg - wh) < (unsigned)w.k[1];
+            bool hr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1];
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                const int col0 = aw + 4 * b;
                 f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
 #pragma unroll
                 for (int h = 0; h < NH; ++h) {
-                    s0 = Mf<T>::mma(km_read<NC>(Kk, g.km_pitch, n, col0, lg + 4 * h), qv[h], s0);
-                    p0 = Mf<T>::mma(km_read<NC>(Vk, g.km_pitch, n, col0, lg + 4 * h), dv[h], p0);
+                    s0 = Mf<T>::mma(km_at(Kk + col0 * NC * 16, la.km[h]), qv[h], s0);
+                    p0 = Mf<T>::mma(km_at(Vk + col0 * NC * 16, la.km[h]), dv[h], p0);
                 }
                 if (two) {
 #pragma unroll
                     for (int h = 0; h < NH; ++h) {
-                        s1 = Mf<T>::mma(km_read<NC>(Kk, g.km_pitch, n, col1, lg + 4 * h), qv[h], s1);
-                        p1 = Mf<T>::mma(km_read<NC>(Vk, g.km_pitch, n, col1, lg + 4 * h), dv[h], p1);
+                        s1 = Mf<T>::mma(km_at(Kk + (col0 + 4) * NC * 16, la.km[h]), qv[h], s1);
+                        p1 = Mf<T>::mma(km_at(Vk + (col0 + 4) * NC * 16, la.km[h]), dv[h], p1);
                     }
                 }
+                const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
+                const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
                 float ds[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool ok0 = row_ok && (unsigned)(col0 + r - ww) < (unsigned)w.k[2];
-                    const bool ok1 = two && row_ok && (unsigned)(col1 + r - ww) < (unsigned)w.k[2];
-                    const float e0 = ok0 ? fast_exp2(s0[r] * c - lse2) : 0.f;
-                    const float e1 = ok1 ? fast_exp2(s1[r] * c - lse2) : 0.f;
+                    const float e0 = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, nlse2) : -INFINITY);
+                    const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
                     ds[r] = e0 * (p0[r] - delta);
                     ds[4 + r] = e1 * (p1[r] - delta);
                 }
@@ -515,10 +570,10 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
                 db.y = Mf<T>::pack(ds[2], ds[3]);
                 db.z = Mf<T>::pack(ds[4], ds[5]);
                 db.w = Mf<T>::pack(ds[6], ds[7]);
-                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+                const char *t0p = Kt + la.tr + col0 * tr_col<D>();
+                const char *t1p = two ? t0p + 4 * tr_col<D>() : t0p;
 #pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    acc[d] = Mf<T>::mma(tr_read<D>(Kt, g.tr_pitch, lg, G0, G1, 16 * d + n), db, acc[d]);
+                for (int d = 0; d < ND; ++d) acc[d] = Mf<T>::mma(tr_at(t0p, t1p, d), db, acc[d]);
             }
         }
     }
@@ -551,8 +606,8 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
     char *Qk = smem;
     char *Ok = smem + 4 * g.km_pitch;
     char *Qt = smem + 8 * g.km_pitch;
-    char *Ot = Qt + 4 * g.tr_pitch;
-    float2 *Rw = reinterpret_cast<float2 *>(Ot + 4 * g.tr_pitch);
+    char *Ot = Qt + g.box_w * tr_col<D>();
+    float2 *Rw = reinterpret_cast<float2 *>(Ot + g.box_w * tr_col<D>());
 
     // the workgroup's query box: planes, rows, columns of the inverse windows
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
@@ -567,7 +622,9 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
 
     const Pt P = patch_point(w, wave, n);  // the lane's key
     const int ih0 = inverse_first(P.h, nh, w.k[1]), ih1 = inverse_last(P.h, nh, w.k[1]);
-    const int iw0 = inverse_first(P.w, nw, w.k[2]) - U2, iw1 = inverse_last(P.w, nw, w.k[2]) - U2;
+    // query columns of this lane group relative to the key's inverse window
+    const int irel = lg - (inverse_first(P.w, nw, w.k[2]) - U2);
+    const int iwn = inverse_last(P.w, nw, w.k[2]) - inverse_first(P.w, nw, w.k[2]);
     const int64_t ko = eoff<D>(w, w.o[0], P.h, P.w);
     uint4 kv[NH], vv[NH];
 #pragma unroll
@@ -576,6 +633,7 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
         vv[h] = *reinterpret_cast<const uint4 *>(a.v + ko + 8 * lg + 32 * h);
     }
     const float c = a.qscale;
+    const LaneAddr<D> la(g.km_pitch, lg, n);
 
     f4 dka[ND], dva[ND];
 #pragma unroll
@@ -591,42 +649,46 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
             __syncthreads();
             stage_km<T, D>(a.q, w, tq, r0, U2, g.box_w, g.km_pitch, Qk);
             stage_km<T, D>(a.dout, w, tq, r0, U2, g.box_w, g.km_pitch, Ok);
-            stage_tr<T, D>(a.q, w, tq, r0, U2, g.box_w, g.tr_pitch, Qt);
-            stage_tr<T, D>(a.dout, w, tq, r0, U2, g.box_w, g.tr_pitch, Ot);
+            stage_tr<T, D>(a.q, w, tq, r0, U2, g.box_w, Qt);
+            stage_tr<T, D>(a.dout, w, tq, r0, U2, g.box_w, Ot);
             stage_rows16(a.lse, a.delta, w, tq, r0, U2, g.box_w, Rw);
             stage_wait();
             if (!wave_on) continue;
-            // query row of this lane group in the slab, inside the key's inverse window?
-            const bool row_ok = (unsigned)(r0 + lg - ih0) <= (unsigned)(ih1 - ih0);
-            const float2 *rrow = Rw + lg * g.box_w;
+            // query rows of the slab inside the key's inverse window
+            bool hr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0);
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b, col1 = col0 + 4;
+                const int col0 = aw + 4 * b;
                 f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
 #pragma unroll
                 for (int h = 0; h < NH; ++h) {
-                    s0 = Mf<T>::mma(km_read<NC>(Qk, g.km_pitch, n, col0, lg + 4 * h), kv[h], s0);
-                    p0 = Mf<T>::mma(km_read<NC>(Ok, g.km_pitch, n, col0, lg + 4 * h), vv[h], p0);
+                    s0 = Mf<T>::mma(km_at(Qk + col0 * NC * 16, la.km[h]), kv[h], s0);
+                    p0 = Mf<T>::mma(km_at(Ok + col0 * NC * 16, la.km[h]), vv[h], p0);
                 }
                 if (two) {
 #pragma unroll
                     for (int h = 0; h < NH; ++h) {
-                        s1 = Mf<T>::mma(km_read<NC>(Qk, g.km_pitch, n, col1, lg + 4 * h), kv[h], s1);
-                        p1 = Mf<T>::mma(km_read<NC>(Ok, g.km_pitch, n, col1, lg + 4 * h), vv[h], p1);
+                        s1 = Mf<T>::mma(km_at(Qk + (col0 + 4) * NC * 16, la.km[h]), kv[h], s1);
+                        p1 = Mf<T>::mma(km_at(Ok + (col0 + 4) * NC * 16, la.km[h]), vv[h], p1);
                     }
                 }
+                // (lse, delta) of the four rows of this lane group's query column
+                const float4 *rp0 = reinterpret_cast<const float4 *>(Rw + 4 * (col0 + lg));
+                const float4 *rp1 = reinterpret_cast<const float4 *>(Rw + 4 * (two ? col0 + 4 + lg : col0 + lg));
+                const float4 l0a = rp0[0], l0b = rp0[1], l1a = rp1[0], l1b = rp1[1];
+                const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, dl0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
+                const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, dl1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
+                const bool w0 = (unsigned)(col0 + irel) <= (unsigned)iwn;
+                const bool w1 = two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
                 float pr[8], ds[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float2 l0 = rrow[col0 + r];
-                    const float2 l1 = rrow[imin(col1 + r, g.box_w - 1)];
-                    const bool ok0 = row_ok && (unsigned)(col0 + r - iw0) <= (unsigned)(iw1 - iw0);
-                    const bool ok1 =
-                        two && row_ok && (unsigned)(col1 + r - iw0) <= (unsigned)(iw1 - iw0);
-                    pr[r] = ok0 ? fast_exp2(s0[r] * c - l0.x) : 0.f;
-                    pr[4 + r] = ok1 ? fast_exp2(s1[r] * c - l1.x) : 0.f;
-                    ds[r] = pr[r] * (p0[r] - l0.y);
-                    ds[4 + r] = pr[4 + r] * (p1[r] - l1.y);
+                    pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, -ls0[r]) : -INFINITY);
+                    pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, -ls1[r]) : -INFINITY);
+                    ds[r] = pr[r] * (p0[r] - dl0[r]);
+                    ds[4 + r] = pr[4 + r] * (p1[r] - dl1[r]);
                 }
                 uint4 pb, db;
                 pb.x = Mf<T>::pack(pr[0], pr[1]);
@@ -637,11 +699,14 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
                 db.y = Mf<T>::pack(ds[2], ds[3]);
                 db.z = Mf<T>::pack(ds[4], ds[5]);
                 db.w = Mf<T>::pack(ds[6], ds[7]);
-                const int G0 = col0 >> 2, G1 = two ? G0 + 1 : G0;
+                const char *o0 = Ot + la.tr + col0 * tr_col<D>();
+                const char *o1 = two ? o0 + 4 * tr_col<D>() : o0;
+                const char *q0 = Qt + la.tr + col0 * tr_col<D>();
+                const char *q1 = two ? q0 + 4 * tr_col<D>() : q0;
 #pragma unroll
                 for (int d = 0; d < ND; ++d) {
-                    dva[d] = Mf<T>::mma(tr_read<D>(Ot, g.tr_pitch, lg, G0, G1, 16 * d + n), pb, dva[d]);
-                    dka[d] = Mf<T>::mma(tr_read<D>(Qt, g.tr_pitch, lg, G0, G1, 16 * d + n), db, dka[d]);
+                    dva[d] = Mf<T>::mma(tr_at(o0, o1, d), pb, dva[d]);
+                    dka[d] = Mf<T>::mma(tr_at(q0, q1, d), db, dka[d]);
                 }
             }
         }
