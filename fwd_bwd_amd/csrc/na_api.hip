@@ -574,7 +574,7 @@ template <typename Kern, typename Args>
 na_status launch_m16(Kern kern, const M16Plan &pl, const Args &a, hipStream_t s) {
     if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
     if (pl.g.n_tiles == 0) return NA_OK;
-    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::kThreads), pl.lds, s, a);
+    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::m16::kTG), pl.lds, s, a);
     return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
 }
 

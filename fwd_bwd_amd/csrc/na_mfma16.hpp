@@ -100,7 +100,10 @@ struct Mf<f16> {
     static constexpr uint32_t kOne2 = 0x3c003c00u;
 };
 
-constexpr int kTH = 4, kTW = 16;  // tile rows (H) and columns (W); T: one plane
+// A workgroup of kWG waves owns a 1 x kTH x kTW tile: two rows of four 4 x 4
+// patches (wave v: patch row v / 4, patch column v % 4).
+constexpr int kWG = 8, kTG = 64 * kWG;
+constexpr int kTH = 8, kTW = 16;  // tile rows (H) and columns (W); T: one plane
 
 struct Geom {
     int ext[3], ker[3], dil[3];
@@ -128,20 +131,21 @@ struct Args {
 
 // Tile id -> batch, head, residue class and tile origin (class coordinates).
 // The head varies fastest (the heads of one token are adjacent in memory),
-// then W, H, T tiles, residue class, batch.
+// then T (the tiles of neighbouring planes share all but one of their key
+// planes, which then come from L2), then W, H tiles, residue class, batch.
 __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
     int rem = tile, q;
     q = fdiv(rem, g.f_heads);
     const int head = rem - q * g.heads;
+    rem = q;
+    q = fdiv(rem, g.f_t);
+    const int tt = rem - q * g.tiles[0];
     rem = q;
     q = fdiv(rem, g.f_tw);
     const int tw = rem - q * g.tiles[2];
     rem = q;
     q = fdiv(rem, g.f_th);
     const int th = rem - q * g.tiles[1];
-    rem = q;
-    q = fdiv(rem, g.f_t);
-    const int tt = rem - q * g.tiles[0];
     rem = q;
     q = fdiv(rem, g.f_nres);
     const int res = rem - q * g.nres;
@@ -191,30 +195,31 @@ __device__ __forceinline__ int kswz(int col) {
 // Key-major slab: rows [r0, r0 + 4) of plane tk (class coordinates), columns
 // [U2, U2 + box_w), of src; row r at lds + r * pitch, chunk s of column c at
 // 16 * (c * NC + (s ^ kswz(c))). Direct global-to-LDS loads, 64 consecutive
-// chunks per wave instruction; wave v stages row v. Points past the grid repeat
-// the last grid point. Completion: stage_wait().
+// chunks per wave instruction; the (row, 64-chunk part) pieces are spread over
+// the workgroup's waves. Points past the grid repeat the last grid point.
+// Completion: stage_wait().
 template <typename T, int D>
 __device__ __forceinline__ void stage_km(const T *src, const TileCtx &w, int tk, int r0, int U2,
                                          int box_w, int pitch, char *lds) {
     constexpr int NC = D * 2 / 16;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int nch = box_w * NC;
-    const int c1 = imin(r0 + wave, w.n[1] - 1);
-    const char *rowp =
-        reinterpret_cast<const char *>(src) + eoff<D>(w, tk, c1, 0) * (int64_t)sizeof(T);
-    char *dst = lds + wave * pitch;
-    for (int part = 0; part * 64 < nch; ++part) {
+    const int nch = box_w * NC, parts = (nch + 63) >> 6;
+    for (int it = wave; it < 4 * parts; it += kWG) {
+        const int row = it & 3, part = it >> 2;
+        const int c1 = imin(r0 + row, w.n[1] - 1);
+        const char *rowp =
+            reinterpret_cast<const char *>(src) + eoff<D>(w, tk, c1, 0) * (int64_t)sizeof(T);
         const int s = part * 64 + lane;
         if (s >= nch) continue;
         const int col = s / NC, pos = s - col * NC;
         const int c2 = imin(U2 + col, w.n[2] - 1);
         const int goff = (int)(c2 * w.lst[2]) * D * 2 + ((pos ^ kswz<NC>(col)) << 4);
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_global_load_lds(rowp + goff, (lds_void *)(dst + part * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(rowp + goff,
+                                         (lds_void *)(lds + row * pitch + part * 1024), 16, 0, 0);
 #else
         (void)goff;
-        (void)dst;
         (void)rowp;
 #endif
     }
@@ -239,7 +244,7 @@ __device__ __forceinline__ void stage_tr(const T *src, const TileCtx &w, int tk,
     const int tasks = box_w * NC;
     const int rows[4] = {imin(r0, w.n[1] - 1), imin(r0 + 1, w.n[1] - 1), imin(r0 + 2, w.n[1] - 1),
                          imin(r0 + 3, w.n[1] - 1)};
-    for (int t = threadIdx.x; t < tasks; t += kThreads) {
+    for (int t = threadIdx.x; t < tasks; t += kTG) {
         const int c = t % NC, col = t / NC;
         const int c2 = imin(U2 + col, w.n[2] - 1);
         uint4 x[4];
@@ -268,7 +273,7 @@ __device__ __forceinline__ void stage_tr(const T *src, const TileCtx &w, int tk,
 __device__ __forceinline__ void stage_rows16(const float *lse, const float *delta,
                                              const TileCtx &w, int tk, int r0, int U2, int box_w,
                                              float2 *rows) {
-    for (int i = threadIdx.x; i < 4 * box_w; i += kThreads) {
+    for (int i = threadIdx.x; i < 4 * box_w; i += kTG) {
         const int col = i >> 2, r = i & 3;
         const int64_t ro = roff(w, tk, imin(r0 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1));
         rows[i] = make_float2(lse[ro] * kLog2e, delta[ro]);
@@ -292,12 +297,13 @@ __device__ __forceinline__ float xsum4(float v) {
 }
 
 // The lane's point of the wave's patch: patch origin (class) + (n / 4, n % 4).
+// Wave v's patch sits at patch row v / 4, patch column v % 4 of the tile.
 struct Pt {
     int h, w;       // clamped into the grid
     bool active;    // unclamped point inside the grid
 };
 __device__ __forceinline__ Pt patch_point(const TileCtx &w, int wave, int n) {
-    const int h = w.o[1] + (n >> 2), c = w.o[2] + 4 * wave + (n & 3);
+    const int h = w.o[1] + 4 * (wave >> 2) + (n >> 2), c = w.o[2] + 4 * (wave & 3) + (n & 3);
     Pt p;
     p.active = h < w.n[1] && c < w.n[2];
     p.h = imin(h, w.n[1] - 1);
@@ -348,7 +354,7 @@ constexpr float kLazyRescale = 8.f;
 // ============================================================================
 // Forward: out, lse.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
     const Geom &g = a.g;
@@ -367,10 +373,13 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
     const int U2 = window_start(w.o[2], nw, w.k[2]);
     // this wave's blocks: from its patch's first window start (aligned down to
     // a group of four columns of the box) to its last window end
-    const bool wave_on = w.o[2] + 4 * wave < nw;
-    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
+    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
     const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
     const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
+    // rows of this wave's window union: slabs outside it are skipped
+    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
+    const int wr0 = window_start(ph0, nh, w.k[1]), wr1 = window_start(ph1, nh, w.k[1]) + w.k[1];
 
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
@@ -408,7 +417,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
             stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kl);
             stage_tr<T, D>(a.v, w, tk, r0, U2, g.box_w, Vl);
             stage_wait();
-            if (!wave_on) continue;
+            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
             // key rows of the slab inside the lane's query window
             bool hr[4];
 #pragma unroll
@@ -471,7 +480,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(Args<T> a) {
 // ============================================================================
 // Backward, query side: delta = <dout, out> and dq.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
     const Geom &g = a.g;
@@ -488,10 +497,13 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
     const int Uh = window_start(w.o[1], nh, w.k[1]);
     const int Hend = window_start(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + w.k[1];
     const int U2 = window_start(w.o[2], nw, w.k[2]);
-    const bool wave_on = w.o[2] + 4 * wave < nw;
-    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
+    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
     const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
     const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
+    // rows of this wave's window union: slabs outside it are skipped
+    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
+    const int wr0 = window_start(ph0, nh, w.k[1]), wr1 = window_start(ph1, nh, w.k[1]) + w.k[1];
 
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
@@ -535,7 +547,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
             stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kk);
             stage_tr<T, D>(a.k, w, tk, r0, U2, g.box_w, Kt);
             stage_wait();
-            if (!wave_on) continue;
+            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
             bool hr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1];
@@ -594,7 +606,7 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(Args<T> a) {
 // keys), P = exp2(S c - lse), dP = dO V^T, dS = P (dP - delta); then
 // dV^T += dO^T P and dK^T += Q^T dS over pairs of query blocks.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
     const Geom &g = a.g;
@@ -615,10 +627,13 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
     const int Uh = inverse_first(w.o[1], nh, w.k[1]);
     const int Hend = inverse_last(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + 1;
     const int U2 = inverse_first(w.o[2], nw, w.k[2]);
-    const bool wave_on = w.o[2] + 4 * wave < nw;
-    const int pw0 = imin(w.o[2] + 4 * wave, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
+    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
     const int aw = (inverse_first(pw0, nw, w.k[2]) - U2) & ~3;
     const int nbw = (inverse_last(pw1, nw, w.k[2]) + 1 - U2 - aw + 3) >> 2;
+    // rows of this wave's inverse union: slabs outside it are skipped
+    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
+    const int wr0 = inverse_first(ph0, nh, w.k[1]), wr1 = inverse_last(ph1, nh, w.k[1]) + 1;
 
     const Pt P = patch_point(w, wave, n);  // the lane's key
     const int ih0 = inverse_first(P.h, nh, w.k[1]), ih1 = inverse_last(P.h, nh, w.k[1]);
@@ -653,7 +668,7 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(Args<T> a) {
             stage_tr<T, D>(a.dout, w, tq, r0, U2, g.box_w, Ot);
             stage_rows16(a.lse, a.delta, w, tq, r0, U2, g.box_w, Rw);
             stage_wait();
-            if (!wave_on) continue;
+            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
             // query rows of the slab inside the key's inverse window
             bool hr[4];
 #pragma unroll
