@@ -366,6 +366,33 @@ def frame_window_mask(grid, kernel, frame_kernel):
     return mask
 
 
+def outer_window_mask(grid, kernel, outer_kernel, dilation=1):
+    """Mask [*grid, K] (K = prod(kernel), window entries in row-major order)
+    restricting windows along the outermost axis (H on 2D grids, T on 3D
+    ones): a query at coordinate x0 along that axis keeps only the keys whose
+    coordinate there lies in the window of size outer_kernel[x0] around x0 --
+    the same centered-and-shifted rule, inside x0's residue class -- among the
+    kernel[0] positions its scores are computed over. outer_kernel[x0] = 0
+    masks every key of the query. The requester's per-frame time kernel is
+    the 3D case."""
+    grid, kernel = tuple(int(g) for g in grid), tuple(int(k) for k in kernel)
+    dil = _as3(dilation, len(grid), 1)[3 - len(grid):]
+    L0, k0, d0 = grid[0], kernel[0], int(dil[0])
+    rest = int(np.prod(kernel[1:]))
+    mask = np.zeros(grid + (k0 * rest,), np.uint8)
+    for x0 in range(L0):
+        fk = int(outer_kernel[x0])
+        if fk == 0:
+            continue
+        s_max = window_start(L0, k0, d0, x0)
+        s_own = window_start(L0, fk, d0, x0)
+        for i0 in range(k0):
+            f = s_max + d0 * i0
+            if s_own <= f < s_own + d0 * fk:
+                mask[x0, ..., i0 * rest:(i0 + 1) * rest] = 1
+    return mask
+
+
 def softmax_bwd(p, dp):
     """Backward of the window softmax: dS = P * (dP - sum_j P dP) over the last axis."""
     p, dp = _f64(p), _f64(dp)

@@ -480,6 +480,38 @@ def check_masked_windows(orc, seed=18):
     assert np.all(Pd[:, :, 2, 1, 3] == 0) and np.all(od[:, :, 2, 1, 3] == 0)
 
 
+def check_outer_window_mask(orc, seed=19):
+    """Windows restricted along the outermost axis: a table worked out by hand
+    from the definition (2D, five rows, kernel 3 x 1, per-row sizes 3, 1, 2, 0,
+    3); and a constant restricted size k' gives neighborhood attention with
+    kernel k' along that axis (2D and 3D, with dilation along it), forward and
+    backward through the masked unfused ops."""
+    import oracle as _o
+    m = _o.outer_window_mask((5, 2), (3, 1), [3, 1, 2, 0, 3])
+    # row 0: window rows 0..2, own window of 3 -> 0..2;  row 1: own window {1};
+    # row 2: window rows 1..3, own 2 -> rows 1, 2;  row 3: nothing;  row 4: rows 2..4
+    want = [[1, 1, 1], [0, 1, 0], [1, 1, 0], [0, 0, 0], [1, 1, 1]]
+    for x0 in range(5):
+        for x1 in range(2):
+            assert list(m[x0, x1]) == want[x0], (x0, list(m[x0, x1]))
+    cases = [((7, 6), (5, 3), 1, (3, 1)), ((9, 5), (3, 3), (2, 1), (1, 2)),
+             ((5, 4, 3), (3, 3, 3), 1, (1, 2))]
+    for grid, kernel, dil, ks in cases:
+        heads, D = 2, 3
+        q, k, v, dout = (_hm(grid, heads, D, seed + j) for j in range(4))
+        tm = lambda x: np.moveaxis(x, 1, -2)  # noqa: E731
+        for kk in ks:
+            mask = _o.outer_window_mask(grid, kernel, [kk] * grid[0], dil)
+            P, out = orc.unfused_fwd(q, k, v, kernel, dil, 0.8, mask=mask)
+            dq, dk, dv = orc.unfused_bwd(q, k, v, P, dout, kernel, dil, 0.8)
+            small = (kk,) + tuple(kernel[1:])
+            o_ref, _ = orc.na_fwd(tm(q), tm(k), tm(v), small, dil, 0.8)
+            g_ref = orc.na_bwd(tm(q), tm(k), tm(v), tm(dout), small, dil, 0.8)
+            assert np.max(np.abs(tm(out) - o_ref)) < 1e-12, (grid, kk)
+            for got, ref in zip((dq, dk, dv), g_ref):
+                assert np.max(np.abs(tm(got) - ref)) < 1e-12, (grid, kk)
+
+
 ALL_CHECKS = [
     ("windows", lambda o: check_windows(o)),
     ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
@@ -502,6 +534,7 @@ ALL_CHECKS = [
     ("rpb_adjoint", check_rpb_adjoint),
     ("rpb_fd", check_rpb_fd),
     ("masked_windows", check_masked_windows),
+    ("outer_window_mask", check_outer_window_mask),
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 
