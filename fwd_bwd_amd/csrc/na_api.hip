@@ -596,6 +596,8 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
             ma.o = static_cast<T *>(a.out);
             ma.lse_out = a.lse;
             ma.qscale = a.qscale;
+            ma.frame = a.frame;
+            ma.frame_axis = a.frame_axis;
             return launch_m16(na::m16::fwd_kernel<T, D>, mp, ma, s);
         }
     }
@@ -609,6 +611,8 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
         fa.out = static_cast<T *>(a.out);
         fa.lse = a.lse;
         fa.qscale = a.qscale;
+        fa.frame = a.frame;
+        fa.frame_axis = a.frame_axis;
         return fast_fwd<T>(pl, fa, s);
     }
     int lds;
@@ -682,6 +686,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             ma.dv = static_cast<T *>(a.dv);
             ma.qscale = a.qscale;
             ma.scale = a.scale;
+            ma.frame = a.frame;
+            ma.frame_axis = a.frame_axis;
             // dq (which also writes delta) strictly before dk/dv, which reads it
             if (phases & kPhaseDq) {
                 ma.g = mq.g;
@@ -709,6 +715,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
         fa.dv = static_cast<T *>(a.dv);
         fa.qscale = a.qscale;
         fa.scale = a.scale;
+        fa.frame = a.frame;
+        fa.frame_axis = a.frame_axis;
         fa.edge = -1;  // dk/dv tiles by walk_lo (border classes set it per launch)
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
@@ -908,8 +916,12 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
     return NA_OK;
 }
 
-na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *v, void *out,
-                 float *lse, void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+na_status fwd_common(const na_problem *p, const void *q, const void *k, const void *v, void *out,
+                     float *lse, const int32_t *frame, void *hip_stream) {
     Prob pr;
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
@@ -923,6 +935,8 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     a.out = out;
     a.lse = lse;
     a.qscale = pr.scale * na::kLog2e;
+    a.frame = frame;
+    a.frame_axis = p->ndim == 3 ? 0 : 1;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define NA_FWD_D(D)                                                   \
     case D:                                                           \
@@ -932,6 +946,25 @@ na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *
     switch (pr.head_dim) { NA_FWD_D(16) NA_FWD_D(32) NA_FWD_D(64) }
 #undef NA_FWD_D
     return NA_ERR_UNSUPPORTED;
+}
+
+bool frame_ok(const int32_t *frame) {
+    return frame && (reinterpret_cast<uintptr_t>(frame) & 3u) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+na_status na_fwd(const na_problem *p, const void *q, const void *k, const void *v, void *out,
+                 float *lse, void *hip_stream) {
+    return fwd_common(p, q, k, v, out, lse, nullptr, hip_stream);
+}
+
+na_status na_fwd_framed(const na_problem *p, const void *q, const void *k, const void *v,
+                        void *out, float *lse, const int32_t *frame_kernel, void *hip_stream) {
+    if (validate(p, nullptr) == NA_OK && !frame_ok(frame_kernel)) return NA_ERR_INVALID_ARG;
+    return fwd_common(p, q, k, v, out, lse, frame_kernel, hip_stream);
 }
 
 size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant, int32_t kv_splits) {
@@ -951,7 +984,7 @@ namespace {
 na_status bwd_common(const na_problem *p, const void *q, const void *k, const void *v,
                      const void *out, const void *dout, const float *lse, void *dq, void *dk,
                      void *dv, float *delta, float *dq_acc, int32_t variant, int32_t kv_splits,
-                     int phases, void *hip_stream) {
+                     int phases, void *hip_stream, const int32_t *frame = nullptr) {
     Prob pr;
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
@@ -969,6 +1002,8 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     a.dq_acc = dq_acc;
     a.qscale = pr.scale * na::kLog2e;
     a.scale = pr.scale;
+    a.frame = frame;
+    a.frame_axis = p->ndim == 3 ? 0 : 1;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define NA_BWD_D(D)                                                                 \
     case D:                                                                         \
@@ -988,10 +1023,12 @@ bool ptrs_ok(std::initializer_list<const void *> ptrs) {
 
 }  // namespace
 
-na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *v,
-                 const void *out, const void *dout, const float *lse, void *dq, void *dk,
-                 void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
-                 int32_t kv_splits, void *hip_stream) {
+namespace {
+
+na_status bwd_entry(const na_problem *p, const void *q, const void *k, const void *v,
+                    const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                    void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                    int32_t kv_splits, const int32_t *frame, void *hip_stream) {
     na_status st = validate(p, nullptr);
     if (st != NA_OK) return st;
     if (variant != NA_BWD_GATHER && variant != NA_BWD_KVPARALLEL) return NA_ERR_INVALID_ARG;
@@ -1008,7 +1045,26 @@ na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *
                                                     round256((size_t)pr.rows * sizeof(float)))
                         : nullptr;
     return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, dq_acc, variant, kv_splits,
-                      kPhaseBoth, hip_stream);
+                      kPhaseBoth, hip_stream, frame);
+}
+
+}  // namespace
+
+na_status na_bwd(const na_problem *p, const void *q, const void *k, const void *v,
+                 const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                 void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                 int32_t kv_splits, void *hip_stream) {
+    return bwd_entry(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, variant,
+                     kv_splits, nullptr, hip_stream);
+}
+
+na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const void *v,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                        void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                        int32_t kv_splits, const int32_t *frame_kernel, void *hip_stream) {
+    if (validate(p, nullptr) == NA_OK && !frame_ok(frame_kernel)) return NA_ERR_INVALID_ARG;
+    return bwd_entry(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, variant,
+                     kv_splits, frame_kernel, hip_stream);
 }
 
 na_status na_bwd_dq(const na_problem *p, const void *q, const void *k, const void *v,

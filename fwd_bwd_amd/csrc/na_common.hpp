@@ -229,6 +229,7 @@ struct Geometry {
 struct TileCtx {
     int n[3], k[3];     // class sizes and window sizes per axis
     int o[3];           // tile origin in class coordinates
+    int r[3], d[3];     // residue class and dilation per axis (absolute = r + d * class)
     int64_t base;       // element offset of (b, class origin token, head, 0)
     int64_t st[3];      // element offset of one class step per axis
     int64_t lbase;      // lse / delta offset of (b, class origin token, head)
@@ -267,6 +268,8 @@ __device__ __forceinline__ bool fill_ctx(const int (&ext)[3], const int (&ker)[3
         w.n[a] = class_size(ext[a], dil[a], r[a]);
         w.k[a] = ker[a];
         w.o[a] = o[a];
+        w.r[a] = r[a];
+        w.d[a] = dil[a];
         inside = inside && (o[a] < w.n[a]);
     }
     const int64_t HW = (int64_t)ext[1] * ext[2];
@@ -494,6 +497,52 @@ __device__ __forceinline__ void lds_quarter(const char *lds, int pt, int sw, int
         const int chunk = (c * G) / EPC, half = (c * G) % EPC;
         Io<T>::quad(p + ((chunk ^ sw) << 4) + half * (int)sizeof(T), d);
     }
+}
+
+// ----------------------------------------------------------------------------
+// Windows restricted along one axis ("frames": T on 3D grids, H on 2D grids).
+// frame[x], x an absolute coordinate along the frame axis, is the size of a
+// window around x (the same centered-and-shifted rule, inside x's residue
+// class) that the keys of the queries at x must also lie in along that axis;
+// 0 masks every key. This is the NATTEN issue requester's per-frame time
+// kernel, applied by index arithmetic: whole planes outside a tile's frame
+// window are skipped, rows are masked.
+
+__device__ __forceinline__ int pick3(const int (&v)[3], int a) {
+    return a == 0 ? v[0] : (a == 1 ? v[1] : v[2]);
+}
+
+// Window size of class coordinate i along axis a (clamped to [0, k]).
+__device__ __forceinline__ int frame_size(const int *frame, const TileCtx &w, int a, int i) {
+    const int v = frame[pick3(w.r, a) + pick3(w.d, a) * i];
+    return imin(imax(v, 0), pick3(w.k, a));
+}
+
+// Whether class coordinate key lies in the frame window of size fk around
+// class coordinate query (n positions on the axis).
+__device__ __forceinline__ bool in_frame(int key, int query, int n, int fk) {
+    return fk > 0 && (unsigned)(key - window_start(query, n, fk)) < (unsigned)fk;
+}
+
+// Bits r (0..31) of the positions start + r lying in the frame window of
+// query (a query's window walk).
+__device__ __forceinline__ unsigned frame_bits(int start, int query, int n, int fk) {
+    if (fk <= 0) return 0u;
+    const int s = window_start(query, n, fk) - start;
+    const int lo = imax(s, 0), hi = imin(s + fk, 32);
+    return hi > lo ? bit_range(lo, hi - lo) : 0u;
+}
+
+// Bits r (0..len-1, len <= 32) of the queries at start + r whose frame window
+// holds key (a key's inverse walk).
+__device__ __forceinline__ unsigned frame_bits_inverse(const int *frame, const TileCtx &w, int a,
+                                                       int start, int key, int n, int len) {
+    unsigned m = 0u;
+    for (int r = 0; r < len; ++r) {
+        const int x = start + r;
+        if (x >= 0 && x < n && in_frame(key, x, n, frame_size(frame, w, a, x))) m |= 1u << r;
+    }
+    return m;
 }
 
 __device__ __forceinline__ int wave_max(int v) {

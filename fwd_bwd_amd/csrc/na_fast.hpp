@@ -69,6 +69,8 @@ struct FwdArgsT {
     T *out;
     float *lse;
     float qscale;  // scale * log2(e)
+    const int *frame;  // windows restricted along frame_axis (null: none)
+    int frame_axis;
 };
 using FwdArgs = FwdArgsT<float>;
 
@@ -85,6 +87,8 @@ struct BwdArgsT {
     // takes the tiles whose inverse walk along H exceeds walk_c exactly when
     // bit 0 of edge is set, and along W exactly when bit 1 is set
     int edge, walk_c;
+    const int *frame;  // windows restricted along frame_axis (null: none)
+    int frame_axis;
 };
 using BwdArgs = BwdArgsT<float>;
 
@@ -159,6 +163,8 @@ __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
         w.n[a] = fdiv(g.ext[a] - r[a] + g.dil[a] - 1, g.f_dil[a]);
         w.k[a] = g.ker[a];
         w.o[a] = o[a];
+        w.r[a] = r[a];
+        w.d[a] = g.dil[a];
         inside = inside && (o[a] < w.n[a]);
     }
     const int64_t HW = (int64_t)g.ext[1] * g.ext[2];
@@ -405,6 +411,14 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
     for (int r = 0; r < 2 * CH; ++r) ed.h[r] = walk_row_valid<CH>(r, lo[1], w.k[1]);
 #pragma unroll
     for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
+    // frames along H (2D grids): walk rows outside the query row's frame window
+    // are masked; along T (3D grids) whole key planes are skipped below
+    if (a.frame && a.frame_axis == 1) {
+        const unsigned fb = frame_bits(us[1], L.p[1], w.n[1], frame_size(a.frame, w, 1, L.p[1]));
+#pragma unroll
+        for (int r = 0; r < 2 * CH; ++r) ed.h[r] = ed.h[r] && ((fb >> r) & 1u);
+    }
+    const int fk_t = (a.frame && a.frame_axis == 0) ? frame_size(a.frame, w, 0, w.o[0]) : 0;
 
     const int ra = a.g.ra, rb = a.g.rb;
     // key-major: this lane supplies entry c of its block's patch
@@ -421,6 +435,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
+        if (a.frame && a.frame_axis == 0 && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         if (j > 0) __syncthreads();
         stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float qr[D];
@@ -493,8 +508,9 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
     }
 
     if (L.active) {
-        store_row<T, D>(a.out + qo, acc, 1.f / l);
-        a.lse[row_off(w, L.p)] = (m + __log2f(l)) * kLn2;
+        // a query whose window is masked away entirely: zero output, lse -inf
+        store_row<T, D>(a.out + qo, acc, l > 0.f ? 1.f / l : 0.f);
+        a.lse[row_off(w, L.p)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -525,6 +541,14 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
     for (int r = 0; r < 2 * CH; ++r) ed.h[r] = walk_row_valid<CH>(r, lo[1], w.k[1]);
 #pragma unroll
     for (int r = 0; r < 2 * CW; ++r) ed.w[r] = walk_row_valid<CW>(r, lo[2], w.k[2]);
+    // frames along H (2D grids): walk rows outside the query row's frame window
+    // are masked; along T (3D grids) whole key planes are skipped below
+    if (a.frame && a.frame_axis == 1) {
+        const unsigned fb = frame_bits(us[1], L.p[1], w.n[1], frame_size(a.frame, w, 1, L.p[1]));
+#pragma unroll
+        for (int r = 0; r < 2 * CH; ++r) ed.h[r] = ed.h[r] && ((fb >> r) & 1u);
+    }
+    const int fk_t = (a.frame && a.frame_axis == 0) ? frame_size(a.frame, w, 0, w.o[0]) : 0;
 
     const int ra = a.g.ra, rb = a.g.rb;
     const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PS;
@@ -550,6 +574,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
         const int tk = t0 + j;
+        if (a.frame && a.frame_axis == 0 && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         if (j > 0) __syncthreads();
         stage_plane<T, D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
         float dor[D];
@@ -678,6 +703,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
     }
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
     const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
+    // frames along H (2D grids): query rows whose frame window misses the key
+    // row are masked; along T (3D grids) whole query planes are skipped below
+    if (a.frame && a.frame_axis == 1)
+        vm[1] &= frame_bits_inverse(a.frame, w, 1, lo[1], L.p[1], w.n[1], 2 * CH);
 
     const int ra = a.g.ra, rb = a.g.rb;
     const char *baseA = smem + (lo[1] - U[1] + (c >> 1)) * ra + (lo[2] - U[2] + (c & 1)) * PS;
@@ -698,6 +727,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
     const int nplanes = T3 ? tq1 - tq0 + 1 : 1;
     for (int j = 0; j < nplanes; ++j) {
         const int tq = tq0 + j;
+        if (a.frame && a.frame_axis == 0 &&
+            !in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq)))
+            continue;
         if (j > 0) __syncthreads();
         stage_plane<T, D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,

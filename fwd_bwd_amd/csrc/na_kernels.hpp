@@ -43,6 +43,8 @@ struct FwdArgs {
     void *out;
     float *lse;
     float qscale;  // scale * log2(e)
+    const int *frame;  // windows restricted along frame_axis (null: none)
+    int frame_axis;
 };
 
 struct BwdArgs {
@@ -54,6 +56,8 @@ struct BwdArgs {
     float *dq_acc;  // KV-parallel variant only
     float qscale;   // scale * log2(e)
     float scale;
+    const int *frame;  // windows restricted along frame_axis (null: none)
+    int frame_axis;
     // dk/dv: when skip_ch > 0, skip the tiles whose 16 x 16 super-tile has an
     // inverse walk of at most skip_ch x skip_cw patches (the register-resident
     // dk/dv kernel covers those)
@@ -268,6 +272,8 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
         key_box(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x], &U.o[x], &U.e[x]);
         us[x] = window_start(lp.f[x], w.n[x], w.k[x]);
         vm[x] = bit_range(window_start(lp.p[x], w.n[x], w.k[x]) - us[x], w.k[x]);
+        if (a.frame && x == a.frame_axis)
+            vm[x] &= frame_bits(us[x], lp.p[x], w.n[x], frame_size(a.frame, w, x, lp.p[x]));
         cnt[x] = window_walk(w.k[x], kPatch[x]);
     }
     const int ncount = cnt[0] * cnt[1] * cnt[2];
@@ -389,7 +395,8 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
         }
         const LanePoint qp = lane_point(w, L);
         if (qp.active) {
-            const float inv = 1.f / Ls;
+            // a query whose window is masked away entirely: zero output, lse -inf
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g] *= inv;
             T *O = static_cast<T *>(a.out) + elem_off(w, qp.p);
@@ -398,7 +405,7 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
 #pragma unroll
                 for (int x = 0; x < PE; x += 4)
                     Io<T>::store4(O + piece_offset<T, D>(j, qd) + x, o + j * PE + x);
-            if (qd == 0) a.lse[row_off(w, qp.p)] = (M + __log2f(Ls)) * kLn2;
+            if (qd == 0) a.lse[row_off(w, qp.p)] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -423,6 +430,8 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
         key_box(w.o[x], kTile[x], kPatch[x], w.n[x], w.k[x], &U.o[x], &U.e[x]);
         us[x] = window_start(lp.f[x], w.n[x], w.k[x]);
         vm[x] = bit_range(window_start(lp.p[x], w.n[x], w.k[x]) - us[x], w.k[x]);
+        if (a.frame && x == a.frame_axis)
+            vm[x] &= frame_bits(us[x], lp.p[x], w.n[x], frame_size(a.frame, w, x, lp.p[x]));
         cnt[x] = window_walk(w.k[x], kPatch[x]);
     }
     const int ncount = cnt[0] * cnt[1] * cnt[2];
@@ -598,6 +607,8 @@ __global__ void __launch_bounds__(kThreads, MODE != 0 ? 1 : kSplitOccupancy<D>) 
         lo[x] = inverse_first(lp.f[x], w.n[x], w.k[x]);
         const int ilo = inverse_first(lp.p[x], w.n[x], w.k[x]);
         vm[x] = bit_range(ilo - lo[x], inverse_last(lp.p[x], w.n[x], w.k[x]) - ilo + 1);
+        if (a.frame && x == a.frame_axis)
+            vm[x] &= frame_bits_inverse(a.frame, w, x, lo[x], lp.p[x], w.n[x], 32);
     }
     const int ncount = cnt[0] * cnt[1] * cnt[2];
 

@@ -127,6 +127,8 @@ struct Args {
     T *o, *dq, *dk, *dv;
     float qscale;  // scale * log2(e)
     float scale;
+    const int *frame;  // windows restricted along frame_axis (null: none)
+    int frame_axis;
 };
 
 // Tile id -> batch, head, residue class and tile origin (class coordinates).
@@ -163,6 +165,8 @@ __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
         w.n[a] = fdiv(g.ext[a] - r[a] + g.dil[a] - 1, g.f_dil[a]);
         w.k[a] = g.ker[a];
         w.o[a] = o[a];
+        w.r[a] = r[a];
+        w.d[a] = g.dil[a];
         inside = inside && (o[a] < w.n[a]);
     }
     // (token, head) row offsets; element offsets are these times head_dim
@@ -409,8 +413,14 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
     float m = -1e30f;  // running maximum, scaled (log2 units)
 
     const int nslab = (Hend - Uh + 3) >> 2;
+    // frames: along T (3D grids) key planes outside the tile's frame window are
+    // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
+    const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
+    const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
+    const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
     for (int j = 0; j < w.k[0]; ++j) {
         const int tk = t0 + j;
+        if (fr_t && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         for (int sl = 0; sl < nslab; ++sl) {
             const int r0 = Uh + 4 * sl;
             __syncthreads();
@@ -421,7 +431,9 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
             // key rows of the slab inside the lane's query window
             bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1];
+            for (int r = 0; r < 4; ++r)
+                hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
+                        (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
                 const int col0 = aw + 4 * b;
@@ -467,14 +479,17 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
         }
     }
     if (!wave_on || !P.active) return;
-    const float inv = 1.f / lsum[0];
+    // a query whose window is masked away entirely: zero output, lse -inf
+    const float inv = lsum[0] > 0.f ? 1.f / lsum[0] : 0.f;
     T *op = a.o + eoff<D>(w, w.o[0], P.h, P.w) + 4 * lg;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
         const float o4[4] = {acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv};
         Io<T>::store4(op + 16 * d, o4);
     }
-    if (lg == 0) a.lse_out[roff(w, w.o[0], P.h, P.w)] = (m + __log2f(lsum[0])) * kLn2;
+    if (lg == 0)
+        a.lse_out[roff(w, w.o[0], P.h, P.w)] =
+            lsum[0] > 0.f ? (m + __log2f(lsum[0])) * kLn2 : -INFINITY;
 }
 
 // ============================================================================
@@ -538,8 +553,14 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
 
     const int nslab = (Hend - Uh + 3) >> 2;
+    // frames: along T (3D grids) key planes outside the tile's frame window are
+    // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
+    const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
+    const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
+    const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
     for (int j = 0; j < w.k[0]; ++j) {
         const int tk = t0 + j;
+        if (fr_t && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         for (int sl = 0; sl < nslab; ++sl) {
             const int r0 = Uh + 4 * sl;
             __syncthreads();
@@ -550,7 +571,9 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
             if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
             bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1];
+            for (int r = 0; r < 4; ++r)
+                hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
+                        (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
                 const int col0 = aw + 4 * b;
@@ -658,7 +681,11 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
     }
 
     const int nslab = (Hend - Uh + 3) >> 2;
+    // frames: along T (3D grids) query planes whose frame window misses the key
+    // plane are skipped; along H (2D grids) such query rows are masked
+    const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
     for (int tq = tq0; tq <= tq1; ++tq) {
+        if (fr_t && !in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq))) continue;
         for (int sl = 0; sl < nslab; ++sl) {
             const int r0 = Uh + 4 * sl;
             __syncthreads();
@@ -672,7 +699,10 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
             // query rows of the slab inside the key's inverse window
             bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0);
+            for (int r = 0; r < 4; ++r)
+                hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0) &&
+                        (!fr_h || in_frame(P.h, r0 + r, nh,
+                                           frame_size(a.frame, w, 1, imin(r0 + r, nh - 1))));
             for (int b = 0; b < nbw; b += 2) {
                 const bool two = b + 1 < nbw;
                 const int col0 = aw + 4 * b;

@@ -35,7 +35,8 @@ EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na
            "na_bwd_dkdv", "na_status_string", "na_window_start", "na_inverse_window",
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
            "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
-           "na_qk_softmax_bwd", "na_source_sha256", "na_bwd_noalloc")
+           "na_qk_softmax_bwd", "na_source_sha256", "na_bwd_noalloc", "na_fwd_framed",
+           "na_bwd_framed")
 
 # rows (batch * tokens * heads) the static delta array of na_bwd_noalloc holds
 NOALLOC_MAX_ROWS = 8388608
@@ -97,6 +98,11 @@ def load() -> ctypes.CDLL:
         lib.na_source_sha256.restype = ctypes.c_char_p
         lib.na_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.na_bwd_noalloc.restype = ctypes.c_int
+        lib.na_fwd_framed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_fwd_framed.restype = ctypes.c_int
+        lib.na_bwd_framed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                      ctypes.c_int32, ctypes.c_int32, vp, vp]
+        lib.na_bwd_framed.restype = ctypes.c_int
         lib.na_window_start.argtypes = [i64, i64, i64, i64]
         lib.na_window_start.restype = i64
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
@@ -307,6 +313,60 @@ def na_bwd_noalloc(q, k, v, out, dout, lse, kernel_size, dilation=1, scale=None,
     _check(load().na_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def _check_frame(frame_kernel: torch.Tensor, q: torch.Tensor):
+    """Per-coordinate window sizes along the outermost grid axis: int32, one
+    per coordinate (q.shape[1]), on q's device, contiguous."""
+    if (not isinstance(frame_kernel, torch.Tensor) or frame_kernel.dtype != torch.int32
+            or tuple(frame_kernel.shape) != (q.shape[1],) or frame_kernel.device != q.device
+            or not frame_kernel.is_contiguous()):
+        raise ValueError(f"frame_kernel must be a contiguous int32 tensor of shape ({q.shape[1]},) "
+                         f"on {q.device}")
+    return _ptr(frame_kernel)
+
+
+def na_fwd_framed(q, k, v, frame_kernel, kernel_size, dilation=1, scale=None, out=None, lse=None):
+    """na_fwd with windows restricted along the outermost axis (T on 3D grids,
+    H on 2D grids) to frame_kernel[x0] positions around each query's x0."""
+    _check_tensors(q, k, v)
+    fp = _check_frame(frame_kernel, q)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_buf(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    _check(load().na_fwd_framed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                fp, _stream_handle(q.device)))
+    return out, lse
+
+
+def na_bwd_framed(q, k, v, out, dout, lse, frame_kernel, kernel_size, dilation=1, scale=None,
+                  variant="gather", kv_splits=0, workspace=None, grads=None):
+    """na_bwd with the windows of na_fwd_framed. Returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, out, dout)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    fp = _check_frame(frame_kernel, q)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    vid = VARIANTS[variant]
+    if kv_splits < 0:
+        raise ValueError("kv_splits must be >= 0")
+    need = bwd_workspace_bytes(p, vid, kv_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(g, name, q.shape, q.dtype, q.device)
+    _check(load().na_bwd_framed(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), vid,
+                                kv_splits, fp, _stream_handle(q.device)))
     return dq, dk, dv
 
 

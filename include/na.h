@@ -146,6 +146,28 @@ na_status na_bwd_dkdv(const na_problem *p, const void *q, const void *k, const v
                       const void *dout, const float *lse, const float *delta, void *dk, void *dv,
                       void *hip_stream);
 
+/* Windows restricted along the outermost axis (T on 3D grids, H on 2D grids):
+ * the NATTEN issue's requester asks for a time kernel that changes from frame
+ * to frame, and the maintainer answers that only masking changes, with tiled
+ * kernels gaining their speed by skipping fully masked key/value tiles.
+ * frame_kernel is a device array of extent[0] int32 values, one per
+ * coordinate x0 along that axis: a query at x0 keeps only the keys whose
+ * coordinate along the axis lies in the window of frame_kernel[x0] positions
+ * around x0 (the same centered-and-shifted rule, in x0's residue class),
+ * inside its window of kernel[0] positions; values are clamped to
+ * [0, kernel[0]], and 0 masks every key of the query (its out is zero and its
+ * lse -inf, and it contributes nothing to the backward). Otherwise exactly
+ * na_fwd and na_bwd (same buffers, rules and errors; frame_kernel must be
+ * non-null and 4-byte aligned). On 3D grids whole key (or query) planes
+ * outside a tile's frame windows are skipped, so runtime follows the
+ * restricted window. */
+na_status na_fwd_framed(const na_problem *p, const void *q, const void *k, const void *v,
+                        void *out, float *lse, const int32_t *frame_kernel, void *hip_stream);
+na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const void *v,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                        void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                        int32_t kv_splits, const int32_t *frame_kernel, void *hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char *na_status_string(na_status s);
 

@@ -247,3 +247,19 @@ def test_workspace_bytes_per_variant_and_copies(lib):
     args = [ctypes.byref(p)] + [fake] * 9 + [fake, ctypes.c_size_t(1 << 40), na.NA_BWD_KVPARALLEL,
                                              -1, None]
     assert lib.na_bwd(*args) == na.NA_ERR_INVALID_ARG
+
+
+def test_framed_entry_points_reject_bad_frame_pointers(lib):
+    """The per-coordinate window sizes of the framed entry points are an int32
+    device array: a null or misaligned pointer is refused before any launch."""
+    p = _p()
+    fake = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 2)
+    for fr in (None, mis):
+        assert lib.na_fwd_framed(ctypes.byref(p), *[fake] * 5, fr, None) == na.NA_ERR_INVALID_ARG
+        ws = na.bwd_workspace_bytes(p, na.NA_BWD_GATHER)
+        assert lib.na_bwd_framed(ctypes.byref(p), *[fake] * 9, fake, ws, 0, 0, fr,
+                                 None) == na.NA_ERR_INVALID_ARG
+    # the problem is validated first
+    bad = _p(kernel=(3, 19))
+    assert lib.na_fwd_framed(ctypes.byref(bad), *[fake] * 5, fake, None) == na.NA_ERR_INVALID_ARG
