@@ -91,7 +91,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 # the sources the fused kernels (the bench phases) are built from
-FUSED_SOURCES = ("na_api.hip", "na_common.hpp", "na_fast.hpp", "na_index.hpp", "na_kernels.hpp")
+FUSED_SOURCES = ("na_api.hip", "na_common.hpp", "na_fast.hpp", "na_host.hpp", "na_index.hpp",
+                 "na_kernels.hpp", "na_mfma16.hpp")
 
 
 def kernel_source_hash():
@@ -434,6 +435,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--variant", default="gather", choices=["gather", "kvparallel"])
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="accumulator copies of the KV-parallel backward (0: atomics)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 3D workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-path leg")
@@ -486,7 +489,7 @@ def main():
         return r, out
 
     w = WORKLOADS[args.workload]
-    r, main_leg = timed(w, args.variant, args.steps, args.warmup)
+    r, main_leg = timed(w, args.variant, args.steps, args.warmup, args.kv_splits)
 
     result = {
         "metric": METRIC,
@@ -504,6 +507,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "grid": list(w.grid),
                    "heads": w.heads, "head_dim": w.head_dim, "kernel": list(w.kernel),
                    "dilation": list(w.dilation), "backward": args.variant,
+                   **({"kv_splits": args.kv_splits} if args.variant == "kvparallel" else {}),
                    "timing": "median of cold passes (1 GiB flush before each pass)"
                    if flush is not None else "median of warm passes"},
         **{k: v for k, v in main_leg.items() if k != "ms_per_step"},

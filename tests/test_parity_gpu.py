@@ -260,21 +260,54 @@ def test_autograd_on_views_of_a_fused_projection():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
+def _axis_strata(n, k, d, rng):
+    """Coordinates along one axis, one per stratum: every coordinate of the two
+    border bands (width k*d: where windows are shifted and inverse windows are
+    irregular, the keys of the border-class launches), then one interior
+    coordinate per residue mod 16*d (every position inside a tile of up to 16
+    along the axis, in every dilation class)."""
+    b = min(n, k * d)
+    lo, hi = list(range(b)), list(range(max(b, n - b), n))
+    inner = [c for c in range(b, n - b)]
+    m = 16 * d
+    mid = []
+    for r in range(m):
+        cs = [c for c in inner if c % m == r]
+        if cs:
+            mid.append(int(rng.choice(cs)))
+    return lo, mid, hi
+
+
 def sample_units(w, n_random=96, seed=0):
-    """Flat (b, token, head) ids: every grid corner and edge midpoint, plus random ones."""
+    """Flat (b, token, head) ids, stratified so that every launch and tile class
+    contributes: for each axis, every coordinate of both border bands and one
+    interior coordinate per tile residue (other axes random); two units in
+    each of the 3^ndim border/interior region combinations (corners, edges,
+    faces, interior); plus random units. Batch elements and heads are dealt
+    round-robin, so each of them appears."""
     rng = np.random.default_rng(seed)
-    grid = w.grid
-    pts = set()
+    grid = tuple(w.grid)
+    strata = [_axis_strata(n, k, d, rng) for n, k, d in zip(grid, w.kernel, w.dilation)]
+    pts = []
+    for a, (lo, mid, hi) in enumerate(strata):
+        for c in lo + mid + hi:
+            p = [int(rng.integers(0, n)) for n in grid]
+            p[a] = c
+            pts.append(tuple(p))
     import itertools
-    for corner in itertools.product(*[(0, 1, g // 2, g - 2, g - 1) for g in grid]):
-        pts.add(tuple(corner))
-    pts = sorted(pts)
-    ids = []
+    for combo in itertools.product(range(3), repeat=len(grid)):
+        for _ in range(2):
+            p = []
+            for a, r in enumerate(combo):
+                band = strata[a][r] or strata[a][1] or strata[a][0]
+                p.append(int(rng.choice(band)))
+            pts.append(tuple(p))
     ntok = int(np.prod(grid))
+    ids = []
     for i, p in enumerate(pts):
         tok = int(np.ravel_multi_index(p, grid))
         b = i % w.batch
-        h = (i * 7) % w.heads
+        h = (i // w.batch) % w.heads
         ids.append((b * ntok + tok) * w.heads + h)
     total = w.batch * ntok * w.heads
     ids.extend(rng.integers(0, total, n_random).tolist())
@@ -286,7 +319,10 @@ FULL = ["2d_1024x1024_k9_h8_d32_f32", "3d_16x256x256_k3x5x5_h8_d32_f32",
         "2d_1024x1024_k9_h8_d32_f16", "3d_16x256x256_k3x5x5_h8_d32_f16"]
 
 
-FULL_CASES = [(n, "gather") for n in FULL] + [("2d_1024x1024_k9_h8_d32_f32", "kvdet")]
+FULL_CASES = [(n, "gather") for n in FULL] + [("2d_1024x1024_k9_h8_d32_f32", "kvdet"),
+                                              ("2d_1024x1024_k9_h8_d32_f32", "kvparallel"),
+                                              ("3d_16x256x256_k3x5x5_h8_d32_f32", "kvdet"),
+                                              ("2d_b4_512x512_k13_d2_h4_d64_bf16", "kvdet")]
 
 
 @pytest.mark.parametrize("name,variant", FULL_CASES, ids=[f"{n}-{v}" for n, v in FULL_CASES])
@@ -311,4 +347,11 @@ def test_full_workload_sampled(name, variant):
     dv_sum = got["dv"].double().sum(axes)
     do_sum = torch.as_tensor(dout).double().sum(axes).to(dv_sum.device)
     assert rel_err(dv_sum.cpu().numpy(), do_sum.cpu().numpy()) < TOL[w.dtype]
+    # sum over keys of dk is 0 for every (b, head, channel): the rows of dS sum
+    # to zero because delta = rowsum(dO o O) = sum_j P_j dP_j. Rounding of the
+    # stored dk adds up like a random walk, so the bound is tol * ||dk||_2.
+    dk = got["dk"].double()
+    dk_sum = dk.sum(axes).abs()
+    dk_l2 = dk.square().sum(axes).sqrt()
+    assert bool((dk_sum <= TOL[w.dtype] * dk_l2).all()), float((dk_sum / dk_l2).max())
     assert torch.isfinite(got["dq"]).all() and torch.isfinite(got["dk"]).all()
