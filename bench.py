@@ -75,7 +75,7 @@ def stats(xs):
 # contraction FLOPs each kernel performs per (query or key) x window entry x channel,
 # without tile waste: fwd = QK^T + PV; dq = QK^T + dO V^T + dS K;
 # dk/dv = QK^T + dO V^T + P^T dO + dS^T Q
-KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+KERNEL_FLOP_UNITS = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8, "bwd_kvparallel": 10}
 
 # the bf16 workloads (3D 2x8x128x128 with a 5x7x7 window; 2D 4x512x512, 13x13, dilation 2,
 # head_dim 64), timed beside the headline for their roofline fractions
@@ -132,7 +132,7 @@ def algorithmic_bytes(w):
     fwd = 4 * t + rows                  # q, k, v read; out written; lse written
     bwd = 8 * t + rows + 2 * rows       # q, k, v, out, dout read; dq, dk, dv written; lse; delta w+r
     return fwd, bwd, {"fwd": 4 * t + rows, "bwd_dq": 5 * t + 2 * rows,
-                      "bwd_dkdv": 6 * t + 2 * rows}
+                      "bwd_dkdv": 6 * t + 2 * rows, "bwd_kvparallel": bwd}
 
 
 class Runner:
@@ -326,7 +326,7 @@ def summarize(w, per):
     }
 
 
-def roofline(w, per):
+def roofline(w, per, tag=None):
     """Roofline entry of the longest kernel (by median duration): its
     contraction FLOPs and algorithmic bytes per launch; bound by whichever of
     the MFMA peak of the workload's type and HBM its intensity puts it under."""
@@ -349,15 +349,15 @@ def roofline(w, per):
         achieved = by / t / 1e9
         out.update({"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)})
-    out["traffic"] = recorded_traffic(name, w.name)
+    out["traffic"] = recorded_traffic(name, tag or w.name)
     return out
 
 
-def leg(w, per, wall=None, warm=None):
+def leg(w, per, wall=None, warm=None, tag=None):
     """Summary of one timed workload: cold (flushed) medians, the roofline of
     its longest kernel, and the warm medians beside them."""
     out = summarize(w, per)
-    out["roofline"] = roofline(w, per)
+    out["roofline"] = roofline(w, per, tag)
     if wall is not None:
         out["wall_ms_per_step"] = round(wall, 4)
     if warm is not None:
@@ -483,7 +483,8 @@ def main():
         warm = None
         if flush is not None:
             warm, _ = r.time(steps, 0, None)
-        out = leg(wl, per, wall, warm)
+        out = leg(wl, per, wall, warm,
+                  wl.name if variant == "gather" else f"{wl.name}_kv{kv_splits}")
         log(f"[bench] {wl.name} ({variant}): step {out['ms_per_step']} ms, "
             f"fwd {out['fwd_ms']} ms, bwd {out['bwd_ms']} ms, {out['tflops_total']} TFLOP/s")
         return r, out
