@@ -92,7 +92,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # the sources the fused kernels (the bench phases) are built from
 FUSED_SOURCES = ("na_api.hip", "na_common.hpp", "na_fast.hpp", "na_host.hpp", "na_index.hpp",
-                 "na_kernels.hpp", "na_mfma16.hpp")
+                 "na_kernels.hpp", "na_m16.hip", "na_mfma16.hpp")
 
 
 def kernel_source_hash():

@@ -9,7 +9,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libna.so")
-SOURCES = [os.path.join(CSRC, "na_api.hip"), os.path.join(CSRC, "na_unfused.hip")]
+SOURCES = [os.path.join(CSRC, "na_api.hip"), os.path.join(CSRC, "na_m16.hip"),
+           os.path.join(CSRC, "na_unfused.hip")]
+# per-source flags: the 16-bit MFMA kernels run without IEEE-mode NaN handling
+# (their maxima then need no operand canonicalisation; they form no NaNs)
+SOURCE_FLAGS = {"na_m16.hip": ["-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]}
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
@@ -56,7 +60,8 @@ def build(verbose: bool = False) -> str:
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(OBJDIR, os.path.splitext(os.path.basename(src))[0] + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", *inc, "-o", obj, src]
+        cmd = [hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", *inc,
+               "-o", obj, src]
         if verbose:
             print(" ".join(cmd))
         objs.append(obj)

@@ -501,6 +501,7 @@ struct M16Plan {
     int lds;
 };
 
+
 // Columns a slab row must hold: the end of the last block any wave of any
 // 16-column tile walks, relative to its tile's box start (the same formulas
 // the kernels evaluate), rounded to groups of four.
@@ -551,15 +552,11 @@ bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
     g.nres = nres;
     g.n_tiles = (int)n_tiles;
     g.box_w = m16_box_w(q, kind == 2);
-    const int NC = (int)q.head_dim * 2 / 16;
-    g.km_pitch = ((g.box_w * NC) | 1) * 16;                 // odd number of 16-byte chunks
-    // transposed slab: one column of four rows per 8 * head_dim + 128 bytes
-    g.tr_pitch = g.box_w * (8 * (int)q.head_dim + 128);
-    const int64_t lds = kind == 0   ? 4LL * g.km_pitch + g.tr_pitch
-                        : kind == 1 ? 8LL * g.km_pitch + g.tr_pitch
-                                    : 8LL * g.km_pitch + 2LL * g.tr_pitch + 32LL * g.box_w;
-    if (lds > kLdsMax) return false;
-    pl->lds = (int)lds;
+    // the kernels are compiled for slab rows of up to 24, 32 or 48 points
+    // (static LDS: two buffers of two slabs each)
+    g.wmax = g.box_w <= 24 ? 24 : g.box_w <= 32 ? 32 : 48;
+    if (g.box_w > g.wmax) return false;
+    pl->lds = 0;
     g.f_heads = na::make_fastdiv(g.heads);
     g.f_tw = na::make_fastdiv(g.tiles[2]);
     g.f_th = na::make_fastdiv(g.tiles[1]);
@@ -570,12 +567,10 @@ bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
     return true;
 }
 
-template <typename Kern, typename Args>
-na_status launch_m16(Kern kern, const M16Plan &pl, const Args &a, hipStream_t s) {
-    if (!na_host::lds_limit_once((const void *)kern)) return NA_ERR_HIP;
-    if (pl.g.n_tiles == 0) return NA_OK;
-    hipLaunchKernelGGL(kern, dim3(pl.g.n_tiles), dim3(na::m16::kTG), pl.lds, s, a);
-    return hipGetLastError() == hipSuccess ? NA_OK : NA_ERR_HIP;
+// kind 0: forward, 1: dq, 2: dk/dv (the kernels are built in na_m16.hip)
+template <typename T, int D>
+na_status launch_m16(int kind, const M16Plan &, const na::m16::Args<T> &a, hipStream_t s) {
+    return na::m16::launch<T, D>(kind, a, s) == hipSuccess ? NA_OK : NA_ERR_HIP;
 }
 
 dim3 flat_grid(int64_t n) { return dim3((unsigned)((n + kThreads - 1) / kThreads)); }
@@ -598,7 +593,7 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
             ma.qscale = a.qscale;
             ma.frame = a.frame;
             ma.frame_axis = a.frame_axis;
-            return launch_m16(na::m16::fwd_kernel<T, D>, mp, ma, s);
+            return launch_m16<T, D>(0, mp, ma, s);
         }
     }
     FastPlan pl;
@@ -691,12 +686,12 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             // dq (which also writes delta) strictly before dk/dv, which reads it
             if (phases & kPhaseDq) {
                 ma.g = mq.g;
-                const na_status st = launch_m16(na::m16::dq_kernel<T, D>, mq, ma, s);
+                const na_status st = launch_m16<T, D>(1, mq, ma, s);
                 if (st != NA_OK) return st;
             }
             if (phases & kPhaseDkdv) {
                 ma.g = mk.g;
-                return launch_m16(na::m16::dkdv_kernel<T, D>, mk, ma, s);
+                return launch_m16<T, D>(2, mk, ma, s);
             }
             return NA_OK;
         }

@@ -12,14 +12,20 @@
 //
 // Work decomposition. A wave owns a patch of 16 points (1 x 4 x 4 along T, H,
 // W in class coordinates of one residue class): queries in the forward and dq
-// kernels, keys in the dk/dv kernel. A workgroup of four waves owns a 1 x 4 x
-// 16 tile (its waves side by side along W), so all its waves share the same
-// rows along T and H and need the same rows of the other side's box: the box
-// is staged one 4-row slab at a time (one plane along T), and every wave walks
-// the 4 x 4 blocks of its own patch's window union (or inverse union) inside
-// the slab. One MFMA contracts 16 points of one side with a 4 x 4 block of the
-// other over 32 channels; pairs of blocks (32 points) form the 32-deep
-// reductions of the weighted sums.
+// kernels, keys in the dk/dv kernel. A workgroup of eight waves owns a 1 x 8 x
+// 16 tile (two rows of four patches), so all its waves need rows of the same
+// planes of the other side's box: the box is staged one 4-row slab of one
+// plane at a time, and every wave walks the 4 x 4 blocks of its own patch's
+// window union (or inverse union) inside the slab, skipping slabs outside it.
+// One MFMA contracts 16 points of one side with a 4 x 4 block of the other
+// over 32 channels; pairs of blocks (32 points) form the 32-deep reductions of
+// the weighted sums.
+//
+// Staging. Slabs are copied with direct global-to-LDS loads into one layout,
+// key-major: each point's channels contiguous in 16-byte chunks (XOR-swizzled
+// at 64 channels), rows an odd number of chunks apart. With two slab buffers
+// the next slab's loads are issued before the current slab is walked, so they
+// run under the walk, and one barrier per slab orders the two.
 //
 // Operand layouts (lane l, lane group g = l / 16, n = l % 16):
 //  * A (16 x 32) and B (32 x 16) operands: lane l holds row / column n and
@@ -27,27 +33,26 @@
 //    4g .. 4g + 3 of column n.
 //  * A block is 4 slab rows by 4 columns; its point m sits at row m % 4,
 //    column m / 4. Scores are formed transposed, S^T = K Q^T: A = a key block
-//    (point n's channels from LDS), B = the wave's queries (registers). Lane l
-//    then holds the scores of query n against column g of the block, rows
-//    0..3 -- exactly the B operand of a weighted sum over a pair of blocks
-//    whose reduction entries 8g .. 8g + 3 are column g of the first block and
-//    8g + 4 .. 8g + 7 column g of the second: O^T += V^T P^T, with A = V^T
-//    read as the four rows of one column at one channel. One lane's four
-//    scores share their column: the window test along W is one compare per
-//    block, the test along H one per slab row.
-//  * LDS: "key-major" slabs hold each point's channels contiguously (16-byte
-//    chunks, XOR-swizzled at 64 channels, odd row pitch in chunks: the A reads
-//    of 16 points at one chunk hit 16 different bank groups); "transposed"
-//    slabs hold, per column and channel, the 8 bytes of the column's four rows,
-//    columns 128 bytes off a multiple of 256 apart, so the 8-byte reads of an
-//    A operand come from 64 different banks.
+//    (point n's chunk of channels, one 16-byte LDS read), B = the wave's
+//    queries (registers). Lane l then holds the scores of query n against
+//    column g of the block, rows 0..3 -- exactly the B operand of a weighted
+//    sum over a pair of blocks whose reduction entries 8g .. 8g + 3 are column
+//    g of the first block and 8g + 4 .. 8g + 7 column g of the second:
+//    O^T += V^T P^T. Its A operand (channel 16d + n of the four rows of
+//    column g) comes from the same key-major slab through the LDS transpose
+//    read ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + s
+//    receives element s of the 8 bytes addressed by lanes a, a + 4, a + 8 and
+//    a + 12 (in that order), so lane a + 4j addresses row j at channels
+//    16d + 4a .. 16d + 4a + 3.
 //  * Row sums of the weights come out of the MFMA as well: one more product
 //    against an all-ones A operand gives every lane the sum for its query.
 //
 // Windows are clamped by index arithmetic only: a score is kept when the key
 // lies in the query's window (equivalently the query in the key's inverse
 // window), which also rejects every point a slab holds past the grid (those
-// repeat the last grid point, so they are finite).
+// repeat the last grid point, so they are finite). Reads past a wave's last
+// block (an odd number of blocks) land on staged or cleared LDS, so they are
+// finite too, and their scores are masked.
 #pragma once
 
 #include "na_common.hpp"
@@ -108,11 +113,10 @@ constexpr int kTH = 8, kTW = 16;  // tile rows (H) and columns (W); T: one plane
 struct Geom {
     int ext[3], ker[3], dil[3];
     int heads, batch;
-    int tiles[3];  // per axis over the largest residue class: planes, 4-row tiles, 16-column tiles
+    int tiles[3];  // per axis over the largest residue class: planes, 8-row tiles, 16-column tiles
     int nres, n_tiles;
     int box_w;     // points per slab row (a multiple of 4)
-    int km_pitch;  // bytes per slab row, key-major layout
-    int tr_pitch;  // bytes of a transposed slab (all four rows)
+    int wmax;      // the kernel's compiled bound on box_w (24, 32 or 48)
     FastDiv f_heads, f_tw, f_th, f_t, f_nres;
     FastDiv f_dil[3], f_dil21;
 };
@@ -229,59 +233,26 @@ __device__ __forceinline__ void stage_km(const T *src, const TileCtx &w, int tk,
     }
 }
 
-// Transposed slab: channel-major by slab column. Column w of the slab holds,
-// for each channel d, the 8 bytes of its four rows (row 0 first) at
-// lds + w * tr_col<D>() + 8 * d. Columns are 8 * D + 128 bytes apart (128 off
-// a multiple of 256), so the two lane groups of a half wave, reading
-// neighbouring columns, hit different banks. Staged through registers: a
-// thread loads one 16-byte chunk (8 channels) of each of the column's four
-// rows and writes 64 bytes.
-template <int D>
-__device__ __forceinline__ constexpr int tr_col() {
-    return 8 * D + 128;
+// Zeroes the workgroup's dynamic LDS (bytes: a multiple of 16).
+__device__ __forceinline__ void clear_lds(char *lds, int bytes) {
+    for (int i = (int)threadIdx.x * 16; i < bytes; i += kTG * 16)
+        *reinterpret_cast<uint4 *>(lds + i) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void stage_tr(const T *src, const TileCtx &w, int tk, int r0, int U2,
-                                         int box_w, char *lds) {
-    constexpr int NC = D * 2 / 16;
-    const int tasks = box_w * NC;
-    const int rows[4] = {imin(r0, w.n[1] - 1), imin(r0 + 1, w.n[1] - 1), imin(r0 + 2, w.n[1] - 1),
-                         imin(r0 + 3, w.n[1] - 1)};
-    for (int t = threadIdx.x; t < tasks; t += kTG) {
-        const int c = t % NC, col = t / NC;
-        const int c2 = imin(U2 + col, w.n[2] - 1);
-        uint4 x[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            x[r] = *reinterpret_cast<const uint4 *>(src + eoff<D>(w, tk, rows[r], c2) + c * 8);
-        char *dst = lds + col * tr_col<D>() + c * 64;
-        const uint32_t a0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
-        const uint32_t a1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
-        const uint32_t a2[4] = {x[2].x, x[2].y, x[2].z, x[2].w};
-        const uint32_t a3[4] = {x[3].x, x[3].y, x[3].z, x[3].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint4 o;  // channels 2e and 2e + 1, rows 0..3 each
-            o.x = (a0[e] & 0xffffu) | (a1[e] << 16);
-            o.y = (a2[e] & 0xffffu) | (a3[e] << 16);
-            o.z = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-            o.w = (a2[e] >> 16) | (a3[e] & 0xffff0000u);
-            *reinterpret_cast<uint4 *>(dst + 16 * e) = o;
-        }
-    }
+// (logsumexp, delta) of the slab point thread i stages (i < 4 box_w; column
+// major: the four rows of column c at 4c .. 4c + 3). rows_load only issues the
+// loads, so that they can run under a walk; rows_store writes
+// (logsumexp * log2(e), delta) to LDS.
+__device__ __forceinline__ float2 rows_load(const float *lse, const float *delta,
+                                            const TileCtx &w, int tk, int r0, int U2, int box_w) {
+    const int i = threadIdx.x;
+    if (i >= 4 * box_w) return make_float2(0.f, 0.f);
+    const int col = i >> 2, r = i & 3;
+    const int64_t ro = roff(w, tk, imin(r0 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1));
+    return make_float2(lse[ro], delta[ro]);
 }
-
-// (logsumexp * log2(e), delta) of every point of a slab, column-major: the
-// four rows of column w at rows[4 w .. 4 w + 3].
-__device__ __forceinline__ void stage_rows16(const float *lse, const float *delta,
-                                             const TileCtx &w, int tk, int r0, int U2, int box_w,
-                                             float2 *rows) {
-    for (int i = threadIdx.x; i < 4 * box_w; i += kTG) {
-        const int col = i >> 2, r = i & 3;
-        const int64_t ro = roff(w, tk, imin(r0 + r, w.n[1] - 1), imin(U2 + col, w.n[2] - 1));
-        rows[i] = make_float2(lse[ro] * kLog2e, delta[ro]);
-    }
+__device__ __forceinline__ void rows_store(float2 v, int box_w, float2 *rows) {
+    if ((int)threadIdx.x < 4 * box_w) rows[threadIdx.x] = make_float2(v.x * kLog2e, v.y);
 }
 
 // Maximum and sum over the four lanes n, n + 16, n + 32, n + 48 (the lane
@@ -315,26 +286,60 @@ __device__ __forceinline__ Pt patch_point(const TileCtx &w, int wave, int n) {
     return p;
 }
 
-// Per-lane LDS addressing of the A operands. A block of 16 points is four
-// slab rows by four columns [col0, col0 + 4) (col0 a multiple of 4), point m
-// at row m % 4, column col0 + m / 4; so lane group g of an MFMA result holds
-// column col0 + g, one row per register.
-//  * key-major: lane n supplies point n, chunk (lg + 4h): base km(h) plus
-//    col0 * NC * 16 (the swizzle only depends on the column within the block);
-//  * transposed: lane (g, n) supplies channel n + 16 d of column col0 + g
-//    (block one of a pair) or col0 + 4 + g (block two): base tr plus
-//    col0 * tr_col, channel blocks 128 bytes apart.
+// A wave's walk: block columns [aw, aw + 4 nbw) of the slab rows (relative to
+// the box start U2, aw a multiple of 4), slab rows [wr0, wr1) of its patch's
+// window (or inverse-window) union; the workgroup's slabs start at row Uh.
+struct Walk {
+    int Uh, U2, nslab, aw, nbw, wr0, wr1;
+    bool on;  // the wave's patch has a point inside the grid
+};
+template <bool Inverse>
+__device__ __forceinline__ int wfirst(int x, int n, int k) {
+    return Inverse ? inverse_first(x, n, k) : window_start(x, n, k);
+}
+template <bool Inverse>
+__device__ __forceinline__ int wend(int x, int n, int k) {
+    return Inverse ? inverse_last(x, n, k) + 1 : window_start(x, n, k) + k;
+}
+template <bool Inverse>
+__device__ __forceinline__ Walk make_walk(const TileCtx &w, int wave) {
+    const int nh = w.n[1], nw = w.n[2], kh = w.k[1], kw = w.k[2];
+    Walk k;
+    k.Uh = wfirst<Inverse>(w.o[1], nh, kh);
+    const int hend = wend<Inverse>(imin(w.o[1] + kTH - 1, nh - 1), nh, kh);
+    k.nslab = (hend - k.Uh + 3) >> 2;
+    k.U2 = wfirst<Inverse>(w.o[2], nw, kw);
+    k.on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
+    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    k.aw = __builtin_amdgcn_readfirstlane((wfirst<Inverse>(pw0, nw, kw) - k.U2) & ~3);
+    k.nbw = __builtin_amdgcn_readfirstlane((wend<Inverse>(pw1, nw, kw) - k.U2 - k.aw + 3) >> 2);
+    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
+    k.wr0 = __builtin_amdgcn_readfirstlane(wfirst<Inverse>(ph0, nh, kh));
+    k.wr1 = __builtin_amdgcn_readfirstlane(wend<Inverse>(ph1, nh, kh));
+    return k;
+}
+
+// Per-lane LDS byte offsets within a slab (block columns added per block).
+//  * km: A operand of a score product: lane n supplies point n (row n % 4,
+//    column n / 4), chunk lg + 4 h;
+//  * tr: transpose read of channels 16 d + 4 (n % 4) .. + 3 of row n / 4 of
+//    the lane group's column (see the header).
 template <int D>
 struct LaneAddr {
-    static constexpr int NC = D * 2 / 16, NH = D / 32;
+    static constexpr int NC = D * 2 / 16, NH = D / 32, ND = D / 16;
     int km[NH];
-    int tr;
-    __device__ __forceinline__ LaneAddr(int km_pitch, int lg, int n) {
+    int tr[ND];
+    __device__ __forceinline__ LaneAddr(int pitch, int lg, int n) {
         const int col = n >> 2, row = n & 3;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-            km[h] = row * km_pitch + ((col * NC + ((lg + 4 * h) ^ kswz<NC>(col))) << 4);
-        tr = lg * tr_col<D>() + 8 * n;
+            km[h] = row * pitch + ((col * NC + ((lg + 4 * h) ^ kswz<NC>(col))) << 4);
+        // block columns start at multiples of 4, so column lg of a block has
+        // the swizzle of lg
+        const int a = n & 3, j = n >> 2, sw = kswz<NC>(lg);
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            tr[d] = j * pitch + ((lg * NC + ((2 * d + (a >> 1)) ^ sw)) << 4) + ((a & 1) << 3);
     }
 };
 
@@ -342,12 +347,26 @@ __device__ __forceinline__ uint4 km_at(const char *lds, int addr) {
     return *reinterpret_cast<const uint4 *>(lds + addr);
 }
 
-// A operand of a weighted sum over a pair of blocks: channel 16 d + n of the
-// lane group's column in block one (t0) and block two (t1).
-__device__ __forceinline__ uint4 tr_at(const char *t0, const char *t1, int d) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(t0 + 128 * d);
-    const uint2 b = *reinterpret_cast<const uint2 *>(t1 + 128 * d);
-    return make_uint4(a.x, a.y, b.x, b.y);
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+__device__ __forceinline__ uint2 lds_tr(const char *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(const_cast<char *>(p)));
+    return __builtin_bit_cast(uint2, v);
+#else
+    (void)p;
+    return make_uint2(0u, 0u);
+#endif
+}
+
+// A operand of a weighted sum over the blocks at blk and blk + second (second
+// = 0 repeats the first block when a wave has an odd number of blocks; its
+// weights are zero then): channel 16 d + n of the lane group's column, rows
+// 0..3 of each block.
+__device__ __forceinline__ uint4 tr_pair(const char *blk, int second, int tr) {
+    const uint2 x = lds_tr(blk + tr), y = lds_tr(blk + second + tr);
+    return make_uint4(x.x, x.y, y.x, y.y);
 }
 
 // Weights are rescaled only when a score exceeds the running maximum by more
@@ -355,45 +374,97 @@ __device__ __forceinline__ uint4 tr_at(const char *t0, const char *t1, int d) {
 // and in the 16-bit operands, and the rescale is rare.
 constexpr float kLazyRescale = 8.f;
 
+// Slab steps of a walk over planes [p0, p1] (those with plane_ok) times slabs
+// [0, nslab), alternating between two buffers (even steps in b0, odd ones in
+// b1): step s + 1 is staged into the other buffer while step s is walked, and
+// one barrier per step separates the two. The buffers are distinct LDS
+// arrays, each named at compile time in its half of the loop, so the compiler
+// sees that the walk's LDS reads and the staging's direct loads into the other
+// buffer do not alias and lets the loads run under the walk.
+// stage(p, sl, buf, i) issues the loads of a step into buffer i, walk(p, sl,
+// buf, i) consumes one, done(i) runs after a walk that has a next step (in
+// buffer i).
+template <typename OK, typename Stage, typename WalkFn, typename Done>
+__device__ __forceinline__ void slab_steps(int p0, int p1, int nslab, char *b0, char *b1,
+                                           OK plane_ok, Stage stage, WalkFn walk, Done done) {
+    int p = p0;
+    while (p <= p1 && !plane_ok(p)) ++p;
+    if (p > p1) return;
+    stage(p, 0, b0, 0);
+    int sl = 0;
+    auto next = [&](int &pn, int &sn) {
+        pn = p;
+        sn = sl + 1;
+        if (sn == nslab) {
+            sn = 0;
+            ++pn;
+            while (pn <= p1 && !plane_ok(pn)) ++pn;
+        }
+        return pn <= p1;
+    };
+    for (;;) {
+        int pn, sn;
+        bool more = next(pn, sn);
+        stage_wait();
+        if (more) stage(pn, sn, b1, 1);
+        walk(p, sl, b0, 0);
+        if (!more) return;
+        done(1);
+        p = pn;
+        sl = sn;
+        more = next(pn, sn);
+        stage_wait();
+        if (more) stage(pn, sn, b0, 0);
+        walk(p, sl, b1, 1);
+        if (!more) return;
+        done(0);
+        p = pn;
+        sl = sn;
+    }
+}
+
+// Static LDS of a kernel with slab rows of up to W points: per buffer the
+// slabs of two tensors and a slack that takes the reads of a wave's odd last
+// block past its slab.
+template <int D, int W>
+struct Slabs {
+    static constexpr int NC = D * 2 / 16;
+    static constexpr int kPitch = ((W * NC) | 1) * 16;  // odd number of 16-byte chunks
+    static constexpr int kSlab = 4 * kPitch;
+    static constexpr int kBuf = 2 * kSlab + 512;
+};
+
 // ============================================================================
 // Forward: out, lse.
-template <typename T, int D>
+template <typename T, int D, int W>
 __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    using S = Slabs<D, W>;
+    __shared__ __align__(16) char buf0[S::kBuf];
+    __shared__ __align__(16) char buf1[S::kBuf];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32, BLK = 4 * NC * 16;
     const Geom &g = a.g;
     TileCtx w;
     if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
-    char *Kl = smem;
-    char *Vl = smem + 4 * g.km_pitch;
+    constexpr int slab = S::kSlab;  // per buffer: the K slab, then the V slab
+    clear_lds(buf0, S::kBuf);
+    clear_lds(buf1, S::kBuf);
+    __syncthreads();
 
-    // the workgroup's box: planes, rows (shared by all waves) and columns
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
-    const int Uh = window_start(w.o[1], nh, w.k[1]);
-    const int Hend = window_start(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + w.k[1];
-    const int U2 = window_start(w.o[2], nw, w.k[2]);
-    // this wave's blocks: from its patch's first window start (aligned down to
-    // a group of four columns of the box) to its last window end
-    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
-    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
-    const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
-    const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
-    // rows of this wave's window union: slabs outside it are skipped
-    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
-    const int wr0 = window_start(ph0, nh, w.k[1]), wr1 = window_start(ph1, nh, w.k[1]) + w.k[1];
-
+    const Walk wk = make_walk<false>(w, wave);
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
     // column of this lane group in a block relative to the lane's window start
-    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - U2);
+    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - wk.U2);
     // scores are kept unscaled; a negative scale flips the query's sign instead.
     // A zero scale becomes the tiniest normal one (every weight still exp2(0)
     // in fp32), so that masked scores (-inf) times it stay -inf.
     const bool neg = a.qscale < 0.f;
     const float c = fmaxf(neg ? -a.qscale : a.qscale, 1.1754944e-38f);
+    const float ic = 1.f / c;
     uint4 qv[NH];
     {
         const T *qp = a.q + eoff<D>(w, w.o[0], P.h, P.w) + 8 * lg;
@@ -404,81 +475,82 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
             qv[h].x ^= flip; qv[h].y ^= flip; qv[h].z ^= flip; qv[h].w ^= flip;
         }
     }
-    const LaneAddr<D> la(g.km_pitch, lg, n);
+    const LaneAddr<D> la(S::kPitch, lg, n);
     const uint4 ones = make_uint4(Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2, Mf<T>::kOne2);
+    const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
 
-    f4 acc[ND], lsum = f4{0.f, 0.f, 0.f, 0.f};
+    f4 acc[ND], lsum = zero;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
-    float m = -1e30f;  // running maximum, scaled (log2 units)
+    for (int d = 0; d < ND; ++d) acc[d] = zero;
+    float m = -1e30f;            // running maximum, scaled (log2 units)
+    float thr = (m + kLazyRescale) * ic;  // unscaled score that triggers a rescale
 
-    const int nslab = (Hend - Uh + 3) >> 2;
     // frames: along T (3D grids) key planes outside the tile's frame window are
     // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
     const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
-    for (int j = 0; j < w.k[0]; ++j) {
-        const int tk = t0 + j;
-        if (fr_t && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
-        for (int sl = 0; sl < nslab; ++sl) {
-            const int r0 = Uh + 4 * sl;
-            __syncthreads();
-            stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kl);
-            stage_tr<T, D>(a.v, w, tk, r0, U2, g.box_w, Vl);
-            stage_wait();
-            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
-            // key rows of the slab inside the lane's query window
-            bool hr[4];
+    auto plane_ok = [&](int tk) { return !fr_t || in_frame(tk, w.o[0], w.n[0], fk_t); };
+    auto stage = [&](int tk, int sl, char *buf, int) {
+        stage_km<T, D>(a.k, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf);
+        stage_km<T, D>(a.v, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf + slab);
+    };
+    auto walk = [&](int, int sl, const char *buf, int) {
+        const int r0 = wk.Uh + 4 * sl;
+        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        const char *Kc = buf, *Vc = buf + slab;
+        // key rows of the slab inside the lane's query window
+        bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
-                        (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
-            for (int b = 0; b < nbw; b += 2) {
-                const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b;
-                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        for (int r = 0; r < 4; ++r)
+            hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
+                    (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
+        for (int b = 0; b < wk.nbw; b += 2) {
+            const int col0 = wk.aw + 4 * b;
+            const bool two = b + 1 < wk.nbw;
+            const char *kb = Kc + col0 * NC * 16;
+            f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(kb + BLK, la.km[0]), qv[0], zero);
 #pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    s0 = Mf<T>::mma(km_at(Kl + col0 * NC * 16, la.km[h]), qv[h], s0);
-                if (two) {
-#pragma unroll
-                    for (int h = 0; h < NH; ++h)
-                        s1 = Mf<T>::mma(km_at(Kl + (col0 + 4) * NC * 16, la.km[h]), qv[h], s1);
-                }
-                const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
-                const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
-                float x[8];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[r] = (w0 && hr[r]) ? s0[r] : -INFINITY;
-                    x[4 + r] = (w1 && hr[r]) ? s1[r] : -INFINITY;
-                }
-                const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-                const float ms = xmax4(mx) * c;
-                if (__any(ms > m + kLazyRescale)) {
-                    const float mn = ms > m + kLazyRescale ? ms : m;
-                    const float alpha = fast_exp2(m - mn);
-                    m = mn;
-#pragma unroll
-                    for (int d = 0; d < ND; ++d) acc[d] *= alpha;
-                    lsum *= alpha;
-                }
-                uint4 pb;
-                pb.x = Mf<T>::pack(fast_exp2(fmaf(x[0], c, -m)), fast_exp2(fmaf(x[1], c, -m)));
-                pb.y = Mf<T>::pack(fast_exp2(fmaf(x[2], c, -m)), fast_exp2(fmaf(x[3], c, -m)));
-                pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
-                pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
-                const char *t0p = Vl + la.tr + col0 * tr_col<D>();
-                const char *t1p = two ? t0p + 4 * tr_col<D>() : t0p;
-#pragma unroll
-                for (int d = 0; d < ND; ++d) acc[d] = Mf<T>::mma(tr_at(t0p, t1p, d), pb, acc[d]);
-                lsum = Mf<T>::mma(ones, pb, lsum);
+            for (int h = 1; h < NH; ++h) {
+                s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
+                s1 = Mf<T>::mma(km_at(kb + BLK, la.km[h]), qv[h], s1);
             }
+            const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
+            const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
+            float x[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[r] = (w0 && hr[r]) ? s0[r] : -INFINITY;
+                x[4 + r] = (w1 && hr[r]) ? s1[r] : -INFINITY;
+            }
+            const float mx = xmax4(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+            if (__any(mx > thr)) {
+                const float mn = mx > thr ? mx * c : m;
+                const float alpha = fast_exp2(m - mn);
+                m = mn;
+                thr = (m + kLazyRescale) * ic;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+                lsum *= alpha;
+            }
+            uint4 pb;
+            pb.x = Mf<T>::pack(fast_exp2(fmaf(x[0], c, -m)), fast_exp2(fmaf(x[1], c, -m)));
+            pb.y = Mf<T>::pack(fast_exp2(fmaf(x[2], c, -m)), fast_exp2(fmaf(x[3], c, -m)));
+            pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
+            pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
+            const char *vb = Vc + col0 * NC * 16;
+            const int second = two ? BLK : 0;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                acc[d] = Mf<T>::mma(tr_pair(vb, second, la.tr[d]), pb, acc[d]);
+            lsum = Mf<T>::mma(ones, pb, lsum);
         }
-    }
-    if (!wave_on || !P.active) return;
+    };
+    slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
+
+    if (!wk.on || !P.active) return;
     // a query whose window is masked away entirely: zero output, lse -inf
     const float inv = lsum[0] > 0.f ? 1.f / lsum[0] : 0.f;
     T *op = a.o + eoff<D>(w, w.o[0], P.h, P.w) + 4 * lg;
@@ -494,35 +566,28 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
 
 // ============================================================================
 // Backward, query side: delta = <dout, out> and dq.
-template <typename T, int D>
+template <typename T, int D, int W>
 __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    using S = Slabs<D, W>;
+    __shared__ __align__(16) char buf0[S::kBuf];
+    __shared__ __align__(16) char buf1[S::kBuf];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32, BLK = 4 * NC * 16;
     const Geom &g = a.g;
     TileCtx w;
     if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
-    char *Vk = smem;
-    char *Kk = smem + 4 * g.km_pitch;
-    char *Kt = smem + 8 * g.km_pitch;
+    constexpr int slab = S::kSlab;  // per buffer: the V slab, then the K slab
+    clear_lds(buf0, S::kBuf);
+    clear_lds(buf1, S::kBuf);
+    __syncthreads();
 
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
-    const int Uh = window_start(w.o[1], nh, w.k[1]);
-    const int Hend = window_start(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + w.k[1];
-    const int U2 = window_start(w.o[2], nw, w.k[2]);
-    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
-    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
-    const int aw = (window_start(pw0, nw, w.k[2]) - U2) & ~3;
-    const int nbw = (window_start(pw1, nw, w.k[2]) + w.k[2] - U2 - aw + 3) >> 2;
-    // rows of this wave's window union: slabs outside it are skipped
-    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
-    const int wr0 = window_start(ph0, nh, w.k[1]), wr1 = window_start(ph1, nh, w.k[1]) + w.k[1];
-
+    const Walk wk = make_walk<false>(w, wave);
     const Pt P = patch_point(w, wave, n);
     const int wh = window_start(P.h, nh, w.k[1]);
-    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - U2);
+    const int wrel = lg - (window_start(P.w, nw, w.k[2]) - wk.U2);
     const int64_t qo = eoff<D>(w, w.o[0], P.h, P.w);
     const int64_t ro = roff(w, w.o[0], P.h, P.w);
     uint4 qv[NH], dv[NH];
@@ -543,76 +608,72 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
             delta += Mf<T>::lo(ow[i]) * Mf<T>::lo(dw[i]) + Mf<T>::hi(ow[i]) * Mf<T>::hi(dw[i]);
     }
     delta = xsum4(delta);
-    if (wave_on && P.active && lg == 0) a.delta[ro] = delta;
+    if (wk.on && P.active && lg == 0) a.delta[ro] = delta;
     const float nlse2 = -a.lse[ro] * kLog2e;
     const float c = a.qscale;
-    const LaneAddr<D> la(g.km_pitch, lg, n);
+    const LaneAddr<D> la(S::kPitch, lg, n);
+    const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
 
     f4 acc[ND];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) acc[d] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < ND; ++d) acc[d] = zero;
 
-    const int nslab = (Hend - Uh + 3) >> 2;
-    // frames: along T (3D grids) key planes outside the tile's frame window are
-    // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
     const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
-    for (int j = 0; j < w.k[0]; ++j) {
-        const int tk = t0 + j;
-        if (fr_t && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
-        for (int sl = 0; sl < nslab; ++sl) {
-            const int r0 = Uh + 4 * sl;
-            __syncthreads();
-            stage_km<T, D>(a.v, w, tk, r0, U2, g.box_w, g.km_pitch, Vk);
-            stage_km<T, D>(a.k, w, tk, r0, U2, g.box_w, g.km_pitch, Kk);
-            stage_tr<T, D>(a.k, w, tk, r0, U2, g.box_w, Kt);
-            stage_wait();
-            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
-            bool hr[4];
+    auto plane_ok = [&](int tk) { return !fr_t || in_frame(tk, w.o[0], w.n[0], fk_t); };
+    auto stage = [&](int tk, int sl, char *buf, int) {
+        stage_km<T, D>(a.v, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf);
+        stage_km<T, D>(a.k, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf + slab);
+    };
+    auto walk = [&](int, int sl, const char *buf, int) {
+        const int r0 = wk.Uh + 4 * sl;
+        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        const char *Vc = buf, *Kc = buf + slab;
+        bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
-                        (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
-            for (int b = 0; b < nbw; b += 2) {
-                const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b;
-                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+        for (int r = 0; r < 4; ++r)
+            hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
+                    (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
+        for (int b = 0; b < wk.nbw; b += 2) {
+            const int col0 = wk.aw + 4 * b;
+            const bool two = b + 1 < wk.nbw;
+            const char *kb = Kc + col0 * NC * 16, *vb = Vc + col0 * NC * 16;
+            f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
+            f4 p0 = Mf<T>::mma(km_at(vb, la.km[0]), dv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(kb + BLK, la.km[0]), qv[0], zero);
+            f4 p1 = Mf<T>::mma(km_at(vb + BLK, la.km[0]), dv[0], zero);
 #pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    s0 = Mf<T>::mma(km_at(Kk + col0 * NC * 16, la.km[h]), qv[h], s0);
-                    p0 = Mf<T>::mma(km_at(Vk + col0 * NC * 16, la.km[h]), dv[h], p0);
-                }
-                if (two) {
-#pragma unroll
-                    for (int h = 0; h < NH; ++h) {
-                        s1 = Mf<T>::mma(km_at(Kk + (col0 + 4) * NC * 16, la.km[h]), qv[h], s1);
-                        p1 = Mf<T>::mma(km_at(Vk + (col0 + 4) * NC * 16, la.km[h]), dv[h], p1);
-                    }
-                }
-                const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
-                const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
-                float ds[8];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e0 = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, nlse2) : -INFINITY);
-                    const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
-                    ds[r] = e0 * (p0[r] - delta);
-                    ds[4 + r] = e1 * (p1[r] - delta);
-                }
-                uint4 db;
-                db.x = Mf<T>::pack(ds[0], ds[1]);
-                db.y = Mf<T>::pack(ds[2], ds[3]);
-                db.z = Mf<T>::pack(ds[4], ds[5]);
-                db.w = Mf<T>::pack(ds[6], ds[7]);
-                const char *t0p = Kt + la.tr + col0 * tr_col<D>();
-                const char *t1p = two ? t0p + 4 * tr_col<D>() : t0p;
-#pragma unroll
-                for (int d = 0; d < ND; ++d) acc[d] = Mf<T>::mma(tr_at(t0p, t1p, d), db, acc[d]);
+            for (int h = 1; h < NH; ++h) {
+                s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
+                p0 = Mf<T>::mma(km_at(vb, la.km[h]), dv[h], p0);
+                s1 = Mf<T>::mma(km_at(kb + BLK, la.km[h]), qv[h], s1);
+                p1 = Mf<T>::mma(km_at(vb + BLK, la.km[h]), dv[h], p1);
             }
+            const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
+            const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
+            float ds[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e0 = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, nlse2) : -INFINITY);
+                const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
+                ds[r] = e0 * (p0[r] - delta);
+                ds[4 + r] = e1 * (p1[r] - delta);
+            }
+            uint4 db;
+            db.x = Mf<T>::pack(ds[0], ds[1]);
+            db.y = Mf<T>::pack(ds[2], ds[3]);
+            db.z = Mf<T>::pack(ds[4], ds[5]);
+            db.w = Mf<T>::pack(ds[6], ds[7]);
+            const int second = two ? BLK : 0;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                acc[d] = Mf<T>::mma(tr_pair(kb, second, la.tr[d]), db, acc[d]);
         }
-    }
-    if (!wave_on || !P.active) return;
+    };
+    slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
+
+    if (!wk.on || !P.active) return;
     T *dp = a.dq + qo + 4 * lg;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
@@ -628,40 +689,33 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
 // inverse windows: S = Q K^T (A = a query block, key-major; B = the wave's
 // keys), P = exp2(S c - lse), dP = dO V^T, dS = P (dP - delta); then
 // dV^T += dO^T P and dK^T += Q^T dS over pairs of query blocks.
-template <typename T, int D>
+template <typename T, int D, int W>
 __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
-    extern __shared__ __align__(16) char smem[];
-    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32;
+    using S = Slabs<D, W>;
+    __shared__ __align__(16) char buf0[S::kBuf];
+    __shared__ __align__(16) char buf1[S::kBuf];
+    constexpr int NC = D * 2 / 16, ND = D / 16, NH = D / 32, BLK = 4 * NC * 16;
     const Geom &g = a.g;
     TileCtx w;
     if (!decode(g, xcd_tile_id(blockIdx.x, g.n_tiles), w)) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
-    char *Qk = smem;
-    char *Ok = smem + 4 * g.km_pitch;
-    char *Qt = smem + 8 * g.km_pitch;
-    char *Ot = Qt + g.box_w * tr_col<D>();
-    float2 *Rw = reinterpret_cast<float2 *>(Ot + g.box_w * tr_col<D>());
+    constexpr int slab = S::kSlab;  // per buffer: the Q slab, then the dout slab
+    // (logsumexp * log2(e), delta) of the slab's points, one array per buffer
+    __shared__ float2 rows0[4 * W], rows1[4 * W];
+    clear_lds(buf0, S::kBuf);
+    clear_lds(buf1, S::kBuf);
+    __syncthreads();
 
-    // the workgroup's query box: planes, rows, columns of the inverse windows
+    // the workgroup's query planes, and this wave's walk of the inverse windows
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
     const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
-    const int Uh = inverse_first(w.o[1], nh, w.k[1]);
-    const int Hend = inverse_last(imin(w.o[1] + kTH - 1, nh - 1), nh, w.k[1]) + 1;
-    const int U2 = inverse_first(w.o[2], nw, w.k[2]);
-    const bool wave_on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
-    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
-    const int aw = (inverse_first(pw0, nw, w.k[2]) - U2) & ~3;
-    const int nbw = (inverse_last(pw1, nw, w.k[2]) + 1 - U2 - aw + 3) >> 2;
-    // rows of this wave's inverse union: slabs outside it are skipped
-    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
-    const int wr0 = inverse_first(ph0, nh, w.k[1]), wr1 = inverse_last(ph1, nh, w.k[1]) + 1;
-
+    const Walk wk = make_walk<true>(w, wave);
     const Pt P = patch_point(w, wave, n);  // the lane's key
     const int ih0 = inverse_first(P.h, nh, w.k[1]), ih1 = inverse_last(P.h, nh, w.k[1]);
     // query columns of this lane group relative to the key's inverse window
-    const int irel = lg - (inverse_first(P.w, nw, w.k[2]) - U2);
+    const int irel = lg - (inverse_first(P.w, nw, w.k[2]) - wk.U2);
     const int iwn = inverse_last(P.w, nw, w.k[2]) - inverse_first(P.w, nw, w.k[2]);
     const int64_t ko = eoff<D>(w, w.o[0], P.h, P.w);
     uint4 kv[NH], vv[NH];
@@ -671,92 +725,98 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
         vv[h] = *reinterpret_cast<const uint4 *>(a.v + ko + 8 * lg + 32 * h);
     }
     const float c = a.qscale;
-    const LaneAddr<D> la(g.km_pitch, lg, n);
+    const LaneAddr<D> la(S::kPitch, lg, n);
+    const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
 
     f4 dka[ND], dva[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-        dka[d] = f4{0.f, 0.f, 0.f, 0.f};
-        dva[d] = f4{0.f, 0.f, 0.f, 0.f};
+        dka[d] = zero;
+        dva[d] = zero;
     }
 
-    const int nslab = (Hend - Uh + 3) >> 2;
     // frames: along T (3D grids) query planes whose frame window misses the key
     // plane are skipped; along H (2D grids) such query rows are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
-    for (int tq = tq0; tq <= tq1; ++tq) {
-        if (fr_t && !in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq))) continue;
-        for (int sl = 0; sl < nslab; ++sl) {
-            const int r0 = Uh + 4 * sl;
-            __syncthreads();
-            stage_km<T, D>(a.q, w, tq, r0, U2, g.box_w, g.km_pitch, Qk);
-            stage_km<T, D>(a.dout, w, tq, r0, U2, g.box_w, g.km_pitch, Ok);
-            stage_tr<T, D>(a.q, w, tq, r0, U2, g.box_w, Qt);
-            stage_tr<T, D>(a.dout, w, tq, r0, U2, g.box_w, Ot);
-            stage_rows16(a.lse, a.delta, w, tq, r0, U2, g.box_w, Rw);
-            stage_wait();
-            if (!wave_on || r0 + 4 <= wr0 || r0 >= wr1) continue;
-            // query rows of the slab inside the key's inverse window
-            bool hr[4];
+    auto plane_ok = [&](int tq) {
+        return !fr_t || in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq));
+    };
+    float2 rv = make_float2(0.f, 0.f);  // the next slab's rows, in flight
+    bool first = true;                  // the first step's rows are stored at once
+    auto stage = [&](int tq, int sl, char *buf, int i) {
+        const int r0 = wk.Uh + 4 * sl;
+        stage_km<T, D>(a.q, w, tq, r0, wk.U2, g.box_w, S::kPitch, buf);
+        stage_km<T, D>(a.dout, w, tq, r0, wk.U2, g.box_w, S::kPitch, buf + slab);
+        rv = rows_load(a.lse, a.delta, w, tq, r0, wk.U2, g.box_w);
+        if (first) rows_store(rv, g.box_w, i ? rows1 : rows0);
+        first = false;
+    };
+    // a later step's rows go to LDS after the walk before it (their array was
+    // last read a step earlier)
+    auto done = [&](int i) { rows_store(rv, g.box_w, i ? rows1 : rows0); };
+    auto walk = [&](int, int sl, const char *buf, int i) {
+        const int r0 = wk.Uh + 4 * sl;
+        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        const char *Qc = buf, *Oc = buf + slab;
+        const float2 *Rc = i ? rows1 : rows0;
+        // query rows of the slab inside the key's inverse window
+        bool hr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0) &&
-                        (!fr_h || in_frame(P.h, r0 + r, nh,
-                                           frame_size(a.frame, w, 1, imin(r0 + r, nh - 1))));
-            for (int b = 0; b < nbw; b += 2) {
-                const bool two = b + 1 < nbw;
-                const int col0 = aw + 4 * b;
-                f4 s0 = f4{0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+        for (int r = 0; r < 4; ++r)
+            hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0) &&
+                    (!fr_h || in_frame(P.h, r0 + r, nh,
+                                       frame_size(a.frame, w, 1, imin(r0 + r, nh - 1))));
+        for (int b = 0; b < wk.nbw; b += 2) {
+            const int col0 = wk.aw + 4 * b;
+            const bool two = b + 1 < wk.nbw;
+            const char *qb = Qc + col0 * NC * 16, *ob = Oc + col0 * NC * 16;
+            f4 s0 = Mf<T>::mma(km_at(qb, la.km[0]), kv[0], zero);
+            f4 p0 = Mf<T>::mma(km_at(ob, la.km[0]), vv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(qb + BLK, la.km[0]), kv[0], zero);
+            f4 p1 = Mf<T>::mma(km_at(ob + BLK, la.km[0]), vv[0], zero);
 #pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    s0 = Mf<T>::mma(km_at(Qk + col0 * NC * 16, la.km[h]), kv[h], s0);
-                    p0 = Mf<T>::mma(km_at(Ok + col0 * NC * 16, la.km[h]), vv[h], p0);
-                }
-                if (two) {
+            for (int h = 1; h < NH; ++h) {
+                s0 = Mf<T>::mma(km_at(qb, la.km[h]), kv[h], s0);
+                p0 = Mf<T>::mma(km_at(ob, la.km[h]), vv[h], p0);
+                s1 = Mf<T>::mma(km_at(qb + BLK, la.km[h]), kv[h], s1);
+                p1 = Mf<T>::mma(km_at(ob + BLK, la.km[h]), vv[h], p1);
+            }
+            // (lse, delta) of the four rows of this lane group's query column
+            const float4 *rp0 = reinterpret_cast<const float4 *>(Rc + 4 * (col0 + lg));
+            const float4 *rp1 = reinterpret_cast<const float4 *>(Rc + 4 * (two ? col0 + 4 + lg : col0 + lg));
+            const float4 l0a = rp0[0], l0b = rp0[1], l1a = rp1[0], l1b = rp1[1];
+            const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, dl0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
+            const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, dl1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
+            const bool w0 = (unsigned)(col0 + irel) <= (unsigned)iwn;
+            const bool w1 = two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
+            float pr[8], ds[8];
 #pragma unroll
-                    for (int h = 0; h < NH; ++h) {
-                        s1 = Mf<T>::mma(km_at(Qk + (col0 + 4) * NC * 16, la.km[h]), kv[h], s1);
-                        p1 = Mf<T>::mma(km_at(Ok + (col0 + 4) * NC * 16, la.km[h]), vv[h], p1);
-                    }
-                }
-                // (lse, delta) of the four rows of this lane group's query column
-                const float4 *rp0 = reinterpret_cast<const float4 *>(Rw + 4 * (col0 + lg));
-                const float4 *rp1 = reinterpret_cast<const float4 *>(Rw + 4 * (two ? col0 + 4 + lg : col0 + lg));
-                const float4 l0a = rp0[0], l0b = rp0[1], l1a = rp1[0], l1b = rp1[1];
-                const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, dl0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
-                const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, dl1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
-                const bool w0 = (unsigned)(col0 + irel) <= (unsigned)iwn;
-                const bool w1 = two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
-                float pr[8], ds[8];
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, -ls0[r]) : -INFINITY);
+                pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, -ls1[r]) : -INFINITY);
+                ds[r] = pr[r] * (p0[r] - dl0[r]);
+                ds[4 + r] = pr[4 + r] * (p1[r] - dl1[r]);
+            }
+            uint4 pb, db;
+            pb.x = Mf<T>::pack(pr[0], pr[1]);
+            pb.y = Mf<T>::pack(pr[2], pr[3]);
+            pb.z = Mf<T>::pack(pr[4], pr[5]);
+            pb.w = Mf<T>::pack(pr[6], pr[7]);
+            db.x = Mf<T>::pack(ds[0], ds[1]);
+            db.y = Mf<T>::pack(ds[2], ds[3]);
+            db.z = Mf<T>::pack(ds[4], ds[5]);
+            db.w = Mf<T>::pack(ds[6], ds[7]);
+            const int second = two ? BLK : 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, -ls0[r]) : -INFINITY);
-                    pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, -ls1[r]) : -INFINITY);
-                    ds[r] = pr[r] * (p0[r] - dl0[r]);
-                    ds[4 + r] = pr[4 + r] * (p1[r] - dl1[r]);
-                }
-                uint4 pb, db;
-                pb.x = Mf<T>::pack(pr[0], pr[1]);
-                pb.y = Mf<T>::pack(pr[2], pr[3]);
-                pb.z = Mf<T>::pack(pr[4], pr[5]);
-                pb.w = Mf<T>::pack(pr[6], pr[7]);
-                db.x = Mf<T>::pack(ds[0], ds[1]);
-                db.y = Mf<T>::pack(ds[2], ds[3]);
-                db.z = Mf<T>::pack(ds[4], ds[5]);
-                db.w = Mf<T>::pack(ds[6], ds[7]);
-                const char *o0 = Ot + la.tr + col0 * tr_col<D>();
-                const char *o1 = two ? o0 + 4 * tr_col<D>() : o0;
-                const char *q0 = Qt + la.tr + col0 * tr_col<D>();
-                const char *q1 = two ? q0 + 4 * tr_col<D>() : q0;
-#pragma unroll
-                for (int d = 0; d < ND; ++d) {
-                    dva[d] = Mf<T>::mma(tr_at(o0, o1, d), pb, dva[d]);
-                    dka[d] = Mf<T>::mma(tr_at(q0, q1, d), db, dka[d]);
-                }
+            for (int d = 0; d < ND; ++d) {
+                dva[d] = Mf<T>::mma(tr_pair(ob, second, la.tr[d]), pb, dva[d]);
+                dka[d] = Mf<T>::mma(tr_pair(qb, second, la.tr[d]), db, dka[d]);
             }
         }
-    }
-    if (!wave_on || !P.active) return;
+    };
+    slab_steps(tq0, tq1, wk.nslab, buf0, buf1, plane_ok, stage, walk, done);
+
+    if (!wk.on || !P.active) return;
     T *kp = a.dk + ko + 4 * lg;
     T *vp = a.dv + ko + 4 * lg;
 #pragma unroll
@@ -768,6 +828,12 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
         Io<T>::store4(vp + 16 * d, v4);
     }
 }
+
+// Launch of kernel `kind` (0 forward, 1 dq, 2 dk/dv) for slab rows of up to
+// a.g.wmax points (24, 32 or 48) on stream s; defined in na_m16.hip for bf16 /
+// f16 and D 32 / 64.
+template <typename T, int D>
+hipError_t launch(int kind, const Args<T> &a, hipStream_t s);
 
 }  // namespace m16
 }  // namespace na
