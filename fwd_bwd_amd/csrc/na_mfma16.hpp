@@ -181,6 +181,22 @@ __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
     w.lst[0] = g.dil[0] * HW * g.heads;
     w.lst[1] = (int64_t)g.dil[1] * g.ext[2] * g.heads;
     w.lst[2] = (int64_t)g.dil[2] * g.heads;
+    // every field is uniform over the workgroup: readfirstlane keeps them, and
+    // the address arithmetic derived from them, in scalar registers
+    auto u32 = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    auto u64 = [](int64_t v) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        w.n[a] = u32(w.n[a]);
+        w.o[a] = u32(w.o[a]);
+        w.r[a] = u32(w.r[a]);
+        w.lst[a] = u64(w.lst[a]);
+    }
+    w.lbase = u64(w.lbase);
     return inside;
 }
 
@@ -201,37 +217,59 @@ __device__ __forceinline__ int kswz(int col) {
 }
 
 // Key-major slab: rows [r0, r0 + 4) of plane tk (class coordinates), columns
-// [U2, U2 + box_w), of src; row r at lds + r * pitch, chunk s of column c at
-// 16 * (c * NC + (s ^ kswz(c))). Direct global-to-LDS loads, 64 consecutive
-// chunks per wave instruction; the (row, 64-chunk part) pieces are spread over
-// the workgroup's waves. Points past the grid repeat the last grid point.
-// Completion: stage_wait().
-template <typename T, int D>
-__device__ __forceinline__ void stage_km(const T *src, const TileCtx &w, int tk, int r0, int U2,
-                                         int box_w, int pitch, char *lds) {
-    constexpr int NC = D * 2 / 16;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int nch = box_w * NC, parts = (nch + 63) >> 6;
-    for (int it = wave; it < 4 * parts; it += kWG) {
-        const int row = it & 3, part = it >> 2;
-        const int c1 = imin(r0 + row, w.n[1] - 1);
-        const char *rowp =
-            reinterpret_cast<const char *>(src) + eoff<D>(w, tk, c1, 0) * (int64_t)sizeof(T);
-        const int s = part * 64 + lane;
-        if (s >= nch) continue;
-        const int col = s / NC, pos = s - col * NC;
-        const int c2 = imin(U2 + col, w.n[2] - 1);
-        const int goff = (int)(c2 * w.lst[2]) * D * 2 + ((pos ^ kswz<NC>(col)) << 4);
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_global_load_lds(rowp + goff,
-                                         (lds_void *)(lds + row * pitch + part * 1024), 16, 0, 0);
-#else
-        (void)goff;
-        (void)rowp;
-#endif
+// [U2, U2 + box_w), of a tensor; row r at lds + r * Pitch, chunk s of column c
+// at 16 * (c * NC + (s ^ kswz(c))). Direct global-to-LDS loads, 64 consecutive
+// chunks per wave instruction; the workgroup's waves take the (row, 64-chunk
+// part) pieces of a slab in turn, wave v the pieces v, v + kWG, ... The lane's
+// byte offset within a global row depends only on its piece, so it is
+// computed once per tile; a step adds the row's (uniform) address. Points past
+// the grid repeat the last grid point. Completion: stage_wait().
+template <int D, int W, int Pitch>
+struct Stager {
+    static constexpr int NC = D * 2 / 16, PARTS = (W * NC + 63) / 64;
+    static constexpr int ITEMS = (4 * PARTS + kWG - 1) / kWG;
+    int goff[ITEMS];  // byte offset of the lane's chunk within its global row
+    bool on[ITEMS];   // the lane has a chunk in this piece
+    int n;            // pieces of this wave (uniform)
+    int wave;
+    __device__ __forceinline__ Stager(const TileCtx &w, int U2, int box_w, int wave_, int lane) {
+        wave = wave_;
+        const int nch = box_w * NC, parts = (nch + 63) >> 6;
+        n = 0;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int it = wave + kWG * i;
+            if (it < 4 * parts) n = i + 1;
+            const int s = (it >> 2) * 64 + lane;
+            const int col = s / NC, pos = s - col * NC;
+            const int c2 = imin(U2 + col, w.n[2] - 1);
+            goff[i] = (int)(c2 * w.lst[2]) * D * 2 + ((pos ^ kswz<NC>(col)) << 4);
+            on[i] = s < nch;
+        }
+        n = __builtin_amdgcn_readfirstlane(n);
     }
-}
+    template <typename T>
+    __device__ __forceinline__ void stage(const T *src, const TileCtx &w, int tk, int r0,
+                                          char *lds) const {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            if (i >= n) break;
+            const int it = wave + kWG * i, row = it & 3, part = it >> 2;
+            const int c1 = imin(r0 + row, w.n[1] - 1);
+            const char *rowp =
+                reinterpret_cast<const char *>(src) + eoff<D>(w, tk, c1, 0) * (int64_t)sizeof(T);
+            if (on[i]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+                __builtin_amdgcn_global_load_lds(rowp + goff[i],
+                                                 (lds_void *)(lds + row * Pitch + part * 1024), 16,
+                                                 0, 0);
+#else
+                (void)rowp;
+#endif
+            }
+        }
+    }
+};
 
 // Zeroes the workgroup's dynamic LDS (bytes: a multiple of 16).
 __device__ __forceinline__ void clear_lds(char *lds, int bytes) {
@@ -387,8 +425,16 @@ constexpr float kLazyRescale = 8.f;
 template <typename OK, typename Stage, typename WalkFn, typename Done>
 __device__ __forceinline__ void slab_steps(int p0, int p1, int nslab, char *b0, char *b1,
                                            OK plane_ok, Stage stage, WalkFn walk, Done done) {
-    int p = p0;
-    while (p <= p1 && !plane_ok(p)) ++p;
+    // every index here is uniform over the workgroup; readfirstlane keeps the
+    // compiler from carrying them as per-lane values
+    p0 = __builtin_amdgcn_readfirstlane(p0);
+    p1 = __builtin_amdgcn_readfirstlane(p1);
+    nslab = __builtin_amdgcn_readfirstlane(nslab);
+    auto skip = [&](int q) {
+        while (q <= p1 && !plane_ok(q)) ++q;
+        return __builtin_amdgcn_readfirstlane(q);
+    };
+    int p = skip(p0);
     if (p > p1) return;
     stage(p, 0, b0, 0);
     int sl = 0;
@@ -397,8 +443,7 @@ __device__ __forceinline__ void slab_steps(int p0, int p1, int nslab, char *b0, 
         sn = sl + 1;
         if (sn == nslab) {
             sn = 0;
-            ++pn;
-            while (pn <= p1 && !plane_ok(pn)) ++pn;
+            pn = skip(p + 1);
         }
         return pn <= p1;
     };
@@ -488,12 +533,25 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
     // frames: along T (3D grids) key planes outside the tile's frame window are
     // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
-    const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
+    // (the frame size of the tile's plane is uniform: readfirstlane keeps the
+    // plane loop scalar)
+    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, w.o[0])) : 0;
+    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(w.o[0], w.n[0], imax(fk_t, 1)));
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
-    auto plane_ok = [&](int tk) { return !fr_t || in_frame(tk, w.o[0], w.n[0], fk_t); };
+    // key rows [hlo, hlo + hlen) of the lane's query: its window rows, cut to
+    // its frame window on 2D grids with frames
+    int hlo = wh, hlen = w.k[1];
+    if (fr_h) {
+        const int fs = window_start(P.h, nh, imax(fk_h, 1));
+        const int hi = imin(wh + w.k[1], fs + fk_h);
+        hlo = imax(wh, fs);
+        hlen = imax(hi - hlo, 0);
+    }
+    auto plane_ok = [&](int tk) { return !fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t; };
+    const Stager<D, W, S::kPitch> st(w, wk.U2, g.box_w, wave, lane);
     auto stage = [&](int tk, int sl, char *buf, int) {
-        stage_km<T, D>(a.k, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf);
-        stage_km<T, D>(a.v, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf + slab);
+        st.stage(a.k, w, tk, wk.Uh + 4 * sl, buf);
+        st.stage(a.v, w, tk, wk.Uh + 4 * sl, buf + slab);
     };
     auto walk = [&](int, int sl, const char *buf, int) {
         const int r0 = wk.Uh + 4 * sl;
@@ -502,9 +560,7 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
         // key rows of the slab inside the lane's query window
         bool hr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
-                    (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
+        for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - hlo) < (unsigned)hlen;
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
@@ -619,12 +675,25 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     for (int d = 0; d < ND; ++d) acc[d] = zero;
 
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
-    const int fk_t = fr_t ? frame_size(a.frame, w, 0, w.o[0]) : 0;
+    // (the frame size of the tile's plane is uniform: readfirstlane keeps the
+    // plane loop scalar)
+    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, w.o[0])) : 0;
+    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(w.o[0], w.n[0], imax(fk_t, 1)));
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
-    auto plane_ok = [&](int tk) { return !fr_t || in_frame(tk, w.o[0], w.n[0], fk_t); };
+    // key rows [hlo, hlo + hlen) of the lane's query: its window rows, cut to
+    // its frame window on 2D grids with frames
+    int hlo = wh, hlen = w.k[1];
+    if (fr_h) {
+        const int fs = window_start(P.h, nh, imax(fk_h, 1));
+        const int hi = imin(wh + w.k[1], fs + fk_h);
+        hlo = imax(wh, fs);
+        hlen = imax(hi - hlo, 0);
+    }
+    auto plane_ok = [&](int tk) { return !fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t; };
+    const Stager<D, W, S::kPitch> st(w, wk.U2, g.box_w, wave, lane);
     auto stage = [&](int tk, int sl, char *buf, int) {
-        stage_km<T, D>(a.v, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf);
-        stage_km<T, D>(a.k, w, tk, wk.Uh + 4 * sl, wk.U2, g.box_w, S::kPitch, buf + slab);
+        st.stage(a.v, w, tk, wk.Uh + 4 * sl, buf);
+        st.stage(a.k, w, tk, wk.Uh + 4 * sl, buf + slab);
     };
     auto walk = [&](int, int sl, const char *buf, int) {
         const int r0 = wk.Uh + 4 * sl;
@@ -632,9 +701,7 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
         const char *Vc = buf, *Kc = buf + slab;
         bool hr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            hr[r] = (unsigned)(r0 + r - wh) < (unsigned)w.k[1] &&
-                    (!fr_h || in_frame(r0 + r, P.h, nh, fk_h));
+        for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - hlo) < (unsigned)hlen;
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
@@ -739,14 +806,17 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
     // plane are skipped; along H (2D grids) such query rows are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
     auto plane_ok = [&](int tq) {
-        return !fr_t || in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq));
+        return !fr_t ||
+               in_frame(w.o[0], tq, w.n[0],
+                        __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, tq)));
     };
     float2 rv = make_float2(0.f, 0.f);  // the next slab's rows, in flight
     bool first = true;                  // the first step's rows are stored at once
+    const Stager<D, W, S::kPitch> st(w, wk.U2, g.box_w, wave, lane);
     auto stage = [&](int tq, int sl, char *buf, int i) {
         const int r0 = wk.Uh + 4 * sl;
-        stage_km<T, D>(a.q, w, tq, r0, wk.U2, g.box_w, S::kPitch, buf);
-        stage_km<T, D>(a.dout, w, tq, r0, wk.U2, g.box_w, S::kPitch, buf + slab);
+        st.stage(a.q, w, tq, r0, buf);
+        st.stage(a.dout, w, tq, r0, buf + slab);
         rv = rows_load(a.lse, a.delta, w, tq, r0, wk.U2, g.box_w);
         if (first) rows_store(rv, g.box_w, i ? rows1 : rows0);
         first = false;
@@ -762,10 +832,13 @@ __global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
         // query rows of the slab inside the key's inverse window
         bool hr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0) &&
-                    (!fr_h || in_frame(P.h, r0 + r, nh,
-                                       frame_size(a.frame, w, 1, imin(r0 + r, nh - 1))));
+        for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - ih0) <= (unsigned)(ih1 - ih0);
+        if (fr_h) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                hr[r] = hr[r] & in_frame(P.h, r0 + r, nh,
+                                         frame_size(a.frame, w, 1, imin(r0 + r, nh - 1)));
+        }
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
