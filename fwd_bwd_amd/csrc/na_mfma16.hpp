@@ -757,7 +757,7 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
 // keys), P = exp2(S c - lse), dP = dO V^T, dS = P (dP - delta); then
 // dV^T += dO^T P and dK^T += Q^T dS over pairs of query blocks.
 template <typename T, int D, int W>
-__global__ void __launch_bounds__(kTG, 2) dkdv_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     using S = Slabs<D, W>;
     __shared__ __align__(16) char buf0[S::kBuf];
     __shared__ __align__(16) char buf1[S::kBuf];
