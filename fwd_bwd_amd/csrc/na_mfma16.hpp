@@ -50,9 +50,9 @@
 // Windows are clamped by index arithmetic only: a score is kept when the key
 // lies in the query's window (equivalently the query in the key's inverse
 // window), which also rejects every point a slab holds past the grid (those
-// repeat the last grid point, so they are finite). Reads past a wave's last
-// block (an odd number of blocks) land on staged or cleared LDS, so they are
-// finite too, and their scores are masked.
+// repeat the last grid point, so they are finite). A wave with an odd number
+// of blocks pairs its last block with itself and masks the copy, so every LDS
+// byte a walk reads was staged for that step.
 #pragma once
 
 #include "na_common.hpp"
@@ -271,12 +271,6 @@ struct Stager {
     }
 };
 
-// Zeroes the workgroup's dynamic LDS (bytes: a multiple of 16).
-__device__ __forceinline__ void clear_lds(char *lds, int bytes) {
-    for (int i = (int)threadIdx.x * 16; i < bytes; i += kTG * 16)
-        *reinterpret_cast<uint4 *>(lds + i) = make_uint4(0u, 0u, 0u, 0u);
-}
-
 // (logsumexp, delta) of the slab point thread i stages (i < 4 box_w; column
 // major: the four rows of column c at 4c .. 4c + 3). rows_load only issues the
 // loads, so that they can run under a walk; rows_store writes
@@ -469,14 +463,13 @@ __device__ __forceinline__ void slab_steps(int p0, int p1, int nslab, char *b0, 
 }
 
 // Static LDS of a kernel with slab rows of up to W points: per buffer the
-// slabs of two tensors and a slack that takes the reads of a wave's odd last
-// block past its slab.
+// slabs of two tensors.
 template <int D, int W>
 struct Slabs {
     static constexpr int NC = D * 2 / 16;
     static constexpr int kPitch = ((W * NC) | 1) * 16;  // odd number of 16-byte chunks
     static constexpr int kSlab = 4 * kPitch;
-    static constexpr int kBuf = 2 * kSlab + 512;
+    static constexpr int kBuf = 2 * kSlab;
 };
 
 // ============================================================================
@@ -494,9 +487,6 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
     constexpr int slab = S::kSlab;  // per buffer: the K slab, then the V slab
-    clear_lds(buf0, S::kBuf);
-    clear_lds(buf1, S::kBuf);
-    __syncthreads();
 
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
     const Walk wk = make_walk<false>(w, wave);
@@ -564,13 +554,15 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
+            // a wave's odd last block pairs with itself (its weights are masked)
+            const int second = two ? BLK : 0;
             const char *kb = Kc + col0 * NC * 16;
             f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
-            f4 s1 = Mf<T>::mma(km_at(kb + BLK, la.km[0]), qv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
-                s1 = Mf<T>::mma(km_at(kb + BLK, la.km[h]), qv[h], s1);
+                s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
             }
             const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
             const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
@@ -597,7 +589,6 @@ __global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
             pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
             pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
             const char *vb = Vc + col0 * NC * 16;
-            const int second = two ? BLK : 0;
 #pragma unroll
             for (int d = 0; d < ND; ++d)
                 acc[d] = Mf<T>::mma(tr_pair(vb, second, la.tr[d]), pb, acc[d]);
@@ -635,9 +626,6 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
     constexpr int slab = S::kSlab;  // per buffer: the V slab, then the K slab
-    clear_lds(buf0, S::kBuf);
-    clear_lds(buf1, S::kBuf);
-    __syncthreads();
 
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
     const Walk wk = make_walk<false>(w, wave);
@@ -705,17 +693,19 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
+            // a wave's odd last block pairs with itself (its weights are masked)
+            const int second = two ? BLK : 0;
             const char *kb = Kc + col0 * NC * 16, *vb = Vc + col0 * NC * 16;
             f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
             f4 p0 = Mf<T>::mma(km_at(vb, la.km[0]), dv[0], zero);
-            f4 s1 = Mf<T>::mma(km_at(kb + BLK, la.km[0]), qv[0], zero);
-            f4 p1 = Mf<T>::mma(km_at(vb + BLK, la.km[0]), dv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
+            f4 p1 = Mf<T>::mma(km_at(vb + second, la.km[0]), dv[0], zero);
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
                 p0 = Mf<T>::mma(km_at(vb, la.km[h]), dv[h], p0);
-                s1 = Mf<T>::mma(km_at(kb + BLK, la.km[h]), qv[h], s1);
-                p1 = Mf<T>::mma(km_at(vb + BLK, la.km[h]), dv[h], p1);
+                s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
+                p1 = Mf<T>::mma(km_at(vb + second, la.km[h]), dv[h], p1);
             }
             const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
             const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
@@ -732,7 +722,6 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
             db.y = Mf<T>::pack(ds[2], ds[3]);
             db.z = Mf<T>::pack(ds[4], ds[5]);
             db.w = Mf<T>::pack(ds[6], ds[7]);
-            const int second = two ? BLK : 0;
 #pragma unroll
             for (int d = 0; d < ND; ++d)
                 acc[d] = Mf<T>::mma(tr_pair(kb, second, la.tr[d]), db, acc[d]);
@@ -771,9 +760,6 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     constexpr int slab = S::kSlab;  // per buffer: the Q slab, then the dout slab
     // (logsumexp * log2(e), delta) of the slab's points, one array per buffer
     __shared__ float2 rows0[4 * W], rows1[4 * W];
-    clear_lds(buf0, S::kBuf);
-    clear_lds(buf1, S::kBuf);
-    __syncthreads();
 
     // the workgroup's query planes, and this wave's walk of the inverse windows
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
@@ -842,17 +828,19 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
         for (int b = 0; b < wk.nbw; b += 2) {
             const int col0 = wk.aw + 4 * b;
             const bool two = b + 1 < wk.nbw;
+            // a wave's odd last block pairs with itself (its weights are masked)
+            const int second = two ? BLK : 0;
             const char *qb = Qc + col0 * NC * 16, *ob = Oc + col0 * NC * 16;
             f4 s0 = Mf<T>::mma(km_at(qb, la.km[0]), kv[0], zero);
             f4 p0 = Mf<T>::mma(km_at(ob, la.km[0]), vv[0], zero);
-            f4 s1 = Mf<T>::mma(km_at(qb + BLK, la.km[0]), kv[0], zero);
-            f4 p1 = Mf<T>::mma(km_at(ob + BLK, la.km[0]), vv[0], zero);
+            f4 s1 = Mf<T>::mma(km_at(qb + second, la.km[0]), kv[0], zero);
+            f4 p1 = Mf<T>::mma(km_at(ob + second, la.km[0]), vv[0], zero);
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(qb, la.km[h]), kv[h], s0);
                 p0 = Mf<T>::mma(km_at(ob, la.km[h]), vv[h], p0);
-                s1 = Mf<T>::mma(km_at(qb + BLK, la.km[h]), kv[h], s1);
-                p1 = Mf<T>::mma(km_at(ob + BLK, la.km[h]), vv[h], p1);
+                s1 = Mf<T>::mma(km_at(qb + second, la.km[h]), kv[h], s1);
+                p1 = Mf<T>::mma(km_at(ob + second, la.km[h]), vv[h], p1);
             }
             // (lse, delta) of the four rows of this lane group's query column
             const float4 *rp0 = reinterpret_cast<const float4 *>(Rc + 4 * (col0 + lg));
@@ -879,7 +867,6 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
             db.y = Mf<T>::pack(ds[2], ds[3]);
             db.z = Mf<T>::pack(ds[4], ds[5]);
             db.w = Mf<T>::pack(ds[6], ds[7]);
-            const int second = two ? BLK : 0;
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
                 dva[d] = Mf<T>::mma(tr_pair(ob, second, la.tr[d]), pb, dva[d]);
