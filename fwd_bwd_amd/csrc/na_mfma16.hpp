@@ -22,8 +22,9 @@
 // the weighted sums.
 //
 // Staging. Slabs are copied with direct global-to-LDS loads into one layout,
-// key-major: each point's channels contiguous in 16-byte chunks (XOR-swizzled
-// at 64 channels), rows an odd number of chunks apart. With two slab buffers
+// key-major: each point's channels in 16-byte chunks, their order rotated by
+// the slab row (and XOR-swizzled at 64 channels) so that both kinds of reads
+// below are free of bank conflicts. With two slab buffers
 // the next slab's loads are issued before the current slab is walked, so they
 // run under the walk, and one barrier per slab orders the two.
 //
@@ -209,16 +210,27 @@ __device__ __forceinline__ int64_t roff(const TileCtx &w, int c0, int c1, int c2
     return w.lbase + c0 * w.lst[0] + c1 * w.lst[1] + c2 * w.lst[2];
 }
 
-// Chunk swizzle of the key-major layout: at 8 chunks per point (64 channels)
-// the chunk index flips bit 2 on every other pair of columns.
+// Key-major layout: chunk c of the point in column col and slab row r sits in
+// slot ((c ^ x(col)) + r) mod NC of the point, x(col) = bit 1 of col at 8
+// chunks per point (64 channels), 0 at 4; rows are a pitch apart that is 128
+// (mod 256) bytes at 4 chunks per point and 16 (mod 256) at 8. Then the
+// 16-byte score-operand reads of a 16-lane group (4 rows x 4 columns) and the
+// 8-byte transpose reads of a 32-lane half (4 rows x 2 columns x 32 bytes)
+// each touch every one of the 64 four-byte banks once (checked over all
+// pitches and XOR / rotation swizzles of this form with a bank model).
 template <int NC>
-__device__ __forceinline__ int kswz(int col) {
-    return NC == 8 ? ((col >> 1) & 1) << 2 : 0;
+__device__ __forceinline__ int kslot(int c, int col, int r) {
+    return ((c ^ (NC == 8 ? (col >> 1) & 1 : 0)) + r) & (NC - 1);
+}
+// The chunk stored in slot s (the inverse of kslot).
+template <int NC>
+__device__ __forceinline__ int kchunk(int s, int col, int r) {
+    return ((s - r) & (NC - 1)) ^ (NC == 8 ? (col >> 1) & 1 : 0);
 }
 
 // Key-major slab: rows [r0, r0 + 4) of plane tk (class coordinates), columns
 // [U2, U2 + box_w), of a tensor; row r at lds + r * Pitch, chunk s of column c
-// at 16 * (c * NC + (s ^ kswz(c))). Direct global-to-LDS loads, 64 consecutive
+// at 16 * (c * NC + kslot(s, c, r)). Direct global-to-LDS loads, 64 consecutive
 // chunks per wave instruction; the workgroup's waves take the (row, 64-chunk
 // part) pieces of a slab in turn, wave v the pieces v, v + kWG, ... The lane's
 // byte offset within a global row depends only on its piece, so it is
@@ -241,9 +253,9 @@ struct Stager {
             const int it = wave + kWG * i;
             if (it < 4 * parts) n = i + 1;
             const int s = (it >> 2) * 64 + lane;
-            const int col = s / NC, pos = s - col * NC;
+            const int col = s / NC, slot = s - col * NC;
             const int c2 = imin(U2 + col, w.n[2] - 1);
-            goff[i] = (int)(c2 * w.lst[2]) * D * 2 + ((pos ^ kswz<NC>(col)) << 4);
+            goff[i] = (int)(c2 * w.lst[2]) * D * 2 + (kchunk<NC>(slot, col, it & 3) << 4);
             on[i] = s < nch;
         }
         n = __builtin_amdgcn_readfirstlane(n);
@@ -265,6 +277,7 @@ struct Stager {
                                                  0, 0);
 #else
                 (void)rowp;
+                (void)part;
 #endif
             }
         }
@@ -365,13 +378,14 @@ struct LaneAddr {
         const int col = n >> 2, row = n & 3;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-            km[h] = row * pitch + ((col * NC + ((lg + 4 * h) ^ kswz<NC>(col))) << 4);
+            km[h] = row * pitch + ((col * NC + kslot<NC>(lg + 4 * h, col, row)) << 4);
         // block columns start at multiples of 4, so column lg of a block has
         // the swizzle of lg
-        const int a = n & 3, j = n >> 2, sw = kswz<NC>(lg);
+        const int a = n & 3, j = n >> 2;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-            tr[d] = j * pitch + ((lg * NC + ((2 * d + (a >> 1)) ^ sw)) << 4) + ((a & 1) << 3);
+            tr[d] = j * pitch + ((lg * NC + kslot<NC>(2 * d + (a >> 1), lg, j)) << 4) +
+                    ((a & 1) << 3);
     }
 };
 
@@ -467,7 +481,9 @@ __device__ __forceinline__ void slab_steps(int p0, int p1, int nslab, char *b0, 
 template <int D, int W>
 struct Slabs {
     static constexpr int NC = D * 2 / 16;
-    static constexpr int kPitch = ((W * NC) | 1) * 16;  // odd number of 16-byte chunks
+    // 128 (4 chunks per point) or 16 (8 chunks) bytes past a multiple of 256
+    static constexpr int kRes = NC == 4 ? 128 : 16;
+    static constexpr int kPitch = (W * NC * 16 - kRes + 255) / 256 * 256 + kRes;
     static constexpr int kSlab = 4 * kPitch;
     static constexpr int kBuf = 2 * kSlab;
 };
