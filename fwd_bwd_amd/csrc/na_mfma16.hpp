@@ -287,7 +287,7 @@ struct Stager {
 // (logsumexp, delta) of the slab point thread i stages (i < 4 box_w; column
 // major: the four rows of column c at 4c .. 4c + 3). rows_load only issues the
 // loads, so that they can run under a walk; rows_store writes
-// (logsumexp * log2(e), delta) to LDS.
+// (-logsumexp * log2(e), -delta) to LDS.
 __device__ __forceinline__ float2 rows_load(const float *lse, const float *delta,
                                             const TileCtx &w, int tk, int r0, int U2, int box_w) {
     const int i = threadIdx.x;
@@ -297,7 +297,7 @@ __device__ __forceinline__ float2 rows_load(const float *lse, const float *delta
     return make_float2(lse[ro], delta[ro]);
 }
 __device__ __forceinline__ void rows_store(float2 v, int box_w, float2 *rows) {
-    if ((int)threadIdx.x < 4 * box_w) rows[threadIdx.x] = make_float2(v.x * kLog2e, v.y);
+    if ((int)threadIdx.x < 4 * box_w) rows[threadIdx.x] = make_float2(-v.x * kLog2e, -v.y);
 }
 
 // Maximum and sum over the four lanes n, n + 16, n + 32, n + 48 (the lane
@@ -671,6 +671,7 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     if (wk.on && P.active && lg == 0) a.delta[ro] = delta;
     const float nlse2 = -a.lse[ro] * kLog2e;
     const float c = a.qscale;
+    const f4 ndelta = f4{-delta, -delta, -delta, -delta};
     const LaneAddr<D> la(S::kPitch, lg, n);
     const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -712,10 +713,11 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
             // a wave's odd last block pairs with itself (its weights are masked)
             const int second = two ? BLK : 0;
             const char *kb = Kc + col0 * NC * 16, *vb = Vc + col0 * NC * 16;
+            // dP - delta: the products start from -delta
             f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
-            f4 p0 = Mf<T>::mma(km_at(vb, la.km[0]), dv[0], zero);
+            f4 p0 = Mf<T>::mma(km_at(vb, la.km[0]), dv[0], ndelta);
             f4 s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
-            f4 p1 = Mf<T>::mma(km_at(vb + second, la.km[0]), dv[0], zero);
+            f4 p1 = Mf<T>::mma(km_at(vb + second, la.km[0]), dv[0], ndelta);
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
@@ -730,8 +732,8 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
             for (int r = 0; r < 4; ++r) {
                 const float e0 = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, nlse2) : -INFINITY);
                 const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
-                ds[r] = e0 * (p0[r] - delta);
-                ds[4 + r] = e1 * (p1[r] - delta);
+                ds[r] = e0 * p0[r];
+                ds[4 + r] = e1 * p1[r];
             }
             uint4 db;
             db.x = Mf<T>::pack(ds[0], ds[1]);
@@ -858,21 +860,21 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
                 s1 = Mf<T>::mma(km_at(qb + second, la.km[h]), kv[h], s1);
                 p1 = Mf<T>::mma(km_at(ob + second, la.km[h]), vv[h], p1);
             }
-            // (lse, delta) of the four rows of this lane group's query column
+            // (-lse * log2 e, -delta) of the four rows of this lane group's query column
             const float4 *rp0 = reinterpret_cast<const float4 *>(Rc + 4 * (col0 + lg));
             const float4 *rp1 = reinterpret_cast<const float4 *>(Rc + 4 * (two ? col0 + 4 + lg : col0 + lg));
             const float4 l0a = rp0[0], l0b = rp0[1], l1a = rp1[0], l1b = rp1[1];
-            const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, dl0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
-            const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, dl1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
+            const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, nd0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
+            const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, nd1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
             const bool w0 = (unsigned)(col0 + irel) <= (unsigned)iwn;
             const bool w1 = two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
             float pr[8], ds[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, -ls0[r]) : -INFINITY);
-                pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, -ls1[r]) : -INFINITY);
-                ds[r] = pr[r] * (p0[r] - dl0[r]);
-                ds[4 + r] = pr[4 + r] * (p1[r] - dl1[r]);
+                pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, ls0[r]) : -INFINITY);
+                pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, ls1[r]) : -INFINITY);
+                ds[r] = pr[r] * (p0[r] + nd0[r]);
+                ds[4 + r] = pr[4 + r] * (p1[r] + nd1[r]);
             }
             uint4 pb, db;
             pb.x = Mf<T>::pack(pr[0], pr[1]);
