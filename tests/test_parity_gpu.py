@@ -130,17 +130,24 @@ SMALL = [
     ((1, 1, 40, 37, 2, 32), (1, 9, 9), 1, torch.float32),
     ((1, 9, 30, 1, 32), (9, 5), 1, torch.float32),
     ((1, 18, 18, 1, 16), (3, 3), 6, torch.float32),
-    # fp16 (binary16 storage, fp32 arithmetic): 2D, 3D, dilation, every head_dim
+    # fp16: 2D, 3D, dilation, every head_dim (head_dim 16: the fp32 kernels after
+    # conversion; 32 and 64: the 16-bit MFMA kernels)
     ((1, 19, 23, 2, 32), (5, 7), 1, torch.float16),
     ((1, 5, 18, 20, 2, 16), (3, 5, 5), 1, torch.float16),
     ((2, 26, 27, 2, 64), (5, 5), 2, torch.float16),
     ((1, 40, 37, 2, 32), (9, 9), 1, torch.float16),
-    # 16-bit tensors on the register-resident kernels (head_dim 32, square walks):
-    # 2D with border launches, 3D, dilation
+    # 16-bit MFMA kernels: 2D with several tiles and ragged tails, 3D, dilation
     ((1, 40, 37, 2, 32), (9, 9), 1, torch.bfloat16),
     ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float16),
     ((1, 5, 40, 36, 1, 32), (3, 7, 7), 1, torch.bfloat16),
     ((1, 35, 33, 2, 32), (5, 5), (1, 2), torch.float16),
+    # 16-bit MFMA kernels with wider slab rows: up to 32 points (k = 13, 17 and a
+    # 3D 11 x 11 window) and up to 48 (k = 21; inverse walks up to 44 columns)
+    ((1, 44, 41, 2, 32), (13, 13), 1, torch.bfloat16),
+    ((1, 40, 38, 1, 64), (17, 15), 1, torch.float16),
+    ((1, 3, 30, 29, 1, 32), (3, 11, 11), 1, torch.float16),
+    ((1, 50, 48, 1, 32), (21, 21), 1, torch.bfloat16),
+    ((1, 46, 49, 1, 64), (19, 21), 1, torch.float16),
 ]
 
 
