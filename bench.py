@@ -58,6 +58,9 @@ METRIC = "NA fwd+bwd ms & TFLOP/s (% roofline): 2D 1024² k9×9, 3D 16×256² k3
 PEAK_TFLOPS = {"fp32_mfma": 157.3, "bf16_mfma": 2516.6}
 PEAK_HBM_GBS = 8000.0
 DTYPE_LABEL = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+# parity bar of the sampled check beside the CPU baseline (max abs error over
+# max abs reference value, per tensor), as in the GPU parity tests
+TOLERANCE = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-3}
 FLUSH_BYTES = 1 << 30
 
 
@@ -169,6 +172,13 @@ class Runner:
         na.na_bwd(self.q, self.k, self.v, self.out, self.dout, self.lse, *self.args,
                   variant="kvparallel", workspace=self.ws, grads=(self.dq, self.dk, self.dv),
                   kv_splits=self.kv_splits)
+
+    def outputs_host(self):
+        """The last pass's results on the host (for the parity check of the
+        CPU-baseline sample)."""
+        torch.cuda.synchronize()
+        return {"out": self.out.cpu(), "lse": self.lse.cpu(), "dq": self.dq.cpu(),
+                "dk": self.dk.cpu(), "dv": self.dv.cpu()}
 
     def phases(self):
         if self.variant == "gather":
@@ -366,7 +376,12 @@ def leg(w, per, wall=None, warm=None, tag=None):
     return out
 
 
-def cpu_baseline(w, host, target_s, seed=1):
+def cpu_baseline(w, host, target_s, seed=1, gpu=None):
+    """The oracle on a random sample of (b, token, head) units sized for about
+    target_s seconds, scaled linearly to the workload. With the GPU results of
+    the timed passes (gpu), the sample's oracle values also give the parity
+    errors of every output tensor at those units (max abs error over max abs
+    reference value)."""
     import oracle
     q, k, v, dout = (t.float().numpy().astype(np.float64) for t in host)
     units = w.tokens * w.heads
@@ -375,30 +390,41 @@ def cpu_baseline(w, host, target_s, seed=1):
     def run(n):
         sel = np.sort(rng.integers(0, units, n))
         t0 = time.perf_counter()
-        oracle.na_fwd(q, k, v, w.kernel, w.dilation, w.the_scale, sel=sel)
-        oracle.na_bwd(q, k, v, dout, w.kernel, w.dilation, w.the_scale, sel=sel)
-        return time.perf_counter() - t0
+        o, lse = oracle.na_fwd(q, k, v, w.kernel, w.dilation, w.the_scale, sel=sel)
+        dq, dk, dv = oracle.na_bwd(q, k, v, dout, w.kernel, w.dilation, w.the_scale, sel=sel)
+        return time.perf_counter() - t0, sel, {"out": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
     # a warm-up call (thread team start-up), then a pilot long enough to time,
     # sizes the sample to about target_s of work; one resize if it came out short
     run(256)
     pilot_n = 8192
-    t_pilot = run(pilot_n)
+    t_pilot = run(pilot_n)[0]
     n = int(max(pilot_n, min(units, pilot_n * target_s / max(t_pilot, 1e-6))))
     log(f"[bench] oracle pilot {pilot_n} units {t_pilot:.2f}s -> sample {n} units")
-    t = run(n)
+    t, sel, ref = run(n)
     if t < 0.5 * target_s and n < units:
         n = int(min(units, n * target_s / max(t, 1e-6)))
         log(f"[bench] oracle sample short ({t:.1f}s) -> {n} units")
-        t = run(n)
+        t, sel, ref = run(n)
     f_fwd, f_bwd = flops(w)
     full_s = t * units / n
-    return {"value": round((f_fwd + f_bwd) / full_s / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": (f"{n} random (b, token, head) units of {w.name}: forward and dq at them "
-                       f"as queries, dk and dv at them as keys, fp64, {t:.1f} s; rate "
-                       f"extrapolated linearly to the whole workload ({full_s:.0f} s)"),
-            "est_full_ms": round(full_s * 1e3, 1)}
+    out = {"value": round((f_fwd + f_bwd) / full_s / 1e12, 6), "unit": "TFLOP/s",
+           "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": (f"{n} random (b, token, head) units of {w.name}: forward and dq at them "
+                      f"as queries, dk and dv at them as keys, fp64, {t:.1f} s; rate "
+                      f"extrapolated linearly to the whole workload ({full_s:.0f} s)"),
+           "est_full_ms": round(full_s * 1e3, 1)}
+    if gpu is not None:
+        errs = {}
+        for name, r in ref.items():
+            flat = gpu[name].float().numpy()
+            g = (flat.reshape(-1)[sel] if name == "lse" else
+                 flat.reshape(-1, w.head_dim)[sel]).astype(np.float64)
+            errs[name] = float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
+        out["parity"] = {"units": int(n), "max_rel_err": {k_: round(e, 8) for k_, e in errs.items()},
+                         "tolerance": TOLERANCE[w.dtype],
+                         "within": bool(all(e <= TOLERANCE[w.dtype] for e in errs.values()))}
+    return out
 
 
 def host_info():
@@ -491,6 +517,7 @@ def main():
 
     w = WORKLOADS[args.workload]
     r, main_leg = timed(w, args.variant, args.steps, args.warmup, args.kv_splits)
+    gpu_main = None if args.no_cpu_baseline else r.outputs_host()
 
     result = {
         "metric": METRIC,
@@ -555,12 +582,13 @@ def main():
             del r16
             torch.cuda.empty_cache()
         result.update(extra)
-    h3 = None
+    h3 = gpu_3d = None
     if not args.no_secondary and args.workload == HEADLINE:
         w3 = WORKLOADS[HEADLINE_3D]
         r3, s3 = timed(w3, args.variant, args.steps, args.warmup)
         result["secondary"] = {"workload": w3.name, **s3}
         h3 = r3.host
+        gpu_3d = None if args.no_cpu_baseline else r3.outputs_host()
         del r3
         torch.cuda.empty_cache()
         run_unfused(w3, h3)
@@ -581,10 +609,10 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, gpu=gpu_main)
         if h3 is not None:
             result["secondary"]["cpu_baseline"] = cpu_baseline(WORKLOADS[HEADLINE_3D], h3,
-                                                               args.cpu_seconds)
+                                                               args.cpu_seconds, gpu=gpu_3d)
     else:
         result["cpu_baseline"] = None
 

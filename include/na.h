@@ -70,9 +70,14 @@ typedef enum {
 
 typedef enum {
     NA_F32 = 0,   /* fp32 tensors, fp32 arithmetic */
-    NA_BF16 = 1,  /* bf16 tensors (round-to-nearest-even on output), fp32 arithmetic */
-    NA_F16 = 2    /* IEEE fp16 tensors (round-to-nearest-even on output), fp32 arithmetic
-                     (the issue's maintainer profiles the fused op at fp16 beside fp32) */
+    NA_BF16 = 1,  /* bf16 tensors (round-to-nearest-even on output) */
+    NA_F16 = 2    /* IEEE fp16 tensors (round-to-nearest-even on output; the issue's
+                     maintainer profiles the fused op at fp16 beside fp32).
+                     16-bit tensors with head_dim 32 or 64: products on the 16-bit
+                     MFMA with fp32 accumulation; the attention weights and score
+                     gradients are rounded to the tensor type before the weighted
+                     sums; softmax statistics, lse and delta stay fp32. Other
+                     16-bit problems: fp32 arithmetic after conversion. */
 } na_dtype;
 
 /* Backward strategies (the NATTEN issue's use_kv_parallelism_in_fused_na

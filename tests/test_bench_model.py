@@ -9,7 +9,9 @@ import os
 import pytest
 
 import bench
-from fwd_bwd_amd.inputs import WORKLOADS
+import torch
+
+from fwd_bwd_amd.inputs import WORKLOADS, make_inputs
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
                                      "arithmetic_intensity.json")))
@@ -104,3 +106,24 @@ def test_summarize_reports_medians_and_the_step_sum():
     assert s["fwd_ms"] == 2.0 and s["fwd_ms_stats"]["min"] == 1.0
     # per step: 6, 10, 14 -> median 10; backward per step 5, 5, 12 -> median 5
     assert s["ms_per_step"] == 10.0 and s["bwd_ms"] == 5.0
+
+
+def test_cpu_baseline_parity_check_reads_the_sampled_units():
+    """bench.cpu_baseline compares the GPU results it is given with the
+    oracle at the sampled units: results equal to the oracle's pass, a 0.1%
+    error in one tensor is reported for that tensor."""
+    import numpy as np
+    import oracle
+    w = WORKLOADS["2d_16x16_k3_h2_d16_f32"]
+    host = make_inputs(w, 0)
+    q, k, v, do = (t.double().numpy() for t in host)
+    o, lse = oracle.na_fwd(q, k, v, w.kernel, w.dilation, w.the_scale)
+    dq, dk, dv = oracle.na_bwd(q, k, v, do, w.kernel, w.dilation, w.the_scale)
+    gpu = {n: torch.tensor(np.asarray(x)) for n, x in
+           (("out", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+    par = bench.cpu_baseline(w, host, 0.2, gpu=gpu)["parity"]
+    assert par["within"] and max(par["max_rel_err"].values()) < 1e-6
+    gpu["dk"] = gpu["dk"] * 1.001
+    par = bench.cpu_baseline(w, host, 0.2, gpu=gpu)["parity"]
+    assert not par["within"]
+    assert abs(par["max_rel_err"]["dk"] - 1e-3) < 1e-5 and par["max_rel_err"]["dq"] < 1e-6
