@@ -109,6 +109,7 @@ struct Mf<f16> {
 // A workgroup of kWG waves owns a 1 x kTH x kTW tile: two rows of four 4 x 4
 // patches (wave v: patch row v / 4, patch column v % 4).
 constexpr int kWG = 8, kTG = 64 * kWG;
+
 constexpr int kTH = 8, kTW = 16;  // tile rows (H) and columns (W); T: one plane
 
 struct Geom {
@@ -490,8 +491,10 @@ struct Slabs {
 
 // ============================================================================
 // Forward: out, lse.
+// Waves per SIMD (the launch bound's second value): the head_dim-32 forward
+// fits 64 VGPRs, four workgroups per CU; wider slabs are bound by their LDS.
 template <typename T, int D, int W>
-__global__ void __launch_bounds__(kTG, 2) fwd_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Args<T> a) {
     using S = Slabs<D, W>;
     __shared__ __align__(16) char buf0[S::kBuf];
     __shared__ __align__(16) char buf1[S::kBuf];
@@ -763,6 +766,8 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
 // inverse windows: S = Q K^T (A = a query block, key-major; B = the wave's
 // keys), P = exp2(S c - lse), dP = dO V^T, dS = P (dP - delta); then
 // dV^T += dO^T P and dK^T += Q^T dS over pairs of query blocks.
+// Four waves per SIMD up to 32-point slab rows: 128 VGPRs, two workgroups per
+// CU also at head_dim 64; wider slabs are bound by their LDS.
 template <typename T, int D, int W>
 __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     using S = Slabs<D, W>;
