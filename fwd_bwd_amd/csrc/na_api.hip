@@ -298,7 +298,7 @@ void set_divisors(na::fast::Geom &g) {
 // edge >= 0: the box only over the tiles of that border class (inverse walk
 // along H above walk_lo exactly when bit 0 is set, along W when bit 1 is).
 bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool pad = false,
-               int cw = 0, int edge = -1) {
+               int cw = 0, int edge = -1, bool one_layout = false) {
     // fp32 with head_dim 16 or 32; bf16 / fp16 (converted to fp32 while staged)
     // with head_dim 32
     if (q.dtype == NA_F32) {
@@ -341,8 +341,11 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
     // row pitches: an odd number of 16-byte slots (A), 2 mod 4 slots (B; both
     // patterns when padded)
     const int slots = mx[2] * PB / 16;
-    const int rb = (slots + ((2 - slots % 4) + 4) % 4) * 16;
-    const int ra = pad ? rb : (slots | 1) * 16;
+    // one_layout (the backward's unpadded plans): both read patterns from the
+    // A pitch, so a tensor the backward reads both ways is staged once (its
+    // d-major reads then take bank conflicts; measured faster than a restaging)
+    const int ra = pad ? (slots + ((2 - slots % 4) + 4) % 4) * 16 : (slots | 1) * 16;
+    const int rb = pad || one_layout ? ra : (slots + ((2 - slots % 4) + 4) % 4) * 16;
     int64_t lds = (int64_t)mx[1] * std::max(ra, rb);
     na::fast::Geom &g = pl->g;
     g = na::fast::Geom{};
@@ -385,7 +388,8 @@ bool fast_plan(const Prob &q, int kind, int c, int walk_lo, FastPlan *pl, bool p
 bool fast_plan_fwd(const Prob &q, FastPlan *pl, bool try_pad = false) {
     const int c = na::window_walk(q.ker[1], 2);
     if (na::window_walk(q.ker[2], 2) != c) return false;
-    return (try_pad && fast_plan(q, 0, c, 0, pl, true)) || fast_plan(q, 0, c, 0, pl);
+    return (try_pad && fast_plan(q, 0, c, 0, pl, true)) ||
+           fast_plan(q, 0, c, 0, pl, false, 0, -1, try_pad);
 }
 
 template <typename Kern, typename Args>
@@ -734,7 +738,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             const int need = max_tile_walk(pr);
             const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
             int done = 0;  // tiles with inverse walk <= done are covered
-            if (fast_plan(pr, 1, c, 0, &pk, true) || fast_plan(pr, 1, c, 0, &pk)) {
+            if (fast_plan(pr, 1, c, 0, &pk, true) || fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true)) {
                 fa.g = pk.g;
                 fa.walk_lo = 0;
                 const na_status st = fast_dkdv<T>(pk, fa, s);
@@ -752,7 +756,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
                     if (((e & 1) && hm <= done) || ((e & 2) && wm <= done)) continue;  // no such tile
                     const int ch = (e & 1) ? hm : done, cw = (e & 2) ? wm : done;
                     use[e] = fast_plan(pr, 1, ch, done, &cls[e], true, cw, e) ||
-                             fast_plan(pr, 1, ch, done, &cls[e], false, cw, e);
+                             fast_plan(pr, 1, ch, done, &cls[e], false, cw, e, true);
                     all = all && use[e];
                 }
                 if (all) {
@@ -780,7 +784,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
                 }
             }
             for (int cb = c + 1; done > 0 && done < need && cb <= need; ++cb) {
-                if (!fast_plan(pr, 1, cb, done, &pk, true) && !fast_plan(pr, 1, cb, done, &pk))
+                if (!fast_plan(pr, 1, cb, done, &pk, true) &&
+                    !fast_plan(pr, 1, cb, done, &pk, false, 0, -1, true))
                     continue;
                 fa.g = pk.g;
                 fa.walk_lo = done;

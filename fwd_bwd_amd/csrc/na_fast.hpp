@@ -634,10 +634,13 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
                     pin4(s[i]);
                 });
         }
+        // the d-major layout: a restaging unless both layouts share the pitch
         if constexpr (!PAD) {
-            __syncthreads();
-            stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
-            stage_wait();
+            if (rb != ra) {
+                __syncthreads();
+                stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], rb, smem);
+                stage_wait();
+            }
         }
 
         // dQ_b[i][c] += k_e[dim(i, g)] * dS[c][e]
@@ -793,12 +796,14 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
         if constexpr (!T3)
             if (L.active) store_row<T, D>(a.dv + ko, dv, 1.f);
         float vr[D];
-        if constexpr (!PAD) {
+        // the key-major layout: a restaging unless both layouts share the pitch
+        const bool restage = !PAD && rb != ra;
+        if (restage) {
             __syncthreads();
             stage_plane<T, D, PS>(a.dout, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         }
         load_row<T, D>(a.v + ko + opaque_zero(), vr);
-        if constexpr (!PAD) stage_wait();
+        if (restage) stage_wait();
 
         // dP_b[i][c] = <dout_i, v_c> - delta_i;  dS = P dP
         {
