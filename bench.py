@@ -23,6 +23,11 @@ flush itself is outside the timed events. Per pass the median, minimum and
 mean over the timed steps are reported; the headline value uses the medians.
 The same steps without the flush are reported beside it ("warm").
 
+The 3D workload is also timed with every window restricted along T to a
+constant 1 and 2 of its 3 planes (na_fwd_framed / na_bwd_framed, "framed"):
+the kernels skip key planes outside a query's frame window, so the time
+should follow the kept fraction of the window.
+
 Beside the headline step the same run times the KV-parallel backward variant
 on the same inputs ("kvparallel", per kv_splits: 0 = float atomics, 1 and 4 =
 bounded accumulator copies, bitwise reproducible), the headline shape with
@@ -139,13 +144,15 @@ def algorithmic_bytes(w):
 
 
 class Runner:
-    def __init__(self, w, variant, seed=0, kv_splits=0):
+    def __init__(self, w, variant, seed=0, kv_splits=0, host=None):
         self.w = w
         self.variant = variant
         self.kv_splits = kv_splits
         dev = torch.device("cuda:0")
-        log(f"[bench] generating inputs for {w.name}")
-        q, k, v, dout = make_inputs(w, seed)
+        if host is None:
+            log(f"[bench] generating inputs for {w.name}")
+            host = make_inputs(w, seed)
+        q, k, v, dout = host
         self.host = (q, k, v, dout)
         self.q, self.k, self.v, self.dout = (t.to(dev) for t in (q, k, v, dout))
         self.out = torch.empty_like(self.q)
@@ -211,6 +218,45 @@ class Runner:
         per = {name: [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]
                for i, (name, _) in enumerate(ph)}
         return per, wall
+
+
+class FramedRunner(Runner):
+    """The same step through na_fwd_framed / na_bwd_framed (gather): every
+    query's window restricted along the outermost axis to frame[x0] positions
+    (the requester's per-frame time kernel on 3D grids)."""
+
+    def __init__(self, w, frame, host=None, seed=0):
+        super().__init__(w, "gather", seed, host=host)
+        self.frame = list(frame)
+        self.fk = torch.tensor(self.frame, dtype=torch.int32, device="cuda:0")
+
+    def fwd(self):
+        na.na_fwd_framed(self.q, self.k, self.v, self.fk, *self.args, out=self.out, lse=self.lse)
+
+    def bwd(self):
+        na.na_bwd_framed(self.q, self.k, self.v, self.out, self.dout, self.lse, self.fk,
+                         *self.args, workspace=self.ws, grads=(self.dq, self.dk, self.dv))
+
+    def phases(self):
+        return [("fwd", self.fwd), ("bwd_framed", self.bwd)]
+
+
+def kept_fraction(w, frame):
+    """Mean share of a query's full window that a restricted window keeps:
+    along the outermost axis a query at x0 keeps min(frame[x0], k0) of the k0
+    window positions."""
+    k0 = w.kernel[0]
+    return float(np.mean([min(max(f, 0), k0) for f in frame])) / k0
+
+
+def framed_leg(w, per, full):
+    """Times of a restricted-window step beside the unrestricted step (full)."""
+    s = summarize(w, per)
+    return {"fwd_ms": s["fwd_ms"], "bwd_ms": s["bwd_ms"], "ms_per_step": s["ms_per_step"],
+            "step_ms_stats": s["step_ms_stats"], "kernel_ms": s["kernel_ms"],
+            "time_vs_full": {"fwd": round(s["fwd_ms"] / full["fwd_ms"], 4),
+                             "bwd": round(s["bwd_ms"] / full["bwd_ms"], 4),
+                             "step": round(s["ms_per_step"] / full["ms_per_step"], 4)}}
 
 
 # ----------------------------------------------------------------------------- unfused leg
@@ -474,6 +520,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hash")
+    ap.add_argument("--frame", type=int, default=None,
+                    help="only time the workload with every window restricted to this many "
+                         "positions along the outermost axis (na_fwd_framed / na_bwd_framed; "
+                         "prints the times alone)")
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -516,6 +566,18 @@ def main():
         return r, out
 
     w = WORKLOADS[args.workload]
+    if args.frame is not None:
+        # restricted windows only (one kernel trace holds the framed launches alone)
+        frame = [args.frame] * w.grid[0]
+        rf = FramedRunner(w, frame)
+        log(f"[bench] timing {w.name} with frame {args.frame}")
+        per, _ = rf.time(args.steps, args.warmup, flush)
+        s = summarize(w, per)
+        print(json.dumps({"workload": w.name, "frame": args.frame,
+                          "kept_fraction": round(kept_fraction(w, frame), 4),
+                          **{k: s[k] for k in ("fwd_ms", "bwd_ms", "ms_per_step", "kernel_ms")}}),
+              flush=True)
+        return
     r, main_leg = timed(w, args.variant, args.steps, args.warmup, args.kv_splits)
     gpu_main = None if args.no_cpu_baseline else r.outputs_host()
 
@@ -591,6 +653,20 @@ def main():
         gpu_3d = None if args.no_cpu_baseline else r3.outputs_host()
         del r3
         torch.cuda.empty_cache()
+        if not args.no_extra and args.variant == "gather":
+            # the same 3D step with windows restricted per frame (na_fwd_framed /
+            # na_bwd_framed): constant time windows of 1 and 2 of the 3 planes
+            framed = {}
+            for f in (1, 2):
+                frame = [f] * w3.grid[0]
+                rf = FramedRunner(w3, frame, host=h3)
+                log(f"[bench] timing {w3.name} with frame {f}")
+                per, _ = rf.time(args.steps, args.warmup, flush)
+                framed[f"frame_{f}"] = {"kept_fraction": round(kept_fraction(w3, frame), 4),
+                                        **framed_leg(w3, per, s3)}
+                del rf
+                torch.cuda.empty_cache()
+            result["secondary"]["framed"] = framed
         run_unfused(w3, h3)
     if unfused:
         result["unfused"] = unfused

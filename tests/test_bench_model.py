@@ -127,3 +127,18 @@ def test_cpu_baseline_parity_check_reads_the_sampled_units():
     par = bench.cpu_baseline(w, host, 0.2, gpu=gpu)["parity"]
     assert not par["within"]
     assert abs(par["max_rel_err"]["dk"] - 1e-3) < 1e-5 and par["max_rel_err"]["dq"] < 1e-6
+
+
+def test_framed_leg_kept_fraction_and_ratios():
+    """The restricted-window leg: a constant frame of f of the 3 time planes
+    keeps f/3 of every window (sizes above the window or below zero are
+    clipped), and the leg's times are reported against the full step."""
+    w = WORKLOADS[bench.HEADLINE_3D]
+    assert bench.kept_fraction(w, [1] * w.grid[0]) == pytest.approx(1 / 3)
+    assert bench.kept_fraction(w, [2] * w.grid[0]) == pytest.approx(2 / 3)
+    assert bench.kept_fraction(w, [5] * 8 + [0] * 8) == pytest.approx(0.5)
+    per = {"fwd": [1.0, 1.0, 1.0], "bwd_framed": [2.0, 3.0, 2.0]}
+    full = {"fwd_ms": 2.0, "bwd_ms": 8.0, "ms_per_step": 10.0}
+    leg = bench.framed_leg(w, per, full)
+    assert leg["ms_per_step"] == 3.0
+    assert leg["time_vs_full"] == {"fwd": 0.5, "bwd": 0.25, "step": 0.3}
