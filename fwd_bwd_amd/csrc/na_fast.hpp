@@ -518,7 +518,9 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
 // Backward, query side: delta and dq.
 // PAD: points one 16-byte slot apart in LDS (row pitch 2 mod 4 slots), which
 // makes key-major and d-major reads both conflict-free, so K is staged once
-// for both of its uses; without it K is staged twice, in each layout.
+// for both of its uses. Without it K is staged once as well when the plan
+// gives both layouts one pitch (the d-major reads then take bank conflicts),
+// else once per layout.
 template <typename T, int D, int CH, int CW, bool T3, bool PAD>
 __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
