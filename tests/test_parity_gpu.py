@@ -168,6 +168,47 @@ def test_small_cases_match_oracle(case, variant):
     compare(got, ref, dtype, f"{_id(case)} {variant}")
 
 
+# Scales other than head_dim^-0.5 (the ABI takes any finite one): negative
+# (the 16-bit forward flips the queries' signs then), zero (uniform weights,
+# dq = dk = 0 exactly), large (peaked softmax: the lazy rescaling of the
+# 16-bit forward and the per-plane rescale of the fp32 one take many steps)
+# and tiny, on one case of each kernel family: fp32 register-resident 2D and
+# 3D, the fp32 split kernels (head_dim 64), the 16-bit MFMA kernels at head_dim
+# 32 (2D, 3D) and 64 (dilated).
+SCALE_CASES = [
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.float32),
+    ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float32),
+    ((1, 20, 20, 1, 64), (9, 9), 1, torch.float32),
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.bfloat16),
+    ((1, 3, 37, 35, 1, 32), (3, 5, 5), 1, torch.float16),
+    ((2, 26, 27, 2, 64), (5, 5), 2, torch.float16),
+]
+
+
+@pytest.mark.parametrize("scale", [-0.7, 0.0, 2.5, 1e-3])
+@pytest.mark.parametrize("case", SCALE_CASES, ids=[_id(c) for c in SCALE_CASES])
+def test_other_scales_match_oracle(case, scale):
+    shape, kernel, dil, dtype = case
+    say("case", _id(case), "scale", scale)
+    q, k, v, dout = make_random(shape, dtype, seed=zlib.crc32(_id(case).encode()) % 1000 + 7)
+    got = gpu_run(q, k, v, dout, kernel, dil, scale, "gather")
+    ref = oracle_full(q, k, v, dout, kernel, dil, scale)
+    errs = compare(got, ref, dtype, f"{_id(case)} scale {scale}")
+    if scale == 0.0:
+        # uniform weights over each window: lse = log(window size), no q / k gradient
+        assert np.all(np64(got["dq"]) == 0) and np.all(np64(got["dk"]) == 0)
+        assert errs["lse"] <= 1e-6
+
+
+def test_kvparallel_with_a_negative_scale():
+    shape, kernel, dil, dtype = (2, 14, 15, 2, 32), (5, 7), (1, 2), torch.float32
+    q, k, v, dout = make_random(shape, dtype, seed=19)
+    for variant in ("kvparallel", "kvdet"):
+        got = gpu_run(q, k, v, dout, kernel, dil, -0.4, variant)
+        ref = oracle_full(q, k, v, dout, kernel, dil, -0.4)
+        compare(got, ref, dtype, f"negative scale {variant}")
+
+
 def test_first_workload_full_and_dout_ones():
     """The 16x16 fp32 workload, every output, dout = ones as in the issue's script."""
     w = WORKLOADS["2d_16x16_k3_h2_d16_f32"]
