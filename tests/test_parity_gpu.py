@@ -148,6 +148,12 @@ SMALL = [
     ((1, 3, 30, 29, 1, 32), (3, 11, 11), 1, torch.float16),
     ((1, 50, 48, 1, 32), (21, 21), 1, torch.bfloat16),
     ((1, 46, 49, 1, 64), (19, 21), 1, torch.float16),
+    # 16-bit MFMA kernels on the degenerate and dilated shapes: dilation along
+    # T and H of a 3D grid, kernel = grid (dense attention), k = 1, even kernels
+    ((1, 6, 20, 18, 2, 32), (3, 5, 5), (2, 2, 1), torch.bfloat16),
+    ((1, 7, 9, 2, 32), (7, 9), 1, torch.bfloat16),
+    ((1, 11, 10, 2, 64), (1, 1), 1, torch.float16),
+    ((1, 12, 11, 1, 32), (4, 2), 1, torch.float16),
 ]
 
 
