@@ -586,7 +586,7 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
     constexpr int PB = D * (int)sizeof(T);
     if constexpr (!std::is_same<T, float>::value && (D == 32 || D == 64)) {
         M16Plan mp;
-        if (m16_plan(pr, 0, &mp)) {
+        if (!a.mask && m16_plan(pr, 0, &mp)) {
             na::m16::Args<T> ma{};
             ma.g = mp.g;
             ma.q = static_cast<const T *>(a.q);
@@ -601,7 +601,8 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
         }
     }
     FastPlan pl;
-    if (fast_plan_fwd(pr, &pl)) {
+    // window masks: the split kernels only
+    if (!a.mask && fast_plan_fwd(pr, &pl)) {
         na::fast::FwdArgsT<T> fa{};
         fa.g = pl.g;
         fa.q = static_cast<const T *>(a.q);
@@ -671,7 +672,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
     if (!geometry(pr, true, 2 * PB + 8, na::kWaves * 64 * (D + 1) * 4, &ak.g, &lds_k)) return NA_ERR_UNSUPPORTED;
     if constexpr (!std::is_same<T, float>::value && (D == 32 || D == 64)) {
         M16Plan mq, mk;
-        if (variant == NA_BWD_GATHER && m16_plan(pr, 1, &mq) && m16_plan(pr, 2, &mk)) {
+        if (variant == NA_BWD_GATHER && !a.mask && m16_plan(pr, 1, &mq) && m16_plan(pr, 2, &mk)) {
             na::m16::Args<T> ma{};
             ma.q = static_cast<const T *>(a.q);
             ma.k = static_cast<const T *>(a.k);
@@ -720,7 +721,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
         if (phases & kPhaseDq) {
-            if (fast_plan_fwd(pr, &pq, true)) {
+            if (!a.mask && fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;
                 const na_status st = fast_dq<T>(pq, fa, s);
                 if (st != NA_OK) return st;
@@ -738,7 +739,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             const int need = max_tile_walk(pr);
             const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
             int done = 0;  // tiles with inverse walk <= done are covered
-            if (fast_plan(pr, 1, c, 0, &pk, true) || fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true)) {
+            if (!a.mask && (fast_plan(pr, 1, c, 0, &pk, true) ||
+                            fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true))) {
                 fa.g = pk.g;
                 fa.walk_lo = 0;
                 const na_status st = fast_dkdv<T>(pk, fa, s);
@@ -921,7 +923,8 @@ na_status na_inverse_window(int64_t extent, int64_t kernel, int64_t dilation, in
 namespace {
 
 na_status fwd_common(const na_problem *p, const void *q, const void *k, const void *v, void *out,
-                     float *lse, const int32_t *frame, void *hip_stream) {
+                     float *lse, const int32_t *frame, void *hip_stream,
+                     const uint8_t *mask = nullptr) {
     Prob pr;
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
@@ -937,6 +940,8 @@ na_status fwd_common(const na_problem *p, const void *q, const void *k, const vo
     a.qscale = pr.scale * na::kLog2e;
     a.frame = frame;
     a.frame_axis = p->ndim == 3 ? 0 : 1;
+    a.mask = mask;
+    a.mask_k = (int)(pr.ker[0] * pr.ker[1] * pr.ker[2]);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define NA_FWD_D(D)                                                   \
     case D:                                                           \
@@ -967,6 +972,12 @@ na_status na_fwd_framed(const na_problem *p, const void *q, const void *k, const
     return fwd_common(p, q, k, v, out, lse, frame_kernel, hip_stream);
 }
 
+na_status na_fwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
+                        void *out, float *lse, const uint8_t *mask, void *hip_stream) {
+    if (validate(p, nullptr) == NA_OK && !mask) return NA_ERR_INVALID_ARG;
+    return fwd_common(p, q, k, v, out, lse, nullptr, hip_stream, mask);
+}
+
 size_t na_bwd_workspace_bytes(const na_problem *p, int32_t variant, int32_t kv_splits) {
     Prob pr;
     if (validate(p, &pr) != NA_OK || kv_splits < 0) return 0;
@@ -984,7 +995,8 @@ namespace {
 na_status bwd_common(const na_problem *p, const void *q, const void *k, const void *v,
                      const void *out, const void *dout, const float *lse, void *dq, void *dk,
                      void *dv, float *delta, float *dq_acc, int32_t variant, int32_t kv_splits,
-                     int phases, void *hip_stream, const int32_t *frame = nullptr) {
+                     int phases, void *hip_stream, const int32_t *frame = nullptr,
+                     const uint8_t *mask = nullptr) {
     Prob pr;
     na_status st = validate(p, &pr);
     if (st != NA_OK) return st;
@@ -1004,6 +1016,8 @@ na_status bwd_common(const na_problem *p, const void *q, const void *k, const vo
     a.scale = pr.scale;
     a.frame = frame;
     a.frame_axis = p->ndim == 3 ? 0 : 1;
+    a.mask = mask;
+    a.mask_k = (int)(pr.ker[0] * pr.ker[1] * pr.ker[2]);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 #define NA_BWD_D(D)                                                                 \
     case D:                                                                         \
@@ -1028,7 +1042,8 @@ namespace {
 na_status bwd_entry(const na_problem *p, const void *q, const void *k, const void *v,
                     const void *out, const void *dout, const float *lse, void *dq, void *dk,
                     void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
-                    int32_t kv_splits, const int32_t *frame, void *hip_stream) {
+                    int32_t kv_splits, const int32_t *frame, void *hip_stream,
+                    const uint8_t *mask = nullptr) {
     na_status st = validate(p, nullptr);
     if (st != NA_OK) return st;
     if (variant != NA_BWD_GATHER && variant != NA_BWD_KVPARALLEL) return NA_ERR_INVALID_ARG;
@@ -1045,7 +1060,7 @@ na_status bwd_entry(const na_problem *p, const void *q, const void *k, const voi
                                                     round256((size_t)pr.rows * sizeof(float)))
                         : nullptr;
     return bwd_common(p, q, k, v, out, dout, lse, dq, dk, dv, delta, dq_acc, variant, kv_splits,
-                      kPhaseBoth, hip_stream, frame);
+                      kPhaseBoth, hip_stream, frame, mask);
 }
 
 }  // namespace
@@ -1065,6 +1080,15 @@ na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const
     if (validate(p, nullptr) == NA_OK && !frame_ok(frame_kernel)) return NA_ERR_INVALID_ARG;
     return bwd_entry(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, variant,
                      kv_splits, frame_kernel, hip_stream);
+}
+
+na_status na_bwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                        void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                        int32_t kv_splits, const uint8_t *mask, void *hip_stream) {
+    if (validate(p, nullptr) == NA_OK && !mask) return NA_ERR_INVALID_ARG;
+    return bwd_entry(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, variant,
+                     kv_splits, nullptr, hip_stream, mask);
 }
 
 na_status na_bwd_dq(const na_problem *p, const void *q, const void *k, const void *v,

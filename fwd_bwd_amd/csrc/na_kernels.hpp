@@ -45,6 +45,8 @@ struct FwdArgs {
     float qscale;  // scale * log2(e)
     const int *frame;  // windows restricted along frame_axis (null: none)
     int frame_axis;
+    const uint8_t *mask;  // window mask, K = mask_k bytes per query token (null: none)
+    int mask_k;
 };
 
 struct BwdArgs {
@@ -58,6 +60,8 @@ struct BwdArgs {
     float scale;
     const int *frame;  // windows restricted along frame_axis (null: none)
     int frame_axis;
+    const uint8_t *mask;  // window mask, K = mask_k bytes per query token (null: none)
+    int mask_k;
     // dk/dv: when skip_ch > 0, skip the tiles whose 16 x 16 super-tile has an
     // inverse walk of at most skip_ch x skip_cw patches (the register-resident
     // dk/dv kernel covers those)
@@ -251,6 +255,45 @@ __device__ __forceinline__ int chunk_mask(const ChunkView &cv, const Box &C, int
     return lo | hi;
 }
 
+// Window masks (the masked entry points). Byte j of the row of query token x
+// (K bytes per token of one (batch, head) plane, tokens in row-major (T, H, W)
+// grid order, shared by every batch element and head) is zero when x drops
+// the j-th key of its window (window offsets in row-major (t, h, w) order).
+// qc, kc: class coordinates of a query and of a key of its window.
+__device__ __forceinline__ bool mask_keeps(const uint8_t *mask, int K, const Geometry &g,
+                                           const TileCtx &w, const int (&qc)[3],
+                                           const int (&kc)[3]) {
+    int64_t tok = 0;
+    int j = 0;
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        tok = tok * g.ext[x] + (int64_t)qc[x] * w.d[x] + w.r[x];
+        j = j * w.k[x] + (kc[x] - window_start(qc[x], w.n[x], w.k[x]));
+    }
+    return mask[tok * K + j] != 0;
+}
+
+// The entry bits mk of an item with the dropped pairs cleared. QUERY_LANE: the
+// lane holds a query and the item's entries are keys of its window, walked
+// from st; else the lane holds a key and the entries are queries of its
+// inverse window, walked from st. Only entries already valid are looked up,
+// so every mask byte read lies in the row of an in-grid query.
+template <bool QUERY_LANE>
+__device__ __forceinline__ int mask_entries(int mk, const uint8_t *mask, int K, const Geometry &g,
+                                            const TileCtx &w, const int (&own)[3],
+                                            const int (&st)[3], const Item &it) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (!((mk >> e) & 1)) continue;
+        const int other[3] = {st[0] + it.c0, st[1] + 2 * it.c1 + (e >> 1),
+                              st[2] + 2 * it.c2 + (e & 1)};
+        const bool keep = QUERY_LANE ? mask_keeps(mask, K, g, w, own, other)
+                                     : mask_keeps(mask, K, g, w, other, own);
+        if (!keep) mk &= ~(1 << e);
+    }
+    return mk;
+}
+
 // ============================================================================
 // Forward: out, lse.
 template <typename T, int D>
@@ -323,7 +366,8 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
                 }
                 s = s0 + s1;
             }
-            const int mk = entry_mask(vm, it) & cm;
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
             float sv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[e] = (mk >> e) & 1 ? s[e] : -INFINITY;
@@ -501,7 +545,8 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
                 }
                 dp = d0 + d1;
             }
-            const int mk = entry_mask(vm, it) & cm;
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
             float ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -708,7 +753,8 @@ __global__ void __launch_bounds__(kThreads, MODE != 0 ? 1 : kSplitOccupancy<D>) 
                 }
                 dp = d0 + d1;
             }
-            const int mk = entry_mask(vm, it) & cm;
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<false>(mk, a.mask, a.mask_k, a.g, w, lp.p, lo, it);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

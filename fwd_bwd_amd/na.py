@@ -36,7 +36,7 @@ EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
            "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
            "na_qk_softmax_bwd", "na_source_sha256", "na_bwd_noalloc", "na_fwd_framed",
-           "na_bwd_framed")
+           "na_bwd_framed", "na_fwd_masked", "na_bwd_masked")
 
 # rows (batch * tokens * heads) the static delta array of na_bwd_noalloc holds
 NOALLOC_MAX_ROWS = 8388608
@@ -103,6 +103,11 @@ def load() -> ctypes.CDLL:
         lib.na_bwd_framed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                       ctypes.c_int32, ctypes.c_int32, vp, vp]
         lib.na_bwd_framed.restype = ctypes.c_int
+        lib.na_fwd_masked.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        lib.na_fwd_masked.restype = ctypes.c_int
+        lib.na_bwd_masked.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                      ctypes.c_int32, ctypes.c_int32, vp, vp]
+        lib.na_bwd_masked.restype = ctypes.c_int
         lib.na_window_start.argtypes = [i64, i64, i64, i64]
         lib.na_window_start.restype = i64
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
@@ -367,6 +372,63 @@ def na_bwd_framed(q, k, v, out, dout, lse, frame_kernel, kernel_size, dilation=1
                                 _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), vid,
                                 kv_splits, fp, _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def _check_window_mask(mask: torch.Tensor, q: torch.Tensor, kernel_size):
+    """Window mask of the masked entry points: contiguous uint8
+    [(T,) H, W, prod(kernel)] (token-major grid order), on q's device."""
+    ks = _tuple(kernel_size, q.dim() - 3)
+    K = 1
+    for k in ks:
+        K *= int(k)
+    want = tuple(q.shape[1:-2]) + (K,)
+    if (not isinstance(mask, torch.Tensor) or mask.dtype != torch.uint8
+            or tuple(mask.shape) != want or mask.device != q.device or not mask.is_contiguous()):
+        raise ValueError(f"mask must be a contiguous uint8 tensor of shape {want} on {q.device}")
+    return _ptr(mask)
+
+
+def na_fwd_masked(q, k, v, mask, kernel_size, dilation=1, scale=None, out=None, lse=None):
+    """na_fwd with an arbitrary set of each query's window keys masked
+    (mask[(t,) h, w, j] == 0 drops the j-th key of the window of token (t, h, w))."""
+    _check_tensors(q, k, v)
+    mp = _check_window_mask(mask, q, kernel_size)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_buf(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    _check(load().na_fwd_masked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                mp, _stream_handle(q.device)))
+    return out, lse
+
+
+def na_bwd_masked(q, k, v, out, dout, lse, mask, kernel_size, dilation=1, scale=None,
+                  variant="gather", kv_splits=0, workspace=None, grads=None):
+    """na_bwd with the windows of na_fwd_masked. Returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, out, dout)
+    _check_buf(lse, "lse", q.shape[:-1], torch.float32, q.device)
+    mp = _check_window_mask(mask, q, kernel_size)
+    p = make_problem(q.shape, q.dtype, kernel_size, dilation, scale)
+    vid = VARIANTS[variant]
+    if kv_splits < 0:
+        raise ValueError("kv_splits must be >= 0")
+    need = bwd_workspace_bytes(p, vid, kv_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(g, name, q.shape, q.dtype, q.device)
+    _check(load().na_bwd_masked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), vid,
+                                kv_splits, mp, _stream_handle(q.device)))
     return dq, dk, dv
 
 

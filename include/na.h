@@ -173,6 +173,27 @@ na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const
                         void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
                         int32_t kv_splits, const int32_t *frame_kernel, void *hip_stream);
 
+/* Windows with an arbitrary set of their keys masked: the requester's other
+ * form in the same thread, a tensor of the attended tokens of each query
+ * within its window (the maintainer: runtime follows the largest window, and
+ * only the masking changes). mask is a device array of bytes
+ * [(T,) H, W, prod(kernel)] in row-major order, one row per query token,
+ * shared by every batch element and head; byte j of a query's row is zero
+ * when the query drops the j-th key of its window (window offsets in
+ * row-major (t, h, w) order), exactly the mask of na_qk. Masked scores are
+ * -inf before the softmax; a query that keeps no key gets a zero output, lse
+ * = -inf and contributes nothing to the backward. Otherwise exactly na_fwd
+ * and na_bwd (same buffers, rules and errors; mask must be non-null). These
+ * run on the general tile kernels (one workgroup walks every patch of its
+ * tile's windows and tests each pair against the mask), not on the faster
+ * register-resident or 16-bit MFMA kernels. */
+na_status na_fwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
+                        void *out, float *lse, const uint8_t *mask, void *hip_stream);
+na_status na_bwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dk,
+                        void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
+                        int32_t kv_splits, const uint8_t *mask, void *hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char *na_status_string(na_status s);
 

@@ -249,6 +249,24 @@ def test_workspace_bytes_per_variant_and_copies(lib):
     assert lib.na_bwd(*args) == na.NA_ERR_INVALID_ARG
 
 
+def test_masked_entry_points_reject_a_null_mask(lib):
+    """The window mask of the masked entry points is a byte array: a null
+    pointer is refused before any launch, after the problem itself."""
+    p = _p()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.na_fwd_masked(ctypes.byref(p), *[fake] * 5, None, None) == na.NA_ERR_INVALID_ARG
+    ws = na.bwd_workspace_bytes(p, na.NA_BWD_GATHER)
+    assert lib.na_bwd_masked(ctypes.byref(p), *[fake] * 9, fake, ws, 0, 0, None,
+                             None) == na.NA_ERR_INVALID_ARG
+    bad = _p(kernel=(3, 19))
+    assert lib.na_fwd_masked(ctypes.byref(bad), *[fake] * 5, fake, None) == na.NA_ERR_INVALID_ARG
+    # misaligned tensors and a short workspace are refused as for na_fwd / na_bwd
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.na_fwd_masked(ctypes.byref(p), mis, *[fake] * 4, fake, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_bwd_masked(ctypes.byref(p), *[fake] * 9, fake, 0, 0, 0, fake,
+                             None) == na.NA_ERR_WORKSPACE
+
+
 def test_framed_entry_points_reject_bad_frame_pointers(lib):
     """The per-coordinate window sizes of the framed entry points are an int32
     device array: a null or misaligned pointer is refused before any launch."""

@@ -1,0 +1,155 @@
+"""GPU parity of the fused entry points with arbitrary window masks
+(na_fwd_masked / na_bwd_masked): per query token, any subset of its window's
+keys. The reference is the oracle's masked unfused path (scores of dropped
+keys set to -inf before the window softmax) with the same mask, on the same
+seeded inputs; lse is the log-sum-exp of the oracle's masked scores.
+
+Bar as for the unmasked parity tests (per tensor, max abs error over max abs
+reference value): 1e-4 fp32, 2e-2 bf16, 2e-3 fp16. A query that keeps no key
+must give a zero output and lse = -inf.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fwd_bwd_amd import na
+from fwd_bwd_amd.inputs import make_random
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-3}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    na.load()
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    fin = np.isfinite(ref)
+    scale = np.max(np.abs(ref[fin])) if fin.any() else 1.0
+    return float(np.max(np.abs(got[fin] - ref[fin])) / scale) if fin.any() else 0.0
+
+
+# (shape [B, (T,) H, W, heads, D], kernel, dilation, dtype)
+CASES = [
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.float32),
+    ((2, 19, 23, 2, 16), (5, 7), (2, 1), torch.float32),
+    ((1, 5, 11, 13, 2, 32), (3, 5, 5), 1, torch.float32),
+    ((1, 6, 20, 18, 2, 32), (5, 3, 3), 1, torch.bfloat16),
+    ((1, 26, 27, 2, 64), (7, 5), 1, torch.float16),
+    ((1, 6, 9, 10, 1, 64), (3, 3, 3), (2, 1, 2), torch.float32),
+]
+
+
+def _id(c):
+    shape, k, d, dt = c
+    return f"{'x'.join(map(str, shape))}-k{'x'.join(map(str, k))}-d{d}-{str(dt)[6:]}"
+
+
+def random_mask(shape, kernel, seed, density=0.7):
+    """A mask [(T,) H, W, K]: each window key kept with the given density,
+    the middle token of the grid dropping every key."""
+    grid = tuple(shape[1:-2])
+    K = int(np.prod(kernel))
+    rng = np.random.default_rng(seed)
+    m = (rng.random(grid + (K,)) < density).astype(np.uint8)
+    m[tuple(g // 2 for g in grid)] = 0
+    return m
+
+
+def reference(q, k, v, dout, kernel, dil, scale, mask):
+    hm = lambda t: np.moveaxis(np64(t), -2, 1)  # noqa: E731  token-major -> head-major
+    tm = lambda x: np.moveaxis(x, 1, -2)        # noqa: E731
+    Q, K, V, DO = (hm(t) for t in (q, k, v, dout))
+    P, out = oracle.unfused_fwd(Q, K, V, kernel, dil, scale, mask=mask)
+    dq, dk, dv = oracle.unfused_bwd(Q, K, V, P, DO, kernel, dil, scale)
+    s = oracle.mask_scores(oracle.na_qk(Q, K, kernel, dil, scale), mask)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = np.max(s, axis=-1, keepdims=True)
+        lse = np.squeeze(m, -1) + np.log(np.sum(np.exp(s - np.where(np.isneginf(m), 0, m)), -1))
+    lse = np.where(np.all(np.isneginf(s), -1), -np.inf, lse)
+    return {"out": tm(out), "lse": np.moveaxis(lse, 1, -1), "dq": tm(dq), "dk": tm(dk),
+            "dv": tm(dv)}
+
+
+def run_masked(q, k, v, dout, mask, kernel, dil, scale, variant, splits):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, dout))
+    md = torch.from_numpy(mask).to(dev)
+    out, lse = na.na_fwd_masked(qd, kd, vd, md, kernel, dil, scale)
+    dq, dk, dv = na.na_bwd_masked(qd, kd, vd, out, dd, lse, md, kernel, dil, scale,
+                                  variant=variant, kv_splits=splits)
+    torch.cuda.synchronize()
+    return {"out": np64(out), "lse": np64(lse), "dq": np64(dq), "dk": np64(dk), "dv": np64(dv)}
+
+
+@pytest.mark.parametrize("variant", [("gather", 0), ("kvparallel", 0), ("kvparallel", 2)],
+                         ids=["gather", "kvparallel", "kvdet"])
+@pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
+def test_masked_matches_oracle(case, variant):
+    shape, kernel, dil, dtype = case
+    seed = zlib.crc32(_id(case).encode()) % 991
+    say("masked", _id(case), variant)
+    q, k, v, dout = make_random(shape, dtype, seed=seed)
+    mask = random_mask(shape, kernel, seed)
+    scale = shape[-1] ** -0.5
+    got = run_masked(q, k, v, dout, mask, kernel, dil, scale, *variant)
+    ref = reference(q, k, v, dout, kernel, dil, scale, mask)
+    errs = {n: rel_err(got[n], ref[n]) for n in ref}
+    say("  ", {n: f"{e:.2e}" for n, e in errs.items()})
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
+    # a query that keeps no key: zero output, lse -inf; everything else finite
+    dead = np.all(mask == 0, axis=-1)
+    assert np.array_equal(np.isneginf(got["lse"]),
+                          np.broadcast_to(dead[None, ..., None], got["lse"].shape))
+    assert np.all(got["out"][:, dead] == 0)
+    for n in ("dq", "dk", "dv"):
+        assert np.all(np.isfinite(got[n])), n
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3]], ids=[_id(CASES[0]), _id(CASES[3])])
+def test_all_ones_mask_equals_unmasked(case):
+    """Keeping every key gives the unmasked function (the masked entry points
+    run other kernels, so within the parity bar rather than bitwise)."""
+    shape, kernel, dil, dtype = case
+    q, k, v, dout = (t.cuda() for t in make_random(shape, dtype, seed=29))
+    ones = torch.ones(tuple(shape[1:-2]) + (int(np.prod(kernel)),), dtype=torch.uint8,
+                      device="cuda")
+    o1, l1 = na.na_fwd(q, k, v, kernel, dil)
+    g1 = na.na_bwd(q, k, v, o1, dout, l1, kernel, dil)
+    o2, l2 = na.na_fwd_masked(q, k, v, ones, kernel, dil)
+    g2 = na.na_bwd_masked(q, k, v, o2, dout, l2, ones, kernel, dil)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("out", "lse", "dq", "dk", "dv"), (o1, l1) + tuple(g1),
+                          (o2, l2) + tuple(g2)):
+        assert rel_err(np64(y), np64(x)) <= TOL[dtype], name
+
+
+def test_masked_gather_is_deterministic():
+    shape, kernel, dil, dtype = CASES[2]
+    q, k, v, dout = (t.cuda() for t in make_random(shape, dtype, seed=31))
+    mask = torch.from_numpy(random_mask(shape, kernel, 31)).cuda()
+    o1, l1 = na.na_fwd_masked(q, k, v, mask, kernel, dil)
+    o2, l2 = na.na_fwd_masked(q, k, v, mask, kernel, dil)
+    g1 = na.na_bwd_masked(q, k, v, o1, dout, l1, mask, kernel, dil)
+    g2 = na.na_bwd_masked(q, k, v, o1, dout, l1, mask, kernel, dil)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
