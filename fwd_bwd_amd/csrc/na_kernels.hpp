@@ -353,6 +353,10 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
             const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, get3(us, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;  // uniform along T
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
+            // items every lane of the wave drops: no work (a masked tile's speedup)
+            if (a.mask && !__any(mk != 0)) continue;
             // S_b[i][c] = <k_i, q_c>: this lane supplies key c of the patch
             f4 s;
             {
@@ -366,8 +370,6 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) fwd_kernel(FwdAr
                 }
                 s = s0 + s1;
             }
-            int mk = entry_mask(vm, it) & cm;
-            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
             float sv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[e] = (mk >> e) & 1 ? s[e] : -INFINITY;
@@ -521,6 +523,10 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
             const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, get3(us, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
+            // items every lane of the wave drops: no work (a masked tile's speedup)
+            if (a.mask && !__any(mk != 0)) continue;
             const int ao = entry_addr(own, it, cv.lim);
             f4 s, dp;
             {
@@ -545,8 +551,6 @@ __global__ void __launch_bounds__(kThreads, kSplitOccupancy<D>) dq_kernel(BwdArg
                 }
                 dp = d0 + d1;
             }
-            int mk = entry_mask(vm, it) & cm;
-            if (a.mask) mk = mask_entries<true>(mk, a.mask, a.mask_k, a.g, w, lp.p, us, it);
             float ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -728,6 +732,10 @@ __global__ void __launch_bounds__(kThreads, MODE != 0 ? 1 : kSplitOccupancy<D>) 
             const Item it = make_item<PB>(i, cnt, C);
             const int cm = chunk_mask(cv, C, get3(lo, cv.A), it);
             if (cv.chunked && cv.A == 0 && cm == 0) continue;
+            int mk = entry_mask(vm, it) & cm;
+            if (a.mask) mk = mask_entries<false>(mk, a.mask, a.mask_k, a.g, w, lp.p, lo, it);
+            // items every lane of the wave drops: no work (a masked tile's speedup)
+            if (a.mask && !__any(mk != 0)) continue;
             // S_b[i][c] = <q_i, k_c>: this lane supplies query c of the patch
             const int ao = entry_addr(own, it, cv.lim);
             f4 s, dp;
@@ -753,8 +761,6 @@ __global__ void __launch_bounds__(kThreads, MODE != 0 ? 1 : kSplitOccupancy<D>) 
                 }
                 dp = d0 + d1;
             }
-            int mk = entry_mask(vm, it) & cm;
-            if (a.mask) mk = mask_entries<false>(mk, a.mask, a.mask_k, a.g, w, lp.p, lo, it);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
