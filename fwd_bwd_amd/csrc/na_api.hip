@@ -8,7 +8,6 @@
 #include <cstdint>
 #include <initializer_list>
 #include <type_traits>
-#include <map>
 #include <mutex>
 
 #include "na.h"
@@ -1125,15 +1124,18 @@ namespace {
 
 static __device__ __align__(256) float scratch[kNoallocRows];
 
-// Device address of `scratch` on the current device (nullptr on a HIP error).
+// Device address of `scratch` on the current device (nullptr on a HIP error
+// or a device index past the table), kept in a fixed table: the lookup itself
+// allocates nothing, host or device.
+constexpr int kNoallocDevices = 64;
+
 float *noalloc_scratch() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocDevices) return nullptr;
     static std::mutex mu;
-    static std::map<int, float *> ptrs;
+    static float *ptrs[kNoallocDevices] = {};
     std::lock_guard<std::mutex> lock(mu);
-    const auto it = ptrs.find(dev);
-    if (it != ptrs.end()) return it->second;
+    if (ptrs[dev]) return ptrs[dev];
     float *ptr = nullptr;
     if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
         return nullptr;
