@@ -281,3 +281,19 @@ def test_framed_entry_points_reject_bad_frame_pointers(lib):
     # the problem is validated first
     bad = _p(kernel=(3, 19))
     assert lib.na_fwd_framed(ctypes.byref(bad), *[fake] * 5, fake, None) == na.NA_ERR_INVALID_ARG
+
+
+def test_window_mask_checks_of_the_binding():
+    """The binding refuses a window mask of the wrong shape, dtype or layout
+    (the C ABI cannot see its size) before any call."""
+    import torch
+    q = torch.zeros((1, 4, 6, 7, 2, 16))
+    good = torch.ones((4, 6, 7, 3 * 5 * 5), dtype=torch.uint8)
+    assert na._check_window_mask(good, q, (3, 5, 5)) == good.data_ptr()
+    for bad in (torch.ones((4, 6, 7, 74), dtype=torch.uint8),       # K of another window
+                torch.ones((4, 6, 7, 75), dtype=torch.int32),       # not bytes
+                torch.ones((4, 7, 6, 75), dtype=torch.uint8),       # grid axes swapped
+                torch.ones((75, 4, 6, 7), dtype=torch.uint8).permute(1, 2, 3, 0),  # strided
+                None):
+        with pytest.raises(ValueError):
+            na._check_window_mask(bad, q, (3, 5, 5))
