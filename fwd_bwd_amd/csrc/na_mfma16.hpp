@@ -52,11 +52,15 @@
 // lies in the query's window (equivalently the query in the key's inverse
 // window), which also rejects every point a slab holds past the grid (those
 // repeat the last grid point, so they are finite). A wave with an odd number
-// of blocks pairs its last block with itself and masks the copy, so every LDS
-// byte a walk reads was staged for that step.
+// of blocks takes its last block alone: the second half of that reduction
+// gets zero weights and repeats the first block's operand (no scores or
+// exponentials for it), so every LDS byte a walk reads was staged for that
+// step.
 #pragma once
 
 #include "na_common.hpp"
+
+#include <type_traits>
 
 namespace na {
 namespace m16 {
@@ -407,12 +411,15 @@ __device__ __forceinline__ uint2 lds_tr(const char *p) {
 #endif
 }
 
-// A operand of a weighted sum over the blocks at blk and blk + second (second
-// = 0 repeats the first block when a wave has an odd number of blocks; its
-// weights are zero then): channel 16 d + n of the lane group's column, rows
-// 0..3 of each block.
+// A operand of a weighted sum over the blocks at blk and blk + second:
+// channel 16 d + n of the lane group's column, rows 0..3 of each block. TWO
+// false (a wave's odd last block, whose second half has zero weights) repeats
+// the first block instead of reading a second.
+template <bool TWO = true>
 __device__ __forceinline__ uint4 tr_pair(const char *blk, int second, int tr) {
-    const uint2 x = lds_tr(blk + tr), y = lds_tr(blk + second + tr);
+    const uint2 x = lds_tr(blk + tr);
+    if constexpr (!TWO) return make_uint4(x.x, x.y, x.x, x.y);
+    const uint2 y = lds_tr(blk + second + tr);
     return make_uint4(x.x, x.y, y.x, y.y);
 }
 
@@ -570,29 +577,31 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
         bool hr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - hlo) < (unsigned)hlen;
-        for (int b = 0; b < wk.nbw; b += 2) {
-            const int col0 = wk.aw + 4 * b;
-            const bool two = b + 1 < wk.nbw;
-            // a wave's odd last block pairs with itself (its weights are masked)
-            const int second = two ? BLK : 0;
+        // a pair of blocks, or (TWO false) a wave's odd last block alone: its
+        // second half of the reduction then has zero weights, so its scores
+        // and exponentials are skipped and its V operand repeats the first
+        // block (finite values times zero weights)
+        auto step = [&](int col0, int second, bool two, auto two_c) {
+            constexpr bool TWO = decltype(two_c)::value;
             const char *kb = Kc + col0 * NC * 16;
-            f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
-            f4 s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
+            f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero), s1 = zero;
+            if constexpr (TWO) s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
-                s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
+                if constexpr (TWO) s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
             }
             const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
-            const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
+            const bool w1 = TWO && two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
             float x[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 x[r] = (w0 && hr[r]) ? s0[r] : -INFINITY;
                 x[4 + r] = (w1 && hr[r]) ? s1[r] : -INFINITY;
             }
-            const float mx = xmax4(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if constexpr (TWO) mx = fmaxf(mx, fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            mx = xmax4(mx);
             if (__any(mx > thr)) {
                 const float mn = mx > thr ? mx * c : m;
                 const float alpha = fast_exp2(m - mn);
@@ -605,14 +614,21 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
             uint4 pb;
             pb.x = Mf<T>::pack(fast_exp2(fmaf(x[0], c, -m)), fast_exp2(fmaf(x[1], c, -m)));
             pb.y = Mf<T>::pack(fast_exp2(fmaf(x[2], c, -m)), fast_exp2(fmaf(x[3], c, -m)));
-            pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
-            pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
+            if constexpr (TWO) {
+                pb.z = Mf<T>::pack(fast_exp2(fmaf(x[4], c, -m)), fast_exp2(fmaf(x[5], c, -m)));
+                pb.w = Mf<T>::pack(fast_exp2(fmaf(x[6], c, -m)), fast_exp2(fmaf(x[7], c, -m)));
+            } else {
+                pb.z = pb.w = 0u;
+            }
             const char *vb = Vc + col0 * NC * 16;
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-                acc[d] = Mf<T>::mma(tr_pair(vb, second, la.tr[d]), pb, acc[d]);
+                acc[d] = Mf<T>::mma(tr_pair<TWO>(vb, second, la.tr[d]), pb, acc[d]);
             lsum = Mf<T>::mma(ones, pb, lsum);
-        }
+        };
+        int b = 0;
+        for (; b + 1 < wk.nbw; b += 2) step(wk.aw + 4 * b, BLK, true, std::true_type{});
+        if (b < wk.nbw) step(wk.aw + 4 * b, 0, false, std::false_type{});
     };
     slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
 
@@ -633,7 +649,7 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
 // ============================================================================
 // Backward, query side: delta = <dout, out> and dq.
 template <typename T, int D, int W>
-__global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
+__global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) dq_kernel(Args<T> a) {
     using S = Slabs<D, W>;
     __shared__ __align__(16) char buf0[S::kBuf];
     __shared__ __align__(16) char buf1[S::kBuf];
@@ -645,6 +661,9 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
     constexpr int slab = S::kSlab;  // per buffer: the V slab, then the K slab
+    // the odd last block alone (below) where its extra code still fits the
+    // register budget of the launch bound
+    constexpr bool kSplitOdd = true;
 
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
     const Walk wk = make_walk<false>(w, wave);
@@ -710,42 +729,63 @@ __global__ void __launch_bounds__(kTG, 2) dq_kernel(Args<T> a) {
         bool hr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) hr[r] = (unsigned)(r0 + r - hlo) < (unsigned)hlen;
-        for (int b = 0; b < wk.nbw; b += 2) {
-            const int col0 = wk.aw + 4 * b;
-            const bool two = b + 1 < wk.nbw;
-            // a wave's odd last block pairs with itself (its weights are masked)
-            const int second = two ? BLK : 0;
+        // a pair of blocks, or (TWO false) a wave's odd last block alone (its
+        // second half of the reduction gets zero score gradients)
+        auto step = [&](int col0, int second, bool two, auto two_c) {
+            constexpr bool TWO = decltype(two_c)::value;
             const char *kb = Kc + col0 * NC * 16, *vb = Vc + col0 * NC * 16;
             // dP - delta: the products start from -delta
             f4 s0 = Mf<T>::mma(km_at(kb, la.km[0]), qv[0], zero);
             f4 p0 = Mf<T>::mma(km_at(vb, la.km[0]), dv[0], ndelta);
-            f4 s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
-            f4 p1 = Mf<T>::mma(km_at(vb + second, la.km[0]), dv[0], ndelta);
+            f4 s1 = zero, p1 = zero;
+            if constexpr (TWO) {
+                s1 = Mf<T>::mma(km_at(kb + second, la.km[0]), qv[0], zero);
+                p1 = Mf<T>::mma(km_at(vb + second, la.km[0]), dv[0], ndelta);
+            }
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(kb, la.km[h]), qv[h], s0);
                 p0 = Mf<T>::mma(km_at(vb, la.km[h]), dv[h], p0);
-                s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
-                p1 = Mf<T>::mma(km_at(vb + second, la.km[h]), dv[h], p1);
+                if constexpr (TWO) {
+                    s1 = Mf<T>::mma(km_at(kb + second, la.km[h]), qv[h], s1);
+                    p1 = Mf<T>::mma(km_at(vb + second, la.km[h]), dv[h], p1);
+                }
             }
             const bool w0 = (unsigned)(col0 + wrel) < (unsigned)w.k[2];
-            const bool w1 = two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
+            const bool w1 = TWO && two && (unsigned)(col0 + 4 + wrel) < (unsigned)w.k[2];
             float ds[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float e0 = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, nlse2) : -INFINITY);
-                const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
                 ds[r] = e0 * p0[r];
-                ds[4 + r] = e1 * p1[r];
+                if constexpr (TWO) {
+                    const float e1 = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, nlse2) : -INFINITY);
+                    ds[4 + r] = e1 * p1[r];
+                }
             }
             uint4 db;
             db.x = Mf<T>::pack(ds[0], ds[1]);
             db.y = Mf<T>::pack(ds[2], ds[3]);
-            db.z = Mf<T>::pack(ds[4], ds[5]);
-            db.w = Mf<T>::pack(ds[6], ds[7]);
+            if constexpr (TWO) {
+                db.z = Mf<T>::pack(ds[4], ds[5]);
+                db.w = Mf<T>::pack(ds[6], ds[7]);
+            } else {
+                db.z = db.w = 0u;
+            }
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-                acc[d] = Mf<T>::mma(tr_pair(kb, second, la.tr[d]), db, acc[d]);
+                acc[d] = Mf<T>::mma(tr_pair<TWO>(kb, second, la.tr[d]), db, acc[d]);
+        };
+        if constexpr (kSplitOdd) {
+            int b = 0;
+            for (; b + 1 < wk.nbw; b += 2) step(wk.aw + 4 * b, BLK, true, std::true_type{});
+            if (b < wk.nbw) step(wk.aw + 4 * b, 0, false, std::false_type{});
+        } else {
+            // the odd last block pairs with itself; the copy's weights are masked
+            for (int b = 0; b < wk.nbw; b += 2) {
+                const bool two = b + 1 < wk.nbw;
+                step(wk.aw + 4 * b, two ? BLK : 0, two, std::true_type{});
+            }
         }
     };
     slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
@@ -781,6 +821,9 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     const int lane = threadIdx.x & 63, lg = lane >> 4, n = lane & 15;
     const int nh = w.n[1], nw = w.n[2];
     constexpr int slab = S::kSlab;  // per buffer: the Q slab, then the dout slab
+    // the odd last block alone (below) where its extra code still fits the
+    // register budget of the launch bound
+    constexpr bool kSplitOdd = D == 32;
     // (logsumexp * log2(e), delta) of the slab's points, one array per buffer
     __shared__ float2 rows0[4 * W], rows1[4 * W];
 
@@ -848,52 +891,79 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
                 hr[r] = hr[r] & in_frame(P.h, r0 + r, nh,
                                          frame_size(a.frame, w, 1, imin(r0 + r, nh - 1)));
         }
-        for (int b = 0; b < wk.nbw; b += 2) {
-            const int col0 = wk.aw + 4 * b;
-            const bool two = b + 1 < wk.nbw;
-            // a wave's odd last block pairs with itself (its weights are masked)
-            const int second = two ? BLK : 0;
+        // a pair of query blocks, or (TWO false) a wave's odd last block alone
+        // (its second half of the reductions gets zero weights and zero score
+        // gradients)
+        auto step = [&](int col0, int second, bool two, auto two_c) {
+            constexpr bool TWO = decltype(two_c)::value;
             const char *qb = Qc + col0 * NC * 16, *ob = Oc + col0 * NC * 16;
             f4 s0 = Mf<T>::mma(km_at(qb, la.km[0]), kv[0], zero);
             f4 p0 = Mf<T>::mma(km_at(ob, la.km[0]), vv[0], zero);
-            f4 s1 = Mf<T>::mma(km_at(qb + second, la.km[0]), kv[0], zero);
-            f4 p1 = Mf<T>::mma(km_at(ob + second, la.km[0]), vv[0], zero);
+            f4 s1 = zero, p1 = zero;
+            if constexpr (TWO) {
+                s1 = Mf<T>::mma(km_at(qb + second, la.km[0]), kv[0], zero);
+                p1 = Mf<T>::mma(km_at(ob + second, la.km[0]), vv[0], zero);
+            }
 #pragma unroll
             for (int h = 1; h < NH; ++h) {
                 s0 = Mf<T>::mma(km_at(qb, la.km[h]), kv[h], s0);
                 p0 = Mf<T>::mma(km_at(ob, la.km[h]), vv[h], p0);
-                s1 = Mf<T>::mma(km_at(qb + second, la.km[h]), kv[h], s1);
-                p1 = Mf<T>::mma(km_at(ob + second, la.km[h]), vv[h], p1);
+                if constexpr (TWO) {
+                    s1 = Mf<T>::mma(km_at(qb + second, la.km[h]), kv[h], s1);
+                    p1 = Mf<T>::mma(km_at(ob + second, la.km[h]), vv[h], p1);
+                }
             }
             // (-lse * log2 e, -delta) of the four rows of this lane group's query column
             const float4 *rp0 = reinterpret_cast<const float4 *>(Rc + 4 * (col0 + lg));
-            const float4 *rp1 = reinterpret_cast<const float4 *>(Rc + 4 * (two ? col0 + 4 + lg : col0 + lg));
-            const float4 l0a = rp0[0], l0b = rp0[1], l1a = rp1[0], l1b = rp1[1];
+            const float4 l0a = rp0[0], l0b = rp0[1];
+            float4 l1a = l0a, l1b = l0b;
+            if constexpr (TWO) {
+                const float4 *rp1 =
+                    reinterpret_cast<const float4 *>(Rc + 4 * (two ? col0 + 4 + lg : col0 + lg));
+                l1a = rp1[0];
+                l1b = rp1[1];
+            }
             const float ls0[4] = {l0a.x, l0a.z, l0b.x, l0b.z}, nd0[4] = {l0a.y, l0a.w, l0b.y, l0b.w};
             const float ls1[4] = {l1a.x, l1a.z, l1b.x, l1b.z}, nd1[4] = {l1a.y, l1a.w, l1b.y, l1b.w};
             const bool w0 = (unsigned)(col0 + irel) <= (unsigned)iwn;
-            const bool w1 = two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
+            const bool w1 = TWO && two && (unsigned)(col0 + 4 + irel) <= (unsigned)iwn;
             float pr[8], ds[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 pr[r] = fast_exp2((w0 && hr[r]) ? fmaf(s0[r], c, ls0[r]) : -INFINITY);
-                pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, ls1[r]) : -INFINITY);
+                if constexpr (TWO)
+                    pr[4 + r] = fast_exp2((w1 && hr[r]) ? fmaf(s1[r], c, ls1[r]) : -INFINITY);
                 ds[r] = pr[r] * (p0[r] + nd0[r]);
-                ds[4 + r] = pr[4 + r] * (p1[r] + nd1[r]);
+                if constexpr (TWO) ds[4 + r] = pr[4 + r] * (p1[r] + nd1[r]);
             }
             uint4 pb, db;
             pb.x = Mf<T>::pack(pr[0], pr[1]);
             pb.y = Mf<T>::pack(pr[2], pr[3]);
-            pb.z = Mf<T>::pack(pr[4], pr[5]);
-            pb.w = Mf<T>::pack(pr[6], pr[7]);
             db.x = Mf<T>::pack(ds[0], ds[1]);
             db.y = Mf<T>::pack(ds[2], ds[3]);
-            db.z = Mf<T>::pack(ds[4], ds[5]);
-            db.w = Mf<T>::pack(ds[6], ds[7]);
+            if constexpr (TWO) {
+                pb.z = Mf<T>::pack(pr[4], pr[5]);
+                pb.w = Mf<T>::pack(pr[6], pr[7]);
+                db.z = Mf<T>::pack(ds[4], ds[5]);
+                db.w = Mf<T>::pack(ds[6], ds[7]);
+            } else {
+                pb.z = pb.w = db.z = db.w = 0u;
+            }
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-                dva[d] = Mf<T>::mma(tr_pair(ob, second, la.tr[d]), pb, dva[d]);
-                dka[d] = Mf<T>::mma(tr_pair(qb, second, la.tr[d]), db, dka[d]);
+                dva[d] = Mf<T>::mma(tr_pair<TWO>(ob, second, la.tr[d]), pb, dva[d]);
+                dka[d] = Mf<T>::mma(tr_pair<TWO>(qb, second, la.tr[d]), db, dka[d]);
+            }
+        };
+        if constexpr (kSplitOdd) {
+            int b = 0;
+            for (; b + 1 < wk.nbw; b += 2) step(wk.aw + 4 * b, BLK, true, std::true_type{});
+            if (b < wk.nbw) step(wk.aw + 4 * b, 0, false, std::false_type{});
+        } else {
+            // the odd last block pairs with itself; the copy's weights are masked
+            for (int b = 0; b < wk.nbw; b += 2) {
+                const bool two = b + 1 < wk.nbw;
+                step(wk.aw + 4 * b, two ? BLK : 0, two, std::true_type{});
             }
         }
     };
