@@ -506,16 +506,16 @@ struct M16Plan {
 
 
 // Columns a slab row must hold: the end of the last block any wave of any
-// 16-column tile walks, relative to its tile's box start (the same formulas
-// the kernels evaluate), rounded to groups of four.
-int m16_box_w(const Prob &q, bool inverse, int *max_blocks = nullptr) {
-    int bw = 4, mb = 1;
-    const int k = q.ker[2];
+// tile (4 << pcsh columns wide) walks, relative to its tile's box start (the
+// same formulas the kernels evaluate), rounded to groups of four.
+int m16_box_w(const Prob &q, bool inverse, int pcsh) {
+    int bw = 4;
+    const int k = q.ker[2], tw = 4 << pcsh;
     for (int r = 0; r < q.dil[2] && r < q.ext[2]; ++r) {
         const int n = na::class_size(q.ext[2], q.dil[2], r);
-        for (int w0 = 0; w0 < n; w0 += na::m16::kTW) {
+        for (int w0 = 0; w0 < n; w0 += tw) {
             const int U2 = inverse ? na::inverse_first(w0, n, k) : na::window_start(w0, n, k);
-            for (int j = 0; j < 4 && w0 + 4 * j < n; ++j) {
+            for (int j = 0; j < (1 << pcsh) && w0 + 4 * j < n; ++j) {
                 const int p0 = w0 + 4 * j, p1 = std::min(p0 + 3, n - 1);
                 const int s0 = inverse ? na::inverse_first(p0, n, k) : na::window_start(p0, n, k);
                 const int e1 = inverse ? na::inverse_last(p1, n, k) + 1
@@ -523,19 +523,69 @@ int m16_box_w(const Prob &q, bool inverse, int *max_blocks = nullptr) {
                 const int aw = (s0 - U2) & ~3;
                 const int nbw = (e1 - U2 - aw + 3) >> 2;
                 bw = std::max(bw, aw + 4 * nbw);
-                mb = std::max(mb, nbw);
             }
         }
     }
-    if (max_blocks) *max_blocks = mb;
     return bw;
+}
+
+// Sum over the tiles of one axis (tile extent te over the largest residue
+// class) of the positions the tile's window union spans: planes (T) or
+// 4-row slabs (H).
+int64_t m16_union_sum(int n, int k, int te, bool inverse, bool slabs) {
+    int64_t sum = 0;
+    for (int o = 0; o < n; o += te) {
+        const int l = std::min(o + te - 1, n - 1);
+        const int a = inverse ? na::inverse_first(o, n, k) : na::window_start(o, n, k);
+        const int b = inverse ? na::inverse_last(l, n, k) + 1 : na::window_start(l, n, k) + k;
+        sum += slabs ? (b - a + 3) / 4 : b - a;
+    }
+    return sum;
+}
+
+// Tile shape of a 16-bit launch. The workgroup stages, per slab step, four rows
+// of box_w points of one plane, and walks them; over the grid that is
+// (T unions) x (H slabs) x (W tiles) steps. The shape taken is the one with the
+// fewest staged points, each step counted with a fixed cost of kStepPoints
+// points for its barrier and set-up. Several planes per tile only pay where a
+// key plane serves several query planes (a window longer than one plane).
+constexpr int kStepPoints = 16;
+struct M16Shape {
+    int tp, prsh, pcsh, box_w;
+};
+M16Shape m16_shape(const Prob &q, bool inverse) {
+    static const int cand[][3] = {{1, 1, 2}, {2, 1, 1}, {2, 0, 2}, {4, 0, 1}};
+    const int n0 = na::class_size(q.ext[0], q.dil[0], 0);
+    const int n1 = na::class_size(q.ext[1], q.dil[1], 0);
+    const int n2 = na::class_size(q.ext[2], q.dil[2], 0);
+    M16Shape best{0, 0, 0, 0};
+    double best_cost = 0.0;
+    for (const auto &c : cand) {
+        if (c[0] > 1 && (q.ker[0] == 1 || n0 == 1)) continue;
+        const int bw = m16_box_w(q, inverse, c[2]);
+        if (bw > 48) continue;
+        const double steps = (double)m16_union_sum(n0, q.ker[0], c[0], inverse, false) *
+                             (double)m16_union_sum(n1, q.ker[1], 4 << c[1], inverse, true) *
+                             (double)((n2 + (4 << c[2]) - 1) / (4 << c[2]));
+        const double cost = steps * (kStepPoints + bw);
+        if (best.tp == 0 || cost < best_cost) {
+            best = M16Shape{c[0], c[1], c[2], bw};
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
     if (q.dtype != NA_BF16 && q.dtype != NA_F16) return false;
     if (q.head_dim != 32 && q.head_dim != 64) return false;
+    const M16Shape sh = m16_shape(q, kind == 2);
+    if (sh.tp == 0) return false;
     na::m16::Geom &g = pl->g;
     g = na::m16::Geom{};
+    g.tp = sh.tp;
+    g.prsh = sh.prsh;
+    g.pcsh = sh.pcsh;
     int64_t n_tiles = q.batch * q.heads;
     int nres = 1;
     for (int a = 0; a < 3; ++a) {
@@ -543,7 +593,7 @@ bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
         g.ker[a] = q.ker[a];
         g.dil[a] = q.dil[a];
         const int nmax = na::class_size(q.ext[a], q.dil[a], 0);
-        const int t = a == 0 ? 1 : a == 1 ? na::m16::kTH : na::m16::kTW;
+        const int t = a == 0 ? sh.tp : a == 1 ? 4 << sh.prsh : 4 << sh.pcsh;
         g.tiles[a] = (nmax + t - 1) / t;
         n_tiles *= g.tiles[a];
         nres *= q.dil[a];
@@ -554,7 +604,7 @@ bool m16_plan(const Prob &q, int kind, M16Plan *pl) {
     g.batch = (int)q.batch;
     g.nres = nres;
     g.n_tiles = (int)n_tiles;
-    g.box_w = m16_box_w(q, kind == 2);
+    g.box_w = sh.box_w;
     // the kernels are compiled for slab rows of up to 24, 32 or 48 points
     // (static LDS: two buffers of two slabs each)
     g.wmax = g.box_w <= 24 ? 24 : g.box_w <= 32 ? 32 : 48;

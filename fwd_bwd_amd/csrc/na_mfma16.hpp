@@ -12,11 +12,13 @@
 //
 // Work decomposition. A wave owns a patch of 16 points (1 x 4 x 4 along T, H,
 // W in class coordinates of one residue class): queries in the forward and dq
-// kernels, keys in the dk/dv kernel. A workgroup of eight waves owns a 1 x 8 x
-// 16 tile (two rows of four patches), so all its waves need rows of the same
-// planes of the other side's box: the box is staged one 4-row slab of one
-// plane at a time, and every wave walks the 4 x 4 blocks of its own patch's
-// window union (or inverse union) inside the slab, skipping slabs outside it.
+// kernels, keys in the dk/dv kernel. A workgroup of eight waves owns a tile of
+// patches (one plane of 1 x 8 x 16 on 2D grids; on 3D grids possibly several
+// planes, see Geom), so its waves need rows of the same planes of the other
+// side's box: the box is staged one 4-row slab of one plane at a time, and
+// every wave walks the 4 x 4 blocks of its own patch's window union (or
+// inverse union) inside the slab, skipping slabs outside it and planes outside
+// its own plane's window.
 // One MFMA contracts 16 points of one side with a 4 x 4 block of the other
 // over 32 channels; pairs of blocks (32 points) form the 32-deep reductions of
 // the weighted sums.
@@ -110,19 +112,23 @@ struct Mf<f16> {
     static constexpr uint32_t kOne2 = 0x3c003c00u;
 };
 
-// A workgroup of kWG waves owns a 1 x kTH x kTW tile: two rows of four 4 x 4
-// patches (wave v: patch row v / 4, patch column v % 4).
+// A workgroup of kWG waves owns a tp x (4 << prsh) x (4 << pcsh) tile of 4 x 4
+// patches, tp << (prsh + pcsh) = kWG: wave v takes plane v >> (prsh + pcsh),
+// patch row (v >> pcsh) mod (1 << prsh), patch column v mod (1 << pcsh). One
+// plane of two rows of four patches (1 x 8 x 16) suits 2D grids; on 3D grids
+// several planes per tile let every staged key plane serve each of the
+// tile's query planes whose window holds it, instead of being staged once per
+// query plane.
 constexpr int kWG = 8, kTG = 64 * kWG;
-
-constexpr int kTH = 8, kTW = 16;  // tile rows (H) and columns (W); T: one plane
 
 struct Geom {
     int ext[3], ker[3], dil[3];
     int heads, batch;
-    int tiles[3];  // per axis over the largest residue class: planes, 8-row tiles, 16-column tiles
+    int tiles[3];  // tiles per axis over the largest residue class
     int nres, n_tiles;
     int box_w;     // points per slab row (a multiple of 4)
     int wmax;      // the kernel's compiled bound on box_w (24, 32 or 48)
+    int tp, prsh, pcsh;  // tile shape: planes, log2 patch rows, log2 patch columns
     FastDiv f_heads, f_tw, f_th, f_t, f_nres;
     FastDiv f_dil[3], f_dil21;
 };
@@ -168,7 +174,7 @@ __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
     const int q1 = fdiv(q, g.f_dil[1]);
     r[1] = q - q1 * g.dil[1];
     r[0] = fdiv(res, g.f_dil21);
-    const int o[3] = {tt, th * kTH, tw * kTW};
+    const int o[3] = {tt * g.tp, th * (4 << g.prsh), tw * (4 << g.pcsh)};
     bool inside = true;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
@@ -321,16 +327,29 @@ __device__ __forceinline__ float xsum4(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// The lane's point of the wave's patch: patch origin (class) + (n / 4, n % 4).
-// Wave v's patch sits at patch row v / 4, patch column v % 4 of the tile.
+// Origin of wave v's patch in class coordinates (uniform over the wave).
+struct Patch {
+    int t, h, w;
+};
+__device__ __forceinline__ Patch patch_origin(const Geom &g, const TileCtx &w, int wave) {
+    Patch p;
+    p.t = w.o[0] + (wave >> (g.prsh + g.pcsh));
+    p.h = w.o[1] + 4 * ((wave >> g.pcsh) & ((1 << g.prsh) - 1));
+    p.w = w.o[2] + 4 * (wave & ((1 << g.pcsh) - 1));
+    return p;
+}
+
+// The lane's point of the wave's patch: patch origin + (0, n / 4, n % 4).
 struct Pt {
-    int h, w;       // clamped into the grid
+    int t, h, w;    // clamped into the grid
     bool active;    // unclamped point inside the grid
 };
-__device__ __forceinline__ Pt patch_point(const TileCtx &w, int wave, int n) {
-    const int h = w.o[1] + 4 * (wave >> 2) + (n >> 2), c = w.o[2] + 4 * (wave & 3) + (n & 3);
+__device__ __forceinline__ Pt patch_point(const Geom &g, const TileCtx &w, int wave, int n) {
+    const Patch o = patch_origin(g, w, wave);
+    const int h = o.h + (n >> 2), c = o.w + (n & 3);
     Pt p;
-    p.active = h < w.n[1] && c < w.n[2];
+    p.active = o.t < w.n[0] && h < w.n[1] && c < w.n[2];
+    p.t = __builtin_amdgcn_readfirstlane(imin(o.t, w.n[0] - 1));
     p.h = imin(h, w.n[1] - 1);
     p.w = imin(c, w.n[2] - 1);
     return p;
@@ -343,6 +362,10 @@ struct Walk {
     int Uh, U2, nslab, aw, nbw, wr0, wr1;
     bool on;  // the wave's patch has a point inside the grid
 };
+// Planes [first, last] of the tile (clamped into the grid).
+__device__ __forceinline__ int tile_last_plane(const Geom &g, const TileCtx &w) {
+    return imin(w.o[0] + g.tp - 1, w.n[0] - 1);
+}
 template <bool Inverse>
 __device__ __forceinline__ int wfirst(int x, int n, int k) {
     return Inverse ? inverse_first(x, n, k) : window_start(x, n, k);
@@ -352,18 +375,19 @@ __device__ __forceinline__ int wend(int x, int n, int k) {
     return Inverse ? inverse_last(x, n, k) + 1 : window_start(x, n, k) + k;
 }
 template <bool Inverse>
-__device__ __forceinline__ Walk make_walk(const TileCtx &w, int wave) {
+__device__ __forceinline__ Walk make_walk(const Geom &g, const TileCtx &w, int wave) {
     const int nh = w.n[1], nw = w.n[2], kh = w.k[1], kw = w.k[2];
+    const Patch po = patch_origin(g, w, wave);
     Walk k;
     k.Uh = wfirst<Inverse>(w.o[1], nh, kh);
-    const int hend = wend<Inverse>(imin(w.o[1] + kTH - 1, nh - 1), nh, kh);
+    const int hend = wend<Inverse>(imin(w.o[1] + (4 << g.prsh) - 1, nh - 1), nh, kh);
     k.nslab = (hend - k.Uh + 3) >> 2;
     k.U2 = wfirst<Inverse>(w.o[2], nw, kw);
-    k.on = w.o[2] + 4 * (wave & 3) < nw && w.o[1] + 4 * (wave >> 2) < nh;
-    const int pw0 = imin(w.o[2] + 4 * (wave & 3), nw - 1), pw1 = imin(pw0 + 3, nw - 1);
+    k.on = po.t < w.n[0] && po.w < nw && po.h < nh;
+    const int pw0 = imin(po.w, nw - 1), pw1 = imin(pw0 + 3, nw - 1);
     k.aw = __builtin_amdgcn_readfirstlane((wfirst<Inverse>(pw0, nw, kw) - k.U2) & ~3);
     k.nbw = __builtin_amdgcn_readfirstlane((wend<Inverse>(pw1, nw, kw) - k.U2 - k.aw + 3) >> 2);
-    const int ph0 = imin(w.o[1] + 4 * (wave >> 2), nh - 1), ph1 = imin(ph0 + 3, nh - 1);
+    const int ph0 = imin(po.h, nh - 1), ph1 = imin(ph0 + 3, nh - 1);
     k.wr0 = __builtin_amdgcn_readfirstlane(wfirst<Inverse>(ph0, nh, kh));
     k.wr1 = __builtin_amdgcn_readfirstlane(wend<Inverse>(ph1, nh, kh));
     return k;
@@ -514,9 +538,13 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
     const int nh = w.n[1], nw = w.n[2];
     constexpr int slab = S::kSlab;  // per buffer: the K slab, then the V slab
 
+    // key planes [t0, t1] of the tile's query planes; [wt0, wt0 + k) of this wave's
+    const int tl = tile_last_plane(g, w);
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
-    const Walk wk = make_walk<false>(w, wave);
-    const Pt P = patch_point(w, wave, n);
+    const int t1 = window_start(tl, w.n[0], w.k[0]) + w.k[0] - 1;
+    const Walk wk = make_walk<false>(g, w, wave);
+    const Pt P = patch_point(g, w, wave, n);
+    const int wt0 = __builtin_amdgcn_readfirstlane(window_start(P.t, w.n[0], w.k[0]));
     const int wh = window_start(P.h, nh, w.k[1]);
     // column of this lane group in a block relative to the lane's window start
     const int wrel = lg - (window_start(P.w, nw, w.k[2]) - wk.U2);
@@ -528,7 +556,7 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
     const float ic = 1.f / c;
     uint4 qv[NH];
     {
-        const T *qp = a.q + eoff<D>(w, w.o[0], P.h, P.w) + 8 * lg;
+        const T *qp = a.q + eoff<D>(w, P.t, P.h, P.w) + 8 * lg;
         const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
@@ -546,13 +574,14 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
     float m = -1e30f;            // running maximum, scaled (log2 units)
     float thr = (m + kLazyRescale) * ic;  // unscaled score that triggers a rescale
 
-    // frames: along T (3D grids) key planes outside the tile's frame window are
-    // skipped; along H (2D grids) slab rows outside the lane's query row's are masked
+    // frames: along T (3D grids) key planes outside a query plane's frame window
+    // are skipped (by the workgroup when no query plane of the tile keeps them);
+    // along H (2D grids) slab rows outside the lane's query row's are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
-    // (the frame size of the tile's plane is uniform: readfirstlane keeps the
-    // plane loop scalar)
-    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, w.o[0])) : 0;
-    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(w.o[0], w.n[0], imax(fk_t, 1)));
+    // (the frame size of the wave's plane is uniform: readfirstlane keeps the
+    // plane tests scalar)
+    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, P.t)) : 0;
+    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(P.t, w.n[0], imax(fk_t, 1)));
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
     // key rows [hlo, hlo + hlen) of the lane's query: its window rows, cut to
     // its frame window on 2D grids with frames
@@ -563,15 +592,28 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
         hlo = imax(wh, fs);
         hlen = imax(hi - hlo, 0);
     }
-    auto plane_ok = [&](int tk) { return !fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t; };
+    // key plane tk in the window (and the frame window) of the wave's query plane
+    auto wave_plane = [&](int tk) {
+        return (unsigned)(tk - wt0) < (unsigned)w.k[0] &&
+               (!fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t);
+    };
+    // key plane tk kept by some query plane of the tile
+    auto plane_ok = [&](int tk) {
+        if (!fr_t) return true;
+        for (int z = w.o[0]; z <= tl; ++z)
+            if ((unsigned)(tk - window_start(z, w.n[0], w.k[0])) < (unsigned)w.k[0] &&
+                in_frame(tk, z, w.n[0], frame_size(a.frame, w, 0, z)))
+                return true;
+        return false;
+    };
     const Stager<D, W, S::kPitch> st(w, wk.U2, g.box_w, wave, lane);
     auto stage = [&](int tk, int sl, char *buf, int) {
         st.stage(a.k, w, tk, wk.Uh + 4 * sl, buf);
         st.stage(a.v, w, tk, wk.Uh + 4 * sl, buf + slab);
     };
-    auto walk = [&](int, int sl, const char *buf, int) {
+    auto walk = [&](int tk, int sl, const char *buf, int) {
         const int r0 = wk.Uh + 4 * sl;
-        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        if (!wk.on || !wave_plane(tk) || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
         const char *Kc = buf, *Vc = buf + slab;
         // key rows of the slab inside the lane's query window
         bool hr[4];
@@ -630,19 +672,19 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) fwd_kernel(Ar
         for (; b + 1 < wk.nbw; b += 2) step(wk.aw + 4 * b, BLK, true, std::true_type{});
         if (b < wk.nbw) step(wk.aw + 4 * b, 0, false, std::false_type{});
     };
-    slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
+    slab_steps(t0, t1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
 
     if (!wk.on || !P.active) return;
     // a query whose window is masked away entirely: zero output, lse -inf
     const float inv = lsum[0] > 0.f ? 1.f / lsum[0] : 0.f;
-    T *op = a.o + eoff<D>(w, w.o[0], P.h, P.w) + 4 * lg;
+    T *op = a.o + eoff<D>(w, P.t, P.h, P.w) + 4 * lg;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
         const float o4[4] = {acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv};
         Io<T>::store4(op + 16 * d, o4);
     }
     if (lg == 0)
-        a.lse_out[roff(w, w.o[0], P.h, P.w)] =
+        a.lse_out[roff(w, P.t, P.h, P.w)] =
             lsum[0] > 0.f ? (m + __log2f(lsum[0])) * kLn2 : -INFINITY;
 }
 
@@ -665,13 +707,17 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) dq_kernel(Arg
     // register budget of the launch bound
     constexpr bool kSplitOdd = true;
 
+    // key planes [t0, t1] of the tile's query planes; [wt0, wt0 + k) of this wave's
+    const int tl = tile_last_plane(g, w);
     const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
-    const Walk wk = make_walk<false>(w, wave);
-    const Pt P = patch_point(w, wave, n);
+    const int t1 = window_start(tl, w.n[0], w.k[0]) + w.k[0] - 1;
+    const Walk wk = make_walk<false>(g, w, wave);
+    const Pt P = patch_point(g, w, wave, n);
+    const int wt0 = __builtin_amdgcn_readfirstlane(window_start(P.t, w.n[0], w.k[0]));
     const int wh = window_start(P.h, nh, w.k[1]);
     const int wrel = lg - (window_start(P.w, nw, w.k[2]) - wk.U2);
-    const int64_t qo = eoff<D>(w, w.o[0], P.h, P.w);
-    const int64_t ro = roff(w, w.o[0], P.h, P.w);
+    const int64_t qo = eoff<D>(w, P.t, P.h, P.w);
+    const int64_t ro = roff(w, P.t, P.h, P.w);
     uint4 qv[NH], dv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -701,11 +747,14 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) dq_kernel(Arg
 #pragma unroll
     for (int d = 0; d < ND; ++d) acc[d] = zero;
 
+    // frames: along T (3D grids) key planes outside a query plane's frame window
+    // are skipped (by the workgroup when no query plane of the tile keeps them);
+    // along H (2D grids) slab rows outside the lane's query row's are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
-    // (the frame size of the tile's plane is uniform: readfirstlane keeps the
-    // plane loop scalar)
-    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, w.o[0])) : 0;
-    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(w.o[0], w.n[0], imax(fk_t, 1)));
+    // (the frame size of the wave's plane is uniform: readfirstlane keeps the
+    // plane tests scalar)
+    const int fk_t = fr_t ? __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, P.t)) : 0;
+    const int fs_t = __builtin_amdgcn_readfirstlane(window_start(P.t, w.n[0], imax(fk_t, 1)));
     const int fk_h = fr_h ? frame_size(a.frame, w, 1, P.h) : 0;
     // key rows [hlo, hlo + hlen) of the lane's query: its window rows, cut to
     // its frame window on 2D grids with frames
@@ -716,15 +765,28 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) dq_kernel(Arg
         hlo = imax(wh, fs);
         hlen = imax(hi - hlo, 0);
     }
-    auto plane_ok = [&](int tk) { return !fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t; };
+    // key plane tk in the window (and the frame window) of the wave's query plane
+    auto wave_plane = [&](int tk) {
+        return (unsigned)(tk - wt0) < (unsigned)w.k[0] &&
+               (!fr_t || (unsigned)(tk - fs_t) < (unsigned)fk_t);
+    };
+    // key plane tk kept by some query plane of the tile
+    auto plane_ok = [&](int tk) {
+        if (!fr_t) return true;
+        for (int z = w.o[0]; z <= tl; ++z)
+            if ((unsigned)(tk - window_start(z, w.n[0], w.k[0])) < (unsigned)w.k[0] &&
+                in_frame(tk, z, w.n[0], frame_size(a.frame, w, 0, z)))
+                return true;
+        return false;
+    };
     const Stager<D, W, S::kPitch> st(w, wk.U2, g.box_w, wave, lane);
     auto stage = [&](int tk, int sl, char *buf, int) {
         st.stage(a.v, w, tk, wk.Uh + 4 * sl, buf);
         st.stage(a.k, w, tk, wk.Uh + 4 * sl, buf + slab);
     };
-    auto walk = [&](int, int sl, const char *buf, int) {
+    auto walk = [&](int tk, int sl, const char *buf, int) {
         const int r0 = wk.Uh + 4 * sl;
-        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        if (!wk.on || !wave_plane(tk) || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
         const char *Vc = buf, *Kc = buf + slab;
         bool hr[4];
 #pragma unroll
@@ -788,7 +850,7 @@ __global__ void __launch_bounds__(kTG, D == 32 && W <= 32 ? 8 : 2) dq_kernel(Arg
             }
         }
     };
-    slab_steps(t0, t0 + w.k[0] - 1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
+    slab_steps(t0, t1, wk.nslab, buf0, buf1, plane_ok, stage, walk, [](int) {});
 
     if (!wk.on || !P.active) return;
     T *dp = a.dq + qo + 4 * lg;
@@ -827,16 +889,20 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     // (logsumexp * log2(e), delta) of the slab's points, one array per buffer
     __shared__ float2 rows0[4 * W], rows1[4 * W];
 
-    // the workgroup's query planes, and this wave's walk of the inverse windows
+    // the workgroup's query planes [tq0, tq1], those of this wave's key plane
+    // [iq0, iq1], and this wave's walk of the inverse windows
+    const int tl = tile_last_plane(g, w);
     const int tq0 = inverse_first(w.o[0], w.n[0], w.k[0]);
-    const int tq1 = inverse_last(w.o[0], w.n[0], w.k[0]);
-    const Walk wk = make_walk<true>(w, wave);
-    const Pt P = patch_point(w, wave, n);  // the lane's key
+    const int tq1 = inverse_last(tl, w.n[0], w.k[0]);
+    const Walk wk = make_walk<true>(g, w, wave);
+    const Pt P = patch_point(g, w, wave, n);  // the lane's key
+    const int iq0 = __builtin_amdgcn_readfirstlane(inverse_first(P.t, w.n[0], w.k[0]));
+    const int iq1 = __builtin_amdgcn_readfirstlane(inverse_last(P.t, w.n[0], w.k[0]));
     const int ih0 = inverse_first(P.h, nh, w.k[1]), ih1 = inverse_last(P.h, nh, w.k[1]);
     // query columns of this lane group relative to the key's inverse window
     const int irel = lg - (inverse_first(P.w, nw, w.k[2]) - wk.U2);
     const int iwn = inverse_last(P.w, nw, w.k[2]) - inverse_first(P.w, nw, w.k[2]);
-    const int64_t ko = eoff<D>(w, w.o[0], P.h, P.w);
+    const int64_t ko = eoff<D>(w, P.t, P.h, P.w);
     uint4 kv[NH], vv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -855,12 +921,22 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     }
 
     // frames: along T (3D grids) query planes whose frame window misses the key
-    // plane are skipped; along H (2D grids) such query rows are masked
+    // plane are skipped (by the workgroup when it misses every key plane of the
+    // tile); along H (2D grids) such query rows are masked
     const bool fr_t = a.frame && a.frame_axis == 0, fr_h = a.frame && a.frame_axis == 1;
+    // query plane tq in the inverse window (and frame) of the wave's key plane
+    auto wave_plane = [&](int tq) {
+        return (unsigned)(tq - iq0) <= (unsigned)(iq1 - iq0) &&
+               (!fr_t || in_frame(P.t, tq, w.n[0],
+                                  __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, tq))));
+    };
+    // query plane tq whose frame window holds some key plane of the tile
     auto plane_ok = [&](int tq) {
-        return !fr_t ||
-               in_frame(w.o[0], tq, w.n[0],
-                        __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, tq)));
+        if (!fr_t) return true;
+        const int fk = __builtin_amdgcn_readfirstlane(frame_size(a.frame, w, 0, tq));
+        for (int z = w.o[0]; z <= tl; ++z)
+            if (in_frame(z, tq, w.n[0], fk)) return true;
+        return false;
     };
     float2 rv = make_float2(0.f, 0.f);  // the next slab's rows, in flight
     bool first = true;                  // the first step's rows are stored at once
@@ -876,9 +952,9 @@ __global__ void __launch_bounds__(kTG, W <= 32 ? 4 : 2) dkdv_kernel(Args<T> a) {
     // a later step's rows go to LDS after the walk before it (their array was
     // last read a step earlier)
     auto done = [&](int i) { rows_store(rv, g.box_w, i ? rows1 : rows0); };
-    auto walk = [&](int, int sl, const char *buf, int i) {
+    auto walk = [&](int tq, int sl, const char *buf, int i) {
         const int r0 = wk.Uh + 4 * sl;
-        if (!wk.on || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
+        if (!wk.on || !wave_plane(tq) || r0 + 4 <= wk.wr0 || r0 >= wk.wr1) return;
         const char *Qc = buf, *Oc = buf + slab;
         const float2 *Rc = i ? rows1 : rows0;
         // query rows of the slab inside the key's inverse window
