@@ -58,6 +58,8 @@ struct UArgs {
     int K, KP, kw;       // row length, one window plane's slice of it, window width
     FastDiv fKP;
     int rows_round;      // qk, av: rows of a wave's 8 x 8 points per LDS round (8, 4, 2, 1)
+    int rows_full;       // qk on several planes: rows per LDS round of whole K-entry rows (0: off)
+    FastDiv fK;
     int chunk_rows;      // av_inverse: box rows per attention chunk in LDS
     int oh, ow;          // av_inverse: walk offset of this pass, in patches
     int accumulate;      // av_inverse: add to out (passes after the first)
@@ -85,24 +87,28 @@ struct RowRun {
     int64_t base;     // global index of entry 0 of the row's first point
     int64_t cstride;  // global elements from one point of the row to the next
     int n;            // elements of the row inside the grid
+    int kp;           // entries per point in the run: one window plane's slice, or (full) K
+    FastDiv fkp;
     bool contiguous;
 };
 
 __device__ __forceinline__ RowRun row_run(const UArgs &a, const TileCtx &w, int t, int row,
-                                          int col0, int cols, int it) {
+                                          int col0, int cols, int it, bool full = false) {
     RowRun rr;
     const int c[3] = {t, row, col0};
-    rr.base = row_off(w, c) * a.K + it * a.KP;
+    rr.kp = full ? a.K : a.KP;
+    rr.fkp = full ? a.fK : a.fKP;
+    rr.base = row_off(w, c) * a.K + it * rr.kp;
     rr.cstride = w.lst[2] * a.K;
-    rr.n = imax(0, imin(cols, w.n[2] - col0)) * a.KP;
-    rr.contiguous = rr.cstride == a.KP;
+    rr.n = imax(0, imin(cols, w.n[2] - col0)) * rr.kp;
+    rr.contiguous = rr.cstride == rr.kp;
     return rr;
 }
 
-__device__ __forceinline__ int64_t run_index(const UArgs &a, const RowRun &rr, int e) {
+__device__ __forceinline__ int64_t run_index(const UArgs &, const RowRun &rr, int e) {
     if (rr.contiguous) return rr.base + e;
-    const int col = fdiv(e, a.fKP);
-    return rr.base + col * rr.cstride + (e - col * a.KP);
+    const int col = fdiv(e, rr.fkp);
+    return rr.base + col * rr.cstride + (e - col * rr.kp);
 }
 
 // Per-lane offsets of the elements e = lane + 64 m (m < kRunSteps) of a row
@@ -115,17 +121,20 @@ struct RunOffs {
     bool ok;  // the run fits kRunSteps steps of 64 lanes
 };
 
-__device__ __forceinline__ RunOffs run_offs(const UArgs &a, const TileCtx &w, int cols) {
+__device__ __forceinline__ RunOffs run_offs(const UArgs &a, const TileCtx &w, int cols,
+                                            bool full = false) {
     RunOffs ro;
     const int lane = threadIdx.x & 63;
-    const int n = cols * a.KP;
+    const int kp = full ? a.K : a.KP;
+    const FastDiv fkp = full ? a.fK : a.fKP;
+    const int n = cols * kp;
     ro.ok = n <= 64 * kRunSteps;
     const int cstride = (int)(w.lst[2] * a.K);
 #pragma unroll
     for (int m = 0; m < kRunSteps; ++m) {
         const int e = lane + 64 * m;
-        const int col = fdiv(e, a.fKP);
-        ro.off[m] = col * cstride + (e - col * a.KP);
+        const int col = fdiv(e, fkp);
+        ro.off[m] = col * cstride + (e - col * kp);
     }
     return ro;
 }
@@ -186,17 +195,21 @@ __device__ __forceinline__ float masked(const uint8_t *m, int64_t i, float v) {
 
 // LDS -> global, one wave: 16-byte pieces where aligned, else 4-byte ones,
 // four LDS reads in flight per lane. With a window mask, entry i of the
-// attention array takes mask[i - mbase] (the mask indexes one plane).
+// attention array takes mask[i - mbase] (the mask indexes one plane). full:
+// whole K-entry rows (rows_full per round) instead of one window plane's slice.
 __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, int wave, int r0,
                                             int it, const float *buf, float *dst,
-                                            const RunOffs &ro, int64_t mbase, bool use_mask) {
+                                            const RunOffs &ro, int64_t mbase, bool use_mask,
+                                            bool full = false) {
     const int lane = threadIdx.x & 63;
     const int qr0 = w.o[1] + 8 * (wave >> 1) + r0, qc0 = w.o[2] + 8 * (wave & 1);
     const uint8_t *mk = use_mask && a.mask ? a.mask - mbase : nullptr;
-    for (int row = 0; row < a.rows_round && qr0 + row < w.n[1]; ++row) {
-        const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it);
-        const float *brow = buf + row * 8 * a.KP;
-        if (run_vec(rr, row * 8 * a.KP) &&
+    const int rows = full ? a.rows_full : a.rows_round;
+    for (int row = 0; row < rows && qr0 + row < w.n[1]; ++row) {
+        const RowRun rr = row_run(a, w, w.o[0], qr0 + row, qc0, 8, it, full);
+        const int kp = rr.kp;
+        const float *brow = buf + row * 8 * kp;
+        if (run_vec(rr, row * 8 * kp) &&
             (!mk || ((reinterpret_cast<uintptr_t>(mk + rr.base) & 3) == 0))) {
             const int n4 = rr.n >> 2;
             const float4 *l4 = reinterpret_cast<const float4 *>(brow);
@@ -253,6 +266,118 @@ __device__ __forceinline__ void store_round(const UArgs &a, const TileCtx &w, in
 }
 
 // ============================================================================
+// qk on grids with several planes, windows of at most rows_planes(CH * CW)
+// planes: the scores of every window plane stay in the lane's registers, and
+// the whole K-entry rows leave through LDS at the end. (Storing each plane's
+// slice as it is formed writes runs of k_h * k_w entries K entries apart,
+// partial lines that cost more than the scores: 1.8 ms of 2.9 ms for a
+// 3 x 5 x 5 window on a 16 x 256 x 256 grid of 8 heads.)
+constexpr int rows_planes(int ni) { return ni <= 4 ? 5 : ni <= 9 ? 3 : 0; }
+
+template <int D, int CH, int CW, bool RPB>
+__device__ __forceinline__ void qk_rows(const UArgs &a, const TileCtx &w, char *smem) {
+    constexpr int PS = D * 4, NC = D / 4, NI = CH * CW;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c = lane & 3, grp = lane >> 2;
+    const Lane L = lane_geom(w, wave, lane);
+
+    int us[3], lo[3], U[3], E[3];
+#pragma unroll
+    for (int x = 1; x < 3; ++x) {
+        us[x] = window_start(L.f[x], w.n[x], w.k[x]);
+        lo[x] = window_start(L.p[x], w.n[x], w.k[x]) - us[x];
+        key_box(w.o[x], x == 1 ? kTH : kTW, 2, w.n[x], w.k[x], &U[x], &E[x]);
+    }
+    const int t0 = window_start(w.o[0], w.n[0], w.k[0]);
+    const int ra = a.g.ra;
+    const char *baseA = smem + (us[1] - U[1] + (c >> 1)) * ra + (us[2] - U[2] + (c & 1)) * PS;
+    const int64_t qo = elem_off(w, L.p);
+    const int lr = 2 * (grp & 3) + (c >> 1), lc = 2 * (grp >> 2) + (c & 1);
+    const int plane_tokens_k = w.k[1] * w.k[2];
+
+    // bias: this head's whole table (2 k_t - 1 planes) in LDS past the staging
+    // area and the row buffers, read when the rows are formed
+    const int RH = 2 * w.k[1] - 1, RW = 2 * w.k[2] - 1;
+    if constexpr (RPB) {
+        const int n = (2 * w.k[0] - 1) * RH * RW;
+        const float *src = a.rpb + (int64_t)tile_head(a, w) * n;
+        float *dstl = reinterpret_cast<float *>(smem + a.rpb_off);
+        for (int i = threadIdx.x; i < n; i += kThreads) dstl[i] = src[i];
+    }
+
+    constexpr int NP = rows_planes(NI);
+    float s[NP][NI][4];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        if (j >= w.k[0]) break;
+        const int tk = t0 + j;
+        if (j > 0) __syncthreads();  // the previous plane is read no more
+        stage_plane<float, D, PS>(a.b, w, tk, U[1], E[1], U[2], E[2], ra, smem);
+        float qr[D];
+        load_row<float, D>(a.a + qo + opaque_zero(), qr);
+#pragma unroll
+        for (int d = 0; d < D; ++d) qr[d] *= a.alpha;
+        stage_wait();
+
+        {
+            f4 kb[2][NC / 2], z0, z1;
+            pipelined<2 * NI>(
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    load_chunks<NC / 2>(baseA + 2 * (i / CW) * ra + 2 * (i % CW) * PS +
+                                            (jj & 1) * (NC / 2) * 16, kb[bb]);
+                },
+                [&](int jj, int bb) {
+                    const int i = jj >> 1;
+                    if ((jj & 1) == 0) z0 = z1 = f4{0.f, 0.f, 0.f, 0.f};
+                    dot_half<NC / 2>(kb[bb], qr, (jj & 1) * (NC / 2), z0, z1);
+                    if ((jj & 1) == 0) return;
+                    const f4 z = z0 + z1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[j][i][e] = z[e];
+                    pin4(s[j][i]);
+                });
+        }
+    }
+    __syncthreads();  // the staged planes are read no more: their LDS takes the rows
+
+    const RunOffs ro = run_offs(a, w, 8, true);
+    const int64_t plane_tokens = (int64_t)a.g.ext[0] * a.g.ext[1] * a.g.ext[2];
+    const int64_t mbase = a.mask ? (w.lbase / plane_tokens) * plane_tokens * a.K : 0;
+    float *buf = reinterpret_cast<float *>(smem) + wave * (a.rows_full * 8 * a.K);
+    for (int r0 = 0; r0 < 8; r0 += a.rows_full) {
+        if (lr >= r0 && lr < r0 + a.rows_full) {
+            float *slot = buf + ((lr - r0) * 8 + lc) * a.K;
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                if (j >= w.k[0]) break;
+                // bias of key plane t0 + j: the lane's entry for walk row h, column
+                // wc at tbl + h * RW + wc (offset key - query + k - 1 per axis)
+                const float *tbl = reinterpret_cast<const float *>(smem + a.rpb_off) +
+                                   ((t0 + j - w.o[0] + w.k[0] - 1) * RH + us[1] - L.p[1] + w.k[1] - 1) * RW +
+                                   (us[2] - L.p[2] + w.k[2] - 1);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int h = 2 * (i / CW) + (e >> 1), wc = 2 * (i % CW) + (e & 1);
+                        const int jh = h - lo[1], jw = wc - lo[2];
+                        if ((unsigned)jh < (unsigned)w.k[1] && (unsigned)jw < (unsigned)w.k[2]) {
+                            if constexpr (RPB)
+                                slot[j * plane_tokens_k + jh * a.kw + jw] = s[j][i][e] + tbl[h * RW + wc];
+                            else
+                                slot[j * plane_tokens_k + jh * a.kw + jw] = s[j][i][e];
+                        }
+                    }
+            }
+        }
+        __syncthreads();
+        store_round(a, w, wave, r0, 0, buf, a.attn_out, ro, mbase, true, true);
+        __syncthreads();
+    }
+}
+
+// ============================================================================
 // qk: attn[x][j] = alpha <a_x, b_{N(x)_j}>
 // MODE 0: the scores. MODE 1 (single-plane grids): the window softmax of the
 // scores, computed in the lane's registers (the whole window is there), so
@@ -265,6 +390,13 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
     constexpr int PS = D * 4, NC = D / 4, NI = CH * CW;
     TileCtx w;
     if (!decode(a.g, tile, w)) return;
+    if constexpr (T3 && MODE == 0 && rows_planes(NI) > 0) {
+        // (rows_full is set only for windows of at most rows_planes(NI) planes)
+        if (a.rows_full > 0) {
+            qk_rows<D, CH, CW, RPB>(a, w, smem);
+            return;
+        }
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c = lane & 3, grp = lane >> 2;
     const Lane L = lane_geom(w, wave, lane);
@@ -796,10 +928,24 @@ inline bool fast_qk(const Geo &geo, int64_t bh, int D, const float *a, const flo
     pl.a.rpb = rpb;
     pl.a.mask = mask;
     pl.a.heads = heads;
+    if (pl.t3 && geo.ker[0] <= rows_planes(pl.c * pl.c)) {
+        // whole rows at the end: the four waves' round buffers of K-entry rows
+        // share the LDS with the staging area
+        int R = 8;
+        while (R > 1 && (int64_t)4 * R * 8 * geo.K * 4 > std::max<int64_t>(pl.lds, kLdsCap)) R /= 2;
+        const int64_t bytes = (int64_t)4 * R * 8 * geo.K * 4;
+        if (bytes <= kLdsCap) {
+            pl.a.rows_full = R;
+            pl.a.fK = na::make_fastdiv(geo.K);
+            pl.lds = (int)std::max<int64_t>(pl.lds, bytes);
+        }
+    }
     if (rpb) {
-        // the bias table plane after the staging area
+        // the bias table plane after the staging area; with whole rows, the
+        // head's whole table after the row buffers
         pl.a.rpb_off = (pl.lds + 15) & ~15;
-        pl.lds = pl.a.rpb_off + (2 * geo.ker[1] - 1) * (2 * geo.ker[2] - 1) * 4;
+        pl.lds = pl.a.rpb_off + (pl.a.rows_full ? 2 * geo.ker[0] - 1 : 1) * (2 * geo.ker[1] - 1) *
+                                    (2 * geo.ker[2] - 1) * 4;
         if (pl.lds > kLdsCap) return false;
     }
 #define X(DD, C, T3)                                                                          \
