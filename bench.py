@@ -307,9 +307,11 @@ class UnfusedRunner:
                 f()
                 ev[s][i + 1].record()
         torch.cuda.synchronize()
-        per = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+        # medians over the steps, as for the fused legs (one slow step must not
+        # move an op's figure)
+        per = {name: float(np.median([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
                for i, (name, _) in enumerate(self.ops)}
-        step = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]))
+        step = float(np.median([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]))
         return step, per
 
     def time_chain(self, steps, warmup):
@@ -325,13 +327,13 @@ class UnfusedRunner:
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for s in range(steps):
             step()
-        e1.record()
+            ev[s + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return float(np.median([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]))
 
 
 def unfused_summary(w, step, per):
