@@ -100,6 +100,18 @@ using BwdArgs = BwdArgsT<float>;
 // W) in bands kFastBand tiles wide along W, residue class, batch.
 constexpr int kFastBand = 8;
 
+// Plane of step j of a walk over planes [first, first + len): the one
+// congruent to j modulo len. The tiles of neighbouring planes, which run at
+// the same time, then stage the same plane in the same step wherever their
+// walks overlap, so that its second and third reads come from L2 (3D grid
+// 16 x 256 x 256, window 3 x 5 x 5: forward HBM reads -16%, dk/dv -5%, step
+// 10.76 -> 10.54 ms). Sums over the planes are taken in this order.
+__device__ __forceinline__ int plane_of_step(int first, int len, int j) {
+    int r = (j - first) % len;
+    if (r < 0) r += len;
+    return first + r;
+}
+
 __device__ __forceinline__ bool decode(const Geom &g, int tile, TileCtx &w) {
     int rem = tile, q;
     q = fdiv(rem, g.f_heads);
@@ -434,7 +446,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
 
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
-        const int tk = t0 + j;
+        const int tk = plane_of_step(t0, nplanes, j);
         if (a.frame && a.frame_axis == 0 && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         if (j > 0) __syncthreads();
         stage_plane<T, D, PS>(a.k, w, tk, U[1], E[1], U[2], E[2], ra, smem);
@@ -575,7 +587,7 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
 
     const int nplanes = T3 ? w.k[0] : 1;
     for (int j = 0; j < nplanes; ++j) {
-        const int tk = t0 + j;
+        const int tk = plane_of_step(t0, nplanes, j);
         if (a.frame && a.frame_axis == 0 && !in_frame(tk, w.o[0], w.n[0], fk_t)) continue;
         if (j > 0) __syncthreads();
         stage_plane<T, D, PS>(a.v, w, tk, U[1], E[1], U[2], E[2], ra, smem);
@@ -731,7 +743,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
 
     const int nplanes = T3 ? tq1 - tq0 + 1 : 1;
     for (int j = 0; j < nplanes; ++j) {
-        const int tq = tq0 + j;
+        const int tq = plane_of_step(tq0, nplanes, j);
         if (a.frame && a.frame_axis == 0 &&
             !in_frame(w.o[0], tq, w.n[0], frame_size(a.frame, w, 0, tq)))
             continue;
