@@ -410,8 +410,26 @@ na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t 
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(32, 2, true) X(32, 3, true) X(32, 4, true)
 
+// Window masks (a.mask) run on the fp32 register-resident forward and dq
+// kernels when the mask is 4-byte aligned (they read it in aligned dwords);
+// 16-bit tensors and the dk/dv side take the split kernels.
+template <typename T>
+bool fast_mask_ok(const uint8_t *mask) {
+    return std::is_same<T, float>::value && (reinterpret_cast<uintptr_t>(mask) & 3u) == 0;
+}
+
 template <typename T>
 na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgsT<T> &a, hipStream_t s) {
+    if constexpr (std::is_same<T, float>::value) {
+        if (a.mask) {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return launch_fast(na::fast::fwd_kernel<T, D, C, C, T3, true>, pl, a, s);
+            NA_FAST_CASES(X)
+#undef X
+            return NA_ERR_UNSUPPORTED;
+        }
+    }
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return launch_fast(na::fast::fwd_kernel<T, D, C, C, T3>, pl, a, s);
@@ -427,6 +445,15 @@ na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgsT<T> &a, hipStream
 template <typename T>
 na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
     if constexpr (std::is_same<T, float>::value) {
+        if (a.mask) {
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3, true>, pl, a, s) \
+                      : launch_fast(na::fast::dq_kernel<T, D, C, C, T3, false, true>, pl, a, s);
+            NA_FAST_CASES(X)
+#undef X
+            return NA_ERR_UNSUPPORTED;
+        }
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3>, pl, a, s)    \
@@ -650,8 +677,8 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
         }
     }
     FastPlan pl;
-    // window masks: the split kernels only
-    if (!a.mask && fast_plan_fwd(pr, &pl)) {
+    // window masks: the fp32 register-resident kernels, else the split kernels
+    if ((!a.mask || fast_mask_ok<T>(a.mask)) && fast_plan_fwd(pr, &pl)) {
         na::fast::FwdArgsT<T> fa{};
         fa.g = pl.g;
         fa.q = static_cast<const T *>(a.q);
@@ -662,6 +689,9 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
         fa.qscale = a.qscale;
         fa.frame = a.frame;
         fa.frame_axis = a.frame_axis;
+        fa.mask = a.mask;
+        fa.mask_k = a.mask_k;
+        fa.mask_bytes = pr.tokens * a.mask_k;
         return fast_fwd<T>(pl, fa, s);
     }
     int lds;
@@ -770,8 +800,11 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
         if (phases & kPhaseDq) {
-            if (!a.mask && fast_plan_fwd(pr, &pq, true)) {
+            if ((!a.mask || fast_mask_ok<T>(a.mask)) && fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;
+                fa.mask = a.mask;
+                fa.mask_k = a.mask_k;
+                fa.mask_bytes = pr.tokens * a.mask_k;
                 const na_status st = fast_dq<T>(pq, fa, s);
                 if (st != NA_OK) return st;
             } else {

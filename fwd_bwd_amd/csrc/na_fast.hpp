@@ -71,6 +71,10 @@ struct FwdArgsT {
     float qscale;  // scale * log2(e)
     const int *frame;  // windows restricted along frame_axis (null: none)
     int frame_axis;
+    // window mask (MASK kernels): mask_k bytes per query token, mask_bytes in all
+    const uint8_t *mask;
+    int64_t mask_bytes;
+    int mask_k;
 };
 using FwdArgs = FwdArgsT<float>;
 
@@ -89,6 +93,10 @@ struct BwdArgsT {
     int edge, walk_c;
     const int *frame;  // windows restricted along frame_axis (null: none)
     int frame_axis;
+    // window mask (MASK kernels, dq): mask_k bytes per query token, mask_bytes in all
+    const uint8_t *mask;
+    int64_t mask_bytes;
+    int mask_k;
 };
 using BwdArgs = BwdArgsT<float>;
 
@@ -383,6 +391,76 @@ __device__ __forceinline__ void store_row(T *dst, const f4 (&acc)[D / 4], float 
         }
 }
 
+// ----------------------------------------------------------------------------
+// Window masks (MASK kernels: na_fwd_masked, and dq of na_bwd_masked). The
+// mask holds mask_k bytes per query token ([(T,) H, W, K] in row-major order,
+// shared by batch elements and heads); byte it * kh * kw + jh * kw + jw of a
+// query's row is zero when the query drops that key of its window (plane it,
+// row jh, column jw of the window).
+
+// Bit b (b < 4) set when byte b of u is nonzero.
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t u) {
+    uint32_t t = u | (u >> 4);
+    t |= t >> 2;
+    t |= t >> 1;
+    t &= 0x01010101u;
+    return (t | (t >> 7) | (t >> 14) | (t >> 21)) & 0xfu;
+}
+
+// Dword of the mask at byte a (a multiple of 4; the mask is 4-byte aligned):
+// read whole when it lies inside the mask, else byte by byte up to its end.
+__device__ __forceinline__ uint32_t mask_dword(const uint8_t *mask, int64_t nbytes, int64_t a) {
+    if (a + 4 <= nbytes) return *reinterpret_cast<const uint32_t *>(mask + a);
+    uint32_t v = 0u;
+    for (int b = 0; b < 4; ++b)
+        if (a + b < nbytes) v |= (uint32_t)mask[a + b] << (8 * b);
+    return v;
+}
+
+// The mask bits of one query's window plane laid over its walk: bit
+// (r & 1) * 16 + q of word r / 2 for walk row r, column q, which is window
+// row r - lo1, column q - lo2 (lo1, lo2 in {0, 1}); zero outside the window.
+// rowbase: byte of the plane's first entry in the query's mask row.
+template <int CH, int CW>
+__device__ __forceinline__ void walk_mask_bits(const uint8_t *mask, int64_t nbytes,
+                                               int64_t rowbase, int kh, int kw, int lo1, int lo2,
+                                               uint32_t (&wb)[CH]) {
+    static_assert(2 * CW <= 16, "a walk row must fit 16 bits");
+#pragma unroll
+    for (int i = 0; i < CH; ++i) wb[i] = 0u;
+    const uint32_t keep = (1u << kw) - 1u;  // kw <= 2 CW - 1 <= 15
+#pragma unroll
+    for (int r = 0; r < 2 * CH; ++r) {
+        const int jh = r - lo1;
+        if ((unsigned)jh >= (unsigned)kh) continue;
+        const int64_t st = rowbase + (int64_t)jh * kw;  // the window row's first byte
+        const int64_t d0 = st & ~(int64_t)3;
+        const uint32_t sh = (uint32_t)(st - d0) * 8u;
+        const uint32_t x0 = mask_dword(mask, nbytes, d0), x1 = mask_dword(mask, nbytes, d0 + 4);
+        const uint32_t x2 = kw > 4 ? mask_dword(mask, nbytes, d0 + 8) : 0u;
+        // bytes 0..3 and 4..7 of the window row, and byte 8
+        const uint64_t lo = (((uint64_t)x1 << 32) | x0) >> sh;
+        const uint64_t hi = (((uint64_t)x2 << 32) | x1) >> sh;
+        const uint32_t bits = nonzero_bytes4((uint32_t)lo) | (nonzero_bytes4((uint32_t)hi) << 4) |
+                              (((uint32_t)(hi >> 32) & 0xffu) ? 0x100u : 0u);
+        wb[r >> 1] |= ((bits & keep) << lo2) << ((r & 1) * 16);
+    }
+}
+
+// Byte of the first entry of the query's mask row: the query's grid token
+// (class coordinates p of residue class r, dilation d) times mask_k.
+__device__ __forceinline__ int64_t mask_row_base(const TileCtx &w, const int (&ext)[3],
+                                                 const int (&p)[3], int mask_k) {
+    const int64_t t = w.r[0] + (int64_t)w.d[0] * p[0];
+    const int64_t h = w.r[1] + (int64_t)w.d[1] * p[1];
+    const int64_t x = w.r[2] + (int64_t)w.d[2] * p[2];
+    return ((t * ext[1] + h) * ext[2] + x) * mask_k;
+}
+
+__device__ __forceinline__ bool walk_bit(const uint32_t *wb, int r, int q) {
+    return (wb[r >> 1] >> ((r & 1) * 16 + q)) & 1u;
+}
+
 // Whether walk row r (0 .. 2C - 1, relative to the block's walk start) lies
 // in the window of a point whose window starts lo (0 or 1) rows after the walk
 // start: rows 1 .. 2C - 3 always do (k >= 2C - 2 for a walk of C patches).
@@ -401,7 +479,9 @@ struct Edge {
 
 // ============================================================================
 // Forward.
-template <typename T, int D, int CH, int CW, bool T3>
+// MASK: the window mask of a.mask as well (its bits per key plane in uint32_t
+// words over the walk, see walk_mask_bits).
+template <typename T, int D, int CH, int CW, bool T3, bool MASK = false>
 __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4, NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
@@ -454,6 +534,12 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
         load_row<T, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
         for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+        uint32_t wb[MASK ? CH : 1];
+        if constexpr (MASK)
+            walk_mask_bits<CH, CW>(a.mask, a.mask_bytes,
+                                   mask_row_base(w, a.g.ext, L.p, a.mask_k) +
+                                       (int64_t)(tk - t0) * w.k[1] * w.k[2],
+                                   w.k[1], w.k[2], lo[1], lo[2], wb);
         stage_wait();
 
         // S_b[i][c] = <k_i, q_c>, masked; plane maximum
@@ -475,7 +561,8 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
                     const f4 z = z0 + z1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        if constexpr (MASK) ok = ok && walk_bit(wb, 2 * c1 + (e >> 1), 2 * c2 + (e & 1));
                         s[i][e] = ok ? z[e] : -INFINITY;
                     }
                     mj = fmaxf(mj, fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3])));
@@ -533,7 +620,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgsT<T> &a, int tile, char *s
 // for both of its uses. Without it K is staged once as well when the plan
 // gives both layouts one pitch (the d-major reads then take bank conflicts),
 // else once per layout.
-template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+template <typename T, int D, int CH, int CW, bool T3, bool PAD, bool MASK = false>
 __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
@@ -622,6 +709,12 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
         load_row<T, D>(a.q + qo + opaque_zero(), qr);
 #pragma unroll
         for (int d = 0; d < D; ++d) qr[d] *= a.qscale;
+        uint32_t wb[MASK ? CH : 1];
+        if constexpr (MASK)
+            walk_mask_bits<CH, CW>(a.mask, a.mask_bytes,
+                                   mask_row_base(w, a.g.ext, L.p, a.mask_k) +
+                                       (int64_t)(tk - t0) * w.k[1] * w.k[2],
+                                   w.k[1], w.k[2], lo[1], lo[2], wb);
         stage_wait();
 
         // P = exp2(S - lse), dS = P (dP - delta)
@@ -641,7 +734,8 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
                     const f4 z = z0 + z1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        bool ok = ed.h[2 * c1 + (e >> 1)] && ed.w[2 * c2 + (e & 1)];
+                        if constexpr (MASK) ok = ok && walk_bit(wb, 2 * c1 + (e >> 1), 2 * c2 + (e & 1));
                         const float p = ok ? fast_exp2(z[e] - lse2) : 0.f;
                         s[i][e] = p * (s[i][e] - delta);
                     }
@@ -872,16 +966,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
 
 // ============================================================================
 // Kernels: one workgroup per tile.
-template <typename T, int D, int CH, int CW, bool T3>
+template <typename T, int D, int CH, int CW, bool T3, bool MASK = false>
 __global__ void __launch_bounds__(kThreads, 2) fwd_kernel(FwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    fwd_tile<T, D, CH, CW, T3>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    fwd_tile<T, D, CH, CW, T3, MASK>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+template <typename T, int D, int CH, int CW, bool T3, bool PAD, bool MASK = false>
 __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dq_tile<T, D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dq_tile<T, D, CH, CW, T3, PAD, MASK>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 template <typename T, int D, int CH, int CW, bool T3, bool PAD>
