@@ -471,8 +471,31 @@ na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_
     return NA_ERR_UNSUPPORTED;
 }
 
+// The masked dk/dv instantiations: the interior square walks of fp32 only, up
+// to 3 patches on grids of several planes (the walk of 4 spilled there).
+#define NA_FAST_CASES_MASKED_DKDV(X)                                                      \
+    X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)                      \
+    X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
+    X(16, 2, true) X(16, 3, true) X(32, 2, true) X(32, 3, true)
+bool fast_dkdv_masked(const FastPlan &pl) {
+    return pl.cw == pl.c && pl.c >= 2 && pl.c <= (pl.t3 ? 3 : 5) &&
+           (pl.g.head_dim == 16 || pl.g.head_dim == 32);
+}
+
 template <typename T>
 na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
+    if constexpr (std::is_same<T, float>::value) {
+        if (a.mask) {
+            if (!fast_dkdv_masked(pl)) return NA_ERR_UNSUPPORTED;
+#define X(D, C, T3)                                                                       \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+        return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, T3, true>, pl, a, s) \
+                      : launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, false, true>, pl, a, s);
+            NA_FAST_CASES_MASKED_DKDV(X)
+#undef X
+            return NA_ERR_UNSUPPORTED;
+        }
+    }
     if (pl.cw != pl.c) {
         // border classes with a longer walk along one axis (rect_walk_compiled)
         if constexpr (!std::is_same<T, bf16>::value) {
@@ -799,12 +822,13 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
         fa.edge = -1;  // dk/dv tiles by walk_lo (border classes set it per launch)
         // dq (which also writes delta) strictly before dk/dv, which reads it
         FastPlan pq, pk;
+        fa.mask = a.mask;
+        fa.mask_k = a.mask_k;
+        fa.mask_bytes = pr.tokens * a.mask_k;
+        const bool mask_fast = !a.mask || fast_mask_ok<T>(a.mask);
         if (phases & kPhaseDq) {
-            if ((!a.mask || fast_mask_ok<T>(a.mask)) && fast_plan_fwd(pr, &pq, true)) {
+            if (mask_fast && fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;
-                fa.mask = a.mask;
-                fa.mask_k = a.mask_k;
-                fa.mask_bytes = pr.tokens * a.mask_k;
                 const na_status st = fast_dq<T>(pq, fa, s);
                 if (st != NA_OK) return st;
             } else {
@@ -821,8 +845,12 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             const int need = max_tile_walk(pr);
             const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
             int done = 0;  // tiles with inverse walk <= done are covered
-            if (!a.mask && (fast_plan(pr, 1, c, 0, &pk, true) ||
-                            fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true))) {
+            // with a window mask: the interior walk only (fast_dkdv_masked), the
+            // border tiles on the split kernel
+            if (mask_fast &&
+                (fast_plan(pr, 1, c, 0, &pk, true) ||
+                 fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true)) &&
+                (!a.mask || fast_dkdv_masked(pk))) {
                 fa.g = pk.g;
                 fa.walk_lo = 0;
                 const na_status st = fast_dkdv<T>(pk, fa, s);
@@ -832,7 +860,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             // border tiles by class: a longer walk along H only, along W only,
             // or along both (corners), each with the walk it needs, when all
             // the classes that occur have a compiled kernel
-            if (done > 0 && done < need) {
+            if (!a.mask && done > 0 && done < need) {
                 const int hm = max_axis_walk(pr, 1), wm = max_axis_walk(pr, 2);
                 FastPlan cls[4];
                 bool use[4] = {false, false, false, false}, all = true;
@@ -867,7 +895,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
                     done = need;
                 }
             }
-            for (int cb = c + 1; done > 0 && done < need && cb <= need; ++cb) {
+            for (int cb = c + 1; !a.mask && done > 0 && done < need && cb <= need; ++cb) {
                 if (!fast_plan(pr, 1, cb, done, &pk, true) &&
                     !fast_plan(pr, 1, cb, done, &pk, false, 0, -1, true))
                     continue;

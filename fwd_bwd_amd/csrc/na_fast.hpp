@@ -770,6 +770,47 @@ __device__ __forceinline__ void dq_tile(const BwdArgsT<T> &a, int tile, char *sm
     if (L.active) store_row<T, D>(a.dq + qo, acc, a.scale);
 }
 
+// The mask bits of the queries of a key's inverse walk (dk/dv with a window
+// mask): bit (r & 1) * 16 + q of word r / 2 for walk row r, column q, the
+// query at (lo1 + r, lo2 + q) of plane tq (class coordinates): that query's
+// mask byte for this key's place in its window. Only the queries of the key's
+// inverse window (vm) are read; the others get zero bits (their bytes are
+// read from the mask's first byte, so that the loads need no branches).
+template <typename T, int CH, int CW>
+__device__ __forceinline__ void inverse_walk_mask_bits(const BwdArgsT<T> &a, const TileCtx &w,
+                                                       const int (&key)[3], int tq,
+                                                       const int (&lo)[3], const unsigned (&vm)[3],
+                                                       uint32_t (&mb)[CH]) {
+    const int64_t H = a.g.ext[1], W = a.g.ext[2], K = a.mask_k;
+    const int kh = w.k[1], kw = w.k[2];
+    const int64_t tabs = w.r[0] + (int64_t)w.d[0] * tq;
+    const int jt = key[0] - window_start(tq, w.n[0], w.k[0]);
+    const int64_t base = ((tabs * H + w.r[1] + (int64_t)w.d[1] * lo[1]) * W + w.r[2] +
+                          (int64_t)w.d[2] * lo[2]) * K + (int64_t)jt * kh * kw;
+    int64_t rowo[2 * CH];
+    int colo[2 * CW];
+#pragma unroll
+    for (int r = 0; r < 2 * CH; ++r) {
+        const int qh = imin(lo[1] + r, w.n[1] - 1);
+        rowo[r] = base + r * w.d[1] * W * K + (int64_t)(key[1] - window_start(qh, w.n[1], kh)) * kw;
+    }
+#pragma unroll
+    for (int q = 0; q < 2 * CW; ++q) {
+        const int qw = imin(lo[2] + q, w.n[2] - 1);
+        colo[q] = q * w.d[2] * (int)K + key[2] - window_start(qw, w.n[2], kw);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) mb[i] = 0u;
+#pragma unroll
+    for (int r = 0; r < 2 * CH; ++r)
+#pragma unroll
+        for (int q = 0; q < 2 * CW; ++q) {
+            const bool in = ((vm[1] >> r) & (vm[2] >> q) & 1u) != 0;
+            const uint8_t b = a.mask[in ? rowo[r] + colo[q] : 0];
+            if (in && b) mb[r >> 1] |= 1u << ((r & 1) * 16 + q);
+        }
+}
+
 // ============================================================================
 // Backward, key side: dk and dv by inverse-neighborhood gather, without
 // atomics. Every block walks CH x CW query patches; entries outside a key's
@@ -783,8 +824,9 @@ __device__ __forceinline__ int tile_walk(const TileCtx &w) {
                 tile_inverse_walk(w.o[2], kTW, 2, w.n[2], w.k[2]));
 }
 
-// PAD: as for dq_tile; dout is then staged once for dV and dS.
-template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+// PAD: as for dq_tile; dout is then staged once for dV and dS. MASK: the
+// window mask of a.mask as well (inverse_walk_mask_bits).
+template <typename T, int D, int CH, int CW, bool T3, bool PAD, bool MASK = false>
 __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *smem) {
     constexpr int PS = D * 4 + (PAD ? 16 : 0), NC = D / 4, G = D / 4, NI = CH * CW;
     TileCtx w;
@@ -845,6 +887,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
         stage_plane<T, D, PS>(a.q, w, tq, U[1], E[1], U[2], E[2], ra, smem);
         stage_rows_plane(a.lse, a.delta, w, tq, U[1], E[1], U[2], E[2], rp,
                          reinterpret_cast<float2 *>(smem + a.g.rows_off));
+        uint32_t mb[MASK ? CH : 1];
+        if constexpr (MASK) inverse_walk_mask_bits<T, CH, CW>(a, w, L.p, tq, lo, vm, mb);
         float kr[D];
         load_row<T, D>(a.k + ko + opaque_zero(), kr);
 #pragma unroll
@@ -876,7 +920,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdArgsT<T> &a, int tile, char *
                     const unsigned hb = vm[1] >> (2 * c1), wb = vm[2] >> (2 * c2);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const bool ok = ((hb >> (e >> 1)) & (wb >> (e & 1)) & 1u) != 0;
+                        bool ok = ((hb >> (e >> 1)) & (wb >> (e & 1)) & 1u) != 0;
+                        if constexpr (MASK) ok = ok && walk_bit(mb, 2 * c1 + (e >> 1), 2 * c2 + (e & 1));
                         s[i][e] = ok ? fast_exp2(z[e]) : 0.f;
                     }
                     pin4(s[i]);
@@ -978,10 +1023,10 @@ __global__ void __launch_bounds__(kThreads, 2) dq_kernel(BwdArgsT<T> a) {
     dq_tile<T, D, CH, CW, T3, PAD, MASK>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
-template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+template <typename T, int D, int CH, int CW, bool T3, bool PAD, bool MASK = false>
 __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<T, D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<T, D, CH, CW, T3, PAD, MASK>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 // The same for the few border tiles with a longer walk: one workgroup per CU,

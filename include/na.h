@@ -183,10 +183,11 @@ na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const
  * row-major (t, h, w) order), exactly the mask of na_qk. Masked scores are
  * -inf before the softmax; a query that keeps no key gets a zero output, lse
  * = -inf and contributes nothing to the backward. Otherwise exactly na_fwd
- * and na_bwd (same buffers, rules and errors; mask must be non-null). These
- * run on the general tile kernels (one workgroup walks every patch of its
- * tile's windows and tests each pair against the mask), not on the faster
- * register-resident or 16-bit MFMA kernels. */
+ * and na_bwd (same buffers, rules and errors; mask must be non-null). fp32
+ * problems with a 4-byte aligned mask run on the register-resident kernels
+ * (forward, dq and the interior dk/dv tiles read the mask rows they need);
+ * 16-bit tensors, the dk/dv border tiles and the KV-parallel backward run on
+ * the general tile kernels, which test every pair against the mask. */
 na_status na_fwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
                         void *out, float *lse, const uint8_t *mask, void *hip_stream);
 na_status na_bwd_masked(const na_problem *p, const void *q, const void *k, const void *v,

@@ -53,6 +53,13 @@ CASES = [
     ((1, 6, 20, 18, 2, 32), (5, 3, 3), 1, torch.bfloat16),
     ((1, 26, 27, 2, 64), (7, 5), 1, torch.float16),
     ((1, 6, 9, 10, 1, 64), (3, 3, 3), (2, 1, 2), torch.float32),
+    # the register-resident fp32 kernels with the mask: every square walk of
+    # the interior tiles (3 x 3 to 9 x 9 windows, head_dim 16 and 32, dilation,
+    # a 3D grid with head_dim 16), border tiles on the general kernels
+    ((1, 21, 19, 2, 16), (3, 3), 1, torch.float32),
+    ((1, 26, 27, 2, 32), (5, 5), (1, 2), torch.float32),
+    ((2, 35, 33, 1, 32), (7, 7), 1, torch.float32),
+    ((1, 4, 18, 20, 2, 16), (3, 3, 3), 1, torch.float32),
 ]
 
 
