@@ -26,7 +26,10 @@ The same steps without the flush are reported beside it ("warm").
 The 3D workload is also timed with every window restricted along T to a
 constant 1 and 2 of its 3 planes (na_fwd_framed / na_bwd_framed, "framed"):
 the kernels skip key planes outside a query's frame window, so the time
-should follow the kept fraction of the window.
+should follow the kept fraction of the window. It is also timed with an
+arbitrary window mask that keeps 2/3 of every window at random
+(na_fwd_masked / na_bwd_masked, "masked"), whose time follows the full
+window.
 
 Beside the headline step the same run times the KV-parallel backward variant
 on the same inputs ("kvparallel", per kv_splits: 0 = float atomics, 1 and 4 =
@@ -239,6 +242,33 @@ class FramedRunner(Runner):
 
     def phases(self):
         return [("fwd", self.fwd), ("bwd_framed", self.bwd)]
+
+
+class MaskedRunner(Runner):
+    """The same step through na_fwd_masked / na_bwd_masked (gather): an
+    arbitrary byte mask over every query's window (1 keeps the key), shared by
+    batch elements and heads."""
+
+    def __init__(self, w, mask, host=None, seed=0):
+        super().__init__(w, "gather", seed, host=host)
+        self.mask = mask.to("cuda:0")
+
+    def fwd(self):
+        na.na_fwd_masked(self.q, self.k, self.v, self.mask, *self.args, out=self.out, lse=self.lse)
+
+    def bwd(self):
+        na.na_bwd_masked(self.q, self.k, self.v, self.out, self.dout, self.lse, self.mask,
+                         *self.args, workspace=self.ws, grads=(self.dq, self.dk, self.dv))
+
+    def phases(self):
+        return [("fwd", self.fwd), ("bwd_masked", self.bwd)]
+
+
+def random_window_mask(w, keep, seed=0):
+    """A seeded byte mask [(T,) H, W, K] keeping each window entry with
+    probability keep."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.rand(tuple(w.grid) + (w.window,), generator=g) < keep).to(torch.uint8)
 
 
 def kept_fraction(w, frame):
@@ -669,6 +699,14 @@ def main():
                 del rf
                 torch.cuda.empty_cache()
             result["secondary"]["framed"] = framed
+            # the same step with an arbitrary window mask keeping 2/3 of every
+            # window at random (na_fwd_masked / na_bwd_masked)
+            rm = MaskedRunner(w3, random_window_mask(w3, 2 / 3), host=h3)
+            log(f"[bench] timing {w3.name} with a random window mask")
+            per, _ = rm.time(args.steps, args.warmup, flush)
+            result["secondary"]["masked"] = {"kept_fraction": 0.6667, **framed_leg(w3, per, s3)}
+            del rm
+            torch.cuda.empty_cache()
         run_unfused(w3, h3)
     if unfused:
         result["unfused"] = unfused

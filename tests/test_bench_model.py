@@ -142,3 +142,14 @@ def test_framed_leg_kept_fraction_and_ratios():
     leg = bench.framed_leg(w, per, full)
     assert leg["ms_per_step"] == 3.0
     assert leg["time_vs_full"] == {"fwd": 0.5, "bwd": 0.25, "step": 0.3}
+
+
+def test_random_window_mask_of_the_masked_leg():
+    """The masked leg's mask: bytes [(T,) H, W, K], seeded, about 2/3 ones."""
+    import torch
+    w = bench.WORKLOADS["2d_16x16_k3_h2_d16_f32"]
+    m1, m2 = bench.random_window_mask(w, 2 / 3), bench.random_window_mask(w, 2 / 3)
+    assert m1.dtype == torch.uint8 and tuple(m1.shape) == tuple(w.grid) + (w.window,)
+    assert torch.equal(m1, m2)
+    assert set(m1.unique().tolist()) <= {0, 1}
+    assert abs(float(m1.float().mean()) - 2 / 3) < 0.05
