@@ -471,15 +471,24 @@ na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_
     return NA_ERR_UNSUPPORTED;
 }
 
-// The masked dk/dv instantiations: the interior square walks of fp32 only, up
-// to 3 patches on grids of several planes (the walk of 4 spilled there).
+// The masked dk/dv instantiations (fp32 only): the interior square walks at two
+// workgroups per CU up to 5 patches on one plane and 3 on several (the walk of
+// 4 spilled there); at head_dim 32 the longer walks of the border classes at
+// one workgroup per CU: 7 x 5, 5 x 7, 6 x 4, 4 x 6, 6 x 6, 7 x 7 on one plane,
+// 4 x 3, 3 x 4, 4 x 4 and (padded) 6 x 4, 4 x 6, 6 x 6 on several.
 #define NA_FAST_CASES_MASKED_DKDV(X)                                                      \
     X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)                      \
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(16, 2, true) X(16, 3, true) X(32, 2, true) X(32, 3, true)
 bool fast_dkdv_masked(const FastPlan &pl) {
-    return pl.cw == pl.c && pl.c >= 2 && pl.c <= (pl.t3 ? 3 : 5) &&
-           (pl.g.head_dim == 16 || pl.g.head_dim == 32);
+    const int ch = pl.c, cw = pl.cw;
+    if (ch == cw && ch >= 2 && ch <= (pl.t3 ? 3 : 5))
+        return pl.g.head_dim == 16 || pl.g.head_dim == 32;
+    if (pl.g.head_dim != 32) return false;
+    auto is = [&](int a, int b) { return ch == a && cw == b; };
+    if (!pl.t3) return is(7, 5) || is(5, 7) || is(6, 4) || is(4, 6) || is(6, 6) || is(7, 7);
+    return is(4, 3) || is(3, 4) || is(4, 4) ||
+           (pl.pad && (is(6, 4) || is(4, 6) || is(6, 6)));
 }
 
 template <typename T>
@@ -487,11 +496,31 @@ na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStrea
     if constexpr (std::is_same<T, float>::value) {
         if (a.mask) {
             if (!fast_dkdv_masked(pl)) return NA_ERR_UNSUPPORTED;
+            if (pl.cw == pl.c && pl.c <= (pl.t3 ? 3 : 5)) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, T3, true>, pl, a, s) \
                       : launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, false, true>, pl, a, s);
-            NA_FAST_CASES_MASKED_DKDV(X)
+                NA_FAST_CASES_MASKED_DKDV(X)
+#undef X
+                return NA_ERR_UNSUPPORTED;
+            }
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && !pl.t3)                                             \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false, false, true>, pl, a, s);
+            X(7, 5) X(5, 7) X(6, 4) X(4, 6) X(6, 6) X(7, 7)
+#undef X
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && pl.t3)                                              \
+        return pl.pad                                                                    \
+                   ? launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s) \
+                   : launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, false, true>, pl, a, s);
+            X(4, 3) X(3, 4) X(4, 4)
+#undef X
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && pl.t3 && pl.pad)                                    \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s);
+            X(6, 4) X(4, 6) X(6, 6)
 #undef X
             return NA_ERR_UNSUPPORTED;
         }
@@ -845,8 +874,8 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             const int need = max_tile_walk(pr);
             const int c = std::max(na::window_walk(pr.ker[1], 2), na::window_walk(pr.ker[2], 2));
             int done = 0;  // tiles with inverse walk <= done are covered
-            // with a window mask: the interior walk only (fast_dkdv_masked), the
-            // border tiles on the split kernel
+            // with a window mask: the walks compiled with it (fast_dkdv_masked);
+            // the split kernel takes the rest
             if (mask_fast &&
                 (fast_plan(pr, 1, c, 0, &pk, true) ||
                  fast_plan(pr, 1, c, 0, &pk, false, 0, -1, true)) &&
@@ -860,15 +889,16 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
             // border tiles by class: a longer walk along H only, along W only,
             // or along both (corners), each with the walk it needs, when all
             // the classes that occur have a compiled kernel
-            if (!a.mask && done > 0 && done < need) {
+            if (done > 0 && done < need) {
                 const int hm = max_axis_walk(pr, 1), wm = max_axis_walk(pr, 2);
                 FastPlan cls[4];
                 bool use[4] = {false, false, false, false}, all = true;
                 for (int e = 1; e <= 3; ++e) {
                     if (((e & 1) && hm <= done) || ((e & 2) && wm <= done)) continue;  // no such tile
                     const int ch = (e & 1) ? hm : done, cw = (e & 2) ? wm : done;
-                    use[e] = fast_plan(pr, 1, ch, done, &cls[e], true, cw, e) ||
-                             fast_plan(pr, 1, ch, done, &cls[e], false, cw, e, true);
+                    use[e] = (fast_plan(pr, 1, ch, done, &cls[e], true, cw, e) ||
+                              fast_plan(pr, 1, ch, done, &cls[e], false, cw, e, true)) &&
+                             (!a.mask || fast_dkdv_masked(cls[e]));
                     all = all && use[e];
                 }
                 if (all) {
@@ -895,10 +925,11 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
                     done = need;
                 }
             }
-            for (int cb = c + 1; !a.mask && done > 0 && done < need && cb <= need; ++cb) {
+            for (int cb = c + 1; done > 0 && done < need && cb <= need; ++cb) {
                 if (!fast_plan(pr, 1, cb, done, &pk, true) &&
                     !fast_plan(pr, 1, cb, done, &pk, false, 0, -1, true))
                     continue;
+                if (a.mask && !fast_dkdv_masked(pk)) continue;
                 fa.g = pk.g;
                 fa.walk_lo = done;
                 if (border_of(pr, done, &fa.g.border)) {

@@ -1031,10 +1031,10 @@ __global__ void __launch_bounds__(kThreads, 2) dkdv_kernel(BwdArgsT<T> a) {
 
 // The same for the few border tiles with a longer walk: one workgroup per CU,
 // so that the longer walk never spills registers.
-template <typename T, int D, int CH, int CW, bool T3, bool PAD>
+template <typename T, int D, int CH, int CW, bool T3, bool PAD, bool MASK = false>
 __global__ void __launch_bounds__(kThreads, 1) dkdv_border_kernel(BwdArgsT<T> a) {
     extern __shared__ __align__(16) char smem[];
-    dkdv_tile<T, D, CH, CW, T3, PAD>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
+    dkdv_tile<T, D, CH, CW, T3, PAD, MASK>(a, xcd_tile_id(blockIdx.x, a.g.n_tiles), smem);
 }
 
 }  // namespace fast
