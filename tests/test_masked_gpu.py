@@ -60,6 +60,7 @@ CASES = [
     ((1, 26, 27, 2, 32), (5, 5), (1, 2), torch.float32),
     ((2, 35, 33, 1, 32), (7, 7), 1, torch.float32),
     ((1, 4, 18, 20, 2, 16), (3, 3, 3), 1, torch.float32),
+    ((1, 7, 12, 13, 2, 32), (3, 3, 3), (2, 1, 2), torch.float32),   # dilation along T and W
 ]
 
 
