@@ -161,3 +161,25 @@ def test_masked_gather_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for x, y in zip(g1, g2):
         assert torch.equal(x, y)
+
+
+def test_mask_at_an_odd_address_matches_the_aligned_one():
+    """The register-resident kernels read the mask in aligned dwords and take
+    only 4-byte aligned masks; a mask starting at an odd byte goes to the
+    general kernels. Both give the same function."""
+    shape, kernel, dil, dtype = CASES[0]
+    q, k, v, dout = (t.cuda() for t in make_random(shape, dtype, seed=37))
+    m = torch.from_numpy(random_mask(shape, kernel, 37))
+    store = torch.zeros(m.numel() + 1, dtype=torch.uint8, device="cuda")
+    odd = store[1:].view(m.shape)
+    odd.copy_(m.cuda())
+    assert odd.data_ptr() % 4 != 0 and odd.is_contiguous()
+    aligned = m.cuda().contiguous()
+    res = []
+    for mk in (aligned, odd):
+        o, l = na.na_fwd_masked(q, k, v, mk, kernel, dil)
+        g = na.na_bwd_masked(q, k, v, o, dout, l, mk, kernel, dil)
+        res.append((o, l) + tuple(g))
+    torch.cuda.synchronize()
+    for name, x, y in zip(("out", "lse", "dq", "dk", "dv"), res[0], res[1]):
+        assert rel_err(np64(y), np64(x)) <= TOL[dtype], name
