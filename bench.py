@@ -563,7 +563,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: neighborhood attention here runs on a single "
-              "MI355X; multi-GPU runs are not part of this build.", file=sys.stderr)
+              "MI355X; this benchmark does not run several GPUs.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

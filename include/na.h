@@ -36,7 +36,7 @@
  *
  * Errors. Argument errors are detected on the host before anything is
  * enqueued and return NA_ERR_INVALID_ARG (or NA_ERR_UNSUPPORTED for a valid
- * problem this build has no kernel for, NA_ERR_WORKSPACE for a workspace that
+ * problem the library has no kernel for, NA_ERR_WORKSPACE for a workspace that
  * is too small). A failed kernel launch returns NA_ERR_HIP. Apart from the
  * static delta array of na_bwd_noalloc, the library keeps no state between
  * calls besides a once-per-kernel raise of the dynamic-LDS limit; calls on
@@ -105,7 +105,7 @@ typedef struct {
     int64_t dtype;        /* na_dtype */
     int64_t batch;        /* B >= 1 */
     int64_t heads;        /* >= 1 */
-    int64_t head_dim;     /* 16, 32 or 64 in this build */
+    int64_t head_dim;     /* 16, 32 or 64 */
     int64_t extent[3];    /* grid extents, outermost first: (T, H, W) for 3D, (H, W, -) for 2D */
     int64_t kernel[3];    /* window size per axis, same order; 1 <= k <= floor(extent / dilation)
                              (and the window limit above) */
