@@ -410,9 +410,10 @@ na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t 
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(32, 2, true) X(32, 3, true) X(32, 4, true)
 
-// Window masks (a.mask) run on the fp32 register-resident forward and dq
-// kernels when the mask is 4-byte aligned (they read it in aligned dwords);
-// 16-bit tensors and the dk/dv side take the split kernels.
+// Window masks (a.mask) run on the fp32 register-resident kernels when the
+// mask is 4-byte aligned (the forward and dq read it in aligned dwords); 16-bit
+// tensors take the split kernels, and so do the dk/dv walks that have no
+// masked instantiation (fast_dkdv_masked).
 template <typename T>
 bool fast_mask_ok(const uint8_t *mask) {
     return std::is_same<T, float>::value && (reinterpret_cast<uintptr_t>(mask) & 3u) == 0;
