@@ -467,6 +467,9 @@ __device__ __forceinline__ void qk_tile(const UArgs &a, int tile, char *smem) {
             float *dstl = reinterpret_cast<float *>(smem + a.rpb_off);
             for (int i = threadIdx.x; i < RH * RW; i += kThreads) dstl[i] = src[i];
             tbl = dstl + (us[1] - L.p[1] + w.k[1] - 1) * RW + (us[2] - L.p[2] + w.k[2] - 1);
+            // the softmax below reads entries other waves copied (the plain
+            // scores read them only after the barrier that frees the staging)
+            if constexpr (MODE == 1) __syncthreads();
         }
         if constexpr (MODE == 1) {
             // window softmax in registers: bias, window and mask decide the

@@ -356,3 +356,23 @@ def test_qk_softmax_and_its_backward(case):
     dS_ref = oracle.softmax_bwd(np64(p2), oracle.na_qk(G, B, kernel, dil, 1.0))
     check({"probs": p, "probs_plain": p2, "dscores": ds},
           {"probs": P_ref, "probs_plain": P2_ref, "dscores": dS_ref}, "qk_softmax " + _id(case))
+
+
+def test_rpb_softmax_in_the_score_kernel_repeats_bitwise():
+    """The score kernel with the window softmax inside reads the bias table its
+    workgroup copies to LDS; every wave must see the whole copy (a barrier
+    between the copy and the reads). Ten runs on the 9 x 9 case: all bitwise
+    equal, and equal to the oracle's probabilities."""
+    shape, kernel, dil = (1, 2, 40, 37, 32), (9, 9), 1
+    q, k, _, _ = make_random(shape, torch.float32, seed=43)
+    g = torch.Generator(device="cpu").manual_seed(44)
+    rpb = torch.randn(na.rpb_shape(kernel, shape[1], 2), generator=g)
+    dev = torch.device("cuda:0")
+    qd, kd, rd = (t.to(dev) for t in (q, k, rpb))
+    scale = shape[-1] ** -0.5
+    runs = [na.na_qk_softmax(qd, kd, kernel, dil, alpha=scale, rpb=rd) for _ in range(10)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert torch.equal(r, runs[0])
+    P, _ = oracle.unfused_fwd(np64(q), np64(k), np64(k), kernel, dil, scale, rpb=np64(rpb))
+    check({"probs": runs[0]}, {"probs": P}, "rpb softmax repeats")
