@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libna.so")
 SOURCES = [os.path.join(CSRC, "na_api.hip"), os.path.join(CSRC, "na_m16.hip"),
-           os.path.join(CSRC, "na_unfused.hip")]
+           os.path.join(CSRC, "na_unfused.hip"), os.path.join(CSRC, "na_mask.hip")]
 # per-source flags: the 16-bit MFMA kernels run without IEEE-mode NaN handling
 # (their maxima then need no operand canonicalisation; they form no NaNs)
 SOURCE_FLAGS = {"na_m16.hip": ["-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]}

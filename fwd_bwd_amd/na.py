@@ -36,7 +36,7 @@ EXPORTS = ("na_check_problem", "na_fwd", "na_bwd_workspace_bytes", "na_bwd", "na
            "na_qk", "na_av", "na_av_inverse", "na_softmax", "na_softmax_bwd", "na_unfused_fwd",
            "na_unfused_bwd", "na_rpb_grad_workspace_bytes", "na_rpb_grad", "na_qk_softmax",
            "na_qk_softmax_bwd", "na_source_sha256", "na_bwd_noalloc", "na_fwd_framed",
-           "na_bwd_framed", "na_fwd_masked", "na_bwd_masked")
+           "na_bwd_framed", "na_fwd_masked", "na_bwd_masked", "na_window_mask_from_indices")
 
 # rows (batch * tokens * heads) the static delta array of na_bwd_noalloc holds
 NOALLOC_MAX_ROWS = 8388608
@@ -108,6 +108,8 @@ def load() -> ctypes.CDLL:
         lib.na_bwd_masked.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                       ctypes.c_int32, ctypes.c_int32, vp, vp]
         lib.na_bwd_masked.restype = ctypes.c_int
+        lib.na_window_mask_from_indices.argtypes = [P, vp, ctypes.c_int32, vp, vp, vp]
+        lib.na_window_mask_from_indices.restype = ctypes.c_int
         lib.na_window_start.argtypes = [i64, i64, i64, i64]
         lib.na_window_start.restype = i64
         lib.na_inverse_window.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64),
@@ -430,6 +432,44 @@ def na_bwd_masked(q, k, v, out, dout, lse, mask, kernel_size, dilation=1, scale=
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), vid,
                                 kv_splits, mp, _stream_handle(q.device)))
     return dq, dk, dv
+
+
+def na_window_mask_from_indices(indices: torch.Tensor, kernel_size, dilation=1, mask=None,
+                                bad=None, check: bool = True):
+    """Window mask of na_fwd_masked / na_bwd_masked from an index tensor of
+    attended tokens: indices is a contiguous int64 tensor [(T,) H, W, m] on the
+    GPU, per query token m flat token indices ((t * H + h) * W + w) of keys in
+    its window, -1 for an unused slot. Returns (mask, bad): mask uint8
+    [(T,) H, W, prod(kernel)], bad int32 [(T,) H, W] = the query's slots that
+    hold neither -1 nor a token of its window. With check (the default) a
+    nonzero bad raises ValueError (reading it back synchronizes the stream)."""
+    if (not isinstance(indices, torch.Tensor) or indices.dtype != torch.int64
+            or indices.dim() not in (3, 4) or not indices.is_contiguous()
+            or indices.device.type != "cuda"):
+        raise ValueError("indices must be a contiguous int64 CUDA tensor [(T,) H, W, m]")
+    grid = tuple(indices.shape[:-1])
+    m = int(indices.shape[-1])
+    if m > 2 ** 31 - 1:
+        raise ValueError("too many slots per query")
+    p = make_problem((1,) + grid + (1, 16), torch.float32, kernel_size, dilation)
+    K = 1
+    for k in p.kernel[:p.ndim]:
+        K *= int(k)
+    if mask is None:
+        mask = torch.empty(grid + (K,), dtype=torch.uint8, device=indices.device)
+    _check_buf(mask, "mask", grid + (K,), torch.uint8, indices.device)
+    if bad is None:
+        bad = torch.empty(grid, dtype=torch.int32, device=indices.device)
+    _check_buf(bad, "bad", grid, torch.int32, indices.device)
+    _check(load().na_window_mask_from_indices(ctypes.byref(p), _ptr(indices), m, _ptr(mask),
+                                              _ptr(bad), _stream_handle(indices.device)))
+    if check:
+        wrong = torch.nonzero(bad)
+        if wrong.numel():
+            first = tuple(int(c) for c in wrong[0])
+            raise ValueError(f"{wrong.shape[0]} query tokens list tokens outside their window "
+                             f"(first: {first}, {int(bad[first])} slots)")
+    return mask, bad
 
 
 def source_sha256() -> str:

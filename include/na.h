@@ -195,6 +195,25 @@ na_status na_bwd_masked(const na_problem *p, const void *q, const void *k, const
                         void *dv, void *workspace, size_t workspace_bytes, int32_t variant,
                         int32_t kv_splits, const uint8_t *mask, void *hip_stream);
 
+/* The requester's index tensor turned into the mask above (same thread of
+ * the NATTEN issue: the attended tokens of each query given as indices, for
+ * na3d_qk; the maintainer: a tiled kernel keeps the largest window and only
+ * masks inside it). indices is a device array of int64 [(T,) H, W, m], 8-byte
+ * aligned: per query token, m flat token indices (t * H + h) * W + w of one
+ * batch element's grid, shared by every batch element and head; -1 marks an
+ * unused slot. Writes mask [(T,) H, W, prod(kernel)] (any alignment): byte j
+ * of a query's row is 1 when a slot lists the j-th key of its window, else 0
+ * (a key listed twice is kept once; m = 0 drops every key), and bad
+ * [(T,) H, W] int32 (4-byte aligned): the number of the query's slots holding
+ * neither -1 nor a token of its window. The masked kernels only visit the
+ * window, so such a row does not describe the caller's attention: the caller
+ * checks bad (the Python binding raises). Only the problem's ndim, extent,
+ * kernel and dilation are read (the same rules as na_check_problem, without
+ * the window limit); NA_ERR_INVALID_ARG for a malformed grid, m < 0, null
+ * mask or bad, null indices with m > 0, or misaligned pointers. */
+na_status na_window_mask_from_indices(const na_problem *p, const int64_t *indices, int32_t m,
+                                      uint8_t *mask, int32_t *bad, void *hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char *na_status_string(na_status s);
 

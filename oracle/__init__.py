@@ -393,6 +393,46 @@ def outer_window_mask(grid, kernel, outer_kernel, dilation=1):
     return mask
 
 
+def window_mask_from_indices(grid, kernel, indices, dilation=1):
+    """The requester's other form of a per-query window (an index tensor of
+    the attended tokens, for na3d_qk) as a mask of the window entries:
+    indices [*grid, m] lists, per query token, flat token indices (row-major
+    over the grid) of the keys it attends to, -1 for an unused slot. Returns
+    (mask [*grid, prod(kernel)] uint8, bad [*grid] int32): a listed token that
+    lies in the query's window sets the entry of its place there (per axis,
+    (coordinate - window start) / dilation, entries row-major over the axes);
+    bad counts the slots that hold neither -1 nor a token of the query's
+    window. Plain loops over queries, slots and axes."""
+    grid, kernel = tuple(int(g) for g in grid), tuple(int(k) for k in kernel)
+    nd = len(grid)
+    dil = _as3(dilation, nd, 1)[3 - nd:]
+    idx = np.asarray(indices, dtype=np.int64)
+    mask = np.zeros(grid + (int(np.prod(kernel)),), np.uint8)
+    bad = np.zeros(grid, np.int32)
+    ntok = int(np.prod(grid))
+    for x in np.ndindex(*grid):
+        starts = [window_start(grid[a], kernel[a], int(dil[a]), x[a]) for a in range(nd)]
+        for y in idx[x]:
+            y = int(y)
+            if y == -1:
+                continue
+            if not 0 <= y < ntok:
+                bad[x] += 1
+                continue
+            yc = np.unravel_index(y, grid)
+            place = []
+            for a in range(nd):
+                rel = int(yc[a]) - starts[a]
+                if rel < 0 or rel % int(dil[a]) or rel // int(dil[a]) >= kernel[a]:
+                    break
+                place.append(rel // int(dil[a]))
+            if len(place) < nd:
+                bad[x] += 1
+                continue
+            mask[x + (int(np.ravel_multi_index(place, kernel)),)] = 1
+    return mask, bad
+
+
 def softmax_bwd(p, dp):
     """Backward of the window softmax: dS = P * (dP - sum_j P dP) over the last axis."""
     p, dp = _f64(p), _f64(dp)

@@ -512,6 +512,63 @@ def check_outer_window_mask(orc, seed=19):
                 assert np.max(np.abs(tm(got) - ref)) < 1e-12, (grid, kk)
 
 
+def window_tokens(grid, kernel, dil, x, window_start):
+    """Flat indices of the tokens of query x's window, from the per-axis
+    window starts (start + dilation * j, j < kernel)."""
+    axes = [[window_start(grid[a], kernel[a], dil[a], x[a]) + dil[a] * j for j in range(kernel[a])]
+            for a in range(len(grid))]
+    return [int(np.ravel_multi_index(c, grid)) for c in itertools.product(*axes)]
+
+
+def check_index_mask(orc, seed=20):
+    """Index tensors of attended tokens turned into window masks. Entries
+    worked out by hand from the definition (2D 5 x 4 grid, 3 x 3 window; a
+    dilated 6 x 7 grid); and, on 2D and 3D grids with dilation, a random
+    subset of every query's window listed as indices (shuffled, with -1 slots
+    and a repeated token) gives, through the masked unfused forward, exactly
+    softmax attention over the listed tokens, computed densely over the whole
+    grid without any window arithmetic."""
+    import oracle as _o
+    # query (0, 0): rows 0..2, cols 0..2; query (4, 3): rows 2..4, cols 1..3
+    idx = np.full((5, 4, 6), -1, np.int64)
+    idx[0, 0] = [0, 10, 7, -1, 20, 10]      # (0,0) -> 0, (2,2) -> 8, (1,3) outside, 20 off-grid
+    idx[4, 3] = [19, 9, 12, -1, -1, -3]     # (4,3) -> 8, (2,1) -> 0, (3,0) outside, -3 invalid
+    m, bad = _o.window_mask_from_indices((5, 4), (3, 3), idx)
+    assert list(np.nonzero(m[0, 0])[0]) == [0, 8] and bad[0, 0] == 2
+    assert list(np.nonzero(m[4, 3])[0]) == [0, 8] and bad[4, 3] == 2
+    assert not m[1:4].any() and not bad[1:4].any()
+    # dilation 2 along H on 6 rows: query (1, 3) sees rows 1, 3, 5 and columns 2..4
+    idx = np.full((6, 7, 3), -1, np.int64)
+    idx[1, 3] = [3 * 7 + 4, 2 * 7 + 3, 5 * 7 + 2]   # (3,4) -> 1*3+2, (2,3) other class, (5,2) -> 6
+    m, bad = _o.window_mask_from_indices((6, 7), (3, 3), idx, (2, 1))
+    assert list(np.nonzero(m[1, 3])[0]) == [5, 6] and bad[1, 3] == 1
+    r = _rng(seed)
+    for grid, kernel, dil in (((7, 6), (3, 5), (2, 1)), ((4, 5, 6), (3, 3, 3), (1, 1, 2))):
+        nd, heads, D = len(grid), 2, 3
+        toks, m_slots = int(np.prod(grid)), int(np.prod(kernel)) + 3
+        idx = np.full(grid + (m_slots,), -1, np.int64)
+        listed = {}
+        for x in np.ndindex(*grid):
+            win = window_tokens(grid, kernel, dil, x, orc.window_start)
+            keep = [t for t in win if r.random() < 0.6] or [win[0]]
+            slots = keep + [keep[0]]
+            r.shuffle(slots)
+            idx[x][:len(slots)] = slots
+            listed[x] = set(keep)
+        mask, bad = _o.window_mask_from_indices(grid, kernel, idx, dil)
+        assert not bad.any()
+        q, k, v = (_hm(grid, heads, D, seed + j) for j in range(3))
+        _, out = orc.unfused_fwd(q, k, v, kernel, dil, 0.8, mask=mask)
+        qf, kf, vf = (a.reshape(1, heads, toks, D) for a in (q, k, v))
+        allowed = np.zeros((toks, toks), bool)
+        for x, ys in listed.items():
+            allowed[np.ravel_multi_index(x, grid), sorted(ys)] = True
+        s = np.where(allowed, 0.8 * np.einsum("bhxc,bhyc->bhxy", qf, kf), -np.inf)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        ref = (p / p.sum(-1, keepdims=True)) @ vf
+        assert np.max(np.abs(out.reshape(ref.shape) - ref)) < 1e-12, grid
+
+
 ALL_CHECKS = [
     ("windows", lambda o: check_windows(o)),
     ("dense2d", lambda o: check_dense(o, grid=(4, 5))),
@@ -535,6 +592,7 @@ ALL_CHECKS = [
     ("rpb_fd", check_rpb_fd),
     ("masked_windows", check_masked_windows),
     ("outer_window_mask", check_outer_window_mask),
+    ("index_mask", check_index_mask),
 ] + [(f"fd{i}", (lambda c: (lambda o: check_fd(o, c)))(c)) for i, c in enumerate(FD_CASES)]
 
 

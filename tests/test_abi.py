@@ -297,3 +297,29 @@ def test_window_mask_checks_of_the_binding():
                 None):
         with pytest.raises(ValueError):
             na._check_window_mask(bad, q, (3, 5, 5))
+
+
+def test_index_mask_entry_point_rejects_bad_arguments_on_the_host(lib):
+    """na_window_mask_from_indices reads only the grid fields of the problem
+    and refuses a malformed grid, a negative slot count and null or misaligned
+    pointers before any launch; the binding refuses indices that are not a
+    contiguous int64 GPU tensor."""
+    import torch
+    fake = ctypes.c_void_p(1 << 20)
+    p = _p()
+    f = lib.na_window_mask_from_indices
+    assert f(ctypes.byref(p), fake, -1, fake, fake, None) == na.NA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), None, 4, fake, fake, None) == na.NA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), fake, 4, None, fake, None) == na.NA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), fake, 4, fake, None, None) == na.NA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 4), 4, fake, fake,
+             None) == na.NA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), fake, 4, fake, ctypes.c_void_p((1 << 20) + 2),
+             None) == na.NA_ERR_INVALID_ARG
+    for bad in (_p(kernel=(3, 17)), _p(kernel=(3, 9), dil=(1, 2)), _p(kernel=(0, 3))):
+        assert f(ctypes.byref(bad), fake, 4, fake, fake, None) == na.NA_ERR_INVALID_ARG
+    assert f(None, fake, 4, fake, fake, None) == na.NA_ERR_INVALID_ARG
+    for idx in (torch.zeros((6, 7, 3), dtype=torch.int32), torch.zeros((6, 7, 3), dtype=torch.int64),
+                torch.zeros((3, 6, 7), dtype=torch.int64).permute(1, 2, 0)):
+        with pytest.raises(ValueError):
+            na.na_window_mask_from_indices(idx, (3, 3))

@@ -8,6 +8,7 @@ Bar as for the unmasked parity tests (per tensor, max abs error over max abs
 reference value): 1e-4 fp32, 2e-2 bf16, 2e-3 fp16. A query that keeps no key
 must give a zero output and lse = -inf.
 """
+import itertools
 import sys
 import zlib
 
@@ -183,3 +184,137 @@ def test_mask_at_an_odd_address_matches_the_aligned_one():
     torch.cuda.synchronize()
     for name, x, y in zip(("out", "lse", "dq", "dk", "dv"), res[0], res[1]):
         assert rel_err(np64(y), np64(x)) <= TOL[dtype], name
+
+
+# ---------------------------------------------------------------------------
+# Index tensors of attended tokens (na_window_mask_from_indices): the mask
+# bytes and the per-query counts of invalid slots are integer results, so the
+# bar is bitwise equality with the oracle's window_mask_from_indices.
+
+def window_tokens(grid, kernel, dil, x):
+    """Flat indices of the tokens of query x's window (oracle window starts)."""
+    axes = [[oracle.window_start(grid[a], kernel[a], dil[a], x[a]) + dil[a] * j
+             for j in range(kernel[a])] for a in range(len(grid))]
+    return [int(np.ravel_multi_index(c, grid)) for c in itertools.product(*axes)]
+
+
+def random_indices(grid, kernel, dil, seed, invalid=False):
+    """Per query token a random subset of its window's tokens, shuffled, one
+    repeated, the rest of its m slots -1; the middle token lists nothing. With
+    invalid, every seventh query also lists tokens outside its window, off
+    the grid and below -1."""
+    r = np.random.default_rng(seed)
+    K, toks = int(np.prod(kernel)), int(np.prod(grid))
+    idx = np.full(tuple(grid) + (K + 4,), -1, np.int64)
+    for n, x in enumerate(np.ndindex(*grid)):
+        if x == tuple(g // 2 for g in grid):
+            continue
+        win = window_tokens(grid, kernel, dil, x)
+        keep = [t for t in win if r.random() < 0.6] or [win[-1]]
+        slots = keep + [keep[0]]
+        if invalid and n % 7 == 0:
+            inside = set(win)
+            outside = [t for t in range(toks) if t not in inside]
+            slots += [toks + n, -2 - n] + ([int(r.choice(outside))] if outside else [])
+        r.shuffle(slots)
+        idx[x][:len(slots)] = slots
+    return idx
+
+
+def _dil(d, nd):
+    return (d,) * nd if isinstance(d, int) else tuple(d)
+
+
+INDEX_CASES = [((40, 37), (9, 9), 1), ((19, 23), (5, 7), (2, 1)), ((5, 11, 13), (3, 5, 5), 1),
+               ((7, 12, 13), (3, 3, 3), (2, 1, 2)), ((4, 9), (1, 3), 1)]
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=[f"{c[0]}-k{c[1]}-d{c[2]}" for c in INDEX_CASES])
+def test_index_mask_matches_oracle(case):
+    grid, kernel, dil = case
+    dil = _dil(dil, len(grid))
+    say("index mask", grid, kernel, dil)
+    idx = random_indices(grid, kernel, dil, seed=len(grid) * 100 + kernel[-1], invalid=True)
+    want_mask, want_bad = oracle.window_mask_from_indices(grid, kernel, idx, dil)
+    assert want_bad.any()
+    mask, bad = na.na_window_mask_from_indices(torch.from_numpy(idx).cuda(), kernel, dil,
+                                               check=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(mask.cpu().numpy(), want_mask)
+    assert np.array_equal(bad.cpu().numpy(), want_bad)
+    with pytest.raises(ValueError):
+        na.na_window_mask_from_indices(torch.from_numpy(idx).cuda(), kernel, dil)
+
+
+def test_index_mask_into_an_odd_address_and_no_slots():
+    """The mask may start at any byte (the clearing kernel then stores bytes);
+    zero slots per query drop every key."""
+    grid, kernel = (19, 23), (5, 7)
+    idx = torch.from_numpy(random_indices(grid, kernel, (1, 1), seed=3)).cuda()
+    want, _ = na.na_window_mask_from_indices(idx, kernel)
+    store = torch.full((want.numel() + 1,), 7, dtype=torch.uint8, device="cuda")
+    odd = store[1:].view(want.shape)
+    na.na_window_mask_from_indices(idx, kernel, mask=odd)
+    torch.cuda.synchronize()
+    assert odd.data_ptr() % 2 == 1 and torch.equal(odd, want) and int(store[0]) == 7
+    none = torch.empty(grid + (0,), dtype=torch.int64, device="cuda")
+    m0, b0 = na.na_window_mask_from_indices(none, kernel)
+    torch.cuda.synchronize()
+    assert not m0.any() and not b0.any()
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[7]],
+                         ids=[_id(CASES[0]), _id(CASES[2]), _id(CASES[7])])
+def test_indices_through_the_masked_kernels_match_oracle(case):
+    """Index tensor -> mask (GPU) -> na_fwd_masked / na_bwd_masked (GPU)
+    against the oracle's masked reference with the oracle's mask from the
+    same indices."""
+    shape, kernel, dil, dtype = case
+    grid = tuple(shape[1:-2])
+    d = _dil(dil, len(grid))
+    seed = zlib.crc32(_id(case).encode()) % 997
+    say("indices through masked kernels", _id(case))
+    idx = random_indices(grid, kernel, d, seed)
+    omask, _ = oracle.window_mask_from_indices(grid, kernel, idx, d)
+    q, k, v, dout = make_random(shape, dtype, seed=seed)
+    mask, _ = na.na_window_mask_from_indices(torch.from_numpy(idx).cuda(), kernel, dil)
+    qd, kd, vd, dd = (t.cuda() for t in (q, k, v, dout))
+    scale = shape[-1] ** -0.5
+    out, lse = na.na_fwd_masked(qd, kd, vd, mask, kernel, dil, scale)
+    dq, dk, dv = na.na_bwd_masked(qd, kd, vd, out, dd, lse, mask, kernel, dil, scale)
+    torch.cuda.synchronize()
+    got = {"out": np64(out), "lse": np64(lse), "dq": np64(dq), "dk": np64(dk), "dv": np64(dv)}
+    ref = reference(q, k, v, dout, kernel, dil, scale, omask)
+    for n in ref:
+        assert rel_err(got[n], ref[n]) <= TOL[dtype], n
+    assert np.array_equal(np.isneginf(got["lse"][0, ..., 0]), ~omask.any(-1))
+
+
+def test_index_mask_at_the_3d_workload_size():
+    """The 3D grid of the 16 x 256 x 256, 3 x 5 x 5 workload (about 1M query
+    tokens, 75 slots each): every query lists its whole window in order except
+    the key at place (token mod 75), which it replaces by -1, so the mask is
+    all ones but that byte. Window starts per axis from the oracle; the
+    indices are built on the GPU."""
+    grid, kernel = (16, 256, 256), (3, 5, 5)
+    K = 75
+    dev = torch.device("cuda:0")
+    axes = []
+    for a in range(3):
+        st = torch.tensor([oracle.window_start(grid[a], kernel[a], 1, x) for x in range(grid[a])],
+                          device=dev)
+        axes.append(st[:, None] + torch.arange(kernel[a], device=dev)[None, :])   # [L, k]
+    t = axes[0][:, None, None, :, None, None]
+    h = axes[1][None, :, None, None, :, None]
+    w = axes[2][None, None, :, None, None, :]
+    idx = ((t * grid[1] + h) * grid[2] + w).reshape(grid + (K,)).contiguous()
+    drop = torch.arange(idx[..., 0].numel(), device=dev).reshape(grid) % K
+    idx.scatter_(-1, drop[..., None], -1)
+    mask, bad = na.na_window_mask_from_indices(idx, kernel)
+    torch.cuda.synchronize()
+    want = torch.ones_like(mask)
+    want.scatter_(-1, drop[..., None], 0)
+    assert not bad.any()
+    assert torch.equal(mask, want)
+    del idx, mask, want
+    torch.cuda.empty_cache()
