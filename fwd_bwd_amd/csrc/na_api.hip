@@ -410,26 +410,26 @@ na_status launch_fast(Kern kern, const FastPlan &pl, const Args &a, hipStream_t 
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(32, 2, true) X(32, 3, true) X(32, 4, true)
 
-// Window masks (a.mask) run on the fp32 register-resident kernels when the
-// mask is 4-byte aligned (the forward and dq read it in aligned dwords); 16-bit
-// tensors take the split kernels, and so do the dk/dv walks that have no
-// masked instantiation (fast_dkdv_masked).
-template <typename T>
-bool fast_mask_ok(const uint8_t *mask) {
-    return std::is_same<T, float>::value && (reinterpret_cast<uintptr_t>(mask) & 3u) == 0;
-}
+// Window masks (a.mask) run on the register-resident kernels when the mask
+// is 4-byte aligned (the forward and dq read it in aligned dwords), 16-bit
+// tensors included (converted to fp32 while staged, as without a mask); the
+// dk/dv walks that have no masked instantiation (fast_dkdv_masked) take the
+// split kernels.
+bool fast_mask_ok(const uint8_t *mask) { return (reinterpret_cast<uintptr_t>(mask) & 3u) == 0; }
 
 template <typename T>
 na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgsT<T> &a, hipStream_t s) {
-    if constexpr (std::is_same<T, float>::value) {
-        if (a.mask) {
+    if (a.mask) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return launch_fast(na::fast::fwd_kernel<T, D, C, C, T3, true>, pl, a, s);
+        if constexpr (std::is_same<T, float>::value) {
             NA_FAST_CASES(X)
-#undef X
-            return NA_ERR_UNSUPPORTED;
+        } else {
+            NA_FAST_CASES16(X)
         }
+#undef X
+        return NA_ERR_UNSUPPORTED;
     }
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
@@ -445,16 +445,20 @@ na_status fast_fwd(const FastPlan &pl, const na::fast::FwdArgsT<T> &a, hipStream
 
 template <typename T>
 na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
-    if constexpr (std::is_same<T, float>::value) {
-        if (a.mask) {
+    if (a.mask) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3, true>, pl, a, s) \
                       : launch_fast(na::fast::dq_kernel<T, D, C, C, T3, false, true>, pl, a, s);
+        if constexpr (std::is_same<T, float>::value) {
             NA_FAST_CASES(X)
-#undef X
-            return NA_ERR_UNSUPPORTED;
+        } else {
+            NA_FAST_CASES16(X)
         }
+#undef X
+        return NA_ERR_UNSUPPORTED;
+    }
+    if constexpr (std::is_same<T, float>::value) {
 #define X(D, C, T3)                                                                       \
     if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
         return pl.pad ? launch_fast(na::fast::dq_kernel<T, D, C, C, T3, T3>, pl, a, s)    \
@@ -472,15 +476,19 @@ na_status fast_dq(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_
     return NA_ERR_UNSUPPORTED;
 }
 
-// The masked dk/dv instantiations (fp32 only): the interior square walks at two
+// The masked dk/dv instantiations: the interior square walks at two
 // workgroups per CU up to 5 patches on one plane and 3 on several (the walk of
 // 4 spilled there); at head_dim 32 the longer walks of the border classes at
 // one workgroup per CU: 7 x 5, 5 x 7, 6 x 4, 4 x 6, 6 x 6, 7 x 7 on one plane,
-// 4 x 3, 3 x 4, 4 x 4 and (padded) 6 x 4, 4 x 6, 6 x 6 on several.
+// 4 x 3, 3 x 4, 4 x 4 and (padded) 6 x 4, 4 x 6, 6 x 6 on several. The 16-bit
+// types take the head_dim 32 ones.
 #define NA_FAST_CASES_MASKED_DKDV(X)                                                      \
     X(16, 2, false) X(16, 3, false) X(16, 4, false) X(16, 5, false)                      \
     X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
     X(16, 2, true) X(16, 3, true) X(32, 2, true) X(32, 3, true)
+#define NA_FAST_CASES16_MASKED_DKDV(X)                                                    \
+    X(32, 2, false) X(32, 3, false) X(32, 4, false) X(32, 5, false)                      \
+    X(32, 2, true) X(32, 3, true)
 bool fast_dkdv_masked(const FastPlan &pl) {
     const int ch = pl.c, cw = pl.cw;
     if (ch == cw && ch >= 2 && ch <= (pl.t3 ? 3 : 5))
@@ -494,37 +502,39 @@ bool fast_dkdv_masked(const FastPlan &pl) {
 
 template <typename T>
 na_status fast_dkdv(const FastPlan &pl, const na::fast::BwdArgsT<T> &a, hipStream_t s) {
-    if constexpr (std::is_same<T, float>::value) {
-        if (a.mask) {
-            if (!fast_dkdv_masked(pl)) return NA_ERR_UNSUPPORTED;
-            if (pl.cw == pl.c && pl.c <= (pl.t3 ? 3 : 5)) {
+    if (a.mask) {
+        if (!fast_dkdv_masked(pl)) return NA_ERR_UNSUPPORTED;
+        if (pl.cw == pl.c && pl.c <= (pl.t3 ? 3 : 5)) {
 #define X(D, C, T3)                                                                       \
-    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                                   \
+    if (a.g.head_dim == D && pl.c == C && pl.t3 == T3)                               \
         return pl.pad ? launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, T3, true>, pl, a, s) \
                       : launch_fast(na::fast::dkdv_kernel<T, D, C, C, T3, false, true>, pl, a, s);
+            if constexpr (std::is_same<T, float>::value) {
                 NA_FAST_CASES_MASKED_DKDV(X)
-#undef X
-                return NA_ERR_UNSUPPORTED;
+            } else {
+                NA_FAST_CASES16_MASKED_DKDV(X)
             }
-#define X(CH, CW)                                                                        \
-    if (pl.c == CH && pl.cw == CW && !pl.t3)                                             \
-        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false, false, true>, pl, a, s);
-            X(7, 5) X(5, 7) X(6, 4) X(4, 6) X(6, 6) X(7, 7)
-#undef X
-#define X(CH, CW)                                                                        \
-    if (pl.c == CH && pl.cw == CW && pl.t3)                                              \
-        return pl.pad                                                                    \
-                   ? launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s) \
-                   : launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, false, true>, pl, a, s);
-            X(4, 3) X(3, 4) X(4, 4)
-#undef X
-#define X(CH, CW)                                                                        \
-    if (pl.c == CH && pl.cw == CW && pl.t3 && pl.pad)                                    \
-        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s);
-            X(6, 4) X(4, 6) X(6, 6)
 #undef X
             return NA_ERR_UNSUPPORTED;
         }
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && !pl.t3)                                         \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, false, false, true>, pl, a, s);
+        X(7, 5) X(5, 7) X(6, 4) X(4, 6) X(6, 6) X(7, 7)
+#undef X
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && pl.t3)                                          \
+        return pl.pad                                                                \
+                   ? launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s) \
+                   : launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, false, true>, pl, a, s);
+        X(4, 3) X(3, 4) X(4, 4)
+#undef X
+#define X(CH, CW)                                                                        \
+    if (pl.c == CH && pl.cw == CW && pl.t3 && pl.pad)                                \
+        return launch_fast(na::fast::dkdv_border_kernel<T, 32, CH, CW, true, true, true>, pl, a, s);
+        X(6, 4) X(4, 6) X(6, 6)
+#undef X
+        return NA_ERR_UNSUPPORTED;
     }
     if (pl.cw != pl.c) {
         // border classes with a longer walk along one axis (rect_walk_compiled)
@@ -730,8 +740,8 @@ na_status run_fwd(const Prob &pr, na::FwdArgs a, hipStream_t s) {
         }
     }
     FastPlan pl;
-    // window masks: the fp32 register-resident kernels, else the split kernels
-    if ((!a.mask || fast_mask_ok<T>(a.mask)) && fast_plan_fwd(pr, &pl)) {
+    // window masks: the register-resident kernels, else the split kernels
+    if ((!a.mask || fast_mask_ok(a.mask)) && fast_plan_fwd(pr, &pl)) {
         na::fast::FwdArgsT<T> fa{};
         fa.g = pl.g;
         fa.q = static_cast<const T *>(a.q);
@@ -855,7 +865,7 @@ na_status run_bwd(const Prob &pr, na::BwdArgs a, int32_t variant, int32_t kv_spl
         fa.mask = a.mask;
         fa.mask_k = a.mask_k;
         fa.mask_bytes = pr.tokens * a.mask_k;
-        const bool mask_fast = !a.mask || fast_mask_ok<T>(a.mask);
+        const bool mask_fast = !a.mask || fast_mask_ok(a.mask);
         if (phases & kPhaseDq) {
             if (mask_fast && fast_plan_fwd(pr, &pq, true)) {
                 fa.g = pq.g;

@@ -77,7 +77,8 @@ typedef enum {
                      MFMA with fp32 accumulation; the attention weights and score
                      gradients are rounded to the tensor type before the weighted
                      sums; softmax statistics, lse and delta stay fp32. Other
-                     16-bit problems: fp32 arithmetic after conversion. */
+                     16-bit problems, and every 16-bit problem with a window
+                     mask: fp32 arithmetic after conversion. */
 } na_dtype;
 
 /* Backward strategies (the NATTEN issue's use_kv_parallelism_in_fused_na
@@ -183,11 +184,14 @@ na_status na_bwd_framed(const na_problem *p, const void *q, const void *k, const
  * row-major (t, h, w) order), exactly the mask of na_qk. Masked scores are
  * -inf before the softmax; a query that keeps no key gets a zero output, lse
  * = -inf and contributes nothing to the backward. Otherwise exactly na_fwd
- * and na_bwd (same buffers, rules and errors; mask must be non-null). fp32
- * problems with a 4-byte aligned mask run on the register-resident kernels
- * (forward, dq and the interior dk/dv tiles read the mask rows they need);
- * 16-bit tensors, the dk/dv border tiles and the KV-parallel backward run on
- * the general tile kernels, which test every pair against the mask. */
+ * and na_bwd (same buffers, rules and errors; mask must be non-null). With a
+ * 4-byte aligned mask, fp32 problems with head_dim 16 or 32 and bf16 / fp16
+ * ones with head_dim 32 run on the register-resident kernels (16-bit tensors
+ * converted to fp32 while staged; forward and dq read each query's mask row,
+ * dk/dv one byte per query of each key's inverse walk) wherever a masked walk
+ * is compiled; other problems, the dk/dv tiles without such a walk and the
+ * KV-parallel backward run on the general tile kernels, which test every
+ * pair against the mask. */
 na_status na_fwd_masked(const na_problem *p, const void *q, const void *k, const void *v,
                         void *out, float *lse, const uint8_t *mask, void *hip_stream);
 na_status na_bwd_masked(const na_problem *p, const void *q, const void *k, const void *v,

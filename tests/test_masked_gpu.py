@@ -62,6 +62,14 @@ CASES = [
     ((2, 35, 33, 1, 32), (7, 7), 1, torch.float32),
     ((1, 4, 18, 20, 2, 16), (3, 3, 3), 1, torch.float32),
     ((1, 7, 12, 13, 2, 32), (3, 3, 3), (2, 1, 2), torch.float32),   # dilation along T and W
+    # 16-bit tensors with head_dim 32 on the same register-resident kernels
+    # (converted while staged): 2D interior walk 5 with border walks 6 and 7,
+    # 2D 7 x 7 with its border classes, 3D walk 4 (masked border kernel) with
+    # longer border walks, 3D with dilation
+    ((1, 40, 37, 2, 32), (9, 9), 1, torch.bfloat16),
+    ((2, 35, 33, 1, 32), (7, 7), 1, torch.float16),
+    ((1, 6, 20, 18, 1, 32), (5, 7, 7), 1, torch.bfloat16),
+    ((1, 7, 12, 13, 2, 32), (3, 3, 3), (2, 1, 2), torch.float16),
 ]
 
 
