@@ -34,7 +34,8 @@ window.
 Beside the headline step the same run times the KV-parallel backward variant
 on the same inputs ("kvparallel", per kv_splits: 0 = float atomics, 1 and 4 =
 bounded accumulator copies, bitwise reproducible), the headline shape with
-fp16 tensors ("fp16") and the two bf16 workloads ("bf16").
+fp16 tensors ("fp16") and the two bf16 workloads ("bf16"; the head_dim-32 one
+also with the random 2/3 window mask, "masked").
 
 The same function is also timed through the unfused ops (the script's method
 = 'unfused': window scores, softmax, weighted sum, and their backward AGRAD,
@@ -721,6 +722,16 @@ def main():
             bf16[name] = {"steps": nb, **sb}
             del rb
             torch.cuda.empty_cache()
+            if wb.head_dim == 32:
+                # the same step with a random window mask keeping 2/3 of every
+                # window: masked 16-bit problems compute in fp32 on the
+                # register-resident kernels
+                rm = MaskedRunner(wb, random_window_mask(wb, 2 / 3))
+                log(f"[bench] timing {name} with a random window mask")
+                per, _ = rm.time(nb, min(args.warmup, 2), flush)
+                bf16[name]["masked"] = {"kept_fraction": 0.6667, **framed_leg(wb, per, sb)}
+                del rm
+                torch.cuda.empty_cache()
         result["bf16"] = bf16
 
     if not args.no_cpu_baseline:
